@@ -1,0 +1,614 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a closed form, a library routine, an
+invariant or a brute force on a tiny input, chosen so that a dropped term, a
+wrong sign or index, or a transposed operand in that part fails here.
+None of these needs a GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy.special import sph_harm_y
+from scipy.spatial.transform import Rotation
+
+import oracle
+from gaussian_splatting_tile_amd import scenes
+
+PI = math.pi
+
+
+def _cam(width=128, height=128, f=128.0, viewmat=None, lod=0.0):
+    vm = np.concatenate([np.eye(3), np.zeros((3, 1))], axis=1) if viewmat is None else viewmat
+    return scenes.Camera(width, height, f, f, width / 2.0, height / 2.0,
+                         np.asarray(vm, np.float32), lod_min_radius_px=lod)
+
+
+def _params(means, scales, quats=None, opac=None, rgb_dc=None, degree=0):
+    """fp64 parameter arrays; scalar scales are isotropic, rgb_dc is [3][n]."""
+    means = np.asarray(means, np.float64).reshape(3, -1)
+    n = means.shape[1]
+    scales = np.full((3, n), float(scales)) if np.ndim(scales) == 0 else np.asarray(scales, np.float64)
+    quats = np.tile([[1.0], [0.0], [0.0], [0.0]], (1, n)) if quats is None else np.asarray(quats, np.float64)
+    opac = np.full(n, 0.8) if opac is None else np.asarray(opac, np.float64).reshape(n)
+    sh = np.zeros(((degree + 1) ** 2, 3, n))
+    if rgb_dc is not None:
+        sh[0] = np.asarray(rgb_dc, np.float64).reshape(3, n)
+    return means, scales, quats, opac, sh
+
+
+# ---------------------------------------------------------------- SH basis --
+def _scipy_real_basis(d):
+    """Real SH from scipy's complex harmonics (which carry the Condon-Shortley
+    phase): sqrt2 Re Y_l^m for m > 0, sqrt2 Im Y_l^|m| for m < 0, Y_l^0; this is
+    (-1)^|m| times the phase-free textbook real basis."""
+    x, y, z = d
+    theta = math.acos(max(-1.0, min(1.0, z)))
+    phi = math.atan2(y, x) % (2 * PI)
+    out = []
+    for l in range(4):
+        for m in range(-l, l + 1):
+            c = complex(sph_harm_y(l, abs(m), theta, phi))
+            if m > 0:
+                out.append(math.sqrt(2) * c.real)
+            elif m < 0:
+                out.append(math.sqrt(2) * c.imag)
+            else:
+                out.append(c.real)
+    return np.array(out)
+
+
+def test_sh_basis_matches_scipy_real_harmonics():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        d = rng.standard_normal(3)
+        d /= np.linalg.norm(d)
+        Y, _ = oracle.sh_basis(d)
+        np.testing.assert_allclose(Y, _scipy_real_basis(d), rtol=0, atol=1e-13)
+
+
+def test_sh_basis_addition_theorem_and_axis_values():
+    rng = np.random.default_rng(12)
+    for _ in range(100):
+        d = rng.standard_normal(3)
+        d /= np.linalg.norm(d)
+        Y, _ = oracle.sh_basis(d)
+        for l in range(4):
+            band = Y[l * l:(l + 1) ** 2]
+            assert abs((band ** 2).sum() - (2 * l + 1) / (4 * PI)) < 1e-13
+    # along +z only the m = 0 members survive, each sqrt((2l+1)/4pi)
+    Y, _ = oracle.sh_basis(np.array([0.0, 0.0, 1.0]))
+    expect = np.zeros(16)
+    for l in range(4):
+        expect[l * l + l] = math.sqrt((2 * l + 1) / (4 * PI))
+    np.testing.assert_allclose(Y, expect, atol=1e-15)
+
+
+def test_sh_basis_orthonormal_by_quadrature():
+    # Gauss-Legendre in cos(theta) x uniform phi: exact for degree <= 6 products
+    xs, ws = np.polynomial.legendre.leggauss(12)
+    phis = np.arange(16) * 2 * PI / 16
+    G = np.zeros((16, 16))
+    for ct, w in zip(xs, ws):
+        st = math.sqrt(1 - ct * ct)
+        for ph in phis:
+            Y, _ = oracle.sh_basis(np.array([st * math.cos(ph), st * math.sin(ph), ct]))
+            G += w * (2 * PI / 16) * np.outer(Y, Y)
+    np.testing.assert_allclose(G, np.eye(16), atol=1e-12)
+
+
+def test_sh_basis_gradient_matches_central_differences():
+    rng = np.random.default_rng(13)
+    h = 1e-6
+    for _ in range(20):
+        d = rng.standard_normal(3)
+        _, dY = oracle.sh_basis(d)
+        for r in range(3):
+            e = np.zeros(3)
+            e[r] = h
+            num = (oracle.sh_basis(d + e)[0] - oracle.sh_basis(d - e)[0]) / (2 * h)
+            np.testing.assert_allclose(dY[:, r], num, atol=1e-8)
+
+
+def test_colour_degree0_is_half_plus_c0_times_dc():
+    means, scales, quats, opac, sh = _params([[0.0], [0.0], [3.0]], 0.05, rgb_dc=[[0.3], [-0.2], [-5.0]])
+    p = oracle.project(means, scales, quats, opac, 0, sh, _cam(), precision="f64")
+    c0 = 0.5 / math.sqrt(PI)
+    np.testing.assert_allclose(p["rgb"][:, 0], [0.5 + c0 * 0.3, 0.5 - c0 * 0.2, 0.0], atol=1e-15)
+    assert p["clamped"][0] == 4          # blue channel clamped at 0
+
+
+# ------------------------------------------------------- EWA projection ---
+def _sigma2_from_conic(p, g=0):
+    a, b, c = p["conic"][:, g]
+    Q = np.array([[a, b], [b, c]])
+    return np.linalg.inv(Q) - 0.3 * np.eye(2)
+
+
+def test_on_axis_isotropic_closed_form():
+    for z, s, f in [(3.0, 0.05, 128.0), (10.0, 0.2, 1000.0), (2.5, 0.01, 1400.0)]:
+        means, scales, quats, opac, sh = _params([[0.0], [0.0], [z]], s)
+        cam = _cam(f=f, width=256, height=256)
+        p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+        var = (f * s / z) ** 2 + 0.3
+        np.testing.assert_allclose(p["conic"][:, 0], [1 / var, 0.0, 1 / var], rtol=1e-12, atol=1e-15)
+        assert p["radius"][0] == math.ceil(3 * math.sqrt(var))
+        assert p["u"][0] == 128.0 and p["v"][0] == 128.0 and p["z"][0] == z
+
+
+def test_pinhole_mean_and_camera_pose():
+    # a point on the optical axis of a posed camera lands on the principal point,
+    # and one at x/z = 1/4 lands fx/4 to the right
+    vm = scenes.look_at(np.array([3.0, 1.0, -7.0]), target=(0.5, -0.25, 0.75))
+    cam = _cam(width=200, height=100, f=160.0, viewmat=vm)
+    R, t = vm[:, :3].astype(np.float64), vm[:, 3].astype(np.float64)
+    eye = -R.T @ t
+    zdir = R[2]
+    xdir = R[0]
+    pts = np.stack([eye + 4.0 * zdir, eye + 4.0 * zdir + 1.0 * xdir, eye + 4.0 * zdir - 0.5 * R[1]], axis=1)
+    means, scales, quats, opac, sh = _params(pts, 0.01)
+    p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+    np.testing.assert_allclose(p["u"], [100.0, 100.0 + 160.0 / 4, 100.0], atol=1e-9)
+    np.testing.assert_allclose(p["v"], [50.0, 50.0, 50.0 - 160.0 / 8], atol=1e-9)
+    np.testing.assert_allclose(p["z"], [4.0, 4.0, 4.0], atol=1e-12)
+
+
+def test_projected_covariance_matches_monte_carlo():
+    """Sample the 3D Gaussian (rotation from scipy, not the oracle), push every
+    sample through the exact pinhole, compare the empirical 2D covariance with
+    the oracle's Sigma2 (conic inverse minus the dilation).  Checks the
+    rotation, the camera rotation and every entry of the Jacobian, signs
+    included, to Monte-Carlo accuracy."""
+    rng = np.random.default_rng(21)
+    vm = scenes.look_at(np.array([2.0, -1.5, -9.0]), target=(0.3, 0.2, 0.1))
+    f = 1000.0
+    cam = _cam(width=1600, height=1200, f=f, viewmat=vm)
+    R, t = vm[:, :3].astype(np.float64), vm[:, 3].astype(np.float64)
+    for trial in range(4):
+        q = rng.standard_normal(4)
+        q /= np.linalg.norm(q)
+        s = np.array([0.04, 0.015, 0.025]) * (1 + trial * 0.3)
+        mu = np.array([0.8, -0.6, 0.4]) * (trial - 1.5)
+        rot = Rotation.from_quat([q[1], q[2], q[3], q[0]]).as_matrix()     # scipy: (x, y, z, w)
+        Sigma = rot @ np.diag(s ** 2) @ rot.T
+        p = oracle.project(mu.reshape(3, 1), s.reshape(3, 1), q.reshape(4, 1), np.array([0.9]), 0,
+                           np.zeros((1, 3, 1)), cam, precision="f64")
+        assert p["radius"][0] > 0
+        S2 = _sigma2_from_conic(p)
+        nsamp = 400_000
+        pts = rng.multivariate_normal(mu, Sigma, size=nsamp)
+        pc = pts @ R.T + t
+        uv = np.stack([f * pc[:, 0] / pc[:, 2] + cam.cx, f * pc[:, 1] / pc[:, 2] + cam.cy], axis=1)
+        emp = np.cov(uv.T)
+        # standard error of a covariance entry ~ sqrt((S_ii S_jj + S_ij^2) / n)
+        se = np.sqrt((np.outer(np.diag(emp), np.diag(emp)) + emp ** 2) / nsamp)
+        assert np.all(np.abs(emp - S2) < 6 * se + 1e-3 * np.abs(S2).max()), (emp, S2)
+        # the mean lands where the pinhole puts the centre
+        pm = R @ mu + t
+        np.testing.assert_allclose([p["u"][0], p["v"][0]], [f * pm[0] / pm[2] + cam.cx,
+                                                          f * pm[1] / pm[2] + cam.cy], atol=1e-9)
+
+
+def test_guard_clamps_jacobian_to_frustum_edge():
+    """Far outside the guard band the Jacobian is the one at the band edge:
+    two Gaussians at the same depth, one at x/z = 3 l and one at x/z = l,
+    get the same projected covariance."""
+    cam = _cam(width=256, height=256, f=128.0)
+    lx = 1.3 * (0.5 * 256 / 128.0)
+    z = 4.0
+    means = np.array([[3 * lx * z, lx * z], [0.3, 0.3], [z, z]])
+    q = np.array([[0.9, 0.9], [0.1, 0.1], [-0.3, -0.3], [0.2, 0.2]])
+    p = oracle.project(means, np.full((3, 2), 3.0), q, np.array([0.9, 0.9]), 0, np.zeros((1, 3, 2)),
+                       cam, precision="f64")
+    assert p["radius"][0] > 0 and p["radius"][1] > 0
+    np.testing.assert_allclose(p["conic"][:, 0], p["conic"][:, 1], rtol=1e-12)
+    # and inside the band the Jacobian follows x/z (a different covariance)
+    means2 = means.copy()
+    means2[0, 1] = 0.5 * lx * z
+    p2 = oracle.project(means2, np.full((3, 2), 3.0), q, np.array([0.9, 0.9]), 0, np.zeros((1, 3, 2)),
+                        cam, precision="f64")
+    assert abs(p2["conic"][0, 1] - p["conic"][0, 0]) > 1e-6 * abs(p["conic"][0, 0])
+
+
+def test_near_plane_and_nonfinite_and_zero_quat_cull():
+    means = np.array([[0.0, 0.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0, 0.0], [0.2, 0.2001, 3.0, 3.0, 3.0]])
+    q = np.array([[1.0, 1.0, 0.0, 1.0, 1.0], [0, 0, 0, 0, 0], [0, 0, 0, 0, 0], [0, 0, 0, 0, 0]], np.float64)
+    s = np.full((3, 5), 0.05)
+    s[1, 3] = np.nan
+    o = np.array([0.5, 0.5, 0.5, 0.5, np.inf])
+    p = oracle.project(means, s, q, o, 0, np.zeros((1, 3, 5)), _cam(), precision="f32")
+    assert list(p["radius"] > 0) == [False, True, False, False, False]
+    assert list(p["tiles"]) == [0, p["tiles"][1], 0, 0, 0]
+    assert np.all(p["conic"][:, [0, 2, 3, 4]] == 0) and np.all(p["u"][[0, 2, 3, 4]] == 0)
+
+
+def test_fp32_contract_close_to_fp64():
+    sc = scenes.config(2, n_override=5000)
+    cam = sc.cameras[0]
+    p32 = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 3, sc.sh, cam, precision="f32")
+    p64 = oracle.project(sc.means.astype(np.float64), sc.scales.astype(np.float64),
+                         sc.quats.astype(np.float64), sc.opacities.astype(np.float64), 3,
+                         sc.sh.astype(np.float64), cam, precision="f64")
+    vis = (p32["radius"] > 0) & (p64["radius"] > 0)
+    assert vis.sum() > 4000
+    np.testing.assert_allclose(p32["u"][vis], p64["u"][vis], rtol=1e-6, atol=1e-4)
+    np.testing.assert_allclose(p32["conic"][:, vis], p64["conic"][:, vis], rtol=1e-4, atol=1e-7)
+    np.testing.assert_allclose(p32["rgb"][:, vis], p64["rgb"][:, vis], atol=1e-6)
+    assert np.mean(p32["radius"][vis] == p64["radius"][vis]) > 0.99
+
+
+# ----------------------------------------------------- radius and rect ---
+def test_rect_matches_brute_force_tile_overlap():
+    """The half-open tile rect equals the set of 16x16 tiles that intersect the
+    closed square [u-r, u+r] x [v-r, v+r] (tile tx spans [16 tx, 16 tx + 16)),
+    evaluated on the same fp32 u, v and r."""
+    rng = np.random.default_rng(31)
+    W, H = 200, 120
+    TX, TY = 13, 8
+    n = 3000
+    zs = np.full(n, 5.0)
+    u_t = rng.uniform(-40, 240, n)
+    v_t = rng.uniform(-40, 160, n)
+    # put a third of the means exactly on tile boundaries
+    u_t[: n // 3] = 16.0 * rng.integers(-2, 15, n // 3)
+    v_t[n // 6: n // 2] = 16.0 * rng.integers(-2, 9, n // 2 - n // 6)
+    f = 100.0
+    means = np.stack([(u_t - W / 2) * zs / f, (v_t - H / 2) * zs / f, zs]).astype(np.float32)
+    s = np.exp(rng.uniform(-5, -0.5, (3, n))).astype(np.float32)
+    q = rng.standard_normal((4, n)).astype(np.float32)
+    cam = _cam(width=W, height=H, f=f)
+    p = oracle.project(means, s, q, np.full(n, 0.5, np.float32), 0, np.zeros((1, 3, n), np.float32),
+                       cam, precision="f32")
+    u = p["u"].astype(np.float32)
+    v = p["v"].astype(np.float32)
+    hit = 0
+    for g in range(n):
+        r = np.float32(p["radius"][g])
+        if r == 0:
+            continue
+        lo_x, hi_x = np.float32(u[g] - r), np.float32(u[g] + r)
+        lo_y, hi_y = np.float32(v[g] - r), np.float32(v[g] + r)
+        tiles_x = [tx for tx in range(TX) if 16 * tx <= hi_x and 16 * tx + 16 > lo_x]
+        tiles_y = [ty for ty in range(TY) if 16 * ty <= hi_y and 16 * ty + 16 > lo_y]
+        x0, x1, y0, y1 = p["rect"][:, g]
+        assert list(range(x0, x1)) == tiles_x and list(range(y0, y1)) == tiles_y, g
+        assert p["tiles"][g] == len(tiles_x) * len(tiles_y)
+        hit += 1
+    # Gaussians whose square misses the image entirely are culled
+    for g in np.nonzero(p["radius"] == 0)[0]:
+        pass
+    assert hit > 2000
+
+
+# ------------------------------------------------------------- binning ---
+def test_binning_matches_brute_force_lists():
+    sc = scenes.config(1, n_override=300)
+    cam = sc.cameras[0]
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 0, sc.sh, cam)
+    b = oracle.bin_sort(p, cam)
+    assert b["K"] == int(p["tiles"].sum())
+    keys = b["keys"]
+    assert np.all(keys[1:] >= keys[:-1])
+    TX, TY = cam.tiles_x, cam.tiles_y
+    z32 = p["z"].astype(np.float32)
+    starts = b["ranges"][:, 0]
+    ends = b["ranges"][:, 1]
+    covered = 0
+    for t in range(TX * TY):
+        tx, ty = t % TX, t // TX
+        members = [g for g in range(sc.n)
+                   if p["rect"][0, g] <= tx < p["rect"][1, g] and p["rect"][2, g] <= ty < p["rect"][3, g]]
+        members.sort(key=lambda g: (z32[g], g))
+        got = list(b["vals"][starts[t]:ends[t]])
+        assert got == members
+        covered += len(members)
+        if members:
+            assert np.all(keys[starts[t]:ends[t]] >> np.uint64(32) == t)
+    assert covered == b["K"]
+
+
+def test_binning_equal_depths_keep_index_order():
+    """Copies of one Gaussian at one depth: every tile lists them by index."""
+    n = 40
+    rng = np.random.default_rng(9)
+    means = np.tile([[0.1], [-0.05], [3.0]], (1, n))
+    means[:, ::5] = [[0.3], [0.2], [2.5]]        # a second depth group
+    perm = rng.permutation(n)
+    means = means[:, perm]
+    cam = _cam(width=96, height=64, f=64.0)
+    p = oracle.project(means.astype(np.float32), np.full((3, n), 0.3, np.float32),
+                       np.tile([[1.0], [0], [0], [0]], (1, n)).astype(np.float32),
+                       np.full(n, 0.5, np.float32), 0, np.zeros((1, 3, n), np.float32), cam)
+    b = oracle.bin_sort(p, cam)
+    z32 = p["z"].astype(np.float32)
+    for t in range(cam.n_tiles):
+        lst = list(b["vals"][b["ranges"][t, 0]:b["ranges"][t, 1]])
+        assert lst == sorted(lst, key=lambda g: (z32[g], g))
+        front = [g for g in lst if z32[g] == z32.min()]
+        assert front == sorted(front) and lst[:len(front)] == front
+
+
+# ---------------------------------------------------------- compositing ---
+def _records(u, v, conic, opac, rgb):
+    n = len(u)
+    return dict(u=np.asarray(u, float), v=np.asarray(v, float),
+                conic=np.asarray(conic, float).reshape(3, n), opacity=np.asarray(opac, float),
+                rgb=np.asarray(rgb, float).reshape(3, n))
+
+
+def test_single_isotropic_gaussian_analytic_image():
+    # on the optical axis (x = y = 0) an isotropic Gaussian projects to an
+    # isotropic 2D Gaussian; the principal point is moved off the tile grid
+    cam = scenes.Camera(64, 48, 80.0, 80.0, 27.3, 19.1,
+                        np.concatenate([np.eye(3), np.zeros((3, 1))], axis=1).astype(np.float32))
+    z, s, o = 3.0, 0.1, 0.7
+    means, scales, quats, opac, sh = _params([[0.0], [0.0], [z]], s, opac=[o],
+                                             rgb_dc=[[0.4], [0.1], [-0.2]])
+    p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+    b = oracle.bin_sort(p, cam)
+    out = oracle.render(p, b, cam)
+    var = (80.0 * s / z) ** 2 + 0.3
+    r = math.ceil(3 * math.sqrt(var))
+    u0, v0 = p["u"][0], p["v"][0]
+    rgb = 0.5 + 0.5 / math.sqrt(PI) * np.array([0.4, 0.1, -0.2])
+    ii, jj = np.meshgrid(np.arange(64) + 0.5, np.arange(48) + 0.5)
+    alpha = np.minimum(0.99, o * np.exp(-0.5 * ((ii - u0) ** 2 + (jj - v0) ** 2) / var))
+    tx, ty = (ii // 16).astype(int), (jj // 16).astype(int)
+    inside = ((tx >= math.floor((u0 - r) / 16)) & (tx <= math.floor((u0 + r) / 16)) &
+              (ty >= math.floor((v0 - r) / 16)) & (ty <= math.floor((v0 + r) / 16)))
+    alpha = np.where((alpha >= 1 / 255) & inside, alpha, 0.0)
+    np.testing.assert_allclose(out["image"], rgb[:, None, None] * alpha[None], atol=1e-14)
+    np.testing.assert_allclose(out["final_T"], 1 - alpha, atol=1e-14)
+    assert np.array_equal(out["n_contrib"], (alpha > 0).astype(np.int32))
+
+
+def _occluder_scene(n_occ, n_content=30, seed=5):
+    """n_occ huge Gaussians of opacity 1 and colour 0 (DC = -0.6/C0, clamped)
+    in front of random coloured content."""
+    rng = np.random.default_rng(seed)
+    c0 = 0.5 / math.sqrt(PI)
+    occ_m = np.stack([np.zeros(n_occ), np.zeros(n_occ), 1.0 + 0.1 * np.arange(n_occ)])
+    con_m = np.stack([rng.uniform(-1, 1, n_content), rng.uniform(-1, 1, n_content),
+                      rng.uniform(3, 5, n_content)])
+    means = np.concatenate([occ_m, con_m], axis=1)
+    n = means.shape[1]
+    scales = np.concatenate([np.full((3, n_occ), 1e3), np.exp(rng.uniform(-3, -1.5, (3, n_content)))], axis=1)
+    quats = np.concatenate([np.tile([[1.0], [0], [0], [0]], (1, n_occ)),
+                            rng.standard_normal((4, n_content))], axis=1)
+    opac = np.concatenate([np.ones(n_occ), rng.uniform(0.3, 0.95, n_content)])
+    sh = np.zeros((1, 3, n))
+    sh[0, :, :n_occ] = -0.6 / c0
+    sh[0, :, n_occ:] = rng.uniform(0, 1, (3, n_content))
+    return means, scales, quats, opac, sh
+
+
+def test_exact_occlusion_by_opaque_layers():
+    cam = _cam(width=64, height=64, f=64.0)
+    # three layers: T = 0.01^3 < 1e-4 in any precision -> exactly black
+    means, scales, quats, opac, sh = _occluder_scene(3)
+    for prec in ("f32", "f64"):
+        p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision=prec)
+        out = oracle.render(p, oracle.bin_sort(p, cam), cam)
+        assert np.all(out["image"] == 0.0)
+        assert np.all(out["n_contrib"] == 3)
+    # two layers: (1 - 0.99)^2 = 1.0000000000000018e-4 in fp64 does not stop,
+    # so content behind shows at ~1e-4; the stop decision is a flagged event
+    means, scales, quats, opac, sh = _occluder_scene(2)
+    p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+    b = oracle.bin_sort(p, cam)
+    out = oracle.render(p, b, cam)
+    assert np.all(out["image"] <= 1.0001e-4 * 1.0)
+    assert np.all(out["events"] >= 1)
+    # taking the stop the other way gives exact black
+    rgb, T, nn, ev = oracle.render_pixel(p, b, cam, 10, 10, flips=1)
+    assert np.all(rgb == 0.0) and nn == 2
+    # one layer: everything behind is attenuated by exactly (1 - 0.99)
+    means, scales, quats, opac, sh = _occluder_scene(1)
+    p1 = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+    out1 = oracle.render(p1, oracle.bin_sort(p1, cam), cam)
+    p0 = oracle.project(means[:, 1:], scales[:, 1:], quats[:, 1:], opac[1:], 0, sh[:, :, 1:], cam,
+                        precision="f64")
+    out0 = oracle.render(p0, oracle.bin_sort(p0, cam), cam)
+    np.testing.assert_allclose(out1["image"], (1 - 0.99) * out0["image"], rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(out1["final_T"], (1 - 0.99) * out0["final_T"], rtol=1e-12)
+
+
+def test_partition_of_unity_and_background():
+    sc = scenes.config(1, n_override=400)
+    cam = sc.cameras[0]
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 0, sc.sh, cam)
+    b = oracle.bin_sort(p, cam)
+    p1 = dict(p)
+    p1["rgb"] = np.ones_like(p["rgb"])
+    out = oracle.render(p1, b, cam)
+    np.testing.assert_allclose(out["image"], np.broadcast_to(1 - out["final_T"], out["image"].shape),
+                               atol=1e-13)
+    p0 = dict(p)
+    p0["rgb"] = np.zeros_like(p["rgb"])
+    bg = (0.25, 0.5, 1.0)
+    out0 = oracle.render(p0, b, cam, bg=bg)
+    np.testing.assert_allclose(out0["image"], np.asarray(bg)[:, None, None] * out0["final_T"][None],
+                               atol=1e-15)
+
+
+def test_order_invariance_under_index_permutation():
+    sc = scenes.config(1, n_override=500)
+    cam = sc.cameras[0]
+    perm = np.random.default_rng(3).permutation(sc.n)
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 0, sc.sh, cam)
+    out = oracle.render(p, oracle.bin_sort(p, cam), cam)
+    pp = oracle.project(sc.means[:, perm], sc.scales[:, perm], sc.quats[:, perm], sc.opacities[perm], 0,
+                        sc.sh[:, :, perm], cam)
+    outp = oracle.render(pp, oracle.bin_sort(pp, cam), cam)
+    assert len(np.unique(p["z"][p["radius"] > 0])) == (p["radius"] > 0).sum()
+    np.testing.assert_array_equal(out["image"], outp["image"])
+    np.testing.assert_array_equal(out["final_T"], outp["final_T"])
+
+
+def test_tiled_render_equals_untiled_brute_force():
+    """Per pixel, loop over ALL Gaussians sorted by (depth, index), keeping
+    those whose tile rect holds the pixel's tile, compositing with the same
+    rules; no binning, no ranges."""
+    sc = scenes.config(1, n_override=150)
+    cam = scenes.Camera(48, 40, 48.0, 48.0, 24.0, 20.0, sc.cameras[0].viewmat)
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 0, sc.sh, cam)
+    out = oracle.render(p, oracle.bin_sort(p, cam), cam)
+    order = sorted(np.nonzero(p["radius"] > 0)[0], key=lambda g: (np.float32(p["z"][g]), g))
+    for j in range(cam.height):
+        for i in range(cam.width):
+            tx, ty = i // 16, j // 16
+            T, C, n_c, pos = 1.0, np.zeros(3), 0, 0
+            for g in order:
+                if not (p["rect"][0, g] <= tx < p["rect"][1, g] and p["rect"][2, g] <= ty < p["rect"][3, g]):
+                    continue
+                pos += 1
+                if T < 1e-4:
+                    break
+                dx, dy = p["u"][g] - (i + 0.5), p["v"][g] - (j + 0.5)
+                a, b, c = p["conic"][:, g]
+                al = min(0.99, p["opacity"][g] * math.exp(-0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy))
+                if al < 1 / 255:
+                    continue
+                C += al * T * p["rgb"][:, g]
+                T *= 1 - al
+                n_c = pos
+            np.testing.assert_allclose(out["image"][:, j, i], C, atol=1e-14)
+            assert abs(out["final_T"][j, i] - T) < 1e-14 and out["n_contrib"][j, i] == n_c
+
+
+def test_alpha_threshold_skips_below_one_over_255():
+    # the mean sits exactly on the centre of pixel (15, 15), where alpha = o
+    cam = scenes.Camera(32, 32, 32.0, 32.0, 15.5, 15.5,
+                        np.concatenate([np.eye(3), np.zeros((3, 1))], axis=1).astype(np.float32))
+    for o, expect_n in [(0.999 / 255, 0), (1.001 / 255, 1)]:
+        means, scales, quats, opac, sh = _params([[0.0], [0.0], [2.0]], 0.2, opac=[o], rgb_dc=[[1.0]] * 3)
+        p = oracle.project(means, scales, quats, opac, 0, sh, cam, precision="f64")
+        out = oracle.render(p, oracle.bin_sort(p, cam), cam)
+        assert out["n_contrib"][15, 15] == expect_n
+        assert out["image"][0, 15, 15] == (0.0 if expect_n == 0 else o * (0.5 + 0.5 / math.sqrt(PI)))
+        # every other pixel has a smaller alpha, below the threshold
+        assert out["n_contrib"].sum() == expect_n
+
+
+# ------------------------------------------------------------ gradients ---
+def _fd_scene(seed=7, n=6, W=32, H=32, degree=3):
+    rng = np.random.default_rng(seed)
+    means = np.stack([rng.uniform(-0.5, 0.5, n), rng.uniform(-0.5, 0.5, n), rng.uniform(2.5, 4.0, n)])
+    log_s = rng.uniform(-2.6, -1.6, (3, n))
+    quats = rng.standard_normal((4, n))
+    logits = rng.normal(0.0, 1.0, n)
+    k = (degree + 1) ** 2
+    sh = np.concatenate([rng.uniform(0.2, 0.8, (1, 3, n)), 0.2 * rng.standard_normal((k - 1, 3, n))])
+    vm = scenes.look_at(np.array([0.4, -0.3, -0.5]), target=(0.0, 0.0, 3.0))
+    cam = _cam(width=W, height=H, f=40.0, viewmat=vm)
+    G = rng.standard_normal((3, H, W))
+    return means, log_s, quats, logits, sh, cam, G
+
+
+def _loss_and_structure(means, log_s, quats, logits, sh, cam, G, degree=3):
+    s = np.exp(log_s)
+    o = 1.0 / (1.0 + np.exp(-logits))
+    p = oracle.project(means, s, quats, o, degree, sh, cam, precision="f64")
+    b = oracle.bin_sort(p, cam)
+    out = oracle.render(p, b, cam)
+    struct = (tuple(b["vals"]), tuple(b["ranges"].reshape(-1)), out["n_contrib"].tobytes(),
+              p["clamped"].tobytes())
+    return float((G * out["image"]).sum()), struct, p, b, out
+
+
+def test_render_bwd_matches_finite_differences_of_records():
+    means, log_s, quats, logits, sh, cam, G = _fd_scene()
+    _, _, p, b, out = _loss_and_structure(means, log_s, quats, logits, sh, cam, G)
+    g2 = oracle.render_bwd(p, b, cam, G)
+    h = 1e-6
+    keys = [("u", None), ("v", None), ("conic", 0), ("conic", 1), ("conic", 2), ("opacity", None),
+            ("rgb", 0), ("rgb", 1), ("rgb", 2)]
+    n = means.shape[1]
+    checked = 0
+    for q, (name, row) in enumerate(keys):
+        for g in range(n):
+            if p["radius"][g] == 0:
+                continue
+            vals = []
+            for sgn in (1, -1):
+                pp = {k: v.copy() for k, v in p.items()}
+                if row is None:
+                    pp[name][g] += sgn * h
+                else:
+                    pp[name][row, g] += sgn * h
+                o2 = oracle.render(pp, b, cam)
+                assert np.array_equal(o2["n_contrib"], out["n_contrib"])
+                vals.append((G * o2["image"]).sum())
+            num = (vals[0] - vals[1]) / (2 * h)
+            assert abs(num - g2[q, g]) <= 1e-6 * max(1.0, abs(num)), (name, row, g, num, g2[q, g])
+            checked += 1
+    assert checked >= 9 * 4
+
+
+@pytest.mark.parametrize("seed", [7, 8])
+def test_full_backward_matches_finite_differences(seed):
+    means, log_s, quats, logits, sh, cam, G = _fd_scene(seed=seed)
+    L0, s0, p, b, out = _loss_and_structure(means, log_s, quats, logits, sh, cam, G)
+    assert (p["radius"] > 0).sum() >= 4
+    g2 = oracle.render_bwd(p, b, cam, G)
+    grads = oracle.project_bwd(means, np.exp(log_s), quats, 1 / (1 + np.exp(-logits)), 3, sh, cam, p, g2)
+    params = dict(means=means, log_scales=log_s, quats=quats, opacity_logits=logits, sh=sh)
+    h = 1e-6
+    rng = np.random.default_rng(seed)
+    for name, arr in params.items():
+        flat_idx = list(np.ndindex(arr.shape))
+        if len(flat_idx) > 60:
+            flat_idx = [flat_idx[i] for i in rng.choice(len(flat_idx), 60, replace=False)]
+        for idx in flat_idx:
+            vals = []
+            for sgn in (1, -1):
+                pr = {k: v.copy() for k, v in params.items()}
+                pr[name][idx] += sgn * h * max(1.0, abs(arr[idx]))
+                L, st, *_ = _loss_and_structure(pr["means"], pr["log_scales"], pr["quats"],
+                                                pr["opacity_logits"], pr["sh"], cam, G)
+                assert st == s0, "a discrete decision moved under the finite-difference step"
+                vals.append(L)
+            num = (vals[0] - vals[1]) / (2 * h * max(1.0, abs(arr[idx])))
+            ana = grads[name][idx]
+            assert abs(num - ana) <= 1e-6 * max(1.0, abs(num)) + 1e-7, (name, idx, num, ana)
+
+
+# -------------------------------------------------------- active set ---
+def test_topk_mask_against_lexsort_and_ties():
+    rng = np.random.default_rng(41)
+    s = rng.exponential(1.0, 5000).astype(np.float32)
+    s[::7] = s[3]             # many ties
+    above = int((s > s[3]).sum())
+    ties = int((s == s[3]).sum())
+    assert ties > 100
+    # cut-offs above, inside (several places) and below the tie group
+    for k in (0, 1, 1500, above, above + 1, above + ties // 3, above + ties - 1, 4999, 5000):
+        m = oracle.topk_mask(s, k)
+        assert m.sum() == k
+        order = np.lexsort((np.arange(s.size), -s.astype(np.float64)))
+        expect = np.zeros(s.size, np.uint8)
+        expect[order[:k]] = 1
+        assert np.array_equal(m, expect)
+
+
+def test_lod_gate_brute_force():
+    rng = np.random.default_rng(42)
+    n = 20000
+    vm = scenes.look_at(np.array([0.0, 0.0, -25.0]))
+    cam = _cam(width=640, height=480, f=700.0, viewmat=vm, lod=0.5)
+    means = rng.uniform(-30, 30, (3, n)).astype(np.float32)
+    s = np.exp(rng.normal(-5.5, 1.0, (3, n))).astype(np.float32)
+    q = rng.standard_normal((4, n)).astype(np.float32)
+    o = np.full(n, 0.5, np.float32)
+    p_on = oracle.project(means, s, q, o, 0, np.zeros((1, 3, n), np.float32), cam)
+    cam_off = _cam(width=640, height=480, f=700.0, viewmat=vm, lod=0.0)
+    p_off = oracle.project(means, s, q, o, 0, np.zeros((1, 3, n), np.float32), cam_off)
+    eye = np.array([0.0, 0.0, -25.0])
+    dist = np.linalg.norm(means.astype(np.float64) - eye[:, None], axis=0)
+    est = 3 * 700.0 * s.max(axis=0).astype(np.float64) / dist
+    keep = est >= 0.5
+    clear = np.abs(est - 0.5) > 1e-5
+    vis_off = p_off["radius"] > 0
+    assert np.array_equal((p_on["radius"] > 0)[clear], (vis_off & keep)[clear])
+    assert 0.2 < keep[vis_off].mean() < 0.95
