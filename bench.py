@@ -1,0 +1,231 @@
+"""Benchmark of the tiled Gaussian-splatting rasterizer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload scene_1m|...]
+
+Workload (default): 1M Gaussians, SH degree 3, fp32, the scene-like mixture
+(64 anisotropic clusters + a background shell at radius 50), 1920x1080,
+fx = fy = 1400, 8 orbit views; synthetic, seeded, resident in HBM before the
+timed region.  One step = the whole hot path for all 8 views: project,
+bin + sort, blend forward, then blend backward and the projection's chain
+rule against an upstream dL/dimage ~ N(0, 1e-2).
+
+Prints ONE JSON line: value = forward ms/frame (project + bin/sort + blend),
+plus fwd+bwd ms/frame, per-call averages, the roofline of the dominant
+kernel (the forward blend, one kernel per gs_render_fwd call, timed with
+events on its stream), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="scene_1m", choices=["scene_1m", "box_100k", "tiny_1k"])
+    ap.add_argument("--views", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    return ap.parse_args()
+
+
+# Algorithmic work of the forward blend per evaluated (pixel, Gaussian) pair,
+# in fp32 VALU lane-op slots: 2 sub (offset), 5 mul/fma (quadratic form),
+# v_exp_f32 (quarter rate: 4 slots), 1 mul (o * G), 1 min (cap), 1 compare
+# (skip), 1 mul (alpha T), 3 fma (colour), 1 sub (T), 1 select (n_contrib),
+# 1 compare (stop) = 21; taken as 20 (the select of the stop is fused).
+BLEND_FWD_SLOTS_PER_PAIR = 20
+# 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: one non-packed fp32 VALU op per lane
+# per clock (packed-fp32 instructions are not used by this library).
+VALU_PEAK_T = 256 * 64 * 2.4e9 / 1e12
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              f"see the sharding design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gaussian_splatting_tile_amd import binding as B
+    from gaussian_splatting_tile_amd import scenes
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    B.lib()                         # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    if args.workload == "scene_1m":
+        sc = scenes.scene_like(seed=3, n=1_000_000, upstream=True, name="scene_1m_sh3_1080p")
+    elif args.workload == "box_100k":
+        sc = scenes.box()
+        sc.upstream_seed = 22
+    else:
+        sc = scenes.tiny()
+        sc.upstream_seed = 11
+    views = min(args.views, len(sc.cameras))
+    print(f"# scene {sc.name}: N={sc.n} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    g = dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities),
+             sh=f(sc.sh))
+    gs = B.gaussians_struct(g, sc.sh_degree)
+    stream = torch.cuda.current_stream()
+
+    # per-view buffers with the exact key capacity (K is deterministic)
+    bufs, Ks = [], []
+    for v in range(views):
+        cam = sc.cameras[v]
+        probe = B.ViewBuffers(sc.n, cam, 16 * sc.n)
+        probe.forward(gs)
+        torch.cuda.synchronize()
+        k = int(probe.k_total.item())
+        del probe
+        b = B.ViewBuffers(sc.n, cam, k)
+        b.dL = f(sc.upstream(v))
+        b.bwd_ws = torch.empty(B.render_bwd_workspace_bytes(sc.n), dtype=torch.uint8, device=dev)
+        bufs.append(b)
+        Ks.append(k)
+    K_sh = (sc.sh_degree + 1) ** 2
+    grads = dict(means=torch.zeros((3, sc.n), device=dev), log_scales=torch.zeros((3, sc.n), device=dev),
+                 quats=torch.zeros((4, sc.n), device=dev), opacity_logits=torch.zeros(sc.n, device=dev),
+                 sh=torch.zeros((K_sh, 3, sc.n), device=dev))
+    bg = (0.0, 0.0, 0.0)
+    do_bwd = not args.no_backward
+
+    names = ("project", "bin_sort", "render_fwd", "render_bwd")
+    ev = {k: [] for k in names}
+    step_ev = []
+
+    def step(record: bool):
+        for gr in grads.values():
+            gr.zero_()
+        e_fwd0 = torch.cuda.Event(enable_timing=True)
+        e_fwd1 = torch.cuda.Event(enable_timing=True)
+        e_end = torch.cuda.Event(enable_timing=True)
+        e_fwd0.record(stream)
+
+        def timed(name, fn):
+            if not record:
+                fn()
+                return
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[name].append((a, b))
+
+        for b in bufs:
+            timed("project", lambda: B.project(gs, b.camc, b.splats, stream))
+            timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
+                                                 None, b.k_total, b.ws, stream))
+            timed("render_fwd", lambda: B.render_fwd(b.splats, b.vals, b.ranges, b.camc, bg, b.image,
+                                                     b.final_T, b.n_contrib, stream))
+        e_fwd1.record(stream)
+        if do_bwd:
+            for b in bufs:
+                timed("render_bwd", lambda: B.render_bwd(gs, b.camc, b.splats, b.vals, b.ranges, bg,
+                                                         b.final_T, b.n_contrib, b.dL, grads, b.bwd_ws,
+                                                         stream))
+        e_end.record(stream)
+        if record:
+            step_ev.append((e_fwd0, e_fwd1, e_end))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"# warmup done; K per view {Ks}", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in step_ev) / (args.steps * views)
+    tot_ms = sum(a.elapsed_time(c) for a, _, c in step_ev) / (args.steps * views)
+    per_call = {k: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None) for k, v in ev.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    # algorithmic work of the blend: evaluated pairs per view, from the outputs
+    # (a pixel that stopped examined n_contrib entries, otherwise its whole list)
+    p_eval = []
+    for b in bufs:
+        rng = b.ranges.long()
+        L = (rng[:, 1] - rng[:, 0]).reshape(b.cam.tiles_y, b.cam.tiles_x)
+        Lpix = L.repeat_interleave(16, 0).repeat_interleave(16, 1)[: b.cam.height, : b.cam.width]
+        stopped = b.final_T < 1e-4
+        pe = torch.where(stopped, b.n_contrib.long(), Lpix).sum().item()
+        p_eval.append(int(pe))
+    pe_mean = sum(p_eval) / len(p_eval)
+    t_blend_s = per_call["render_fwd"] / 1e3
+    achieved = pe_mean * BLEND_FWD_SLOTS_PER_PAIR / t_blend_s / 1e12
+
+    res = {
+        "metric": "ms/frame fwd (+fwd+bwd) at 1M Gaussians SH3 1920x1080; % VALU / HBM peak",
+        "value": round(fwd_ms, 4),
+        "unit": "ms/frame",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded scene generator; no dataset)",
+        "config": {"workload": sc.name, "gaussians": sc.n, "sh_degree": sc.sh_degree,
+                   "width": sc.cameras[0].width, "height": sc.cameras[0].height, "views_per_step": views,
+                   "step": "all views: project + bin/sort + blend fwd" + (", then blend bwd + project bwd"
+                                                                          if do_bwd else "")},
+        "fwd_ms_per_frame": round(fwd_ms, 4),
+        "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,
+        "per_call_ms": {k: (round(v, 4) if v is not None else None) for k, v in per_call.items()},
+        "K_per_view": Ks,
+        "P_eval_per_view": p_eval,
+        "roofline": {"kernel": "render_fwd_kernel (forward blend)", "bound": "alu",
+                     "achieved": round(achieved, 3), "peak": round(VALU_PEAK_T, 2), "unit": "TFLOP/s",
+                     "frac": round(achieved / VALU_PEAK_T, 4), "traffic": None,
+                     "work_unit": f"{BLEND_FWD_SLOTS_PER_PAIR} fp32 VALU lane-op slots per evaluated "
+                                  f"(pixel, Gaussian) pair; peak = 256 CU x 64 lanes x 2.4 GHz"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(sc)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(sc):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    project + bin + composite of one full view (forward), repeated while under
+    ~15 s; reported in ms/frame."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    frames = 0
+    while True:
+        oracle.forward(sc, view=frames % len(sc.cameras))
+        frames += 1
+        if time.perf_counter() - t0 > 10.0 or frames >= 4:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e3 / frames, 1), "unit": "ms/frame", "cores": threads, "kind": "oracle",
+            "sample": f"{frames} full forward view(s) of {sc.name} (project fp32-contract, brute-force "
+                      f"binning + qsort, fp64 compositing), OpenMP"}
+
+
+if __name__ == "__main__":
+    main()

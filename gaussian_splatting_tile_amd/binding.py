@@ -1,0 +1,214 @@
+"""ctypes binding of libgs_hip.so (C ABI in include/gs.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+stream, every step of the rasterizer runs in the HIP library.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import build as _build
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE, GS_ERR_HIP = range(5)
+GS_SH_F32, GS_SH_F16 = 0, 1
+SPLAT_FLOATS = 12          # gs_splat is 48 bytes
+
+
+class GsCamera(C.Structure):
+    _fields_ = [("width", C.c_int32), ("height", C.c_int32), ("fx", C.c_float), ("fy", C.c_float),
+                ("cx", C.c_float), ("cy", C.c_float), ("viewmat", C.c_float * 12),
+                ("znear", C.c_float), ("guard", C.c_float), ("lod_min_radius_px", C.c_float)]
+
+
+class GsGaussians(C.Structure):
+    _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("sh_dtype", C.c_int32),
+                ("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p),
+                ("opacities", C.c_void_p), ("sh", C.c_void_p), ("active", C.c_void_p)]
+
+
+class GsGrads(C.Structure):
+    _fields_ = [("means", C.c_void_p), ("log_scales", C.c_void_p), ("quats", C.c_void_p),
+                ("opacity_logits", C.c_void_p), ("sh", C.c_void_p)]
+
+
+class GsError(RuntimeError):
+    pass
+
+
+_lib = None
+SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_render_fwd",
+           "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_active_mask_workspace_bytes",
+           "gs_active_mask", "gs_status_string", "gs_version")
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """Load the HIP library (built in tree by build.py); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise GsError(f"HIP library not built: {path} (run python -m gaussian_splatting_tile_amd.build)")
+    L = C.CDLL(path)
+    for name in SYMBOLS:
+        getattr(L, name)
+    vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
+    L.gs_project.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp]
+    L.gs_bin_sort_workspace_bytes.argtypes = [i64, i64, C.c_int32]
+    L.gs_bin_sort_workspace_bytes.restype = sz
+    L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, sz, vp]
+    L.gs_render_fwd.argtypes = [vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
+    L.gs_render_bwd_workspace_bytes.argtypes = [i64]
+    L.gs_render_bwd_workspace_bytes.restype = sz
+    L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, vp,
+                                vp, C.POINTER(GsGrads), vp, sz, vp]
+    L.gs_active_mask_workspace_bytes.argtypes = [i64]
+    L.gs_active_mask_workspace_bytes.restype = sz
+    L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
+    L.gs_status_string.restype = C.c_char_p
+    L.gs_status_string.argtypes = [C.c_int]
+    L.gs_version.restype = C.c_int32
+    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_bwd", "gs_active_mask"):
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != GS_OK:
+        msg = lib().gs_status_string(status).decode()
+        raise GsError(f"{what} failed: {msg} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def camera_struct(cam) -> GsCamera:
+    """From an object with width, height, fx, fy, cx, cy, viewmat[3][4],
+    znear, guard, lod_min_radius_px (see scenes.Camera)."""
+    c = GsCamera()
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    vm = [float(x) for x in __import__("numpy").asarray(cam.viewmat, dtype="float32").reshape(-1)]
+    for i in range(12):
+        c.viewmat[i] = vm[i]
+    c.znear, c.guard = float(cam.znear), float(cam.guard)
+    c.lod_min_radius_px = float(getattr(cam, "lod_min_radius_px", 0.0))
+    return c
+
+
+def gaussians_struct(g: Dict[str, torch.Tensor], sh_degree: int, active: Optional[torch.Tensor] = None
+                     ) -> GsGaussians:
+    s = GsGaussians()
+    s.n = int(g["means"].shape[1])
+    s.sh_degree = int(sh_degree)
+    s.sh_dtype = GS_SH_F16 if g["sh"].dtype == torch.float16 else GS_SH_F32
+    for k in ("means", "scales", "quats", "opacities"):
+        t = g[k]
+        assert t.is_cuda and t.dtype == torch.float32 and t.is_contiguous(), k
+    assert g["sh"].is_cuda and g["sh"].is_contiguous()
+    s.means, s.scales, s.quats = g["means"].data_ptr(), g["scales"].data_ptr(), g["quats"].data_ptr()
+    s.opacities, s.sh = g["opacities"].data_ptr(), g["sh"].data_ptr()
+    if active is not None:
+        assert active.is_cuda and active.dtype == torch.uint8 and active.is_contiguous()
+        s.active = active.data_ptr()
+    return s
+
+
+# ---- the four calls ---------------------------------------------------------
+def project(gs: GsGaussians, cam: GsCamera, splats: torch.Tensor, stream=None):
+    _check(lib().gs_project(C.byref(gs), C.byref(cam), _ptr(splats), _stream(stream)), "gs_project")
+
+
+def bin_sort_workspace_bytes(n: int, k_capacity: int, n_tiles: int) -> int:
+    return int(lib().gs_bin_sort_workspace_bytes(n, k_capacity, n_tiles))
+
+
+def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, keys, k_total, workspace,
+             stream=None):
+    _check(lib().gs_bin_sort(_ptr(splats), int(n), C.byref(cam), int(k_capacity), _ptr(vals),
+                             _ptr(tile_ranges), _ptr(keys), _ptr(k_total), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream(stream)), "gs_bin_sort")
+
+
+def render_fwd(splats, vals, tile_ranges, cam: GsCamera, bg: Sequence[float], image, final_T,
+               n_contrib, stream=None):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    _check(lib().gs_render_fwd(_ptr(splats), _ptr(vals), _ptr(tile_ranges), C.byref(cam),
+                               C.cast(bgv, C.c_void_p), _ptr(image), _ptr(final_T), _ptr(n_contrib),
+                               _stream(stream)), "gs_render_fwd")
+
+
+def render_bwd_workspace_bytes(n: int) -> int:
+    return int(lib().gs_render_bwd_workspace_bytes(n))
+
+
+def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, bg, final_T, n_contrib,
+               dL_dimage, grads: Dict[str, torch.Tensor], workspace, stream=None):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
+                 _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
+    _check(lib().gs_render_bwd(C.byref(gs), C.byref(cam), _ptr(splats), _ptr(vals), _ptr(tile_ranges),
+                               C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
+                               C.byref(gr), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gs_render_bwd")
+
+
+def active_mask_workspace_bytes(n: int) -> int:
+    return int(lib().gs_active_mask_workspace_bytes(n))
+
+
+def active_mask(scores, n, keep, mask, workspace, stream=None):
+    _check(lib().gs_active_mask(_ptr(scores), int(n), int(keep), _ptr(mask), _ptr(workspace),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "gs_active_mask")
+
+
+# ---- buffers for one view ---------------------------------------------------
+class ViewBuffers:
+    """Device buffers for rendering one camera with a fixed key capacity."""
+
+    def __init__(self, n: int, cam, k_capacity: int, device="cuda", with_keys: bool = False):
+        self.n = n
+        self.cam = cam
+        self.camc = camera_struct(cam)
+        self.n_tiles = ((cam.width + 15) // 16) * ((cam.height + 15) // 16)
+        self.k_capacity = int(k_capacity)
+        kc = max(self.k_capacity, 1)
+        self.splats = torch.empty((max(n, 1), SPLAT_FLOATS), dtype=torch.float32, device=device)
+        self.vals = torch.empty(kc, dtype=torch.int32, device=device)
+        self.keys = torch.empty(kc, dtype=torch.int64, device=device) if with_keys else None
+        self.ranges = torch.empty((self.n_tiles, 2), dtype=torch.int32, device=device)
+        self.k_total = torch.zeros(1, dtype=torch.int64, device=device)
+        wsb = bin_sort_workspace_bytes(n, self.k_capacity, self.n_tiles)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+        H, W = cam.height, cam.width
+        self.image = torch.empty((3, H, W), dtype=torch.float32, device=device)
+        self.final_T = torch.empty((H, W), dtype=torch.float32, device=device)
+        self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=device)
+
+    def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
+        project(gs, self.camc, self.splats, stream)
+        bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.keys,
+                 self.k_total, self.ws, stream)
+        render_fwd(self.splats, self.vals, self.ranges, self.camc, bg, self.image, self.final_T,
+                   self.n_contrib, stream)

@@ -1,0 +1,154 @@
+// C ABI of the rasterizer (declared in include/gs.h): argument checks,
+// workspace sizing and the launch sequence of each call.  No allocation, no
+// synchronisation, no host round trip.
+#include <math.h>
+
+#include "gs_internal.h"
+
+using namespace gsi;
+
+namespace {
+
+constexpr int32_t kVersion = 1;
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
+
+bool camera_ok(const gs_camera *c)
+{
+    if (!c) return false;
+    if (c->width < 1 || c->height < 1 || c->width > 32768 || c->height > 32768) return false;
+    if (!finite_pos(c->fx) || !finite_pos(c->fy) || !isfinite(c->cx) || !isfinite(c->cy)) return false;
+    for (int i = 0; i < 12; i++)
+        if (!isfinite(c->viewmat[i])) return false;
+    if (!isfinite(c->znear) || !finite_pos(c->guard)) return false;
+    if (!isfinite(c->lod_min_radius_px) || c->lod_min_radius_px < 0.0f) return false;
+    return true;
+}
+
+gs_status gaussians_ok(const gs_gaussians *g)
+{
+    if (!g || g->n < 0 || g->n > INT32_MAX) return GS_ERR_INVALID_ARG;
+    if (g->sh_degree < 0 || g->sh_degree > 3) return GS_ERR_UNSUPPORTED;
+    if (g->sh_dtype != GS_SH_F32 && g->sh_dtype != GS_SH_F16) return GS_ERR_UNSUPPORTED;
+    if (g->n > 0 && (!g->means || !g->scales || !g->quats || !g->opacities || !g->sh))
+        return GS_ERR_INVALID_ARG;
+    return GS_OK;
+}
+
+gs_status from_hip(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t gs_version(void) { return kVersion; }
+
+const char *gs_status_string(gs_status s)
+{
+    switch (s) {
+    case GS_OK: return "ok";
+    case GS_ERR_INVALID_ARG: return "invalid argument";
+    case GS_ERR_UNSUPPORTED: return "unsupported argument value";
+    case GS_ERR_WORKSPACE: return "workspace too small";
+    case GS_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+gs_status gs_project(const gs_gaussians *gaussians, const gs_camera *camera, gs_splat *splats,
+                     void *stream)
+{
+    gs_status st = gaussians_ok(gaussians);
+    if (st != GS_OK) return st;
+    if (!camera_ok(camera)) return GS_ERR_INVALID_ARG;
+    if (gaussians->n > 0 && !splats) return GS_ERR_INVALID_ARG;
+    return from_hip(launch_project(*gaussians, make_cam(*camera), (Splat *)splats, (hipStream_t)stream));
+}
+
+size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles)
+{
+    if (n < 0 || k_capacity < 0) return 0;
+    return bin_sort_workspace(n, k_capacity, n_tiles);
+}
+
+gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
+                      uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys, uint64_t *k_total,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
+        return GS_ERR_INVALID_ARG;
+    if (!camera_ok(camera) || !tile_ranges || !k_total) return GS_ERR_INVALID_ARG;
+    if (n > 0 && !splats) return GS_ERR_INVALID_ARG;
+    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
+    const Cam cam = make_cam(*camera);
+    const size_t need = bin_sort_workspace(n, k_capacity, cam.tiles_x * cam.tiles_y);
+    if (workspace_bytes < need || !workspace) return GS_ERR_WORKSPACE;
+    return from_hip(launch_bin_sort((const Splat *)splats, n, cam, k_capacity, vals, tile_ranges, keys,
+                                    k_total, workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint32_t *tile_ranges,
+                        const gs_camera *camera, const float *bg, float *image, float *final_T,
+                        uint32_t *n_contrib, void *stream)
+{
+    if (!camera_ok(camera) || !tile_ranges || !bg || !image || !final_T || !n_contrib)
+        return GS_ERR_INVALID_ARG;
+    for (int c = 0; c < 3; c++)
+        if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
+    return from_hip(launch_render_fwd((const Splat *)splats, vals, tile_ranges, make_cam(*camera), bg,
+                                      image, final_T, n_contrib, (hipStream_t)stream));
+}
+
+size_t gs_render_bwd_workspace_bytes(int64_t n)
+{
+    if (n < 0) return 0;
+    return align_up((size_t)n * 9 * sizeof(float), 256) + 256;
+}
+
+gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
+                        const uint32_t *vals, const uint32_t *tile_ranges, const float *bg,
+                        const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
+                        const gs_grads *grads, void *workspace, size_t workspace_bytes, void *stream)
+{
+    gs_status st = gaussians_ok(gaussians);
+    if (st != GS_OK) return st;
+    if (!camera_ok(camera) || !tile_ranges || !bg || !final_T || !n_contrib || !dL_dimage || !grads)
+        return GS_ERR_INVALID_ARG;
+    for (int c = 0; c < 3; c++)
+        if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
+    const int64_t n = gaussians->n;
+    if (n > 0 && (!splats || !grads->means || !grads->log_scales || !grads->quats ||
+                  !grads->opacity_logits || !grads->sh))
+        return GS_ERR_INVALID_ARG;
+    if (workspace_bytes < gs_render_bwd_workspace_bytes(n) || !workspace) return GS_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const Cam cam = make_cam(*camera);
+    float *grad2d = (float *)workspace;
+    hipError_t e = launch_fill_u32((uint32_t *)grad2d, 0u, (size_t)n * 9, s);
+    if (e != hipSuccess) return GS_ERR_HIP;
+    e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, cam, bg, final_T, n_contrib,
+                          dL_dimage, n, grad2d, s);
+    if (e != hipSuccess) return GS_ERR_HIP;
+    return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, grad2d, *grads, s));
+}
+
+size_t gs_active_mask_workspace_bytes(int64_t n)
+{
+    if (n < 0) return 0;
+    return active_mask_workspace(n);
+}
+
+gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    if (n < 0 || n > INT32_MAX || keep < 0 || keep > n) return GS_ERR_INVALID_ARG;
+    if (n > 0 && (!scores || !mask)) return GS_ERR_INVALID_ARG;
+    if (workspace_bytes < active_mask_workspace(n) || (!workspace && active_mask_workspace(n) > 0))
+        return GS_ERR_WORKSPACE;
+    hipError_t e = launch_active_mask(scores, n, keep, mask, workspace, workspace_bytes,
+                                      (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return GS_ERR_UNSUPPORTED;
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal declarations of the gfx950 rasterizer library (not installed; the
+// public interface is include/gs.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "gs.h"
+
+namespace gsi {
+
+constexpr int kTile = 16;                 // tile side in pixels
+constexpr int kTilePixels = kTile * kTile;
+constexpr int kBlock = 256;               // threads per block (4 wave64)
+
+// Tile rectangle of a splat: the half-open range of 16x16 tiles meeting the
+// square [u - r, u + r] x [v - r, v + r], clamped to the grid.  Every step is
+// exact or one correctly rounded fp32 operation, so the projection and the
+// binning kernels (and any other IEEE fp32 implementation of the same steps)
+// agree bit for bit.
+struct Rect { int x0, x1, y0, y1; };
+
+__device__ __forceinline__ Rect tile_rect(float u, float v, float rf, float tiles_x, float tiles_y)
+{
+#pragma clang fp contract(off)
+    float fx0 = floorf((u - rf) / 16.0f);
+    float fx1 = floorf((u + rf) / 16.0f) + 1.0f;
+    float fy0 = floorf((v - rf) / 16.0f);
+    float fy1 = floorf((v + rf) / 16.0f) + 1.0f;
+    fx0 = fminf(fmaxf(fx0, 0.0f), tiles_x);
+    fx1 = fminf(fmaxf(fx1, 0.0f), tiles_x);
+    fy0 = fminf(fmaxf(fy0, 0.0f), tiles_y);
+    fy1 = fminf(fmaxf(fy1, 0.0f), tiles_y);
+    return Rect{(int)fx0, (int)fx1, (int)fy0, (int)fy1};
+}
+
+// Camera as the kernels take it (by value, in the kernel argument segment).
+struct Cam {
+    int width, height, tiles_x, tiles_y;
+    float fx, fy, cx, cy;
+    float R[9];
+    float t[3];
+    float znear, guard, lod;
+};
+
+inline Cam make_cam(const gs_camera &c)
+{
+    Cam k;
+    k.width = c.width;
+    k.height = c.height;
+    k.tiles_x = (c.width + kTile - 1) / kTile;
+    k.tiles_y = (c.height + kTile - 1) / kTile;
+    k.fx = c.fx; k.fy = c.fy; k.cx = c.cx; k.cy = c.cy;
+    for (int i = 0; i < 3; i++) {
+        for (int j = 0; j < 3; j++) k.R[i * 3 + j] = c.viewmat[i * 4 + j];
+        k.t[i] = c.viewmat[i * 4 + 3];
+    }
+    k.znear = c.znear;
+    k.guard = c.guard;
+    k.lod = c.lod_min_radius_px;
+    return k;
+}
+
+// Splat record as the kernels see it: three 16-byte words.
+struct __align__(16) Splat {
+    float4 a;   // u, v, depth, radius (int bits)
+    float4 b;   // conic a, b, c, opacity
+    float4 c;   // r, g, b, tiles_touched (uint bits)
+};
+static_assert(sizeof(Splat) == sizeof(gs_splat), "splat layout");
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launch helpers (host) -------------------------------------------------
+hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s);
+hipError_t launch_project_bwd(const gs_gaussians &g, const Cam &cam, const Splat *splats,
+                              const float *grad2d, const gs_grads &out, hipStream_t s);
+
+struct SortWorkspace;
+size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles);
+hipError_t launch_bin_sort(const Splat *splats, int64_t n, const Cam &cam, int64_t k_capacity,
+                           uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys, uint64_t *k_total,
+                           void *ws, size_t ws_bytes, hipStream_t s);
+size_t active_mask_workspace(int64_t n);
+hipError_t launch_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *ws,
+                              size_t ws_bytes, hipStream_t s);
+
+hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
+                             const Cam &cam, const float bg[3], float *image, float *final_T,
+                             uint32_t *n_contrib, hipStream_t s);
+hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
+                             const Cam &cam, const float bg[3], const float *final_T,
+                             const uint32_t *n_contrib, const float *dL_dimage, int64_t n,
+                             float *grad2d, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s);
+
+}  // namespace gsi

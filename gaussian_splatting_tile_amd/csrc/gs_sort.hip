@@ -1,0 +1,552 @@
+// Tile binning and depth sort (gfx950).
+//
+// The result is the stable LSB radix sort of the 64-bit keys
+//     key = tile << 32 | bits(depth)      (depth > 0, so the bits are monotone)
+// emitted in (Gaussian index, tile row-major) order, i.e. every tile's list
+// ordered by depth with the lower Gaussian index first among equal depths.
+//
+// An LSB radix sort handles the low digits first.  The low 32 bits (the
+// depth) are the same for every key a Gaussian emits, so the depth passes run
+// on the N projected Gaussians instead of on the K >= N duplicated keys:
+//   1. depth passes: stable 4 x 8-bit LSB sort of (depth bits, g) over the
+//      visible Gaussians (culled ones drop out in the first pass);
+//   2. duplication in that order: an exclusive scan of tiles_touched gives
+//      each Gaussian its slots, where it writes (tile, g) for its rect;
+//   3. tile passes: stable LSB passes of <= 8 bits over the tile id (the high
+//      digits of the key) on the K entries;
+//   4. tile ranges from the boundaries of the sorted tile ids.
+// Duplication keeps the relative order of the Gaussians, so this is the same
+// permutation as sorting all K 64-bit keys, with the depth digits moved
+// before the duplication.
+//
+// No host round trip: item counts (visible Gaussians, K) stay in device
+// memory; every grid is sized from host-known upper bounds and blocks past
+// the live count exit early.  Each radix pass is reduce-then-scan:
+// per-block digit counts (upsweep), a per-digit scan across blocks, then a
+// downsweep that ranks each 2048-item tile with wave ballots (match of equal
+// digits), orders it in LDS and writes every digit's run contiguously.
+#include "gs_internal.h"
+
+namespace gsi {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = kBlock / kWave;          // 4
+constexpr int kIpt = 8;                         // items per thread per tile
+constexpr int kTileItems = kBlock * kIpt;       // 2048
+constexpr int kWaveItems = kWave * kIpt;        // 512
+constexpr int kMaxGrid = 1024;                  // radix blocks per pass
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Inclusive scan across one wave64 (Kogge-Stone with cross-lane moves).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        T y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Exclusive scan of one value per thread across the 256-thread block;
+// returns the exclusive prefix, *total receives the block sum.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T x, T *total)
+{
+    __shared__ T wsum[kWaves];
+    const T inc = wave_inclusive_scan(x);
+    if (lane_id() == kWave - 1) wsum[wave_id()] = inc;
+    __syncthreads();
+    T before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        if (w < wave_id()) before += wsum[w];
+        all += wsum[w];
+    }
+    __syncthreads();
+    if (total) *total = all;
+    return before + inc - x;
+}
+
+__device__ __forceinline__ void chunk_of(uint32_t n, uint32_t &begin, uint32_t &end)
+{
+    const uint32_t G = gridDim.x;
+    uint32_t chunk = (n + G - 1) / G;
+    chunk = (chunk + kTileItems - 1) / kTileItems * kTileItems;
+    const uint64_t b = (uint64_t)blockIdx.x * chunk;
+    begin = b < n ? (uint32_t)b : n;
+    const uint64_t e = b + chunk;
+    end = e < n ? (uint32_t)e : n;
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t *__restrict__ keys,
+                                                        const uint32_t *__restrict__ n_ptr, int shift,
+                                                        int bits, int drop_sentinel,
+                                                        uint32_t *__restrict__ counts)
+{
+    __shared__ uint32_t hist[kWaves][256];
+    const uint32_t n = *n_ptr;
+    uint32_t begin, end;
+    chunk_of(n, begin, end);
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int i = threadIdx.x; i < kWaves * 256; i += kBlock) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    uint32_t *h = hist[wave_id()];
+    for (uint32_t i = begin + threadIdx.x; i < end; i += kBlock) {
+        const uint32_t k = keys[i];
+        if (drop_sentinel && k == kSentinel) continue;
+        atomicAdd(&h[(k >> shift) & mask], 1u);
+    }
+    __syncthreads();
+    const int d = threadIdx.x;   // 256 threads = 256 digits
+    counts[(size_t)d * gridDim.x + blockIdx.x] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+}
+
+// One block per digit: exclusive scan of that digit's per-block counts.
+__global__ __launch_bounds__(kBlock) void radix_scan(uint32_t *__restrict__ counts, int G,
+                                                     uint32_t *__restrict__ digit_total)
+{
+    uint32_t *row = counts + (size_t)blockIdx.x * G;
+    const int per = (G + kBlock - 1) / kBlock;
+    const int b0 = threadIdx.x * per;
+    uint32_t local = 0;
+    for (int i = 0; i < per; i++)
+        if (b0 + i < G) local += row[b0 + i];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(local, &total);
+    for (int i = 0; i < per; i++)
+        if (b0 + i < G) {
+            const uint32_t c = row[b0 + i];
+            row[b0 + i] = run;
+            run += c;
+        }
+    if (threadIdx.x == 0) digit_total[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void radix_downsweep(
+    const uint32_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
+    uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
+    const uint32_t *__restrict__ n_ptr, uint32_t *__restrict__ n_out_ptr, int shift, int bits,
+    int drop_sentinel, const uint32_t *__restrict__ counts, const uint32_t *__restrict__ digit_total)
+{
+    __shared__ uint32_t digit_base[256];
+    __shared__ uint32_t tile_start[256];
+    __shared__ uint32_t tile_cnt[256];
+    __shared__ uint32_t wave_cnt[kWaves][256];
+    __shared__ uint32_t sk[kTileItems];
+    __shared__ uint32_t sv[kTileItems];
+    __shared__ uint32_t s_tile_total;
+
+    const uint32_t n = *n_ptr;
+    uint32_t begin, end;
+    chunk_of(n, begin, end);
+    const uint32_t mask = (1u << bits) - 1u;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+
+    {   // global start of each digit for this block
+        const uint32_t t = digit_total[tid];
+        uint32_t all;
+        const uint32_t ex = block_exclusive_scan(t, &all);
+        digit_base[tid] = ex + counts[(size_t)tid * gridDim.x + blockIdx.x];
+        if (blockIdx.x == 0 && tid == 0 && n_out_ptr) *n_out_ptr = all;
+    }
+    __syncthreads();
+
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (uint32_t tb = begin; tb < end; tb += kTileItems) {
+        for (int i = lane; i < 256; i += kWave) wave_cnt[w][i] = 0;
+        // the wave's own row is written by its own lanes only; no barrier needed
+        uint32_t k[kIpt], v[kIpt], loc[kIpt];
+        bool ok[kIpt];
+#pragma unroll
+        for (int r = 0; r < kIpt; r++) {
+            const uint32_t idx = tb + w * kWaveItems + r * kWave + lane;
+            bool valid = idx < end;
+            uint32_t kk = valid ? keys_in[idx] : 0u;
+            if (drop_sentinel && kk == kSentinel) valid = false;
+            const uint32_t d = (kk >> shift) & mask;
+            uint64_t peers = __ballot(valid);
+            for (int bit = 0; bit < bits; bit++) {
+                const uint64_t bb = __ballot((d >> bit) & 1u);
+                peers &= ((d >> bit) & 1u) ? bb : ~bb;
+            }
+            const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
+            uint32_t before = 0;
+            if (valid) before = wave_cnt[w][d];
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) wave_cnt[w][d] = before + (uint32_t)__popcll(peers);
+            __builtin_amdgcn_wave_barrier();
+            k[r] = kk;
+            v[r] = valid ? vals_in[idx] : 0u;
+            loc[r] = before + rank;
+            ok[r] = valid;
+        }
+        __syncthreads();
+        {   // per digit: exclusive prefix over waves, tile totals, tile starts
+            const int d = tid;
+            uint32_t run = 0;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ww++) {
+                const uint32_t c = wave_cnt[ww][d];
+                wave_cnt[ww][d] = run;
+                run += c;
+            }
+            tile_cnt[d] = run;
+            uint32_t all;
+            tile_start[d] = block_exclusive_scan(run, &all);
+            if (tid == 0) s_tile_total = all;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kIpt; r++) {
+            if (!ok[r]) continue;
+            const uint32_t d = (k[r] >> shift) & mask;
+            const uint32_t pos = tile_start[d] + wave_cnt[w][d] + loc[r];
+            sk[pos] = k[r];
+            sv[pos] = v[r];
+        }
+        __syncthreads();
+        const uint32_t tot = s_tile_total;
+        for (uint32_t i = tid; i < tot; i += kBlock) {
+            const uint32_t kk = sk[i];
+            const uint32_t d = (kk >> shift) & mask;
+            const uint32_t o = digit_base[d] + (i - tile_start[d]);
+            keys_out[o] = kk;
+            vals_out[o] = sv[i];
+        }
+        __syncthreads();
+        digit_base[tid] += tile_cnt[tid];
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Setup: counters, empty tile ranges, depth keys of the visible Gaussians.
+__global__ __launch_bounds__(kBlock) void bin_init(const Splat *__restrict__ splats, uint32_t n,
+                                                   uint32_t *__restrict__ dkeys,
+                                                   uint32_t *__restrict__ dvals,
+                                                   uint32_t *__restrict__ ranges, uint32_t n_ranges,
+                                                   uint32_t *__restrict__ counters)
+{
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) {
+        const float4 a = splats[i].a;
+        const uint32_t tiles = __float_as_uint(splats[i].c.w);
+        dkeys[i] = tiles ? __float_as_uint(a.z) : kSentinel;
+        dvals[i] = i;
+    }
+    if (i < n_ranges) ranges[i] = 0;
+    if (i == 0) {
+        counters[0] = n;   // items entering the first depth pass
+        counters[1] = 0;   // visible Gaussians after it
+        counters[2] = 0;   // K clamped to the capacity
+    }
+}
+
+// Block sums of tiles_touched over depth-ordered Gaussians.
+__global__ __launch_bounds__(kBlock) void scan_reduce(const Splat *__restrict__ splats,
+                                                      const uint32_t *__restrict__ order,
+                                                      const uint32_t *__restrict__ m_ptr,
+                                                      uint64_t *__restrict__ block_sums)
+{
+    const uint32_t m = *m_ptr;
+    const uint32_t base = blockIdx.x * kTileItems;
+    uint64_t s = 0;
+    if (base < m) {
+        for (int r = 0; r < kIpt; r++) {
+            const uint32_t j = base + r * kBlock + threadIdx.x;
+            if (j < m) s += __float_as_uint(splats[order[j]].c.w);
+        }
+    }
+    uint64_t total;
+    block_exclusive_scan(s, &total);
+    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+// Exclusive scan of the block sums (one block); K and the clamped count.
+__global__ __launch_bounds__(kBlock) void scan_blocks(uint64_t *__restrict__ block_sums,
+                                                      const uint32_t *__restrict__ m_ptr,
+                                                      uint64_t cap, uint64_t *__restrict__ k_total,
+                                                      uint32_t *__restrict__ k_eff)
+{
+    const uint32_t m = *m_ptr;
+    const int nb = (int)((m + kTileItems - 1) / kTileItems);
+    const int per = (nb + kBlock - 1) / kBlock;
+    const int b0 = threadIdx.x * per;
+    uint64_t local = 0;
+    for (int i = 0; i < per; i++)
+        if (b0 + i < nb) local += block_sums[b0 + i];
+    uint64_t total;
+    uint64_t run = block_exclusive_scan(local, &total);
+    for (int i = 0; i < per; i++)
+        if (b0 + i < nb) {
+            const uint64_t c = block_sums[b0 + i];
+            block_sums[b0 + i] = run;
+            run += c;
+        }
+    if (threadIdx.x == 0) {
+        *k_total = total;
+        *k_eff = (uint32_t)(total < cap ? total : cap);
+    }
+}
+
+// Each depth-ordered Gaussian writes (tile id, g) for every tile of its rect,
+// row-major, at its slots.  The block re-scans its own 2048 counts in LDS.
+// Work is balanced across the block: after the scan, the block's entries are
+// handed out 256 at a time, each thread locating its Gaussian by a binary
+// search over the block's offsets.
+__global__ __launch_bounds__(kBlock) void duplicate_keys(
+    const Splat *__restrict__ splats, const uint32_t *__restrict__ order,
+    const uint32_t *__restrict__ m_ptr, const uint64_t *__restrict__ block_offsets, Cam cam,
+    uint64_t cap, uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ vals)
+{
+    __shared__ uint32_t s_off[kTileItems + 1];
+    __shared__ uint32_t s_g[kTileItems];
+    const uint32_t m = *m_ptr;
+    const uint32_t base = blockIdx.x * kTileItems;
+    if (base >= m) return;
+    const uint32_t cnt_items = min((uint32_t)kTileItems, m - base);
+    // blocked layout for the scan: thread t owns items t*8 .. t*8+7
+    uint32_t c[kIpt];
+    uint32_t local = 0;
+#pragma unroll
+    for (int r = 0; r < kIpt; r++) {
+        const uint32_t li = threadIdx.x * kIpt + r;
+        c[r] = 0;
+        if (li < cnt_items) {
+            const uint32_t g = order[base + li];
+            s_g[li] = g;
+            c[r] = __float_as_uint(splats[g].c.w);
+        }
+        local += c[r];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(local, &total);
+#pragma unroll
+    for (int r = 0; r < kIpt; r++) {
+        s_off[threadIdx.x * kIpt + r] = run;
+        run += c[r];
+    }
+    if (threadIdx.x == 0) s_off[kTileItems] = total;
+    __syncthreads();
+    const uint64_t blk = block_offsets[blockIdx.x];
+    for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
+        const uint64_t slot = blk + e;
+        if (slot >= cap) break;
+        // find li with s_off[li] <= e < s_off[li + 1]
+        int lo = 0, hi = (int)cnt_items - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        const uint32_t g = s_g[lo];
+        const uint32_t within = e - s_off[lo];
+        const float4 a = splats[g].a;
+        const Rect rc = tile_rect(a.x, a.y, (float)__float_as_int(a.w), (float)cam.tiles_x,
+                                  (float)cam.tiles_y);
+        const uint32_t wdt = (uint32_t)(rc.x1 - rc.x0);
+        const uint32_t ty = (uint32_t)rc.y0 + within / wdt;
+        const uint32_t tx = (uint32_t)rc.x0 + within % wdt;
+        tile_keys[slot] = ty * (uint32_t)cam.tiles_x + tx;
+        vals[slot] = g;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const uint32_t *__restrict__ tile_keys,
+                                                             const uint32_t *__restrict__ vals,
+                                                             const uint32_t *__restrict__ k_ptr,
+                                                             const Splat *__restrict__ splats,
+                                                             uint32_t *__restrict__ ranges,
+                                                             uint64_t *__restrict__ keys64)
+{
+    const uint32_t k = *k_ptr;
+    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+    if (i >= k) return;
+    const uint32_t t = tile_keys[i];
+    if (i == 0 || tile_keys[i - 1] != t) ranges[2 * t] = i;
+    if (i == k - 1 || tile_keys[i + 1] != t) ranges[2 * t + 1] = i + 1;
+    if (keys64) keys64[i] = ((uint64_t)t << 32) | __float_as_uint(splats[vals[i]].a.z);
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t value, size_t count)
+{
+    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < count) p[i] = value;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace carving.
+struct Carve {
+    char *p;
+    size_t off = 0;
+    template <typename T>
+    T *take(size_t count)
+    {
+        off = align_up(off, 256);
+        T *r = (T *)(p + off);
+        off += count * sizeof(T);
+        return r;
+    }
+};
+
+int radix_grid(uint64_t max_items)
+{
+    uint64_t g = (max_items + kTileItems - 1) / kTileItems;
+    if (g < 1) g = 1;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return (int)g;
+}
+
+int bits_for(uint32_t count)
+{
+    int b = 0;
+    while ((1ull << b) < count) b++;
+    return b;
+}
+
+struct BinWs {
+    uint32_t *dk[2], *dv[2];           // depth sort ping-pong [n]
+    uint64_t *block_sums;              // [ceil(n / 2048)]
+    uint32_t *tk[2], *tv;              // tile keys ping-pong, values scratch [cap]
+    uint32_t *counts;                  // [256 * kMaxGrid]
+    uint32_t *digit_total;             // [256]
+    uint32_t *counters;                // [4]
+};
+
+size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
+{
+    Carve c{base};
+    const size_t nn = (size_t)(n > 0 ? n : 1), kk = (size_t)(cap > 0 ? cap : 1);
+    BinWs w;
+    w.dk[0] = c.take<uint32_t>(nn);
+    w.dv[0] = c.take<uint32_t>(nn);
+    w.dk[1] = c.take<uint32_t>(nn);
+    w.dv[1] = c.take<uint32_t>(nn);
+    w.block_sums = c.take<uint64_t>((nn + kTileItems - 1) / kTileItems);
+    w.tk[0] = c.take<uint32_t>(kk);
+    w.tk[1] = c.take<uint32_t>(kk);
+    w.tv = c.take<uint32_t>(kk);
+    w.counts = c.take<uint32_t>(256 * kMaxGrid);
+    w.digit_total = c.take<uint32_t>(256);
+    w.counters = c.take<uint32_t>(4);
+    if (ws) *ws = w;
+    return c.off + 256;
+}
+
+hipError_t radix_pass(const uint32_t *kin, const uint32_t *vin, uint32_t *kout, uint32_t *vout,
+                      const uint32_t *n_ptr, uint32_t *n_out_ptr, uint64_t max_items, int shift,
+                      int bits, int drop, const BinWs &w, hipStream_t s)
+{
+    const int G = radix_grid(max_items);
+    radix_upsweep<<<G, kBlock, 0, s>>>(kin, n_ptr, shift, bits, drop, w.counts);
+    radix_scan<<<256, kBlock, 0, s>>>(w.counts, G, w.digit_total);
+    radix_downsweep<<<G, kBlock, 0, s>>>(kin, vin, kout, vout, n_ptr, n_out_ptr, shift, bits, drop,
+                                         w.counts, w.digit_total);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles)
+{
+    (void)n_tiles;
+    return carve_bin(nullptr, n, k_capacity, nullptr);
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s)
+{
+    if (count == 0) return hipSuccess;
+    fill_u32_kernel<<<(unsigned)((count + kBlock - 1) / kBlock), kBlock, 0, s>>>(p, value, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int64_t cap,
+                           uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys, uint64_t *k_total,
+                           void *ws_ptr, size_t ws_bytes, hipStream_t s)
+{
+    (void)ws_bytes;
+    BinWs w;
+    carve_bin((char *)ws_ptr, n64, cap, &w);
+    const uint32_t n = (uint32_t)n64;
+    const uint32_t n_tiles = (uint32_t)(cam.tiles_x * cam.tiles_y);
+    const uint32_t n_ranges = 2 * n_tiles;
+    hipError_t e;
+
+    const uint32_t init_items = n > n_ranges ? n : n_ranges;
+    bin_init<<<(init_items + kBlock - 1) / kBlock, kBlock, 0, s>>>(splats, n, w.dk[0], w.dv[0],
+                                                                   tile_ranges, n_ranges, w.counters);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // 1. depth: 4 x 8-bit passes; the first drops the culled Gaussians
+    int cur = 0;
+    for (int pass = 0; pass < 4; pass++) {
+        const uint32_t *n_in = pass == 0 ? &w.counters[0] : &w.counters[1];
+        e = radix_pass(w.dk[cur], w.dv[cur], w.dk[cur ^ 1], w.dv[cur ^ 1], n_in, &w.counters[1], n,
+                       8 * pass, 8, pass == 0, w, s);
+        if (e != hipSuccess) return e;
+        cur ^= 1;
+    }
+    const uint32_t *order = w.dv[cur];
+
+    // 2. slots and duplication (K in counters[2] after clamping to cap)
+    const uint32_t nblk = (n + kTileItems - 1) / kTileItems;
+    if (nblk > 0) {
+        scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], w.block_sums);
+        scan_blocks<<<1, kBlock, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total,
+                                         &w.counters[2]);
+        // 3. tile passes: choose the buffers so the last pass lands in `vals`
+        const int tbits = bits_for(n_tiles);
+        const int passes = tbits == 0 ? 0 : (tbits + 7) / 8;
+        uint32_t *kbuf[2] = {w.tk[0], w.tk[1]};
+        uint32_t *vbuf[2];
+        // pass p reads (k[p&1], v[p&1]) and writes (k[(p+1)&1], v[(p+1)&1]);
+        // the final destination must be `vals`
+        if (passes % 2 == 0) { vbuf[0] = vals; vbuf[1] = w.tv; }
+        else { vbuf[0] = w.tv; vbuf[1] = vals; }
+        duplicate_keys<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], w.block_sums, cam,
+                                               (uint64_t)cap, kbuf[0], vbuf[0]);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        int shift = 0;
+        for (int p = 0; p < passes; p++) {
+            const int bits = (tbits - shift) < 8 ? (tbits - shift) : 8;
+            e = radix_pass(kbuf[p & 1], vbuf[p & 1], kbuf[(p + 1) & 1], vbuf[(p + 1) & 1],
+                           &w.counters[2], nullptr, (uint64_t)cap, shift, bits, 0, w, s);
+            if (e != hipSuccess) return e;
+            shift += bits;
+        }
+        // with zero passes (one tile) the duplicated order is already final
+        const uint32_t *sorted_tiles = kbuf[passes & 1];
+        if (passes == 0) {
+            // vbuf[0] == vals when passes is even
+        }
+        // 4. ranges (and the optional 64-bit keys)
+        const uint64_t kgrid = ((uint64_t)cap + kBlock - 1) / kBlock;
+        if (kgrid > 0)
+            tile_ranges_kernel<<<(unsigned)kgrid, kBlock, 0, s>>>(sorted_tiles, vals, &w.counters[2],
+                                                                  splats, tile_ranges, keys);
+    } else {
+        // no Gaussians: K = 0
+        fill_u32_kernel<<<1, kBlock, 0, s>>>((uint32_t *)k_total, 0u, 2);
+    }
+    return hipGetLastError();
+}
+
+size_t active_mask_workspace(int64_t n)
+{
+    (void)n;
+    return 0;
+}
+
+hipError_t launch_active_mask(const float *, int64_t, int64_t, uint8_t *, void *, size_t, hipStream_t)
+{
+    return hipErrorNotSupported;
+}
+
+}  // namespace gsi

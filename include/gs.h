@@ -1,0 +1,220 @@
+/*
+ * gs.h -- C ABI of the MI355X (gfx950) tiled 3D Gaussian-splatting rasterizer.
+ *
+ * One view is rendered by four calls on one stream:
+ *   gs_project     per Gaussian: cull, EWA projection to a 2D conic, 3-sigma
+ *                  tile rect, SH colour, depth -> one 48-byte splat record;
+ *   gs_bin_sort    per (Gaussian, tile) pair: keys (tile << 32 | depth bits)
+ *                  sorted with an LSB radix sort, index order among equal
+ *                  keys; per-tile [start, end) ranges of the sorted list;
+ *   gs_render_fwd  per pixel: front-to-back alpha compositing of its tile's
+ *                  list;
+ *   gs_render_bwd  reverse pass through the compositing and the projection:
+ *                  gradients with respect to means, log-scales, quaternions,
+ *                  opacity logits and SH coefficients (accumulated).
+ *
+ * Where the pages touch this path (they give no formulas):
+ *   - Gaussians are projected onto the image plane over screen tiles and
+ *     blended per pixel by alpha compositing -- VisionTech 4DGS page, section
+ *     on its technical architecture and key mechanisms;
+ *   - each Gaussian carries position, scale, rotation, opacity and SH colour
+ *     -- GlobalSplat page, step (4) of its pipeline;
+ *   - Gaussians are projected to screen tiles before anything is exchanged --
+ *     BlitzGS page, section 2.1; the distance-LOD gate and importance mask
+ *     that shrink the per-view active set -- BlitzGS page, section 2.3;
+ *   - intermediate results cached in on-chip shared memory to cut global
+ *     memory traffic; stages of the raster pipeline run as separate thread
+ *     blocks -- "Gsplat" section of the pixel-diffusion page (sections 2.2
+ *     and 3.2);
+ *   - SH coefficients dominate the memory of a splat scene and may be stored
+ *     in 16 bits while gradients stay fp32 -- Spirula Studio page, sections
+ *     on the memory budget and the quantization switch.
+ * The rules the pages leave open are fixed as follows: pinhole camera with
+ * OpenCV axes; 0.3 px^2 low-pass dilation; radius ceil(3 sqrt(lambda_max));
+ * 16x16 tiles; alpha = min(0.99, o exp(power)); entries with alpha < 1/255
+ * are skipped; a pixel stops once its transmittance T < 1e-4 (tested before
+ * each entry); image = sum alpha_i T_i rgb_i + T_final bg.
+ *
+ * Conventions for every call:
+ *   - Device pointers are caller-owned device memory on the current device;
+ *     host pointers are named as such.  The library never allocates device
+ *     memory: temporaries live in a caller workspace sized by the matching
+ *     *_workspace_bytes query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; results are ready once the stream
+ *     is synchronised.  Nothing is read back to the host, so a view's four
+ *     calls can be enqueued back to back (and captured in a graph).
+ *   - Argument errors are returned synchronously and nothing is enqueued.
+ *     A failed kernel launch returns GS_ERR_HIP.
+ *   - Calls on different streams may run concurrently if they use disjoint
+ *     outputs and workspaces.  The library keeps no global mutable state.
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gs_status {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARG = 1,     /* a pointer, size or camera field is invalid */
+    GS_ERR_UNSUPPORTED = 2,     /* e.g. SH degree above 3                      */
+    GS_ERR_WORKSPACE = 3,       /* workspace smaller than the query returned   */
+    GS_ERR_HIP = 4              /* a kernel launch failed                      */
+} gs_status;
+
+typedef enum gs_sh_dtype { GS_SH_F32 = 0, GS_SH_F16 = 1 } gs_sh_dtype;
+
+/* Pinhole camera (host memory). */
+typedef struct gs_camera {
+    int32_t width, height;      /* image size in pixels, 1..32768 each        */
+    float fx, fy, cx, cy;       /* focal lengths and principal point (px)      */
+    float viewmat[12];          /* row-major 3x4 world->camera [R | t];
+                                   camera axes x right, y down, z forward     */
+    float znear;                /* Gaussians with camera z <= znear are culled
+                                   (0.2 in every workload)                     */
+    float guard;                /* Jacobian taken at x/z, y/z clamped to guard
+                                   x the half field of view (1.3)              */
+    float lod_min_radius_px;    /* distance-LOD gate: cull when the undilated
+                                   3-sigma radius 3 max(fx,fy) max(s) / |mu-c|
+                                   is below this many pixels; 0 = off          */
+} gs_camera;
+
+/* The Gaussians (device memory, structure of arrays). */
+typedef struct gs_gaussians {
+    int64_t n;                  /* number of Gaussians, 0 .. 2^31-1            */
+    int32_t sh_degree;          /* 0..3; K = (sh_degree+1)^2 coefficients      */
+    int32_t sh_dtype;           /* gs_sh_dtype of `sh`                          */
+    const float *means;         /* [3][n] world positions                      */
+    const float *scales;        /* [3][n] activated scales (exp of log-scale)  */
+    const float *quats;         /* [4][n] rotations (w, x, y, z), any norm > 0 */
+    const float *opacities;     /* [n] activated opacities (sigmoid of logit)  */
+    const void *sh;             /* [K][3][n] SH coefficients, band order
+                                   l = 0..3, m = -l..l, float or half          */
+    const uint8_t *active;      /* [n] per-Gaussian keep mask, or NULL = all   */
+} gs_gaussians;
+
+/* One projected Gaussian (device memory, 48 bytes, 16-byte aligned).
+ * A culled Gaussian has every field 0. */
+typedef struct gs_splat {
+    float u, v;                 /* image-plane mean (px); pixel (i, j) covers
+                                   [i, i+1) x [j, j+1)                          */
+    float depth;                /* camera-space z (> znear)                     */
+    int32_t radius;             /* ceil(3 sqrt(lambda_max)) px, 0 = culled      */
+    float conic_a, conic_b, conic_c;  /* inverse of the dilated 2D covariance:
+                                   [[a, b], [b, c]]                            */
+    float opacity;
+    float r, g, b;              /* max(0, 0.5 + sum_j k_j Y_j(view direction)) */
+    uint32_t tiles_touched;     /* tiles in the rect (0 = culled)               */
+} gs_splat;
+
+/* Gradients (device memory, fp32, structure of arrays, accumulated with +=
+ * so a batch of views sums; the caller zeroes them once per batch). */
+typedef struct gs_grads {
+    float *means;               /* [3][n]                                       */
+    float *log_scales;          /* [3][n]  d/d log-scale = s * d/ds             */
+    float *quats;               /* [4][n]  through the normalisation            */
+    float *opacity_logits;      /* [n]     d/d logit = o (1 - o) d/do           */
+    float *sh;                  /* [K][3][n] always fp32, also for half SH      */
+} gs_grads;
+
+/* ---------------------------------------------------------------------- */
+
+/* Projection + SH colour of every Gaussian for one camera.
+ * Writes splats[n].  Every value that decides a tile (u, v, depth, radius,
+ * the rect) and the conic are computed in fp32 one correctly rounded
+ * operation at a time in a fixed order, so they are reproducible bit for
+ * bit by any IEEE fp32 implementation of the same sequence.
+ * Errors: GS_ERR_INVALID_ARG for NULL pointers with n > 0, n < 0, a camera
+ * with non-positive size or focal length; GS_ERR_UNSUPPORTED for
+ * sh_degree outside 0..3 or an unknown sh_dtype. */
+gs_status gs_project(const gs_gaussians *gaussians /* host struct */,
+                     const gs_camera *camera /* host */, gs_splat *splats,
+                     void *stream);
+
+/* Workspace for gs_bin_sort, in bytes, for n Gaussians, a key capacity
+ * k_capacity and the camera's tile count. */
+size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles);
+
+/* Tile binning and depth sort of one view.
+ * Input: splats[n] from gs_project with the same camera.
+ * Output:
+ *   vals[k_capacity]        Gaussian index of each sorted (tile, depth) entry
+ *   tile_ranges[2*n_tiles]  [start, end) of each tile's entries in vals,
+ *                           (0, 0) for an empty tile; tiles are row-major,
+ *                           n_tiles = ceil(W/16) * ceil(H/16)
+ *   keys[k_capacity]        (optional, NULL to skip) the 64-bit sort keys
+ *                           tile << 32 | bits of the fp32 depth
+ *   k_total                 device uint64: K, the number of entries
+ * The order is that of a stable sort of the keys in emission order (Gaussian
+ * index, then tile row-major), i.e. by (tile, depth, Gaussian index).
+ * If K > k_capacity nothing is written past k_capacity, k_total still holds
+ * the true K and vals / tile_ranges are undefined: the caller reads k_total
+ * after synchronising and retries with a larger buffer.  k_capacity must be
+ * below 2^32.
+ * Errors: GS_ERR_INVALID_ARG (NULL pointers, bad sizes), GS_ERR_WORKSPACE. */
+gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
+                      const gs_camera *camera /* host */, int64_t k_capacity,
+                      uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys,
+                      uint64_t *k_total, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Forward compositing of every pixel.
+ * Inputs: splats (gs_project), vals and tile_ranges (gs_bin_sort),
+ * bg: host float[3] background colour.
+ * Outputs: image[3][H][W] (fp32, channel planes), final_T[H][W] (the
+ * transmittance left after the pixel's last entry), n_contrib[H][W]
+ * (1 + position in the tile's list of the last composited entry, 0 if
+ * none).  final_T and n_contrib are what gs_render_bwd needs.
+ * Errors: GS_ERR_INVALID_ARG. */
+gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
+                        const uint32_t *tile_ranges, const gs_camera *camera,
+                        const float *bg /* host [3] */, float *image,
+                        float *final_T, uint32_t *n_contrib, void *stream);
+
+/* Workspace for gs_render_bwd, in bytes (per-Gaussian 2D gradients). */
+size_t gs_render_bwd_workspace_bytes(int64_t n);
+
+/* Backward of one view: given dL/dimage[3][H][W], accumulates (+=) into
+ * grads the gradient of L with respect to the raw parameters.  Every
+ * discrete decision of the forward (tile membership, order, the 1/255 skip,
+ * the stop, the 0.99 cap, the colour clamp at 0, the guard clamp) is held as
+ * the forward took it; depth gets no gradient.  The inputs must be those of
+ * the matching forward call.  Per (Gaussian, tile) the 9 screen-space
+ * gradients are reduced across the tile's pixels on chip before one set of
+ * atomic adds, so the low bits of the result depend on scheduling.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE. */
+gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
+                        const gs_camera *camera /* host */,
+                        const gs_splat *splats, const uint32_t *vals,
+                        const uint32_t *tile_ranges, const float *bg /* host [3] */,
+                        const float *final_T, const uint32_t *n_contrib,
+                        const float *dL_dimage, const gs_grads *grads /* host struct */,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace for gs_active_mask, in bytes. */
+size_t gs_active_mask_workspace_bytes(int64_t n);
+
+/* Importance mask of the BlitzGS page (section 2.3): mask[g] = 1 for the
+ * `keep` Gaussians with the highest scores (ties to the lower index), else 0.
+ * scores: device float[n], finite and >= 0.  keep in 0..n.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
+gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep,
+                         uint8_t *mask, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Static description of a status code. */
+const char *gs_status_string(gs_status status);
+
+/* Library version, for the binding's load check. */
+int32_t gs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */

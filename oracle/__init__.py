@@ -29,7 +29,8 @@ class OrcCam(C.Structure):
 class OrcProjOut(C.Structure):
     _fields_ = [("u", C.c_void_p), ("v", C.c_void_p), ("z", C.c_void_p), ("radius", C.c_void_p),
                 ("rect", C.c_void_p), ("conic", C.c_void_p), ("opacity", C.c_void_p),
-                ("rgb", C.c_void_p), ("tiles", C.c_void_p), ("clamped", C.c_void_p)]
+                ("rgb", C.c_void_p), ("tiles", C.c_void_p), ("clamped", C.c_void_p),
+                ("rgb_raw", C.c_void_p)]
 
 
 class OrcBands(C.Structure):
@@ -93,9 +94,10 @@ def project(means, scales, quats, opacities, sh_degree, sh, cam, active=None,
     n = means.shape[1]
     out = dict(u=np.zeros(n), v=np.zeros(n), z=np.zeros(n), radius=np.zeros(n, np.int32),
                rect=np.zeros((4, n), np.int32), conic=np.zeros((3, n)), opacity=np.zeros(n),
-               rgb=np.zeros((3, n)), tiles=np.zeros(n, np.int32), clamped=np.zeros(n, np.uint8))
+               rgb=np.zeros((3, n)), tiles=np.zeros(n, np.int32), clamped=np.zeros(n, np.uint8),
+               rgb_raw=np.zeros((3, n)))
     po = OrcProjOut(*[_p(out[k]) for k in ("u", "v", "z", "radius", "rect", "conic", "opacity",
-                                           "rgb", "tiles", "clamped")])
+                                           "rgb", "tiles", "clamped", "rgb_raw")])
     act = None if active is None else np.ascontiguousarray(active, dtype=np.uint8)
     c = cam_struct(cam)
     fn = lib().orc_project_f32 if precision == "f32" else lib().orc_project_f64

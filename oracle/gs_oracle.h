@@ -52,6 +52,7 @@ typedef struct orc_proj_out {
     double *rgb;             /* [3][n] */
     int32_t *tiles;          /* tiles touched */
     uint8_t *clamped;        /* bit ch set when rgb channel ch was clamped at 0 */
+    double *rgb_raw;         /* [3][n]: 0.5 + sum k_j Y_j before the clamp */
 } orc_proj_out;
 
 /* Projection + SH colour.  The _f32 variant takes float inputs and follows the

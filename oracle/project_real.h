@@ -191,7 +191,11 @@ void FN(orc_project)(int64_t n, const REAL *means, const REAL *scales,
             out->u[g] = out->v[g] = out->z[g] = 0.0;
             out->radius[g] = 0;
             for (int k = 0; k < 4; k++) out->rect[k * n + g] = 0;
-            for (int k = 0; k < 3; k++) { out->conic[k * n + g] = 0.0; out->rgb[k * n + g] = 0.0; }
+            for (int k = 0; k < 3; k++) {
+                out->conic[k * n + g] = 0.0;
+                out->rgb[k * n + g] = 0.0;
+                out->rgb_raw[k * n + g] = 0.0;
+            }
             out->opacity[g] = 0.0;
             out->tiles[g] = 0;
             continue;
@@ -218,6 +222,7 @@ void FN(orc_project)(int64_t n, const REAL *means, const REAL *scales,
             double s = 0.0;
             for (int j = 0; j < K; j++) s += (double)sh[((int64_t)j * 3 + ch) * n + g] * Y[j];
             const double val = 0.5 + s;
+            out->rgb_raw[ch * n + g] = val;
             if (val < 0.0) out->clamped[g] |= (uint8_t)(1u << ch);
             out->rgb[ch * n + g] = val < 0.0 ? 0.0 : val;
         }

@@ -1,0 +1,63 @@
+"""Host-side checks of the C ABI that need no GPU: the library builds, loads,
+and exports every function include/gs.h declares; the header's struct
+layouts match the binding's; argument errors that are decided on the host
+come back without touching a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from gaussian_splatting_tile_amd import binding as B
+from gaussian_splatting_tile_amd import build as gbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "gs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gs_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    if gbuild.needs_build():
+        gbuild.build()
+    L = B.lib()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"{n} missing from {B.lib_path()}"
+    assert set(names) == set(B.SYMBOLS)
+
+
+def test_struct_layouts_match_header():
+    assert C.sizeof(B.GsCamera) == 4 * 2 + 4 * 4 + 4 * 12 + 4 * 3
+    assert C.sizeof(B.GsGaussians) == 8 + 4 + 4 + 8 * 6
+    assert C.sizeof(B.GsGrads) == 8 * 5
+    assert B.SPLAT_FLOATS * 4 == 48
+
+
+def test_status_strings_and_version():
+    L = B.lib()
+    assert L.gs_version() >= 1
+    assert L.gs_status_string(0).decode() == "ok"
+    assert "workspace" in L.gs_status_string(3).decode()
+
+
+def test_host_side_argument_errors_without_device():
+    L = B.lib()
+    cam = B.GsCamera()
+    cam.width, cam.height, cam.fx, cam.fy = 0, 10, 1.0, 1.0
+    gs = B.GsGaussians()
+    gs.n = 0
+    assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_INVALID_ARG
+    cam.width = 10
+    cam.guard = 1.3
+    gs.sh_degree = 7
+    assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
+    assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_bin_sort_workspace_bytes(1000, 5000, 64) > 5000 * 12
+    assert L.gs_render_bwd_workspace_bytes(1000) >= 1000 * 36
