@@ -1,11 +1,14 @@
 // Per-pixel alpha compositing, forward and backward (gfx950).
 //
-// One 256-lane block (four wave64) per 16x16 tile, one lane per pixel.  The
-// tile's depth-sorted list is consumed in batches of 256 records: the block
-// gathers the batch into LDS once (the on-chip caching of intermediate
-// results that the "Gsplat" section of the pixel-diffusion page prescribes),
-// then every lane walks it from LDS.  Compositing is VALU-bound: per
-// (pixel, Gaussian) pair it costs ~17 fp32 VALU operations and one v_exp_f32.
+// One wave64 per 16x16 tile, four pixels per lane: lane l owns column
+// l & 15 and rows (l >> 4) + 4 r, r = 0..3.  The tile's depth-sorted list is
+// consumed in batches of 64 records: each lane gathers one record into LDS
+// (the on-chip caching of intermediate results that the "Gsplat" section of
+// the pixel-diffusion page prescribes), then every lane walks the batch from
+// LDS with broadcast reads.  The four pixels of a lane share their column, so
+// the x-offset terms of the quadratic form are computed once per record and
+// the LDS reads and loop control are spread over four pixels.  A tile is one
+// wave, so no block barrier is ever needed beyond the LDS fill.
 //
 // Rules (readings; the pages name tiled alpha blending but give no formula):
 //   alpha = min(0.99, o exp(-1/2 d^T conic d)),  d = mean - pixel centre
@@ -14,15 +17,21 @@
 //   took T below 1e-4 was composited);
 //   C = sum alpha_i T_i rgb_i,  image = C + T_final bg.
 //
-// The forward and the backward evaluate alpha with the same function below
-// (contraction off, explicit fma, v_exp_f32), so the backward retraces the
-// forward's skip decisions exactly.
+// The exponent's quadratic form is evaluated in fp64: for thin Gaussians
+// seen far along their major axis its three terms reach ~1e5 and cancel to a
+// result of order 1, so any fp32 evaluation carries an exponent error near
+// 1e-3; in fp64 it is exact to ~1e-11, and on this chip an fp64 FMA issues
+// at the rate of a non-packed fp32 one.  The forward and the backward
+// evaluate exp(power) with the same sequence of operations, so the backward
+// retraces the forward's skip decisions exactly.
 #include "gs_internal.h"
 
 namespace gsi {
 namespace {
 
-constexpr int kBatch = kBlock;               // records staged per batch
+constexpr int kLanes = 64;                   // one wave per tile
+constexpr int kPx = 4;                       // pixels per lane
+constexpr int kBatch = kLanes;               // records staged per batch
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
@@ -37,95 +46,125 @@ __device__ __forceinline__ int tile_of_block(int n_tiles)
     return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 }
 
-struct Staged {
-    float4 uvo;    // u, v, opacity, -
-    float4 q;      // -a/2 log2e, -b log2e, -c/2 log2e, -   (exp2 form of the conic)
-    float4 rgb;    // r, g, b, -
+// A staged record: the exponent in exp2 form,
+//   exp(power) = exp2(qa dx^2 + qb dx dy + qc dy^2),  (qa, qb, qc) = -log2(e) (a/2, b, c/2),
+// kept in fp64 together with the mean; opacity and colour stay fp32.
+struct Stage {
+    double2 uv;      // u, v
+    double2 qab;     // qa, qb
+    double qc;
+    float4 orgb;     // opacity, r, g, b
 };
 
-__device__ __forceinline__ Staged stage(const Splat &s)
+__device__ __forceinline__ void stage_record(const Splat &s, double2 &uv, double2 &qab, double &qc, float4 &orgb)
 {
-    Staged t;
-    t.uvo = make_float4(s.a.x, s.a.y, s.b.w, 0.0f);
-    t.q = make_float4(-0.5f * kLog2e * s.b.x, -kLog2e * s.b.y, -0.5f * kLog2e * s.b.z, 0.0f);
-    t.rgb = make_float4(s.c.x, s.c.y, s.c.z, 0.0f);
-    return t;
+    const double l = -(double)kLog2e;
+    uv = make_double2((double)s.a.x, (double)s.a.y);
+    qab = make_double2(0.5 * l * (double)s.b.x, l * (double)s.b.y);
+    qc = 0.5 * l * (double)s.b.z;
+    orgb = make_float4(s.b.w, s.c.x, s.c.y, s.c.z);
 }
 
-// exp(power) at the pixel, in the exp2 form: exp2(a' dx^2 + b' dx dy + c' dy^2).
-__device__ __forceinline__ float gauss_at(const float4 &uvo, const float4 &q, float px, float py,
-                                          float &dx, float &dy)
+// Per record and column: the dx terms shared by the lane's four pixels.
+struct ColTerms { double dx, adx2, bdx; };
+
+__device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double2 &qab, double px)
 {
 #pragma clang fp contract(off)
-    dx = uvo.x - px;
-    dy = uvo.y - py;
-    const float t = fmaf(q.y, dy, q.x * dx);       // a' dx + b' dy
-    const float e = fmaf(q.z * dy, dy, t * dx);    // a' dx^2 + b' dx dy + c' dy^2
-    return __builtin_amdgcn_exp2f(e);
+    ColTerms c;
+    c.dx = uv.x - px;                 // exact: difference of two floats
+    c.adx2 = (qab.x * c.dx) * c.dx;
+    c.bdx = qab.y * c.dx;
+    return c;
 }
 
-__global__ __launch_bounds__(kBlock) void render_fwd_kernel(
+// exp(power) at one pixel of the column; dy returned for the gradients.
+__device__ __forceinline__ float gauss_at(const ColTerms &c, double qc, double v, double py, double &dy)
+{
+#pragma clang fp contract(off)
+    dy = v - py;
+    const double e = fma(dy, fma(qc, dy, c.bdx), c.adx2);
+    return __builtin_amdgcn_exp2f((float)e);
+}
+
+__global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
     const uint32_t *__restrict__ ranges, Cam cam, float bg0, float bg1, float bg2,
     float *__restrict__ image, float *__restrict__ final_T, uint32_t *__restrict__ n_contrib)
 {
-    __shared__ float4 s_uvo[kBatch];
-    __shared__ float4 s_q[kBatch];
-    __shared__ float4 s_rgb[kBatch];
+    __shared__ double2 s_uv[kBatch];
+    __shared__ double2 s_qab[kBatch];
+    __shared__ double s_qc[kBatch];
+    __shared__ float4 s_orgb[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int tile = tile_of_block(n_tiles);
     if (tile >= n_tiles) return;
+    const int lane = threadIdx.x;
     const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
-    const int i = tx * kTile + (threadIdx.x & (kTile - 1));
-    const int j = ty * kTile + (threadIdx.x >> 4);
-    const bool inside = i < cam.width && j < cam.height;
-    const float px = (float)i + 0.5f, py = (float)j + 0.5f;
+    const int x = tx * kTile + (lane & 15);
+    const int y0 = ty * kTile + (lane >> 4);
+    const double px = (double)x + 0.5;
+
+    double py[kPx];
+    float T[kPx], c0[kPx], c1[kPx], c2[kPx];
+    uint32_t last[kPx];
+    bool done[kPx];
+#pragma unroll
+    for (int r = 0; r < kPx; r++) {
+        const int y = y0 + 4 * r;
+        py[r] = (double)y + 0.5;
+        T[r] = 1.0f;
+        c0[r] = c1[r] = c2[r] = 0.0f;
+        last[r] = 0;
+        done[r] = !(x < cam.width && y < cam.height);
+    }
 
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
-    float T = 1.0f, c0 = 0.0f, c1 = 0.0f, c2 = 0.0f;
-    uint32_t last = 0;
-    bool done = !inside;
-
     for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
-        if (__syncthreads_and(done)) break;
-        const uint32_t m = b0 + threadIdx.x;
-        if (m < end) {
-            const Staged st = stage(splats[vals[m]]);
-            s_uvo[threadIdx.x] = st.uvo;
-            s_q[threadIdx.x] = st.q;
-            s_rgb[threadIdx.x] = st.rgb;
-        }
+        if (__all(done[0] && done[1] && done[2] && done[3])) break;
+        const uint32_t m = b0 + lane;
+        if (m < end)
+            stage_record(splats[vals[m]], s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
         __syncthreads();
         const int nb = (int)min((uint32_t)kBatch, end - b0);
-        if (!__all(done)) {
-            for (int k = 0; k < nb; k++) {
-                float dx, dy;
-                const float4 uvo = s_uvo[k];
-                const float raw = uvo.z * gauss_at(uvo, s_q[k], px, py, dx, dy);
+        const uint32_t pos0 = b0 - start + 1u;
+        for (int k = 0; k < nb; k++) {
+            const double2 uv = s_uv[k];
+            const double qc = s_qc[k];
+            const float4 orgb = s_orgb[k];
+            const ColTerms ct = col_terms(uv, s_qab[k], px);
+            const uint32_t pos = pos0 + (uint32_t)k;
+#pragma unroll
+            for (int r = 0; r < kPx; r++) {
+                double dy;
+                const float raw = orgb.x * gauss_at(ct, qc, uv.y, py[r], dy);
                 const float alpha = fminf(kAlphaMax, raw);
-                const bool take = !done && alpha >= kAlphaMin;
-                const float w = take ? alpha * T : 0.0f;
-                const float4 col = s_rgb[k];
-                c0 = fmaf(col.x, w, c0);
-                c1 = fmaf(col.y, w, c1);
-                c2 = fmaf(col.z, w, c2);
-                T = T - w;
-                last = take ? (b0 - start) + (uint32_t)k + 1u : last;
-                done = done || T < kTMin;
-                if ((k & 15) == 15 && __all(done)) break;
+                const bool take = !done[r] && alpha >= kAlphaMin;
+                const float w = take ? alpha * T[r] : 0.0f;
+                c0[r] = fmaf(orgb.y, w, c0[r]);
+                c1[r] = fmaf(orgb.z, w, c1[r]);
+                c2[r] = fmaf(orgb.w, w, c2[r]);
+                T[r] = T[r] - w;
+                last[r] = take ? pos : last[r];
+                done[r] = done[r] || T[r] < kTMin;
             }
+            if ((k & 31) == 31 && __all(done[0] && done[1] && done[2] && done[3])) break;
         }
         __syncthreads();
     }
-    if (inside) {
-        const size_t hw = (size_t)cam.width * cam.height;
-        const size_t p = (size_t)j * cam.width + i;
-        image[p] = c0 + T * bg0;
-        image[hw + p] = c1 + T * bg1;
-        image[2 * hw + p] = c2 + T * bg2;
-        final_T[p] = T;
-        n_contrib[p] = last;
+    const size_t hw = (size_t)cam.width * cam.height;
+#pragma unroll
+    for (int r = 0; r < kPx; r++) {
+        const int y = y0 + 4 * r;
+        if (x < cam.width && y < cam.height) {
+            const size_t p = (size_t)y * cam.width + x;
+            image[p] = c0[r] + T[r] * bg0;
+            image[hw + p] = c1[r] + T[r] * bg1;
+            image[2 * hw + p] = c2[r] + T[r] * bg2;
+            final_T[p] = T[r];
+            n_contrib[p] = last[r];
+        }
     }
 }
 
@@ -137,125 +176,204 @@ __global__ __launch_bounds__(kBlock) void render_fwd_kernel(
 //   dL/drgb_i   = alpha_i T_i G
 //   dL/dalpha_i = T_i <rgb_i - A, G>
 //   below the cap: dL/do = exp(power) dL/dalpha, dL/dpower = alpha dL/dalpha
-//   power = -1/2 (a dx^2 + c dy^2) - b dx dy (dx = u - px):
+//   power = -1/2 (a dx^2 + c dy^2) - b dx dy  (dx = u - px, dy = v - py):
 //     d/du = -(a dx + b dy), d/dv = -(c dy + b dx),
 //     d/da = -dx^2/2, d/db = -dx dy, d/dc = -dy^2/2.
-// The 9 per-pixel values of an entry are summed over the wave with cross-lane
-// moves, over the block's waves in LDS, then added to grad2d[9][n] with one
-// atomic per value per (Gaussian, tile).
+// A lane's four pixels share dx, so it accumulates S0 = sum dp, S1 = sum dp dy,
+// S2 = sum dp dy^2 (dp = dL/dpower) and forms the five conic/mean terms once.
+// The 9 per-lane values of a record are then summed over the wave by a split
+// butterfly (each exchange halves the values a lane carries) and nine lanes
+// add the totals to grad2d[9][n] with hardware float atomics: one atomic per
+// value per (Gaussian, tile).
 
-__device__ __forceinline__ float wave_sum(float v)
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    int r;
+    const int iv = __float_as_int(v);
+    switch (ctrl_sel) {
+    case 1: r = __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 2: r = __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    default: r = __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false); break; // row_ror:8
+    }
+    return __int_as_float(r);
 }
 
-__global__ __launch_bounds__(kBlock) void render_bwd_kernel(
+__device__ __forceinline__ float swz_xor4(float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+}
+__device__ __forceinline__ float swz_xor16(float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// Wave sums of v[0..8]; lane L in {0,1,2,3,4,5,6,8,9} returns the total of
+// value {0,5,3,8,1,6,4,2,7}[.] respectively (see reduce_slot).
+__device__ __forceinline__ float wave_reduce9(const float v[9], int lane)
+{
+    bool hi = (lane & 1) != 0;                    // xor 1: 9 values -> 5
+    float s[5];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float keep = hi ? v[i + 5] : v[i];
+        const float send = hi ? v[i] : v[i + 5];
+        s[i] = keep + dpp_f(send, 1);
+    }
+    s[4] = v[4] + dpp_f(v[4], 1);
+    hi = (lane & 2) != 0;                         // xor 2: 5 -> 3
+    const float n0 = (hi ? s[3] : s[0]) + dpp_f(hi ? s[0] : s[3], 2);
+    const float n1 = (hi ? s[4] : s[1]) + dpp_f(hi ? s[1] : s[4], 2);
+    const float n2 = s[2] + dpp_f(s[2], 2);
+    hi = (lane & 8) != 0;                         // xor 8: 3 -> 2
+    const float m0 = (hi ? n2 : n0) + dpp_f(hi ? n0 : n2, 8);
+    const float m1 = n1 + dpp_f(n1, 8);
+    hi = (lane & 4) != 0;                         // xor 4: 2 -> 1
+    float f = (hi ? m1 : m0) + swz_xor4(hi ? m0 : m1);
+    f += swz_xor16(f);                            // xor 16
+    f += __shfl_xor(f, 32, 64);                   // xor 32
+    return f;
+}
+
+// Which of the nine totals lane L holds after wave_reduce9, or -1.
+__device__ __forceinline__ int reduce_slot(int lane)
+{
+    switch (lane) {
+    case 0: return 0;
+    case 1: return 5;
+    case 2: return 3;
+    case 3: return 8;
+    case 4: return 1;
+    case 5: return 6;
+    case 6: return 4;
+    case 8: return 2;
+    case 9: return 7;
+    default: return -1;
+    }
+}
+
+__global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
     const uint32_t *__restrict__ ranges, Cam cam, float bg0, float bg1, float bg2,
     const float *__restrict__ final_T, const uint32_t *__restrict__ n_contrib,
     const float *__restrict__ dL_dimage, int n, float *__restrict__ grad2d)
 {
-    __shared__ float4 s_uvo[kBatch];
-    __shared__ float4 s_q[kBatch];
-    __shared__ float4 s_rgb[kBatch];
+    __shared__ double2 s_uv[kBatch];
+    __shared__ double2 s_qab[kBatch];
+    __shared__ double s_qc[kBatch];
+    __shared__ float4 s_orgb[kBatch];
     __shared__ float4 s_conic[kBatch];
     __shared__ uint32_t s_g[kBatch];
-    __shared__ float s_acc[9][kBatch];
-    __shared__ uint32_t s_max;
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int tile = tile_of_block(n_tiles);
     if (tile >= n_tiles) return;
+    const int lane = threadIdx.x;
     const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
-    const int i = tx * kTile + (threadIdx.x & (kTile - 1));
-    const int j = ty * kTile + (threadIdx.x >> 4);
-    const bool inside = i < cam.width && j < cam.height;
-    const float px = (float)i + 0.5f, py = (float)j + 0.5f;
-    const int lane = threadIdx.x & 63;
+    const int x = tx * kTile + (lane & 15);
+    const int y0 = ty * kTile + (lane >> 4);
+    const double px = (double)x + 0.5;
+    const size_t hw = (size_t)cam.width * cam.height;
 
-    const uint32_t start = ranges[2 * tile];
-    float T = 1.0f, G0 = 0.0f, G1 = 0.0f, G2 = 0.0f;
-    uint32_t last = 0;
-    if (inside) {
-        const size_t hw = (size_t)cam.width * cam.height;
-        const size_t p = (size_t)j * cam.width + i;
-        T = final_T[p];
-        last = n_contrib[p];
-        G0 = dL_dimage[p];
-        G1 = dL_dimage[hw + p];
-        G2 = dL_dimage[2 * hw + p];
+    double py[kPx];
+    float T[kPx], G0[kPx], G1[kPx], G2[kPx], A0[kPx], A1[kPx], A2[kPx];
+    uint32_t last[kPx];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int r = 0; r < kPx; r++) {
+        const int y = y0 + 4 * r;
+        py[r] = (double)y + 0.5;
+        T[r] = 1.0f;
+        G0[r] = G1[r] = G2[r] = 0.0f;
+        last[r] = 0;
+        if (x < cam.width && y < cam.height) {
+            const size_t p = (size_t)y * cam.width + x;
+            T[r] = final_T[p];
+            last[r] = n_contrib[p];
+            G0[r] = dL_dimage[p];
+            G1[r] = dL_dimage[hw + p];
+            G2[r] = dL_dimage[2 * hw + p];
+        }
+        A0[r] = bg0; A1[r] = bg1; A2[r] = bg2;
+        lmax = max(lmax, last[r]);
     }
-    float A0 = bg0, A1 = bg1, A2 = bg2;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
 
-    if (threadIdx.x == 0) s_max = 0;
-    __syncthreads();
-    atomicMax(&s_max, last);
-    __syncthreads();
-    const uint32_t stop = start + s_max;      // entries at or past this are unused
-
+    const int slot = reduce_slot(lane);
+    const uint32_t start = ranges[2 * tile];
+    const uint32_t stop = start + lmax;           // entries at or past this are unused
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
         const uint32_t bbeg = (uint32_t)max((int64_t)start, bend - kBatch);
         const int nb = (int)(bend - bbeg);
-        if ((int)threadIdx.x < nb) {
-            const uint32_t g = vals[bbeg + threadIdx.x];
+        if (lane < nb) {
+            const uint32_t g = vals[bbeg + lane];
             const Splat s = splats[g];
-            const Staged st = stage(s);
-            s_uvo[threadIdx.x] = st.uvo;
-            s_q[threadIdx.x] = st.q;
-            s_rgb[threadIdx.x] = st.rgb;
-            s_conic[threadIdx.x] = s.b;
-            s_g[threadIdx.x] = g;
+            stage_record(s, s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
+            s_conic[lane] = s.b;
+            s_g[lane] = g;
         }
-        for (int q = threadIdx.x; q < 9 * kBatch; q += kBlock) (&s_acc[0][0])[q] = 0.0f;
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
             const uint32_t pos = bbeg + (uint32_t)k - start;    // list position
-            float dx, dy;
-            const float4 uvo = s_uvo[k];
-            const float gexp = gauss_at(uvo, s_q[k], px, py, dx, dy);
-            const float raw = uvo.z * gexp;
-            const float alpha = fminf(kAlphaMax, raw);
-            const bool take = inside && pos < last && alpha >= kAlphaMin;
-            if (__ballot(take) == 0) continue;
-            float v[9];
+            const double2 uv = s_uv[k];
+            const double qc = s_qc[k];
+            const float4 orgb = s_orgb[k];
+            const ColTerms ct = col_terms(uv, s_qab[k], px);
+            float gexp[kPx], dys[kPx];
+            bool take[kPx];
+            bool any = false;
 #pragma unroll
-            for (int q = 0; q < 9; q++) v[q] = 0.0f;
-            if (take) {
-                const float4 col = s_rgb[k];
-                const float4 cn = s_conic[k];
+            for (int r = 0; r < kPx; r++) {
+                double dy;
+                gexp[r] = gauss_at(ct, qc, uv.y, py[r], dy);
+                dys[r] = (float)dy;
+                const float alpha = fminf(kAlphaMax, orgb.x * gexp[r]);
+                take[r] = pos < last[r] && alpha >= kAlphaMin;
+                any = any || take[r];
+            }
+            if (__ballot(any) == 0) continue;
+            const float4 col = make_float4(orgb.y, orgb.z, orgb.w, 0.0f);
+            float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f, S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kPx; r++) {
+                if (!take[r]) continue;
+                const float raw = orgb.x * gexp[r];
+                const float alpha = fminf(kAlphaMax, raw);
                 const float one_m = 1.0f - alpha;
-                T = T * __builtin_amdgcn_rcpf(one_m);
-                const float w = alpha * T;
-                v[6] = w * G0;
-                v[7] = w * G1;
-                v[8] = w * G2;
-                const float dla = T * ((col.x - A0) * G0 + (col.y - A1) * G1 + (col.z - A2) * G2);
-                A0 = alpha * col.x + one_m * A0;
-                A1 = alpha * col.y + one_m * A1;
-                A2 = alpha * col.z + one_m * A2;
+                T[r] = T[r] * __builtin_amdgcn_rcpf(one_m);
+                const float w = alpha * T[r];
+                g6 = fmaf(w, G0[r], g6);
+                g7 = fmaf(w, G1[r], g7);
+                g8 = fmaf(w, G2[r], g8);
+                const float dla = T[r] * ((col.x - A0[r]) * G0[r] + (col.y - A1[r]) * G1[r] +
+                                          (col.z - A2[r]) * G2[r]);
+                A0[r] = alpha * col.x + one_m * A0[r];
+                A1[r] = alpha * col.y + one_m * A1[r];
+                A2[r] = alpha * col.z + one_m * A2[r];
                 if (raw < kAlphaMax) {
-                    v[5] = dla * gexp;
+                    go = fmaf(dla, gexp[r], go);
                     const float dp = dla * alpha;
-                    v[0] = -dp * (cn.x * dx + cn.y * dy);
-                    v[1] = -dp * (cn.z * dy + cn.y * dx);
-                    v[2] = -0.5f * dp * dx * dx;
-                    v[3] = -dp * dx * dy;
-                    v[4] = -0.5f * dp * dy * dy;
+                    const float t = dp * dys[r];
+                    S0 += dp;
+                    S1 += t;
+                    S2 = fmaf(t, dys[r], S2);
                 }
             }
-#pragma unroll
-            for (int q = 0; q < 9; q++) {
-                const float s = wave_sum(v[q]);
-                if (lane == 0) atomicAdd(&s_acc[q][k], s);
-            }
-        }
-        __syncthreads();
-        for (int q = threadIdx.x; q < 9 * nb; q += kBlock) {
-            const int comp = q / nb, k = q % nb;
-            const float val = s_acc[comp][k];
-            if (val != 0.0f) atomicAdd(&grad2d[(size_t)comp * n + s_g[k]], val);
+            const float4 cn = s_conic[k];
+            const float dx = (float)ct.dx;
+            float v[9];
+            v[0] = -(cn.x * dx * S0 + cn.y * S1);
+            v[1] = -(cn.z * S1 + cn.y * dx * S0);
+            v[2] = -0.5f * dx * dx * S0;
+            v[3] = -dx * S1;
+            v[4] = -0.5f * S2;
+            v[5] = go;
+            v[6] = g6;
+            v[7] = g7;
+            v[8] = g8;
+            const float tot = wave_reduce9(v, lane);
+            if (slot >= 0 && tot != 0.0f)
+                unsafeAtomicAdd(&grad2d[(size_t)slot * n + s_g[k]], tot);
         }
         __syncthreads();
     }
@@ -269,7 +387,7 @@ hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const ui
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int grid = 8 * ((n_tiles + 7) / 8);
-    render_fwd_kernel<<<grid, kBlock, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], image,
+    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], image,
                                               final_T, n_contrib);
     return hipGetLastError();
 }
@@ -281,7 +399,7 @@ hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const ui
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int grid = 8 * ((n_tiles + 7) / 8);
-    render_bwd_kernel<<<grid, kBlock, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], final_T,
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], final_T,
                                               n_contrib, dL_dimage, (int)n, grad2d);
     return hipGetLastError();
 }

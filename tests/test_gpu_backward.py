@@ -1,0 +1,134 @@
+"""GPU backward parity: gs_render_bwd through the C ABI against the oracle's
+fp64 reverse pass (same forward decisions), within 1e-3 relative error.
+
+Pixels where the oracle's forward holds a near-threshold decision (alpha near
+1/255, T near 1e-4, alpha near the 0.99 cap) get a zero upstream gradient:
+there either branch is a correct forward, and the two sides may have taken
+different ones.  Gaussians whose colour sits within 1e-5 of the clamp at 0
+are left out of the SH and mean comparison for the same reason.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_splatting_tile_amd import binding as B
+from gaussian_splatting_tile_amd import scenes
+from tests.gpu_util import run_view, say
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("means", "log_scales", "quats", "opacity_logits", "sh")
+
+
+def _upstream(cam, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((3, cam.height, cam.width)) * 0.1).astype(np.float32)
+
+
+def _oracle_grads(sc, view, G, tile_mask=None, sh=None):
+    cam = sc.cameras[view]
+    sh = sc.sh_decoded() if sh is None else sh
+    op = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sh, cam)
+    ob = oracle.bin_sort(op, cam)
+    oo = oracle.render(op, ob, cam, tile_mask=tile_mask)
+    amb = (oo["events"] > 0) | (oo["capflag"] > 0)
+    Gz = G.astype(np.float64).copy()
+    Gz[:, amb] = 0.0
+    if tile_mask is not None:
+        tx = (np.arange(cam.width) // 16)[None, :]
+        ty = (np.arange(cam.height) // 16)[:, None]
+        sel = tile_mask.reshape(-1)[ty * cam.tiles_x + tx].astype(bool)
+        Gz[:, ~sel] = 0.0
+    g2 = oracle.render_bwd(op, ob, cam, Gz, tile_mask=tile_mask)
+    grads = oracle.project_bwd(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sh, cam, op, g2)
+    near_clamp = np.abs(op["rgb_raw"]).min(axis=0) < 1e-5
+    return grads, Gz.astype(np.float32), near_clamp, int(amb.sum())
+
+
+def _gpu_grads(sc, views_and_G, sh=None):
+    K_sh = (sc.sh_degree + 1) ** 2
+    n = sc.n
+    grads = dict(means=torch.zeros((3, n), device="cuda"), log_scales=torch.zeros((3, n), device="cuda"),
+                 quats=torch.zeros((4, n), device="cuda"), opacity_logits=torch.zeros(n, device="cuda"),
+                 sh=torch.zeros((K_sh, 3, n), device="cuda"))
+    ws = torch.empty(B.render_bwd_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    for view, G in views_and_G:
+        buf, K = run_view(sc, view, with_keys=False, sh=sh)
+        g, act, gs = buf._keep
+        dL = torch.from_numpy(np.ascontiguousarray(G)).cuda()
+        B.render_bwd(gs, buf.camc, buf.splats, buf.vals, buf.ranges, (0.0, 0.0, 0.0), buf.final_T,
+                     buf.n_contrib, dL, grads, ws)
+        torch.cuda.synchronize()
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+
+
+def _compare(gpu, ref, near_clamp, name, rel=1e-3):
+    """Per tensor: relative L2 error <= rel, and elementwise
+    |g - r| <= rel * max(|r|, 1e-2 * max|r|)."""
+    report = {}
+    for k in NAMES:
+        g, r = gpu[k], ref[k]
+        if k in ("sh", "means"):
+            keep = ~near_clamp
+            g = g[..., keep]
+            r = r[..., keep]
+        scale = np.abs(r).max(initial=0.0)
+        if scale == 0.0:
+            assert np.abs(g).max(initial=0.0) == 0.0, (name, k)
+            continue
+        l2 = np.linalg.norm(g - r) / np.linalg.norm(r)
+        bound = rel * np.maximum(np.abs(r), 1e-2 * scale)
+        frac_bad = float(np.mean(np.abs(g - r) > bound))
+        worst = float((np.abs(g - r) / np.maximum(np.abs(r), 1e-2 * scale)).max())
+        report[k] = dict(rel_l2=float(l2), worst_rel=worst, frac_over=frac_bad)
+    say(f"[gpu] {name}: {report}")
+    for k, rep in report.items():
+        assert rep["rel_l2"] <= rel, (name, k, rep)
+        assert rep["frac_over"] == 0.0, (name, k, rep)
+    return report
+
+
+def test_backward_tiny_1k_sh0():
+    sc = scenes.config(1)
+    say("[gpu] backward tiny_1k")
+    G = _upstream(sc.cameras[0], 101)
+    ref, Gz, nc, amb = _oracle_grads(sc, 0, G)
+    gpu = _gpu_grads(sc, [(0, Gz)])
+    _compare(gpu, ref, nc, "bwd tiny_1k")
+
+
+def test_backward_box_100k_sh3():
+    sc = scenes.config(2)
+    say("[gpu] backward box_100k")
+    G = _upstream(sc.cameras[0], 102)
+    ref, Gz, nc, amb = _oracle_grads(sc, 0, G)
+    gpu = _gpu_grads(sc, [(0, Gz)])
+    _compare(gpu, ref, nc, "bwd box_100k")
+
+
+def test_backward_accumulates_over_views():
+    sc = scenes.scene_like(seed=8, n=60_000, width=640, height=360, f=466.7, n_views=2)
+    say("[gpu] backward two views accumulate")
+    G0 = _upstream(sc.cameras[0], 103)
+    G1 = _upstream(sc.cameras[1], 104)
+    r0, Gz0, nc0, _ = _oracle_grads(sc, 0, G0)
+    r1, Gz1, nc1, _ = _oracle_grads(sc, 1, G1)
+    ref = {k: r0[k] + r1[k] for k in NAMES}
+    gpu = _gpu_grads(sc, [(0, Gz0), (1, Gz1)])
+    _compare(gpu, ref, nc0 | nc1, "bwd 2 views")
+
+
+def test_backward_scene_5m_1080p_tile_sample():
+    """The 5M-Gaussian 1080p workload on a seeded 1/8 sample of tiles
+    (upstream gradient zero outside the sample)."""
+    sc = scenes.config(4)
+    cam = sc.cameras[0]
+    say(f"[gpu] backward scene_5m 1080p, tile sample")
+    rng = np.random.default_rng(404)
+    tile_mask = (rng.random(cam.n_tiles) < 0.125).astype(np.uint8)
+    G = sc.upstream(0)
+    ref, Gz, nc, amb = _oracle_grads(sc, 0, G, tile_mask=tile_mask)
+    gpu = _gpu_grads(sc, [(0, Gz)])
+    _compare(gpu, ref, nc, "bwd scene_5m sample")

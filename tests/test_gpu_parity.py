@@ -64,6 +64,23 @@ def test_scene_1m_sh3_1080p(view):
     _check_view(sc, view, f"scene_1m_view{view}")
 
 
+def test_needle_gaussians_exponent_precision():
+    """Very thin, long Gaussians (aspect ratio ~1e4) in every orientation: far
+    along the major axis the exponent's terms reach ~1e5 and cancel, which
+    an fp32 evaluation of the quadratic form cannot reproduce to 1e-4."""
+    rng = np.random.default_rng(77)
+    n = 1500
+    sc = scenes.tiny(seed=77, n=n, width=512, height=384)
+    sc.cameras[0].fx = sc.cameras[0].fy = 450.0
+    sc.means[2] = rng.uniform(3.0, 6.0, n).astype(np.float32)
+    sc.means[0:2] = rng.uniform(-2.0, 2.0, (2, n)).astype(np.float32)
+    ls = np.stack([rng.uniform(-1.5, 0.0, n), np.full(n, -9.0), np.full(n, -9.0)]).astype(np.float32)
+    sc.log_scales = ls
+    sc.scales = np.exp(ls).astype(np.float32)
+    sc.opacities = rng.uniform(0.3, 0.99, n).astype(np.float32)
+    _check_view(sc, 0, "needles_1500")
+
+
 def test_ragged_image_sizes():
     # widths/heights that are not multiples of 16, and a single partial tile
     for (w, h) in [(100, 37), (15, 9), (16, 16), (17, 33)]:
