@@ -95,7 +95,8 @@ def main():
         del probe
         b = B.ViewBuffers(sc.n, cam, k)
         b.dL = f(sc.upstream(v))
-        b.bwd_ws = torch.empty(B.render_bwd_workspace_bytes(sc.n), dtype=torch.uint8, device=dev)
+        b.bwd_ws = torch.empty(B.render_bwd_workspace_bytes(sc.n, cam.width, cam.height), dtype=torch.uint8,
+                               device=dev)
         bufs.append(b)
         Ks.append(k)
     K_sh = (sc.sh_degree + 1) ** 2
@@ -133,7 +134,7 @@ def main():
             timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
                                                  None, b.k_total, b.ws, stream))
             timed("render_fwd", lambda: B.render_fwd(b.splats, b.vals, b.ranges, b.camc, bg, b.image,
-                                                     b.final_T, b.n_contrib, stream))
+                                                     b.final_T, b.n_contrib, b.fwd_ws, stream))
         e_fwd1.record(stream)
         if do_bwd:
             for b in bufs:

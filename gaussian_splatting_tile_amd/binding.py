@@ -42,7 +42,8 @@ class GsError(RuntimeError):
 
 
 _lib = None
-SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_render_fwd",
+SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_render_fwd_workspace_bytes",
+           "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_active_mask_workspace_bytes",
            "gs_active_mask", "gs_status_string", "gs_version")
 
@@ -67,8 +68,10 @@ def lib():
     L.gs_bin_sort_workspace_bytes.argtypes = [i64, i64, C.c_int32]
     L.gs_bin_sort_workspace_bytes.restype = sz
     L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, sz, vp]
-    L.gs_render_fwd.argtypes = [vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
-    L.gs_render_bwd_workspace_bytes.argtypes = [i64]
+    L.gs_render_fwd_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+    L.gs_render_fwd_workspace_bytes.restype = sz
+    L.gs_render_fwd.argtypes = [vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp, sz, vp]
+    L.gs_render_bwd_workspace_bytes.argtypes = [i64, C.c_int32, C.c_int32]
     L.gs_render_bwd_workspace_bytes.restype = sz
     L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, vp,
                                 vp, C.POINTER(GsGrads), vp, sz, vp]
@@ -149,16 +152,24 @@ def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, keys, k_to
                              _stream(stream)), "gs_bin_sort")
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def render_fwd_workspace_bytes(width: int, height: int) -> int:
+    return int(lib().gs_render_fwd_workspace_bytes(width, height))
+
+
 def render_fwd(splats, vals, tile_ranges, cam: GsCamera, bg: Sequence[float], image, final_T,
-               n_contrib, stream=None):
+               n_contrib, workspace, stream=None):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     _check(lib().gs_render_fwd(_ptr(splats), _ptr(vals), _ptr(tile_ranges), C.byref(cam),
                                C.cast(bgv, C.c_void_p), _ptr(image), _ptr(final_T), _ptr(n_contrib),
-                               _stream(stream)), "gs_render_fwd")
+                               _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_render_fwd")
 
 
-def render_bwd_workspace_bytes(n: int) -> int:
-    return int(lib().gs_render_bwd_workspace_bytes(n))
+def render_bwd_workspace_bytes(n: int, width: int, height: int) -> int:
+    return int(lib().gs_render_bwd_workspace_bytes(n, width, height))
 
 
 def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, bg, final_T, n_contrib,
@@ -205,10 +216,11 @@ class ViewBuffers:
         self.image = torch.empty((3, H, W), dtype=torch.float32, device=device)
         self.final_T = torch.empty((H, W), dtype=torch.float32, device=device)
         self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=device)
+        self.fwd_ws = torch.empty(render_fwd_workspace_bytes(W, H), dtype=torch.uint8, device=device)
 
     def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
         project(gs, self.camc, self.splats, stream)
         bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.keys,
                  self.k_total, self.ws, stream)
         render_fwd(self.splats, self.vals, self.ranges, self.camc, bg, self.image, self.final_T,
-                   self.n_contrib, stream)
+                   self.n_contrib, self.fwd_ws, stream)

@@ -87,22 +87,37 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera
                                     k_total, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
+static int tiles_of(int32_t width, int32_t height)
+{
+    return ((width + kTile - 1) / kTile) * ((height + kTile - 1) / kTile);
+}
+
+size_t gs_render_fwd_workspace_bytes(int32_t width, int32_t height)
+{
+    if (width < 1 || height < 1 || width > 32768 || height > 32768) return 0;
+    return render_schedule_workspace(tiles_of(width, height));
+}
+
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint32_t *tile_ranges,
                         const gs_camera *camera, const float *bg, float *image, float *final_T,
-                        uint32_t *n_contrib, void *stream)
+                        uint32_t *n_contrib, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!camera_ok(camera) || !tile_ranges || !bg || !image || !final_T || !n_contrib)
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < gs_render_fwd_workspace_bytes(camera->width, camera->height))
+        return GS_ERR_WORKSPACE;
     return from_hip(launch_render_fwd((const Splat *)splats, vals, tile_ranges, make_cam(*camera), bg,
-                                      image, final_T, n_contrib, (hipStream_t)stream));
+                                      image, final_T, n_contrib, workspace, (hipStream_t)stream));
 }
 
-size_t gs_render_bwd_workspace_bytes(int64_t n)
+static size_t grad2d_bytes(int64_t n) { return align_up((size_t)n * 9 * sizeof(float), 256); }
+
+size_t gs_render_bwd_workspace_bytes(int64_t n, int32_t width, int32_t height)
 {
-    if (n < 0) return 0;
-    return align_up((size_t)n * 9 * sizeof(float), 256) + 256;
+    if (n < 0 || width < 1 || height < 1 || width > 32768 || height > 32768) return 0;
+    return grad2d_bytes(n) + render_schedule_workspace(tiles_of(width, height));
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
@@ -120,14 +135,16 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     if (n > 0 && (!splats || !grads->means || !grads->log_scales || !grads->quats ||
                   !grads->opacity_logits || !grads->sh))
         return GS_ERR_INVALID_ARG;
-    if (workspace_bytes < gs_render_bwd_workspace_bytes(n) || !workspace) return GS_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, camera->width, camera->height))
+        return GS_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const Cam cam = make_cam(*camera);
     float *grad2d = (float *)workspace;
+    void *sched = (char *)workspace + grad2d_bytes(n);
     hipError_t e = launch_fill_u32((uint32_t *)grad2d, 0u, (size_t)n * 9, s);
     if (e != hipSuccess) return GS_ERR_HIP;
     e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, cam, bg, final_T, n_contrib,
-                          dL_dimage, n, grad2d, s);
+                          dL_dimage, n, grad2d, sched, s);
     if (e != hipSuccess) return GS_ERR_HIP;
     return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, grad2d, *grads, s));
 }

@@ -37,13 +37,58 @@ constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTMin = 1e-4f;
 
-// Block index -> tile, so that each XCD (blocks are dealt to the 8 XCDs
-// round robin) walks a contiguous band of tiles: neighbouring tiles share
-// most of their Gaussians, and the band's records then stay in one L2.
-__device__ __forceinline__ int tile_of_block(int n_tiles)
+// Tile schedule.  Per-tile work varies by two orders of magnitude (list
+// lengths 1 .. ~3000 at 1080p), and one wave per tile puts every tile of a
+// view in flight at once, so a static tile -> wave mapping leaves the busiest
+// SIMD with ~2x the mean load.  Instead a single block buckets the tiles by
+// list length (~1.4x wide buckets, longest first; empty tiles last) and the
+// blend runs as persistent waves that pull tile indices from an atomic
+// counter in that order: longest-processing-time-first list scheduling.
+constexpr int kSchedBins = 66;
+constexpr int kSchedThreads = 1024;
+
+__device__ __forceinline__ int length_bin(uint32_t L)
 {
-    const int per_xcd = (n_tiles + 7) / 8;
-    return (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (L == 0) return 0;
+    const int lg = 31 - __clz(L);                  // floor(log2 L)
+    const int half = lg > 0 ? (int)((L >> (lg - 1)) & 1u) : 0;
+    return 1 + 2 * lg + half;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const uint32_t *__restrict__ ranges,
+                                                                int n_tiles, uint32_t *__restrict__ order,
+                                                                uint32_t *__restrict__ head)
+{
+    __shared__ uint32_t hist[kSchedBins];
+    __shared__ uint32_t base[kSchedBins];
+    const int tid = threadIdx.x;
+    if (tid < kSchedBins) hist[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += kSchedThreads)
+        atomicAdd(&hist[length_bin(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t run = 0;
+        for (int b = kSchedBins - 1; b >= 0; b--) {
+            base[b] = run;
+            run += hist[b];
+        }
+        *head = 0;
+    }
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += kSchedThreads) {
+        const int b = length_bin(ranges[2 * t + 1] - ranges[2 * t]);
+        order[atomicAdd(&base[b], 1u)] = (uint32_t)t;
+    }
+}
+
+// Next tile for this wave, or -1 when the queue is drained.
+__device__ __forceinline__ int next_tile(const uint32_t *order, uint32_t *head, int n_tiles)
+{
+    uint32_t i = 0;
+    if (threadIdx.x == 0) i = atomicAdd(head, 1u);
+    i = (uint32_t)__shfl((int)i, 0, 64);
+    return i < (uint32_t)n_tiles ? (int)order[i] : -1;
 }
 
 // A staged record: the exponent in exp2 form,
@@ -89,8 +134,9 @@ __device__ __forceinline__ float gauss_at(const ColTerms &c, double qc, double v
 
 __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, Cam cam, float bg0, float bg1, float bg2,
-    float *__restrict__ image, float *__restrict__ final_T, uint32_t *__restrict__ n_contrib)
+    const uint32_t *__restrict__ ranges, const uint32_t *__restrict__ order, uint32_t *__restrict__ head,
+    Cam cam, float bg0, float bg1, float bg2, float *__restrict__ image, float *__restrict__ final_T,
+    uint32_t *__restrict__ n_contrib)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double2 s_qab[kBatch];
@@ -98,72 +144,72 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     __shared__ float4 s_orgb[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int tile = tile_of_block(n_tiles);
-    if (tile >= n_tiles) return;
     const int lane = threadIdx.x;
-    const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
-    const int x = tx * kTile + (lane & 15);
-    const int y0 = ty * kTile + (lane >> 4);
-    const double px = (double)x + 0.5;
-
-    double py[kPx];
-    float T[kPx], c0[kPx], c1[kPx], c2[kPx];
-    uint32_t last[kPx];
-    bool done[kPx];
-#pragma unroll
-    for (int r = 0; r < kPx; r++) {
-        const int y = y0 + 4 * r;
-        py[r] = (double)y + 0.5;
-        T[r] = 1.0f;
-        c0[r] = c1[r] = c2[r] = 0.0f;
-        last[r] = 0;
-        done[r] = !(x < cam.width && y < cam.height);
-    }
-
-    const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
-    for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
-        if (__all(done[0] && done[1] && done[2] && done[3])) break;
-        const uint32_t m = b0 + lane;
-        if (m < end)
-            stage_record(splats[vals[m]], s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
-        __syncthreads();
-        const int nb = (int)min((uint32_t)kBatch, end - b0);
-        const uint32_t pos0 = b0 - start + 1u;
-        for (int k = 0; k < nb; k++) {
-            const double2 uv = s_uv[k];
-            const double qc = s_qc[k];
-            const float4 orgb = s_orgb[k];
-            const ColTerms ct = col_terms(uv, s_qab[k], px);
-            const uint32_t pos = pos0 + (uint32_t)k;
-#pragma unroll
-            for (int r = 0; r < kPx; r++) {
-                double dy;
-                const float raw = orgb.x * gauss_at(ct, qc, uv.y, py[r], dy);
-                const float alpha = fminf(kAlphaMax, raw);
-                const bool take = !done[r] && alpha >= kAlphaMin;
-                const float w = take ? alpha * T[r] : 0.0f;
-                c0[r] = fmaf(orgb.y, w, c0[r]);
-                c1[r] = fmaf(orgb.z, w, c1[r]);
-                c2[r] = fmaf(orgb.w, w, c2[r]);
-                T[r] = T[r] - w;
-                last[r] = take ? pos : last[r];
-                done[r] = done[r] || T[r] < kTMin;
-            }
-            if ((k & 31) == 31 && __all(done[0] && done[1] && done[2] && done[3])) break;
-        }
-        __syncthreads();
-    }
     const size_t hw = (size_t)cam.width * cam.height;
+    for (int tile = next_tile(order, head, n_tiles); tile >= 0; tile = next_tile(order, head, n_tiles)) {
+        const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
+        const int x = tx * kTile + (lane & 15);
+        const int y0 = ty * kTile + (lane >> 4);
+        const double px = (double)x + 0.5;
+
+        // A pixel is live while T >= 1e-4; pixels outside the image start at
+        // T = 0 and never composite.
+        double py[kPx];
+        float T[kPx], c0[kPx], c1[kPx], c2[kPx];
+        uint32_t last[kPx];
 #pragma unroll
-    for (int r = 0; r < kPx; r++) {
-        const int y = y0 + 4 * r;
-        if (x < cam.width && y < cam.height) {
-            const size_t p = (size_t)y * cam.width + x;
-            image[p] = c0[r] + T[r] * bg0;
-            image[hw + p] = c1[r] + T[r] * bg1;
-            image[2 * hw + p] = c2[r] + T[r] * bg2;
-            final_T[p] = T[r];
-            n_contrib[p] = last[r];
+        for (int r = 0; r < kPx; r++) {
+            const int y = y0 + 4 * r;
+            py[r] = (double)y + 0.5;
+            T[r] = (x < cam.width && y < cam.height) ? 1.0f : 0.0f;
+            c0[r] = c1[r] = c2[r] = 0.0f;
+            last[r] = 0;
+        }
+
+        const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+        for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
+            if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
+            const uint32_t m = b0 + lane;
+            if (m < end)
+                stage_record(splats[vals[m]], s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
+            __syncthreads();
+            const int nb = (int)min((uint32_t)kBatch, end - b0);
+            const uint32_t pos0 = b0 - start + 1u;
+            for (int k = 0; k < nb; k++) {
+                const double2 uv = s_uv[k];
+                const double qc = s_qc[k];
+                const float4 orgb = s_orgb[k];
+                const ColTerms ct = col_terms(uv, s_qab[k], px);
+                const uint32_t pos = pos0 + (uint32_t)k;
+#pragma unroll
+                for (int r = 0; r < kPx; r++) {
+                    double dy;
+                    const float raw = orgb.x * gauss_at(ct, qc, uv.y, py[r], dy);
+                    const float alpha = fminf(kAlphaMax, raw);
+                    const bool take = T[r] >= kTMin && alpha >= kAlphaMin;
+                    const float w = take ? alpha * T[r] : 0.0f;
+                    c0[r] = fmaf(orgb.y, w, c0[r]);
+                    c1[r] = fmaf(orgb.z, w, c1[r]);
+                    c2[r] = fmaf(orgb.w, w, c2[r]);
+                    T[r] = T[r] - w;
+                    last[r] = take ? pos : last[r];
+                }
+                if ((k & 31) == 31 && __all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin))
+                    break;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < kPx; r++) {
+            const int y = y0 + 4 * r;
+            if (x < cam.width && y < cam.height) {
+                const size_t p = (size_t)y * cam.width + x;
+                image[p] = c0[r] + T[r] * bg0;
+                image[hw + p] = c1[r] + T[r] * bg1;
+                image[2 * hw + p] = c2[r] + T[r] * bg2;
+                final_T[p] = T[r];
+                n_contrib[p] = last[r];
+            }
         }
     }
 }
@@ -253,9 +299,10 @@ __device__ __forceinline__ int reduce_slot(int lane)
 
 __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, Cam cam, float bg0, float bg1, float bg2,
-    const float *__restrict__ final_T, const uint32_t *__restrict__ n_contrib,
-    const float *__restrict__ dL_dimage, int n, float *__restrict__ grad2d)
+    const uint32_t *__restrict__ ranges, const uint32_t *__restrict__ order, uint32_t *__restrict__ head,
+    Cam cam, float bg0, float bg1, float bg2, const float *__restrict__ final_T,
+    const uint32_t *__restrict__ n_contrib, const float *__restrict__ dL_dimage, int n,
+    float *__restrict__ grad2d)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double2 s_qab[kBatch];
@@ -265,14 +312,14 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     __shared__ uint32_t s_g[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int tile = tile_of_block(n_tiles);
-    if (tile >= n_tiles) return;
     const int lane = threadIdx.x;
+    const size_t hw = (size_t)cam.width * cam.height;
+    const int slot = reduce_slot(lane);
+    for (int tile = next_tile(order, head, n_tiles); tile >= 0; tile = next_tile(order, head, n_tiles)) {
     const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
     const int x = tx * kTile + (lane & 15);
     const int y0 = ty * kTile + (lane >> 4);
     const double px = (double)x + 0.5;
-    const size_t hw = (size_t)cam.width * cam.height;
 
     double py[kPx];
     float T[kPx], G0[kPx], G1[kPx], G2[kPx], A0[kPx], A1[kPx], A2[kPx];
@@ -299,7 +346,6 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
 
-    const int slot = reduce_slot(lane);
     const uint32_t start = ranges[2 * tile];
     const uint32_t stop = start + lmax;           // entries at or past this are unused
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
@@ -377,30 +423,52 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
         }
         __syncthreads();
     }
+    }
 }
 
 }  // namespace
 
+// Persistent grid: as many one-wave blocks as fit on the device at once.
+template <typename K>
+int resident_blocks(K kernel, int n_tiles)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return n_tiles;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return n_tiles;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kLanes, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const long long g = (long long)cus * per_cu;
+    return (int)(g < n_tiles ? g : n_tiles);
+}
+
+size_t render_schedule_workspace(int n_tiles) { return align_up(((size_t)n_tiles + 64) * sizeof(uint32_t), 256); }
+
 hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
                              const Cam &cam, const float bg[3], float *image, float *final_T,
-                             uint32_t *n_contrib, hipStream_t s)
+                             uint32_t *n_contrib, void *ws, hipStream_t s)
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int grid = 8 * ((n_tiles + 7) / 8);
-    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], image,
-                                              final_T, n_contrib);
+    uint32_t *order = (uint32_t *)ws;
+    uint32_t *head = order + n_tiles;
+    schedule_tiles<<<1, kSchedThreads, 0, s>>>(ranges, n_tiles, order, head);
+    const int grid = resident_blocks(render_fwd_kernel, n_tiles);
+    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, order, head, cam, bg[0], bg[1], bg[2],
+                                              image, final_T, n_contrib);
     return hipGetLastError();
 }
 
 hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
                              const Cam &cam, const float bg[3], const float *final_T,
                              const uint32_t *n_contrib, const float *dL_dimage, int64_t n,
-                             float *grad2d, hipStream_t s)
+                             float *grad2d, void *ws, hipStream_t s)
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int grid = 8 * ((n_tiles + 7) / 8);
-    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, cam, bg[0], bg[1], bg[2], final_T,
-                                              n_contrib, dL_dimage, (int)n, grad2d);
+    uint32_t *order = (uint32_t *)ws;
+    uint32_t *head = order + n_tiles;
+    schedule_tiles<<<1, kSchedThreads, 0, s>>>(ranges, n_tiles, order, head);
+    const int grid = resident_blocks(render_bwd_kernel, n_tiles);
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, order, head, cam, bg[0], bg[1], bg[2],
+                                              final_T, n_contrib, dL_dimage, (int)n, grad2d);
     return hipGetLastError();
 }
 

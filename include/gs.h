@@ -163,6 +163,10 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
                       uint64_t *k_total, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* Workspace for gs_render_fwd, in bytes, for an image of width x height
+ * (the tile schedule: one index per 16x16 tile). */
+size_t gs_render_fwd_workspace_bytes(int32_t width, int32_t height);
+
 /* Forward compositing of every pixel.
  * Inputs: splats (gs_project), vals and tile_ranges (gs_bin_sort),
  * bg: host float[3] background colour.
@@ -170,14 +174,18 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
  * transmittance left after the pixel's last entry), n_contrib[H][W]
  * (1 + position in the tile's list of the last composited entry, 0 if
  * none).  final_T and n_contrib are what gs_render_bwd needs.
- * Errors: GS_ERR_INVALID_ARG. */
+ * Tiles are processed longest list first by persistent waves; the result
+ * does not depend on the order.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
                         const uint32_t *tile_ranges, const gs_camera *camera,
                         const float *bg /* host [3] */, float *image,
-                        float *final_T, uint32_t *n_contrib, void *stream);
+                        float *final_T, uint32_t *n_contrib, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
-/* Workspace for gs_render_bwd, in bytes (per-Gaussian 2D gradients). */
-size_t gs_render_bwd_workspace_bytes(int64_t n);
+/* Workspace for gs_render_bwd, in bytes: per-Gaussian 2D gradients for n
+ * Gaussians and the tile schedule of a width x height image. */
+size_t gs_render_bwd_workspace_bytes(int64_t n, int32_t width, int32_t height);
 
 /* Backward of one view: given dL/dimage[3][H][W], accumulates (+=) into
  * grads the gradient of L with respect to the raw parameters.  Every

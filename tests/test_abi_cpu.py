@@ -60,4 +60,6 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_bin_sort_workspace_bytes(1000, 5000, 64) > 5000 * 12
-    assert L.gs_render_bwd_workspace_bytes(1000) >= 1000 * 36
+    assert L.gs_render_bwd_workspace_bytes(1000, 128, 128) >= 1000 * 36
+    assert L.gs_render_fwd_workspace_bytes(128, 128) >= 64 * 4
+    assert L.gs_render_fwd_workspace_bytes(0, 128) == 0
