@@ -95,8 +95,7 @@ def main():
         del probe
         b = B.ViewBuffers(sc.n, cam, k)
         b.dL = f(sc.upstream(v))
-        b.bwd_ws = torch.empty(B.render_bwd_workspace_bytes(sc.n, cam.width, cam.height), dtype=torch.uint8,
-                               device=dev)
+        b.bwd_ws = torch.empty(B.render_bwd_workspace_bytes(sc.n), dtype=torch.uint8, device=dev)
         bufs.append(b)
         Ks.append(k)
     K_sh = (sc.sh_degree + 1) ** 2
@@ -132,15 +131,13 @@ def main():
         for b in bufs:
             timed("project", lambda: B.project(gs, b.camc, b.splats, stream))
             timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
-                                                 None, b.k_total, b.ws, stream))
-            timed("render_fwd", lambda: B.render_fwd(b.splats, b.vals, b.ranges, b.camc, bg, b.image,
-                                                     b.final_T, b.n_contrib, b.fwd_ws, stream))
+                                                 b.schedule, None, b.k_total, b.ws, stream))
+            timed("render_fwd", lambda: B.render_fwd(b.splats, b.vals, b.ranges, b.schedule, b.camc, bg,
+                                                     b.image, b.final_T, b.n_contrib, stream))
         e_fwd1.record(stream)
         if do_bwd:
             for b in bufs:
-                timed("render_bwd", lambda: B.render_bwd(gs, b.camc, b.splats, b.vals, b.ranges, bg,
-                                                         b.final_T, b.n_contrib, b.dL, grads, b.bwd_ws,
-                                                         stream))
+                timed("render_bwd", lambda: b.backward(gs, b.dL, grads, b.bwd_ws, bg, stream))
         e_end.record(stream)
         if record:
             step_ev.append((e_fwd0, e_fwd1, e_end))

@@ -42,7 +42,7 @@ class GsError(RuntimeError):
 
 
 _lib = None
-SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_render_fwd_workspace_bytes",
+SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bin_sort",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_active_mask_workspace_bytes",
            "gs_active_mask", "gs_status_string", "gs_version")
@@ -67,13 +67,13 @@ def lib():
     L.gs_project.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp]
     L.gs_bin_sort_workspace_bytes.argtypes = [i64, i64, C.c_int32]
     L.gs_bin_sort_workspace_bytes.restype = sz
-    L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, sz, vp]
-    L.gs_render_fwd_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
-    L.gs_render_fwd_workspace_bytes.restype = sz
-    L.gs_render_fwd.argtypes = [vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp, sz, vp]
-    L.gs_render_bwd_workspace_bytes.argtypes = [i64, C.c_int32, C.c_int32]
+    L.gs_schedule_words.argtypes = [C.c_int32, C.c_int32]
+    L.gs_schedule_words.restype = sz
+    L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
+    L.gs_render_bwd_workspace_bytes.argtypes = [i64]
     L.gs_render_bwd_workspace_bytes.restype = sz
-    L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, vp,
+    L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, vp, vp,
                                 vp, C.POINTER(GsGrads), vp, sz, vp]
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
@@ -144,41 +144,40 @@ def bin_sort_workspace_bytes(n: int, k_capacity: int, n_tiles: int) -> int:
     return int(lib().gs_bin_sort_workspace_bytes(n, k_capacity, n_tiles))
 
 
-def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, keys, k_total, workspace,
-             stream=None):
-    _check(lib().gs_bin_sort(_ptr(splats), int(n), C.byref(cam), int(k_capacity), _ptr(vals),
-                             _ptr(tile_ranges), _ptr(keys), _ptr(k_total), _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                             _stream(stream)), "gs_bin_sort")
-
-
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def render_fwd_workspace_bytes(width: int, height: int) -> int:
-    return int(lib().gs_render_fwd_workspace_bytes(width, height))
+def schedule_words(width: int, height: int) -> int:
+    return int(lib().gs_schedule_words(width, height))
 
 
-def render_fwd(splats, vals, tile_ranges, cam: GsCamera, bg: Sequence[float], image, final_T,
-               n_contrib, workspace, stream=None):
+def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, keys, k_total, workspace,
+             stream=None):
+    _check(lib().gs_bin_sort(_ptr(splats), int(n), C.byref(cam), int(k_capacity), _ptr(vals),
+                             _ptr(tile_ranges), _ptr(schedule), _ptr(keys), _ptr(k_total), _ptr(workspace),
+                             _nbytes(workspace), _stream(stream)), "gs_bin_sort")
+
+
+def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[float], image, final_T,
+               n_contrib, stream=None):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
-    _check(lib().gs_render_fwd(_ptr(splats), _ptr(vals), _ptr(tile_ranges), C.byref(cam),
+    _check(lib().gs_render_fwd(_ptr(splats), _ptr(vals), _ptr(tile_ranges), _ptr(schedule), C.byref(cam),
                                C.cast(bgv, C.c_void_p), _ptr(image), _ptr(final_T), _ptr(n_contrib),
-                               _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_render_fwd")
+                               _stream(stream)), "gs_render_fwd")
 
 
-def render_bwd_workspace_bytes(n: int, width: int, height: int) -> int:
-    return int(lib().gs_render_bwd_workspace_bytes(n, width, height))
+def render_bwd_workspace_bytes(n: int) -> int:
+    return int(lib().gs_render_bwd_workspace_bytes(n))
 
 
-def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, bg, final_T, n_contrib,
+def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, schedule, bg, final_T, n_contrib,
                dL_dimage, grads: Dict[str, torch.Tensor], workspace, stream=None):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
                  _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
     _check(lib().gs_render_bwd(C.byref(gs), C.byref(cam), _ptr(splats), _ptr(vals), _ptr(tile_ranges),
-                               C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
+                               _ptr(schedule), C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
                                C.byref(gr), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_render_bwd")
@@ -216,11 +215,15 @@ class ViewBuffers:
         self.image = torch.empty((3, H, W), dtype=torch.float32, device=device)
         self.final_T = torch.empty((H, W), dtype=torch.float32, device=device)
         self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=device)
-        self.fwd_ws = torch.empty(render_fwd_workspace_bytes(W, H), dtype=torch.uint8, device=device)
+        self.schedule = torch.empty(schedule_words(W, H), dtype=torch.int32, device=device)
 
     def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
         project(gs, self.camc, self.splats, stream)
-        bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.keys,
-                 self.k_total, self.ws, stream)
-        render_fwd(self.splats, self.vals, self.ranges, self.camc, bg, self.image, self.final_T,
-                   self.n_contrib, self.fwd_ws, stream)
+        bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.schedule,
+                 self.keys, self.k_total, self.ws, stream)
+        render_fwd(self.splats, self.vals, self.ranges, self.schedule, self.camc, bg, self.image, self.final_T,
+                   self.n_contrib, stream)
+
+    def backward(self, gs: GsGaussians, dL_dimage, grads, workspace, bg=(0.0, 0.0, 0.0), stream=None):
+        render_bwd(gs, self.camc, self.splats, self.vals, self.ranges, self.schedule, bg, self.final_T,
+                   self.n_contrib, dL_dimage, grads, workspace, stream)

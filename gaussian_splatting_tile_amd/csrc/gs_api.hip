@@ -71,63 +71,62 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tile
     return bin_sort_workspace(n, k_capacity, n_tiles);
 }
 
-gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
-                      uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys, uint64_t *k_total,
-                      void *workspace, size_t workspace_bytes, void *stream)
-{
-    if (n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
-        return GS_ERR_INVALID_ARG;
-    if (!camera_ok(camera) || !tile_ranges || !k_total) return GS_ERR_INVALID_ARG;
-    if (n > 0 && !splats) return GS_ERR_INVALID_ARG;
-    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
-    const Cam cam = make_cam(*camera);
-    const size_t need = bin_sort_workspace(n, k_capacity, cam.tiles_x * cam.tiles_y);
-    if (workspace_bytes < need || !workspace) return GS_ERR_WORKSPACE;
-    return from_hip(launch_bin_sort((const Splat *)splats, n, cam, k_capacity, vals, tile_ranges, keys,
-                                    k_total, workspace, workspace_bytes, (hipStream_t)stream));
-}
-
 static int tiles_of(int32_t width, int32_t height)
 {
     return ((width + kTile - 1) / kTile) * ((height + kTile - 1) / kTile);
 }
 
-size_t gs_render_fwd_workspace_bytes(int32_t width, int32_t height)
+size_t gs_schedule_words(int32_t width, int32_t height)
 {
     if (width < 1 || height < 1 || width > 32768 || height > 32768) return 0;
-    return render_schedule_workspace(tiles_of(width, height));
+    return schedule_words(tiles_of(width, height));
+}
+
+gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
+                      uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint64_t *keys,
+                      uint64_t *k_total, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
+        return GS_ERR_INVALID_ARG;
+    if (!camera_ok(camera) || !tile_ranges || !schedule || !k_total) return GS_ERR_INVALID_ARG;
+    if (n > 0 && !splats) return GS_ERR_INVALID_ARG;
+    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
+    const Cam cam = make_cam(*camera);
+    const size_t need = bin_sort_workspace(n, k_capacity, cam.tiles_x * cam.tiles_y);
+    if (workspace_bytes < need || !workspace) return GS_ERR_WORKSPACE;
+    return from_hip(launch_bin_sort((const Splat *)splats, n, cam, k_capacity, vals, tile_ranges, schedule,
+                                    keys, k_total, workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint32_t *tile_ranges,
-                        const gs_camera *camera, const float *bg, float *image, float *final_T,
-                        uint32_t *n_contrib, void *workspace, size_t workspace_bytes, void *stream)
+                        uint32_t *schedule, const gs_camera *camera, const float *bg, float *image,
+                        float *final_T, uint32_t *n_contrib, void *stream)
 {
-    if (!camera_ok(camera) || !tile_ranges || !bg || !image || !final_T || !n_contrib)
+    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !image || !final_T || !n_contrib)
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < gs_render_fwd_workspace_bytes(camera->width, camera->height))
-        return GS_ERR_WORKSPACE;
-    return from_hip(launch_render_fwd((const Splat *)splats, vals, tile_ranges, make_cam(*camera), bg,
-                                      image, final_T, n_contrib, workspace, (hipStream_t)stream));
+    return from_hip(launch_render_fwd((const Splat *)splats, vals, tile_ranges, schedule, make_cam(*camera),
+                                      bg, image, final_T, n_contrib, (hipStream_t)stream));
 }
 
 static size_t grad2d_bytes(int64_t n) { return align_up((size_t)n * 9 * sizeof(float), 256); }
 
-size_t gs_render_bwd_workspace_bytes(int64_t n, int32_t width, int32_t height)
+size_t gs_render_bwd_workspace_bytes(int64_t n)
 {
-    if (n < 0 || width < 1 || height < 1 || width > 32768 || height > 32768) return 0;
-    return grad2d_bytes(n) + render_schedule_workspace(tiles_of(width, height));
+    if (n < 0) return 0;
+    return grad2d_bytes(n) + 256;
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
-                        const uint32_t *vals, const uint32_t *tile_ranges, const float *bg,
+                        const uint32_t *vals, const uint32_t *tile_ranges, uint32_t *schedule, const float *bg,
                         const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
                         const gs_grads *grads, void *workspace, size_t workspace_bytes, void *stream)
 {
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
-    if (!camera_ok(camera) || !tile_ranges || !bg || !final_T || !n_contrib || !dL_dimage || !grads)
+    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !final_T || !n_contrib || !dL_dimage ||
+        !grads)
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
@@ -135,16 +134,14 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     if (n > 0 && (!splats || !grads->means || !grads->log_scales || !grads->quats ||
                   !grads->opacity_logits || !grads->sh))
         return GS_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, camera->width, camera->height))
-        return GS_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n)) return GS_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const Cam cam = make_cam(*camera);
     float *grad2d = (float *)workspace;
-    void *sched = (char *)workspace + grad2d_bytes(n);
     hipError_t e = launch_fill_u32((uint32_t *)grad2d, 0u, (size_t)n * 9, s);
     if (e != hipSuccess) return GS_ERR_HIP;
-    e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, cam, bg, final_T, n_contrib,
-                          dL_dimage, n, grad2d, sched, s);
+    e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, cam, bg, final_T, n_contrib,
+                          dL_dimage, n, grad2d, s);
     if (e != hipSuccess) return GS_ERR_HIP;
     return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, grad2d, *grads, s));
 }

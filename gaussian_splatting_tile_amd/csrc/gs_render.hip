@@ -37,58 +37,28 @@ constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTMin = 1e-4f;
 
-// Tile schedule.  Per-tile work varies by two orders of magnitude (list
-// lengths 1 .. ~3000 at 1080p), and one wave per tile puts every tile of a
-// view in flight at once, so a static tile -> wave mapping leaves the busiest
-// SIMD with ~2x the mean load.  Instead a single block buckets the tiles by
-// list length (~1.4x wide buckets, longest first; empty tiles last) and the
-// blend runs as persistent waves that pull tile indices from an atomic
-// counter in that order: longest-processing-time-first list scheduling.
-constexpr int kSchedBins = 66;
-constexpr int kSchedThreads = 1024;
-
-__device__ __forceinline__ int length_bin(uint32_t L)
-{
-    if (L == 0) return 0;
-    const int lg = 31 - __clz(L);                  // floor(log2 L)
-    const int half = lg > 0 ? (int)((L >> (lg - 1)) & 1u) : 0;
-    return 1 + 2 * lg + half;
-}
-
-__global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const uint32_t *__restrict__ ranges,
-                                                                int n_tiles, uint32_t *__restrict__ order,
-                                                                uint32_t *__restrict__ head)
-{
-    __shared__ uint32_t hist[kSchedBins];
-    __shared__ uint32_t base[kSchedBins];
-    const int tid = threadIdx.x;
-    if (tid < kSchedBins) hist[tid] = 0;
-    __syncthreads();
-    for (int t = tid; t < n_tiles; t += kSchedThreads)
-        atomicAdd(&hist[length_bin(ranges[2 * t + 1] - ranges[2 * t])], 1u);
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t run = 0;
-        for (int b = kSchedBins - 1; b >= 0; b--) {
-            base[b] = run;
-            run += hist[b];
-        }
-        *head = 0;
-    }
-    __syncthreads();
-    for (int t = tid; t < n_tiles; t += kSchedThreads) {
-        const int b = length_bin(ranges[2 * t + 1] - ranges[2 * t]);
-        order[atomicAdd(&base[b], 1u)] = (uint32_t)t;
-    }
-}
-
-// Next tile for this wave, or -1 when the queue is drained.
+// Tiles come from the longest-first schedule built by the binning: order[T]
+// followed by a (head, done) counter pair per kernel.  Persistent waves take
+// the next tile index from `head`; the last wave to finish resets both
+// counters, so the next launch on the stream starts from zero again.
 __device__ __forceinline__ int next_tile(const uint32_t *order, uint32_t *head, int n_tiles)
 {
     uint32_t i = 0;
     if (threadIdx.x == 0) i = atomicAdd(head, 1u);
     i = (uint32_t)__shfl((int)i, 0, 64);
     return i < (uint32_t)n_tiles ? (int)order[i] : -1;
+}
+
+__device__ __forceinline__ void retire_wave(uint32_t *head, uint32_t *done)
+{
+    if (threadIdx.x == 0) {
+        // every wave's last head increment precedes its done increment, so the
+        // last wave to get here knows no head increment is still to come
+        if (atomicAdd(done, 1u) == gridDim.x - 1) {
+            atomicExch(head, 0u);
+            atomicExch(done, 0u);
+        }
+    }
 }
 
 // A staged record: the exponent in exp2 form,
@@ -134,9 +104,8 @@ __device__ __forceinline__ float gauss_at(const ColTerms &c, double qc, double v
 
 __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, const uint32_t *__restrict__ order, uint32_t *__restrict__ head,
-    Cam cam, float bg0, float bg1, float bg2, float *__restrict__ image, float *__restrict__ final_T,
-    uint32_t *__restrict__ n_contrib)
+    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, Cam cam, float bg0, float bg1,
+    float bg2, float *__restrict__ image, float *__restrict__ final_T, uint32_t *__restrict__ n_contrib)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double2 s_qab[kBatch];
@@ -146,7 +115,8 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
     const size_t hw = (size_t)cam.width * cam.height;
-    for (int tile = next_tile(order, head, n_tiles); tile >= 0; tile = next_tile(order, head, n_tiles)) {
+    uint32_t *head = sched + n_tiles, *done = sched + n_tiles + 1;
+    for (int tile = next_tile(sched, head, n_tiles); tile >= 0; tile = next_tile(sched, head, n_tiles)) {
         const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
         const int x = tx * kTile + (lane & 15);
         const int y0 = ty * kTile + (lane >> 4);
@@ -212,6 +182,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
             }
         }
     }
+    retire_wave(head, done);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,8 +270,8 @@ __device__ __forceinline__ int reduce_slot(int lane)
 
 __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, const uint32_t *__restrict__ order, uint32_t *__restrict__ head,
-    Cam cam, float bg0, float bg1, float bg2, const float *__restrict__ final_T,
+    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, Cam cam, float bg0, float bg1,
+    float bg2, const float *__restrict__ final_T,
     const uint32_t *__restrict__ n_contrib, const float *__restrict__ dL_dimage, int n,
     float *__restrict__ grad2d)
 {
@@ -315,7 +286,8 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const int lane = threadIdx.x;
     const size_t hw = (size_t)cam.width * cam.height;
     const int slot = reduce_slot(lane);
-    for (int tile = next_tile(order, head, n_tiles); tile >= 0; tile = next_tile(order, head, n_tiles)) {
+    uint32_t *head = sched + n_tiles + 2, *done = sched + n_tiles + 3;
+    for (int tile = next_tile(sched, head, n_tiles); tile >= 0; tile = next_tile(sched, head, n_tiles)) {
     const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
     const int x = tx * kTile + (lane & 15);
     const int y0 = ty * kTile + (lane >> 4);
@@ -424,6 +396,7 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
         __syncthreads();
     }
     }
+    retire_wave(head, done);
 }
 
 }  // namespace
@@ -441,33 +414,25 @@ int resident_blocks(K kernel, int n_tiles)
     return (int)(g < n_tiles ? g : n_tiles);
 }
 
-size_t render_schedule_workspace(int n_tiles) { return align_up(((size_t)n_tiles + 64) * sizeof(uint32_t), 256); }
-
 hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             const Cam &cam, const float bg[3], float *image, float *final_T,
-                             uint32_t *n_contrib, void *ws, hipStream_t s)
+                             uint32_t *schedule, const Cam &cam, const float bg[3], float *image,
+                             float *final_T, uint32_t *n_contrib, hipStream_t s)
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    uint32_t *order = (uint32_t *)ws;
-    uint32_t *head = order + n_tiles;
-    schedule_tiles<<<1, kSchedThreads, 0, s>>>(ranges, n_tiles, order, head);
     const int grid = resident_blocks(render_fwd_kernel, n_tiles);
-    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, order, head, cam, bg[0], bg[1], bg[2],
+    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, cam, bg[0], bg[1], bg[2],
                                               image, final_T, n_contrib);
     return hipGetLastError();
 }
 
 hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             const Cam &cam, const float bg[3], const float *final_T,
+                             uint32_t *schedule, const Cam &cam, const float bg[3], const float *final_T,
                              const uint32_t *n_contrib, const float *dL_dimage, int64_t n,
-                             float *grad2d, void *ws, hipStream_t s)
+                             float *grad2d, hipStream_t s)
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    uint32_t *order = (uint32_t *)ws;
-    uint32_t *head = order + n_tiles;
-    schedule_tiles<<<1, kSchedThreads, 0, s>>>(ranges, n_tiles, order, head);
     const int grid = resident_blocks(render_bwd_kernel, n_tiles);
-    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, order, head, cam, bg[0], bg[1], bg[2],
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, cam, bg[0], bg[1], bg[2],
                                               final_T, n_contrib, dL_dimage, (int)n, grad2d);
     return hipGetLastError();
 }

@@ -250,41 +250,60 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Splat *__restrict__ spl
     }
 }
 
-// Block sums of tiles_touched over depth-ordered Gaussians.
+// Per depth-ordered Gaussian j (256 per block): its tile rect (x0, y0 packed,
+// width) for the duplication, and the block's sum of tiles touched.
+constexpr int kScanItems = kBlock;               // Gaussians per scan / duplication block
+
 __global__ __launch_bounds__(kBlock) void scan_reduce(const Splat *__restrict__ splats,
                                                       const uint32_t *__restrict__ order,
-                                                      const uint32_t *__restrict__ m_ptr,
+                                                      const uint32_t *__restrict__ m_ptr, Cam cam,
+                                                      uint2 *__restrict__ rect_info,
+                                                      uint32_t *__restrict__ counts,
                                                       uint64_t *__restrict__ block_sums)
 {
     const uint32_t m = *m_ptr;
-    const uint32_t base = blockIdx.x * kTileItems;
-    uint64_t s = 0;
-    if (base < m) {
-        for (int r = 0; r < kIpt; r++) {
-            const uint32_t j = base + r * kBlock + threadIdx.x;
-            if (j < m) s += __float_as_uint(splats[order[j]].c.w);
-        }
+    const uint32_t j = blockIdx.x * kScanItems + threadIdx.x;
+    if (blockIdx.x * kScanItems >= m) return;
+    uint64_t c = 0;
+    if (j < m) {
+        const Splat sp = splats[order[j]];
+        const Rect rc = tile_rect(sp.a.x, sp.a.y, (float)__float_as_int(sp.a.w), (float)cam.tiles_x,
+                                  (float)cam.tiles_y);
+        const uint32_t w = (uint32_t)(rc.x1 - rc.x0);
+        c = __float_as_uint(sp.c.w);
+        rect_info[j] = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16), w);
+        counts[j] = (uint32_t)c;
     }
     uint64_t total;
-    block_exclusive_scan(s, &total);
+    block_exclusive_scan(c, &total);
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
 }
 
 // Exclusive scan of the block sums (one block); K and the clamped count.
-__global__ __launch_bounds__(kBlock) void scan_blocks(uint64_t *__restrict__ block_sums,
-                                                      const uint32_t *__restrict__ m_ptr,
-                                                      uint64_t cap, uint64_t *__restrict__ k_total,
-                                                      uint32_t *__restrict__ k_eff)
+__global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block_sums,
+                                                    const uint32_t *__restrict__ m_ptr, uint64_t cap,
+                                                    uint64_t *__restrict__ k_total,
+                                                    uint32_t *__restrict__ k_eff)
 {
+    __shared__ uint64_t wsum[16];
     const uint32_t m = *m_ptr;
-    const int nb = (int)((m + kTileItems - 1) / kTileItems);
-    const int per = (nb + kBlock - 1) / kBlock;
+    const int nb = (int)((m + kScanItems - 1) / kScanItems);
+    const int per = (nb + 1023) / 1024;
     const int b0 = threadIdx.x * per;
     uint64_t local = 0;
     for (int i = 0; i < per; i++)
         if (b0 + i < nb) local += block_sums[b0 + i];
-    uint64_t total;
-    uint64_t run = block_exclusive_scan(local, &total);
+    // block-wide exclusive scan of `local` over 1024 threads (16 waves)
+    const uint64_t inc = wave_inclusive_scan(local);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    uint64_t before = 0, total = 0;
+    for (int i = 0; i < 16; i++) {
+        if (i < w) before += wsum[i];
+        total += wsum[i];
+    }
+    uint64_t run = before + inc - local;
     for (int i = 0; i < per; i++)
         if (b0 + i < nb) {
             const uint64_t c = block_sums[b0 + i];
@@ -298,64 +317,58 @@ __global__ __launch_bounds__(kBlock) void scan_blocks(uint64_t *__restrict__ blo
 }
 
 // Each depth-ordered Gaussian writes (tile id, g) for every tile of its rect,
-// row-major, at its slots.  The block re-scans its own 2048 counts in LDS.
-// Work is balanced across the block: after the scan, the block's entries are
-// handed out 256 at a time, each thread locating its Gaussian by a binary
-// search over the block's offsets.
+// row-major, at its slots.  A block takes 256 Gaussians, scans their counts
+// in LDS, then hands the block's entries out 256 at a time: each lane finds
+// its Gaussian by binary search over the block's offsets, so the work is
+// balanced however unequal the rects are.
 __global__ __launch_bounds__(kBlock) void duplicate_keys(
-    const Splat *__restrict__ splats, const uint32_t *__restrict__ order,
-    const uint32_t *__restrict__ m_ptr, const uint64_t *__restrict__ block_offsets, Cam cam,
-    uint64_t cap, uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ vals)
+    const uint32_t *__restrict__ order, const uint32_t *__restrict__ m_ptr,
+    const uint2 *__restrict__ rect_info, const uint32_t *__restrict__ counts,
+    const uint64_t *__restrict__ block_offsets, int tiles_x, uint64_t cap,
+    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ vals)
 {
-    __shared__ uint32_t s_off[kTileItems + 1];
-    __shared__ uint32_t s_g[kTileItems];
+    __shared__ uint32_t s_off[kScanItems];
+    __shared__ uint32_t s_g[kScanItems];
+    __shared__ uint32_t s_xy[kScanItems];
+    __shared__ uint32_t s_w[kScanItems];
+    __shared__ float s_inv[kScanItems];
     const uint32_t m = *m_ptr;
-    const uint32_t base = blockIdx.x * kTileItems;
+    const uint32_t base = blockIdx.x * kScanItems;
     if (base >= m) return;
-    const uint32_t cnt_items = min((uint32_t)kTileItems, m - base);
-    // blocked layout for the scan: thread t owns items t*8 .. t*8+7
-    uint32_t c[kIpt];
-    uint32_t local = 0;
-#pragma unroll
-    for (int r = 0; r < kIpt; r++) {
-        const uint32_t li = threadIdx.x * kIpt + r;
-        c[r] = 0;
-        if (li < cnt_items) {
-            const uint32_t g = order[base + li];
-            s_g[li] = g;
-            c[r] = __float_as_uint(splats[g].c.w);
-        }
-        local += c[r];
+    const uint32_t n_items = min((uint32_t)kScanItems, m - base);
+    const uint32_t j = base + threadIdx.x;
+    uint32_t c = 0;
+    if (threadIdx.x < n_items) {
+        const uint2 ri = rect_info[j];
+        c = counts[j];
+        s_g[threadIdx.x] = order[j];
+        s_xy[threadIdx.x] = ri.x;
+        s_w[threadIdx.x] = ri.y;
+        s_inv[threadIdx.x] = 1.0f / (float)ri.y;
     }
     uint32_t total;
-    uint32_t run = block_exclusive_scan(local, &total);
-#pragma unroll
-    for (int r = 0; r < kIpt; r++) {
-        s_off[threadIdx.x * kIpt + r] = run;
-        run += c[r];
-    }
-    if (threadIdx.x == 0) s_off[kTileItems] = total;
+    s_off[threadIdx.x] = block_exclusive_scan(c, &total);
     __syncthreads();
     const uint64_t blk = block_offsets[blockIdx.x];
     for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
         const uint64_t slot = blk + e;
         if (slot >= cap) break;
-        // find li with s_off[li] <= e < s_off[li + 1]
-        int lo = 0, hi = (int)cnt_items - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= e) lo = mid; else hi = mid - 1;
-        }
-        const uint32_t g = s_g[lo];
+        // the last li with s_off[li] <= e (every listed Gaussian has >= 1 tile)
+        int lo = 0;
+#pragma unroll
+        for (int step = kScanItems / 2; step > 0; step >>= 1)
+            if (lo + step < (int)n_items && s_off[lo + step] <= e) lo += step;
         const uint32_t within = e - s_off[lo];
-        const float4 a = splats[g].a;
-        const Rect rc = tile_rect(a.x, a.y, (float)__float_as_int(a.w), (float)cam.tiles_x,
-                                  (float)cam.tiles_y);
-        const uint32_t wdt = (uint32_t)(rc.x1 - rc.x0);
-        const uint32_t ty = (uint32_t)rc.y0 + within / wdt;
-        const uint32_t tx = (uint32_t)rc.x0 + within % wdt;
-        tile_keys[slot] = ty * (uint32_t)cam.tiles_x + tx;
-        vals[slot] = g;
+        const uint32_t w = s_w[lo];
+        // within / w via the reciprocal, corrected to the exact quotient
+        uint32_t q = (uint32_t)((float)within * s_inv[lo]);
+        if (q * w > within) q--;
+        else if ((q + 1) * w <= within) q++;
+        const uint32_t xy = s_xy[lo];
+        const uint32_t ty = (xy >> 16) + q;
+        const uint32_t tx = (xy & 0xFFFFu) + (within - q * w);
+        tile_keys[slot] = ty * (uint32_t)tiles_x + tx;
+        vals[slot] = s_g[lo];
     }
 }
 
@@ -373,6 +386,52 @@ __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const uint32_t *__r
     if (i == 0 || tile_keys[i - 1] != t) ranges[2 * t] = i;
     if (i == k - 1 || tile_keys[i + 1] != t) ranges[2 * t + 1] = i + 1;
     if (keys64) keys64[i] = ((uint64_t)t << 32) | __float_as_uint(splats[vals[i]].a.z);
+}
+
+// Tile schedule for the blend kernels.  Per-tile work varies by two orders
+// of magnitude (list lengths 1 .. ~3000 at 1080p) and the blend puts every
+// tile of a view in flight at once, so a static tile -> wave mapping leaves
+// the busiest SIMD with ~2x the mean load.  One block buckets the tiles by
+// list length (~1.4x wide buckets, longest first, empty tiles last); the
+// blend kernels pull tiles from a counter in that order (longest-processing-
+// time-first list scheduling).  The schedule is order[n_tiles] followed by
+// two counter pairs (forward, backward), zeroed here and reset by the last
+// wave of each blend launch.
+constexpr int kSchedBins = 66;
+constexpr int kSchedThreads = 1024;
+
+__device__ __forceinline__ int length_bin(uint32_t L)
+{
+    if (L == 0) return 0;
+    const int lg = 31 - __clz(L);                  // floor(log2 L)
+    const int half = lg > 0 ? (int)((L >> (lg - 1)) & 1u) : 0;
+    return 1 + 2 * lg + half;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const uint32_t *__restrict__ ranges,
+                                                                int n_tiles, uint32_t *__restrict__ sched)
+{
+    __shared__ uint32_t hist[kSchedBins];
+    __shared__ uint32_t base[kSchedBins];
+    const int tid = threadIdx.x;
+    if (tid < kSchedBins) hist[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += kSchedThreads)
+        atomicAdd(&hist[length_bin(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t run = 0;
+        for (int b = kSchedBins - 1; b >= 0; b--) {
+            base[b] = run;
+            run += hist[b];
+        }
+    }
+    if (tid < 4) sched[n_tiles + tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < n_tiles; t += kSchedThreads) {
+        const int b = length_bin(ranges[2 * t + 1] - ranges[2 * t]);
+        sched[atomicAdd(&base[b], 1u)] = (uint32_t)t;
+    }
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, uint32_t value, size_t count)
@@ -413,9 +472,11 @@ int bits_for(uint32_t count)
 
 struct BinWs {
     uint32_t *dk[2], *dv[2];           // depth sort ping-pong [n]
-    uint64_t *block_sums;              // [ceil(n / 2048)]
+    uint2 *rect_info;                  // [n] per depth-ordered Gaussian
+    uint32_t *counts;                  // [n] tiles touched, depth order
+    uint64_t *block_sums;              // [ceil(n / 256)]
     uint32_t *tk[2], *tv;              // tile keys ping-pong, values scratch [cap]
-    uint32_t *counts;                  // [256 * kMaxGrid]
+    uint32_t *digit_counts;            // [256 * kMaxGrid]
     uint32_t *digit_total;             // [256]
     uint32_t *counters;                // [4]
 };
@@ -429,11 +490,13 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     w.dv[0] = c.take<uint32_t>(nn);
     w.dk[1] = c.take<uint32_t>(nn);
     w.dv[1] = c.take<uint32_t>(nn);
-    w.block_sums = c.take<uint64_t>((nn + kTileItems - 1) / kTileItems);
+    w.rect_info = c.take<uint2>(nn);
+    w.counts = c.take<uint32_t>(nn);
+    w.block_sums = c.take<uint64_t>((nn + kScanItems - 1) / kScanItems);
     w.tk[0] = c.take<uint32_t>(kk);
     w.tk[1] = c.take<uint32_t>(kk);
     w.tv = c.take<uint32_t>(kk);
-    w.counts = c.take<uint32_t>(256 * kMaxGrid);
+    w.digit_counts = c.take<uint32_t>(256 * kMaxGrid);
     w.digit_total = c.take<uint32_t>(256);
     w.counters = c.take<uint32_t>(4);
     if (ws) *ws = w;
@@ -445,10 +508,10 @@ hipError_t radix_pass(const uint32_t *kin, const uint32_t *vin, uint32_t *kout, 
                       int bits, int drop, const BinWs &w, hipStream_t s)
 {
     const int G = radix_grid(max_items);
-    radix_upsweep<<<G, kBlock, 0, s>>>(kin, n_ptr, shift, bits, drop, w.counts);
-    radix_scan<<<256, kBlock, 0, s>>>(w.counts, G, w.digit_total);
+    radix_upsweep<<<G, kBlock, 0, s>>>(kin, n_ptr, shift, bits, drop, w.digit_counts);
+    radix_scan<<<256, kBlock, 0, s>>>(w.digit_counts, G, w.digit_total);
     radix_downsweep<<<G, kBlock, 0, s>>>(kin, vin, kout, vout, n_ptr, n_out_ptr, shift, bits, drop,
-                                         w.counts, w.digit_total);
+                                         w.digit_counts, w.digit_total);
     return hipGetLastError();
 }
 
@@ -468,8 +531,8 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_
 }
 
 hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int64_t cap,
-                           uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys, uint64_t *k_total,
-                           void *ws_ptr, size_t ws_bytes, hipStream_t s)
+                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint64_t *keys,
+                           uint64_t *k_total, void *ws_ptr, size_t ws_bytes, hipStream_t s)
 {
     (void)ws_bytes;
     BinWs w;
@@ -484,34 +547,33 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
                                                                    tile_ranges, n_ranges, w.counters);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    // 1. depth: 4 x 8-bit passes; the first drops the culled Gaussians
-    int cur = 0;
-    for (int pass = 0; pass < 4; pass++) {
-        const uint32_t *n_in = pass == 0 ? &w.counters[0] : &w.counters[1];
-        e = radix_pass(w.dk[cur], w.dv[cur], w.dk[cur ^ 1], w.dv[cur ^ 1], n_in, &w.counters[1], n,
-                       8 * pass, 8, pass == 0, w, s);
-        if (e != hipSuccess) return e;
-        cur ^= 1;
-    }
-    const uint32_t *order = w.dv[cur];
+    if (n > 0) {
+        // 1. depth: 4 x 8-bit passes; the first drops the culled Gaussians
+        int cur = 0;
+        for (int pass = 0; pass < 4; pass++) {
+            const uint32_t *n_in = pass == 0 ? &w.counters[0] : &w.counters[1];
+            e = radix_pass(w.dk[cur], w.dv[cur], w.dk[cur ^ 1], w.dv[cur ^ 1], n_in, &w.counters[1], n,
+                           8 * pass, 8, pass == 0, w, s);
+            if (e != hipSuccess) return e;
+            cur ^= 1;
+        }
+        const uint32_t *order = w.dv[cur];
 
-    // 2. slots and duplication (K in counters[2] after clamping to cap)
-    const uint32_t nblk = (n + kTileItems - 1) / kTileItems;
-    if (nblk > 0) {
-        scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], w.block_sums);
-        scan_blocks<<<1, kBlock, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total,
-                                         &w.counters[2]);
+        // 2. slots and duplication (K clamped to the capacity in counters[2])
+        const uint32_t nblk = (n + kScanItems - 1) / kScanItems;
+        scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], cam, w.rect_info, w.counts,
+                                            w.block_sums);
+        scan_blocks<<<1, 1024, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total, &w.counters[2]);
         // 3. tile passes: choose the buffers so the last pass lands in `vals`
         const int tbits = bits_for(n_tiles);
         const int passes = tbits == 0 ? 0 : (tbits + 7) / 8;
         uint32_t *kbuf[2] = {w.tk[0], w.tk[1]};
         uint32_t *vbuf[2];
-        // pass p reads (k[p&1], v[p&1]) and writes (k[(p+1)&1], v[(p+1)&1]);
-        // the final destination must be `vals`
+        // pass p reads (k[p&1], v[p&1]) and writes (k[(p+1)&1], v[(p+1)&1])
         if (passes % 2 == 0) { vbuf[0] = vals; vbuf[1] = w.tv; }
         else { vbuf[0] = w.tv; vbuf[1] = vals; }
-        duplicate_keys<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], w.block_sums, cam,
-                                               (uint64_t)cap, kbuf[0], vbuf[0]);
+        duplicate_keys<<<nblk, kBlock, 0, s>>>(order, &w.counters[1], w.rect_info, w.counts, w.block_sums,
+                                               cam.tiles_x, (uint64_t)cap, kbuf[0], vbuf[0]);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         int shift = 0;
         for (int p = 0; p < passes; p++) {
@@ -521,11 +583,8 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
             if (e != hipSuccess) return e;
             shift += bits;
         }
-        // with zero passes (one tile) the duplicated order is already final
+        // (with one tile there is no pass: the depth order is already final)
         const uint32_t *sorted_tiles = kbuf[passes & 1];
-        if (passes == 0) {
-            // vbuf[0] == vals when passes is even
-        }
         // 4. ranges (and the optional 64-bit keys)
         const uint64_t kgrid = ((uint64_t)cap + kBlock - 1) / kBlock;
         if (kgrid > 0)
@@ -535,8 +594,12 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
         // no Gaussians: K = 0
         fill_u32_kernel<<<1, kBlock, 0, s>>>((uint32_t *)k_total, 0u, 2);
     }
+    // 5. longest-first tile schedule for the blend kernels
+    schedule_tiles<<<1, kSchedThreads, 0, s>>>(tile_ranges, (int)n_tiles, schedule);
     return hipGetLastError();
 }
+
+size_t schedule_words(int n_tiles) { return (size_t)n_tiles + 4; }
 
 size_t active_mask_workspace(int64_t n)
 {

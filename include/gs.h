@@ -140,6 +140,10 @@ gs_status gs_project(const gs_gaussians *gaussians /* host struct */,
  * k_capacity and the camera's tile count. */
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles);
 
+/* Number of 32-bit words of the tile schedule for a width x height image:
+ * one per 16x16 tile plus four queue counters. */
+size_t gs_schedule_words(int32_t width, int32_t height);
+
 /* Tile binning and depth sort of one view.
  * Input: splats[n] from gs_project with the same camera.
  * Output:
@@ -147,6 +151,10 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tile
  *   tile_ranges[2*n_tiles]  [start, end) of each tile's entries in vals,
  *                           (0, 0) for an empty tile; tiles are row-major,
  *                           n_tiles = ceil(W/16) * ceil(H/16)
+ *   schedule[gs_schedule_words(W, H)]  the tiles ordered longest list first
+ *                           (the order in which the blend kernels take
+ *                           them) and zeroed queue counters; pass it to
+ *                           gs_render_fwd / gs_render_bwd
  *   keys[k_capacity]        (optional, NULL to skip) the 64-bit sort keys
  *                           tile << 32 | bits of the fp32 depth
  *   k_total                 device uint64: K, the number of entries
@@ -159,33 +167,30 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tile
  * Errors: GS_ERR_INVALID_ARG (NULL pointers, bad sizes), GS_ERR_WORKSPACE. */
 gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
                       const gs_camera *camera /* host */, int64_t k_capacity,
-                      uint32_t *vals, uint32_t *tile_ranges, uint64_t *keys,
-                      uint64_t *k_total, void *workspace, size_t workspace_bytes,
-                      void *stream);
-
-/* Workspace for gs_render_fwd, in bytes, for an image of width x height
- * (the tile schedule: one index per 16x16 tile). */
-size_t gs_render_fwd_workspace_bytes(int32_t width, int32_t height);
+                      uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule,
+                      uint64_t *keys, uint64_t *k_total, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* Forward compositing of every pixel.
- * Inputs: splats (gs_project), vals and tile_ranges (gs_bin_sort),
+ * Inputs: splats (gs_project), vals, tile_ranges and schedule (gs_bin_sort),
  * bg: host float[3] background colour.
  * Outputs: image[3][H][W] (fp32, channel planes), final_T[H][W] (the
  * transmittance left after the pixel's last entry), n_contrib[H][W]
  * (1 + position in the tile's list of the last composited entry, 0 if
  * none).  final_T and n_contrib are what gs_render_bwd needs.
- * Tiles are processed longest list first by persistent waves; the result
- * does not depend on the order.
- * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
+ * Tiles are processed by persistent waves in the schedule's order; the
+ * result does not depend on it.  The call uses the schedule's forward queue
+ * counters and leaves them reset, so calls sharing a schedule must be
+ * ordered on one stream.
+ * Errors: GS_ERR_INVALID_ARG. */
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
-                        const uint32_t *tile_ranges, const gs_camera *camera,
-                        const float *bg /* host [3] */, float *image,
-                        float *final_T, uint32_t *n_contrib, void *workspace,
-                        size_t workspace_bytes, void *stream);
+                        const uint32_t *tile_ranges, uint32_t *schedule,
+                        const gs_camera *camera, const float *bg /* host [3] */,
+                        float *image, float *final_T, uint32_t *n_contrib,
+                        void *stream);
 
-/* Workspace for gs_render_bwd, in bytes: per-Gaussian 2D gradients for n
- * Gaussians and the tile schedule of a width x height image. */
-size_t gs_render_bwd_workspace_bytes(int64_t n, int32_t width, int32_t height);
+/* Workspace for gs_render_bwd, in bytes (per-Gaussian 2D gradients). */
+size_t gs_render_bwd_workspace_bytes(int64_t n);
 
 /* Backward of one view: given dL/dimage[3][H][W], accumulates (+=) into
  * grads the gradient of L with respect to the raw parameters.  Every
@@ -194,12 +199,14 @@ size_t gs_render_bwd_workspace_bytes(int64_t n, int32_t width, int32_t height);
  * the forward took it; depth gets no gradient.  The inputs must be those of
  * the matching forward call.  Per (Gaussian, tile) the 9 screen-space
  * gradients are reduced across the tile's pixels on chip before one set of
- * atomic adds, so the low bits of the result depend on scheduling.
+ * atomic adds, so the low bits of the result depend on scheduling.  It uses
+ * the schedule's backward queue counters (see gs_render_fwd).
  * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE. */
 gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
                         const gs_camera *camera /* host */,
                         const gs_splat *splats, const uint32_t *vals,
-                        const uint32_t *tile_ranges, const float *bg /* host [3] */,
+                        const uint32_t *tile_ranges, uint32_t *schedule,
+                        const float *bg /* host [3] */,
                         const float *final_T, const uint32_t *n_contrib,
                         const float *dL_dimage, const gs_grads *grads /* host struct */,
                         void *workspace, size_t workspace_bytes, void *stream);

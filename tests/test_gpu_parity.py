@@ -131,6 +131,29 @@ def test_forward_is_deterministic():
     b2, _ = run_view(sc, 0)
     assert torch.equal(b1.image, b2.image) and torch.equal(b1.final_T, b2.final_T)
     assert torch.equal(b1.n_contrib, b2.n_contrib) and torch.equal(b1.vals, b2.vals)
+    # the schedule's queue counters reset themselves: blending again from the
+    # same schedule (three times, with a backward in between) gives the same image
+    img = b1.image.clone()
+    g, act, gs = b1._keep
+    grads = dict(means=torch.zeros((3, sc.n), device="cuda"), log_scales=torch.zeros((3, sc.n), device="cuda"),
+                 quats=torch.zeros((4, sc.n), device="cuda"), opacity_logits=torch.zeros(sc.n, device="cuda"),
+                 sh=torch.zeros((16, 3, sc.n), device="cuda"))
+    ws = torch.empty(B.render_bwd_workspace_bytes(sc.n), dtype=torch.uint8, device="cuda")
+    for it in range(3):
+        b1.image.zero_()
+        B.render_fwd(b1.splats, b1.vals, b1.ranges, b1.schedule, b1.camc, (0.0, 0.0, 0.0), b1.image,
+                     b1.final_T, b1.n_contrib)
+        if it == 1:
+            b1.backward(gs, torch.ones_like(b1.image), grads, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(b1.image, img), it
+    n_t = b1.ranges.shape[0]
+    assert torch.all(b1.schedule[n_t:] == 0)
+    order = b1.schedule[:n_t].cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(n_t))
+    lens = (b1.ranges[:, 1] - b1.ranges[:, 0]).cpu().numpy()[order]
+    # longest first, to within one ~1.4x length bucket
+    assert np.all(lens[1:] <= np.maximum(lens[:-1], 1) * 1.5 + 1)
 
 
 def test_invalid_arguments_are_rejected():
@@ -150,5 +173,6 @@ def test_invalid_arguments_are_rejected():
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(B.GsError, match="workspace"):
         B.bin_sort(out, 10, cam, 100, torch.empty(100, dtype=torch.int32, device="cuda"),
-                   torch.empty(128, dtype=torch.int32, device="cuda"), None,
+                   torch.empty(128, dtype=torch.int32, device="cuda"),
+                   torch.empty(B.schedule_words(128, 128), dtype=torch.int32, device="cuda"), None,
                    torch.empty(1, dtype=torch.int64, device="cuda"), small)
