@@ -17,6 +17,15 @@
 //   took T below 1e-4 was composited);
 //   C = sum alpha_i T_i rgb_i,  image = C + T_final bg.
 //
+// Before a batch is walked, each lane tests the record it staged against the
+// whole tile: if the minimum of the conic's quadratic form over the box of
+// the tile's pixel centres still leaves o exp(power) below 1/255 (with a
+// margin far above the arithmetic error), no pixel of the tile can composite
+// it, and the record is dropped from the batch by a ballot compaction.  The
+// binning's square 3-sigma rects make ~40 % of a tile's list such records.
+// Outputs are unchanged: a dropped record would have been skipped by every
+// pixel, and list positions (n_contrib) are kept with each staged record.
+//
 // The exponent's quadratic form is evaluated in fp64: for thin Gaussians
 // seen far along their major axis its three terms reach ~1e5 and cancel to a
 // result of order 1, so any fp32 evaluation carries an exponent error near
@@ -61,45 +70,107 @@ __device__ __forceinline__ void retire_wave(uint32_t *head, uint32_t *done)
     }
 }
 
-// A staged record: the exponent in exp2 form,
-//   exp(power) = exp2(qa dx^2 + qb dx dy + qc dy^2),  (qa, qb, qc) = -log2(e) (a/2, b, c/2),
-// kept in fp64 together with the mean; opacity and colour stay fp32.
-struct Stage {
-    double2 uv;      // u, v
-    double2 qab;     // qa, qb
-    double qc;
-    float4 orgb;     // opacity, r, g, b
-};
-
-__device__ __forceinline__ void stage_record(const Splat &s, double2 &uv, double2 &qab, double &qc, float4 &orgb)
+// A staged record: the exponent in exp2 form with the opacity folded in,
+//   o exp(power) = exp2(log2 o + qa dx^2 + qb dx dy + qc dy^2),
+//   (qa, qb, qc) = -log2(e) (a/2, b, c/2),
+// kept in fp64 together with the mean; the colour stays fp32.
+__device__ __forceinline__ void stage_record(const Splat &s, double2 &uv, double4 &q, float4 &rgb)
 {
     const double l = -(double)kLog2e;
     uv = make_double2((double)s.a.x, (double)s.a.y);
-    qab = make_double2(0.5 * l * (double)s.b.x, l * (double)s.b.y);
-    qc = 0.5 * l * (double)s.b.z;
-    orgb = make_float4(s.b.w, s.c.x, s.c.y, s.c.z);
+    q = make_double4(0.5 * l * (double)s.b.x, l * (double)s.b.y, 0.5 * l * (double)s.b.z,
+                     (double)__builtin_amdgcn_logf(s.b.w));
+    rgb = make_float4(s.c.x, s.c.y, s.c.z, s.b.w);
+}
+
+// Can any pixel centre of the tile whose top-left pixel is (x0, y0) reach
+// alpha >= 1/255?  The minimum of Q(d) = a dx^2 + 2 b dx dy + c dy^2 over the
+// box of pixel centres is at the mean if it lies inside, else on an edge,
+// where Q is a 1D quadratic minimised in closed form.  A record is dropped
+// only when o exp(-Q_min / 2) is below 1/255 by a relative margin of 1e-3,
+// far above the error of the per-pixel evaluation.
+// The edge minimiser is located in fp32 and clamped into the box; Q is then
+// evaluated there in fp64.  Q at any point of the box is >= its minimum, and
+// the location error only adds c * O(ulp)^2 (Q is stationary there), far
+// inside the margin.
+__device__ __forceinline__ bool may_contribute(float fu, float fv, const float4 &conic_o, int x0, int y0)
+{
+    const double a = conic_o.x, b = conic_o.y, c = conic_o.z;
+    const double dxl = (double)x0 + 0.5 - (double)fu, dyl = (double)y0 + 0.5 - (double)fv;
+    if (dxl <= 0.0 && dxl + 15.0 >= 0.0 && dyl <= 0.0 && dyl + 15.0 >= 0.0) return true;
+    const float rb_c = -conic_o.y / conic_o.z, rb_a = -conic_o.y / conic_o.x;
+    const float fxl = (float)dxl, fyl = (float)dyl;
+    double best = 1e300;
+#pragma unroll 1
+    for (int e = 0; e < 4; e++) {
+        double dx, dy;
+        if (e < 2) {                   // edges x = const: minimise over dy
+            dx = dxl + 15.0 * e;
+            dy = (double)fminf(fmaxf(rb_c * (float)dx, fyl), fyl + 15.0f);
+            dy = fmin(fmax(dy, dyl), dyl + 15.0);
+        } else {                       // edges y = const: minimise over dx
+            dy = dyl + 15.0 * (e - 2);
+            dx = (double)fminf(fmaxf(rb_a * (float)dy, fxl), fxl + 15.0f);
+            dx = fmin(fmax(dx, dxl), dxl + 15.0);
+        }
+        best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);
+    }
+    const float amax = conic_o.w * __expf((float)(-0.5 * best));
+    return amax >= kAlphaMin * (1.0f - 1e-3f);
 }
 
 // Per record and column: the dx terms shared by the lane's four pixels.
-struct ColTerms { double dx, adx2, bdx; };
+struct ColTerms { double dx, a0, bdx; };
 
-__device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double2 &qab, double px)
+__device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double4 &q, double px)
 {
 #pragma clang fp contract(off)
     ColTerms c;
     c.dx = uv.x - px;                 // exact: difference of two floats
-    c.adx2 = (qab.x * c.dx) * c.dx;
-    c.bdx = qab.y * c.dx;
+    c.a0 = (q.x * c.dx) * c.dx + q.w;
+    c.bdx = q.y * c.dx;
     return c;
 }
 
-// exp(power) at one pixel of the column; dy returned for the gradients.
-__device__ __forceinline__ float gauss_at(const ColTerms &c, double qc, double v, double py, double &dy)
+// o exp(power) at one pixel of the column; dy returned for the gradients.
+__device__ __forceinline__ float alpha_raw(const ColTerms &c, double qc, double v, double py, double &dy)
 {
 #pragma clang fp contract(off)
     dy = v - py;
-    const double e = fma(dy, fma(qc, dy, c.bdx), c.adx2);
+    const double e = fma(dy, fma(qc, dy, c.bdx), c.a0);
     return __builtin_amdgcn_exp2f((float)e);
+}
+
+// Stage one record per lane into LDS, dropping those that cannot reach any
+// pixel of the tile; returns the number kept.  Kept records keep their order.
+template <bool kBwd>
+__device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
+                                           uint32_t b0, uint32_t end, uint32_t start, int x0, int y0,
+                                           double2 *s_uv, double4 *s_q, float4 *s_rgb, uint32_t *s_pos,
+                                           float4 *s_conic, uint32_t *s_g)
+{
+    const int lane = threadIdx.x;
+    const uint32_t m = b0 + lane;
+    bool keep = false;
+    uint32_t g = 0;
+    if (m < end) {
+        g = vals[m];
+        const float4 sa = splats[g].a;
+        keep = may_contribute(sa.x, sa.y, splats[g].b, x0, y0);
+    }
+    const uint64_t mask = __ballot(keep);
+    if (keep) {
+        const Splat s = splats[g];
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int slot = __popcll(mask & lt);
+        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
+        s_pos[slot] = m - start;
+        if (kBwd) {
+            s_conic[slot] = s.b;
+            s_g[slot] = g;
+        }
+    }
+    return __popcll(mask);
 }
 
 __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
@@ -108,9 +179,9 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
     float bg2, float *__restrict__ image, float *__restrict__ final_T, uint32_t *__restrict__ n_contrib)
 {
     __shared__ double2 s_uv[kBatch];
-    __shared__ double2 s_qab[kBatch];
-    __shared__ double s_qc[kBatch];
-    __shared__ float4 s_orgb[kBatch];
+    __shared__ double4 s_q[kBatch];
+    __shared__ float4 s_rgb[kBatch];
+    __shared__ uint32_t s_pos[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
@@ -139,28 +210,25 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
         const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
-            const uint32_t m = b0 + lane;
-            if (m < end)
-                stage_record(splats[vals[m]], s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
+            const int nb = stage_batch<false>(splats, vals, b0, end, start, tx * kTile, ty * kTile, s_uv, s_q,
+                                              s_rgb, s_pos, nullptr, nullptr);
             __syncthreads();
-            const int nb = (int)min((uint32_t)kBatch, end - b0);
-            const uint32_t pos0 = b0 - start + 1u;
             for (int k = 0; k < nb; k++) {
                 const double2 uv = s_uv[k];
-                const double qc = s_qc[k];
-                const float4 orgb = s_orgb[k];
-                const ColTerms ct = col_terms(uv, s_qab[k], px);
-                const uint32_t pos = pos0 + (uint32_t)k;
+                const double4 q = s_q[k];
+                const float4 rgb = s_rgb[k];
+                const uint32_t pos = s_pos[k] + 1u;
+                const ColTerms ct = col_terms(uv, q, px);
 #pragma unroll
                 for (int r = 0; r < kPx; r++) {
                     double dy;
-                    const float raw = orgb.x * gauss_at(ct, qc, uv.y, py[r], dy);
+                    const float raw = alpha_raw(ct, q.z, uv.y, py[r], dy);
                     const float alpha = fminf(kAlphaMax, raw);
-                    const bool take = T[r] >= kTMin && alpha >= kAlphaMin;
+                    const bool take = T[r] >= kTMin && raw >= kAlphaMin;
                     const float w = take ? alpha * T[r] : 0.0f;
-                    c0[r] = fmaf(orgb.y, w, c0[r]);
-                    c1[r] = fmaf(orgb.z, w, c1[r]);
-                    c2[r] = fmaf(orgb.w, w, c2[r]);
+                    c0[r] = fmaf(rgb.x, w, c0[r]);
+                    c1[r] = fmaf(rgb.y, w, c1[r]);
+                    c2[r] = fmaf(rgb.z, w, c2[r]);
                     T[r] = T[r] - w;
                     last[r] = take ? pos : last[r];
                 }
@@ -276,9 +344,9 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     float *__restrict__ grad2d)
 {
     __shared__ double2 s_uv[kBatch];
-    __shared__ double2 s_qab[kBatch];
-    __shared__ double s_qc[kBatch];
-    __shared__ float4 s_orgb[kBatch];
+    __shared__ double4 s_q[kBatch];
+    __shared__ float4 s_rgb[kBatch];
+    __shared__ uint32_t s_pos[kBatch];
     __shared__ float4 s_conic[kBatch];
     __shared__ uint32_t s_g[kBatch];
 
@@ -322,40 +390,33 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const uint32_t stop = start + lmax;           // entries at or past this are unused
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
         const uint32_t bbeg = (uint32_t)max((int64_t)start, bend - kBatch);
-        const int nb = (int)(bend - bbeg);
-        if (lane < nb) {
-            const uint32_t g = vals[bbeg + lane];
-            const Splat s = splats[g];
-            stage_record(s, s_uv[lane], s_qab[lane], s_qc[lane], s_orgb[lane]);
-            s_conic[lane] = s.b;
-            s_g[lane] = g;
-        }
+        const int nb = stage_batch<true>(splats, vals, bbeg, (uint32_t)bend, start, tx * kTile, ty * kTile,
+                                         s_uv, s_q, s_rgb, s_pos, s_conic, s_g);
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
-            const uint32_t pos = bbeg + (uint32_t)k - start;    // list position
+            const uint32_t pos = s_pos[k];                     // list position
             const double2 uv = s_uv[k];
-            const double qc = s_qc[k];
-            const float4 orgb = s_orgb[k];
-            const ColTerms ct = col_terms(uv, s_qab[k], px);
-            float gexp[kPx], dys[kPx];
+            const double4 q = s_q[k];
+            const ColTerms ct = col_terms(uv, q, px);
+            float raws[kPx], dys[kPx];
             bool take[kPx];
             bool any = false;
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
                 double dy;
-                gexp[r] = gauss_at(ct, qc, uv.y, py[r], dy);
+                raws[r] = alpha_raw(ct, q.z, uv.y, py[r], dy);
                 dys[r] = (float)dy;
-                const float alpha = fminf(kAlphaMax, orgb.x * gexp[r]);
-                take[r] = pos < last[r] && alpha >= kAlphaMin;
+                take[r] = pos < last[r] && raws[r] >= kAlphaMin;
                 any = any || take[r];
             }
             if (__ballot(any) == 0) continue;
-            const float4 col = make_float4(orgb.y, orgb.z, orgb.w, 0.0f);
+            const float4 col = s_rgb[k];
+            const float inv_o = 1.0f / col.w;
             float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f, S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
                 if (!take[r]) continue;
-                const float raw = orgb.x * gexp[r];
+                const float raw = raws[r];
                 const float alpha = fminf(kAlphaMax, raw);
                 const float one_m = 1.0f - alpha;
                 T[r] = T[r] * __builtin_amdgcn_rcpf(one_m);
@@ -369,7 +430,7 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
                 A1[r] = alpha * col.y + one_m * A1[r];
                 A2[r] = alpha * col.z + one_m * A2[r];
                 if (raw < kAlphaMax) {
-                    go = fmaf(dla, gexp[r], go);
+                    go = fmaf(dla, raw * inv_o, go);
                     const float dp = dla * alpha;
                     const float t = dp * dys[r];
                     S0 += dp;
