@@ -42,7 +42,7 @@ class GsError(RuntimeError):
 
 
 _lib = None
-SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bin_sort",
+SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_active_mask_workspace_bytes",
            "gs_active_mask", "gs_status_string", "gs_version")
@@ -69,12 +69,14 @@ def lib():
     L.gs_bin_sort_workspace_bytes.restype = sz
     L.gs_schedule_words.argtypes = [C.c_int32, C.c_int32]
     L.gs_schedule_words.restype = sz
-    L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gs_bwd_index_words.argtypes = [i64, i64]
+    L.gs_bwd_index_words.restype = sz
+    L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
-    L.gs_render_bwd_workspace_bytes.argtypes = [i64]
+    L.gs_render_bwd_workspace_bytes.argtypes = [i64, i64]
     L.gs_render_bwd_workspace_bytes.restype = sz
-    L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, vp, vp,
-                                vp, C.POINTER(GsGrads), vp, sz, vp]
+    L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, i64, vp, vp,
+                                vp, vp, C.POINTER(GsGrads), vp, sz, vp]
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
     L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
@@ -152,11 +154,15 @@ def schedule_words(width: int, height: int) -> int:
     return int(lib().gs_schedule_words(width, height))
 
 
-def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, keys, k_total, workspace,
-             stream=None):
+def bwd_index_words(n: int, k_capacity: int) -> int:
+    return int(lib().gs_bwd_index_words(n, k_capacity))
+
+
+def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, bwd_index, keys, k_total,
+             workspace, stream=None):
     _check(lib().gs_bin_sort(_ptr(splats), int(n), C.byref(cam), int(k_capacity), _ptr(vals),
-                             _ptr(tile_ranges), _ptr(schedule), _ptr(keys), _ptr(k_total), _ptr(workspace),
-                             _nbytes(workspace), _stream(stream)), "gs_bin_sort")
+                             _ptr(tile_ranges), _ptr(schedule), _ptr(bwd_index), _ptr(keys), _ptr(k_total),
+                             _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_bin_sort")
 
 
 def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[float], image, final_T,
@@ -167,17 +173,17 @@ def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[
                                _stream(stream)), "gs_render_fwd")
 
 
-def render_bwd_workspace_bytes(n: int) -> int:
-    return int(lib().gs_render_bwd_workspace_bytes(n))
+def render_bwd_workspace_bytes(n: int, k_capacity: int) -> int:
+    return int(lib().gs_render_bwd_workspace_bytes(n, k_capacity))
 
 
-def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, schedule, bg, final_T, n_contrib,
-               dL_dimage, grads: Dict[str, torch.Tensor], workspace, stream=None):
+def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg,
+               final_T, n_contrib, dL_dimage, grads: Dict[str, torch.Tensor], workspace, stream=None):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
                  _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
     _check(lib().gs_render_bwd(C.byref(gs), C.byref(cam), _ptr(splats), _ptr(vals), _ptr(tile_ranges),
-                               _ptr(schedule), C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
+                               _ptr(schedule), _ptr(bwd_index), int(k_capacity), C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
                                C.byref(gr), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)),
            "gs_render_bwd")
@@ -197,7 +203,8 @@ def active_mask(scores, n, keep, mask, workspace, stream=None):
 class ViewBuffers:
     """Device buffers for rendering one camera with a fixed key capacity."""
 
-    def __init__(self, n: int, cam, k_capacity: int, device="cuda", with_keys: bool = False):
+    def __init__(self, n: int, cam, k_capacity: int, device="cuda", with_keys: bool = False,
+                 with_backward: bool = True):
         self.n = n
         self.cam = cam
         self.camc = camera_struct(cam)
@@ -216,14 +223,19 @@ class ViewBuffers:
         self.final_T = torch.empty((H, W), dtype=torch.float32, device=device)
         self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=device)
         self.schedule = torch.empty(schedule_words(W, H), dtype=torch.int32, device=device)
+        self.bwd_index = (torch.empty(bwd_index_words(n, self.k_capacity), dtype=torch.int32, device=device)
+                          if with_backward else None)
 
     def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
         project(gs, self.camc, self.splats, stream)
         bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.schedule,
-                 self.keys, self.k_total, self.ws, stream)
+                 self.bwd_index, self.keys, self.k_total, self.ws, stream)
         render_fwd(self.splats, self.vals, self.ranges, self.schedule, self.camc, bg, self.image, self.final_T,
                    self.n_contrib, stream)
 
+    def backward_workspace(self, device="cuda"):
+        return torch.empty(render_bwd_workspace_bytes(self.n, self.k_capacity), dtype=torch.uint8, device=device)
+
     def backward(self, gs: GsGaussians, dL_dimage, grads, workspace, bg=(0.0, 0.0, 0.0), stream=None):
-        render_bwd(gs, self.camc, self.splats, self.vals, self.ranges, self.schedule, bg, self.final_T,
-                   self.n_contrib, dL_dimage, grads, workspace, stream)
+        render_bwd(gs, self.camc, self.splats, self.vals, self.ranges, self.schedule, self.bwd_index,
+                   self.k_capacity, bg, self.final_T, self.n_contrib, dL_dimage, grads, workspace, stream)

@@ -82,9 +82,16 @@ size_t gs_schedule_words(int32_t width, int32_t height)
     return schedule_words(tiles_of(width, height));
 }
 
+size_t gs_bwd_index_words(int64_t n, int64_t k_capacity)
+{
+    if (n < 0 || k_capacity < 0) return 0;
+    return (size_t)k_capacity + (size_t)n;
+}
+
 gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
-                      uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint64_t *keys,
-                      uint64_t *k_total, void *workspace, size_t workspace_bytes, void *stream)
+                      uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
+                      uint64_t *keys, uint64_t *k_total, void *workspace, size_t workspace_bytes,
+                      void *stream)
 {
     if (n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
         return GS_ERR_INVALID_ARG;
@@ -95,7 +102,8 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera
     const size_t need = bin_sort_workspace(n, k_capacity, cam.tiles_x * cam.tiles_y);
     if (workspace_bytes < need || !workspace) return GS_ERR_WORKSPACE;
     return from_hip(launch_bin_sort((const Splat *)splats, n, cam, k_capacity, vals, tile_ranges, schedule,
-                                    keys, k_total, workspace, workspace_bytes, (hipStream_t)stream));
+                                    bwd_index, keys, k_total, workspace, workspace_bytes,
+                                    (hipStream_t)stream));
 }
 
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint32_t *tile_ranges,
@@ -110,40 +118,43 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
                                       bg, image, final_T, n_contrib, (hipStream_t)stream));
 }
 
-static size_t grad2d_bytes(int64_t n) { return align_up((size_t)n * 9 * sizeof(float), 256); }
-
-size_t gs_render_bwd_workspace_bytes(int64_t n)
+size_t gs_render_bwd_workspace_bytes(int64_t n, int64_t k_capacity)
 {
-    if (n < 0) return 0;
-    return grad2d_bytes(n) + 256;
+    if (n < 0 || k_capacity < 0) return 0;
+    return align_up((size_t)k_capacity * 9 * sizeof(float), 256) + align_up((size_t)n * 9 * sizeof(float), 256) +
+           256;
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
-                        const uint32_t *vals, const uint32_t *tile_ranges, uint32_t *schedule, const float *bg,
-                        const float *final_T, const uint32_t *n_contrib, const float *dL_dimage,
-                        const gs_grads *grads, void *workspace, size_t workspace_bytes, void *stream)
+                        const uint32_t *vals, const uint32_t *tile_ranges, uint32_t *schedule,
+                        const uint32_t *bwd_index, int64_t k_capacity, const float *bg, const float *final_T,
+                        const uint32_t *n_contrib, const float *dL_dimage, const gs_grads *grads,
+                        void *workspace, size_t workspace_bytes, void *stream)
 {
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
     if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !final_T || !n_contrib || !dL_dimage ||
-        !grads)
+        !grads || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
     const int64_t n = gaussians->n;
-    if (n > 0 && (!splats || !grads->means || !grads->log_scales || !grads->quats ||
+    if (n > 0 && (!splats || !bwd_index || !grads->means || !grads->log_scales || !grads->quats ||
                   !grads->opacity_logits || !grads->sh))
         return GS_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n)) return GS_ERR_WORKSPACE;
+    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, k_capacity)) return GS_ERR_WORKSPACE;
+    if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
     const Cam cam = make_cam(*camera);
-    float *grad2d = (float *)workspace;
-    hipError_t e = launch_fill_u32((uint32_t *)grad2d, 0u, (size_t)n * 9, s);
+    // every entry's nine partial sums are written by the blend backward
+    float *partial = (float *)workspace;
+    hipError_t e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, bwd_index, cam, bg, final_T,
+                          n_contrib, dL_dimage, partial, s);
     if (e != hipSuccess) return GS_ERR_HIP;
-    e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, cam, bg, final_T, n_contrib,
-                          dL_dimage, n, grad2d, s);
-    if (e != hipSuccess) return GS_ERR_HIP;
-    return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, grad2d, *grads, s));
+    float *g2 = (float *)((char *)workspace + align_up((size_t)k_capacity * 9 * sizeof(float), 256));
+    return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, partial, bwd_index + k_capacity,
+                                       (uint64_t)k_capacity, g2, *grads, s));
 }
 
 size_t gs_active_mask_workspace_bytes(int64_t n)

@@ -75,14 +75,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---- launch helpers (host) -------------------------------------------------
 hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s);
 hipError_t launch_project_bwd(const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                              const float *grad2d, const gs_grads &out, hipStream_t s);
+                              const float *partial, const uint32_t *first_slot, uint64_t k_capacity,
+                              float *g2, const gs_grads &out, hipStream_t s);
 
 struct SortWorkspace;
 size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles);
 size_t schedule_words(int n_tiles);
 hipError_t launch_bin_sort(const Splat *splats, int64_t n, const Cam &cam, int64_t k_capacity,
-                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint64_t *keys,
-                           uint64_t *k_total, void *ws, size_t ws_bytes, hipStream_t s);
+                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
+                           uint64_t *keys, uint64_t *k_total, void *ws, size_t ws_bytes, hipStream_t s);
 size_t active_mask_workspace(int64_t n);
 hipError_t launch_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *ws,
                               size_t ws_bytes, hipStream_t s);
@@ -91,9 +92,9 @@ hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const ui
                              uint32_t *schedule, const Cam &cam, const float bg[3], float *image,
                              float *final_T, uint32_t *n_contrib, hipStream_t s);
 hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const Cam &cam, const float bg[3], const float *final_T,
-                             const uint32_t *n_contrib, const float *dL_dimage, int64_t n,
-                             float *grad2d, hipStream_t s);
+                             uint32_t *schedule, const uint32_t *entry_slots, const Cam &cam,
+                             const float bg[3], const float *final_T, const uint32_t *n_contrib,
+                             const float *dL_dimage, float *partial, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s);
 
 }  // namespace gsi

@@ -324,8 +324,9 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward: grad2d[9][n] = d/du, d/dv, d/da, d/db, d/dc, d/dopacity, d/drgb
-// (from the compositing pass) -> raw parameter gradients, +=.  The forward
+// Backward: the screen-space gradients d/du, d/dv, d/da, d/db, d/dc,
+// d/dopacity, d/drgb (summed from the compositing pass's per-tile partials)
+// -> raw parameter gradients, +=.  The forward
 // sequence above is recomputed; the guard clamp and the colour clamp keep the
 // branch the forward took.
 //   conic = Sigma'^-1:      dSigma' = -Q A Q, A = [[da, db/2], [db/2, dc]]
@@ -336,11 +337,45 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 //   colour:                 dk_j = Y_j drgb (unclamped channels),
 //                           dmu += (I - d d^T) / |mu - c| sum_j k_j grad Y_j drgb
 //   raw outputs:            dlog s = s ds,  dlogit = o (1 - o) do.
+// The screen-space gradients of each Gaussian: the sum, in slot order, of
+// its per-tile partial sums, which sit at its tiles_touched contiguous
+// duplication slots (slots at or past the capacity were never written).
+// Seven Gaussians per wave, one lane per (Gaussian, component); the result
+// is stored component-major, g2[q][n].  Culled Gaussians get zeros.
+constexpr int kSumPerWave = 7;
+__global__ __launch_bounds__(kBlock) void sum_partials_kernel(int n, const Splat *__restrict__ splats,
+                                                             const float *__restrict__ partial,
+                                                             const uint32_t *__restrict__ first_slot,
+                                                             uint64_t k_capacity, float *__restrict__ g2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
+    const int gl = lane / 9, q = lane - 9 * gl;
+    if (gl >= kSumPerWave) return;
+    const int g = wave * kSumPerWave + gl;
+    if (g >= n) return;
+    float acc = 0.0f;
+    if (__float_as_int(splats[g].a.w) != 0) {
+        const uint64_t first = first_slot[g];
+        uint64_t last = first + __float_as_uint(splats[g].c.w);
+        if (last > k_capacity) last = k_capacity;
+        // eight independent loads in flight per step; the sum stays in slot order
+        for (uint64_t sl = first; sl < last; sl += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = sl + j < last ? partial[(sl + j) * 9 + q] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) acc += v[j];
+        }
+    }
+    g2[(size_t)q * n + g] = acc;
+}
+
 template <int DEG, typename TSH>
 __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
     int n, const float *__restrict__ means, const float *__restrict__ scales,
     const float *__restrict__ quats, const float *__restrict__ opac, const TSH *__restrict__ sh,
-    Cam cam, const Splat *__restrict__ splats, const float *__restrict__ grad2d,
+    Cam cam, const Splat *__restrict__ splats, const float *__restrict__ g2s,
     float *__restrict__ d_means, float *__restrict__ d_log_scales, float *__restrict__ d_quats,
     float *__restrict__ d_logits, float *__restrict__ d_sh)
 {
@@ -348,7 +383,11 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
     const int g = blockIdx.x * kBlock + threadIdx.x;
     if (g >= n) return;
     // culled Gaussians have radius 0 and receive nothing
-    if (__float_as_int(splats[g].a.w) == 0) return;
+    const float4 ra = splats[g].a;
+    if (__float_as_int(ra.w) == 0) return;
+    float g2[9];
+#pragma unroll
+    for (int q = 0; q < 9; q++) g2[q] = g2s[(size_t)q * n + g];
     const float mx = means[g], my = means[n + g], mz = means[2 * n + g];
 
     // colour (fp32, the forward's sequence, so the clamp decisions agree)
@@ -370,7 +409,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
                 sum = sum + kv[j] * Y[j];
             }
             if (0.5f + sum < 0.0f) continue;
-            const float gr = grad2d[(6 + ch) * n + g];
+            const float gr = g2[6 + ch];
 #pragma unroll
             for (int j = 0; j < K; j++) {
                 float *p = d_sh + ((size_t)(j * 3 + ch)) * n + g;
@@ -386,9 +425,9 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
         dmu_c[2] = (dd[2] - dz * ddot) / dn;
     }
 
-    const double gu = grad2d[g], gv = grad2d[n + g];
-    const double ga = grad2d[2 * n + g], gb = grad2d[3 * n + g], gc = grad2d[4 * n + g];
-    const float go = grad2d[5 * n + g];
+    const double gu = g2[0], gv = g2[1];
+    const double ga = g2[2], gb = g2[3], gc = g2[4];
+    const float go = g2[5];
     const float s[3] = {scales[g], scales[n + g], scales[2 * n + g]};
     const float o = opac[g];
     // The chain rule runs in fp64 on a fp64 recomputation of the geometry:
@@ -501,13 +540,13 @@ void launch_project_t(const gs_gaussians &g, const Cam &cam, Splat *splats, hipS
 }
 
 template <int DEG, typename TSH>
-void launch_project_bwd_t(const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                          const float *grad2d, const gs_grads &out, hipStream_t s)
+void launch_project_bwd_t(const gs_gaussians &g, const Cam &cam, const Splat *splats, const float *g2,
+                          const gs_grads &out, hipStream_t s)
 {
     const int n = (int)g.n;
     project_bwd_kernel<DEG, TSH><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, cam, splats, grad2d,
-        out.means, out.log_scales, out.quats, out.opacity_logits, out.sh);
+        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, cam, splats, g2, out.means,
+        out.log_scales, out.quats, out.opacity_logits, out.sh);
 }
 
 template <typename TSH>
@@ -522,14 +561,14 @@ void dispatch_project(int deg, const gs_gaussians &g, const Cam &cam, Splat *spl
 }
 
 template <typename TSH>
-void dispatch_project_bwd(int deg, const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                          const float *grad2d, const gs_grads &out, hipStream_t s)
+void dispatch_project_bwd(int deg, const gs_gaussians &g, const Cam &cam, const Splat *splats, const float *g2,
+                          const gs_grads &out, hipStream_t s)
 {
     switch (deg) {
-    case 0: launch_project_bwd_t<0, TSH>(g, cam, splats, grad2d, out, s); break;
-    case 1: launch_project_bwd_t<1, TSH>(g, cam, splats, grad2d, out, s); break;
-    case 2: launch_project_bwd_t<2, TSH>(g, cam, splats, grad2d, out, s); break;
-    default: launch_project_bwd_t<3, TSH>(g, cam, splats, grad2d, out, s); break;
+    case 0: launch_project_bwd_t<0, TSH>(g, cam, splats, g2, out, s); break;
+    case 1: launch_project_bwd_t<1, TSH>(g, cam, splats, g2, out, s); break;
+    case 2: launch_project_bwd_t<2, TSH>(g, cam, splats, g2, out, s); break;
+    default: launch_project_bwd_t<3, TSH>(g, cam, splats, g2, out, s); break;
     }
 }
 
@@ -546,13 +585,18 @@ hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, 
 }
 
 hipError_t launch_project_bwd(const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                              const float *grad2d, const gs_grads &out, hipStream_t s)
+                              const float *partial, const uint32_t *first_slot, uint64_t k_capacity,
+                              float *g2, const gs_grads &out, hipStream_t s)
 {
     if (g.n == 0) return hipSuccess;
+    const int n = (int)g.n;
+    const long long waves = (n + kSumPerWave - 1) / kSumPerWave;
+    const unsigned blocks = (unsigned)((waves * 64 + kBlock - 1) / kBlock);
+    sum_partials_kernel<<<blocks, kBlock, 0, s>>>(n, splats, partial, first_slot, k_capacity, g2);
     if (g.sh_dtype == GS_SH_F16)
-        dispatch_project_bwd<__half>(g.sh_degree, g, cam, splats, grad2d, out, s);
+        dispatch_project_bwd<__half>(g.sh_degree, g, cam, splats, g2, out, s);
     else
-        dispatch_project_bwd<float>(g.sh_degree, g, cam, splats, grad2d, out, s);
+        dispatch_project_bwd<float>(g.sh_degree, g, cam, splats, g2, out, s);
     return hipGetLastError();
 }
 

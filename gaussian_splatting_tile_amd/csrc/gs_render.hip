@@ -141,13 +141,23 @@ __device__ __forceinline__ float alpha_raw(const ColTerms &c, double qc, double 
     return __builtin_amdgcn_exp2f((float)e);
 }
 
+// The backward writes all nine partial sums of every entry of a tile's list,
+// zeros where the entry cannot reach any pixel that uses it.
+__device__ __forceinline__ void zero_partial(float *__restrict__ partial, uint32_t entry_slot)
+{
+    float *p = partial + (size_t)entry_slot * 9;
+#pragma unroll
+    for (int q = 0; q < 9; q++) p[q] = 0.0f;
+}
+
 // Stage one record per lane into LDS, dropping those that cannot reach any
 // pixel of the tile; returns the number kept.  Kept records keep their order.
 template <bool kBwd>
 __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-                                           uint32_t b0, uint32_t end, uint32_t start, int x0, int y0,
-                                           double2 *s_uv, double4 *s_q, float4 *s_rgb, uint32_t *s_pos,
-                                           float4 *s_conic, uint32_t *s_g)
+                                           const uint32_t *__restrict__ entry_slots, uint32_t b0, uint32_t end,
+                                           uint32_t start, int x0, int y0, double2 *s_uv, double4 *s_q,
+                                           float4 *s_rgb, uint32_t *s_pos, float4 *s_conic, uint32_t *s_slot,
+                                           float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
     const uint32_t m = b0 + lane;
@@ -157,6 +167,7 @@ __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, con
         g = vals[m];
         const float4 sa = splats[g].a;
         keep = may_contribute(sa.x, sa.y, splats[g].b, x0, y0);
+        if (kBwd && !keep) zero_partial(partial, entry_slots[m]);
     }
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -167,7 +178,7 @@ __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, con
         s_pos[slot] = m - start;
         if (kBwd) {
             s_conic[slot] = s.b;
-            s_g[slot] = g;
+            s_slot[slot] = entry_slots[m];
         }
     }
     return __popcll(mask);
@@ -210,8 +221,8 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
         const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
-            const int nb = stage_batch<false>(splats, vals, b0, end, start, tx * kTile, ty * kTile, s_uv, s_q,
-                                              s_rgb, s_pos, nullptr, nullptr);
+            const int nb = stage_batch<false>(splats, vals, nullptr, b0, end, start, tx * kTile, ty * kTile, s_uv,
+                                              s_q, s_rgb, s_pos, nullptr, nullptr, nullptr);
             __syncthreads();
             for (int k = 0; k < nb; k++) {
                 const double2 uv = s_uv[k];
@@ -257,9 +268,10 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
 // Backward.  Per pixel, walk the composited entries back to front:
 //   T_i = T_{i+1} / (1 - alpha_i)                (T before entry i)
 //   A   = colour of everything behind entry i, normalised by T_{i+1}
-//         (A starts at bg and A <- alpha_i rgb_i + (1 - alpha_i) A)
+//         (A starts at bg and A <- alpha_i rgb_i + (1 - alpha_i) A); only
+//         <A, G> is needed, so that scalar is carried
 //   dL/drgb_i   = alpha_i T_i G
-//   dL/dalpha_i = T_i <rgb_i - A, G>
+//   dL/dalpha_i = T_i (<rgb_i, G> - <A, G>)
 //   below the cap: dL/do = exp(power) dL/dalpha, dL/dpower = alpha dL/dalpha
 //   power = -1/2 (a dx^2 + c dy^2) - b dx dy  (dx = u - px, dy = v - py):
 //     d/du = -(a dx + b dy), d/dv = -(c dy + b dx),
@@ -267,55 +279,59 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
 // A lane's four pixels share dx, so it accumulates S0 = sum dp, S1 = sum dp dy,
 // S2 = sum dp dy^2 (dp = dL/dpower) and forms the five conic/mean terms once.
 // The 9 per-lane values of a record are then summed over the wave by a split
-// butterfly (each exchange halves the values a lane carries) and nine lanes
-// add the totals to grad2d[9][n] with hardware float atomics: one atomic per
-// value per (Gaussian, tile).
+// butterfly on VALU lane swaps and DPP moves (each exchange halves the values
+// a lane carries) and nine lanes store the totals at the record's
+// duplication slot, partial[slot][9]: every (Gaussian, tile) pair owns one
+// slot, the slots of a Gaussian are contiguous, and the projection backward
+// sums them.  No atomics, so the gradients are bit-reproducible.
 
-__device__ __forceinline__ float dpp_f(float v, int ctrl_sel)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v)
 {
-    int r;
     const int iv = __float_as_int(v);
-    switch (ctrl_sel) {
-    case 1: r = __builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
-    case 2: r = __builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
-    default: r = __builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false); break; // row_ror:8
-    }
-    return __int_as_float(r);
+    return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8 (lane i <- (i + 8) mod 16)
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror (lane i <- 7 - i within 8)
+
+// Split exchange across lanes i and i ^ 32 (i ^ 16): lanes of the lower half
+// (even rows) return a[i] + a[partner], lanes of the upper half (odd rows)
+// b[i] + b[partner].  v_permlane32_swap / v_permlane16_swap swap the upper
+// half of the first operand with the lower half of the second, so the sum of
+// the two results is exactly that.
+__device__ __forceinline__ float xchg32(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xchg16(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float swz_xor4(float v)
-{
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
-}
-__device__ __forceinline__ float swz_xor16(float v)
-{
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
-
-// Wave sums of v[0..8]; lane L in {0,1,2,3,4,5,6,8,9} returns the total of
-// value {0,5,3,8,1,6,4,2,7}[.] respectively (see reduce_slot).
+// Wave sums of v[0..8] by a split butterfly: each exchange halves the values
+// a lane carries (9 -> 5 -> 3 -> 2 -> 1), then two plain steps finish.
+// Lane 0, 4, 8, 16, 20, 32, 36, 40, 48 returns the total of value
+// 0, 1, 2, 3, 4, 5, 6, 7, 8 (see reduce_slot).
 __device__ __forceinline__ float wave_reduce9(const float v[9], int lane)
 {
-    bool hi = (lane & 1) != 0;                    // xor 1: 9 values -> 5
     float s[5];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float keep = hi ? v[i + 5] : v[i];
-        const float send = hi ? v[i] : v[i + 5];
-        s[i] = keep + dpp_f(send, 1);
-    }
-    s[4] = v[4] + dpp_f(v[4], 1);
-    hi = (lane & 2) != 0;                         // xor 2: 5 -> 3
-    const float n0 = (hi ? s[3] : s[0]) + dpp_f(hi ? s[0] : s[3], 2);
-    const float n1 = (hi ? s[4] : s[1]) + dpp_f(hi ? s[1] : s[4], 2);
-    const float n2 = s[2] + dpp_f(s[2], 2);
-    hi = (lane & 8) != 0;                         // xor 8: 3 -> 2
-    const float m0 = (hi ? n2 : n0) + dpp_f(hi ? n0 : n2, 8);
-    const float m1 = n1 + dpp_f(n1, 8);
-    hi = (lane & 4) != 0;                         // xor 4: 2 -> 1
-    float f = (hi ? m1 : m0) + swz_xor4(hi ? m0 : m1);
-    f += swz_xor16(f);                            // xor 16
-    f += __shfl_xor(f, 32, 64);                   // xor 32
+    for (int i = 0; i < 4; i++) s[i] = xchg32(v[i], v[i + 5]);       // lanes >= 32 keep v[5..8]
+    s[4] = xchg32(v[4], v[4]);
+    const float n0 = xchg16(s[0], s[3]);                              // odd rows keep s3, s4
+    const float n1 = xchg16(s[1], s[4]);
+    const float n2 = xchg16(s[2], s[2]);
+    bool hi = (lane & 8) != 0;                                        // i ^ 8: 3 -> 2
+    const float m0 = (hi ? n2 : n0) + dpp_f<kDppRowRor8>(hi ? n0 : n2);
+    const float m1 = n1 + dpp_f<kDppRowRor8>(n1);
+    hi = (lane & 4) != 0;                                             // i ^ 7 within 8: 2 -> 1
+    float f = (hi ? m1 : m0) + dpp_f<kDppHalfMirror>(hi ? m0 : m1);
+    f += dpp_f<kDppQuadXor2>(f);
+    f += dpp_f<kDppQuadXor1>(f);
     return f;
 }
 
@@ -324,31 +340,30 @@ __device__ __forceinline__ int reduce_slot(int lane)
 {
     switch (lane) {
     case 0: return 0;
-    case 1: return 5;
-    case 2: return 3;
-    case 3: return 8;
     case 4: return 1;
-    case 5: return 6;
-    case 6: return 4;
     case 8: return 2;
-    case 9: return 7;
+    case 16: return 3;
+    case 20: return 4;
+    case 32: return 5;
+    case 36: return 6;
+    case 40: return 7;
+    case 48: return 8;
     default: return -1;
     }
 }
 
 __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, Cam cam, float bg0, float bg1,
-    float bg2, const float *__restrict__ final_T,
-    const uint32_t *__restrict__ n_contrib, const float *__restrict__ dL_dimage, int n,
-    float *__restrict__ grad2d)
+    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, const uint32_t *__restrict__ entry_slots,
+    Cam cam, float bg0, float bg1, float bg2, const float *__restrict__ final_T,
+    const uint32_t *__restrict__ n_contrib, const float *__restrict__ dL_dimage, float *__restrict__ partial)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double4 s_q[kBatch];
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
     __shared__ float4 s_conic[kBatch];
-    __shared__ uint32_t s_g[kBatch];
+    __shared__ uint32_t s_slot[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const double px = (double)x + 0.5;
 
     double py[kPx];
-    float T[kPx], G0[kPx], G1[kPx], G2[kPx], A0[kPx], A1[kPx], A2[kPx];
+    float T[kPx], G0[kPx], G1[kPx], G2[kPx], AG[kPx];
     uint32_t last[kPx];
     uint32_t lmax = 0;
 #pragma unroll
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
             G1[r] = dL_dimage[hw + p];
             G2[r] = dL_dimage[2 * hw + p];
         }
-        A0[r] = bg0; A1[r] = bg1; A2[r] = bg2;
+        AG[r] = bg0 * G0[r] + bg1 * G1[r] + bg2 * G2[r];
         lmax = max(lmax, last[r]);
     }
 #pragma unroll
@@ -390,8 +405,8 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const uint32_t stop = start + lmax;           // entries at or past this are unused
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
         const uint32_t bbeg = (uint32_t)max((int64_t)start, bend - kBatch);
-        const int nb = stage_batch<true>(splats, vals, bbeg, (uint32_t)bend, start, tx * kTile, ty * kTile,
-                                         s_uv, s_q, s_rgb, s_pos, s_conic, s_g);
+        const int nb = stage_batch<true>(splats, vals, entry_slots, bbeg, (uint32_t)bend, start, tx * kTile,
+                                         ty * kTile, s_uv, s_q, s_rgb, s_pos, s_conic, s_slot, partial);
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
             const uint32_t pos = s_pos[k];                     // list position
@@ -409,9 +424,12 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
                 take[r] = pos < last[r] && raws[r] >= kAlphaMin;
                 any = any || take[r];
             }
-            if (__ballot(any) == 0) continue;
+            if (__ballot(any) == 0) {
+                if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = 0.0f;
+                continue;
+            }
             const float4 col = s_rgb[k];
-            const float inv_o = 1.0f / col.w;
+            const float inv_o = __builtin_amdgcn_rcpf(col.w);
             float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f, S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
@@ -424,11 +442,9 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
                 g6 = fmaf(w, G0[r], g6);
                 g7 = fmaf(w, G1[r], g7);
                 g8 = fmaf(w, G2[r], g8);
-                const float dla = T[r] * ((col.x - A0[r]) * G0[r] + (col.y - A1[r]) * G1[r] +
-                                          (col.z - A2[r]) * G2[r]);
-                A0[r] = alpha * col.x + one_m * A0[r];
-                A1[r] = alpha * col.y + one_m * A1[r];
-                A2[r] = alpha * col.z + one_m * A2[r];
+                const float cg = fmaf(col.z, G2[r], fmaf(col.y, G1[r], col.x * G0[r]));
+                const float dla = T[r] * (cg - AG[r]);
+                AG[r] = fmaf(alpha, cg, one_m * AG[r]);
                 if (raw < kAlphaMax) {
                     go = fmaf(dla, raw * inv_o, go);
                     const float dp = dla * alpha;
@@ -451,11 +467,13 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
             v[7] = g7;
             v[8] = g8;
             const float tot = wave_reduce9(v, lane);
-            if (slot >= 0 && tot != 0.0f)
-                unsafeAtomicAdd(&grad2d[(size_t)slot * n + s_g[k]], tot);
+            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot;
         }
         __syncthreads();
     }
+    // entries past the last one any pixel used
+    const uint32_t end = ranges[2 * tile + 1];
+    for (uint32_t m = stop + lane; m < end; m += kLanes) zero_partial(partial, entry_slots[m]);
     }
     retire_wave(head, done);
 }
@@ -487,14 +505,14 @@ hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const ui
 }
 
 hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const Cam &cam, const float bg[3], const float *final_T,
-                             const uint32_t *n_contrib, const float *dL_dimage, int64_t n,
-                             float *grad2d, hipStream_t s)
+                             uint32_t *schedule, const uint32_t *entry_slots, const Cam &cam,
+                             const float bg[3], const float *final_T, const uint32_t *n_contrib,
+                             const float *dL_dimage, float *partial, hipStream_t s)
 {
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int grid = resident_blocks(render_bwd_kernel, n_tiles);
-    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, cam, bg[0], bg[1], bg[2],
-                                              final_T, n_contrib, dL_dimage, (int)n, grad2d);
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, entry_slots, cam, bg[0], bg[1],
+                                              bg[2], final_T, n_contrib, dL_dimage, partial);
     return hipGetLastError();
 }
 

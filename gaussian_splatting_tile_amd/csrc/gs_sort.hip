@@ -130,11 +130,15 @@ __global__ __launch_bounds__(kBlock) void radix_scan(uint32_t *__restrict__ coun
     if (threadIdx.x == 0) digit_total[blockIdx.x] = total;
 }
 
+// Values: vals_in NULL means the identity (the item's input index).  With
+// kTwo a second value array rides along (vals2_in, vals2_out).
+template <bool kTwo>
 __global__ __launch_bounds__(kBlock) void radix_downsweep(
     const uint32_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
-    uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
-    const uint32_t *__restrict__ n_ptr, uint32_t *__restrict__ n_out_ptr, int shift, int bits,
-    int drop_sentinel, const uint32_t *__restrict__ counts, const uint32_t *__restrict__ digit_total)
+    const uint32_t *__restrict__ vals2_in, uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
+    uint32_t *__restrict__ vals2_out, const uint32_t *__restrict__ n_ptr, uint32_t *__restrict__ n_out_ptr,
+    int shift, int bits, int drop_sentinel, const uint32_t *__restrict__ counts,
+    const uint32_t *__restrict__ digit_total)
 {
     __shared__ uint32_t digit_base[256];
     __shared__ uint32_t tile_start[256];
@@ -142,6 +146,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     __shared__ uint32_t wave_cnt[kWaves][256];
     __shared__ uint32_t sk[kTileItems];
     __shared__ uint32_t sv[kTileItems];
+    __shared__ uint32_t sv2[kTwo ? kTileItems : 1];
     __shared__ uint32_t s_tile_total;
 
     const uint32_t n = *n_ptr;
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     for (uint32_t tb = begin; tb < end; tb += kTileItems) {
         for (int i = lane; i < 256; i += kWave) wave_cnt[w][i] = 0;
         // the wave's own row is written by its own lanes only; no barrier needed
-        uint32_t k[kIpt], v[kIpt], loc[kIpt];
+        uint32_t k[kIpt], v[kIpt], v2[kIpt], loc[kIpt];
         bool ok[kIpt];
 #pragma unroll
         for (int r = 0; r < kIpt; r++) {
@@ -184,7 +189,8 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             if (valid && rank == 0) wave_cnt[w][d] = before + (uint32_t)__popcll(peers);
             __builtin_amdgcn_wave_barrier();
             k[r] = kk;
-            v[r] = valid ? vals_in[idx] : 0u;
+            v[r] = valid ? (vals_in ? vals_in[idx] : idx) : 0u;
+            if (kTwo) v2[r] = valid ? vals2_in[idx] : 0u;
             loc[r] = before + rank;
             ok[r] = valid;
         }
@@ -211,6 +217,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             const uint32_t pos = tile_start[d] + wave_cnt[w][d] + loc[r];
             sk[pos] = k[r];
             sv[pos] = v[r];
+            if (kTwo) sv2[pos] = v2[r];
         }
         __syncthreads();
         const uint32_t tot = s_tile_total;
@@ -220,6 +227,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             const uint32_t o = digit_base[d] + (i - tile_start[d]);
             keys_out[o] = kk;
             vals_out[o] = sv[i];
+            if (kTwo) vals2_out[o] = sv2[i];
         }
         __syncthreads();
         digit_base[tid] += tile_cnt[tid];
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
     const uint32_t *__restrict__ order, const uint32_t *__restrict__ m_ptr,
     const uint2 *__restrict__ rect_info, const uint32_t *__restrict__ counts,
     const uint64_t *__restrict__ block_offsets, int tiles_x, uint64_t cap,
-    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ vals)
+    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ gslot, uint32_t *__restrict__ first_slot)
 {
     __shared__ uint32_t s_off[kScanItems];
     __shared__ uint32_t s_g[kScanItems];
@@ -350,6 +358,10 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
     s_off[threadIdx.x] = block_exclusive_scan(c, &total);
     __syncthreads();
     const uint64_t blk = block_offsets[blockIdx.x];
+    if (first_slot && threadIdx.x < n_items) {
+        const uint64_t f = blk + s_off[threadIdx.x];
+        first_slot[s_g[threadIdx.x]] = (uint32_t)(f < 0xFFFFFFFFull ? f : 0xFFFFFFFFull);
+    }
     for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
         const uint64_t slot = blk + e;
         if (slot >= cap) break;
@@ -368,15 +380,21 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
         const uint32_t ty = (xy >> 16) + q;
         const uint32_t tx = (xy & 0xFFFFu) + (within - q * w);
         tile_keys[slot] = ty * (uint32_t)tiles_x + tx;
-        vals[slot] = s_g[lo];
+        gslot[slot] = s_g[lo];
     }
 }
 
+// Tile ranges from the boundaries of the sorted tile ids and the optional
+// 64-bit keys.  Without tile passes (a one-tile image) the duplication order
+// is final: the entries' Gaussians are copied from gslot and their slots are
+// the identity.
 __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const uint32_t *__restrict__ tile_keys,
-                                                             const uint32_t *__restrict__ vals,
                                                              const uint32_t *__restrict__ k_ptr,
                                                              const Splat *__restrict__ splats,
+                                                             const uint32_t *__restrict__ gslot,
                                                              uint32_t *__restrict__ ranges,
+                                                             uint32_t *__restrict__ vals,
+                                                             uint32_t *__restrict__ entry_slots,
                                                              uint64_t *__restrict__ keys64)
 {
     const uint32_t k = *k_ptr;
@@ -385,7 +403,15 @@ __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const uint32_t *__r
     const uint32_t t = tile_keys[i];
     if (i == 0 || tile_keys[i - 1] != t) ranges[2 * t] = i;
     if (i == k - 1 || tile_keys[i + 1] != t) ranges[2 * t + 1] = i + 1;
-    if (keys64) keys64[i] = ((uint64_t)t << 32) | __float_as_uint(splats[vals[i]].a.z);
+    uint32_t g;
+    if (gslot) {
+        g = gslot[i];
+        vals[i] = g;
+        if (entry_slots) entry_slots[i] = i;
+    } else if (keys64) {
+        g = vals[i];
+    }
+    if (keys64) keys64[i] = ((uint64_t)t << 32) | __float_as_uint(splats[g].a.z);
 }
 
 // Tile schedule for the blend kernels.  Per-tile work varies by two orders
@@ -475,7 +501,8 @@ struct BinWs {
     uint2 *rect_info;                  // [n] per depth-ordered Gaussian
     uint32_t *counts;                  // [n] tiles touched, depth order
     uint64_t *block_sums;              // [ceil(n / 256)]
-    uint32_t *tk[2], *tv;              // tile keys ping-pong, values scratch [cap]
+    uint32_t *tk[2], *tv[2], *ts[2];   // tile keys, Gaussians, slots ping-pong [cap]
+    uint32_t *gslot;                   // [cap] Gaussian of each duplication slot
     uint32_t *digit_counts;            // [256 * kMaxGrid]
     uint32_t *digit_total;             // [256]
     uint32_t *counters;                // [4]
@@ -495,7 +522,11 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     w.block_sums = c.take<uint64_t>((nn + kScanItems - 1) / kScanItems);
     w.tk[0] = c.take<uint32_t>(kk);
     w.tk[1] = c.take<uint32_t>(kk);
-    w.tv = c.take<uint32_t>(kk);
+    w.tv[0] = c.take<uint32_t>(kk);
+    w.tv[1] = c.take<uint32_t>(kk);
+    w.ts[0] = c.take<uint32_t>(kk);
+    w.ts[1] = c.take<uint32_t>(kk);
+    w.gslot = c.take<uint32_t>(kk);
     w.digit_counts = c.take<uint32_t>(256 * kMaxGrid);
     w.digit_total = c.take<uint32_t>(256);
     w.counters = c.take<uint32_t>(4);
@@ -503,15 +534,20 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     return c.off + 256;
 }
 
-hipError_t radix_pass(const uint32_t *kin, const uint32_t *vin, uint32_t *kout, uint32_t *vout,
-                      const uint32_t *n_ptr, uint32_t *n_out_ptr, uint64_t max_items, int shift,
-                      int bits, int drop, const BinWs &w, hipStream_t s)
+// One stable pass; v2in/v2out (both or neither) carry a second value array.
+hipError_t radix_pass(const uint32_t *kin, const uint32_t *vin, const uint32_t *v2in, uint32_t *kout,
+                      uint32_t *vout, uint32_t *v2out, const uint32_t *n_ptr, uint32_t *n_out_ptr,
+                      uint64_t max_items, int shift, int bits, int drop, const BinWs &w, hipStream_t s)
 {
     const int G = radix_grid(max_items);
     radix_upsweep<<<G, kBlock, 0, s>>>(kin, n_ptr, shift, bits, drop, w.digit_counts);
     radix_scan<<<256, kBlock, 0, s>>>(w.digit_counts, G, w.digit_total);
-    radix_downsweep<<<G, kBlock, 0, s>>>(kin, vin, kout, vout, n_ptr, n_out_ptr, shift, bits, drop,
-                                         w.digit_counts, w.digit_total);
+    if (v2out)
+        radix_downsweep<true><<<G, kBlock, 0, s>>>(kin, vin, v2in, kout, vout, v2out, n_ptr, n_out_ptr, shift,
+                                                   bits, drop, w.digit_counts, w.digit_total);
+    else
+        radix_downsweep<false><<<G, kBlock, 0, s>>>(kin, vin, nullptr, kout, vout, nullptr, n_ptr, n_out_ptr,
+                                                    shift, bits, drop, w.digit_counts, w.digit_total);
     return hipGetLastError();
 }
 
@@ -531,8 +567,8 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_
 }
 
 hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int64_t cap,
-                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint64_t *keys,
-                           uint64_t *k_total, void *ws_ptr, size_t ws_bytes, hipStream_t s)
+                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
+                           uint64_t *keys, uint64_t *k_total, void *ws_ptr, size_t ws_bytes, hipStream_t s)
 {
     (void)ws_bytes;
     BinWs w;
@@ -552,8 +588,8 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
         int cur = 0;
         for (int pass = 0; pass < 4; pass++) {
             const uint32_t *n_in = pass == 0 ? &w.counters[0] : &w.counters[1];
-            e = radix_pass(w.dk[cur], w.dv[cur], w.dk[cur ^ 1], w.dv[cur ^ 1], n_in, &w.counters[1], n,
-                           8 * pass, 8, pass == 0, w, s);
+            e = radix_pass(w.dk[cur], w.dv[cur], nullptr, w.dk[cur ^ 1], w.dv[cur ^ 1], nullptr, n_in,
+                           &w.counters[1], n, 8 * pass, 8, pass == 0, w, s);
             if (e != hipSuccess) return e;
             cur ^= 1;
         }
@@ -564,32 +600,40 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
         scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], cam, w.rect_info, w.counts,
                                             w.block_sums);
         scan_blocks<<<1, 1024, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total, &w.counters[2]);
-        // 3. tile passes: choose the buffers so the last pass lands in `vals`
+        // 3. tile passes over the tile ids, carrying each entry's Gaussian
+        // and, for the backward index, its duplication slot (the identity on
+        // the way in); the last pass writes straight into the outputs
         const int tbits = bits_for(n_tiles);
         const int passes = tbits == 0 ? 0 : (tbits + 7) / 8;
-        uint32_t *kbuf[2] = {w.tk[0], w.tk[1]};
-        uint32_t *vbuf[2];
-        // pass p reads (k[p&1], v[p&1]) and writes (k[(p+1)&1], v[(p+1)&1])
-        if (passes % 2 == 0) { vbuf[0] = vals; vbuf[1] = w.tv; }
-        else { vbuf[0] = w.tv; vbuf[1] = vals; }
+        uint32_t *entry_slots = bwd_index;                     // [cap], optional
+        uint32_t *first_slot = bwd_index ? bwd_index + cap : nullptr;   // [n]
         duplicate_keys<<<nblk, kBlock, 0, s>>>(order, &w.counters[1], w.rect_info, w.counts, w.block_sums,
-                                               cam.tiles_x, (uint64_t)cap, kbuf[0], vbuf[0]);
+                                               cam.tiles_x, (uint64_t)cap, w.tk[0], w.gslot, first_slot);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         int shift = 0;
         for (int p = 0; p < passes; p++) {
             const int bits = (tbits - shift) < 8 ? (tbits - shift) : 8;
-            e = radix_pass(kbuf[p & 1], vbuf[p & 1], kbuf[(p + 1) & 1], vbuf[(p + 1) & 1],
-                           &w.counters[2], nullptr, (uint64_t)cap, shift, bits, 0, w, s);
+            const bool last = p == passes - 1;
+            const uint32_t *gin = p == 0 ? w.gslot : w.tv[(p - 1) & 1];
+            uint32_t *gout = last ? vals : w.tv[p & 1];
+            if (entry_slots) {
+                const uint32_t *sin = p == 0 ? nullptr : w.ts[(p - 1) & 1];
+                uint32_t *sout = last ? entry_slots : w.ts[p & 1];
+                e = radix_pass(w.tk[p & 1], sin, gin, w.tk[(p + 1) & 1], sout, gout, &w.counters[2], nullptr,
+                               (uint64_t)cap, shift, bits, 0, w, s);
+            } else {
+                e = radix_pass(w.tk[p & 1], gin, nullptr, w.tk[(p + 1) & 1], gout, nullptr, &w.counters[2],
+                               nullptr, (uint64_t)cap, shift, bits, 0, w, s);
+            }
             if (e != hipSuccess) return e;
             shift += bits;
         }
-        // (with one tile there is no pass: the depth order is already final)
-        const uint32_t *sorted_tiles = kbuf[passes & 1];
-        // 4. ranges (and the optional 64-bit keys)
+        // 4. ranges and the optional 64-bit keys
         const uint64_t kgrid = ((uint64_t)cap + kBlock - 1) / kBlock;
         if (kgrid > 0)
-            tile_ranges_kernel<<<(unsigned)kgrid, kBlock, 0, s>>>(sorted_tiles, vals, &w.counters[2],
-                                                                  splats, tile_ranges, keys);
+            tile_ranges_kernel<<<(unsigned)kgrid, kBlock, 0, s>>>(w.tk[passes & 1], &w.counters[2], splats,
+                                                                  passes == 0 ? w.gslot : nullptr, tile_ranges,
+                                                                  vals, entry_slots, keys);
     } else {
         // no Gaussians: K = 0
         fill_u32_kernel<<<1, kBlock, 0, s>>>((uint32_t *)k_total, 0u, 2);

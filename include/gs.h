@@ -144,6 +144,10 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tile
  * one per 16x16 tile plus four queue counters. */
 size_t gs_schedule_words(int32_t width, int32_t height);
 
+/* Number of 32-bit words of the backward index for n Gaussians and a key
+ * capacity k_capacity (see gs_bin_sort). */
+size_t gs_bwd_index_words(int64_t n, int64_t k_capacity);
+
 /* Tile binning and depth sort of one view.
  * Input: splats[n] from gs_project with the same camera.
  * Output:
@@ -155,6 +159,11 @@ size_t gs_schedule_words(int32_t width, int32_t height);
  *                           (the order in which the blend kernels take
  *                           them) and zeroed queue counters; pass it to
  *                           gs_render_fwd / gs_render_bwd
+ *   bwd_index[gs_bwd_index_words(n, k_capacity)]  (optional, NULL to
+ *                           skip; needed by gs_render_bwd) the duplication
+ *                           slot of every sorted entry (k_capacity words),
+ *                           then the first slot of every Gaussian (n words);
+ *                           a Gaussian's tiles_touched slots are contiguous
  *   keys[k_capacity]        (optional, NULL to skip) the 64-bit sort keys
  *                           tile << 32 | bits of the fp32 depth
  *   k_total                 device uint64: K, the number of entries
@@ -168,8 +177,8 @@ size_t gs_schedule_words(int32_t width, int32_t height);
 gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
                       const gs_camera *camera /* host */, int64_t k_capacity,
                       uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule,
-                      uint64_t *keys, uint64_t *k_total, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      uint32_t *bwd_index, uint64_t *keys, uint64_t *k_total,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Forward compositing of every pixel.
  * Inputs: splats (gs_project), vals, tile_ranges and schedule (gs_bin_sort),
@@ -189,23 +198,27 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
                         float *image, float *final_T, uint32_t *n_contrib,
                         void *stream);
 
-/* Workspace for gs_render_bwd, in bytes (per-Gaussian 2D gradients). */
-size_t gs_render_bwd_workspace_bytes(int64_t n);
+/* Workspace for gs_render_bwd, in bytes: nine fp32 partial sums per key
+ * slot for a key capacity k_capacity, and nine fp32 sums per Gaussian. */
+size_t gs_render_bwd_workspace_bytes(int64_t n, int64_t k_capacity);
 
 /* Backward of one view: given dL/dimage[3][H][W], accumulates (+=) into
  * grads the gradient of L with respect to the raw parameters.  Every
  * discrete decision of the forward (tile membership, order, the 1/255 skip,
  * the stop, the 0.99 cap, the colour clamp at 0, the guard clamp) is held as
  * the forward took it; depth gets no gradient.  The inputs must be those of
- * the matching forward call.  Per (Gaussian, tile) the 9 screen-space
- * gradients are reduced across the tile's pixels on chip before one set of
- * atomic adds, so the low bits of the result depend on scheduling.  It uses
- * the schedule's backward queue counters (see gs_render_fwd).
+ * the matching forward call, with bwd_index and the same k_capacity from
+ * its gs_bin_sort.  Per (Gaussian, tile) the 9 screen-space gradients are
+ * reduced across the tile's pixels on chip and stored at the pair's slot;
+ * each Gaussian then sums its own slots.  No atomics are used: the result is
+ * bit-reproducible.  It uses the schedule's backward queue counters (see
+ * gs_render_fwd).
  * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE. */
 gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
                         const gs_camera *camera /* host */,
                         const gs_splat *splats, const uint32_t *vals,
                         const uint32_t *tile_ranges, uint32_t *schedule,
+                        const uint32_t *bwd_index, int64_t k_capacity,
                         const float *bg /* host [3] */,
                         const float *final_T, const uint32_t *n_contrib,
                         const float *dL_dimage, const gs_grads *grads /* host struct */,

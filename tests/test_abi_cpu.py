@@ -57,9 +57,10 @@ def test_host_side_argument_errors_without_device():
     cam.guard = 1.3
     gs.sh_degree = 7
     assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
-    assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_bin_sort_workspace_bytes(1000, 5000, 64) > 5000 * 12
-    assert L.gs_render_bwd_workspace_bytes(1000) >= 1000 * 36
+    assert L.gs_render_bwd_workspace_bytes(1000, 4000) >= 5000 * 36
+    assert L.gs_bwd_index_words(10, 100) == 110
     assert L.gs_schedule_words(128, 128) == 64 + 4
     assert L.gs_schedule_words(0, 128) == 0

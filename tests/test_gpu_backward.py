@@ -53,9 +53,9 @@ def _gpu_grads(sc, views_and_G, sh=None):
     grads = dict(means=torch.zeros((3, n), device="cuda"), log_scales=torch.zeros((3, n), device="cuda"),
                  quats=torch.zeros((4, n), device="cuda"), opacity_logits=torch.zeros(n, device="cuda"),
                  sh=torch.zeros((K_sh, 3, n), device="cuda"))
-    ws = torch.empty(B.render_bwd_workspace_bytes(n), dtype=torch.uint8, device="cuda")
     for view, G in views_and_G:
         buf, K = run_view(sc, view, with_keys=False, sh=sh)
+        ws = buf.backward_workspace()
         g, act, gs = buf._keep
         dL = torch.from_numpy(np.ascontiguousarray(G)).cuda()
         buf.backward(gs, dL, grads, ws)

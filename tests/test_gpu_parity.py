@@ -138,7 +138,7 @@ def test_forward_is_deterministic():
     grads = dict(means=torch.zeros((3, sc.n), device="cuda"), log_scales=torch.zeros((3, sc.n), device="cuda"),
                  quats=torch.zeros((4, sc.n), device="cuda"), opacity_logits=torch.zeros(sc.n, device="cuda"),
                  sh=torch.zeros((16, 3, sc.n), device="cuda"))
-    ws = torch.empty(B.render_bwd_workspace_bytes(sc.n), dtype=torch.uint8, device="cuda")
+    ws = b1.backward_workspace()
     for it in range(3):
         b1.image.zero_()
         B.render_fwd(b1.splats, b1.vals, b1.ranges, b1.schedule, b1.camc, (0.0, 0.0, 0.0), b1.image,
@@ -147,6 +147,12 @@ def test_forward_is_deterministic():
             b1.backward(gs, torch.ones_like(b1.image), grads, ws)
         torch.cuda.synchronize()
         assert torch.equal(b1.image, img), it
+    # the backward is free of atomics: a second call gives bit-identical gradients
+    grads2 = {k: torch.zeros_like(v) for k, v in grads.items()}
+    b1.backward(gs, torch.ones_like(b1.image), grads2, ws)
+    torch.cuda.synchronize()
+    for k in grads:
+        assert torch.equal(grads[k], grads2[k]), k
     n_t = b1.ranges.shape[0]
     assert torch.all(b1.schedule[n_t:] == 0)
     order = b1.schedule[:n_t].cpu().numpy()
@@ -174,5 +180,5 @@ def test_invalid_arguments_are_rejected():
     with pytest.raises(B.GsError, match="workspace"):
         B.bin_sort(out, 10, cam, 100, torch.empty(100, dtype=torch.int32, device="cuda"),
                    torch.empty(128, dtype=torch.int32, device="cuda"),
-                   torch.empty(B.schedule_words(128, 128), dtype=torch.int32, device="cuda"), None,
+                   torch.empty(B.schedule_words(128, 128), dtype=torch.int32, device="cuda"), None, None,
                    torch.empty(1, dtype=torch.int64, device="cuda"), small)
