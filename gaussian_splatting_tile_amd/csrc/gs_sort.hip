@@ -645,15 +645,4 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
 
 size_t schedule_words(int n_tiles) { return (size_t)n_tiles + 4; }
 
-size_t active_mask_workspace(int64_t n)
-{
-    (void)n;
-    return 0;
-}
-
-hipError_t launch_active_mask(const float *, int64_t, int64_t, uint8_t *, void *, size_t, hipStream_t)
-{
-    return hipErrorNotSupported;
-}
-
 }  // namespace gsi

@@ -228,8 +228,14 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
 size_t gs_active_mask_workspace_bytes(int64_t n);
 
 /* Importance mask of the BlitzGS page (section 2.3): mask[g] = 1 for the
- * `keep` Gaussians with the highest scores (ties to the lower index), else 0.
- * scores: device float[n], finite and >= 0.  keep in 0..n.
+ * `keep` Gaussians with the highest scores (ties, -0 and +0 included, to the
+ * lower index), else 0; the result feeds gs_gaussians.active.
+ *   scores  device float[n], finite (any sign; a NaN score gives a mask that
+ *           is well defined but unspecified); any alignment
+ *   n       0 .. INT32_MAX;  keep 0 .. n
+ *   mask    device uint8[n], written in full; any alignment
+ * Radix select on the device: four 8-bit histogram passes, then one pass
+ * that writes the mask; no host synchronisation.
  * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
 gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep,
                          uint8_t *mask, void *workspace, size_t workspace_bytes,
