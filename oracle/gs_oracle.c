@@ -169,7 +169,9 @@ int64_t orc_bin(int64_t n, const int32_t *rect, const double *z, int tiles_x,
  *   image = sum alpha_i T_i rgb_i + T_final bg;
  *   n_contrib = 1 + list position of the last composited entry (0 if none).
  * A decision whose value lies within the relative band of its threshold is
- * an "event"; bit k of flips reverses the k-th event. */
+ * an "event"; bit k of flips reverses the k-th event.  The stop test depends
+ * on T alone, so its repeats while T is unchanged (entries skipped in
+ * between) are one decision: one event, taken the same way each time. */
 typedef struct {
     int n_comp;                 /* entries composited                     */
     int64_t evals;              /* entries examined before the stop       */
@@ -188,12 +190,18 @@ static void composite(const double *u, const double *v, const double *conic,
     double T = 1.0, C[3] = {0.0, 0.0, 0.0};
     int32_t last = 0;
     int ev = 0;
+    int stop_held = 0, stop_value = 0;   /* the event decision for the current T */
     st->n_comp = 0; st->evals = 0; st->events = 0; st->capflag = 0;
     for (uint32_t m = start; m < end; m++) {
         int stop = T < t_thr;
         if (fabs(T - t_thr) <= bands->trans * t_thr) {
-            if ((flips >> ev) & 1u) stop = !stop;
-            ev++;
+            if (!stop_held) {
+                if ((flips >> ev) & 1u) stop = !stop;
+                ev++;
+                stop_held = 1;
+                stop_value = stop;
+            }
+            stop = stop_value;
         }
         if (stop) break;
         st->evals++;
@@ -212,6 +220,7 @@ static void composite(const double *u, const double *v, const double *conic,
         if (fabs(raw - cap) <= bands->cap * cap) st->capflag = 1;
         for (int ch = 0; ch < 3; ch++) C[ch] += alpha * T * rgb[ch * n + g];
         T = T * (1.0 - alpha);
+        stop_held = 0;
         last = (int32_t)(m - start + 1);
         st->n_comp++;
     }

@@ -414,6 +414,34 @@ def test_exact_occlusion_by_opaque_layers():
     np.testing.assert_allclose(out1["final_T"], (1 - 0.99) * out0["final_T"], rtol=1e-12)
 
 
+def test_stop_decision_is_held_while_T_is_unchanged():
+    """The stop test depends on T alone: with the near-threshold stop taken
+    the other way, entries skipped afterwards (alpha < 1/255) leave T as it
+    was, so the later re-tests keep that decision and the next visible entry
+    composites.  Hand-built records, one 16x16 tile, power = 0 except for
+    the far entry."""
+    cam = _cam(width=16, height=16, f=16.0)
+    o = np.array([0.99, 0.98, 0.5 + 5e-8, 0.9, 0.7])
+    n = o.shape[0]
+    conic = np.zeros((3, n))
+    conic[:, 3] = (1.0, 0.0, 1.0)
+    u = np.full(n, 8.5)
+    u[3] = 1000.0                              # alpha = 0: skipped
+    rgb = np.zeros((3, n))
+    rgb[:, 4] = 1.0
+    proj = dict(u=u, v=np.full(n, 8.5), conic=conic, opacity=o, rgb=rgb)
+    bins = dict(vals=np.arange(n, dtype=np.uint32), ranges=np.array([[0, n]], np.uint32))
+    # T after three entries: 0.01 * 0.02 * (0.5 - 5e-8) = 1e-4 (1 - 1e-7) -> stop
+    rgb0, T0, n0, ev0 = oracle.render_pixel(proj, bins, cam, 8, 8)
+    assert n0 == 3 and ev0 == 1 and np.all(rgb0 == 0.0)
+    assert abs(T0 - 1e-4 * (1 - 1e-7)) < 1e-18
+    # reversed: the skip of entry 3 does not re-open the decision
+    rgb1, T1, n1, ev1 = oracle.render_pixel(proj, bins, cam, 8, 8, flips=1)
+    assert ev1 == 1 and n1 == 5
+    np.testing.assert_allclose(rgb1, T0 * 0.7, rtol=1e-12)
+    np.testing.assert_allclose(T1, T0 * 0.3, rtol=1e-12)
+
+
 def test_partition_of_unity_and_background():
     sc = scenes.config(1, n_override=400)
     cam = sc.cameras[0]
