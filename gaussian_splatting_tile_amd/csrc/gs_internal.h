@@ -36,6 +36,38 @@ __device__ __forceinline__ Rect tile_rect(float u, float v, float rf, float tile
 }
 
 // Camera as the kernels take it (by value, in the kernel argument segment).
+// Principal frame of a 2D conic [[a, b], [b, c]] in fp64: the unit
+// eigenvector (ex, ey) of the larger eigenvalue l1 and the smaller one l2;
+// the second axis is (-ey, ex).  Each component of the eigenvector is formed
+// without cancellation; an isotropic conic gets the x axis.  The blend
+// backward expresses the covariance gradient in this frame and the
+// projection backward maps it back with the same frame.
+__device__ __forceinline__ void conic_frame(double a, double b, double c, double &ex, double &ey, double &l1,
+                                            double &l2)
+{
+    const double hd = 0.5 * (a - c);
+    const double h = sqrt(hd * hd + b * b);
+    l1 = 0.5 * (a + c) + h;
+    l2 = 0.5 * (a + c) - h;       // relative error ~1e-16 l1 / l2, ample in fp64
+    double vx, vy;
+    if (hd >= 0.0) {
+        vx = hd + h;
+        vy = b;
+    } else {
+        vx = b;
+        vy = h - hd;
+    }
+    const double nrm = sqrt(vx * vx + vy * vy);
+    if (nrm > 0.0) {
+        const double inv = 1.0 / nrm;
+        ex = vx * inv;
+        ey = vy * inv;
+    } else {
+        ex = 1.0;
+        ey = 0.0;
+    }
+}
+
 struct Cam {
     int width, height, tiles_x, tiles_y;
     float fx, fy, cx, cy;

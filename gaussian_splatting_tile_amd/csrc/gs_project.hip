@@ -324,12 +324,14 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward: the screen-space gradients d/du, d/dv, d/da, d/db, d/dc,
-// d/dopacity, d/drgb (summed from the compositing pass's per-tile partials)
-// -> raw parameter gradients, +=.  The forward
-// sequence above is recomputed; the guard clamp and the colour clamp keep the
-// branch the forward took.
-//   conic = Sigma'^-1:      dSigma' = -Q A Q, A = [[da, db/2], [db/2, dc]]
+// Backward: the screen-space gradients d/du, d/dv, d/dSigma' (xx, xy, yy,
+// per element of the symmetric matrix), d/dopacity, d/drgb (summed from the
+// compositing pass's per-tile partials) -> raw parameter gradients, +=.  The
+// forward sequence above is recomputed; the guard clamp and the colour clamp
+// keep the branch the forward took.  The compositing pass already carried
+// the conic's gradient through the record's conic per pixel; the fp64
+// inverse replaces it below.
+//   Sigma' = Sigma2 + 0.3 I: dSigma2 = dSigma'
 //   Sigma2 = T Sigma T^T:   dSigma = T^T dSigma2 T,  dT = 2 dSigma2 T Sigma
 //   T = J W:                dJ = dT W^T;  J and (u, v) differentiated in (x, y, z)
 //   Sigma = M M^T:          dM = 2 dSigma M;  ds_j = sum_i Rq_ij dM_ij;  dRq = dM diag(s)
@@ -354,21 +356,27 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(int n, const Splat
     if (gl >= kSumPerWave) return;
     const int g = wave * kSumPerWave + gl;
     if (g >= n) return;
-    float acc = 0.0f;
-    if (__float_as_int(splats[g].a.w) != 0) {
-        const uint64_t first = first_slot[g];
-        uint64_t last = first + __float_as_uint(splats[g].c.w);
-        if (last > k_capacity) last = k_capacity;
-        // eight independent loads in flight per step; the sum stays in slot order
-        for (uint64_t sl = first; sl < last; sl += 8) {
+    // fp64: a large Gaussian sums thousands of per-tile partials
+    double acc = 0.0;
+    // (first_slot is not written for culled Gaussians; it is read, not used)
+    const int radius = __float_as_int(splats[g].a.w);
+    const uint32_t tiles = __float_as_uint(splats[g].c.w);
+    const uint32_t first = first_slot[g];
+    if (radius != 0) {
+        const uint64_t end64 = (uint64_t)first + tiles;
+        const uint32_t last = (uint32_t)(end64 < k_capacity ? end64 : k_capacity);
+        // eight loads in flight per step, none predicated (indices past the
+        // Gaussian's last slot re-read that slot and add nothing); the sum
+        // stays in slot order
+        for (uint32_t sl = first; sl < last; sl += 8) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) v[j] = sl + j < last ? partial[(sl + j) * 9 + q] : 0.0f;
+            for (int j = 0; j < 8; j++) v[j] = partial[(size_t)min(sl + j, last - 1) * 9 + q];
 #pragma unroll
-            for (int j = 0; j < 8; j++) acc += v[j];
+            for (int j = 0; j < 8; j++) acc += sl + j < last ? (double)v[j] : 0.0;
         }
     }
-    g2[(size_t)q * n + g] = acc;
+    g2[(size_t)q * n + g] = (float)acc;
 }
 
 template <int DEG, typename TSH>
@@ -425,8 +433,16 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
         dmu_c[2] = (dd[2] - dz * ddot) / dn;
     }
 
-    const double gu = g2[0], gv = g2[1];
-    const double ga = g2[2], gb = g2[3], gc = g2[4];
+    // The compositing pass worked in the principal frame V of the record's
+    // conic Qr: mean gradient V (g0, g1), covariance gradient V W V^T.
+    double ex, ey;
+    {
+        const float4 cr = splats[g].b;
+        double l1, l2;
+        conic_frame(cr.x, cr.y, cr.z, ex, ey, l1, l2);
+    }
+    const double gu = ex * (double)g2[0] - ey * (double)g2[1];
+    const double gv = ey * (double)g2[0] + ex * (double)g2[1];
     const float go = g2[5];
     const float s[3] = {scales[g], scales[n + g], scales[2 * n + g]};
     const float o = opac[g];
@@ -441,13 +457,30 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
     for (int i = 0; i < 9; i++) R[i] = cam.R[i];
     const double z = G.z;
 
-    const double q00 = G.p11 / G.det, q01 = -(G.p01 / G.det), q11 = G.p00 / G.det;
-    const double A00 = ga, A01 = 0.5 * gb, A11 = gc;
-    const double QA00 = q00 * A00 + q01 * A01, QA01 = q00 * A01 + q01 * A11;
-    const double QA10 = q01 * A00 + q11 * A01, QA11 = q01 * A01 + q11 * A11;
-    const double D00 = -(QA00 * q00 + QA01 * q01);
-    const double D01 = -(QA00 * q01 + QA01 * q11);
-    const double D11 = -(QA10 * q01 + QA11 * q11);
+    // dL/dSigma' (= dL/dSigma2, the dilation is additive), per element.  The
+    // compositing pass summed W = V^T Qr (-A) Qr V with the record's fp32
+    // conic Qr (A = dL/dconic); the derivative through the exact inverse is
+    // -Q A Q = F W F^T with Q = Sigma'^-1 in fp64 and F = Q Qr^-1 V, a
+    // rotation up to the rounding of the fp32 conic.
+    double D00, D01, D11;
+    {
+        const double q00 = G.p11 / G.det, q01 = -(G.p01 / G.det), q11 = G.p00 / G.det;
+        const float4 cr = splats[g].b;
+        const double ra = cr.x, rb = cr.y, rc = cr.z;
+        const double rdet = ra * rc - rb * rb;
+        const double i00 = rc / rdet, i01 = -rb / rdet, i11 = ra / rdet;   // Qr^-1
+        const double E00 = q00 * i00 + q01 * i01, E01 = q00 * i01 + q01 * i11;
+        const double E10 = q01 * i00 + q11 * i01, E11 = q01 * i01 + q11 * i11;
+        // F = E V, V = [[ex, -ey], [ey, ex]]
+        const double F00 = E00 * ex + E01 * ey, F01 = -(E00 * ey) + E01 * ex;
+        const double F10 = E10 * ex + E11 * ey, F11 = -(E10 * ey) + E11 * ex;
+        const double W00 = g2[2], W01 = g2[3], W11 = g2[4];
+        const double P00 = F00 * W00 + F01 * W01, P01 = F00 * W01 + F01 * W11;
+        const double P10 = F10 * W00 + F11 * W01, P11 = F10 * W01 + F11 * W11;
+        D00 = P00 * F00 + P01 * F01;
+        D01 = P00 * F10 + P01 * F11;
+        D11 = P10 * F10 + P11 * F11;
+    }
     const double *T = G.T;
     double dS[3][3];
 #pragma unroll

@@ -132,11 +132,11 @@ __device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double4 &
     return c;
 }
 
-// o exp(power) at one pixel of the column; dy returned for the gradients.
-__device__ __forceinline__ float alpha_raw(const ColTerms &c, double qc, double v, double py, double &dy)
+// o exp(power) at one pixel of the column, dy = v - py.  A lane's pixels sit
+// at rows y0 + 4 r, so dy = (v - (y0 + 1/2)) - 4 r: both steps are exact in
+// fp64 (v is a float, the rest small integers and halves).
+__device__ __forceinline__ float alpha_raw(const ColTerms &c, double qc, double dy)
 {
-#pragma clang fp contract(off)
-    dy = v - py;
     const double e = fma(dy, fma(qc, dy, c.bdx), c.a0);
     return __builtin_amdgcn_exp2f((float)e);
 }
@@ -156,7 +156,7 @@ template <bool kBwd>
 __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
                                            const uint32_t *__restrict__ entry_slots, uint32_t b0, uint32_t end,
                                            uint32_t start, int x0, int y0, double2 *s_uv, double4 *s_q,
-                                           float4 *s_rgb, uint32_t *s_pos, float4 *s_conic, uint32_t *s_slot,
+                                           float4 *s_rgb, uint32_t *s_pos, uint32_t *s_slot, double4 *s_P,
                                            float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
@@ -177,8 +177,11 @@ __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, con
         stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
         s_pos[slot] = m - start;
         if (kBwd) {
-            s_conic[slot] = s.b;
             s_slot[slot] = entry_slots[m];
+            // w' = P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex))
+            double ex, ey, l1, l2;
+            conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
+            s_P[slot] = make_double4(l1 * ex, l1 * ey, -(l2 * ey), l2 * ex);
         }
     }
     return __popcll(mask);
@@ -206,13 +209,12 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
 
         // A pixel is live while T >= 1e-4; pixels outside the image start at
         // T = 0 and never composite.
-        double py[kPx];
+        const double py0 = (double)y0 + 0.5;
         float T[kPx], c0[kPx], c1[kPx], c2[kPx];
         uint32_t last[kPx];
 #pragma unroll
         for (int r = 0; r < kPx; r++) {
             const int y = y0 + 4 * r;
-            py[r] = (double)y + 0.5;
             T[r] = (x < cam.width && y < cam.height) ? 1.0f : 0.0f;
             c0[r] = c1[r] = c2[r] = 0.0f;
             last[r] = 0;
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
                 const float4 rgb = s_rgb[k];
                 const uint32_t pos = s_pos[k] + 1u;
                 const ColTerms ct = col_terms(uv, q, px);
+                const double dy0 = uv.y - py0;
 #pragma unroll
                 for (int r = 0; r < kPx; r++) {
-                    double dy;
-                    const float raw = alpha_raw(ct, q.z, uv.y, py[r], dy);
+                    const float raw = alpha_raw(ct, q.z, dy0 - 4.0 * r);
                     const float alpha = fminf(kAlphaMax, raw);
                     const bool take = T[r] >= kTMin && raw >= kAlphaMin;
                     const float w = take ? alpha * T[r] : 0.0f;
@@ -273,12 +275,19 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
 //   dL/drgb_i   = alpha_i T_i G
 //   dL/dalpha_i = T_i (<rgb_i, G> - <A, G>)
 //   below the cap: dL/do = exp(power) dL/dalpha, dL/dpower = alpha dL/dalpha
-//   power = -1/2 (a dx^2 + c dy^2) - b dx dy  (dx = u - px, dy = v - py):
-//     d/du = -(a dx + b dy), d/dv = -(c dy + b dx),
-//     d/da = -dx^2/2, d/db = -dx dy, d/dc = -dy^2/2.
-// A lane's four pixels share dx, so it accumulates S0 = sum dp, S1 = sum dp dy,
-// S2 = sum dp dy^2 (dp = dL/dpower) and forms the five conic/mean terms once.
-// The 9 per-lane values of a record are then summed over the wave by a split
+//   power = -1/2 d^T Q d, d = (u - px, v - py), Q = Sigma'^-1 = [[a, b], [b, c]]:
+//     with w = Q d:  d/d(u, v) = -w,  d/dSigma' = Q (d d^T / 2) Q = w w^T / 2.
+// The gradient goes to the dilated 2D covariance Sigma', expressed in the
+// principal frame V of Q (Q = V L V^T): w' = V^T w = L V^T d.  For a thin
+// Gaussian Q's eigenvalues differ by up to ~1e4; summed as conic gradients
+// or in image axes, fp32 rounding of the large-eigenvalue direction would
+// swamp the small one after the change of variables.  In the principal
+// frame each direction keeps its own relative precision.  w' is formed per
+// pixel in fp64 (no cancellation) and rounded once; a lane accumulates, over
+// its pixels with dp = dL/dpower,
+//   W1 = sum dp w'_1,  W2 = sum dp w'_2,  W11, W12, W22 = sum dp w' w'^T.
+// The 9 per-lane values of a record, (-W1, -W2, W11/2, W12/2, W22/2, dL/do,
+// dL/drgb), are then summed over the wave by a split
 // butterfly on VALU lane swaps and DPP moves (each exchange halves the values
 // a lane carries) and nine lanes store the totals at the record's
 // duplication slot, partial[slot][9]: every (Gaussian, tile) pair owns one
@@ -352,7 +361,7 @@ __device__ __forceinline__ int reduce_slot(int lane)
     }
 }
 
-__global__ __launch_bounds__(kLanes) void render_bwd_kernel(
+__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) void render_bwd_kernel(
     const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
     const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, const uint32_t *__restrict__ entry_slots,
     Cam cam, float bg0, float bg1, float bg2, const float *__restrict__ final_T,
@@ -362,8 +371,8 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     __shared__ double4 s_q[kBatch];
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
-    __shared__ float4 s_conic[kBatch];
     __shared__ uint32_t s_slot[kBatch];
+    __shared__ double4 s_P[kBatch];
 
     const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
@@ -376,14 +385,13 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     const int y0 = ty * kTile + (lane >> 4);
     const double px = (double)x + 0.5;
 
-    double py[kPx];
+    const double py0 = (double)y0 + 0.5;
     float T[kPx], G0[kPx], G1[kPx], G2[kPx], AG[kPx];
     uint32_t last[kPx];
     uint32_t lmax = 0;
 #pragma unroll
     for (int r = 0; r < kPx; r++) {
         const int y = y0 + 4 * r;
-        py[r] = (double)y + 0.5;
         T[r] = 1.0f;
         G0[r] = G1[r] = G2[r] = 0.0f;
         last[r] = 0;
@@ -406,21 +414,20 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
         const uint32_t bbeg = (uint32_t)max((int64_t)start, bend - kBatch);
         const int nb = stage_batch<true>(splats, vals, entry_slots, bbeg, (uint32_t)bend, start, tx * kTile,
-                                         ty * kTile, s_uv, s_q, s_rgb, s_pos, s_conic, s_slot, partial);
+                                         ty * kTile, s_uv, s_q, s_rgb, s_pos, s_slot, s_P, partial);
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
             const uint32_t pos = s_pos[k];                     // list position
             const double2 uv = s_uv[k];
             const double4 q = s_q[k];
             const ColTerms ct = col_terms(uv, q, px);
-            float raws[kPx], dys[kPx];
+            const double dy0 = uv.y - py0;
+            float raws[kPx];
             bool take[kPx];
             bool any = false;
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
-                double dy;
-                raws[r] = alpha_raw(ct, q.z, uv.y, py[r], dy);
-                dys[r] = (float)dy;
+                raws[r] = alpha_raw(ct, q.z, dy0 - 4.0 * r);
                 take[r] = pos < last[r] && raws[r] >= kAlphaMin;
                 any = any || take[r];
             }
@@ -430,7 +437,10 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
             }
             const float4 col = s_rgb[k];
             const float inv_o = __builtin_amdgcn_rcpf(col.w);
-            float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f, S0 = 0.0f, S1 = 0.0f, S2 = 0.0f;
+            const double4 P = s_P[k];
+            const double p1dx = P.x * ct.dx, p2dx = P.z * ct.dx;
+            float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f;
+            float W1 = 0.0f, W2 = 0.0f, W11 = 0.0f, W12 = 0.0f, W22 = 0.0f;
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
                 if (!take[r]) continue;
@@ -448,20 +458,23 @@ __global__ __launch_bounds__(kLanes) void render_bwd_kernel(
                 if (raw < kAlphaMax) {
                     go = fmaf(dla, raw * inv_o, go);
                     const float dp = dla * alpha;
-                    const float t = dp * dys[r];
-                    S0 += dp;
-                    S1 += t;
-                    S2 = fmaf(t, dys[r], S2);
+                    const double dy = dy0 - 4.0 * r;
+                    const float w1 = (float)fma(P.y, dy, p1dx);
+                    const float w2 = (float)fma(P.w, dy, p2dx);
+                    const float t1 = dp * w1, t2 = dp * w2;
+                    W1 += t1;
+                    W2 += t2;
+                    W11 = fmaf(t1, w1, W11);
+                    W12 = fmaf(t1, w2, W12);
+                    W22 = fmaf(t2, w2, W22);
                 }
             }
-            const float4 cn = s_conic[k];
-            const float dx = (float)ct.dx;
             float v[9];
-            v[0] = -(cn.x * dx * S0 + cn.y * S1);
-            v[1] = -(cn.z * S1 + cn.y * dx * S0);
-            v[2] = -0.5f * dx * dx * S0;
-            v[3] = -dx * S1;
-            v[4] = -0.5f * S2;
+            v[0] = -W1;
+            v[1] = -W2;
+            v[2] = 0.5f * W11;
+            v[3] = 0.5f * W12;
+            v[4] = 0.5f * W22;
             v[5] = go;
             v[6] = g6;
             v[7] = g7;

@@ -63,9 +63,12 @@ def _gpu_grads(sc, views_and_G, sh=None):
     return {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
 
 
-def _compare(gpu, ref, near_clamp, name, rel=1e-3):
+def _compare(gpu, ref, near_clamp, name, rel=1e-3, floor=1e-3):
     """Per tensor: relative L2 error <= rel, and elementwise
-    |g - r| <= rel * max(|r|, 1e-2 * max|r|)."""
+    |g - r| <= rel * max(|r|, floor * max|r|).  The floor stands for the
+    fp32 accumulation error of an element that is a near-cancelling sum of
+    per-pixel terms; the worst element at the looser floor 1e-2 is reported
+    too."""
     report = {}
     for k in NAMES:
         g, r = gpu[k], ref[k]
@@ -78,14 +81,19 @@ def _compare(gpu, ref, near_clamp, name, rel=1e-3):
             assert np.abs(g).max(initial=0.0) == 0.0, (name, k)
             continue
         l2 = np.linalg.norm(g - r) / np.linalg.norm(r)
-        bound = rel * np.maximum(np.abs(r), 1e-2 * scale)
-        frac_bad = float(np.mean(np.abs(g - r) > bound))
-        worst = float((np.abs(g - r) / np.maximum(np.abs(r), 1e-2 * scale)).max())
-        report[k] = dict(rel_l2=float(l2), worst_rel=worst, frac_over=frac_bad)
+        err = np.abs(g - r)
+        rep = dict(rel_l2=float(l2))
+        for f in (floor, 1e-2):
+            den = np.maximum(np.abs(r), f * scale)
+            rel_e = err / den
+            i = int(np.argmax(rel_e))
+            rep[f"floor{f:g}"] = dict(worst=float(rel_e.flat[i]), frac_over=float(np.mean(rel_e > rel)),
+                                      at=(float(g.flat[i]), float(r.flat[i])), max=float(scale))
+        report[k] = rep
     say(f"[gpu] {name}: {report}")
     for k, rep in report.items():
         assert rep["rel_l2"] <= rel, (name, k, rep)
-        assert rep["frac_over"] == 0.0, (name, k, rep)
+        assert rep[f"floor{floor:g}"]["frac_over"] == 0.0, (name, k, rep)
     return report
 
 
