@@ -9,6 +9,11 @@ timed region.  One step = the whole hot path for all 8 views: project,
 bin + sort, blend forward, then blend backward and the projection's chain
 rule against an upstream dL/dimage ~ N(0, 1e-2).
 
+Other workloads: scene_5m (5M Gaussians, same law, 1920x1080, 8 views) and
+scene_10m_4k (10M Gaussians, SH stored fp16, 3840x2160, f = 2800; each step
+first builds the importance mask keeping 30 % of the Gaussians by their
+Exp(1) scores, and the projection applies it and the 0.5 px LOD gate).
+
 Prints ONE JSON line: value = forward ms/frame (project + bin/sort + blend),
 plus fwd+bwd ms/frame, per-call averages, the roofline of the dominant
 kernel (the forward blend, one kernel per gs_render_fwd call, timed with
@@ -32,10 +37,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="scene_1m", choices=["scene_1m", "box_100k", "tiny_1k"])
+    ap.add_argument("--workload", default="scene_1m",
+                    choices=["scene_1m", "scene_5m", "scene_10m_4k", "box_100k", "tiny_1k"])
     ap.add_argument("--views", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size kernel for "
+                         "calibrating the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -69,9 +78,24 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.calib_copy_mib > 0:
+        words = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(words, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
+
     t0 = time.time()
     if args.workload == "scene_1m":
         sc = scenes.scene_like(seed=3, n=1_000_000, upstream=True, name="scene_1m_sh3_1080p")
+    elif args.workload == "scene_5m":
+        sc = scenes.config(4)
+    elif args.workload == "scene_10m_4k":
+        sc = scenes.config(5)
     elif args.workload == "box_100k":
         sc = scenes.box()
         sc.upstream_seed = 22
@@ -83,9 +107,19 @@ def main():
 
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities),
-             sh=f(sc.sh))
-    gs = B.gaussians_struct(g, sc.sh_degree)
+             sh=f(sc.sh_fp16 if sc.sh_fp16 is not None else sc.sh))
     stream = torch.cuda.current_stream()
+    # importance mask (a global pre-pass of every step when the workload has scores)
+    use_mask = sc.importance is not None
+    if use_mask:
+        keep = scenes.keep_count(sc.n, sc.keep_fraction)
+        scores = f(sc.importance)
+        mask = torch.zeros(sc.n, dtype=torch.uint8, device=dev)
+        mask_ws = torch.empty(B.active_mask_workspace_bytes(sc.n), dtype=torch.uint8, device=dev)
+        B.active_mask(scores, sc.n, keep, mask, mask_ws, stream)
+        gs = B.gaussians_struct(g, sc.sh_degree, mask)
+    else:
+        gs = B.gaussians_struct(g, sc.sh_degree)
 
     # per-view buffers with the exact key capacity (K is deterministic)
     bufs, Ks = [], []
@@ -108,7 +142,7 @@ def main():
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
 
-    names = ("project", "bin_sort", "render_fwd", "render_bwd")
+    names = ("active_mask", "project", "bin_sort", "render_fwd", "render_bwd")
     ev = {k: [] for k in names}
     step_ev = []
 
@@ -131,6 +165,8 @@ def main():
             b.record(stream)
             ev[name].append((a, b))
 
+        if use_mask:
+            timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
         for b in bufs:
             timed("project", lambda: B.project(gs, b.camc, b.splats, stream))
             timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
@@ -174,8 +210,10 @@ def main():
     t_blend_s = per_call["render_fwd"] / 1e3
     achieved = pn_mean * BLEND_FWD_SLOTS_PER_PAIR / t_blend_s / 1e12
 
+    cam0 = sc.cameras[0]
     res = {
-        "metric": "ms/frame fwd (+fwd+bwd) at 1M Gaussians SH3 1920x1080; % VALU / HBM peak",
+        "metric": (f"ms/frame fwd (+fwd+bwd) at {sc.n / 1e6:g}M Gaussians SH{sc.sh_degree} "
+                   f"{cam0.width}x{cam0.height}; % VALU / HBM peak"),
         "value": round(fwd_ms, 4),
         "unit": "ms/frame",
         "n_gpus": 1,
@@ -185,12 +223,15 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if sc.sh_fp16 is None else "f32 (SH stored f16)",
         "data": "synthetic (seeded scene generator; no dataset)",
         "config": {"workload": sc.name, "gaussians": sc.n, "sh_degree": sc.sh_degree,
                    "width": sc.cameras[0].width, "height": sc.cameras[0].height, "views_per_step": views,
-                   "step": "all views: project + bin/sort + blend fwd" + (", then blend bwd + project bwd"
-                                                                          if do_bwd else "")},
+                   "importance_keep": (keep if use_mask else None),
+                   "lod_min_radius_px": cam0.lod_min_radius_px,
+                   "step": ("importance mask, then " if use_mask else "") +
+                           "all views: project + bin/sort + blend fwd" +
+                           (", then blend bwd + project bwd" if do_bwd else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,
         "per_call_ms": {k: (round(v, 4) if v is not None else None) for k, v in per_call.items()},
@@ -199,14 +240,43 @@ def main():
         "P_needed_per_view": p_need,
         "roofline": {"kernel": "render_fwd_kernel (forward blend)", "bound": "alu",
                      "achieved": round(achieved, 3), "peak": round(VALU_PEAK_T, 2), "unit": "TFLOP/s",
-                     "frac": round(achieved / VALU_PEAK_T, 4), "traffic": None,
+                     "frac": round(achieved / VALU_PEAK_T, 4),
+                     "traffic": measured_traffic() if args.workload == "scene_1m" else None,
                      "work_unit": f"{BLEND_FWD_SLOTS_PER_PAIR} fp32 VALU lane-op slots per evaluated "
                                   f"(pixel, Gaussian) pair whose entry can reach alpha >= 1/255 in its tile "
                                   f"(P_needed); peak = 256 CU x 64 lanes x 2.4 GHz"},
     }
-    if not args.no_cpu_baseline:
+    # the oracle is timed beside the default workload only (a 10M / 4K view
+    # takes it minutes)
+    if not args.no_cpu_baseline and args.workload == "scene_1m":
         res["cpu_baseline"] = cpu_baseline(sc)
     print(json.dumps(res), flush=True)
+
+
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "traffic_scene_1m_sh3_1080p.md")
+TRAFFIC_SOURCES = ("gaussian_splatting_tile_amd/csrc/gs_render.hip", "gaussian_splatting_tile_amd/csrc/gs_internal.h")
+
+
+def measured_traffic():
+    """HBM bytes per forward-blend launch from the committed counter summary,
+    or None when the kernel source has changed since the counters were taken
+    (the summary records the sources' sha256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch:", "source_sha256")))
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(root, f), "rb").read())
+    recorded = next((v for k, v in fields.items() if k.startswith("source_sha256")), None)
+    if recorded is None or recorded.strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def blend_pairs(torch, b):
