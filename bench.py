@@ -6,8 +6,9 @@ Workload (default): 1M Gaussians, SH degree 3, fp32, the scene-like mixture
 (64 anisotropic clusters + a background shell at radius 50), 1920x1080,
 fx = fy = 1400, 8 orbit views; synthetic, seeded, resident in HBM before the
 timed region.  One step = the whole hot path for all 8 views: project,
-bin + sort, blend forward, then blend backward and the projection's chain
-rule against an upstream dL/dimage ~ N(0, 1e-2).
+bin + sort, blend forward, then per view the screen-space backward against an
+upstream dL/dimage ~ N(0, 1e-2), and the projection's chain rule for all 8
+views in one batched pass.
 
 Other workloads: scene_5m (5M Gaussians, same law, 1920x1080, 8 views) and
 scene_10m_4k (10M Gaussians, SH stored fp16, 3840x2160, f = 2800; each step
@@ -132,7 +133,8 @@ def main():
         del probe
         b = B.ViewBuffers(sc.n, cam, k)
         b.dL = f(sc.upstream(v))
-        b.bwd_ws = b.backward_workspace(dev)
+        b.bwd_ws = torch.empty(B.render_bwd_screen_workspace_bytes(k), dtype=torch.uint8, device=dev)
+        b.g2 = torch.empty((9, sc.n), dtype=torch.float32, device=dev)
         bufs.append(b)
         Ks.append(k)
     K_sh = (sc.sh_degree + 1) ** 2
@@ -142,7 +144,7 @@ def main():
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
 
-    names = ("active_mask", "project", "bin_sort", "render_fwd", "render_bwd")
+    names = ("active_mask", "project", "bin_sort", "render_fwd", "render_bwd_screen", "project_bwd_batch")
     ev = {k: [] for k in names}
     step_ev = []
 
@@ -176,8 +178,12 @@ def main():
                                                      b.image, b.final_T, b.n_contrib, stream))
         e_fwd1.record(stream)
         if do_bwd:
+            # per view the screen-space backward, then the chain rule of all
+            # views in one pass over the Gaussians
             for b in bufs:
-                timed("render_bwd", lambda: b.backward(gs, b.dL, grads, b.bwd_ws, bg, stream))
+                timed("render_bwd_screen", lambda: b.backward_screen(b.dL, b.g2, b.bwd_ws, bg, stream))
+            timed("project_bwd_batch", lambda: B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs],
+                                                             [b.g2 for b in bufs], grads, stream))
         e_end.record(stream)
         if record:
             step_ev.append((e_fwd0, e_fwd1, e_end))
@@ -231,7 +237,7 @@ def main():
                    "lod_min_radius_px": cam0.lod_min_radius_px,
                    "step": ("importance mask, then " if use_mask else "") +
                            "all views: project + bin/sort + blend fwd" +
-                           (", then blend bwd + project bwd" if do_bwd else "")},
+                           (", then blend bwd per view + one batched project bwd" if do_bwd else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,
         "per_call_ms": {k: (round(v, 4) if v is not None else None) for k, v in per_call.items()},

@@ -44,7 +44,8 @@ class GsError(RuntimeError):
 _lib = None
 SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
            "gs_render_fwd",
-           "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_active_mask_workspace_bytes",
+           "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
+           "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
            "gs_active_mask", "gs_status_string", "gs_version")
 
 
@@ -77,13 +78,20 @@ def lib():
     L.gs_render_bwd_workspace_bytes.restype = sz
     L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, i64, vp, vp,
                                 vp, vp, C.POINTER(GsGrads), vp, sz, vp]
+    L.gs_render_bwd_screen_workspace_bytes.argtypes = [i64]
+    L.gs_render_bwd_screen_workspace_bytes.restype = sz
+    L.gs_render_bwd_screen.argtypes = [C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp,
+                                       vp, sz, vp]
+    L.gs_project_bwd.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp),
+                                 C.POINTER(vp), C.POINTER(GsGrads), vp]
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
     L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
-    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_bwd", "gs_active_mask"):
+    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_bwd", "gs_render_bwd_screen",
+                 "gs_project_bwd", "gs_active_mask"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -189,6 +197,32 @@ def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, schedu
            "gs_render_bwd")
 
 
+def render_bwd_screen_workspace_bytes(k_capacity: int) -> int:
+    return int(lib().gs_render_bwd_screen_workspace_bytes(k_capacity))
+
+
+def render_bwd_screen(cam: GsCamera, n, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg, final_T,
+                      n_contrib, dL_dimage, g2, workspace, stream=None):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    _check(lib().gs_render_bwd_screen(C.byref(cam), int(n), _ptr(splats), _ptr(vals), _ptr(tile_ranges),
+                                      _ptr(schedule), _ptr(bwd_index), int(k_capacity), C.cast(bgv, C.c_void_p),
+                                      _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(g2), _ptr(workspace),
+                                      _nbytes(workspace), _stream(stream)), "gs_render_bwd_screen")
+
+
+def project_bwd(gs: GsGaussians, cams, splats_list, g2_list, grads: Dict[str, torch.Tensor], stream=None):
+    """Chain rule of a batch of views: cams is a list of GsCamera, splats_list
+    and g2_list the matching device tensors."""
+    nv = len(cams)
+    cam_arr = (GsCamera * max(nv, 1))(*cams)
+    sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
+    g2_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in g2_list])
+    gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
+                 _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
+    _check(lib().gs_project_bwd(C.byref(gs), nv, cam_arr, sp_arr, g2_arr, C.byref(gr), _stream(stream)),
+           "gs_project_bwd")
+
+
 def active_mask_workspace_bytes(n: int) -> int:
     return int(lib().gs_active_mask_workspace_bytes(n))
 
@@ -235,6 +269,11 @@ class ViewBuffers:
 
     def backward_workspace(self, device="cuda"):
         return torch.empty(render_bwd_workspace_bytes(self.n, self.k_capacity), dtype=torch.uint8, device=device)
+
+    def backward_screen(self, dL_dimage, g2, workspace, bg=(0.0, 0.0, 0.0), stream=None):
+        """Screen-space backward of this view into g2 [9][n] (for project_bwd)."""
+        render_bwd_screen(self.camc, self.n, self.splats, self.vals, self.ranges, self.schedule, self.bwd_index,
+                          self.k_capacity, bg, self.final_T, self.n_contrib, dL_dimage, g2, workspace, stream)
 
     def backward(self, gs: GsGaussians, dL_dimage, grads, workspace, bg=(0.0, 0.0, 0.0), stream=None):
         render_bwd(gs, self.camc, self.splats, self.vals, self.ranges, self.schedule, self.bwd_index,

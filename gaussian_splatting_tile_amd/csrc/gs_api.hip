@@ -118,11 +118,55 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
                                       bg, image, final_T, n_contrib, (hipStream_t)stream));
 }
 
+static size_t partial_bytes(int64_t k_capacity) { return align_up((size_t)k_capacity * 9 * sizeof(float), 256); }
+
 size_t gs_render_bwd_workspace_bytes(int64_t n, int64_t k_capacity)
 {
     if (n < 0 || k_capacity < 0) return 0;
-    return align_up((size_t)k_capacity * 9 * sizeof(float), 256) + align_up((size_t)n * 9 * sizeof(float), 256) +
-           256;
+    return partial_bytes(k_capacity) + align_up((size_t)n * 9 * sizeof(float), 256) + 256;
+}
+
+size_t gs_render_bwd_screen_workspace_bytes(int64_t k_capacity)
+{
+    if (k_capacity < 0) return 0;
+    return partial_bytes(k_capacity) + 256;
+}
+
+// Checks shared by the two backward entry points that take a view's forward outputs.
+static gs_status screen_args_ok(const gs_camera *camera, int64_t n, const gs_splat *splats, const uint32_t *vals,
+                                const uint32_t *tile_ranges, const uint32_t *schedule, const uint32_t *bwd_index,
+                                int64_t k_capacity, const float *bg, const float *final_T,
+                                const uint32_t *n_contrib, const float *dL_dimage)
+{
+    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !final_T || !n_contrib || !dL_dimage ||
+        n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
+        return GS_ERR_INVALID_ARG;
+    for (int c = 0; c < 3; c++)
+        if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
+    if (n > 0 && (!splats || !bwd_index)) return GS_ERR_INVALID_ARG;
+    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
+    return GS_OK;
+}
+
+static bool grads_ok(const gs_grads *grads, int64_t n)
+{
+    return grads && (n == 0 || (grads->means && grads->log_scales && grads->quats && grads->opacity_logits &&
+                                grads->sh));
+}
+
+// The blend backward and the per-Gaussian sums of one view into g2[9][n].
+static hipError_t screen_backward(int64_t n, const Cam &cam, const gs_splat *splats, const uint32_t *vals,
+                                  const uint32_t *tile_ranges, uint32_t *schedule, const uint32_t *bwd_index,
+                                  int64_t k_capacity, const float *bg, const float *final_T,
+                                  const uint32_t *n_contrib, const float *dL_dimage, float *g2, float *partial,
+                                  hipStream_t s)
+{
+    // every entry's nine partial sums are written by the blend backward
+    hipError_t e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, bwd_index, cam, bg,
+                                     final_T, n_contrib, dL_dimage, partial, s);
+    if (e != hipSuccess) return e;
+    return launch_sum_partials(n, (const Splat *)splats, partial, bwd_index + k_capacity, (uint64_t)k_capacity,
+                               g2, s);
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
@@ -133,28 +177,72 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
 {
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
-    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !final_T || !n_contrib || !dL_dimage ||
-        !grads || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
-        return GS_ERR_INVALID_ARG;
-    for (int c = 0; c < 3; c++)
-        if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
     const int64_t n = gaussians->n;
-    if (n > 0 && (!splats || !bwd_index || !grads->means || !grads->log_scales || !grads->quats ||
-                  !grads->opacity_logits || !grads->sh))
-        return GS_ERR_INVALID_ARG;
-    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
+    st = screen_args_ok(camera, n, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg, final_T,
+                        n_contrib, dL_dimage);
+    if (st != GS_OK) return st;
+    if (!grads_ok(grads, n)) return GS_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, k_capacity)) return GS_ERR_WORKSPACE;
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
     const Cam cam = make_cam(*camera);
-    // every entry's nine partial sums are written by the blend backward
     float *partial = (float *)workspace;
-    hipError_t e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, bwd_index, cam, bg, final_T,
-                          n_contrib, dL_dimage, partial, s);
+    float *g2 = (float *)((char *)workspace + partial_bytes(k_capacity));
+    hipError_t e = screen_backward(n, cam, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg, final_T,
+                                   n_contrib, dL_dimage, g2, partial, s);
     if (e != hipSuccess) return GS_ERR_HIP;
-    float *g2 = (float *)((char *)workspace + align_up((size_t)k_capacity * 9 * sizeof(float), 256));
-    return from_hip(launch_project_bwd(*gaussians, cam, (const Splat *)splats, partial, bwd_index + k_capacity,
-                                       (uint64_t)k_capacity, g2, *grads, s));
+    ViewBatch vb;
+    vb.count = 1;
+    vb.cam[0] = cam;
+    vb.splats[0] = (const Splat *)splats;
+    vb.g2[0] = g2;
+    return from_hip(launch_project_bwd(*gaussians, vb, *grads, s));
+}
+
+gs_status gs_render_bwd_screen(const gs_camera *camera, int64_t n, const gs_splat *splats, const uint32_t *vals,
+                               const uint32_t *tile_ranges, uint32_t *schedule, const uint32_t *bwd_index,
+                               int64_t k_capacity, const float *bg, const float *final_T,
+                               const uint32_t *n_contrib, const float *dL_dimage, float *g2, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    gs_status st = screen_args_ok(camera, n, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg,
+                                  final_T, n_contrib, dL_dimage);
+    if (st != GS_OK) return st;
+    if (n > 0 && !g2) return GS_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < gs_render_bwd_screen_workspace_bytes(k_capacity)) return GS_ERR_WORKSPACE;
+    if (n == 0) return GS_OK;
+    return from_hip(screen_backward(n, make_cam(*camera), splats, vals, tile_ranges, schedule, bwd_index,
+                                    k_capacity, bg, final_T, n_contrib, dL_dimage, g2, (float *)workspace,
+                                    (hipStream_t)stream));
+}
+
+gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                         const gs_splat *const *splats, const float *const *g2, const gs_grads *grads, void *stream)
+{
+    gs_status st = gaussians_ok(gaussians);
+    if (st != GS_OK) return st;
+    const int64_t n = gaussians->n;
+    if (n_views < 0 || (n_views > 0 && (!cameras || !splats || !g2)) || !grads_ok(grads, n))
+        return GS_ERR_INVALID_ARG;
+    for (int v = 0; v < n_views; v++) {
+        if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
+        if (n > 0 && (!splats[v] || !g2[v])) return GS_ERR_INVALID_ARG;
+    }
+    if (n == 0) return GS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    // batches of up to kMaxViews views per launch, in view order
+    for (int v0 = 0; v0 < n_views; v0 += kMaxViews) {
+        ViewBatch vb;
+        vb.count = n_views - v0 < kMaxViews ? n_views - v0 : kMaxViews;
+        for (int i = 0; i < vb.count; i++) {
+            vb.cam[i] = make_cam(cameras[v0 + i]);
+            vb.splats[i] = (const Splat *)splats[v0 + i];
+            vb.g2[i] = g2[v0 + i];
+        }
+        hipError_t e = launch_project_bwd(*gaussians, vb, *grads, s);
+        if (e != hipSuccess) return GS_ERR_HIP;
+    }
+    return GS_OK;
 }
 
 size_t gs_active_mask_workspace_bytes(int64_t n)

@@ -35,7 +35,6 @@ __device__ __forceinline__ Rect tile_rect(float u, float v, float rf, float tile
     return Rect{(int)fx0, (int)fx1, (int)fy0, (int)fy1};
 }
 
-// Camera as the kernels take it (by value, in the kernel argument segment).
 // Principal frame of a 2D conic [[a, b], [b, c]] in fp64: the unit
 // eigenvector (ex, ey) of the larger eigenvalue l1 and the smaller one l2;
 // the second axis is (-ey, ex).  Each component of the eigenvector is formed
@@ -68,6 +67,7 @@ __device__ __forceinline__ void conic_frame(double a, double b, double c, double
     }
 }
 
+// Camera as the kernels take it (by value, in the kernel argument segment).
 struct Cam {
     int width, height, tiles_x, tiles_y;
     float fx, fy, cx, cy;
@@ -106,9 +106,21 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- launch helpers (host) -------------------------------------------------
 hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s);
-hipError_t launch_project_bwd(const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                              const float *partial, const uint32_t *first_slot, uint64_t k_capacity,
-                              float *g2, const gs_grads &out, hipStream_t s);
+// Per-Gaussian screen-space gradients of one view, g2[9][n], from the
+// blend backward's per-slot partial sums.
+hipError_t launch_sum_partials(int64_t n, const Splat *splats, const float *partial, const uint32_t *first_slot,
+                               uint64_t k_capacity, float *g2, hipStream_t s);
+
+// Views whose screen-space gradients one projection-backward launch takes.
+constexpr int kMaxViews = 16;
+struct ViewBatch {
+    int count;
+    Cam cam[kMaxViews];
+    const Splat *splats[kMaxViews];
+    const float *g2[kMaxViews];
+};
+hipError_t launch_project_bwd(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out,
+                              hipStream_t s);
 
 struct SortWorkspace;
 size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles);

@@ -379,59 +379,122 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(int n, const Splat
     g2[(size_t)q * n + g] = (float)acc;
 }
 
+// The projection backward runs as two kernels over a batch of views, one
+// thread per Gaussian each: the colour part (SH gradients and the view
+// direction's share of the mean gradient, fp32 like the forward's colour)
+// and the geometry part (the fp64 chain rule).  Each reads the Gaussian's
+// parameters once for the whole batch and sums its gradients in registers
+// in view order; the SH gradients are updated in place per view (the lines
+// stay in cache between views).
+// Colour part: one lane per (Gaussian, channel), 21 Gaussians per wave with
+// the channel fastest.  A lane holds its channel's K coefficients and their
+// gradient sums in registers for the whole batch, so the SH rows are read
+// once and their gradients updated once.  Per view, for an unclamped channel:
+//   dk_j += Y_j(d) dL/drgb,   d(direction) += dL/drgb grad_d sum_j k_j Y_j(d);
+// the three channels' shares of the mean gradient are added across lanes.
+constexpr int kColourPerWave = 21;
 template <int DEG, typename TSH>
-__global__ __launch_bounds__(kBlock) void project_bwd_kernel(
-    int n, const float *__restrict__ means, const float *__restrict__ scales,
-    const float *__restrict__ quats, const float *__restrict__ opac, const TSH *__restrict__ sh,
-    Cam cam, const Splat *__restrict__ splats, const float *__restrict__ g2s,
-    float *__restrict__ d_means, float *__restrict__ d_log_scales, float *__restrict__ d_quats,
-    float *__restrict__ d_logits, float *__restrict__ d_sh)
+__global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const float *__restrict__ means,
+                                                                   const TSH *__restrict__ sh, const ViewBatch views,
+                                                                   float *__restrict__ d_means,
+                                                                   float *__restrict__ d_sh)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const int g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= n) return;
-    // culled Gaussians have radius 0 and receive nothing
-    const float4 ra = splats[g].a;
-    if (__float_as_int(ra.w) == 0) return;
-    float g2[9];
+    const int lane = threadIdx.x & 63;
+    const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
+    const int gl = lane / 3, ch = lane - 3 * gl;
+    const int g = wave * kColourPerWave + gl;
+    const bool valid = gl < kColourPerWave && g < n;
+    float kv[K], acc[K];
+    float mx = 0.0f, my = 0.0f, mz = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 9; q++) g2[q] = g2s[(size_t)q * n + g];
-    const float mx = means[g], my = means[n + g], mz = means[2 * n + g];
-
-    // colour (fp32, the forward's sequence, so the clamp decisions agree)
-    float dmu_c[3];
-    {
+    for (int j = 0; j < K; j++) {
+        kv[j] = valid ? ld_sh(sh + (size_t)(j * 3 + ch) * n + g) : 0.0f;
+        acc[j] = 0.0f;
+    }
+    if (valid) {
+        mx = means[g];
+        my = means[n + g];
+        mz = means[2 * n + g];
+    }
+    float dm[3] = {0.0f, 0.0f, 0.0f};
+    bool visible = false;
+    for (int v = 0; v < views.count; v++) {
+        // culled Gaussians have radius 0 and receive nothing
+        if (!valid || __float_as_int(views.splats[v][g].a.w) == 0) continue;
+        visible = true;
+        const Cam &cam = views.cam[v];
         float dx, dy, dz, dn;
         view_dir(cam, mx, my, mz, dx, dy, dz, dn);
-        float Y[K], w[K];
+        float Y[K];
         sh_basis<DEG>(dx, dy, dz, Y);
+        float sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < K; j++) w[j] = 0.0f;
+        for (int j = 0; j < K; j++) sum = sum + kv[j] * Y[j];
+        // the forward's clamp at 0 keeps its branch
+        if (0.5f + sum < 0.0f) continue;
+        const float gr = views.g2[v][(size_t)(6 + ch) * n + g];
 #pragma unroll
-        for (int ch = 0; ch < 3; ch++) {
-            float kv[K];
-            float sum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < K; j++) {
-                kv[j] = ld_sh(sh + ((size_t)(j * 3 + ch)) * n + g);
-                sum = sum + kv[j] * Y[j];
-            }
-            if (0.5f + sum < 0.0f) continue;
-            const float gr = g2[6 + ch];
-#pragma unroll
-            for (int j = 0; j < K; j++) {
-                float *p = d_sh + ((size_t)(j * 3 + ch)) * n + g;
-                *p = *p + Y[j] * gr;
-                w[j] = w[j] + kv[j] * gr;
-            }
-        }
+        for (int j = 0; j < K; j++) acc[j] = acc[j] + Y[j] * gr;
         float dd[3];
-        sh_dir_grad<DEG>(w, dx, dy, dz, dd);
+        sh_dir_grad<DEG>(kv, dx, dy, dz, dd);
+        dd[0] *= gr;
+        dd[1] *= gr;
+        dd[2] *= gr;
         const float ddot = dx * dd[0] + dy * dd[1] + dz * dd[2];
-        dmu_c[0] = (dd[0] - dx * ddot) / dn;
-        dmu_c[1] = (dd[1] - dy * ddot) / dn;
-        dmu_c[2] = (dd[2] - dz * ddot) / dn;
+        dm[0] += (dd[0] - dx * ddot) / dn;
+        dm[1] += (dd[1] - dy * ddot) / dn;
+        dm[2] += (dd[2] - dz * ddot) / dn;
     }
+    // channel lanes 3 gl + 1 and 3 gl + 2 hand their mean shares to 3 gl
+    float tot[3];
+#pragma unroll
+    for (int j = 0; j < 3; j++) {
+        const float a1 = __shfl(dm[j], lane + 1, 64), a2 = __shfl(dm[j], lane + 2, 64);
+        tot[j] = (dm[j] + a1) + a2;
+    }
+    if (!visible) return;
+#pragma unroll
+    for (int j = 0; j < K; j++) {
+        float *p = d_sh + (size_t)(j * 3 + ch) * n + g;
+        *p = *p + acc[j];
+    }
+    if (ch == 0) {
+#pragma unroll
+        for (int j = 0; j < 3; j++) d_means[j * n + g] += tot[j];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
+    int n, const float *__restrict__ means, const float *__restrict__ scales, const float *__restrict__ quats,
+    const float *__restrict__ opac, const ViewBatch views, float *__restrict__ d_means,
+    float *__restrict__ d_log_scales, float *__restrict__ d_quats, float *__restrict__ d_logits)
+{
+    const int g = blockIdx.x * kBlock + threadIdx.x;
+    if (g >= n) return;
+    const float mx0 = means[g], my0 = means[n + g], mz0 = means[2 * n + g];
+    const float s0 = scales[g], s1 = scales[n + g], s2 = scales[2 * n + g];
+    const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];
+    const float o = opac[g];
+    float acc_mean[3] = {0.0f, 0.0f, 0.0f}, acc_ls[3] = {0.0f, 0.0f, 0.0f};
+    float acc_q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc_logit = 0.0f;
+    bool touched = false;
+    for (int v = 0; v < views.count; v++) {
+    const Splat *__restrict__ splats = views.splats[v];
+    if (__float_as_int(splats[g].a.w) == 0) continue;
+    touched = true;
+    // The view-independent part (rotation, 3D covariance) is recomputed per
+    // view from opaque copies of the parameters: held across views in fp64
+    // it would cost ~50 registers.
+    float mx = mx0, my = my0, mz = mz0, qw = qw0, qx = qx0, qy = qy0, qz = qz0;
+    float s[3] = {s0, s1, s2};
+    asm volatile("" : "+v"(mx), "+v"(my), "+v"(mz), "+v"(qw), "+v"(qx), "+v"(qy), "+v"(qz));
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]));
+    const Cam &cam = views.cam[v];
+    const float *__restrict__ g2s = views.g2[v];
+    float g2[6];
+#pragma unroll
+    for (int q = 0; q < 6; q++) g2[q] = g2s[(size_t)q * n + g];
 
     // The compositing pass worked in the principal frame V of the record's
     // conic Qr: mean gradient V (g0, g1), covariance gradient V W V^T.
@@ -444,14 +507,11 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
     const double gu = ex * (double)g2[0] - ey * (double)g2[1];
     const double gv = ey * (double)g2[0] + ex * (double)g2[1];
     const float go = g2[5];
-    const float s[3] = {scales[g], scales[n + g], scales[2 * n + g]};
-    const float o = opac[g];
     // The chain rule runs in fp64 on a fp64 recomputation of the geometry:
     // for thin Gaussians the conic is ill-conditioned (eigenvalue ratios up
     // to ~1e5), and fp32 intermediates would cost several digits.
     GeoT<double> G;
-    geometry<double>(cam, mx, my, mz, s[0], s[1], s[2], quats[g], quats[n + g], quats[2 * n + g],
-                     quats[3 * n + g], G);
+    geometry<double>(cam, mx, my, mz, s[0], s[1], s[2], qw, qx, qy, qz, G);
     double R[9];
 #pragma unroll
     for (int i = 0; i < 9; i++) R[i] = cam.R[i];
@@ -553,16 +613,23 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(
     const double qh[4] = {w, a, b, c};
 
 #pragma unroll
-    for (int j = 0; j < 3; j++) {
-        const double dmu = R[j] * dpx + R[3 + j] * dpy + R[6 + j] * dpz;
-        d_means[j * n + g] += (float)dmu + dmu_c[j];
-    }
+    for (int j = 0; j < 3; j++) acc_mean[j] += (float)(R[j] * dpx + R[3 + j] * dpy + R[6 + j] * dpz);
 #pragma unroll
-    for (int r = 0; r < 3; r++) d_log_scales[r * n + g] += (float)((double)s[r] * ds[r]);
+    for (int r = 0; r < 3; r++) acc_ls[r] += (float)((double)s[r] * ds[r]);
 #pragma unroll
-    for (int r = 0; r < 4; r++) d_quats[r * n + g] += (float)((dq[r] - qh[r] * qdot) / G.nq);
-    d_logits[g] += o * (1.0f - o) * go;
+    for (int r = 0; r < 4; r++) acc_q[r] += (float)((dq[r] - qh[r] * qdot) / G.nq);
+    acc_logit += o * (1.0f - o) * go;
+    }   // views
+    if (!touched) return;
+#pragma unroll
+    for (int j = 0; j < 3; j++) d_means[j * n + g] += acc_mean[j];
+#pragma unroll
+    for (int j = 0; j < 3; j++) d_log_scales[j * n + g] += acc_ls[j];
+#pragma unroll
+    for (int j = 0; j < 4; j++) d_quats[j * n + g] += acc_q[j];
+    d_logits[g] += acc_logit;
 }
+
 
 template <int DEG, typename TSH>
 void launch_project_t(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s)
@@ -573,13 +640,15 @@ void launch_project_t(const gs_gaussians &g, const Cam &cam, Splat *splats, hipS
 }
 
 template <int DEG, typename TSH>
-void launch_project_bwd_t(const gs_gaussians &g, const Cam &cam, const Splat *splats, const float *g2,
-                          const gs_grads &out, hipStream_t s)
+void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
 {
     const int n = (int)g.n;
-    project_bwd_kernel<DEG, TSH><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, cam, splats, g2, out.means,
-        out.log_scales, out.quats, out.opacity_logits, out.sh);
+    const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
+    project_bwd_color_kernel<DEG, TSH><<<(unsigned)((colour_waves * 64 + kBlock - 1) / kBlock), kBlock, 0, s>>>(
+        n, g.means, (const TSH *)g.sh, views, out.means, out.sh);
+    project_bwd_geom_kernel<<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
+        n, g.means, g.scales, g.quats, g.opacities, views, out.means, out.log_scales, out.quats,
+        out.opacity_logits);
 }
 
 template <typename TSH>
@@ -594,14 +663,14 @@ void dispatch_project(int deg, const gs_gaussians &g, const Cam &cam, Splat *spl
 }
 
 template <typename TSH>
-void dispatch_project_bwd(int deg, const gs_gaussians &g, const Cam &cam, const Splat *splats, const float *g2,
-                          const gs_grads &out, hipStream_t s)
+void dispatch_project_bwd(int deg, const gs_gaussians &g, const ViewBatch &views, const gs_grads &out,
+                          hipStream_t s)
 {
     switch (deg) {
-    case 0: launch_project_bwd_t<0, TSH>(g, cam, splats, g2, out, s); break;
-    case 1: launch_project_bwd_t<1, TSH>(g, cam, splats, g2, out, s); break;
-    case 2: launch_project_bwd_t<2, TSH>(g, cam, splats, g2, out, s); break;
-    default: launch_project_bwd_t<3, TSH>(g, cam, splats, g2, out, s); break;
+    case 0: launch_project_bwd_t<0, TSH>(g, views, out, s); break;
+    case 1: launch_project_bwd_t<1, TSH>(g, views, out, s); break;
+    case 2: launch_project_bwd_t<2, TSH>(g, views, out, s); break;
+    default: launch_project_bwd_t<3, TSH>(g, views, out, s); break;
     }
 }
 
@@ -617,19 +686,24 @@ hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, 
     return hipGetLastError();
 }
 
-hipError_t launch_project_bwd(const gs_gaussians &g, const Cam &cam, const Splat *splats,
-                              const float *partial, const uint32_t *first_slot, uint64_t k_capacity,
-                              float *g2, const gs_grads &out, hipStream_t s)
+hipError_t launch_sum_partials(int64_t n64, const Splat *splats, const float *partial, const uint32_t *first_slot,
+                               uint64_t k_capacity, float *g2, hipStream_t s)
 {
-    if (g.n == 0) return hipSuccess;
-    const int n = (int)g.n;
+    if (n64 == 0) return hipSuccess;
+    const int n = (int)n64;
     const long long waves = (n + kSumPerWave - 1) / kSumPerWave;
     const unsigned blocks = (unsigned)((waves * 64 + kBlock - 1) / kBlock);
     sum_partials_kernel<<<blocks, kBlock, 0, s>>>(n, splats, partial, first_slot, k_capacity, g2);
+    return hipGetLastError();
+}
+
+hipError_t launch_project_bwd(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
+{
+    if (g.n == 0 || views.count == 0) return hipSuccess;
     if (g.sh_dtype == GS_SH_F16)
-        dispatch_project_bwd<__half>(g.sh_degree, g, cam, splats, g2, out, s);
+        dispatch_project_bwd<__half>(g.sh_degree, g, views, out, s);
     else
-        dispatch_project_bwd<float>(g.sh_degree, g, cam, splats, g2, out, s);
+        dispatch_project_bwd<float>(g.sh_degree, g, views, out, s);
     return hipGetLastError();
 }
 

@@ -11,7 +11,10 @@
  *                  list;
  *   gs_render_bwd  reverse pass through the compositing and the projection:
  *                  gradients with respect to means, log-scales, quaternions,
- *                  opacity logits and SH coefficients (accumulated).
+ *                  opacity logits and SH coefficients (accumulated); also
+ *                  available split as gs_render_bwd_screen per view and
+ *                  gs_project_bwd over a batch of views.
+ * gs_active_mask builds the optional importance mask that gs_project honours.
  *
  * Where the pages touch this path (they give no formulas):
  *   - Gaussians are projected onto the image plane over screen tiles and
@@ -223,6 +226,48 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
                         const float *final_T, const uint32_t *n_contrib,
                         const float *dL_dimage, const gs_grads *grads /* host struct */,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same backward split in two, for batches of views: the screen-space
+ * part of one view (gs_render_bwd_screen) and the projection's chain rule of
+ * several views in one pass over the Gaussians (gs_project_bwd), which reads
+ * each Gaussian's parameters once per batch instead of once per view.
+ * gs_render_bwd(view) = gs_render_bwd_screen(view) + gs_project_bwd({view}). */
+
+/* Workspace for gs_render_bwd_screen, in bytes: nine fp32 partial sums per
+ * key slot, for a key capacity k_capacity. */
+size_t gs_render_bwd_screen_workspace_bytes(int64_t k_capacity);
+
+/* Screen-space backward of one view (the reverse compositing pass of
+ * gs_render_bwd and its per-Gaussian sum): writes g2[9][n] (device fp32,
+ * component-major, every Gaussian, zeros for those culled in the view).  The
+ * nine components are an internal representation that only gs_project_bwd
+ * reads with the same view's records: the mean gradient and the 2D
+ * covariance gradient in the principal frame of the record's conic, the
+ * opacity gradient and the colour gradient.  Arguments as gs_render_bwd; n is
+ * the number of Gaussians of the view's records.  Deterministic (no atomics).
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
+gs_status gs_render_bwd_screen(const gs_camera *camera /* host */, int64_t n,
+                               const gs_splat *splats, const uint32_t *vals,
+                               const uint32_t *tile_ranges, uint32_t *schedule,
+                               const uint32_t *bwd_index, int64_t k_capacity,
+                               const float *bg /* host [3] */, const float *final_T,
+                               const uint32_t *n_contrib, const float *dL_dimage,
+                               float *g2, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Projection backward of n_views views (the chain rule of the EWA projection
+ * and the SH colour, as in gs_render_bwd): grads += sum over the views of the
+ * raw-parameter gradients, the views taken in order.
+ *   cameras  host gs_camera[n_views]
+ *   splats   host array of n_views device pointers: each view's records
+ *   g2       host array of n_views device pointers: each view's g2[9][n]
+ *            from gs_render_bwd_screen
+ * Up to 16 views go into one launch; longer batches take several.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED. */
+gs_status gs_project_bwd(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
+                         const gs_camera *cameras, const gs_splat *const *splats,
+                         const float *const *g2, const gs_grads *grads /* host struct */,
+                         void *stream);
 
 /* Workspace for gs_active_mask, in bytes. */
 size_t gs_active_mask_workspace_bytes(int64_t n);

@@ -59,6 +59,13 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
     assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    bgv = (C.c_float * 3)(0.0, 0.0, 0.0)
+    assert L.gs_render_bwd_screen(None, 10, None, None, None, None, None, 0, C.cast(bgv, C.c_void_p), None,
+                                  None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_project_bwd(C.byref(gs), 1, None, None, None, None, None) == B.GS_ERR_UNSUPPORTED
+    gs.sh_degree = 0
+    assert L.gs_project_bwd(C.byref(gs), -1, None, None, None, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_render_bwd_screen_workspace_bytes(1000) >= 1000 * 36
     assert L.gs_bin_sort_workspace_bytes(1000, 5000, 64) > 5000 * 12
     assert L.gs_render_bwd_workspace_bytes(1000, 4000) >= 5000 * 36
     assert L.gs_bwd_index_words(10, 100) == 110

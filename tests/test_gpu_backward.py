@@ -139,3 +139,38 @@ def test_backward_scene_5m_1080p_tile_sample():
     ref, Gz, nc, amb = _oracle_grads(sc, 0, G, tile_mask=tile_mask)
     gpu = _gpu_grads(sc, [(0, Gz)])
     _compare(gpu, ref, nc, "bwd scene_5m sample")
+
+
+def test_batched_projection_backward_matches_per_view_calls():
+    """gs_render_bwd_screen per view + one gs_project_bwd over the views gives
+    the per-view gs_render_bwd sum (up to the order of fp32 additions), and
+    the oracle's gradients."""
+    sc = scenes.scene_like(seed=9, n=40_000, width=480, height=272, f=350.0, n_views=3)
+    say("[gpu] batched projection backward, 3 views")
+    Gs = [_upstream(sc.cameras[v], 200 + v) for v in range(3)]
+    refs = [_oracle_grads(sc, v, Gs[v]) for v in range(3)]
+    ref = {k: sum(r[0][k] for r in refs) for k in NAMES}
+    nc = refs[0][2] | refs[1][2] | refs[2][2]
+    per_view = _gpu_grads(sc, [(v, refs[v][1]) for v in range(3)])
+    n = sc.n
+    grads = dict(means=torch.zeros((3, n), device="cuda"), log_scales=torch.zeros((3, n), device="cuda"),
+                 quats=torch.zeros((4, n), device="cuda"), opacity_logits=torch.zeros(n, device="cuda"),
+                 sh=torch.zeros((16, 3, n), device="cuda"))
+    bufs, g2s = [], []
+    for v in range(3):
+        buf, K = run_view(sc, v, with_keys=False)
+        ws = torch.empty(B.render_bwd_screen_workspace_bytes(buf.k_capacity), dtype=torch.uint8, device="cuda")
+        g2 = torch.full((9, n), float("nan"), device="cuda")
+        buf.backward_screen(torch.from_numpy(np.ascontiguousarray(refs[v][1])).cuda(), g2, ws)
+        bufs.append(buf)
+        g2s.append(g2)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(g).all()) for g in g2s)     # every Gaussian's row is written
+    gs = bufs[0]._keep[2]
+    B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs], g2s, grads)
+    torch.cuda.synchronize()
+    batched = {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    for k in NAMES:
+        scale = np.abs(per_view[k]).max()
+        assert np.abs(batched[k] - per_view[k]).max() <= 1e-5 * scale, k
+    _compare(batched, ref, nc, "bwd batched 3 views")
