@@ -26,6 +26,20 @@ class GsCamera(C.Structure):
                 ("znear", C.c_float), ("guard", C.c_float), ("lod_min_radius_px", C.c_float)]
 
 
+class GsFwdView(C.Structure):
+    _fields_ = [("camera", GsCamera), ("splats", C.c_void_p), ("vals", C.c_void_p),
+                ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("image", C.c_void_p),
+                ("final_T", C.c_void_p), ("n_contrib", C.c_void_p)]
+
+
+class GsBwdView(C.Structure):
+    _fields_ = [("camera", GsCamera), ("n", C.c_int64), ("splats", C.c_void_p), ("vals", C.c_void_p),
+                ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("bwd_index", C.c_void_p),
+                ("k_capacity", C.c_int64), ("final_T", C.c_void_p), ("n_contrib", C.c_void_p),
+                ("dL_dimage", C.c_void_p), ("g2", C.c_void_p), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t)]
+
+
 class GsGaussians(C.Structure):
     _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("sh_dtype", C.c_int32),
                 ("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p),
@@ -43,6 +57,7 @@ class GsError(RuntimeError):
 
 _lib = None
 SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
+           "gs_render_fwd_views", "gs_render_bwd_screen_views",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
@@ -74,6 +89,8 @@ def lib():
     L.gs_bwd_index_words.restype = sz
     L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
+    L.gs_render_fwd_views.argtypes = [C.c_int32, C.POINTER(GsFwdView), vp, vp]
+    L.gs_render_bwd_screen_views.argtypes = [C.c_int32, C.POINTER(GsBwdView), vp, vp]
     L.gs_render_bwd_workspace_bytes.argtypes = [i64, i64]
     L.gs_render_bwd_workspace_bytes.restype = sz
     L.gs_render_bwd.argtypes = [C.POINTER(GsGaussians), C.POINTER(GsCamera), vp, vp, vp, vp, vp, i64, vp, vp,
@@ -90,7 +107,8 @@ def lib():
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
-    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_bwd", "gs_render_bwd_screen",
+    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_fwd_views", "gs_render_bwd",
+                 "gs_render_bwd_screen", "gs_render_bwd_screen_views",
                  "gs_project_bwd", "gs_active_mask"):
         getattr(L, name).restype = C.c_int
     _lib = L
@@ -181,6 +199,18 @@ def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[
                                _stream(stream)), "gs_render_fwd")
 
 
+def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None):
+    """gs_render_fwd_views over ViewBuffers objects (their splats, bins and
+    schedules must be current)."""
+    nv = len(bufs)
+    arr = (GsFwdView * max(nv, 1))()
+    for i, b in enumerate(bufs):
+        arr[i] = GsFwdView(b.camc, _ptr(b.splats), _ptr(b.vals), _ptr(b.ranges), _ptr(b.schedule),
+                           _ptr(b.image), _ptr(b.final_T), _ptr(b.n_contrib))
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    _check(lib().gs_render_fwd_views(nv, arr, C.cast(bgv, C.c_void_p), _stream(stream)), "gs_render_fwd_views")
+
+
 def render_bwd_workspace_bytes(n: int, k_capacity: int) -> int:
     return int(lib().gs_render_bwd_workspace_bytes(n, k_capacity))
 
@@ -208,6 +238,20 @@ def render_bwd_screen(cam: GsCamera, n, splats, vals, tile_ranges, schedule, bwd
                                       _ptr(schedule), _ptr(bwd_index), int(k_capacity), C.cast(bgv, C.c_void_p),
                                       _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(g2), _ptr(workspace),
                                       _nbytes(workspace), _stream(stream)), "gs_render_bwd_screen")
+
+
+def render_bwd_screen_views(bufs, dLs, g2s, workspaces, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None):
+    """gs_render_bwd_screen_views over ViewBuffers objects with their upstream
+    gradients, g2 outputs and workspaces."""
+    nv = len(bufs)
+    arr = (GsBwdView * max(nv, 1))()
+    for i, (b, dL, g2, ws) in enumerate(zip(bufs, dLs, g2s, workspaces)):
+        arr[i] = GsBwdView(b.camc, b.n, _ptr(b.splats), _ptr(b.vals), _ptr(b.ranges), _ptr(b.schedule),
+                           _ptr(b.bwd_index), b.k_capacity, _ptr(b.final_T), _ptr(b.n_contrib), _ptr(dL),
+                           _ptr(g2), _ptr(ws), _nbytes(ws))
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    _check(lib().gs_render_bwd_screen_views(nv, arr, C.cast(bgv, C.c_void_p), _stream(stream)),
+           "gs_render_bwd_screen_views")
 
 
 def project_bwd(gs: GsGaussians, cams, splats_list, g2_list, grads: Dict[str, torch.Tensor], stream=None):

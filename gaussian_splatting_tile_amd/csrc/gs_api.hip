@@ -114,8 +114,61 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
-    return from_hip(launch_render_fwd((const Splat *)splats, vals, tile_ranges, schedule, make_cam(*camera),
-                                      bg, image, final_T, n_contrib, (hipStream_t)stream));
+    FwdBatch b;
+    b.count = 1;
+    b.bg[0] = bg[0];
+    b.bg[1] = bg[1];
+    b.bg[2] = bg[2];
+    b.v[0].cam = make_cam(*camera);
+    b.max_tiles = b.v[0].cam.tiles_x * b.v[0].cam.tiles_y;
+    b.queue = schedule + b.max_tiles;
+    b.v[0].splats = (const Splat *)splats;
+    b.v[0].vals = vals;
+    b.v[0].ranges = tile_ranges;
+    b.v[0].order = schedule;
+    b.v[0].image = image;
+    b.v[0].final_T = final_T;
+    b.v[0].n_contrib = n_contrib;
+    return from_hip(launch_render_fwd(b, (hipStream_t)stream));
+}
+
+gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views, const float *bg, void *stream)
+{
+    if (n_views < 0 || (n_views > 0 && !views) || !bg) return GS_ERR_INVALID_ARG;
+    for (int c = 0; c < 3; c++)
+        if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
+    for (int v = 0; v < n_views; v++) {
+        const gs_fwd_view &w = views[v];
+        if (!camera_ok(&w.camera) || !w.tile_ranges || !w.schedule || !w.image || !w.final_T || !w.n_contrib)
+            return GS_ERR_INVALID_ARG;
+    }
+    for (int v0 = 0; v0 < n_views; v0 += kMaxBlendViews) {
+        FwdBatch b;
+        b.count = n_views - v0 < kMaxBlendViews ? n_views - v0 : kMaxBlendViews;
+        b.bg[0] = bg[0];
+        b.bg[1] = bg[1];
+        b.bg[2] = bg[2];
+        b.max_tiles = 0;
+        for (int i = 0; i < b.count; i++) {
+            const gs_fwd_view &w = views[v0 + i];
+            FwdView &d = b.v[i];
+            d.cam = make_cam(w.camera);
+            d.splats = (const Splat *)w.splats;
+            d.vals = w.vals;
+            d.ranges = w.tile_ranges;
+            d.order = w.schedule;
+            d.image = w.image;
+            d.final_T = w.final_T;
+            d.n_contrib = w.n_contrib;
+            const int nt = d.cam.tiles_x * d.cam.tiles_y;
+            if (nt > b.max_tiles) b.max_tiles = nt;
+        }
+        // the queue counters of the batch's first view
+        b.queue = views[v0].schedule + b.v[0].cam.tiles_x * b.v[0].cam.tiles_y;
+        hipError_t e = launch_render_fwd(b, (hipStream_t)stream);
+        if (e != hipSuccess) return GS_ERR_HIP;
+    }
+    return GS_OK;
 }
 
 static size_t partial_bytes(int64_t k_capacity) { return align_up((size_t)k_capacity * 9 * sizeof(float), 256); }
@@ -154,19 +207,41 @@ static bool grads_ok(const gs_grads *grads, int64_t n)
                                 grads->sh));
 }
 
-// The blend backward and the per-Gaussian sums of one view into g2[9][n].
-static hipError_t screen_backward(int64_t n, const Cam &cam, const gs_splat *splats, const uint32_t *vals,
-                                  const uint32_t *tile_ranges, uint32_t *schedule, const uint32_t *bwd_index,
-                                  int64_t k_capacity, const float *bg, const float *final_T,
-                                  const uint32_t *n_contrib, const float *dL_dimage, float *g2, float *partial,
-                                  hipStream_t s)
+// The blend backward and the per-Gaussian sums of up to kMaxBlendViews views
+// (g2[9][n] each).  Every entry's nine partial sums are written by the blend
+// backward, so the partial buffers need no clearing.
+static hipError_t screen_backward(int count, const gs_bwd_view *views, const float *bg, hipStream_t s)
 {
-    // every entry's nine partial sums are written by the blend backward
-    hipError_t e = launch_render_bwd((const Splat *)splats, vals, tile_ranges, schedule, bwd_index, cam, bg,
-                                     final_T, n_contrib, dL_dimage, partial, s);
-    if (e != hipSuccess) return e;
-    return launch_sum_partials(n, (const Splat *)splats, partial, bwd_index + k_capacity, (uint64_t)k_capacity,
-                               g2, s);
+    BwdBatch b;
+    b.count = count;
+    b.bg[0] = bg[0];
+    b.bg[1] = bg[1];
+    b.bg[2] = bg[2];
+    b.max_tiles = 0;
+    for (int i = 0; i < count; i++) {
+        const gs_bwd_view &w = views[i];
+        BwdView &d = b.v[i];
+        d.cam = make_cam(w.camera);
+        d.splats = (const Splat *)w.splats;
+        d.vals = w.vals;
+        d.ranges = w.tile_ranges;
+        d.order = w.schedule;
+        d.entry_slots = w.bwd_index;
+        d.final_T = w.final_T;
+        d.n_contrib = w.n_contrib;
+        d.dL_dimage = w.dL_dimage;
+        d.partial = (float *)w.workspace;
+        const int nt = d.cam.tiles_x * d.cam.tiles_y;
+        if (nt > b.max_tiles) b.max_tiles = nt;
+    }
+    b.queue = views[0].schedule + b.v[0].cam.tiles_x * b.v[0].cam.tiles_y + 2;
+    hipError_t e = launch_render_bwd(b, s);
+    for (int i = 0; i < count && e == hipSuccess; i++) {
+        const gs_bwd_view &w = views[i];
+        e = launch_sum_partials(w.n, (const Splat *)w.splats, (const float *)w.workspace,
+                                w.bwd_index + w.k_capacity, (uint64_t)w.k_capacity, w.g2, s);
+    }
+    return e;
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,
@@ -185,15 +260,27 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, k_capacity)) return GS_ERR_WORKSPACE;
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
-    const Cam cam = make_cam(*camera);
-    float *partial = (float *)workspace;
     float *g2 = (float *)((char *)workspace + partial_bytes(k_capacity));
-    hipError_t e = screen_backward(n, cam, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg, final_T,
-                                   n_contrib, dL_dimage, g2, partial, s);
+    gs_bwd_view w;
+    w.camera = *camera;
+    w.n = n;
+    w.splats = splats;
+    w.vals = vals;
+    w.tile_ranges = tile_ranges;
+    w.schedule = schedule;
+    w.bwd_index = bwd_index;
+    w.k_capacity = k_capacity;
+    w.final_T = final_T;
+    w.n_contrib = n_contrib;
+    w.dL_dimage = dL_dimage;
+    w.g2 = g2;
+    w.workspace = workspace;
+    w.workspace_bytes = workspace_bytes;
+    hipError_t e = screen_backward(1, &w, bg, s);
     if (e != hipSuccess) return GS_ERR_HIP;
     ViewBatch vb;
     vb.count = 1;
-    vb.cam[0] = cam;
+    vb.cam[0] = make_cam(*camera);
     vb.splats[0] = (const Splat *)splats;
     vb.g2[0] = g2;
     return from_hip(launch_project_bwd(*gaussians, vb, *grads, s));
@@ -211,9 +298,48 @@ gs_status gs_render_bwd_screen(const gs_camera *camera, int64_t n, const gs_spla
     if (n > 0 && !g2) return GS_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < gs_render_bwd_screen_workspace_bytes(k_capacity)) return GS_ERR_WORKSPACE;
     if (n == 0) return GS_OK;
-    return from_hip(screen_backward(n, make_cam(*camera), splats, vals, tile_ranges, schedule, bwd_index,
-                                    k_capacity, bg, final_T, n_contrib, dL_dimage, g2, (float *)workspace,
-                                    (hipStream_t)stream));
+    gs_bwd_view w;
+    w.camera = *camera;
+    w.n = n;
+    w.splats = splats;
+    w.vals = vals;
+    w.tile_ranges = tile_ranges;
+    w.schedule = schedule;
+    w.bwd_index = bwd_index;
+    w.k_capacity = k_capacity;
+    w.final_T = final_T;
+    w.n_contrib = n_contrib;
+    w.dL_dimage = dL_dimage;
+    w.g2 = g2;
+    w.workspace = workspace;
+    w.workspace_bytes = workspace_bytes;
+    return from_hip(screen_backward(1, &w, bg, (hipStream_t)stream));
+}
+
+gs_status gs_render_bwd_screen_views(int32_t n_views, const gs_bwd_view *views, const float *bg, void *stream)
+{
+    if (n_views < 0 || (n_views > 0 && !views) || !bg) return GS_ERR_INVALID_ARG;
+    for (int v = 0; v < n_views; v++) {
+        const gs_bwd_view &w = views[v];
+        gs_status st = screen_args_ok(&w.camera, w.n, w.splats, w.vals, w.tile_ranges, w.schedule, w.bwd_index,
+                                      w.k_capacity, bg, w.final_T, w.n_contrib, w.dL_dimage);
+        if (st != GS_OK) return st;
+        if (w.n > 0 && !w.g2) return GS_ERR_INVALID_ARG;
+        if (!w.workspace || w.workspace_bytes < gs_render_bwd_screen_workspace_bytes(w.k_capacity))
+            return GS_ERR_WORKSPACE;
+    }
+    // views without Gaussians have nothing to do; the rest go in batches
+    gs_bwd_view batch[kMaxBlendViews];
+    int count = 0;
+    for (int v = 0; v <= n_views; v++) {
+        if (v < n_views && views[v].n > 0) batch[count++] = views[v];
+        if (count == kMaxBlendViews || (v == n_views && count > 0)) {
+            hipError_t e = screen_backward(count, batch, bg, (hipStream_t)stream);
+            if (e != hipSuccess) return GS_ERR_HIP;
+            count = 0;
+        }
+    }
+    return GS_OK;
 }
 
 gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,

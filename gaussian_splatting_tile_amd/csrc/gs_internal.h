@@ -132,13 +132,47 @@ size_t active_mask_workspace(int64_t n);
 hipError_t launch_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *ws,
                               size_t ws_bytes, hipStream_t s);
 
-hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const Cam &cam, const float bg[3], float *image,
-                             float *final_T, uint32_t *n_contrib, hipStream_t s);
-hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const uint32_t *entry_slots, const Cam &cam,
-                             const float bg[3], const float *final_T, const uint32_t *n_contrib,
-                             const float *dL_dimage, float *partial, hipStream_t s);
+// Views blended by one launch: their tiles form one work queue.
+constexpr int kMaxBlendViews = 8;
+struct FwdView {
+    Cam cam;
+    const Splat *splats;
+    const uint32_t *vals;
+    const uint32_t *ranges;
+    const uint32_t *order;        // the view's schedule (tiles, longest list first)
+    float *image;
+    float *final_T;
+    uint32_t *n_contrib;
+};
+struct FwdBatch {
+    int count;
+    int max_tiles;                // items = count * max_tiles, view = item % count
+    float bg[3];
+    uint32_t *queue;              // head, done: the first view's forward counters
+    FwdView v[kMaxBlendViews];
+};
+hipError_t launch_render_fwd(const FwdBatch &batch, hipStream_t s);
+// Views whose blend backward one launch runs over one work queue.
+struct BwdView {
+    Cam cam;
+    const Splat *splats;
+    const uint32_t *vals;
+    const uint32_t *ranges;
+    const uint32_t *order;        // the view's schedule
+    const uint32_t *entry_slots;  // duplication slot of each sorted entry
+    const float *final_T;
+    const uint32_t *n_contrib;
+    const float *dL_dimage;
+    float *partial;               // [k_capacity][9]
+};
+struct BwdBatch {
+    int count;
+    int max_tiles;
+    float bg[3];
+    uint32_t *queue;              // head, done: the first view's backward counters
+    BwdView v[kMaxBlendViews];
+};
+hipError_t launch_render_bwd(const BwdBatch &batch, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s);
 
 }  // namespace gsi

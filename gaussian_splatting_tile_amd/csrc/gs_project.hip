@@ -404,7 +404,14 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
     const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
     const int gl = lane / 3, ch = lane - 3 * gl;
     const int g = wave * kColourPerWave + gl;
-    const bool valid = gl < kColourPerWave && g < n;
+    bool valid = gl < kColourPerWave && g < n;
+    // nothing to do for a Gaussian culled in every view of the batch (with
+    // an importance mask most are): test that before touching its SH rows
+    if (valid) {
+        bool any = false;
+        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+        valid = any;
+    }
     float kv[K], acc[K];
     float mx = 0.0f, my = 0.0f, mz = 0.0f;
 #pragma unroll
@@ -472,6 +479,11 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
 {
     const int g = blockIdx.x * kBlock + threadIdx.x;
     if (g >= n) return;
+    {   // culled in every view: nothing to read or write
+        bool any = false;
+        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+        if (!any) return;
+    }
     const float mx0 = means[g], my0 = means[n + g], mz0 = means[2 * n + g];
     const float s0 = scales[g], s1 = scales[n + g], s2 = scales[2 * n + g];
     const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];

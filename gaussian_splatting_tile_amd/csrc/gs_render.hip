@@ -50,12 +50,14 @@ constexpr float kTMin = 1e-4f;
 // followed by a (head, done) counter pair per kernel.  Persistent waves take
 // the next tile index from `head`; the last wave to finish resets both
 // counters, so the next launch on the stream starts from zero again.
-__device__ __forceinline__ int next_tile(const uint32_t *order, uint32_t *head, int n_tiles)
+// (the item index is made wave-uniform, so per-view fields are read with
+// scalar loads)
+__device__ __forceinline__ int next_item(uint32_t *head, int n_items)
 {
     uint32_t i = 0;
     if (threadIdx.x == 0) i = atomicAdd(head, 1u);
-    i = (uint32_t)__shfl((int)i, 0, 64);
-    return i < (uint32_t)n_tiles ? (int)order[i] : -1;
+    i = __builtin_amdgcn_readfirstlane(i);
+    return i < (uint32_t)n_items ? (int)i : -1;
 }
 
 __device__ __forceinline__ void retire_wave(uint32_t *head, uint32_t *done)
@@ -150,6 +152,44 @@ __device__ __forceinline__ void zero_partial(float *__restrict__ partial, uint32
     for (int q = 0; q < 9; q++) p[q] = 0.0f;
 }
 
+// A record fetched into registers ahead of its staging (software
+// pipelining of the blend's global gathers across batches).
+struct Fetched {
+    uint32_t m;          // list position
+    bool valid;
+    float4 a, b, c;
+};
+
+__device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, uint32_t g, bool valid, Fetched &f)
+{
+    if (valid) {
+        f.a = splats[g].a;
+        f.b = splats[g].b;
+        f.c = splats[g].c;
+    }
+}
+
+// Stage the fetched records of one batch into LDS, dropping those that
+// cannot reach any pixel of the tile; returns the number kept, in order.
+__device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, double2 *s_uv,
+                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos)
+{
+    const int lane = threadIdx.x;
+    const bool keep = f.valid && may_contribute(f.a.x, f.a.y, f.b, x0, y0);
+    const uint64_t mask = __ballot(keep);
+    if (keep) {
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int slot = __popcll(mask & lt);
+        Splat s;
+        s.a = f.a;
+        s.b = f.b;
+        s.c = f.c;
+        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
+        s_pos[slot] = f.m - start;
+    }
+    return __popcll(mask);
+}
+
 // Stage one record per lane into LDS, dropping those that cannot reach any
 // pixel of the tile; returns the number kept.  Kept records keep their order.
 template <bool kBwd>
@@ -187,21 +227,36 @@ __device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, con
     return __popcll(mask);
 }
 
-__global__ __launch_bounds__(kLanes) void render_fwd_kernel(
-    const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, Cam cam, float bg0, float bg1,
-    float bg2, float *__restrict__ image, float *__restrict__ final_T, uint32_t *__restrict__ n_contrib)
+// Persistent waves take work items from one queue over the views of the
+// batch: item i is view i mod V, the (i div V)-th tile of that view's
+// longest-first order, so the views' long tiles come first together and one
+// view's tail overlaps the others' work.
+__global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double4 s_q[kBatch];
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
 
-    const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
-    const size_t hw = (size_t)cam.width * cam.height;
-    uint32_t *head = sched + n_tiles, *done = sched + n_tiles + 1;
-    for (int tile = next_tile(sched, head, n_tiles); tile >= 0; tile = next_tile(sched, head, n_tiles)) {
+    const int n_items = batch.count * batch.max_tiles;
+    uint32_t *head = batch.queue, *done = batch.queue + 1;
+    for (int item = next_item(head, n_items); item >= 0; item = next_item(head, n_items)) {
+        const int vi = item % batch.count;
+        const FwdView &V = batch.v[vi];
+        const Cam &cam = V.cam;
+        const int n_tiles = cam.tiles_x * cam.tiles_y;
+        const int rank = item / batch.count;
+        if (rank >= n_tiles) continue;
+        const int tile = (int)V.order[rank];
+        const Splat *__restrict__ splats = V.splats;
+        const uint32_t *__restrict__ vals = V.vals;
+        const uint32_t *__restrict__ ranges = V.ranges;
+        float *__restrict__ image = V.image;
+        float *__restrict__ final_T = V.final_T;
+        uint32_t *__restrict__ n_contrib = V.n_contrib;
+        const float bg0 = batch.bg[0], bg1 = batch.bg[1], bg2 = batch.bg[2];
+        const size_t hw = (size_t)cam.width * cam.height;
         const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
         const int x = tx * kTile + (lane & 15);
         const int y0 = ty * kTile + (lane >> 4);
@@ -221,16 +276,41 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(
         }
 
         const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+        // Two-stage pipeline over the batches: while batch i is blended, the
+        // records of batch i + 1 and the list entries of batch i + 2 are in
+        // flight.
+        Fetched cur;
+        cur.m = start + lane;
+        cur.valid = cur.m < end;
+        fetch_record(splats, cur.valid ? vals[cur.m] : 0u, cur.valid, cur);
+        uint32_t next_m = start + kBatch + lane;
+        bool next_valid = next_m < end;
+        uint32_t next_g = next_valid ? vals[next_m] : 0u;
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
-            const int nb = stage_batch<false>(splats, vals, nullptr, b0, end, start, tx * kTile, ty * kTile, s_uv,
-                                              s_q, s_rgb, s_pos, nullptr, nullptr, nullptr);
+            const int nb = stage_fetched(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos);
+            cur.m = next_m;
+            cur.valid = next_valid;
+            fetch_record(splats, next_g, next_valid, cur);
+            next_m += kBatch;
+            next_valid = next_m < end;
+            next_g = next_valid ? vals[next_m] : 0u;
             __syncthreads();
+            // the next record's LDS reads are issued before this one's math
+            double2 uv_n = s_uv[0];
+            double4 q_n = s_q[0];
+            float4 rgb_n = s_rgb[0];
+            uint32_t pos_n = s_pos[0];
             for (int k = 0; k < nb; k++) {
-                const double2 uv = s_uv[k];
-                const double4 q = s_q[k];
-                const float4 rgb = s_rgb[k];
-                const uint32_t pos = s_pos[k] + 1u;
+                const double2 uv = uv_n;
+                const double4 q = q_n;
+                const float4 rgb = rgb_n;
+                const uint32_t pos = pos_n + 1u;
+                const int kn = k + 1 < nb ? k + 1 : k;
+                uv_n = s_uv[kn];
+                q_n = s_q[kn];
+                rgb_n = s_rgb[kn];
+                pos_n = s_pos[kn];
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
 #pragma unroll
@@ -361,11 +441,9 @@ __device__ __forceinline__ int reduce_slot(int lane)
     }
 }
 
+// Work items as in the forward: one queue over the views of the batch.
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) void render_bwd_kernel(
-    const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-    const uint32_t *__restrict__ ranges, uint32_t *__restrict__ sched, const uint32_t *__restrict__ entry_slots,
-    Cam cam, float bg0, float bg1, float bg2, const float *__restrict__ final_T,
-    const uint32_t *__restrict__ n_contrib, const float *__restrict__ dL_dimage, float *__restrict__ partial)
+    const BwdBatch batch)
 {
     __shared__ double2 s_uv[kBatch];
     __shared__ double4 s_q[kBatch];
@@ -374,12 +452,28 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
     __shared__ uint32_t s_slot[kBatch];
     __shared__ double4 s_P[kBatch];
 
-    const int n_tiles = cam.tiles_x * cam.tiles_y;
     const int lane = threadIdx.x;
-    const size_t hw = (size_t)cam.width * cam.height;
     const int slot = reduce_slot(lane);
-    uint32_t *head = sched + n_tiles + 2, *done = sched + n_tiles + 3;
-    for (int tile = next_tile(sched, head, n_tiles); tile >= 0; tile = next_tile(sched, head, n_tiles)) {
+    const int n_items = batch.count * batch.max_tiles;
+    uint32_t *head = batch.queue, *done = batch.queue + 1;
+    for (int item = next_item(head, n_items); item >= 0; item = next_item(head, n_items)) {
+    const int vi = item % batch.count;
+    const BwdView &V = batch.v[vi];
+    const Cam &cam = V.cam;
+    const int n_tiles = cam.tiles_x * cam.tiles_y;
+    const int rank = item / batch.count;
+    if (rank >= n_tiles) continue;
+    const int tile = (int)V.order[rank];
+    const Splat *__restrict__ splats = V.splats;
+    const uint32_t *__restrict__ vals = V.vals;
+    const uint32_t *__restrict__ ranges = V.ranges;
+    const uint32_t *__restrict__ entry_slots = V.entry_slots;
+    const float *__restrict__ final_T = V.final_T;
+    const uint32_t *__restrict__ n_contrib = V.n_contrib;
+    const float *__restrict__ dL_dimage = V.dL_dimage;
+    float *__restrict__ partial = V.partial;
+    const float bg0 = batch.bg[0], bg1 = batch.bg[1], bg2 = batch.bg[2];
+    const size_t hw = (size_t)cam.width * cam.height;
     const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
     const int x = tx * kTile + (lane & 15);
     const int y0 = ty * kTile + (lane >> 4);
@@ -506,26 +600,17 @@ int resident_blocks(K kernel, int n_tiles)
     return (int)(g < n_tiles ? g : n_tiles);
 }
 
-hipError_t launch_render_fwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const Cam &cam, const float bg[3], float *image,
-                             float *final_T, uint32_t *n_contrib, hipStream_t s)
+hipError_t launch_render_fwd(const FwdBatch &batch, hipStream_t s)
 {
-    const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int grid = resident_blocks(render_fwd_kernel, n_tiles);
-    render_fwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, cam, bg[0], bg[1], bg[2],
-                                              image, final_T, n_contrib);
+    const int grid = resident_blocks(render_fwd_kernel, batch.count * batch.max_tiles);
+    render_fwd_kernel<<<grid, kLanes, 0, s>>>(batch);
     return hipGetLastError();
 }
 
-hipError_t launch_render_bwd(const Splat *splats, const uint32_t *vals, const uint32_t *ranges,
-                             uint32_t *schedule, const uint32_t *entry_slots, const Cam &cam,
-                             const float bg[3], const float *final_T, const uint32_t *n_contrib,
-                             const float *dL_dimage, float *partial, hipStream_t s)
+hipError_t launch_render_bwd(const BwdBatch &batch, hipStream_t s)
 {
-    const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int grid = resident_blocks(render_bwd_kernel, n_tiles);
-    render_bwd_kernel<<<grid, kLanes, 0, s>>>(splats, vals, ranges, schedule, entry_slots, cam, bg[0], bg[1],
-                                              bg[2], final_T, n_contrib, dL_dimage, partial);
+    const int grid = resident_blocks(render_bwd_kernel, batch.count * batch.max_tiles);
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(batch);
     return hipGetLastError();
 }
 

@@ -201,6 +201,28 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
                         float *image, float *final_T, uint32_t *n_contrib,
                         void *stream);
 
+/* One view's arguments of gs_render_fwd, for gs_render_fwd_views. */
+typedef struct gs_fwd_view {
+    gs_camera camera;
+    const gs_splat *splats;
+    const uint32_t *vals;
+    const uint32_t *tile_ranges;
+    uint32_t *schedule;
+    float *image;
+    float *final_T;
+    uint32_t *n_contrib;
+} gs_fwd_view;
+
+/* gs_render_fwd of n_views views (host array) with one background colour,
+ * up to 8 views per launch: the views' tiles form one work queue (each
+ * view's longest tiles first, the views interleaved), so one view's last
+ * long tiles overlap the others' work instead of idling the device.  The
+ * outputs are those of n_views gs_render_fwd calls.  A launch uses the
+ * forward queue counters of its first view's schedule.
+ * Errors: GS_ERR_INVALID_ARG. */
+gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views,
+                              const float *bg /* host [3] */, void *stream);
+
 /* Workspace for gs_render_bwd, in bytes: nine fp32 partial sums per key
  * slot for a key capacity k_capacity, and nine fp32 sums per Gaussian. */
 size_t gs_render_bwd_workspace_bytes(int64_t n, int64_t k_capacity);
@@ -254,6 +276,34 @@ gs_status gs_render_bwd_screen(const gs_camera *camera /* host */, int64_t n,
                                const uint32_t *n_contrib, const float *dL_dimage,
                                float *g2, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/* One view's arguments of gs_render_bwd_screen, for
+ * gs_render_bwd_screen_views. */
+typedef struct gs_bwd_view {
+    gs_camera camera;
+    int64_t n;
+    const gs_splat *splats;
+    const uint32_t *vals;
+    const uint32_t *tile_ranges;
+    uint32_t *schedule;
+    const uint32_t *bwd_index;
+    int64_t k_capacity;
+    const float *final_T;
+    const uint32_t *n_contrib;
+    const float *dL_dimage;
+    float *g2;
+    void *workspace;
+    size_t workspace_bytes;
+} gs_bwd_view;
+
+/* gs_render_bwd_screen of n_views views (host array) with one background
+ * colour, up to 8 views per launch of the blend backward: as in
+ * gs_render_fwd_views the views' tiles form one work queue.  Outputs as
+ * n_views gs_render_bwd_screen calls.  A launch uses the backward queue
+ * counters of its first view's schedule.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_WORKSPACE. */
+gs_status gs_render_bwd_screen_views(int32_t n_views, const gs_bwd_view *views,
+                                     const float *bg /* host [3] */, void *stream);
 
 /* Projection backward of n_views views (the chain rule of the EWA projection
  * and the SH colour, as in gs_render_bwd): grads += sum over the views of the

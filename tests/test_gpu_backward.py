@@ -141,10 +141,11 @@ def test_backward_scene_5m_1080p_tile_sample():
     _compare(gpu, ref, nc, "bwd scene_5m sample")
 
 
-def test_batched_projection_backward_matches_per_view_calls():
-    """gs_render_bwd_screen per view + one gs_project_bwd over the views gives
+def test_batched_backward_matches_per_view_calls():
+    """gs_render_bwd_screen_views over the views + one gs_project_bwd gives
     the per-view gs_render_bwd sum (up to the order of fp32 additions), and
-    the oracle's gradients."""
+    the oracle's gradients; the batched screen pass equals the single-view
+    one bit for bit."""
     sc = scenes.scene_like(seed=9, n=40_000, width=480, height=272, f=350.0, n_views=3)
     say("[gpu] batched projection backward, 3 views")
     Gs = [_upstream(sc.cameras[v], 200 + v) for v in range(3)]
@@ -156,16 +157,24 @@ def test_batched_projection_backward_matches_per_view_calls():
     grads = dict(means=torch.zeros((3, n), device="cuda"), log_scales=torch.zeros((3, n), device="cuda"),
                  quats=torch.zeros((4, n), device="cuda"), opacity_logits=torch.zeros(n, device="cuda"),
                  sh=torch.zeros((16, 3, n), device="cuda"))
-    bufs, g2s = [], []
+    bufs, g2s, wss, dLs = [], [], [], []
     for v in range(3):
         buf, K = run_view(sc, v, with_keys=False)
-        ws = torch.empty(B.render_bwd_screen_workspace_bytes(buf.k_capacity), dtype=torch.uint8, device="cuda")
-        g2 = torch.full((9, n), float("nan"), device="cuda")
-        buf.backward_screen(torch.from_numpy(np.ascontiguousarray(refs[v][1])).cuda(), g2, ws)
+        wss.append(torch.empty(B.render_bwd_screen_workspace_bytes(buf.k_capacity), dtype=torch.uint8,
+                               device="cuda"))
+        g2s.append(torch.full((9, n), float("nan"), device="cuda"))
+        dLs.append(torch.from_numpy(np.ascontiguousarray(refs[v][1])).cuda())
         bufs.append(buf)
-        g2s.append(g2)
+    # one view through gs_render_bwd_screen, the three through the batched call
+    g2_single = torch.full((9, n), float("nan"), device="cuda")
+    bufs[1].backward_screen(dLs[1], g2_single, wss[1])
+    torch.cuda.synchronize()
+    B.render_bwd_screen_views(bufs, dLs, g2s, wss)
     torch.cuda.synchronize()
     assert all(bool(torch.isfinite(g).all()) for g in g2s)     # every Gaussian's row is written
+    assert torch.equal(g2_single, g2s[1])
+    for b in bufs:
+        assert torch.all(b.schedule[b.ranges.shape[0]:] == 0)
     gs = bufs[0]._keep[2]
     B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs], g2s, grads)
     torch.cuda.synchronize()

@@ -182,3 +182,27 @@ def test_invalid_arguments_are_rejected():
                    torch.empty(128, dtype=torch.int32, device="cuda"),
                    torch.empty(B.schedule_words(128, 128), dtype=torch.int32, device="cuda"), None, None,
                    torch.empty(1, dtype=torch.int64, device="cuda"), small)
+
+
+def test_batched_forward_equals_per_view_calls():
+    """gs_render_fwd_views over views of different sizes gives the per-view
+    gs_render_fwd outputs bit for bit and leaves the queue counters reset."""
+    say("[gpu] batched forward, 3 views of different sizes")
+    bufs = []
+    for i, (w, h) in enumerate([(640, 360), (333, 201), (512, 512)]):
+        sc = scenes.scene_like(seed=30 + i, n=30_000, width=w, height=h, f=0.7 * w, n_views=1)
+        buf, K = run_view(sc, 0)
+        bufs.append(buf)
+    ref = [(b.image.clone(), b.final_T.clone(), b.n_contrib.clone()) for b in bufs]
+    for b in bufs:
+        b.image.fill_(-1.0)
+        b.final_T.fill_(-1.0)
+        b.n_contrib.fill_(7)
+    for rep in range(2):
+        B.render_fwd_views(bufs, (0.0, 0.0, 0.0))
+        torch.cuda.synchronize()
+        for b, (img, T, nc) in zip(bufs, ref):
+            assert torch.equal(b.image, img) and torch.equal(b.final_T, T) and torch.equal(b.n_contrib, nc)
+        for b in bufs:
+            n_t = b.ranges.shape[0]
+            assert torch.all(b.schedule[n_t:] == 0)
