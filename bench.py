@@ -6,7 +6,7 @@ Workload (default): 1M Gaussians, SH degree 3, fp32, the scene-like mixture
 (64 anisotropic clusters + a background shell at radius 50), 1920x1080,
 fx = fy = 1400, 8 orbit views; synthetic, seeded, resident in HBM before the
 timed region.  One step = the whole hot path for all 8 views: project and
-bin + sort per view, the 8 forward blends in one batched launch, then the 8
+bin + sort per view (the views spread over 4 streams), the 8 forward blends in one batched launch, then the 8
 screen-space backwards against an upstream dL/dimage ~ N(0, 1e-2) in one
 batched launch, and the projection's chain rule for all 8 views in one
 batched pass.
@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="scene_1m",
                     choices=["scene_1m", "scene_5m", "scene_10m_4k", "box_100k", "tiny_1k"])
     ap.add_argument("--views", type=int, default=8)
+    ap.add_argument("--streams", type=int, default=4,
+                    help="HIP streams for the per-view projection and binning (1 = all on one stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -146,6 +148,10 @@ def main():
     do_bwd = not args.no_backward
 
     names = ("active_mask", "project", "bin_sort", "render_fwd_batch", "render_bwd_batch", "project_bwd_batch")
+    # the views' projection and binning are independent: they run on a few
+    # streams (default priority) and join before the batched blend
+    side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
+    lanes = [stream] + side
     ev = {k: [] for k in names}
     step_ev = []
 
@@ -157,24 +163,33 @@ def main():
         e_end = torch.cuda.Event(enable_timing=True)
         e_fwd0.record(stream)
 
-        def timed(name, fn):
+        def timed(name, fn, st=stream):
             if not record:
                 fn()
                 return
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+            a.record(st)
             fn()
-            b.record(stream)
+            b.record(st)
             ev[name].append((a, b))
 
         if use_mask:
             timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
-        for b in bufs:
-            timed("project", lambda: B.project(gs, b.camc, b.splats, stream))
+        go = torch.cuda.Event()
+        go.record(stream)
+        for st in side:
+            st.wait_event(go)
+        for i, b in enumerate(bufs):
+            st = lanes[i % len(lanes)]
+            timed("project", lambda: B.project(gs, b.camc, b.splats, st), st)
             timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
                                                  b.schedule, b.bwd_index if do_bwd else None, None, b.k_total,
-                                                 b.ws, stream))
+                                                 b.ws, st), st)
+        for st in side:
+            joined = torch.cuda.Event()
+            joined.record(st)
+            stream.wait_event(joined)
         # the 8 views' blends share one work queue
         timed("render_fwd_batch", lambda: B.render_fwd_views(bufs, bg, stream))
         e_fwd1.record(stream)

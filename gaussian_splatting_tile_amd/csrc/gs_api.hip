@@ -236,12 +236,19 @@ static hipError_t screen_backward(int count, const gs_bwd_view *views, const flo
     }
     b.queue = views[0].schedule + b.v[0].cam.tiles_x * b.v[0].cam.tiles_y + 2;
     hipError_t e = launch_render_bwd(b, s);
-    for (int i = 0; i < count && e == hipSuccess; i++) {
+    if (e != hipSuccess) return e;
+    SumBatch sb;
+    sb.count = count;
+    for (int i = 0; i < count; i++) {
         const gs_bwd_view &w = views[i];
-        e = launch_sum_partials(w.n, (const Splat *)w.splats, (const float *)w.workspace,
-                                w.bwd_index + w.k_capacity, (uint64_t)w.k_capacity, w.g2, s);
+        sb.v[i].n = (int)w.n;
+        sb.v[i].splats = (const Splat *)w.splats;
+        sb.v[i].partial = (const float *)w.workspace;
+        sb.v[i].first_slot = w.bwd_index + w.k_capacity;
+        sb.v[i].k_capacity = (uint64_t)w.k_capacity;
+        sb.v[i].g2 = w.g2;
     }
-    return e;
+    return launch_sum_partials(sb, s);
 }
 
 gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, const gs_splat *splats,

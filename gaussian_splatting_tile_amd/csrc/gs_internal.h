@@ -106,10 +106,22 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- launch helpers (host) -------------------------------------------------
 hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s);
-// Per-Gaussian screen-space gradients of one view, g2[9][n], from the
-// blend backward's per-slot partial sums.
-hipError_t launch_sum_partials(int64_t n, const Splat *splats, const float *partial, const uint32_t *first_slot,
-                               uint64_t k_capacity, float *g2, hipStream_t s);
+// Per-Gaussian screen-space gradients, g2[9][n], of up to kMaxSumViews views
+// in one launch, from the blend backward's per-slot partial sums.
+constexpr int kMaxSumViews = 8;
+struct SumView {
+    int n;
+    const Splat *splats;
+    const float *partial;
+    const uint32_t *first_slot;
+    uint64_t k_capacity;
+    float *g2;
+};
+struct SumBatch {
+    int count;
+    SumView v[kMaxSumViews];
+};
+hipError_t launch_sum_partials(const SumBatch &batch, hipStream_t s);
 
 // Views whose screen-space gradients one projection-backward launch takes.
 constexpr int kMaxViews = 16;
@@ -173,6 +185,7 @@ struct BwdBatch {
     BwdView v[kMaxBlendViews];
 };
 hipError_t launch_render_bwd(const BwdBatch &batch, hipStream_t s);
+static_assert(kMaxSumViews >= kMaxBlendViews, "a blend-backward batch is summed in one launch");
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s);
 
 }  // namespace gsi

@@ -345,11 +345,16 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 // Seven Gaussians per wave, one lane per (Gaussian, component); the result
 // is stored component-major, g2[q][n].  Culled Gaussians get zeros.
 constexpr int kSumPerWave = 7;
-__global__ __launch_bounds__(kBlock) void sum_partials_kernel(int n, const Splat *__restrict__ splats,
-                                                             const float *__restrict__ partial,
-                                                             const uint32_t *__restrict__ first_slot,
-                                                             uint64_t k_capacity, float *__restrict__ g2)
+// The views of a batch are blockIdx.y.
+__global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch batch)
 {
+    const SumView &V = batch.v[blockIdx.y];
+    const int n = V.n;
+    const Splat *__restrict__ splats = V.splats;
+    const float *__restrict__ partial = V.partial;
+    const uint32_t *__restrict__ first_slot = V.first_slot;
+    const uint64_t k_capacity = V.k_capacity;
+    float *__restrict__ g2 = V.g2;
     const int lane = threadIdx.x & 63;
     const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
     const int gl = lane / 9, q = lane - 9 * gl;
@@ -698,14 +703,14 @@ hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, 
     return hipGetLastError();
 }
 
-hipError_t launch_sum_partials(int64_t n64, const Splat *splats, const float *partial, const uint32_t *first_slot,
-                               uint64_t k_capacity, float *g2, hipStream_t s)
+hipError_t launch_sum_partials(const SumBatch &batch, hipStream_t s)
 {
-    if (n64 == 0) return hipSuccess;
-    const int n = (int)n64;
-    const long long waves = (n + kSumPerWave - 1) / kSumPerWave;
+    int n_max = 0;
+    for (int i = 0; i < batch.count; i++) n_max = batch.v[i].n > n_max ? batch.v[i].n : n_max;
+    if (batch.count == 0 || n_max == 0) return hipSuccess;
+    const long long waves = (n_max + kSumPerWave - 1) / kSumPerWave;
     const unsigned blocks = (unsigned)((waves * 64 + kBlock - 1) / kBlock);
-    sum_partials_kernel<<<blocks, kBlock, 0, s>>>(n, splats, partial, first_slot, k_capacity, g2);
+    sum_partials_kernel<<<dim3(blocks, batch.count), kBlock, 0, s>>>(batch);
     return hipGetLastError();
 }
 

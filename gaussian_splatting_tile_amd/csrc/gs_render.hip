@@ -374,11 +374,13 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
 // slot, the slots of a Gaussian are contiguous, and the projection backward
 // sums them.  No atomics, so the gradients are bit-reproducible.
 
+// (every control used here reads a valid lane; old = 0 with bound_ctrl lets
+// the compiler fold the move into the add that consumes it)
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float v)
 {
     const int iv = __float_as_int(v);
-    return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, kCtrl, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, kCtrl, 0xF, 0xF, true));
 }
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
