@@ -5,8 +5,9 @@
 Workload (default): 1M Gaussians, SH degree 3, fp32, the scene-like mixture
 (64 anisotropic clusters + a background shell at radius 50), 1920x1080,
 fx = fy = 1400, 8 orbit views; synthetic, seeded, resident in HBM before the
-timed region.  One step = the whole hot path for all 8 views: project and
-bin + sort per view (the views spread over 4 streams), the 8 forward blends in one batched launch, then the 8
+timed region.  One step = the whole hot path for all 8 views: the 8 views'
+records in one batched projection, bin + sort per view (the views spread
+over 4 streams), the 8 forward blends in one batched launch, then the 8
 screen-space backwards against an upstream dL/dimage ~ N(0, 1e-2) in one
 batched launch, and the projection's chain rule for all 8 views in one
 batched pass.
@@ -147,7 +148,8 @@ def main():
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
 
-    names = ("active_mask", "project", "bin_sort", "render_fwd_batch", "render_bwd_batch", "project_bwd_batch")
+    names = ("active_mask", "project_batch", "bin_sort", "render_fwd_batch", "render_bwd_batch",
+             "project_bwd_batch")
     # the views' projection and binning are independent: they run on a few
     # streams (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
@@ -176,13 +178,15 @@ def main():
 
         if use_mask:
             timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
+        # the views' records in one pass over the Gaussians
+        timed("project_batch", lambda: B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
+                                                       stream))
         go = torch.cuda.Event()
         go.record(stream)
         for st in side:
             st.wait_event(go)
         for i, b in enumerate(bufs):
             st = lanes[i % len(lanes)]
-            timed("project", lambda: B.project(gs, b.camc, b.splats, st), st)
             timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
                                                  b.schedule, b.bwd_index if do_bwd else None, None, b.k_total,
                                                  b.ws, st), st)
@@ -253,7 +257,7 @@ def main():
                    "importance_keep": (keep if use_mask else None),
                    "lod_min_radius_px": cam0.lod_min_radius_px,
                    "step": ("importance mask, then " if use_mask else "") +
-                           "per view project + bin/sort, batched blend fwd of all views" +
+                           "batched project, per view bin/sort, batched blend fwd of all views" +
                            (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,

@@ -57,7 +57,7 @@ class GsError(RuntimeError):
 
 _lib = None
 SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
-           "gs_render_fwd_views", "gs_render_bwd_screen_views",
+           "gs_render_fwd_views", "gs_render_bwd_screen_views", "gs_project_views",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
@@ -90,6 +90,7 @@ def lib():
     L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
     L.gs_render_fwd_views.argtypes = [C.c_int32, C.POINTER(GsFwdView), vp, vp]
+    L.gs_project_views.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp), vp]
     L.gs_render_bwd_screen_views.argtypes = [C.c_int32, C.POINTER(GsBwdView), vp, vp]
     L.gs_render_bwd_workspace_bytes.argtypes = [i64, i64]
     L.gs_render_bwd_workspace_bytes.restype = sz
@@ -107,7 +108,8 @@ def lib():
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
-    for name in ("gs_project", "gs_bin_sort", "gs_render_fwd", "gs_render_fwd_views", "gs_render_bwd",
+    for name in ("gs_project", "gs_project_views", "gs_bin_sort", "gs_render_fwd", "gs_render_fwd_views",
+                 "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
                  "gs_project_bwd", "gs_active_mask"):
         getattr(L, name).restype = C.c_int
@@ -197,6 +199,14 @@ def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[
     _check(lib().gs_render_fwd(_ptr(splats), _ptr(vals), _ptr(tile_ranges), _ptr(schedule), C.byref(cam),
                                C.cast(bgv, C.c_void_p), _ptr(image), _ptr(final_T), _ptr(n_contrib),
                                _stream(stream)), "gs_render_fwd")
+
+
+def project_views(gs: GsGaussians, cams, splats_list, stream=None):
+    """gs_project_views: records for every camera of the list in one pass."""
+    nv = len(cams)
+    cam_arr = (GsCamera * max(nv, 1))(*cams)
+    sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
+    _check(lib().gs_project_views(C.byref(gs), nv, cam_arr, sp_arr, _stream(stream)), "gs_project_views")
 
 
 def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None):

@@ -62,7 +62,34 @@ gs_status gs_project(const gs_gaussians *gaussians, const gs_camera *camera, gs_
     if (st != GS_OK) return st;
     if (!camera_ok(camera)) return GS_ERR_INVALID_ARG;
     if (gaussians->n > 0 && !splats) return GS_ERR_INVALID_ARG;
-    return from_hip(launch_project(*gaussians, make_cam(*camera), (Splat *)splats, (hipStream_t)stream));
+    ProjBatch b;
+    b.count = 1;
+    b.cam[0] = make_cam(*camera);
+    b.out[0] = (Splat *)splats;
+    return from_hip(launch_project(*gaussians, b, (hipStream_t)stream));
+}
+
+gs_status gs_project_views(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                           gs_splat *const *splats, void *stream)
+{
+    gs_status st = gaussians_ok(gaussians);
+    if (st != GS_OK) return st;
+    if (n_views < 0 || (n_views > 0 && (!cameras || !splats))) return GS_ERR_INVALID_ARG;
+    for (int v = 0; v < n_views; v++) {
+        if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
+        if (gaussians->n > 0 && !splats[v]) return GS_ERR_INVALID_ARG;
+    }
+    for (int v0 = 0; v0 < n_views; v0 += kMaxProjViews) {
+        ProjBatch b;
+        b.count = n_views - v0 < kMaxProjViews ? n_views - v0 : kMaxProjViews;
+        for (int i = 0; i < b.count; i++) {
+            b.cam[i] = make_cam(cameras[v0 + i]);
+            b.out[i] = (Splat *)splats[v0 + i];
+        }
+        hipError_t e = launch_project(*gaussians, b, (hipStream_t)stream);
+        if (e != hipSuccess) return GS_ERR_HIP;
+    }
+    return GS_OK;
 }
 
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles)

@@ -105,7 +105,14 @@ static_assert(sizeof(Splat) == sizeof(gs_splat), "splat layout");
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- launch helpers (host) -------------------------------------------------
-hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s);
+// Views one projection launch writes records for (parameters read once).
+constexpr int kMaxProjViews = 16;
+struct ProjBatch {
+    int count;
+    Cam cam[kMaxProjViews];
+    Splat *out[kMaxProjViews];
+};
+hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStream_t s);
 // Per-Gaussian screen-space gradients, g2[9][n], of up to kMaxSumViews views
 // in one launch, from the blend backward's per-slot partial sums.
 constexpr int kMaxSumViews = 8;

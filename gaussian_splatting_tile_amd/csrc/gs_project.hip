@@ -261,7 +261,7 @@ template <int DEG, typename TSH>
 __global__ __launch_bounds__(kBlock) void project_kernel(
     int n, const float *__restrict__ means, const float *__restrict__ scales,
     const float *__restrict__ quats, const float *__restrict__ opac, const TSH *__restrict__ sh,
-    const uint8_t *__restrict__ active, Cam cam, Splat *__restrict__ out)
+    const uint8_t *__restrict__ active, const ProjBatch views)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int g = blockIdx.x * kBlock + threadIdx.x;
@@ -270,10 +270,19 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     const float sx = scales[g], sy = scales[n + g], sz = scales[2 * n + g];
     const float qw = quats[g], qx = quats[n + g], qy = quats[2 * n + g], qz = quats[3 * n + g];
     const float o = opac[g];
+    const bool on = (active == nullptr || active[g] != 0) && all_finite(mx, my, mz, sx, sy, sz, qw, qx, qy, qz, o);
 
+    // the views of the batch, parameters read once; the SH rows are re-read
+    // per view (cache hits) through an opaque copy of their pointer, so the
+    // compiler does not hold all 3 K coefficients in registers
+    for (int v = 0; v < views.count; v++) {
+    const Cam &cam = views.cam[v];
+    Splat *__restrict__ out = views.out[v];
+    const TSH *shv = sh;
+    asm volatile("" : "+s"(shv));
     Splat rec;
     rec.a = rec.b = rec.c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    bool vis = (active == nullptr || active[g] != 0) && all_finite(mx, my, mz, sx, sy, sz, qw, qx, qy, qz, o);
+    bool vis = on;
     Geo G;
     if (vis) vis = geometry(cam, mx, my, mz, sx, sy, sz, qw, qx, qy, qz, G);
     if (vis && cam.lod > 0.0f) {
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
             for (int ch = 0; ch < 3; ch++) {
                 float s = 0.0f;
 #pragma unroll
-                for (int j = 0; j < K; j++) s = s + ld_sh(sh + ((size_t)(j * 3 + ch)) * n + g) * Y[j];
+                for (int j = 0; j < K; j++) s = s + ld_sh(shv + ((size_t)(j * 3 + ch)) * n + g) * Y[j];
                 const float val = 0.5f + s;
                 col[ch] = val < 0.0f ? 0.0f : val;
             }
@@ -321,6 +330,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
         }
     }
     out[g] = rec;
+    }   // views
 }
 
 // ---------------------------------------------------------------------------
@@ -649,11 +659,11 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
 
 
 template <int DEG, typename TSH>
-void launch_project_t(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s)
+void launch_project_t(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
 {
     const int n = (int)g.n;
     project_kernel<DEG, TSH><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.active, cam, splats);
+        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.active, views);
 }
 
 template <int DEG, typename TSH>
@@ -669,13 +679,13 @@ void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const g
 }
 
 template <typename TSH>
-void dispatch_project(int deg, const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s)
+void dispatch_project(int deg, const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
 {
     switch (deg) {
-    case 0: launch_project_t<0, TSH>(g, cam, splats, s); break;
-    case 1: launch_project_t<1, TSH>(g, cam, splats, s); break;
-    case 2: launch_project_t<2, TSH>(g, cam, splats, s); break;
-    default: launch_project_t<3, TSH>(g, cam, splats, s); break;
+    case 0: launch_project_t<0, TSH>(g, views, s); break;
+    case 1: launch_project_t<1, TSH>(g, views, s); break;
+    case 2: launch_project_t<2, TSH>(g, views, s); break;
+    default: launch_project_t<3, TSH>(g, views, s); break;
     }
 }
 
@@ -693,13 +703,13 @@ void dispatch_project_bwd(int deg, const gs_gaussians &g, const ViewBatch &views
 
 }  // namespace
 
-hipError_t launch_project(const gs_gaussians &g, const Cam &cam, Splat *splats, hipStream_t s)
+hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
 {
-    if (g.n == 0) return hipSuccess;
+    if (g.n == 0 || views.count == 0) return hipSuccess;
     if (g.sh_dtype == GS_SH_F16)
-        dispatch_project<__half>(g.sh_degree, g, cam, splats, s);
+        dispatch_project<__half>(g.sh_degree, g, views, s);
     else
-        dispatch_project<float>(g.sh_degree, g, cam, splats, s);
+        dispatch_project<float>(g.sh_degree, g, views, s);
     return hipGetLastError();
 }
 

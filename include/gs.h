@@ -139,6 +139,15 @@ gs_status gs_project(const gs_gaussians *gaussians /* host struct */,
                      const gs_camera *camera /* host */, gs_splat *splats,
                      void *stream);
 
+/* gs_project for n_views cameras (host array) in one pass over the
+ * Gaussians: each Gaussian's parameters are read once for the batch (up to
+ * 16 views per launch) and one record array is written per view (splats:
+ * host array of n_views device pointers).  Same records as n_views
+ * gs_project calls.
+ * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED. */
+gs_status gs_project_views(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
+                           const gs_camera *cameras, gs_splat *const *splats, void *stream);
+
 /* Workspace for gs_bin_sort, in bytes, for n Gaussians, a key capacity
  * k_capacity and the camera's tile count. */
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles);

@@ -206,3 +206,20 @@ def test_batched_forward_equals_per_view_calls():
         for b in bufs:
             n_t = b.ranges.shape[0]
             assert torch.all(b.schedule[n_t:] == 0)
+
+
+def test_batched_projection_equals_per_view_calls():
+    """gs_project_views writes, for every camera, the records gs_project writes."""
+    sc = scenes.scene_like(seed=41, n=50_000, width=640, height=360, f=450.0, n_views=5)
+    say("[gpu] batched projection, 5 views")
+    g = device_gaussians(sc)
+    gs = B.gaussians_struct(g, sc.sh_degree)
+    cams = [B.camera_struct(c) for c in sc.cameras]
+    outs = [torch.full((sc.n, 12), -1.0, device="cuda") for _ in cams]
+    B.project_views(gs, cams, outs)
+    torch.cuda.synchronize()
+    for cam, out in zip(cams, outs):
+        ref = torch.empty((sc.n, 12), device="cuda")
+        B.project(gs, cam, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
