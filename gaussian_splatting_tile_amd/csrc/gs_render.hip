@@ -190,6 +190,36 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
     return __popcll(mask);
 }
 
+// The backward's staging of fetched records: as stage_fetched, plus the
+// entry's duplication slot and the principal frame of its conic; a dropped
+// entry gets its nine partial sums zeroed.
+__device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
+                                                 int y0, double2 *s_uv, double4 *s_q, float4 *s_rgb,
+                                                 uint32_t *s_pos, uint32_t *s_slot, double4 *s_P,
+                                                 float *__restrict__ partial)
+{
+    const int lane = threadIdx.x;
+    const bool keep = f.valid && may_contribute(f.a.x, f.a.y, f.b, x0, y0);
+    if (f.valid && !keep) zero_partial(partial, entry_slot);
+    const uint64_t mask = __ballot(keep);
+    if (keep) {
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int slot = __popcll(mask & lt);
+        Splat s;
+        s.a = f.a;
+        s.b = f.b;
+        s.c = f.c;
+        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
+        s_pos[slot] = f.m - start;
+        s_slot[slot] = entry_slot;
+        // w' = P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex))
+        double ex, ey, l1, l2;
+        conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
+        s_P[slot] = make_double4(l1 * ex, l1 * ey, -(l2 * ey), l2 * ex);
+    }
+    return __popcll(mask);
+}
+
 // Stage one record per lane into LDS, dropping those that cannot reach any
 // pixel of the tile; returns the number kept.  Kept records keep their order.
 template <bool kBwd>
@@ -507,10 +537,38 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
 
     const uint32_t start = ranges[2 * tile];
     const uint32_t stop = start + lmax;           // entries at or past this are unused
+    // Batches back to front, pipelined as in the forward: while batch i is
+    // processed, the records of batch i + 1 and the list entries (and slots)
+    // of batch i + 2 are in flight.  Batch j covers [bend_j - 64, bend_j),
+    // clipped at start.
+    Fetched cur;
+    uint32_t cur_slot = 0;
+    {
+        const int64_t m = (int64_t)stop - kBatch + lane;
+        cur.valid = m >= (int64_t)start && m < (int64_t)stop;
+        cur.m = cur.valid ? (uint32_t)m : 0u;
+        uint32_t g = 0;
+        if (cur.valid) {
+            g = vals[cur.m];
+            cur_slot = entry_slots[cur.m];
+        }
+        fetch_record(splats, g, cur.valid, cur);
+    }
+    int64_t next_m = (int64_t)stop - 2 * kBatch + lane;
+    bool next_valid = next_m >= (int64_t)start && next_m < (int64_t)stop;
+    uint32_t next_g = next_valid ? vals[(uint32_t)next_m] : 0u;
+    uint32_t next_slot = next_valid ? entry_slots[(uint32_t)next_m] : 0u;
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
-        const uint32_t bbeg = (uint32_t)max((int64_t)start, bend - kBatch);
-        const int nb = stage_batch<true>(splats, vals, entry_slots, bbeg, (uint32_t)bend, start, tx * kTile,
-                                         ty * kTile, s_uv, s_q, s_rgb, s_pos, s_slot, s_P, partial);
+        const int nb = stage_fetched_bwd(cur, cur_slot, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos,
+                                         s_slot, s_P, partial);
+        cur.m = next_valid ? (uint32_t)next_m : 0u;
+        cur.valid = next_valid;
+        cur_slot = next_slot;
+        fetch_record(splats, next_g, next_valid, cur);
+        next_m -= kBatch;
+        next_valid = next_m >= (int64_t)start && next_m < (int64_t)stop;
+        next_g = next_valid ? vals[(uint32_t)next_m] : 0u;
+        next_slot = next_valid ? entry_slots[(uint32_t)next_m] : 0u;
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
             const uint32_t pos = s_pos[k];                     // list position
