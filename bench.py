@@ -138,7 +138,7 @@ def main():
         b = B.ViewBuffers(sc.n, cam, k)
         b.dL = f(sc.upstream(v))
         b.bwd_ws = torch.empty(B.render_bwd_screen_workspace_bytes(k), dtype=torch.uint8, device=dev)
-        b.g2 = torch.empty((9, sc.n), dtype=torch.float32, device=dev)
+        b.g2 = torch.empty((sc.n, 9), dtype=torch.float32, device=dev)
         bufs.append(b)
         Ks.append(k)
     K_sh = (sc.sh_degree + 1) ** 2

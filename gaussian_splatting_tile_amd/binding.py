@@ -252,7 +252,7 @@ def render_bwd_screen(cam: GsCamera, n, splats, vals, tile_ranges, schedule, bwd
 
 def render_bwd_screen_views(bufs, dLs, g2s, workspaces, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None):
     """gs_render_bwd_screen_views over ViewBuffers objects with their upstream
-    gradients, g2 outputs and workspaces."""
+    gradients, g2 outputs [n][9] and workspaces."""
     nv = len(bufs)
     arr = (GsBwdView * max(nv, 1))()
     for i, (b, dL, g2, ws) in enumerate(zip(bufs, dLs, g2s, workspaces)):
@@ -325,7 +325,7 @@ class ViewBuffers:
         return torch.empty(render_bwd_workspace_bytes(self.n, self.k_capacity), dtype=torch.uint8, device=device)
 
     def backward_screen(self, dL_dimage, g2, workspace, bg=(0.0, 0.0, 0.0), stream=None):
-        """Screen-space backward of this view into g2 [9][n] (for project_bwd)."""
+        """Screen-space backward of this view into g2 [n][9] (for project_bwd)."""
         render_bwd_screen(self.camc, self.n, self.splats, self.vals, self.ranges, self.schedule, self.bwd_index,
                           self.k_capacity, bg, self.final_T, self.n_contrib, dL_dimage, g2, workspace, stream)
 

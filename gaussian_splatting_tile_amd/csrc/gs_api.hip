@@ -112,7 +112,7 @@ size_t gs_schedule_words(int32_t width, int32_t height)
 size_t gs_bwd_index_words(int64_t n, int64_t k_capacity)
 {
     if (n < 0 || k_capacity < 0) return 0;
-    return (size_t)k_capacity + (size_t)n;
+    return (size_t)k_capacity + 2 * (size_t)n + 2;
 }
 
 gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
@@ -235,7 +235,7 @@ static bool grads_ok(const gs_grads *grads, int64_t n)
 }
 
 // The blend backward and the per-Gaussian sums of up to kMaxBlendViews views
-// (g2[9][n] each).  Every entry's nine partial sums are written by the blend
+// (g2[n][9] each).  Every entry's nine partial sums are written by the blend
 // backward, so the partial buffers need no clearing.
 static hipError_t screen_backward(int count, const gs_bwd_view *views, const float *bg, hipStream_t s)
 {
@@ -269,9 +269,10 @@ static hipError_t screen_backward(int count, const gs_bwd_view *views, const flo
     for (int i = 0; i < count; i++) {
         const gs_bwd_view &w = views[i];
         sb.v[i].n = (int)w.n;
-        sb.v[i].splats = (const Splat *)w.splats;
         sb.v[i].partial = (const float *)w.workspace;
-        sb.v[i].first_slot = w.bwd_index + w.k_capacity;
+        sb.v[i].order = w.bwd_index + w.k_capacity;
+        sb.v[i].off = w.bwd_index + w.k_capacity + w.n;
+        sb.v[i].count = w.bwd_index + w.k_capacity + 2 * w.n + 1;
         sb.v[i].k_capacity = (uint64_t)w.k_capacity;
         sb.v[i].g2 = w.g2;
     }

@@ -113,16 +113,17 @@ struct ProjBatch {
     Splat *out[kMaxProjViews];
 };
 hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStream_t s);
-// Per-Gaussian screen-space gradients, g2[9][n], of up to kMaxSumViews views
+// Per-Gaussian screen-space gradients, g2[n][9], of up to kMaxSumViews views
 // in one launch, from the blend backward's per-slot partial sums.
 constexpr int kMaxSumViews = 8;
 struct SumView {
     int n;
-    const Splat *splats;
-    const float *partial;
-    const uint32_t *first_slot;
+    const float *partial;         // [k_capacity][9]
+    const uint32_t *order;        // the visible Gaussians in depth order
+    const uint32_t *off;          // their first duplication slots (+ K at the end)
+    const uint32_t *count;        // the number of visible Gaussians
     uint64_t k_capacity;
-    float *g2;
+    float *g2;                    // [n][9]
 };
 struct SumBatch {
     int count;

@@ -355,43 +355,71 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 // Seven Gaussians per wave, one lane per (Gaussian, component); the result
 // is stored component-major, g2[q][n].  Culled Gaussians get zeros.
 constexpr int kSumPerWave = 7;
-// The views of a batch are blockIdx.y.
+constexpr uint32_t kSumSmall = 16;     // slots a lane sums on its own
+// The screen-space gradients of each Gaussian visible in a view: the sum of
+// its per-tile partial rows, which sit at its tiles_touched contiguous
+// duplication slots.  Gaussians are taken in depth order, seven per wave,
+// so a wave reads one contiguous stretch of rows (the slots of consecutive
+// depth ranks are consecutive) and needs no record.  A Gaussian with at most
+// kSumSmall slots is summed by nine lanes, one component each, in slot
+// order; the few larger ones (near the camera they span thousands of tiles)
+// by the whole wave in turn: lane (j, q) takes slots j, j + 7, ... of
+// component q, then the seven partial sums are added in j order.  Both
+// orders are fixed, so the result is reproducible.  Slots at or past the
+// capacity were never written and are left out.  Output: g2[g][9].
 __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch batch)
 {
     const SumView &V = batch.v[blockIdx.y];
-    const int n = V.n;
-    const Splat *__restrict__ splats = V.splats;
     const float *__restrict__ partial = V.partial;
-    const uint32_t *__restrict__ first_slot = V.first_slot;
     const uint64_t k_capacity = V.k_capacity;
     float *__restrict__ g2 = V.g2;
     const int lane = threadIdx.x & 63;
     const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
     const int gl = lane / 9, q = lane - 9 * gl;
-    if (gl >= kSumPerWave) return;
-    const int g = wave * kSumPerWave + gl;
-    if (g >= n) return;
-    // fp64: a large Gaussian sums thousands of per-tile partials
+    const uint32_t n_vis = *V.count;
+    const uint32_t j = (uint32_t)wave * kSumPerWave + gl;
+    const bool valid = gl < kSumPerWave && j < n_vis;
+    uint32_t g = 0, first = 0, count = 0;
+    if (valid) {
+        g = V.order[j];
+        const uint64_t s0 = V.off[j], s1 = V.off[j + 1];
+        const uint64_t a = s0 < k_capacity ? s0 : k_capacity, b = s1 < k_capacity ? s1 : k_capacity;
+        first = (uint32_t)a;
+        count = (uint32_t)(b - a);
+    }
+    // fp64: the sums run over up to thousands of partials
     double acc = 0.0;
-    // (first_slot is not written for culled Gaussians; it is read, not used)
-    const int radius = __float_as_int(splats[g].a.w);
-    const uint32_t tiles = __float_as_uint(splats[g].c.w);
-    const uint32_t first = first_slot[g];
-    if (radius != 0) {
-        const uint64_t end64 = (uint64_t)first + tiles;
-        const uint32_t last = (uint32_t)(end64 < k_capacity ? end64 : k_capacity);
+    const bool big = count > kSumSmall;
+    if (valid && !big && count > 0) {
+        const uint32_t last = first + count;
         // eight loads in flight per step, none predicated (indices past the
-        // Gaussian's last slot re-read that slot and add nothing); the sum
-        // stays in slot order
+        // Gaussian's last slot re-read that slot and add nothing)
         for (uint32_t sl = first; sl < last; sl += 8) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) v[j] = partial[(size_t)min(sl + j, last - 1) * 9 + q];
+            for (int t = 0; t < 8; t++) v[t] = partial[(size_t)min(sl + t, last - 1) * 9 + q];
 #pragma unroll
-            for (int j = 0; j < 8; j++) acc += sl + j < last ? (double)v[j] : 0.0;
+            for (int t = 0; t < 8; t++) acc += sl + t < last ? (double)v[t] : 0.0;
         }
     }
-    g2[(size_t)q * n + g] = (float)acc;
+    // the wave's large Gaussians, one after another
+    uint64_t bigs = __ballot(valid && big && q == 0);
+    const int cj = lane / 9, cq = lane - 9 * (lane / 9);       // cooperative layout (63 lanes)
+    while (bigs) {
+        const int src = __builtin_ctzll(bigs);                 // lane (gl_b, 0) of that Gaussian
+        bigs &= bigs - 1;
+        const uint32_t bfirst = (uint32_t)__shfl((int)first, src, 64);
+        const uint32_t bcount = (uint32_t)__shfl((int)count, src, 64);
+        double part = 0.0;
+        if (cj < kSumPerWave)
+            for (uint32_t t = cj; t < bcount; t += kSumPerWave)
+                part += (double)partial[((size_t)bfirst + t) * 9 + cq];
+        // lane (gl_b, q) collects component q: sum over j = 0..6 in order
+        double tot = 0.0;
+        for (int t = 0; t < kSumPerWave; t++) tot += __shfl(part, t * 9 + q, 64);
+        if (gl == src / 9) acc = tot;
+    }
+    if (valid) g2[(size_t)g * 9 + q] = (float)acc;
 }
 
 // The projection backward runs as two kernels over a batch of views, one
@@ -410,7 +438,9 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch bat
 constexpr int kColourPerWave = 21;
 template <int DEG, typename TSH>
 __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const float *__restrict__ means,
-                                                                   const TSH *__restrict__ sh, const ViewBatch views,
+                                                                   const TSH *__restrict__ sh,
+                                                                   const uint8_t *__restrict__ active,
+                                                                   const ViewBatch views,
                                                                    float *__restrict__ d_means,
                                                                    float *__restrict__ d_sh)
 {
@@ -419,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
     const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
     const int gl = lane / 3, ch = lane - 3 * gl;
     const int g = wave * kColourPerWave + gl;
-    bool valid = gl < kColourPerWave && g < n;
+    bool valid = gl < kColourPerWave && g < n && (active == nullptr || active[g] != 0);
     // nothing to do for a Gaussian culled in every view of the batch (with
     // an importance mask most are): test that before touching its SH rows
     if (valid) {
@@ -455,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
         for (int j = 0; j < K; j++) sum = sum + kv[j] * Y[j];
         // the forward's clamp at 0 keeps its branch
         if (0.5f + sum < 0.0f) continue;
-        const float gr = views.g2[v][(size_t)(6 + ch) * n + g];
+        const float gr = views.g2[v][(size_t)g * 9 + 6 + ch];
 #pragma unroll
         for (int j = 0; j < K; j++) acc[j] = acc[j] + Y[j] * gr;
         float dd[3];
@@ -489,11 +519,12 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
 
 __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
     int n, const float *__restrict__ means, const float *__restrict__ scales, const float *__restrict__ quats,
-    const float *__restrict__ opac, const ViewBatch views, float *__restrict__ d_means,
-    float *__restrict__ d_log_scales, float *__restrict__ d_quats, float *__restrict__ d_logits)
+    const float *__restrict__ opac, const uint8_t *__restrict__ active, const ViewBatch views,
+    float *__restrict__ d_means, float *__restrict__ d_log_scales, float *__restrict__ d_quats,
+    float *__restrict__ d_logits)
 {
     const int g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= n) return;
+    if (g >= n || (active != nullptr && active[g] == 0)) return;
     {   // culled in every view: nothing to read or write
         bool any = false;
         for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
@@ -521,7 +552,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
     const float *__restrict__ g2s = views.g2[v];
     float g2[6];
 #pragma unroll
-    for (int q = 0; q < 6; q++) g2[q] = g2s[(size_t)q * n + g];
+    for (int q = 0; q < 6; q++) g2[q] = g2s[(size_t)g * 9 + q];
 
     // The compositing pass worked in the principal frame V of the record's
     // conic Qr: mean gradient V (g0, g1), covariance gradient V W V^T.
@@ -672,9 +703,9 @@ void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const g
     const int n = (int)g.n;
     const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
     project_bwd_color_kernel<DEG, TSH><<<(unsigned)((colour_waves * 64 + kBlock - 1) / kBlock), kBlock, 0, s>>>(
-        n, g.means, (const TSH *)g.sh, views, out.means, out.sh);
+        n, g.means, (const TSH *)g.sh, g.active, views, out.means, out.sh);
     project_bwd_geom_kernel<<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, views, out.means, out.log_scales, out.quats,
+        n, g.means, g.scales, g.quats, g.opacities, g.active, views, out.means, out.log_scales, out.quats,
         out.opacity_logits);
 }
 

@@ -291,7 +291,8 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Splat *__restrict__ 
 __global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block_sums,
                                                     const uint32_t *__restrict__ m_ptr, uint64_t cap,
                                                     uint64_t *__restrict__ k_total,
-                                                    uint32_t *__restrict__ k_eff)
+                                                    uint32_t *__restrict__ k_eff,
+                                                    uint32_t *__restrict__ bwd_off, uint32_t *__restrict__ bwd_count)
 {
     __shared__ uint64_t wsum[16];
     const uint32_t m = *m_ptr;
@@ -321,6 +322,10 @@ __global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block
     if (threadIdx.x == 0) {
         *k_total = total;
         *k_eff = (uint32_t)(total < cap ? total : cap);
+        if (bwd_off) {
+            bwd_off[m] = (uint32_t)(total < 0xFFFFFFFFull ? total : 0xFFFFFFFFull);
+            *bwd_count = m;
+        }
     }
 }
 
@@ -333,7 +338,8 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
     const uint32_t *__restrict__ order, const uint32_t *__restrict__ m_ptr,
     const uint2 *__restrict__ rect_info, const uint32_t *__restrict__ counts,
     const uint64_t *__restrict__ block_offsets, int tiles_x, uint64_t cap,
-    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ gslot, uint32_t *__restrict__ first_slot)
+    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ gslot, uint32_t *__restrict__ bwd_order,
+    uint32_t *__restrict__ bwd_off)
 {
     __shared__ uint32_t s_off[kScanItems];
     __shared__ uint32_t s_g[kScanItems];
@@ -358,9 +364,11 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
     s_off[threadIdx.x] = block_exclusive_scan(c, &total);
     __syncthreads();
     const uint64_t blk = block_offsets[blockIdx.x];
-    if (first_slot && threadIdx.x < n_items) {
+    if (bwd_order && threadIdx.x < n_items) {
+        // backward index: the depth-ordered Gaussians and their first slots
         const uint64_t f = blk + s_off[threadIdx.x];
-        first_slot[s_g[threadIdx.x]] = (uint32_t)(f < 0xFFFFFFFFull ? f : 0xFFFFFFFFull);
+        bwd_order[j] = s_g[threadIdx.x];
+        bwd_off[j] = (uint32_t)(f < 0xFFFFFFFFull ? f : 0xFFFFFFFFull);
     }
     for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
         const uint64_t slot = blk + e;
@@ -599,16 +607,20 @@ hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int
         const uint32_t nblk = (n + kScanItems - 1) / kScanItems;
         scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], cam, w.rect_info, w.counts,
                                             w.block_sums);
-        scan_blocks<<<1, 1024, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total, &w.counters[2]);
+        // backward index: [entry slot: cap][depth-ordered Gaussian: n][first slot: n + 1][visible count]
+        uint32_t *bwd_order = bwd_index ? bwd_index + cap : nullptr;
+        uint32_t *bwd_off = bwd_index ? bwd_index + cap + n : nullptr;
+        uint32_t *bwd_count = bwd_index ? bwd_index + cap + 2 * (size_t)n + 1 : nullptr;
+        scan_blocks<<<1, 1024, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total, &w.counters[2],
+                                       bwd_off, bwd_count);
         // 3. tile passes over the tile ids, carrying each entry's Gaussian
         // and, for the backward index, its duplication slot (the identity on
         // the way in); the last pass writes straight into the outputs
         const int tbits = bits_for(n_tiles);
         const int passes = tbits == 0 ? 0 : (tbits + 7) / 8;
         uint32_t *entry_slots = bwd_index;                     // [cap], optional
-        uint32_t *first_slot = bwd_index ? bwd_index + cap : nullptr;   // [n]
         duplicate_keys<<<nblk, kBlock, 0, s>>>(order, &w.counters[1], w.rect_info, w.counts, w.block_sums,
-                                               cam.tiles_x, (uint64_t)cap, w.tk[0], w.gslot, first_slot);
+                                               cam.tiles_x, (uint64_t)cap, w.tk[0], w.gslot, bwd_order, bwd_off);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         int shift = 0;
         for (int p = 0; p < passes; p++) {

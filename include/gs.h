@@ -174,8 +174,10 @@ size_t gs_bwd_index_words(int64_t n, int64_t k_capacity);
  *   bwd_index[gs_bwd_index_words(n, k_capacity)]  (optional, NULL to
  *                           skip; needed by gs_render_bwd) the duplication
  *                           slot of every sorted entry (k_capacity words),
- *                           then the first slot of every Gaussian (n words);
- *                           a Gaussian's tiles_touched slots are contiguous
+ *                           the visible Gaussians in depth order (n words),
+ *                           their first slots and K (n + 1 words), the number
+ *                           of visible Gaussians (1 word); a Gaussian's
+ *                           tiles_touched slots are contiguous
  *   keys[k_capacity]        (optional, NULL to skip) the 64-bit sort keys
  *                           tile << 32 | bits of the fp32 depth
  *   k_total                 device uint64: K, the number of entries
@@ -269,8 +271,9 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians /* host struct */,
 size_t gs_render_bwd_screen_workspace_bytes(int64_t k_capacity);
 
 /* Screen-space backward of one view (the reverse compositing pass of
- * gs_render_bwd and its per-Gaussian sum): writes g2[9][n] (device fp32,
- * component-major, every Gaussian, zeros for those culled in the view).  The
+ * gs_render_bwd and its per-Gaussian sum): writes g2[n][9] (device fp32,
+ * one row of nine per Gaussian) for every Gaussian visible in the view;
+ * rows of Gaussians culled in the view (radius 0) are left unwritten.  The
  * nine components are an internal representation that only gs_project_bwd
  * reads with the same view's records: the mean gradient and the 2D
  * covariance gradient in the principal frame of the record's conic, the
@@ -319,7 +322,7 @@ gs_status gs_render_bwd_screen_views(int32_t n_views, const gs_bwd_view *views,
  * raw-parameter gradients, the views taken in order.
  *   cameras  host gs_camera[n_views]
  *   splats   host array of n_views device pointers: each view's records
- *   g2       host array of n_views device pointers: each view's g2[9][n]
+ *   g2       host array of n_views device pointers: each view's g2[n][9]
  *            from gs_render_bwd_screen
  * Up to 16 views go into one launch; longer batches take several.
  * Errors: GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED. */

@@ -68,6 +68,6 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_render_bwd_screen_workspace_bytes(1000) >= 1000 * 36
     assert L.gs_bin_sort_workspace_bytes(1000, 5000, 64) > 5000 * 12
     assert L.gs_render_bwd_workspace_bytes(1000, 4000) >= 5000 * 36
-    assert L.gs_bwd_index_words(10, 100) == 110
+    assert L.gs_bwd_index_words(10, 100) == 100 + 2 * 10 + 2
     assert L.gs_schedule_words(128, 128) == 64 + 4
     assert L.gs_schedule_words(0, 128) == 0

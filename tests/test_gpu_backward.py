@@ -162,17 +162,21 @@ def test_batched_backward_matches_per_view_calls():
         buf, K = run_view(sc, v, with_keys=False)
         wss.append(torch.empty(B.render_bwd_screen_workspace_bytes(buf.k_capacity), dtype=torch.uint8,
                                device="cuda"))
-        g2s.append(torch.full((9, n), float("nan"), device="cuda"))
+        g2s.append(torch.full((n, 9), float("nan"), device="cuda"))
         dLs.append(torch.from_numpy(np.ascontiguousarray(refs[v][1])).cuda())
         bufs.append(buf)
     # one view through gs_render_bwd_screen, the three through the batched call
-    g2_single = torch.full((9, n), float("nan"), device="cuda")
+    g2_single = torch.full((n, 9), float("nan"), device="cuda")
     bufs[1].backward_screen(dLs[1], g2_single, wss[1])
     torch.cuda.synchronize()
     B.render_bwd_screen_views(bufs, dLs, g2s, wss)
     torch.cuda.synchronize()
-    assert all(bool(torch.isfinite(g).all()) for g in g2s)     # every Gaussian's row is written
-    assert torch.equal(g2_single, g2s[1])
+    for b, g in zip(bufs, g2s):
+        visible = b.splats[:, 3].view(torch.int32) != 0
+        assert bool(torch.isfinite(g[visible]).all())             # visible Gaussians' rows written
+        assert bool(torch.isnan(g[~visible]).all())               # culled ones' rows untouched
+    vis1 = bufs[1].splats[:, 3].view(torch.int32) != 0
+    assert torch.equal(g2_single[vis1], g2s[1][vis1])
     for b in bufs:
         assert torch.all(b.schedule[b.ranges.shape[0]:] == 0)
     gs = bufs[0]._keep[2]
