@@ -436,32 +436,57 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch bat
 //   dk_j += Y_j(d) dL/drgb,   d(direction) += dL/drgb grad_d sum_j k_j Y_j(d);
 // the three channels' shares of the mean gradient are added across lanes.
 constexpr int kColourPerWave = 21;
+// Gaussians of a wave's range that the projection backward must visit: in
+// the importance mask (if any) and visible in at least one view of the batch.
+// With a mask most are not, and a wave of mostly idle lanes costs as much as
+// a full one, so each wave first compacts its range (64 per ballot) into a
+// per-wave list in LDS and then works through the list densely.
+constexpr int kMaxCompact = 1024;             // Gaussians per wave range, at most
+__device__ __forceinline__ int compact_range(long long g_begin, long long g_end, const uint8_t *__restrict__ active,
+                                             const ViewBatch &views, uint32_t *list)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int cnt = 0;
+    for (long long base = g_begin; base < g_end; base += 64) {
+        const long long g = base + lane;
+        bool keep = g < g_end && (active == nullptr || active[g] != 0);
+        if (keep) {
+            bool any = false;
+            for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+            keep = any;
+        }
+        const uint64_t m = __ballot(keep);
+        if (keep) list[cnt + __popcll(m & lt)] = (uint32_t)g;
+        cnt += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return cnt;
+}
+
+// One round of the colour part: lane (gl, ch) takes Gaussian g (valid lanes
+// only; every lane of the wave calls this, for the cross-lane sums).
 template <int DEG, typename TSH>
-__global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const float *__restrict__ means,
-                                                                   const TSH *__restrict__ sh,
-                                                                   const uint8_t *__restrict__ active,
-                                                                   const ViewBatch views,
-                                                                   float *__restrict__ d_means,
-                                                                   float *__restrict__ d_sh)
+__device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int ch, const float *__restrict__ means,
+                                                const TSH *__restrict__ sh, const ViewBatch &views,
+                                                float *__restrict__ d_means, float *__restrict__ d_sh)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int lane = threadIdx.x & 63;
-    const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
-    const int gl = lane / 3, ch = lane - 3 * gl;
-    const int g = wave * kColourPerWave + gl;
-    bool valid = gl < kColourPerWave && g < n && (active == nullptr || active[g] != 0);
-    // nothing to do for a Gaussian culled in every view of the batch (with
-    // an importance mask most are): test that before touching its SH rows
-    if (valid) {
-        bool any = false;
-        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
-        valid = any;
-    }
+    // opaque copies of the row pointers and the row stride: the 2 K row
+    // offsets are invariant across the caller's rounds and would otherwise
+    // be held in registers
+    const TSH *shr = sh;
+    float *dshr = d_sh;
+    int n = n_;
+    asm volatile("" : "+s"(shr), "+s"(dshr), "+s"(n));
     float kv[K], acc[K];
     float mx = 0.0f, my = 0.0f, mz = 0.0f;
 #pragma unroll
     for (int j = 0; j < K; j++) {
-        kv[j] = valid ? ld_sh(sh + (size_t)(j * 3 + ch) * n + g) : 0.0f;
+        kv[j] = valid ? ld_sh(shr + (size_t)(j * 3 + ch) * n + g) : 0.0f;
         acc[j] = 0.0f;
     }
     if (valid) {
@@ -508,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
     if (!visible) return;
 #pragma unroll
     for (int j = 0; j < K; j++) {
-        float *p = d_sh + (size_t)(j * 3 + ch) * n + g;
+        float *p = dshr + (size_t)(j * 3 + ch) * n + g;
         *p = *p + acc[j];
     }
     if (ch == 0) {
@@ -517,19 +542,51 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, const 
     }
 }
 
-__global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
-    int n, const float *__restrict__ means, const float *__restrict__ scales, const float *__restrict__ quats,
-    const float *__restrict__ opac, const uint8_t *__restrict__ active, const ViewBatch views,
-    float *__restrict__ d_means, float *__restrict__ d_log_scales, float *__restrict__ d_quats,
-    float *__restrict__ d_logits)
+// Without a mask (COMPACT false) wave w takes Gaussians 21 w .. 21 w + 20 and
+// Gaussians culled in every view drop out lane by lane; with one, each wave
+// compacts its range of per_wave Gaussians first and takes rounds of 21.
+template <int DEG, typename TSH, bool COMPACT>
+__global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int per_wave,
+                                                                   const float *__restrict__ means,
+                                                                   const TSH *__restrict__ sh,
+                                                                   const uint8_t *__restrict__ active,
+                                                                   const ViewBatch views,
+                                                                   float *__restrict__ d_means,
+                                                                   float *__restrict__ d_sh)
 {
-    const int g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= n || (active != nullptr && active[g] == 0)) return;
-    {   // culled in every view: nothing to read or write
-        bool any = false;
-        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
-        if (!any) return;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int gl = lane / 3, ch = lane - 3 * gl;
+    if constexpr (COMPACT) {
+        __shared__ uint32_t s_list[kBlock / 64][kMaxCompact];
+        const long long g_begin = ((long long)blockIdx.x * (kBlock / 64) + wv) * per_wave;
+        const long long g_end = g_begin + per_wave < n ? g_begin + per_wave : n;
+        const int cnt = compact_range(g_begin, g_end, active, views, s_list[wv]);
+        for (int r0 = 0; r0 < cnt; r0 += kColourPerWave) {
+            const int idx = r0 + gl;
+            const bool valid = gl < kColourPerWave && idx < cnt;
+            const int g = valid ? (int)s_list[wv][idx] : 0;
+            colour_backward<DEG, TSH>(n, g, valid, ch, means, sh, views, d_means, d_sh);
+        }
+    } else {
+        const long long wave = (long long)blockIdx.x * (kBlock / 64) + wv;
+        const long long gg = wave * kColourPerWave + gl;
+        bool valid = gl < kColourPerWave && gg < n && (active == nullptr || active[gg] != 0);
+        // culled in every view of the batch: leave the SH rows untouched
+        if (valid) {
+            bool any = false;
+            for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][gg].a.w) != 0);
+            valid = any;
+        }
+        colour_backward<DEG, TSH>(n, valid ? (int)gg : 0, valid, ch, means, sh, views, d_means, d_sh);
     }
+}
+
+// The geometry part for one Gaussian (visible in at least one view).
+__device__ __forceinline__ void geom_backward(
+    int n, int g, const float *__restrict__ means, const float *__restrict__ scales, const float *__restrict__ quats,
+    const float *__restrict__ opac, const ViewBatch &views, float *__restrict__ d_means,
+    float *__restrict__ d_log_scales, float *__restrict__ d_quats, float *__restrict__ d_logits)
+{
     const float mx0 = means[g], my0 = means[n + g], mz0 = means[2 * n + g];
     const float s0 = scales[g], s1 = scales[n + g], s2 = scales[2 * n + g];
     const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];
@@ -688,6 +745,35 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
     d_logits[g] += acc_logit;
 }
 
+template <bool COMPACT>
+__global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
+    int n, int per_wave, const float *__restrict__ means, const float *__restrict__ scales,
+    const float *__restrict__ quats, const float *__restrict__ opac, const uint8_t *__restrict__ active,
+    const ViewBatch views, float *__restrict__ d_means, float *__restrict__ d_log_scales,
+    float *__restrict__ d_quats, float *__restrict__ d_logits)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if constexpr (COMPACT) {
+        __shared__ uint32_t s_list[kBlock / 64][kMaxCompact];
+        const long long g_begin = ((long long)blockIdx.x * (kBlock / 64) + wv) * per_wave;
+        const long long g_end = g_begin + per_wave < n ? g_begin + per_wave : n;
+        const int cnt = compact_range(g_begin, g_end, active, views, s_list[wv]);
+        for (int r0 = 0; r0 < cnt; r0 += 64) {
+            const int idx = r0 + lane;
+            if (idx < cnt)
+                geom_backward(n, (int)s_list[wv][idx], means, scales, quats, opac, views, d_means, d_log_scales,
+                              d_quats, d_logits);
+        }
+    } else {
+        const long long g = (long long)blockIdx.x * kBlock + threadIdx.x;
+        if (g >= n || (active != nullptr && active[g] == 0)) return;
+        bool any = false;   // culled in every view: nothing to read or write
+        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+        if (!any) return;
+        geom_backward(n, (int)g, means, scales, quats, opac, views, d_means, d_log_scales, d_quats, d_logits);
+    }
+}
+
 
 template <int DEG, typename TSH>
 void launch_project_t(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
@@ -701,12 +787,29 @@ template <int DEG, typename TSH>
 void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
 {
     const int n = (int)g.n;
-    const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
-    project_bwd_color_kernel<DEG, TSH><<<(unsigned)((colour_waves * 64 + kBlock - 1) / kBlock), kBlock, 0, s>>>(
-        n, g.means, (const TSH *)g.sh, g.active, views, out.means, out.sh);
-    project_bwd_geom_kernel<<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, g.active, views, out.means, out.log_scales, out.quats,
-        out.opacity_logits);
+    if (g.active == nullptr) {
+        const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
+        project_bwd_color_kernel<DEG, TSH, false>
+            <<<(unsigned)((colour_waves + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, s>>>(
+                n, 0, g.means, (const TSH *)g.sh, nullptr, views, out.means, out.sh);
+        project_bwd_geom_kernel<false><<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(
+            n, 0, g.means, g.scales, g.quats, g.opacities, nullptr, views, out.means, out.log_scales, out.quats,
+            out.opacity_logits);
+        return;
+    }
+    // With a mask: ranges large enough that a compacted wave is mostly full,
+    // while keeping ~16K waves
+    long long m = (long long)n / (64LL * 16384);
+    if (m < 1) m = 1;
+    if (m > kMaxCompact / 64) m = kMaxCompact / 64;
+    const int per_wave = (int)(64 * m);
+    const long long waves = (n + per_wave - 1) / per_wave;
+    const unsigned blocks = (unsigned)((waves + kBlock / 64 - 1) / (kBlock / 64));
+    project_bwd_color_kernel<DEG, TSH, true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, (const TSH *)g.sh,
+                                                                       g.active, views, out.means, out.sh);
+    project_bwd_geom_kernel<true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, g.scales, g.quats, g.opacities,
+                                                            g.active, views, out.means, out.log_scales, out.quats,
+                                                            out.opacity_logits);
 }
 
 template <typename TSH>
