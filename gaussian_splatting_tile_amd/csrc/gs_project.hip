@@ -496,9 +496,23 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
     }
     float dm[3] = {0.0f, 0.0f, 0.0f};
     bool visible = false;
+    // the next view's radius and gradient are loaded one view ahead (a
+    // culled Gaussian's gradient row holds no value and is not used)
+    int rad_next = 0;
+    float gr_next = 0.0f;
+    if (valid && views.count > 0) {
+        rad_next = __float_as_int(views.splats[0][g].a.w);
+        gr_next = views.g2[0][(size_t)g * 9 + 6 + ch];
+    }
     for (int v = 0; v < views.count; v++) {
+        const int rad = rad_next;
+        const float gr = gr_next;
+        if (valid && v + 1 < views.count) {
+            rad_next = __float_as_int(views.splats[v + 1][g].a.w);
+            gr_next = views.g2[v + 1][(size_t)g * 9 + 6 + ch];
+        }
         // culled Gaussians have radius 0 and receive nothing
-        if (!valid || __float_as_int(views.splats[v][g].a.w) == 0) continue;
+        if (!valid || rad == 0) continue;
         visible = true;
         const Cam &cam = views.cam[v];
         float dx, dy, dz, dn;
@@ -510,7 +524,6 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
         for (int j = 0; j < K; j++) sum = sum + kv[j] * Y[j];
         // the forward's clamp at 0 keeps its branch
         if (0.5f + sum < 0.0f) continue;
-        const float gr = views.g2[v][(size_t)g * 9 + 6 + ch];
 #pragma unroll
         for (int j = 0; j < K; j++) acc[j] = acc[j] + Y[j] * gr;
         float dd[3];
@@ -594,9 +607,30 @@ __device__ __forceinline__ void geom_backward(
     float acc_mean[3] = {0.0f, 0.0f, 0.0f}, acc_ls[3] = {0.0f, 0.0f, 0.0f};
     float acc_q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc_logit = 0.0f;
     bool touched = false;
+    // the next view's radius, conic and gradients are loaded one view ahead
+    // (a culled Gaussian's gradient row holds no value and is not used)
+    int rad_next = 0;
+    float4 cr_next = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float g2_next[6] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (views.count > 0) {
+        rad_next = __float_as_int(views.splats[0][g].a.w);
+        cr_next = views.splats[0][g].b;
+#pragma unroll
+        for (int q = 0; q < 6; q++) g2_next[q] = views.g2[0][(size_t)g * 9 + q];
+    }
     for (int v = 0; v < views.count; v++) {
-    const Splat *__restrict__ splats = views.splats[v];
-    if (__float_as_int(splats[g].a.w) == 0) continue;
+    const int rad = rad_next;
+    const float4 cr = cr_next;
+    float g2[6];
+#pragma unroll
+    for (int q = 0; q < 6; q++) g2[q] = g2_next[q];
+    if (v + 1 < views.count) {
+        rad_next = __float_as_int(views.splats[v + 1][g].a.w);
+        cr_next = views.splats[v + 1][g].b;
+#pragma unroll
+        for (int q = 0; q < 6; q++) g2_next[q] = views.g2[v + 1][(size_t)g * 9 + q];
+    }
+    if (rad == 0) continue;
     touched = true;
     // The view-independent part (rotation, 3D covariance) is recomputed per
     // view from opaque copies of the parameters: held across views in fp64
@@ -606,16 +640,11 @@ __device__ __forceinline__ void geom_backward(
     asm volatile("" : "+v"(mx), "+v"(my), "+v"(mz), "+v"(qw), "+v"(qx), "+v"(qy), "+v"(qz));
     asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]));
     const Cam &cam = views.cam[v];
-    const float *__restrict__ g2s = views.g2[v];
-    float g2[6];
-#pragma unroll
-    for (int q = 0; q < 6; q++) g2[q] = g2s[(size_t)g * 9 + q];
 
     // The compositing pass worked in the principal frame V of the record's
     // conic Qr: mean gradient V (g0, g1), covariance gradient V W V^T.
     double ex, ey;
     {
-        const float4 cr = splats[g].b;
         double l1, l2;
         conic_frame(cr.x, cr.y, cr.z, ex, ey, l1, l2);
     }
@@ -640,7 +669,6 @@ __device__ __forceinline__ void geom_backward(
     double D00, D01, D11;
     {
         const double q00 = G.p11 / G.det, q01 = -(G.p01 / G.det), q11 = G.p00 / G.det;
-        const float4 cr = splats[g].b;
         const double ra = cr.x, rb = cr.y, rc = cr.z;
         const double rdet = ra * rc - rb * rb;
         const double i00 = rc / rdet, i01 = -rb / rdet, i11 = ra / rdet;   // Qr^-1
