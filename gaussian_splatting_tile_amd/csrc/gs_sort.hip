@@ -99,10 +99,20 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t *__restri
     for (int i = threadIdx.x; i < kWaves * 256; i += kBlock) (&hist[0][0])[i] = 0;
     __syncthreads();
     uint32_t *h = hist[wave_id()];
-    for (uint32_t i = begin + threadIdx.x; i < end; i += kBlock) {
-        const uint32_t k = keys[i];
-        if (drop_sentinel && k == kSentinel) continue;
-        atomicAdd(&h[(k >> shift) & mask], 1u);
+    // kIpt independent loads in flight per thread (indexes past the end are
+    // clamped to the last item and not counted)
+    for (uint32_t base = begin; base < end; base += kTileItems) {
+        uint32_t k[kIpt];
+#pragma unroll
+        for (int r = 0; r < kIpt; r++) {
+            const uint32_t i = base + r * kBlock + threadIdx.x;
+            k[r] = keys[i < end ? i : end - 1];
+        }
+#pragma unroll
+        for (int r = 0; r < kIpt; r++) {
+            const uint32_t i = base + r * kBlock + threadIdx.x;
+            if (i < end && !(drop_sentinel && k[r] == kSentinel)) atomicAdd(&h[(k[r] >> shift) & mask], 1u);
+        }
     }
     __syncthreads();
     const int d = threadIdx.x;   // 256 threads = 256 digits
@@ -165,20 +175,39 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     __syncthreads();
 
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    // The items of tile tb + kTileItems are loaded while tile tb is ranked
+    // and written (indexes past the end are clamped to the last item; those
+    // lanes are not ranked).
+    uint32_t k[kIpt], v[kIpt], v2[kIpt];
+    auto load_tile = [&](uint32_t tb, uint32_t *kk, uint32_t *vv, uint32_t *vv2) {
+#pragma unroll
+        for (int r = 0; r < kIpt; r++) {
+            const uint32_t idx = tb + w * kWaveItems + r * kWave + lane;
+            const uint32_t ci = idx < end ? idx : end - 1;
+            kk[r] = keys_in[ci];
+            vv[r] = vals_in ? vals_in[ci] : idx;
+            if (kTwo) vv2[r] = vals2_in[ci];
+        }
+    };
+    if (begin < end) load_tile(begin, k, v, v2);
     for (uint32_t tb = begin; tb < end; tb += kTileItems) {
+        uint32_t nk[kIpt], nv[kIpt], nv2[kIpt];
+        const bool more = tb + kTileItems < end;
+        if (more) load_tile(tb + kTileItems, nk, nv, nv2);
         for (int i = lane; i < 256; i += kWave) wave_cnt[w][i] = 0;
         // the wave's own row is written by its own lanes only; no barrier needed
-        uint32_t k[kIpt], v[kIpt], v2[kIpt], loc[kIpt];
+        uint32_t loc[kIpt];
         bool ok[kIpt];
 #pragma unroll
         for (int r = 0; r < kIpt; r++) {
             const uint32_t idx = tb + w * kWaveItems + r * kWave + lane;
             bool valid = idx < end;
-            uint32_t kk = valid ? keys_in[idx] : 0u;
-            if (drop_sentinel && kk == kSentinel) valid = false;
-            const uint32_t d = (kk >> shift) & mask;
+            if (drop_sentinel && k[r] == kSentinel) valid = false;
+            const uint32_t d = (k[r] >> shift) & mask;
             uint64_t peers = __ballot(valid);
-            for (int bit = 0; bit < bits; bit++) {
+            // digit bits above the pass width are zero in every lane
+#pragma unroll
+            for (int bit = 0; bit < 8; bit++) {
                 const uint64_t bb = __ballot((d >> bit) & 1u);
                 peers &= ((d >> bit) & 1u) ? bb : ~bb;
             }
@@ -188,9 +217,6 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             __builtin_amdgcn_wave_barrier();
             if (valid && rank == 0) wave_cnt[w][d] = before + (uint32_t)__popcll(peers);
             __builtin_amdgcn_wave_barrier();
-            k[r] = kk;
-            v[r] = valid ? (vals_in ? vals_in[idx] : idx) : 0u;
-            if (kTwo) v2[r] = valid ? vals2_in[idx] : 0u;
             loc[r] = before + rank;
             ok[r] = valid;
         }
@@ -232,6 +258,14 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
         __syncthreads();
         digit_base[tid] += tile_cnt[tid];
         __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int r = 0; r < kIpt; r++) {
+                k[r] = nk[r];
+                v[r] = nv[r];
+                if (kTwo) v2[r] = nv2[r];
+            }
+        }
     }
 }
 
