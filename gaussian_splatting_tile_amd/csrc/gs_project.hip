@@ -349,24 +349,31 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 //   colour:                 dk_j = Y_j drgb (unclamped channels),
 //                           dmu += (I - d d^T) / |mu - c| sum_j k_j grad Y_j drgb
 //   raw outputs:            dlog s = s ds,  dlogit = o (1 - o) do.
-// The screen-space gradients of each Gaussian: the sum, in slot order, of
-// its per-tile partial sums, which sit at its tiles_touched contiguous
-// duplication slots (slots at or past the capacity were never written).
-// Seven Gaussians per wave, one lane per (Gaussian, component); the result
-// is stored component-major, g2[q][n].  Culled Gaussians get zeros.
-constexpr int kSumPerWave = 7;
-constexpr uint32_t kSumSmall = 16;     // slots a lane sums on its own
 // The screen-space gradients of each Gaussian visible in a view: the sum of
 // its per-tile partial rows, which sit at its tiles_touched contiguous
-// duplication slots.  Gaussians are taken in depth order, seven per wave,
-// so a wave reads one contiguous stretch of rows (the slots of consecutive
-// depth ranks are consecutive) and needs no record.  A Gaussian with at most
-// kSumSmall slots is summed by nine lanes, one component each, in slot
-// order; the few larger ones (near the camera they span thousands of tiles)
-// by the whole wave in turn: lane (j, q) takes slots j, j + 7, ... of
-// component q, then the seven partial sums are added in j order.  Both
-// orders are fixed, so the result is reproducible.  Slots at or past the
-// capacity were never written and are left out.  Output: g2[g][9].
+// duplication slots.  Gaussians are taken in depth order, 63 per wave (the
+// slots of consecutive depth ranks are consecutive, so a wave reads one
+// contiguous stretch of rows and needs no record), in nine rounds of seven.
+// A Gaussian with at most kSumSmall slots is summed by nine lanes, one
+// component each, in slot order; the few larger ones (near the camera they
+// span thousands of tiles) by the whole wave in turn: lane (j, q) takes slots
+// j, j + 7, ... of component q, then the seven partial sums are added in j
+// order.  Both orders are fixed, so the result is reproducible.  The rows of
+// round r + 1 (their first eight slots) are loaded while round r is summed.
+// Slots at or past the capacity were never written and are left out.
+// Output: g2[g][9], visible Gaussians only.
+constexpr int kSumPerRound = 7;
+constexpr int kSumRounds = 9;
+constexpr int kSumPerWave = kSumPerRound * kSumRounds;   // 63
+constexpr uint32_t kSumSmall = 16;     // slots a lane sums on its own
+constexpr int kSumAhead = 8;           // slots per lane loaded one round ahead
+
+struct SumRound {
+    uint32_t g, first, count;
+    bool valid;
+    float v[kSumAhead];
+};
+
 __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch batch)
 {
     const SumView &V = batch.v[blockIdx.y];
@@ -374,52 +381,75 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch bat
     const uint64_t k_capacity = V.k_capacity;
     float *__restrict__ g2 = V.g2;
     const int lane = threadIdx.x & 63;
-    const int wave = (int)((blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6);
-    const int gl = lane / 9, q = lane - 9 * gl;
+    const uint32_t wave = (blockIdx.x * (unsigned)kBlock + threadIdx.x) >> 6;
     const uint32_t n_vis = *V.count;
-    const uint32_t j = (uint32_t)wave * kSumPerWave + gl;
-    const bool valid = gl < kSumPerWave && j < n_vis;
-    uint32_t g = 0, first = 0, count = 0;
-    if (valid) {
-        g = V.order[j];
+    const uint32_t j0 = wave * kSumPerWave;
+    if (j0 >= n_vis) return;
+    // lane L < 63 holds depth rank j0 + L: its Gaussian, first slot, slot count
+    uint32_t my_g = 0, my_first = 0, my_count = 0;
+    if (lane < kSumPerWave && j0 + lane < n_vis) {
+        const uint32_t j = j0 + lane;
+        my_g = V.order[j];
         const uint64_t s0 = V.off[j], s1 = V.off[j + 1];
         const uint64_t a = s0 < k_capacity ? s0 : k_capacity, b = s1 < k_capacity ? s1 : k_capacity;
-        first = (uint32_t)a;
-        count = (uint32_t)(b - a);
+        my_first = (uint32_t)a;
+        my_count = (uint32_t)(b - a);
     }
-    // fp64: the sums run over up to thousands of partials
-    double acc = 0.0;
-    const bool big = count > kSumSmall;
-    if (valid && !big && count > 0) {
-        const uint32_t last = first + count;
-        // eight loads in flight per step, none predicated (indices past the
-        // Gaussian's last slot re-read that slot and add nothing)
-        for (uint32_t sl = first; sl < last; sl += 8) {
-            float v[8];
+    const int gl = lane / 9, q = lane - 9 * gl;
+    // round r: lane (gl, q) takes rank j0 + 7 r + gl; its first eight slots
+    // are loaded unpredicated (indices past the last slot re-read it)
+    auto fetch = [&](int r, SumRound &R) {
+        const int src = r * kSumPerRound + (gl < kSumPerRound ? gl : 0);
+        R.g = (uint32_t)__shfl((int)my_g, src, 64);
+        R.first = (uint32_t)__shfl((int)my_first, src, 64);
+        R.count = (uint32_t)__shfl((int)my_count, src, 64);
+        R.valid = gl < kSumPerRound && j0 + (uint32_t)src < n_vis;
+        if (R.valid && R.count > 0 && R.count <= kSumSmall) {
+            const uint32_t last = R.first + R.count - 1;
 #pragma unroll
-            for (int t = 0; t < 8; t++) v[t] = partial[(size_t)min(sl + t, last - 1) * 9 + q];
-#pragma unroll
-            for (int t = 0; t < 8; t++) acc += sl + t < last ? (double)v[t] : 0.0;
+            for (int t = 0; t < kSumAhead; t++) R.v[t] = partial[(size_t)min(R.first + t, last) * 9 + q];
         }
-    }
-    // the wave's large Gaussians, one after another
-    uint64_t bigs = __ballot(valid && big && q == 0);
+    };
     const int cj = lane / 9, cq = lane - 9 * (lane / 9);       // cooperative layout (63 lanes)
-    while (bigs) {
-        const int src = __builtin_ctzll(bigs);                 // lane (gl_b, 0) of that Gaussian
-        bigs &= bigs - 1;
-        const uint32_t bfirst = (uint32_t)__shfl((int)first, src, 64);
-        const uint32_t bcount = (uint32_t)__shfl((int)count, src, 64);
-        double part = 0.0;
-        if (cj < kSumPerWave)
-            for (uint32_t t = cj; t < bcount; t += kSumPerWave)
-                part += (double)partial[((size_t)bfirst + t) * 9 + cq];
-        // lane (gl_b, q) collects component q: sum over j = 0..6 in order
-        double tot = 0.0;
-        for (int t = 0; t < kSumPerWave; t++) tot += __shfl(part, t * 9 + q, 64);
-        if (gl == src / 9) acc = tot;
+    SumRound cur, nxt;
+    fetch(0, cur);
+    for (int r = 0; r < kSumRounds; r++) {
+        if (j0 + (uint32_t)(r * kSumPerRound) >= n_vis) break;   // wave-uniform
+        if (r + 1 < kSumRounds) fetch(r + 1, nxt);
+        // fp64: the sums run over up to thousands of partials
+        double acc = 0.0;
+        const bool big = cur.count > kSumSmall;
+        if (cur.valid && !big && cur.count > 0) {
+#pragma unroll
+            for (int t = 0; t < kSumAhead; t++) acc += (uint32_t)t < cur.count ? (double)cur.v[t] : 0.0;
+            const uint32_t last = cur.first + cur.count;
+            for (uint32_t sl = cur.first + kSumAhead; sl < last; sl += 8) {
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 8; t++) v[t] = partial[(size_t)min(sl + t, last - 1) * 9 + q];
+#pragma unroll
+                for (int t = 0; t < 8; t++) acc += sl + t < last ? (double)v[t] : 0.0;
+            }
+        }
+        // the round's large Gaussians, one after another
+        uint64_t bigs = __ballot(cur.valid && big && q == 0);
+        while (bigs) {
+            const int src = __builtin_ctzll(bigs);                 // lane (gl_b, 0) of that Gaussian
+            bigs &= bigs - 1;
+            const uint32_t bfirst = (uint32_t)__shfl((int)cur.first, src, 64);
+            const uint32_t bcount = (uint32_t)__shfl((int)cur.count, src, 64);
+            double part = 0.0;
+            if (cj < kSumPerRound)
+                for (uint32_t t = cj; t < bcount; t += kSumPerRound)
+                    part += (double)partial[((size_t)bfirst + t) * 9 + cq];
+            // lane (gl_b, q) collects component q: sum over j = 0..6 in order
+            double tot = 0.0;
+            for (int t = 0; t < kSumPerRound; t++) tot += __shfl(part, t * 9 + q, 64);
+            if (gl == src / 9) acc = tot;
+        }
+        if (cur.valid) g2[(size_t)cur.g * 9 + q] = (float)acc;
+        cur = nxt;
     }
-    if (valid) g2[(size_t)g * 9 + q] = (float)acc;
 }
 
 // The projection backward runs as two kernels over a batch of views, one

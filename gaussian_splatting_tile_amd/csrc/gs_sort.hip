@@ -23,7 +23,7 @@
 // memory; every grid is sized from host-known upper bounds and blocks past
 // the live count exit early.  Each radix pass is reduce-then-scan:
 // per-block digit counts (upsweep), a per-digit scan across blocks, then a
-// downsweep that ranks each 2048-item tile with wave ballots (match of equal
+// downsweep that ranks each 4096-item tile with wave ballots (match of equal
 // digits), orders it in LDS and writes every digit's run contiguously.
 #include "gs_internal.h"
 
@@ -32,10 +32,10 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kWaves = kBlock / kWave;          // 4
-constexpr int kIpt = 8;                         // items per thread per tile
-constexpr int kTileItems = kBlock * kIpt;       // 2048
-constexpr int kWaveItems = kWave * kIpt;        // 512
-constexpr int kMaxGrid = 1024;                  // radix blocks per pass
+constexpr int kIpt = 16;                        // items per thread per tile
+constexpr int kTileItems = kBlock * kIpt;       // 4096
+constexpr int kWaveItems = kWave * kIpt;        // 1024
+constexpr int kMaxGrid = 512;                   // radix blocks per pass
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
