@@ -6,8 +6,9 @@ Workload (default): 1M Gaussians, SH degree 3, fp32, the scene-like mixture
 (64 anisotropic clusters + a background shell at radius 50), 1920x1080,
 fx = fy = 1400, 8 orbit views; synthetic, seeded, resident in HBM before the
 timed region.  One step = the whole hot path for all 8 views: the 8 views'
-records in one batched projection, bin + sort per view (the views spread
-over 4 streams), the 8 forward blends in one batched launch, then the 8
+records in one batched projection, the 8 views' binning and depth sorts in
+one batched call (one launch per sort step), the 8 forward blends in one
+batched launch, then the 8
 screen-space backwards against an upstream dL/dimage ~ N(0, 1e-2) in one
 batched launch, and the projection's chain rule for all 8 views in one
 batched pass.
@@ -43,8 +44,10 @@ def parse():
     ap.add_argument("--workload", default="scene_1m",
                     choices=["scene_1m", "scene_5m", "scene_10m_4k", "box_100k", "tiny_1k"])
     ap.add_argument("--views", type=int, default=8)
-    ap.add_argument("--streams", type=int, default=4,
-                    help="HIP streams for the per-view projection and binning (1 = all on one stream)")
+    ap.add_argument("--sort", choices=["batched", "per-view"], default="batched",
+                    help="bin/sort all views in one gs_bin_sort_views call, or one gs_bin_sort per view")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="HIP streams the views' sorts spread over (batched: one group of views per stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -148,10 +151,10 @@ def main():
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
 
-    names = ("active_mask", "project_batch", "bin_sort", "render_fwd_batch", "render_bwd_batch",
-             "project_bwd_batch")
-    # the views' projection and binning are independent: they run on a few
-    # streams (default priority) and join before the batched blend
+    names = ("active_mask", "project_batch", "bin_sort", "bin_sort_batch", "render_fwd_batch",
+             "render_bwd_batch", "project_bwd_batch")
+    # the views' sorts are independent: they may run on a few streams
+    # (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
     lanes = [stream] + side
     ev = {k: [] for k in names}
@@ -185,11 +188,19 @@ def main():
         go.record(stream)
         for st in side:
             st.wait_event(go)
-        for i, b in enumerate(bufs):
-            st = lanes[i % len(lanes)]
-            timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
-                                                 b.schedule, b.bwd_index if do_bwd else None, None, b.k_total,
-                                                 b.ws, st), st)
+        if args.sort == "batched":
+            # the views split into one group per stream, each group sorted
+            # by one gs_bin_sort_views call
+            for i, st in enumerate(lanes):
+                grp = bufs[i::len(lanes)]
+                if grp:
+                    timed("bin_sort_batch", lambda: B.bin_sort_views(grp, do_bwd, st), st)
+        else:
+            for i, b in enumerate(bufs):
+                st = lanes[i % len(lanes)]
+                timed("bin_sort", lambda: B.bin_sort(b.splats, b.n, b.camc, b.k_capacity, b.vals, b.ranges,
+                                                     b.schedule, b.bwd_index if do_bwd else None, None,
+                                                     b.k_total, b.ws, st), st)
         for st in side:
             joined = torch.cuda.Event()
             joined.record(st)
@@ -257,7 +268,9 @@ def main():
                    "importance_keep": (keep if use_mask else None),
                    "lod_min_radius_px": cam0.lod_min_radius_px,
                    "step": ("importance mask, then " if use_mask else "") +
-                           "batched project, per view bin/sort, batched blend fwd of all views" +
+                           "batched project, " +
+                           ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
+                           ", batched blend fwd of all views" +
                            (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,

@@ -32,6 +32,13 @@ class GsFwdView(C.Structure):
                 ("final_T", C.c_void_p), ("n_contrib", C.c_void_p)]
 
 
+class GsSortView(C.Structure):
+    _fields_ = [("camera", GsCamera), ("splats", C.c_void_p), ("n", C.c_int64), ("k_capacity", C.c_int64),
+                ("vals", C.c_void_p), ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p),
+                ("bwd_index", C.c_void_p), ("keys", C.c_void_p), ("k_total", C.c_void_p),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+
+
 class GsBwdView(C.Structure):
     _fields_ = [("camera", GsCamera), ("n", C.c_int64), ("splats", C.c_void_p), ("vals", C.c_void_p),
                 ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("bwd_index", C.c_void_p),
@@ -57,6 +64,7 @@ class GsError(RuntimeError):
 
 _lib = None
 SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
+           "gs_bin_sort_views",
            "gs_render_fwd_views", "gs_render_bwd_screen_views", "gs_project_views",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
@@ -88,6 +96,7 @@ def lib():
     L.gs_bwd_index_words.argtypes = [i64, i64]
     L.gs_bwd_index_words.restype = sz
     L.gs_bin_sort.argtypes = [vp, i64, C.POINTER(GsCamera), i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gs_bin_sort_views.argtypes = [C.c_int32, C.POINTER(GsSortView), vp]
     L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
     L.gs_render_fwd_views.argtypes = [C.c_int32, C.POINTER(GsFwdView), vp, vp]
     L.gs_project_views.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp), vp]
@@ -108,7 +117,8 @@ def lib():
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
-    for name in ("gs_project", "gs_project_views", "gs_bin_sort", "gs_render_fwd", "gs_render_fwd_views",
+    for name in ("gs_project", "gs_project_views", "gs_bin_sort", "gs_bin_sort_views", "gs_render_fwd",
+                 "gs_render_fwd_views",
                  "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
                  "gs_project_bwd", "gs_active_mask"):
@@ -191,6 +201,19 @@ def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, 
     _check(lib().gs_bin_sort(_ptr(splats), int(n), C.byref(cam), int(k_capacity), _ptr(vals),
                              _ptr(tile_ranges), _ptr(schedule), _ptr(bwd_index), _ptr(keys), _ptr(k_total),
                              _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_bin_sort")
+
+
+def bin_sort_views(bufs, with_bwd: bool = True, stream=None):
+    """gs_bin_sort_views over ViewBuffers objects (their splats must be
+    current): one launch per sort step for up to 8 views."""
+    nv = len(bufs)
+    arr = (GsSortView * max(nv, 1))()
+    for i, b in enumerate(bufs):
+        arr[i] = GsSortView(b.camc, _ptr(b.splats), int(b.n), int(b.k_capacity), _ptr(b.vals), _ptr(b.ranges),
+                            _ptr(b.schedule), _ptr(b.bwd_index) if with_bwd else None, _ptr(b.keys),
+                            _ptr(b.k_total),
+                            _ptr(b.ws), _nbytes(b.ws))
+    _check(lib().gs_bin_sort_views(nv, arr, _stream(stream)), "gs_bin_sort_views")
 
 
 def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[float], image, final_T,

@@ -115,22 +115,73 @@ size_t gs_bwd_index_words(int64_t n, int64_t k_capacity)
     return (size_t)k_capacity + 2 * (size_t)n + 2;
 }
 
+static gs_status check_sort_view(const gs_sort_view &v)
+{
+    if (v.n < 0 || v.n > INT32_MAX || v.k_capacity < 0 || v.k_capacity >= (int64_t)UINT32_MAX)
+        return GS_ERR_INVALID_ARG;
+    if (!camera_ok(&v.camera) || !v.tile_ranges || !v.schedule || !v.k_total) return GS_ERR_INVALID_ARG;
+    if (v.n > 0 && !v.splats) return GS_ERR_INVALID_ARG;
+    if (v.k_capacity > 0 && !v.vals) return GS_ERR_INVALID_ARG;
+    const Cam cam = make_cam(v.camera);
+    const size_t need = bin_sort_workspace(v.n, v.k_capacity, cam.tiles_x * cam.tiles_y);
+    if (v.workspace_bytes < need || !v.workspace) return GS_ERR_WORKSPACE;
+    return GS_OK;
+}
+
+static SortJob sort_job(const gs_sort_view &v)
+{
+    SortJob j;
+    j.splats = (const Splat *)v.splats;
+    j.n = v.n;
+    j.cam = make_cam(v.camera);
+    j.cap = v.k_capacity;
+    j.vals = v.vals;
+    j.ranges = v.tile_ranges;
+    j.schedule = v.schedule;
+    j.bwd_index = v.bwd_index;
+    j.keys = v.keys;
+    j.k_total = v.k_total;
+    j.ws = v.workspace;
+    return j;
+}
+
 gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera, int64_t k_capacity,
                       uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
                       uint64_t *keys, uint64_t *k_total, void *workspace, size_t workspace_bytes,
                       void *stream)
 {
-    if (n < 0 || n > INT32_MAX || k_capacity < 0 || k_capacity >= (int64_t)UINT32_MAX)
-        return GS_ERR_INVALID_ARG;
-    if (!camera_ok(camera) || !tile_ranges || !schedule || !k_total) return GS_ERR_INVALID_ARG;
-    if (n > 0 && !splats) return GS_ERR_INVALID_ARG;
-    if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
-    const Cam cam = make_cam(*camera);
-    const size_t need = bin_sort_workspace(n, k_capacity, cam.tiles_x * cam.tiles_y);
-    if (workspace_bytes < need || !workspace) return GS_ERR_WORKSPACE;
-    return from_hip(launch_bin_sort((const Splat *)splats, n, cam, k_capacity, vals, tile_ranges, schedule,
-                                    bwd_index, keys, k_total, workspace, workspace_bytes,
-                                    (hipStream_t)stream));
+    if (!camera) return GS_ERR_INVALID_ARG;
+    gs_sort_view v;
+    v.camera = *camera;
+    v.splats = splats;
+    v.n = n;
+    v.k_capacity = k_capacity;
+    v.vals = vals;
+    v.tile_ranges = tile_ranges;
+    v.schedule = schedule;
+    v.bwd_index = bwd_index;
+    v.keys = keys;
+    v.k_total = k_total;
+    v.workspace = workspace;
+    v.workspace_bytes = workspace_bytes;
+    return gs_bin_sort_views(1, &v, stream);
+}
+
+gs_status gs_bin_sort_views(int32_t n_views, const gs_sort_view *views, void *stream)
+{
+    if (n_views < 0 || (n_views > 0 && !views)) return GS_ERR_INVALID_ARG;
+    for (int v = 0; v < n_views; v++) {
+        const gs_status st = check_sort_view(views[v]);
+        if (st != GS_OK) return st;
+    }
+    for (int v0 = 0; v0 < n_views; v0 += kMaxSortViews) {
+        const int count = n_views - v0 < kMaxSortViews ? n_views - v0 : kMaxSortViews;
+        SortJob jobs[kMaxSortViews];
+        for (int i = 0; i < count; i++) jobs[i] = sort_job(views[v0 + i]);
+        const gs_status st = from_hip(launch_bin_sort_views(count, jobs, (hipStream_t)stream));
+        if (st != GS_OK) return st;
+    }
+    return GS_OK;
 }
 
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint32_t *tile_ranges,

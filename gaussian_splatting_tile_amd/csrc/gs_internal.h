@@ -142,12 +142,22 @@ struct ViewBatch {
 hipError_t launch_project_bwd(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out,
                               hipStream_t s);
 
-struct SortWorkspace;
 size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles);
 size_t schedule_words(int n_tiles);
-hipError_t launch_bin_sort(const Splat *splats, int64_t n, const Cam &cam, int64_t k_capacity,
-                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
-                           uint64_t *keys, uint64_t *k_total, void *ws, size_t ws_bytes, hipStream_t s);
+// Views one binning launch sequence sorts together.
+constexpr int kMaxSortViews = 8;
+struct SortJob {
+    const Splat *splats;
+    int64_t n;
+    Cam cam;
+    int64_t cap;                  // key capacity
+    uint32_t *vals, *ranges, *schedule;
+    uint32_t *bwd_index;          // optional
+    uint64_t *keys;               // optional
+    uint64_t *k_total;
+    void *ws;                     // bin_sort_workspace(n, cap) bytes
+};
+hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s);
 size_t active_mask_workspace(int64_t n);
 hipError_t launch_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *ws,
                               size_t ws_bytes, hipStream_t s);

@@ -272,14 +272,13 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     const float o = opac[g];
     const bool on = (active == nullptr || active[g] != 0) && all_finite(mx, my, mz, sx, sy, sz, qw, qx, qy, qz, o);
 
-    // the views of the batch, parameters read once; the SH rows are re-read
-    // per view (cache hits) through an opaque copy of their pointer, so the
-    // compiler does not hold all 3 K coefficients in registers
+    // the views of the batch, parameters and SH coefficients read once
+    float shc[3 * K];
+#pragma unroll
+    for (int i = 0; i < 3 * K; i++) shc[i] = on ? ld_sh(sh + (size_t)i * n + g) : 0.0f;
     for (int v = 0; v < views.count; v++) {
     const Cam &cam = views.cam[v];
     Splat *__restrict__ out = views.out[v];
-    const TSH *shv = sh;
-    asm volatile("" : "+s"(shv));
     Splat rec;
     rec.a = rec.b = rec.c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     bool vis = on;
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
             for (int ch = 0; ch < 3; ch++) {
                 float s = 0.0f;
 #pragma unroll
-                for (int j = 0; j < K; j++) s = s + ld_sh(shv + ((size_t)(j * 3 + ch)) * n + g) * Y[j];
+                for (int j = 0; j < K; j++) s = s + shc[j * 3 + ch] * Y[j];
                 const float val = 0.5f + s;
                 col[ch] = val < 0.0f ? 0.0f : val;
             }

@@ -86,13 +86,36 @@ __device__ __forceinline__ void chunk_of(uint32_t n, uint32_t &begin, uint32_t &
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t *__restrict__ keys,
-                                                        const uint32_t *__restrict__ n_ptr, int shift,
-                                                        int bits, int drop_sentinel,
-                                                        uint32_t *__restrict__ counts)
+// Every kernel below runs over a batch of views: blockIdx.y picks the view,
+// whose arguments sit in the kernel argument segment; the x grid is sized
+// for the largest view and blocks past a view's own extent exit early.
+template <typename A>
+struct Batch {
+    int count;
+    A v[kMaxSortViews];
+};
+
+// Per-view arguments of one radix pass.  vals_in NULL means the identity
+// (the item's input index); vals2_in/vals2_out (both or neither) carry a
+// second value array.
+struct PassArgs {
+    const uint32_t *keys_in, *vals_in, *vals2_in;
+    uint32_t *keys_out, *vals_out, *vals2_out;
+    const uint32_t *n_ptr;       // live items
+    uint32_t *n_out_ptr;         // items kept (optional)
+    uint32_t *counts;            // per-digit, per-block counts [256][grid]
+    uint32_t *digit_total;       // [256]
+    int shift, bits;
+};
+
+__global__ __launch_bounds__(kBlock) void radix_upsweep(const Batch<PassArgs> b, int drop_sentinel)
 {
     __shared__ uint32_t hist[kWaves][256];
-    const uint32_t n = *n_ptr;
+    const PassArgs &a = b.v[blockIdx.y];
+    const uint32_t *__restrict__ keys = a.keys_in;
+    uint32_t *__restrict__ counts = a.counts;
+    const int shift = a.shift, bits = a.bits;
+    const uint32_t n = *a.n_ptr;
     uint32_t begin, end;
     chunk_of(n, begin, end);
     const uint32_t mask = (1u << bits) - 1u;
@@ -120,10 +143,11 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t *__restri
 }
 
 // One block per digit: exclusive scan of that digit's per-block counts.
-__global__ __launch_bounds__(kBlock) void radix_scan(uint32_t *__restrict__ counts, int G,
-                                                     uint32_t *__restrict__ digit_total)
+__global__ __launch_bounds__(kBlock) void radix_scan(const Batch<PassArgs> b, int G)
 {
-    uint32_t *row = counts + (size_t)blockIdx.x * G;
+    const PassArgs &a = b.v[blockIdx.y];
+    uint32_t *__restrict__ digit_total = a.digit_total;
+    uint32_t *row = a.counts + (size_t)blockIdx.x * G;
     const int per = (G + kBlock - 1) / kBlock;
     const int b0 = threadIdx.x * per;
     uint32_t local = 0;
@@ -140,16 +164,22 @@ __global__ __launch_bounds__(kBlock) void radix_scan(uint32_t *__restrict__ coun
     if (threadIdx.x == 0) digit_total[blockIdx.x] = total;
 }
 
-// Values: vals_in NULL means the identity (the item's input index).  With
-// kTwo a second value array rides along (vals2_in, vals2_out).
+// With kTwo, the views that have a second value array carry it along.
 template <bool kTwo>
-__global__ __launch_bounds__(kBlock) void radix_downsweep(
-    const uint32_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
-    const uint32_t *__restrict__ vals2_in, uint32_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
-    uint32_t *__restrict__ vals2_out, const uint32_t *__restrict__ n_ptr, uint32_t *__restrict__ n_out_ptr,
-    int shift, int bits, int drop_sentinel, const uint32_t *__restrict__ counts,
-    const uint32_t *__restrict__ digit_total)
+__global__ __launch_bounds__(kBlock) void radix_downsweep(const Batch<PassArgs> b, int drop_sentinel)
 {
+    const PassArgs &a = b.v[blockIdx.y];
+    const uint32_t *__restrict__ keys_in = a.keys_in;
+    const uint32_t *__restrict__ vals_in = a.vals_in;
+    const uint32_t *__restrict__ vals2_in = a.vals2_in;
+    uint32_t *__restrict__ keys_out = a.keys_out;
+    uint32_t *__restrict__ vals_out = a.vals_out;
+    uint32_t *__restrict__ vals2_out = a.vals2_out;
+    uint32_t *__restrict__ n_out_ptr = a.n_out_ptr;
+    const uint32_t *__restrict__ counts = a.counts;
+    const uint32_t *__restrict__ digit_total = a.digit_total;
+    const int shift = a.shift, bits = a.bits;
+    const bool two = kTwo && vals2_out != nullptr;
     __shared__ uint32_t digit_base[256];
     __shared__ uint32_t tile_start[256];
     __shared__ uint32_t tile_cnt[256];
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     __shared__ uint32_t sv2[kTwo ? kTileItems : 1];
     __shared__ uint32_t s_tile_total;
 
-    const uint32_t n = *n_ptr;
+    const uint32_t n = *a.n_ptr;
     uint32_t begin, end;
     chunk_of(n, begin, end);
     const uint32_t mask = (1u << bits) - 1u;
@@ -186,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             const uint32_t ci = idx < end ? idx : end - 1;
             kk[r] = keys_in[ci];
             vv[r] = vals_in ? vals_in[ci] : idx;
-            if (kTwo) vv2[r] = vals2_in[ci];
+            if (two) vv2[r] = vals2_in[ci];
         }
     };
     if (begin < end) load_tile(begin, k, v, v2);
@@ -243,7 +273,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             const uint32_t pos = tile_start[d] + wave_cnt[w][d] + loc[r];
             sk[pos] = k[r];
             sv[pos] = v[r];
-            if (kTwo) sv2[pos] = v2[r];
+            if (two) sv2[pos] = v2[r];
         }
         __syncthreads();
         const uint32_t tot = s_tile_total;
@@ -253,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             const uint32_t o = digit_base[d] + (i - tile_start[d]);
             keys_out[o] = kk;
             vals_out[o] = sv[i];
-            if (kTwo) vals2_out[o] = sv2[i];
+            if (two) vals2_out[o] = sv2[i];
         }
         __syncthreads();
         digit_base[tid] += tile_cnt[tid];
@@ -263,7 +293,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
             for (int r = 0; r < kIpt; r++) {
                 k[r] = nk[r];
                 v[r] = nv[r];
-                if (kTwo) v2[r] = nv2[r];
+                if (two) v2[r] = nv2[r];
             }
         }
     }
@@ -271,12 +301,21 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
 
 // ---------------------------------------------------------------------------
 // Setup: counters, empty tile ranges, depth keys of the visible Gaussians.
-__global__ __launch_bounds__(kBlock) void bin_init(const Splat *__restrict__ splats, uint32_t n,
-                                                   uint32_t *__restrict__ dkeys,
-                                                   uint32_t *__restrict__ dvals,
-                                                   uint32_t *__restrict__ ranges, uint32_t n_ranges,
-                                                   uint32_t *__restrict__ counters)
+struct InitArgs {
+    const Splat *splats;
+    uint32_t n, n_ranges;
+    uint32_t *dkeys, *dvals, *ranges, *counters;
+};
+
+__global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
 {
+    const InitArgs &a = b.v[blockIdx.y];
+    const Splat *__restrict__ splats = a.splats;
+    const uint32_t n = a.n, n_ranges = a.n_ranges;
+    uint32_t *__restrict__ dkeys = a.dkeys;
+    uint32_t *__restrict__ dvals = a.dvals;
+    uint32_t *__restrict__ ranges = a.ranges;
+    uint32_t *__restrict__ counters = a.counters;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i < n) {
         const float4 a = splats[i].a;
@@ -296,21 +335,38 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Splat *__restrict__ spl
 // width) for the duplication, and the block's sum of tiles touched.
 constexpr int kScanItems = kBlock;               // Gaussians per scan / duplication block
 
-__global__ __launch_bounds__(kBlock) void scan_reduce(const Splat *__restrict__ splats,
-                                                      const uint32_t *__restrict__ order,
-                                                      const uint32_t *__restrict__ m_ptr, Cam cam,
-                                                      uint2 *__restrict__ rect_info,
-                                                      uint32_t *__restrict__ counts,
-                                                      uint64_t *__restrict__ block_sums)
+// Per-view arguments of the slot scan and the duplication.
+struct DupArgs {
+    const Splat *splats;
+    const uint32_t *order;       // visible Gaussians in depth order
+    const uint32_t *m_ptr;       // their number
+    int tiles_x, tiles_y;
+    uint64_t cap;                // key capacity
+    uint2 *rect_info;
+    uint32_t *counts;
+    uint64_t *block_sums;        // per 256 Gaussians: tiles, then their exclusive scan
+    uint64_t *k_total;
+    uint32_t *k_eff;             // K clamped to the capacity
+    uint32_t *tile_keys, *gslot; // duplicated entries
+    uint32_t *bwd_order, *bwd_off, *bwd_count;   // optional backward index parts
+};
+
+__global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
 {
-    const uint32_t m = *m_ptr;
+    const DupArgs &a = b.v[blockIdx.y];
+    const Splat *__restrict__ splats = a.splats;
+    const uint32_t *__restrict__ order = a.order;
+    uint2 *__restrict__ rect_info = a.rect_info;
+    uint32_t *__restrict__ counts = a.counts;
+    uint64_t *__restrict__ block_sums = a.block_sums;
+    const uint32_t m = *a.m_ptr;
     const uint32_t j = blockIdx.x * kScanItems + threadIdx.x;
     if (blockIdx.x * kScanItems >= m) return;
     uint64_t c = 0;
     if (j < m) {
         const Splat sp = splats[order[j]];
-        const Rect rc = tile_rect(sp.a.x, sp.a.y, (float)__float_as_int(sp.a.w), (float)cam.tiles_x,
-                                  (float)cam.tiles_y);
+        const Rect rc = tile_rect(sp.a.x, sp.a.y, (float)__float_as_int(sp.a.w), (float)a.tiles_x,
+                                  (float)a.tiles_y);
         const uint32_t w = (uint32_t)(rc.x1 - rc.x0);
         c = __float_as_uint(sp.c.w);
         rect_info[j] = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16), w);
@@ -322,14 +378,14 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Splat *__restrict__ 
 }
 
 // Exclusive scan of the block sums (one block); K and the clamped count.
-__global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block_sums,
-                                                    const uint32_t *__restrict__ m_ptr, uint64_t cap,
-                                                    uint64_t *__restrict__ k_total,
-                                                    uint32_t *__restrict__ k_eff,
-                                                    uint32_t *__restrict__ bwd_off, uint32_t *__restrict__ bwd_count)
+__global__ __launch_bounds__(1024) void scan_blocks(const Batch<DupArgs> b)
 {
     __shared__ uint64_t wsum[16];
-    const uint32_t m = *m_ptr;
+    const DupArgs &a = b.v[blockIdx.y];
+    uint64_t *__restrict__ block_sums = a.block_sums;
+    const uint64_t cap = a.cap;
+    uint32_t *__restrict__ bwd_off = a.bwd_off;
+    const uint32_t m = *a.m_ptr;
     const int nb = (int)((m + kScanItems - 1) / kScanItems);
     const int per = (nb + 1023) / 1024;
     const int b0 = threadIdx.x * per;
@@ -354,11 +410,11 @@ __global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block
             run += c;
         }
     if (threadIdx.x == 0) {
-        *k_total = total;
-        *k_eff = (uint32_t)(total < cap ? total : cap);
+        *a.k_total = total;
+        *a.k_eff = (uint32_t)(total < cap ? total : cap);
         if (bwd_off) {
             bwd_off[m] = (uint32_t)(total < 0xFFFFFFFFull ? total : 0xFFFFFFFFull);
-            *bwd_count = m;
+            *a.bwd_count = m;
         }
     }
 }
@@ -368,19 +424,25 @@ __global__ __launch_bounds__(1024) void scan_blocks(uint64_t *__restrict__ block
 // in LDS, then hands the block's entries out 256 at a time: each lane finds
 // its Gaussian by binary search over the block's offsets, so the work is
 // balanced however unequal the rects are.
-__global__ __launch_bounds__(kBlock) void duplicate_keys(
-    const uint32_t *__restrict__ order, const uint32_t *__restrict__ m_ptr,
-    const uint2 *__restrict__ rect_info, const uint32_t *__restrict__ counts,
-    const uint64_t *__restrict__ block_offsets, int tiles_x, uint64_t cap,
-    uint32_t *__restrict__ tile_keys, uint32_t *__restrict__ gslot, uint32_t *__restrict__ bwd_order,
-    uint32_t *__restrict__ bwd_off)
+__global__ __launch_bounds__(kBlock) void duplicate_keys(const Batch<DupArgs> b)
 {
     __shared__ uint32_t s_off[kScanItems];
     __shared__ uint32_t s_g[kScanItems];
     __shared__ uint32_t s_xy[kScanItems];
     __shared__ uint32_t s_w[kScanItems];
     __shared__ float s_inv[kScanItems];
-    const uint32_t m = *m_ptr;
+    const DupArgs &a = b.v[blockIdx.y];
+    const uint32_t *__restrict__ order = a.order;
+    const uint2 *__restrict__ rect_info = a.rect_info;
+    const uint32_t *__restrict__ counts = a.counts;
+    const uint64_t *__restrict__ block_offsets = a.block_sums;
+    const int tiles_x = a.tiles_x;
+    const uint64_t cap = a.cap;
+    uint32_t *__restrict__ tile_keys = a.tile_keys;
+    uint32_t *__restrict__ gslot = a.gslot;
+    uint32_t *__restrict__ bwd_order = a.bwd_order;
+    uint32_t *__restrict__ bwd_off = a.bwd_off;
+    const uint32_t m = *a.m_ptr;
     const uint32_t base = blockIdx.x * kScanItems;
     if (base >= m) return;
     const uint32_t n_items = min((uint32_t)kScanItems, m - base);
@@ -430,16 +492,26 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(
 // 64-bit keys.  Without tile passes (a one-tile image) the duplication order
 // is final: the entries' Gaussians are copied from gslot and their slots are
 // the identity.
-__global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const uint32_t *__restrict__ tile_keys,
-                                                             const uint32_t *__restrict__ k_ptr,
-                                                             const Splat *__restrict__ splats,
-                                                             const uint32_t *__restrict__ gslot,
-                                                             uint32_t *__restrict__ ranges,
-                                                             uint32_t *__restrict__ vals,
-                                                             uint32_t *__restrict__ entry_slots,
-                                                             uint64_t *__restrict__ keys64)
+struct RangeArgs {
+    const uint32_t *tile_keys;   // sorted tile ids
+    const uint32_t *k_ptr;       // K clamped to the capacity
+    const Splat *splats;
+    const uint32_t *gslot;       // without tile passes: the duplication order's Gaussians
+    uint32_t *ranges, *vals, *entry_slots;
+    uint64_t *keys64;
+};
+
+__global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const Batch<RangeArgs> b)
 {
-    const uint32_t k = *k_ptr;
+    const RangeArgs &a = b.v[blockIdx.y];
+    const uint32_t *__restrict__ tile_keys = a.tile_keys;
+    const Splat *__restrict__ splats = a.splats;
+    const uint32_t *__restrict__ gslot = a.gslot;
+    uint32_t *__restrict__ ranges = a.ranges;
+    uint32_t *__restrict__ vals = a.vals;
+    uint32_t *__restrict__ entry_slots = a.entry_slots;
+    uint64_t *__restrict__ keys64 = a.keys64;
+    const uint32_t k = *a.k_ptr;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i >= k) return;
     const uint32_t t = tile_keys[i];
@@ -476,9 +548,22 @@ __device__ __forceinline__ int length_bin(uint32_t L)
     return 1 + 2 * lg + half;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const uint32_t *__restrict__ ranges,
-                                                                int n_tiles, uint32_t *__restrict__ sched)
+struct SchedArgs {
+    const uint32_t *ranges;
+    int n_tiles;
+    uint32_t *sched;
+    uint64_t *k_total;           // for a view without Gaussians: K = 0 is written here
+    uint32_t *bwd_tail;          // and here its backward index's K and visible count (0, 0)
+};
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const Batch<SchedArgs> b)
 {
+    const SchedArgs &a = b.v[blockIdx.y];
+    const uint32_t *__restrict__ ranges = a.ranges;
+    const int n_tiles = a.n_tiles;
+    uint32_t *__restrict__ sched = a.sched;
+    if (a.k_total != nullptr && threadIdx.x == 0) *a.k_total = 0;
+    if (a.bwd_tail != nullptr && threadIdx.x < 2) a.bwd_tail[threadIdx.x] = 0;
     __shared__ uint32_t hist[kSchedBins];
     __shared__ uint32_t base[kSchedBins];
     const int tid = threadIdx.x;
@@ -576,20 +661,15 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     return c.off + 256;
 }
 
-// One stable pass; v2in/v2out (both or neither) carry a second value array.
-hipError_t radix_pass(const uint32_t *kin, const uint32_t *vin, const uint32_t *v2in, uint32_t *kout,
-                      uint32_t *vout, uint32_t *v2out, const uint32_t *n_ptr, uint32_t *n_out_ptr,
-                      uint64_t max_items, int shift, int bits, int drop, const BinWs &w, hipStream_t s)
+// One stable pass over the views of a batch (grid: G blocks per view).
+hipError_t radix_pass(const Batch<PassArgs> &b, int G, int drop, bool two, hipStream_t s)
 {
-    const int G = radix_grid(max_items);
-    radix_upsweep<<<G, kBlock, 0, s>>>(kin, n_ptr, shift, bits, drop, w.digit_counts);
-    radix_scan<<<256, kBlock, 0, s>>>(w.digit_counts, G, w.digit_total);
-    if (v2out)
-        radix_downsweep<true><<<G, kBlock, 0, s>>>(kin, vin, v2in, kout, vout, v2out, n_ptr, n_out_ptr, shift,
-                                                   bits, drop, w.digit_counts, w.digit_total);
+    radix_upsweep<<<dim3(G, b.count), kBlock, 0, s>>>(b, drop);
+    radix_scan<<<dim3(256, b.count), kBlock, 0, s>>>(b, G);
+    if (two)
+        radix_downsweep<true><<<dim3(G, b.count), kBlock, 0, s>>>(b, drop);
     else
-        radix_downsweep<false><<<G, kBlock, 0, s>>>(kin, vin, nullptr, kout, vout, nullptr, n_ptr, n_out_ptr,
-                                                    shift, bits, drop, w.digit_counts, w.digit_total);
+        radix_downsweep<false><<<dim3(G, b.count), kBlock, 0, s>>>(b, drop);
     return hipGetLastError();
 }
 
@@ -608,84 +688,139 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_bin_sort(const Splat *splats, int64_t n64, const Cam &cam, int64_t cap,
-                           uint32_t *vals, uint32_t *tile_ranges, uint32_t *schedule, uint32_t *bwd_index,
-                           uint64_t *keys, uint64_t *k_total, void *ws_ptr, size_t ws_bytes, hipStream_t s)
+// The views of a batch go through every step together, one launch per step
+// (blockIdx.y = view), so small views still fill the device.
+hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
 {
-    (void)ws_bytes;
-    BinWs w;
-    carve_bin((char *)ws_ptr, n64, cap, &w);
-    const uint32_t n = (uint32_t)n64;
-    const uint32_t n_tiles = (uint32_t)(cam.tiles_x * cam.tiles_y);
-    const uint32_t n_ranges = 2 * n_tiles;
+    if (count < 1 || count > kMaxSortViews) return hipErrorInvalidValue;
     hipError_t e;
+    BinWs w[kMaxSortViews];
+    uint32_t n_max = 0, init_max = 0, tbits_max = 0;
+    uint64_t cap_max = 0;
+    bool any_bwd = false;
+    for (int v = 0; v < count; v++) {
+        const SortJob &J = jobs[v];
+        carve_bin((char *)J.ws, J.n, J.cap, &w[v]);
+        const uint32_t n = (uint32_t)J.n;
+        const uint32_t n_ranges = 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y);
+        n_max = n > n_max ? n : n_max;
+        init_max = n > init_max ? n : init_max;
+        init_max = n_ranges > init_max ? n_ranges : init_max;
+        const uint32_t tb = (uint32_t)bits_for((uint32_t)(J.cam.tiles_x * J.cam.tiles_y));
+        tbits_max = tb > tbits_max ? tb : tbits_max;
+        cap_max = (uint64_t)J.cap > cap_max ? (uint64_t)J.cap : cap_max;
+        any_bwd = any_bwd || J.bwd_index != nullptr;
+    }
 
-    const uint32_t init_items = n > n_ranges ? n : n_ranges;
-    bin_init<<<(init_items + kBlock - 1) / kBlock, kBlock, 0, s>>>(splats, n, w.dk[0], w.dv[0],
-                                                                   tile_ranges, n_ranges, w.counters);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {   // counters, empty ranges, depth keys
+        Batch<InitArgs> b;
+        b.count = count;
+        for (int v = 0; v < count; v++) {
+            const SortJob &J = jobs[v];
+            b.v[v] = InitArgs{J.splats, (uint32_t)J.n, 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y),
+                              w[v].dk[0], w[v].dv[0], J.ranges, w[v].counters};
+        }
+        bin_init<<<dim3((init_max + kBlock - 1) / kBlock, count), kBlock, 0, s>>>(b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
-    if (n > 0) {
-        // 1. depth: 4 x 8-bit passes; the first drops the culled Gaussians
+    // the views with Gaussians go through the sort; the others have K = 0
+    int live[kMaxSortViews], n_live = 0;
+    for (int v = 0; v < count; v++)
+        if (jobs[v].n > 0) live[n_live++] = v;
+
+    if (n_live > 0) {
+        // 1. depth: 4 x 8-bit passes over the Gaussians; the first drops the
+        // culled ones
         int cur = 0;
         for (int pass = 0; pass < 4; pass++) {
-            const uint32_t *n_in = pass == 0 ? &w.counters[0] : &w.counters[1];
-            e = radix_pass(w.dk[cur], w.dv[cur], nullptr, w.dk[cur ^ 1], w.dv[cur ^ 1], nullptr, n_in,
-                           &w.counters[1], n, 8 * pass, 8, pass == 0, w, s);
-            if (e != hipSuccess) return e;
+            Batch<PassArgs> b;
+            b.count = n_live;
+            for (int i = 0; i < n_live; i++) {
+                const BinWs &W = w[live[i]];
+                b.v[i] = PassArgs{W.dk[cur], W.dv[cur], nullptr, W.dk[cur ^ 1], W.dv[cur ^ 1], nullptr,
+                                  pass == 0 ? &W.counters[0] : &W.counters[1], &W.counters[1],
+                                  W.digit_counts, W.digit_total, 8 * pass, 8};
+            }
+            if ((e = radix_pass(b, radix_grid(n_max), pass == 0, false, s)) != hipSuccess) return e;
             cur ^= 1;
         }
-        const uint32_t *order = w.dv[cur];
 
         // 2. slots and duplication (K clamped to the capacity in counters[2])
-        const uint32_t nblk = (n + kScanItems - 1) / kScanItems;
-        scan_reduce<<<nblk, kBlock, 0, s>>>(splats, order, &w.counters[1], cam, w.rect_info, w.counts,
-                                            w.block_sums);
-        // backward index: [entry slot: cap][depth-ordered Gaussian: n][first slot: n + 1][visible count]
-        uint32_t *bwd_order = bwd_index ? bwd_index + cap : nullptr;
-        uint32_t *bwd_off = bwd_index ? bwd_index + cap + n : nullptr;
-        uint32_t *bwd_count = bwd_index ? bwd_index + cap + 2 * (size_t)n + 1 : nullptr;
-        scan_blocks<<<1, 1024, 0, s>>>(w.block_sums, &w.counters[1], (uint64_t)cap, k_total, &w.counters[2],
-                                       bwd_off, bwd_count);
+        Batch<DupArgs> d;
+        d.count = n_live;
+        for (int i = 0; i < n_live; i++) {
+            const SortJob &J = jobs[live[i]];
+            const BinWs &W = w[live[i]];
+            const size_t n = (size_t)J.n, cap = (size_t)J.cap;
+            // backward index: [entry slot: cap][depth-ordered Gaussian: n][first slot: n + 1][visible count]
+            uint32_t *bi = J.bwd_index;
+            d.v[i] = DupArgs{J.splats, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
+                             W.rect_info, W.counts, W.block_sums, J.k_total, &W.counters[2], W.tk[0], W.gslot,
+                             bi ? bi + cap : nullptr, bi ? bi + cap + n : nullptr,
+                             bi ? bi + cap + 2 * n + 1 : nullptr};
+        }
+        const uint32_t nblk = (n_max + kScanItems - 1) / kScanItems;
+        scan_reduce<<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        scan_blocks<<<dim3(1, n_live), 1024, 0, s>>>(d);
+        duplicate_keys<<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+
         // 3. tile passes over the tile ids, carrying each entry's Gaussian
         // and, for the backward index, its duplication slot (the identity on
-        // the way in); the last pass writes straight into the outputs
-        const int tbits = bits_for(n_tiles);
-        const int passes = tbits == 0 ? 0 : (tbits + 7) / 8;
-        uint32_t *entry_slots = bwd_index;                     // [cap], optional
-        duplicate_keys<<<nblk, kBlock, 0, s>>>(order, &w.counters[1], w.rect_info, w.counts, w.block_sums,
-                                               cam.tiles_x, (uint64_t)cap, w.tk[0], w.gslot, bwd_order, bwd_off);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        int shift = 0;
+        // the way in); the last pass writes straight into the outputs.  A
+        // view with fewer tile bits than the batch's widest takes zero-bit
+        // passes (a stable copy).
+        const int passes = tbits_max == 0 ? 0 : ((int)tbits_max + 7) / 8;
         for (int p = 0; p < passes; p++) {
-            const int bits = (tbits - shift) < 8 ? (tbits - shift) : 8;
             const bool last = p == passes - 1;
-            const uint32_t *gin = p == 0 ? w.gslot : w.tv[(p - 1) & 1];
-            uint32_t *gout = last ? vals : w.tv[p & 1];
-            if (entry_slots) {
-                const uint32_t *sin = p == 0 ? nullptr : w.ts[(p - 1) & 1];
-                uint32_t *sout = last ? entry_slots : w.ts[p & 1];
-                e = radix_pass(w.tk[p & 1], sin, gin, w.tk[(p + 1) & 1], sout, gout, &w.counters[2], nullptr,
-                               (uint64_t)cap, shift, bits, 0, w, s);
-            } else {
-                e = radix_pass(w.tk[p & 1], gin, nullptr, w.tk[(p + 1) & 1], gout, nullptr, &w.counters[2],
-                               nullptr, (uint64_t)cap, shift, bits, 0, w, s);
+            Batch<PassArgs> b;
+            b.count = n_live;
+            for (int i = 0; i < n_live; i++) {
+                const SortJob &J = jobs[live[i]];
+                const BinWs &W = w[live[i]];
+                const int tbits = bits_for((uint32_t)(J.cam.tiles_x * J.cam.tiles_y));
+                const int shift = 8 * p < tbits ? 8 * p : tbits;
+                const int bits = tbits - shift < 8 ? tbits - shift : 8;
+                const uint32_t *gin = p == 0 ? W.gslot : W.tv[(p - 1) & 1];
+                uint32_t *gout = last ? J.vals : W.tv[p & 1];
+                uint32_t *entry_slots = J.bwd_index;                  // [cap], optional
+                if (entry_slots) {
+                    const uint32_t *sin = p == 0 ? nullptr : W.ts[(p - 1) & 1];
+                    uint32_t *sout = last ? entry_slots : W.ts[p & 1];
+                    b.v[i] = PassArgs{W.tk[p & 1], sin, gin, W.tk[(p + 1) & 1], sout, gout, &W.counters[2],
+                                      nullptr, W.digit_counts, W.digit_total, shift, bits};
+                } else {
+                    b.v[i] = PassArgs{W.tk[p & 1], gin, nullptr, W.tk[(p + 1) & 1], gout, nullptr,
+                                      &W.counters[2], nullptr, W.digit_counts, W.digit_total, shift, bits};
+                }
             }
-            if (e != hipSuccess) return e;
-            shift += bits;
+            if ((e = radix_pass(b, radix_grid(cap_max), 0, any_bwd, s)) != hipSuccess) return e;
         }
+
         // 4. ranges and the optional 64-bit keys
-        const uint64_t kgrid = ((uint64_t)cap + kBlock - 1) / kBlock;
-        if (kgrid > 0)
-            tile_ranges_kernel<<<(unsigned)kgrid, kBlock, 0, s>>>(w.tk[passes & 1], &w.counters[2], splats,
-                                                                  passes == 0 ? w.gslot : nullptr, tile_ranges,
-                                                                  vals, entry_slots, keys);
-    } else {
-        // no Gaussians: K = 0
-        fill_u32_kernel<<<1, kBlock, 0, s>>>((uint32_t *)k_total, 0u, 2);
+        Batch<RangeArgs> r;
+        r.count = n_live;
+        for (int i = 0; i < n_live; i++) {
+            const SortJob &J = jobs[live[i]];
+            const BinWs &W = w[live[i]];
+            r.v[i] = RangeArgs{W.tk[passes & 1], &W.counters[2], J.splats, passes == 0 ? W.gslot : nullptr,
+                               J.ranges, J.vals, J.bwd_index, J.keys};
+        }
+        const uint64_t kgrid = (cap_max + kBlock - 1) / kBlock;
+        if (kgrid > 0) tile_ranges_kernel<<<dim3((unsigned)kgrid, n_live), kBlock, 0, s>>>(r);
     }
+
     // 5. longest-first tile schedule for the blend kernels
-    schedule_tiles<<<1, kSchedThreads, 0, s>>>(tile_ranges, (int)n_tiles, schedule);
+    Batch<SchedArgs> sb;
+    sb.count = count;
+    for (int v = 0; v < count; v++) {
+        const SortJob &J = jobs[v];
+        const bool empty = J.n == 0;
+        sb.v[v] = SchedArgs{J.ranges, J.cam.tiles_x * J.cam.tiles_y, J.schedule, empty ? J.k_total : nullptr,
+                            empty && J.bwd_index ? J.bwd_index + J.cap : nullptr};
+    }
+    schedule_tiles<<<dim3(1, count), kSchedThreads, 0, s>>>(sb);
     return hipGetLastError();
 }
 

@@ -194,6 +194,31 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n,
                       uint32_t *bwd_index, uint64_t *keys, uint64_t *k_total,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* One view's arguments of gs_bin_sort, for gs_bin_sort_views. */
+typedef struct gs_sort_view {
+    gs_camera camera;
+    const gs_splat *splats;
+    int64_t n;
+    int64_t k_capacity;
+    uint32_t *vals;
+    uint32_t *tile_ranges;
+    uint32_t *schedule;
+    uint32_t *bwd_index;        /* optional */
+    uint64_t *keys;             /* optional */
+    uint64_t *k_total;
+    void *workspace;            /* its own, gs_bin_sort_workspace_bytes */
+    size_t workspace_bytes;
+} gs_sort_view;
+
+/* gs_bin_sort for n_views views (host array) at once: the views go through
+ * each step of the sort together, one launch per step for up to 8 views, so
+ * views of a few million keys still fill the device.  Every view has its
+ * own buffers and workspace; the results are those of n_views gs_bin_sort
+ * calls.  Views may differ in size and resolution.
+ * Errors: as gs_bin_sort, checked for every view before anything runs. */
+gs_status gs_bin_sort_views(int32_t n_views, const gs_sort_view *views /* host */,
+                            void *stream);
+
 /* Forward compositing of every pixel.
  * Inputs: splats (gs_project), vals, tile_ranges and schedule (gs_bin_sort),
  * bg: host float[3] background colour.

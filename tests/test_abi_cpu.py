@@ -59,6 +59,23 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
     assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    # batched sort: every view is checked before anything runs
+    views = (B.GsSortView * 2)()
+    assert L.gs_bin_sort_views(-1, views, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_bin_sort_views(2, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_bin_sort_views(0, None, None) == B.GS_OK
+    for v in views:
+        v.camera = cam
+        v.n, v.k_capacity = 0, 0
+        v.tile_ranges = v.schedule = v.k_total = v.workspace = 0x1000
+        v.workspace_bytes = 1 << 20
+    views[1].k_total = None
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    views[1].k_total = 0x1000
+    views[1].n = 100
+    views[1].splats = 0x1000
+    views[1].workspace_bytes = 16
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_WORKSPACE
     bgv = (C.c_float * 3)(0.0, 0.0, 0.0)
     assert L.gs_render_bwd_screen(None, 10, None, None, None, None, None, 0, C.cast(bgv, C.c_void_p), None,
                                   None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG

@@ -223,3 +223,62 @@ def test_batched_projection_equals_per_view_calls():
         B.project(gs, cam, ref)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
+def _bins_of(buf, K):
+    """The defined parts of a view's binning outputs, as host arrays."""
+    n, cap = buf.n, buf.k_capacity
+    bi = buf.bwd_index.cpu().numpy().view(np.uint32)
+    n_vis = int(bi[cap + 2 * n + 1])
+    out = {"K": int(buf.k_total.item()), "vals": buf.vals[:K].cpu().numpy().copy(),
+           "ranges": buf.ranges.cpu().numpy().copy(), "slots": bi[:K].copy(),
+           "order": bi[cap:cap + n_vis].copy(), "off": bi[cap + n:cap + n + n_vis + 1].copy(), "n_vis": n_vis}
+    if buf.keys is not None:
+        out["keys"] = buf.keys[:K].cpu().numpy().copy()
+    sched = buf.schedule.cpu().numpy().view(np.uint32)
+    n_t = buf.ranges.shape[0]
+    assert np.array_equal(np.sort(sched[:n_t]), np.arange(n_t)) and np.all(sched[n_t:] == 0)
+    return out
+
+
+def test_batched_sort_equals_per_view_calls():
+    """gs_bin_sort_views over five views of different sizes and resolutions
+    (one of a single tile, one without Gaussians) writes what five
+    gs_bin_sort calls write, and the oracle's bins."""
+    specs = [(640, 360, 30_000), (333, 201, 20_000), (15, 9, 500), (512, 512, 25_000), (64, 64, 0)]
+    bufs, ref, Ks = [], [], []
+    for i, (w, h, n) in enumerate(specs):
+        say(f"[gpu] batched sort: view {i} {w}x{h} N={n} (per-view call)")
+        if n == 0:
+            t = scenes.tiny(seed=4, n=50, width=w, height=h)
+            sc = scenes.Scene("empty", t.means[:, :0].copy(), t.log_scales[:, :0].copy(), t.scales[:, :0].copy(),
+                              t.quats[:, :0].copy(), t.opacity_logits[:0].copy(), t.opacities[:0].copy(), 0,
+                              t.sh[:, :, :0].copy(), t.cameras)
+            buf, K = run_view(sc, 0, k_capacity=0)
+        else:
+            sc = scenes.scene_like(seed=50 + i, n=n, width=w, height=h, f=0.7 * w, n_views=1)
+            buf, K = run_view(sc, 0)
+            op = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sc.sh, sc.cameras[0])
+            compare_bins(buf, K, oracle.bin_sort(op, sc.cameras[0]), f"view {i}")
+        bufs.append(buf)
+        Ks.append(K)
+        ref.append(_bins_of(buf, K))
+        if n == 0:
+            assert K == 0 and ref[-1]["n_vis"] == 0 and list(ref[-1]["off"]) == [0]
+    for rep in range(2):
+        say(f"[gpu] batched sort: gs_bin_sort_views over {len(bufs)} views, call {rep}")
+        for b in bufs:
+            b.vals.fill_(-1)
+            b.ranges.fill_(-1)
+            b.bwd_index.fill_(-1)
+            b.schedule.fill_(-1)
+            b.k_total.fill_(-1)
+            if b.keys is not None:
+                b.keys.fill_(-1)
+        B.bin_sort_views(bufs, True)
+        torch.cuda.synchronize()
+        for i, (b, K, r) in enumerate(zip(bufs, Ks, ref)):
+            got = _bins_of(b, K)
+            for key in r:
+                assert np.array_equal(np.asarray(got[key]), np.asarray(r[key])), f"view {i}: {key} differs"
+
