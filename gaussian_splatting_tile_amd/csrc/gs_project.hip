@@ -272,10 +272,12 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     const float o = opac[g];
     const bool on = (active == nullptr || active[g] != 0) && all_finite(mx, my, mz, sx, sy, sz, qw, qx, qy, qz, o);
 
-    // the views of the batch, parameters and SH coefficients read once
+    // the views of the batch, parameters and SH coefficients read once (all
+    // lanes load, g < n; a masked-out Gaussian's coefficients go unused, and
+    // predicated loads would each wait for the previous one)
     float shc[3 * K];
 #pragma unroll
-    for (int i = 0; i < 3 * K; i++) shc[i] = on ? ld_sh(sh + (size_t)i * n + g) : 0.0f;
+    for (int i = 0; i < 3 * K; i++) shc[i] = ld_sh(sh + (size_t)i * n + g);
     for (int v = 0; v < views.count; v++) {
     const Cam &cam = views.cam[v];
     Splat *__restrict__ out = views.out[v];

@@ -300,11 +300,15 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(const Batch<PassArgs> 
 }
 
 // ---------------------------------------------------------------------------
-// Setup: counters, empty tile ranges, depth keys of the visible Gaussians.
+// Setup: counters, empty tile ranges, depth keys of the visible Gaussians
+// and, in index order, their tile rects (x0 | y0 << 16, w | h << 16), so the
+// scan after the depth sort gathers 8 bytes per Gaussian instead of a record.
 struct InitArgs {
     const Splat *splats;
     uint32_t n, n_ranges;
+    int tiles_x, tiles_y;
     uint32_t *dkeys, *dvals, *ranges, *counters;
+    uint2 *grect;
 };
 
 __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
@@ -318,10 +322,15 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
     uint32_t *__restrict__ counters = a.counters;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i < n) {
-        const float4 a = splats[i].a;
+        const float4 sa = splats[i].a;
         const uint32_t tiles = __float_as_uint(splats[i].c.w);
-        dkeys[i] = tiles ? __float_as_uint(a.z) : kSentinel;
+        dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;
         dvals[i] = i;
+        if (tiles) {
+            const Rect rc = tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x, (float)a.tiles_y);
+            a.grect[i] = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16),
+                                    (uint32_t)(rc.x1 - rc.x0) | ((uint32_t)(rc.y1 - rc.y0) << 16));
+        }
     }
     if (i < n_ranges) ranges[i] = 0;
     if (i == 0) {
@@ -332,12 +341,13 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
 }
 
 // Per depth-ordered Gaussian j (256 per block): its tile rect (x0, y0 packed,
-// width) for the duplication, and the block's sum of tiles touched.
+// width) and tile count for the duplication, and the block's sum of tiles
+// touched.
 constexpr int kScanItems = kBlock;               // Gaussians per scan / duplication block
 
 // Per-view arguments of the slot scan and the duplication.
 struct DupArgs {
-    const Splat *splats;
+    const uint2 *grect;          // tile rects by Gaussian index (bin_init)
     const uint32_t *order;       // visible Gaussians in depth order
     const uint32_t *m_ptr;       // their number
     int tiles_x, tiles_y;
@@ -354,7 +364,7 @@ struct DupArgs {
 __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
 {
     const DupArgs &a = b.v[blockIdx.y];
-    const Splat *__restrict__ splats = a.splats;
+    const uint2 *__restrict__ grect = a.grect;
     const uint32_t *__restrict__ order = a.order;
     uint2 *__restrict__ rect_info = a.rect_info;
     uint32_t *__restrict__ counts = a.counts;
@@ -364,13 +374,11 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
     if (blockIdx.x * kScanItems >= m) return;
     uint64_t c = 0;
     if (j < m) {
-        const Splat sp = splats[order[j]];
-        const Rect rc = tile_rect(sp.a.x, sp.a.y, (float)__float_as_int(sp.a.w), (float)a.tiles_x,
-                                  (float)a.tiles_y);
-        const uint32_t w = (uint32_t)(rc.x1 - rc.x0);
-        c = __float_as_uint(sp.c.w);
-        rect_info[j] = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16), w);
-        counts[j] = (uint32_t)c;
+        const uint2 r = grect[order[j]];
+        const uint32_t w = r.y & 0xFFFFu, h = r.y >> 16;
+        c = (uint64_t)(w * h);
+        rect_info[j] = make_uint2(r.x, w);
+        counts[j] = w * h;
     }
     uint64_t total;
     block_exclusive_scan(c, &total);
@@ -625,6 +633,7 @@ int bits_for(uint32_t count)
 
 struct BinWs {
     uint32_t *dk[2], *dv[2];           // depth sort ping-pong [n]
+    uint2 *grect;                      // [n] tile rect by Gaussian index
     uint2 *rect_info;                  // [n] per depth-ordered Gaussian
     uint32_t *counts;                  // [n] tiles touched, depth order
     uint64_t *block_sums;              // [ceil(n / 256)]
@@ -644,6 +653,7 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     w.dv[0] = c.take<uint32_t>(nn);
     w.dk[1] = c.take<uint32_t>(nn);
     w.dv[1] = c.take<uint32_t>(nn);
+    w.grect = c.take<uint2>(nn);
     w.rect_info = c.take<uint2>(nn);
     w.counts = c.take<uint32_t>(nn);
     w.block_sums = c.take<uint64_t>((nn + kScanItems - 1) / kScanItems);
@@ -718,7 +728,8 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         for (int v = 0; v < count; v++) {
             const SortJob &J = jobs[v];
             b.v[v] = InitArgs{J.splats, (uint32_t)J.n, 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y),
-                              w[v].dk[0], w[v].dv[0], J.ranges, w[v].counters};
+                              J.cam.tiles_x, J.cam.tiles_y, w[v].dk[0], w[v].dv[0], J.ranges, w[v].counters,
+                              w[v].grect};
         }
         bin_init<<<dim3((init_max + kBlock - 1) / kBlock, count), kBlock, 0, s>>>(b);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -755,7 +766,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             const size_t n = (size_t)J.n, cap = (size_t)J.cap;
             // backward index: [entry slot: cap][depth-ordered Gaussian: n][first slot: n + 1][visible count]
             uint32_t *bi = J.bwd_index;
-            d.v[i] = DupArgs{J.splats, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
+            d.v[i] = DupArgs{W.grect, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
                              W.rect_info, W.counts, W.block_sums, J.k_total, &W.counters[2], W.tk[0], W.gslot,
                              bi ? bi + cap : nullptr, bi ? bi + cap + n : nullptr,
                              bi ? bi + cap + 2 * n + 1 : nullptr};
