@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--views", type=int, default=8)
     ap.add_argument("--sort", choices=["batched", "per-view"], default="batched",
                     help="bin/sort all views in one gs_bin_sort_views call, or one gs_bin_sort per view")
-    ap.add_argument("--streams", type=int, default=1,
+    ap.add_argument("--streams", type=int, default=4,
                     help="HIP streams the views' sorts spread over (batched: one group of views per stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
@@ -239,11 +239,12 @@ def main():
 
     # algorithmic work of the blend per view, from the outputs: a pixel that
     # stopped examined n_contrib entries of its tile's list, otherwise all.
-    p_eval, p_need = [], []
+    p_eval, p_need, p_tile = [], [], []
     for b in bufs:
-        pe, pn = blend_pairs(torch, b)
+        pe, pn, pt = blend_pairs(torch, b)
         p_eval.append(pe)
         p_need.append(pn)
+        p_tile.append(pt)
     # one forward-blend launch covers all the step's views
     t_blend_s = per_call["render_fwd_batch"] / 1e3
     achieved = sum(p_need) * BLEND_FWD_SLOTS_PER_PAIR / t_blend_s / 1e12
@@ -278,12 +279,13 @@ def main():
         "K_per_view": Ks,
         "P_eval_per_view": p_eval,
         "P_needed_per_view": p_need,
+        "P_tile_per_view": p_tile,
         "roofline": {"kernel": "render_fwd_kernel (forward blend)", "bound": "alu",
                      "achieved": round(achieved, 3), "peak": round(VALU_PEAK_T, 2), "unit": "TFLOP/s",
                      "frac": round(achieved / VALU_PEAK_T, 4),
                      "traffic": measured_traffic() if args.workload == "scene_1m" else None,
                      "work_unit": f"{BLEND_FWD_SLOTS_PER_PAIR} fp32 VALU lane-op slots per evaluated "
-                                  f"(pixel, Gaussian) pair whose entry can reach alpha >= 1/255 in its tile "
+                                  f"(pixel, Gaussian) pair whose entry can reach alpha >= 1/255 in the pixel's 16x4 strip of its tile "
                                   f"(P_needed), summed over the {views} views of one launch; "
                                   f"peak = 256 CU x 64 lanes x 2.4 GHz"},
     }
@@ -322,7 +324,9 @@ def measured_traffic():
 
 def blend_pairs(torch, b):
     """(pairs examined under the compositing rule, pairs among them whose list
-    entry can reach alpha >= 1/255 at some pixel centre of its tile)."""
+    entry can reach alpha >= 1/255 at some pixel centre of the pixel's 16x4
+    strip of its tile (rows 4r .. 4r+3, the strip a wave's pixel r covers),
+    the same count with the whole tile instead of the strip)."""
     cam = b.cam
     TX, TY = cam.tiles_x, cam.tiles_y
     rng = b.ranges.long()
@@ -337,19 +341,36 @@ def blend_pairs(torch, b):
     u, v, a, bb, c, o = sp[:, 0], sp[:, 1], sp[:, 4], sp[:, 5], sp[:, 6], sp[:, 7]
     dxl = (tile % TX).double() * 16 + 0.5 - u
     dyl = (tile // TX).double() * 16 + 0.5 - v
+    del sp, tile
     q = lambda dx, dy: a * dx * dx + 2 * bb * dx * dy + c * dy * dy
-    best = torch.full_like(u, float("inf"))
-    for dx in (dxl, dxl + 15):
-        best = torch.minimum(best, q(dx, torch.clamp(-bb * dx / c, dyl, dyl + 15)))
-    for dy in (dyl, dyl + 15):
-        best = torch.minimum(best, q(torch.clamp(-bb * dy / a, dxl, dxl + 15), dy))
-    inside = (dxl <= 0) & (dxl + 15 >= 0) & (dyl <= 0) & (dyl + 15 >= 0)
-    best = torch.where(inside, torch.zeros_like(best), best)
-    keep = (o * torch.exp(-0.5 * best) >= (1.0 / 255.0) * (1 - 1e-3)).long()
-    ck = torch.cat([torch.zeros(1, dtype=torch.long, device=keep.device), torch.cumsum(keep, 0)])
+
+    def box_keep(dyb, h):
+        # the minimum of the quadratic form over the box of pixel centres
+        # [dxl, dxl + 15] x [dyb, dyb + h] (at the mean if inside, else on an edge)
+        best = torch.full_like(u, float("inf"))
+        for dx in (dxl, dxl + 15):
+            best = torch.minimum(best, q(dx, torch.clamp(-bb * dx / c, dyb, dyb + h)))
+        for dy in (dyb, dyb + h):
+            best = torch.minimum(best, q(torch.clamp(-bb * dy / a, dxl, dxl + 15), dy))
+        inside = (dxl <= 0) & (dxl + 15 >= 0) & (dyb <= 0) & (dyb + h >= 0)
+        best = torch.where(inside, torch.zeros_like(best), best)
+        return o * torch.exp(-0.5 * best) >= (1.0 / 255.0) * (1 - 1e-3)
+
     s_pix = start.reshape(TY, TX).repeat_interleave(16, 0).repeat_interleave(16, 1)[: cam.height, : cam.width]
-    p_need = int((ck[s_pix + examined] - ck[s_pix]).sum().item())
-    return p_eval, p_need
+    zero = torch.zeros(1, dtype=torch.long, device=u.device)
+
+    def count(keep, sel=None):
+        ck = torch.cat([zero, torch.cumsum(keep.long(), 0)])
+        d = ck[s_pix + examined] - ck[s_pix]
+        return int((d if sel is None else d * sel).sum().item())
+
+    keep_tile = box_keep(dyl, 15)
+    p_tile = count(keep_tile)
+    strip = ((torch.arange(cam.height, device=u.device) % 16) // 4)[:, None].expand(cam.height, cam.width)
+    p_need = 0
+    for r in range(4):
+        p_need += count(keep_tile & box_keep(dyl + 4 * r, 3), (strip == r).long())
+    return p_eval, p_need, p_tile
 
 
 def cpu_baseline(sc):

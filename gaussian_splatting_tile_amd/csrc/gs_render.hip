@@ -85,21 +85,24 @@ __device__ __forceinline__ void stage_record(const Splat &s, double2 &uv, double
     rgb = make_float4(s.c.x, s.c.y, s.c.z, s.b.w);
 }
 
-// Can any pixel centre of the tile whose top-left pixel is (x0, y0) reach
-// alpha >= 1/255?  The minimum of Q(d) = a dx^2 + 2 b dx dy + c dy^2 over the
-// box of pixel centres is at the mean if it lies inside, else on an edge,
-// where Q is a 1D quadratic minimised in closed form.  A record is dropped
-// only when o exp(-Q_min / 2) is below 1/255 by a relative margin of 1e-3,
-// far above the error of the per-pixel evaluation.
+// Can any pixel centre of the box of pixels [x0, x0 + w] x [y0, y0 + h]
+// (inclusive, pixel indices) reach alpha >= 1/255?  The minimum of
+// Q(d) = a dx^2 + 2 b dx dy + c dy^2 over the box of pixel centres is at the
+// mean if it lies inside, else on an edge, where Q is a 1D quadratic
+// minimised in closed form.  A record is dropped only when o exp(-Q_min / 2)
+// is below 1/255 by a relative margin of 1e-3, far above the error of the
+// per-pixel evaluation.
 // The edge minimiser is located in fp32 and clamped into the box; Q is then
 // evaluated there in fp64.  Q at any point of the box is >= its minimum, and
 // the location error only adds c * O(ulp)^2 (Q is stationary there), far
 // inside the margin.
-__device__ __forceinline__ bool may_contribute(float fu, float fv, const float4 &conic_o, int x0, int y0)
+__device__ __forceinline__ bool box_may_contribute(float fu, float fv, const float4 &conic_o, int x0, int y0, int w,
+                                                   int h)
 {
     const double a = conic_o.x, b = conic_o.y, c = conic_o.z;
+    const double W = (double)w, H = (double)h;
     const double dxl = (double)x0 + 0.5 - (double)fu, dyl = (double)y0 + 0.5 - (double)fv;
-    if (dxl <= 0.0 && dxl + 15.0 >= 0.0 && dyl <= 0.0 && dyl + 15.0 >= 0.0) return true;
+    if (dxl <= 0.0 && dxl + W >= 0.0 && dyl <= 0.0 && dyl + H >= 0.0) return true;
     const float rb_c = -conic_o.y / conic_o.z, rb_a = -conic_o.y / conic_o.x;
     const float fxl = (float)dxl, fyl = (float)dyl;
     double best = 1e300;
@@ -107,18 +110,33 @@ __device__ __forceinline__ bool may_contribute(float fu, float fv, const float4 
     for (int e = 0; e < 4; e++) {
         double dx, dy;
         if (e < 2) {                   // edges x = const: minimise over dy
-            dx = dxl + 15.0 * e;
-            dy = (double)fminf(fmaxf(rb_c * (float)dx, fyl), fyl + 15.0f);
-            dy = fmin(fmax(dy, dyl), dyl + 15.0);
+            dx = dxl + W * e;
+            dy = (double)fminf(fmaxf(rb_c * (float)dx, fyl), fyl + (float)h);
+            dy = fmin(fmax(dy, dyl), dyl + H);
         } else {                       // edges y = const: minimise over dx
-            dy = dyl + 15.0 * (e - 2);
-            dx = (double)fminf(fmaxf(rb_a * (float)dy, fxl), fxl + 15.0f);
-            dx = fmin(fmax(dx, dxl), dxl + 15.0);
+            dy = dyl + H * (e - 2);
+            dx = (double)fminf(fmaxf(rb_a * (float)dy, fxl), fxl + (float)w);
+            dx = fmin(fmax(dx, dxl), dxl + W);
         }
         best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);
     }
     const float amax = conic_o.w * __expf((float)(-0.5 * best));
     return amax >= kAlphaMin * (1.0f - 1e-3f);
+}
+
+// The strips of a tile a record can reach: bit r is set when some pixel of
+// rows 4 r .. 4 r + 3 of the tile (the rows a lane's pixel r covers across
+// the wave) may reach alpha >= 1/255; 0 when no pixel of the tile can.  A
+// wave skips pixel r of every lane for a record whose bit r is clear: exact,
+// since each of those pixels would have skipped the record.
+__device__ __forceinline__ uint32_t strip_mask(float fu, float fv, const float4 &conic_o, int x0, int y0)
+{
+    if (!box_may_contribute(fu, fv, conic_o, x0, y0, kTile - 1, kTile - 1)) return 0u;
+    uint32_t m = 0;
+#pragma unroll 1
+    for (int r = 0; r < 4; r++)
+        if (box_may_contribute(fu, fv, conic_o, x0, y0 + 4 * r, kTile - 1, 3)) m |= 1u << r;
+    return m;
 }
 
 // Per record and column: the dx terms shared by the lane's four pixels.
@@ -169,13 +187,15 @@ __device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, u
     }
 }
 
-// Stage the fetched records of one batch into LDS, dropping those that
-// cannot reach any pixel of the tile; returns the number kept, in order.
+// Stage the fetched records of one batch into LDS with their strip masks,
+// dropping those that cannot reach any pixel of the tile; returns the number
+// kept, in order.
 __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, double2 *s_uv,
-                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos)
+                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos, uint32_t *s_strips)
 {
     const int lane = threadIdx.x;
-    const bool keep = f.valid && may_contribute(f.a.x, f.a.y, f.b, x0, y0);
+    const uint32_t strips = f.valid ? strip_mask(f.a.x, f.a.y, f.b, x0, y0) : 0u;
+    const bool keep = strips != 0u;
     const uint64_t mask = __ballot(keep);
     if (keep) {
         const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -186,20 +206,22 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
         s.c = f.c;
         stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
         s_pos[slot] = f.m - start;
+        s_strips[slot] = strips;
     }
     return __popcll(mask);
 }
 
-// The backward's staging of fetched records: as stage_fetched, plus the
-// entry's duplication slot and the principal frame of its conic; a dropped
-// entry gets its nine partial sums zeroed.
+// The backward's staging of fetched records: the tile test only (per-strip
+// skipping did not pay off against the backward's per-record reduction),
+// plus the entry's duplication slot and the principal frame of its conic; a
+// dropped entry gets its nine partial sums zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
                                                  int y0, double2 *s_uv, double4 *s_q, float4 *s_rgb,
                                                  uint32_t *s_pos, uint32_t *s_slot, double4 *s_P,
                                                  float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
-    const bool keep = f.valid && may_contribute(f.a.x, f.a.y, f.b, x0, y0);
+    const bool keep = f.valid && box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1);
     if (f.valid && !keep) zero_partial(partial, entry_slot);
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -220,43 +242,6 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
     return __popcll(mask);
 }
 
-// Stage one record per lane into LDS, dropping those that cannot reach any
-// pixel of the tile; returns the number kept.  Kept records keep their order.
-template <bool kBwd>
-__device__ __forceinline__ int stage_batch(const Splat *__restrict__ splats, const uint32_t *__restrict__ vals,
-                                           const uint32_t *__restrict__ entry_slots, uint32_t b0, uint32_t end,
-                                           uint32_t start, int x0, int y0, double2 *s_uv, double4 *s_q,
-                                           float4 *s_rgb, uint32_t *s_pos, uint32_t *s_slot, double4 *s_P,
-                                           float *__restrict__ partial)
-{
-    const int lane = threadIdx.x;
-    const uint32_t m = b0 + lane;
-    bool keep = false;
-    uint32_t g = 0;
-    if (m < end) {
-        g = vals[m];
-        const float4 sa = splats[g].a;
-        keep = may_contribute(sa.x, sa.y, splats[g].b, x0, y0);
-        if (kBwd && !keep) zero_partial(partial, entry_slots[m]);
-    }
-    const uint64_t mask = __ballot(keep);
-    if (keep) {
-        const Splat s = splats[g];
-        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        const int slot = __popcll(mask & lt);
-        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
-        s_pos[slot] = m - start;
-        if (kBwd) {
-            s_slot[slot] = entry_slots[m];
-            // w' = P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex))
-            double ex, ey, l1, l2;
-            conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
-            s_P[slot] = make_double4(l1 * ex, l1 * ey, -(l2 * ey), l2 * ex);
-        }
-    }
-    return __popcll(mask);
-}
-
 // Persistent waves take work items from one queue over the views of the
 // batch: item i is view i mod V, the (i div V)-th tile of that view's
 // longest-first order, so the views' long tiles come first together and one
@@ -267,6 +252,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
     __shared__ double4 s_q[kBatch];
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
+    __shared__ uint32_t s_strips[kBatch];
 
     const int lane = threadIdx.x;
     const int n_items = batch.count * batch.max_tiles;
@@ -318,7 +304,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
         uint32_t next_g = next_valid ? vals[next_m] : 0u;
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
-            const int nb = stage_fetched(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos);
+            const int nb = stage_fetched(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos, s_strips);
             cur.m = next_m;
             cur.valid = next_valid;
             fetch_record(splats, next_g, next_valid, cur);
@@ -331,20 +317,25 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
             double4 q_n = s_q[0];
             float4 rgb_n = s_rgb[0];
             uint32_t pos_n = s_pos[0];
+            uint32_t strips_n = s_strips[0];
             for (int k = 0; k < nb; k++) {
                 const double2 uv = uv_n;
                 const double4 q = q_n;
                 const float4 rgb = rgb_n;
                 const uint32_t pos = pos_n + 1u;
+                // wave-uniform: the branches below are scalar
+                const uint32_t strips = __builtin_amdgcn_readfirstlane(strips_n);
                 const int kn = k + 1 < nb ? k + 1 : k;
                 uv_n = s_uv[kn];
                 q_n = s_q[kn];
                 rgb_n = s_rgb[kn];
                 pos_n = s_pos[kn];
+                strips_n = s_strips[kn];
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
 #pragma unroll
                 for (int r = 0; r < kPx; r++) {
+                    if (!((strips >> r) & 1u)) continue;
                     const float raw = alpha_raw(ct, q.z, dy0 - 4.0 * r);
                     const float alpha = fminf(kAlphaMax, raw);
                     const bool take = T[r] >= kTMin && raw >= kAlphaMin;
