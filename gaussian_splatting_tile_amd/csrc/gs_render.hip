@@ -312,25 +312,13 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
             next_valid = next_m < end;
             next_g = next_valid ? vals[next_m] : 0u;
             __syncthreads();
-            // the next record's LDS reads are issued before this one's math
-            double2 uv_n = s_uv[0];
-            double4 q_n = s_q[0];
-            float4 rgb_n = s_rgb[0];
-            uint32_t pos_n = s_pos[0];
-            uint32_t strips_n = s_strips[0];
             for (int k = 0; k < nb; k++) {
-                const double2 uv = uv_n;
-                const double4 q = q_n;
-                const float4 rgb = rgb_n;
-                const uint32_t pos = pos_n + 1u;
+                const double2 uv = s_uv[k];
+                const double4 q = s_q[k];
+                const float4 rgb = s_rgb[k];
+                const uint32_t pos = s_pos[k] + 1u;
                 // wave-uniform: the branches below are scalar
-                const uint32_t strips = __builtin_amdgcn_readfirstlane(strips_n);
-                const int kn = k + 1 < nb ? k + 1 : k;
-                uv_n = s_uv[kn];
-                q_n = s_q[kn];
-                rgb_n = s_rgb[kn];
-                pos_n = s_pos[kn];
-                strips_n = s_strips[kn];
+                const uint32_t strips = __builtin_amdgcn_readfirstlane(s_strips[k]);
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
 #pragma unroll
