@@ -212,7 +212,8 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
 }
 
 // The backward's staging of fetched records: the tile test only (per-strip
-// skipping did not pay off against the backward's per-record reduction),
+// skipping, by the staged strip mask or by the strips' largest n_contrib,
+// measured slower: its registers push the backward into spills),
 // plus the entry's duplication slot and the principal frame of its conic; a
 // dropped entry gets its nine partial sums zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
@@ -240,6 +241,16 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
         s_P[slot] = make_double4(l1 * ex, l1 * ey, -(l2 * ey), l2 * ex);
     }
     return __popcll(mask);
+}
+
+// Bit r set while some lane's pixel r (strip r of the tile) has not stopped.
+__device__ __forceinline__ uint32_t live_strips(const float T[4])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        if (__ballot(T[r] >= kTMin) != 0ull) m |= 1u << r;
+    return m;
 }
 
 // Persistent waves take work items from one queue over the views of the
@@ -303,7 +314,8 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
         bool next_valid = next_m < end;
         uint32_t next_g = next_valid ? vals[next_m] : 0u;
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
-            if (__all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin)) break;
+            uint32_t live = live_strips(T);
+            if (live == 0u) break;
             const int nb = stage_fetched(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos, s_strips);
             cur.m = next_m;
             cur.valid = next_valid;
@@ -317,8 +329,9 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                 const double4 q = s_q[k];
                 const float4 rgb = s_rgb[k];
                 const uint32_t pos = s_pos[k] + 1u;
-                // wave-uniform: the branches below are scalar
-                const uint32_t strips = __builtin_amdgcn_readfirstlane(s_strips[k]);
+                // wave-uniform: the branches below are scalar; a strip whose
+                // pixels have all stopped is skipped too
+                const uint32_t strips = __builtin_amdgcn_readfirstlane(s_strips[k]) & live;
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
 #pragma unroll
@@ -334,8 +347,10 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                     T[r] = T[r] - w;
                     last[r] = take ? pos : last[r];
                 }
-                if ((k & 31) == 31 && __all(T[0] < kTMin && T[1] < kTMin && T[2] < kTMin && T[3] < kTMin))
-                    break;
+                if ((k & 7) == 7) {
+                    live = live_strips(T);
+                    if (live == 0u) break;
+                }
             }
             __syncthreads();
         }
