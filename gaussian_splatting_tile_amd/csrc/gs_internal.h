@@ -198,6 +198,7 @@ struct BwdView {
 struct BwdBatch {
     int count;
     int max_tiles;
+    int view_major;               // items = views one after another (set by the launcher)
     float bg[3];
     uint32_t *queue;              // head, done: the first view's backward counters
     BwdView v[kMaxBlendViews];

@@ -483,11 +483,11 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
     const int n_items = batch.count * batch.max_tiles;
     uint32_t *head = batch.queue, *done = batch.queue + 1;
     for (int item = next_item(head, n_items); item >= 0; item = next_item(head, n_items)) {
-    const int vi = item % batch.count;
+    const int vi = batch.view_major ? item / batch.max_tiles : item % batch.count;
     const BwdView &V = batch.v[vi];
     const Cam &cam = V.cam;
     const int n_tiles = cam.tiles_x * cam.tiles_y;
-    const int rank = item / batch.count;
+    const int rank = batch.view_major ? item % batch.max_tiles : item / batch.count;
     if (rank >= n_tiles) continue;
     const int tile = (int)V.order[rank];
     const Splat *__restrict__ splats = V.splats;
@@ -665,10 +665,18 @@ hipError_t launch_render_fwd(const FwdBatch &batch, hipStream_t s)
     return hipGetLastError();
 }
 
+// The backward interleaves the views' tiles (as the forward does) while a
+// view has few tiles per resident wave, where one view's tail would idle the
+// device; with many (4K views: ~6 per wave) it runs the views one after
+// another, so the records and list entries it gathers come from one view at a
+// time and stay in the last-level cache (10M/4K: 18.5 -> 17.4 ms per 8 views;
+// at 1080p the interleaved order is 5 % faster).
 hipError_t launch_render_bwd(const BwdBatch &batch, hipStream_t s)
 {
     const int grid = resident_blocks(render_bwd_kernel, batch.count * batch.max_tiles);
-    render_bwd_kernel<<<grid, kLanes, 0, s>>>(batch);
+    BwdBatch b = batch;
+    b.view_major = batch.max_tiles >= 4 * grid ? 1 : 0;
+    render_bwd_kernel<<<grid, kLanes, 0, s>>>(b);
     return hipGetLastError();
 }
 

@@ -326,11 +326,15 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
         const uint32_t tiles = __float_as_uint(splats[i].c.w);
         dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;
         dvals[i] = i;
+        // written for every Gaussian (culled ones get an unused value): a
+        // full, coalesced row costs less than scattered partial lines
+        uint2 gr = make_uint2(0u, 0u);
         if (tiles) {
             const Rect rc = tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x, (float)a.tiles_y);
-            a.grect[i] = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16),
-                                    (uint32_t)(rc.x1 - rc.x0) | ((uint32_t)(rc.y1 - rc.y0) << 16));
+            gr = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16),
+                            (uint32_t)(rc.x1 - rc.x0) | ((uint32_t)(rc.y1 - rc.y0) << 16));
         }
+        a.grect[i] = gr;
     }
     if (i < n_ranges) ranges[i] = 0;
     if (i == 0) {

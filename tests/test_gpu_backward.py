@@ -187,3 +187,34 @@ def test_batched_backward_matches_per_view_calls():
         scale = np.abs(per_view[k]).max()
         assert np.abs(batched[k] - per_view[k]).max() <= 1e-5 * scale, k
     _compare(batched, ref, nc, "bwd batched 3 views")
+
+
+def test_batched_backward_large_views_equals_per_view_calls():
+    """Views of 2880x2048 (23040 tiles, more than 4 per resident wave of the
+    blend backward), where the batched launch runs the views one after
+    another instead of interleaving their tiles: every view's per-Gaussian
+    sums equal its single-view call's bit for bit."""
+    sc = scenes.scene_like(seed=19, n=20_000, width=2880, height=2048, f=2000.0, n_views=3)
+    say("[gpu] batched blend backward, 3 views of 2880x2048")
+    n = sc.n
+    bufs, g2s, wss, dLs, singles = [], [], [], [], []
+    for v in range(3):
+        buf, K = run_view(sc, v, with_keys=False)
+        ws = torch.empty(B.render_bwd_screen_workspace_bytes(buf.k_capacity), dtype=torch.uint8, device="cuda")
+        dL = torch.from_numpy(np.ascontiguousarray(_upstream(sc.cameras[v], 300 + v).astype(np.float32))).cuda()
+        g1 = torch.full((n, 9), float("nan"), device="cuda")
+        buf.backward_screen(dL, g1, ws)
+        torch.cuda.synchronize()
+        bufs.append(buf)
+        wss.append(ws)
+        dLs.append(dL)
+        singles.append(g1)
+        g2s.append(torch.full((n, 9), float("nan"), device="cuda"))
+    B.render_bwd_screen_views(bufs, dLs, g2s, wss)
+    torch.cuda.synchronize()
+    for b, g, g1 in zip(bufs, g2s, singles):
+        visible = b.splats[:, 3].view(torch.int32) != 0
+        assert int(visible.sum()) > 0
+        assert torch.equal(g[visible], g1[visible])
+        assert bool(torch.isnan(g[~visible]).all())
+        assert torch.all(b.schedule[b.ranges.shape[0]:] == 0)
