@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 constexpr int kSumPerRound = 7;
 constexpr int kSumRounds = 9;
 constexpr int kSumPerWave = kSumPerRound * kSumRounds;   // 63
-constexpr uint32_t kSumSmall = 16;     // slots a lane sums on its own
+constexpr uint32_t kSumSmall = 32;     // slots a lane sums on its own
 constexpr int kSumAhead = 8;           // slots per lane loaded one round ahead
 
 struct SumRound {
@@ -440,9 +440,20 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch bat
             const uint32_t bfirst = (uint32_t)__shfl((int)cur.first, src, 64);
             const uint32_t bcount = (uint32_t)__shfl((int)cur.count, src, 64);
             double part = 0.0;
-            if (cj < kSumPerRound)
-                for (uint32_t t = cj; t < bcount; t += kSumPerRound)
-                    part += (double)partial[((size_t)bfirst + t) * 9 + cq];
+            if (cj < kSumPerRound) {
+                // four rows in flight per step; the sum stays in slot order
+                uint32_t t = cj;
+                for (; t + 3 * kSumPerRound < bcount; t += 4 * kSumPerRound) {
+                    const float *row = partial + ((size_t)bfirst + t) * 9 + cq;
+                    const float r0 = row[0], r1 = row[9 * kSumPerRound], r2 = row[18 * kSumPerRound],
+                                r3 = row[27 * kSumPerRound];
+                    part += (double)r0;
+                    part += (double)r1;
+                    part += (double)r2;
+                    part += (double)r3;
+                }
+                for (; t < bcount; t += kSumPerRound) part += (double)partial[((size_t)bfirst + t) * 9 + cq];
+            }
             // lane (gl_b, q) collects component q: sum over j = 0..6 in order
             double tot = 0.0;
             for (int t = 0; t < kSumPerRound; t++) tot += __shfl(part, t * 9 + q, 64);
