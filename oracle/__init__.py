@@ -126,7 +126,10 @@ def bin_sort(proj: Dict[str, np.ndarray], cam) -> Dict[str, np.ndarray]:
     return dict(K=k, vals=vals, tile_of=tile_of, ranges=ranges.reshape(-1, 2), keys=keys)
 
 
-def render(proj, bins, cam, bg=(0.0, 0.0, 0.0), tile_mask=None, bands=None):
+def render(proj, bins, cam, bg=(0.0, 0.0, 0.0), tile_mask=None, bands=None, weight=False):
+    """Forward compositing (orc_render).  With weight=True the result also
+    holds weight[n]: per Gaussian, the sum over the rendered pixels of its
+    blending weight alpha_i T_i."""
     W, H = cam.width, cam.height
     n = proj["u"].shape[0]
     image = np.full((3, H, W), np.nan)
@@ -134,6 +137,7 @@ def render(proj, bins, cam, bg=(0.0, 0.0, 0.0), tile_mask=None, bands=None):
     n_contrib = np.full((H, W), -1, np.int32)
     events = np.zeros((H, W), np.int32)
     capflag = np.zeros((H, W), np.uint8)
+    w = np.zeros(n, np.float64) if weight else None
     bgv = np.asarray(bg, dtype=np.float64)
     tm = None if tile_mask is None else np.ascontiguousarray(tile_mask, dtype=np.uint8)
     b = bands_struct(**(bands or {}))
@@ -144,9 +148,12 @@ def render(proj, bins, cam, bg=(0.0, 0.0, 0.0), tile_mask=None, bands=None):
     p_eval = lib().orc_render(C.byref(c), _p(arr["u"]), _p(arr["v"]), _p(arr["conic"]),
                               _p(arr["opacity"]), _p(arr["rgb"]), C.c_int64(n), _p(vals),
                               _p(ranges), _p(bgv), _p(tm), C.byref(b), _p(image), _p(final_T),
-                              _p(n_contrib), _p(events), _p(capflag))
-    return dict(image=image, final_T=final_T, n_contrib=n_contrib, events=events,
-                capflag=capflag, p_eval=int(p_eval))
+                              _p(n_contrib), _p(events), _p(capflag), _p(w))
+    out = dict(image=image, final_T=final_T, n_contrib=n_contrib, events=events,
+               capflag=capflag, p_eval=int(p_eval))
+    if weight:
+        out["weight"] = w
+    return out
 
 
 def render_pixel(proj, bins, cam, px, py, flips=0, bg=(0.0, 0.0, 0.0), bands=None):

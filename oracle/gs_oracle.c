@@ -184,7 +184,7 @@ static void composite(const double *u, const double *v, const double *conic,
                       const uint32_t *vals, uint32_t start, uint32_t end,
                       const double *bg, const orc_bands *bands, double px,
                       double py, uint32_t flips, double out_c[3], double *out_T,
-                      int32_t *out_n, pix_stats *st)
+                      int32_t *out_n, pix_stats *st, double *weight)
 {
     const double a_thr = 1.0 / 255.0, t_thr = 1e-4, cap = 0.99;
     double T = 1.0, C[3] = {0.0, 0.0, 0.0};
@@ -219,6 +219,10 @@ static void composite(const double *u, const double *v, const double *conic,
         if (skip) continue;
         if (fabs(raw - cap) <= bands->cap * cap) st->capflag = 1;
         for (int ch = 0; ch < 3; ch++) C[ch] += alpha * T * rgb[ch * n + g];
+        if (weight) {
+#pragma omp atomic
+            weight[g] += alpha * T;
+        }
         T = T * (1.0 - alpha);
         stop_held = 0;
         last = (int32_t)(m - start + 1);
@@ -235,7 +239,8 @@ int64_t orc_render(const orc_cam *cam, const double *u, const double *v,
                    int64_t n, const uint32_t *vals, const uint32_t *ranges,
                    const double *bg, const uint8_t *tile_mask,
                    const orc_bands *bands, double *image, double *final_T,
-                   int32_t *n_contrib, int32_t *events, uint8_t *capflag)
+                   int32_t *n_contrib, int32_t *events, uint8_t *capflag,
+                   double *weight)
 {
     const int W = cam->width, H = cam->height;
     const int TX = (W + 15) / 16, TY = (H + 15) / 16;
@@ -252,7 +257,7 @@ int64_t orc_render(const orc_cam *cam, const double *u, const double *v,
                 pix_stats st;
                 composite(u, v, conic, opac, rgb, n, vals, ranges[2 * t],
                           ranges[2 * t + 1], bg, bands, i + 0.5, j + 0.5, 0u, c,
-                          &T, &nc, &st);
+                          &T, &nc, &st, weight);
                 const int64_t p = (int64_t)j * W + i;
                 for (int ch = 0; ch < 3; ch++) image[ch * HW + p] = c[ch];
                 final_T[p] = T;
@@ -276,7 +281,7 @@ int orc_render_pixel(const orc_cam *cam, const double *u, const double *v,
     const int t = (py / 16) * TX + px / 16;
     pix_stats st;
     composite(u, v, conic, opac, rgb, n, vals, ranges[2 * t], ranges[2 * t + 1],
-              bg, bands, px + 0.5, py + 0.5, flips, out_rgb, out_T, out_n, &st);
+              bg, bands, px + 0.5, py + 0.5, flips, out_rgb, out_T, out_n, &st, NULL);
     return st.events;
 }
 

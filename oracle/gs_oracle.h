@@ -81,13 +81,21 @@ typedef struct orc_bands { double alpha, trans, cap, clamp; } orc_bands;
  * all).  Outputs are [3][H][W], [H][W], [H][W]; events[H][W] counts the
  * near-threshold alpha-skip and stop decisions; capflag[H][W] marks pixels
  * whose composited set holds an alpha within the band of the 0.99 cap.
+ * weight[n] (NULL to skip) receives += for every composited entry its
+ * blending weight alpha_i T_i: the share of the pixel's colour that the
+ * Gaussian supplies.  Summed over a view's pixels (and by the caller over
+ * views) this is the per-Gaussian visibility weight that the BlitzGS page's
+ * section 2.2 scores Gaussians by (reading: the page names a cross-view
+ * visibility weight and gives no formula; the sum of blending weights is
+ * the plainest one).
  * Returns the number of list entries examined (P_eval). */
 int64_t orc_render(const orc_cam *cam, const double *u, const double *v,
                    const double *conic, const double *opac, const double *rgb,
                    int64_t n, const uint32_t *vals, const uint32_t *ranges,
                    const double *bg, const uint8_t *tile_mask,
                    const orc_bands *bands, double *image, double *final_T,
-                   int32_t *n_contrib, int32_t *events, uint8_t *capflag);
+                   int32_t *n_contrib, int32_t *events, uint8_t *capflag,
+                   double *weight);
 
 /* One pixel with the k-th near-threshold decision (in encounter order) taken
  * the other way when bit k of flips is set. */

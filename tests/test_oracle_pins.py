@@ -361,6 +361,9 @@ def test_single_isotropic_gaussian_analytic_image():
     np.testing.assert_allclose(out["image"], rgb[:, None, None] * alpha[None], atol=1e-14)
     np.testing.assert_allclose(out["final_T"], 1 - alpha, atol=1e-14)
     assert np.array_equal(out["n_contrib"], (alpha > 0).astype(np.int32))
+    # alone, the Gaussian's blending weight at each pixel is its alpha (T = 1)
+    w = oracle.render(p, b, cam, weight=True)["weight"]
+    np.testing.assert_allclose(w[0], alpha.sum(), rtol=1e-13)
 
 
 def _occluder_scene(n_occ, n_content=30, seed=5):
@@ -458,6 +461,34 @@ def test_partition_of_unity_and_background():
     out0 = oracle.render(p0, b, cam, bg=bg)
     np.testing.assert_allclose(out0["image"], np.asarray(bg)[:, None, None] * out0["final_T"][None],
                                atol=1e-15)
+
+
+def test_blend_weights_sum_to_coverage_and_colour():
+    """Per pixel the blending weights alpha_i T_i telescope to 1 - T_final,
+    and the pixel's colour (bg = 0) is sum_i alpha_i T_i rgb_i.  Summed over
+    the image: sum_g weight_g = sum_p (1 - T_final(p)) and
+    sum_p image_c(p) = sum_g weight_g rgb_g,c; with random colours the second
+    holds only if each Gaussian gets its own weight.  Culled Gaussians get 0,
+    and a permutation of the indices permutes the weights."""
+    sc = scenes.config(1, n_override=600)
+    cam = sc.cameras[0]
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 0, sc.sh, cam)
+    b = oracle.bin_sort(p, cam)
+    out = oracle.render(p, b, cam, weight=True)
+    w = out["weight"]
+    assert np.all(w >= 0.0) and np.all(w[p["radius"] == 0] == 0.0) and np.count_nonzero(w) > 100
+    np.testing.assert_allclose(w.sum(), (1.0 - out["final_T"]).sum(), rtol=1e-12)
+    rgb = np.random.default_rng(11).uniform(0.0, 1.0, p["rgb"].shape)
+    pc = dict(p)
+    pc["rgb"] = rgb
+    outc = oracle.render(pc, b, cam, weight=True)
+    np.testing.assert_allclose(outc["weight"], w, rtol=1e-13)   # colours do not move the weights
+    np.testing.assert_allclose(outc["image"].sum(axis=(1, 2)), rgb @ w, rtol=1e-12)
+    perm = np.random.default_rng(12).permutation(sc.n)
+    pp = oracle.project(sc.means[:, perm], sc.scales[:, perm], sc.quats[:, perm], sc.opacities[perm], 0,
+                        sc.sh[:, :, perm], cam)
+    wp = oracle.render(pp, oracle.bin_sort(pp, cam), cam, weight=True)["weight"]
+    np.testing.assert_allclose(wp, w[perm], rtol=1e-12, atol=0.0)
 
 
 def test_order_invariance_under_index_permutation():
