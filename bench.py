@@ -50,6 +50,8 @@ def parse():
                     help="HIP streams the views' sorts spread over (batched: one group of views per stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--weights", action="store_true",
+                    help="the forward blend also accumulates per-Gaussian blending weights (one array for all views)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for "
                          "calibrating the HBM byte counters of a profiler run)")
@@ -150,6 +152,7 @@ def main():
                  sh=torch.zeros((K_sh, 3, sc.n), device=dev))
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
+    wts = torch.zeros(sc.n, dtype=torch.float32, device=dev) if args.weights else None
 
     names = ("active_mask", "project_batch", "bin_sort", "bin_sort_batch", "render_fwd_batch",
              "render_bwd_batch", "project_bwd_batch")
@@ -206,7 +209,9 @@ def main():
             joined.record(st)
             stream.wait_event(joined)
         # the 8 views' blends share one work queue
-        timed("render_fwd_batch", lambda: B.render_fwd_views(bufs, bg, stream))
+        if wts is not None:
+            wts.zero_()
+        timed("render_fwd_batch", lambda: B.render_fwd_views(bufs, bg, stream, weights=wts))
         e_fwd1.record(stream)
         if do_bwd:
             # the screen-space backward of all views in one launch (plus the
@@ -272,6 +277,7 @@ def main():
                            "batched project, " +
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
                            ", batched blend fwd of all views" +
+                           (" with per-Gaussian blending weights" if args.weights else "") +
                            (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,

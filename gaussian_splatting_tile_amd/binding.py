@@ -29,7 +29,7 @@ class GsCamera(C.Structure):
 class GsFwdView(C.Structure):
     _fields_ = [("camera", GsCamera), ("splats", C.c_void_p), ("vals", C.c_void_p),
                 ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("image", C.c_void_p),
-                ("final_T", C.c_void_p), ("n_contrib", C.c_void_p)]
+                ("final_T", C.c_void_p), ("n_contrib", C.c_void_p), ("weight", C.c_void_p)]
 
 
 class GsSortView(C.Structure):
@@ -232,14 +232,18 @@ def project_views(gs: GsGaussians, cams, splats_list, stream=None):
     _check(lib().gs_project_views(C.byref(gs), nv, cam_arr, sp_arr, _stream(stream)), "gs_project_views")
 
 
-def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None):
+def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None, weights=None):
     """gs_render_fwd_views over ViewBuffers objects (their splats, bins and
-    schedules must be current)."""
+    schedules must be current).  weights: None, one float32 [n] tensor shared
+    by all views, or a list with one tensor (or None) per view; the
+    per-Gaussian blending weights are added to it."""
     nv = len(bufs)
+    if weights is None or isinstance(weights, torch.Tensor):
+        weights = [weights] * nv
     arr = (GsFwdView * max(nv, 1))()
     for i, b in enumerate(bufs):
         arr[i] = GsFwdView(b.camc, _ptr(b.splats), _ptr(b.vals), _ptr(b.ranges), _ptr(b.schedule),
-                           _ptr(b.image), _ptr(b.final_T), _ptr(b.n_contrib))
+                           _ptr(b.image), _ptr(b.final_T), _ptr(b.n_contrib), _ptr(weights[i]))
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     _check(lib().gs_render_fwd_views(nv, arr, C.cast(bgv, C.c_void_p), _stream(stream)), "gs_render_fwd_views")
 

@@ -207,6 +207,7 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
     b.v[0].image = image;
     b.v[0].final_T = final_T;
     b.v[0].n_contrib = n_contrib;
+    b.v[0].weight = nullptr;
     return from_hip(launch_render_fwd(b, (hipStream_t)stream));
 }
 
@@ -238,6 +239,7 @@ gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views, const f
             d.image = w.image;
             d.final_T = w.final_T;
             d.n_contrib = w.n_contrib;
+            d.weight = w.weight;
             const int nt = d.cam.tiles_x * d.cam.tiles_y;
             if (nt > b.max_tiles) b.max_tiles = nt;
         }

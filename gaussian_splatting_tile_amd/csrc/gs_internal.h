@@ -173,6 +173,7 @@ struct FwdView {
     float *image;
     float *final_T;
     uint32_t *n_contrib;
+    float *weight;                // optional: += per-Gaussian blending weights
 };
 struct FwdBatch {
     int count;

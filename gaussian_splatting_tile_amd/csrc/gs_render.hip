@@ -174,12 +174,14 @@ __device__ __forceinline__ void zero_partial(float *__restrict__ partial, uint32
 // pipelining of the blend's global gathers across batches).
 struct Fetched {
     uint32_t m;          // list position
+    uint32_t g;          // Gaussian
     bool valid;
     float4 a, b, c;
 };
 
 __device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, uint32_t g, bool valid, Fetched &f)
 {
+    f.g = g;
     if (valid) {
         f.a = splats[g].a;
         f.b = splats[g].b;
@@ -187,11 +189,13 @@ __device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, u
     }
 }
 
-// Stage the fetched records of one batch into LDS with their strip masks,
-// dropping those that cannot reach any pixel of the tile; returns the number
-// kept, in order.
+// Stage the fetched records of one batch into LDS with their strip masks
+// (and, with kWeight, their Gaussians), dropping those that cannot reach any
+// pixel of the tile; returns the number kept, in order.
+template <bool kWeight>
 __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, double2 *s_uv,
-                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos, uint32_t *s_strips)
+                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos, uint32_t *s_strips,
+                                             uint32_t *s_g)
 {
     const int lane = threadIdx.x;
     const uint32_t strips = f.valid ? strip_mask(f.a.x, f.a.y, f.b, x0, y0) : 0u;
@@ -207,6 +211,7 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
         stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
         s_pos[slot] = f.m - start;
         s_strips[slot] = strips;
+        if (kWeight) s_g[slot] = f.g;
     }
     return __popcll(mask);
 }
@@ -243,6 +248,48 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
     return __popcll(mask);
 }
 
+// (every control used here reads a valid lane; old = 0 with bound_ctrl lets
+// the compiler fold the move into the add that consumes it)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    const int iv = __float_as_int(v);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, kCtrl, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8 (lane i <- (i + 8) mod 16)
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror (lane i <- 7 - i within 8)
+
+// Split exchange across lanes i and i ^ 32 (i ^ 16): lanes of the lower half
+// (even rows) return a[i] + a[partner], lanes of the upper half (odd rows)
+// b[i] + b[partner].  v_permlane32_swap / v_permlane16_swap swap the upper
+// half of the first operand with the lower half of the second, so the sum of
+// the two results is exactly that.
+__device__ __forceinline__ float xchg32(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xchg16(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of one value over the wave, in every lane: quad, 8-lane and 16-lane
+// steps on DPP moves folded into the adds, then the 32- and 64-lane steps on
+// lane swaps.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppRowRor8>(v);
+    v = xchg16(v, v);
+    return xchg32(v, v);
+}
+
 // Bit r set while some lane's pixel r (strip r of the tile) has not stopped.
 __device__ __forceinline__ uint32_t live_strips(const float T[4])
 {
@@ -257,6 +304,10 @@ __device__ __forceinline__ uint32_t live_strips(const float T[4])
 // batch: item i is view i mod V, the (i div V)-th tile of that view's
 // longest-first order, so the views' long tiles come first together and one
 // view's tail overlaps the others' work.
+// With kWeight, each record's blending weights over the wave's pixels are
+// summed across the wave and added to its Gaussian's entry of the view's
+// weight array (views without one skip it).
+template <bool kWeight>
 __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch)
 {
     __shared__ double2 s_uv[kBatch];
@@ -264,6 +315,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
     __shared__ uint32_t s_strips[kBatch];
+    __shared__ uint32_t s_g[kWeight ? kBatch : 1];
 
     const int lane = threadIdx.x;
     const int n_items = batch.count * batch.max_tiles;
@@ -316,7 +368,8 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             uint32_t live = live_strips(T);
             if (live == 0u) break;
-            const int nb = stage_fetched(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos, s_strips);
+            const int nb = stage_fetched<kWeight>(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos,
+                                                  s_strips, s_g);
             cur.m = next_m;
             cur.valid = next_valid;
             fetch_record(splats, next_g, next_valid, cur);
@@ -334,6 +387,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                 const uint32_t strips = __builtin_amdgcn_readfirstlane(s_strips[k]) & live;
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
+                float wsum = 0.0f;
 #pragma unroll
                 for (int r = 0; r < kPx; r++) {
                     if (!((strips >> r) & 1u)) continue;
@@ -346,6 +400,11 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                     c2[r] = fmaf(rgb.z, w, c2[r]);
                     T[r] = T[r] - w;
                     last[r] = take ? pos : last[r];
+                    if (kWeight) wsum += w;
+                }
+                if (kWeight && V.weight != nullptr && __ballot(wsum > 0.0f) != 0ull) {
+                    wsum = wave_sum(wsum);
+                    if (lane == 0) atomicAdd(V.weight + s_g[k], wsum);
                 }
                 if ((k & 7) == 7) {
                     live = live_strips(T);
@@ -397,35 +456,6 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
 // duplication slot, partial[slot][9]: every (Gaussian, tile) pair owns one
 // slot, the slots of a Gaussian are contiguous, and the projection backward
 // sums them.  No atomics, so the gradients are bit-reproducible.
-
-// (every control used here reads a valid lane; old = 0 with bound_ctrl lets
-// the compiler fold the move into the add that consumes it)
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    const int iv = __float_as_int(v);
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, kCtrl, 0xF, 0xF, true));
-}
-constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kDppRowRor8 = 0x128;     // row_ror:8 (lane i <- (i + 8) mod 16)
-constexpr int kDppHalfMirror = 0x141;  // row_half_mirror (lane i <- 7 - i within 8)
-
-// Split exchange across lanes i and i ^ 32 (i ^ 16): lanes of the lower half
-// (even rows) return a[i] + a[partner], lanes of the upper half (odd rows)
-// b[i] + b[partner].  v_permlane32_swap / v_permlane16_swap swap the upper
-// half of the first operand with the lower half of the second, so the sum of
-// the two results is exactly that.
-__device__ __forceinline__ float xchg32(float a, float b)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xchg16(float a, float b)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Wave sums of v[0..8] by a split butterfly: each exchange halves the values
 // a lane carries (9 -> 5 -> 3 -> 2 -> 1), then two plain steps finish.
@@ -660,8 +690,15 @@ int resident_blocks(K kernel, int n_tiles)
 
 hipError_t launch_render_fwd(const FwdBatch &batch, hipStream_t s)
 {
-    const int grid = resident_blocks(render_fwd_kernel, batch.count * batch.max_tiles);
-    render_fwd_kernel<<<grid, kLanes, 0, s>>>(batch);
+    bool weights = false;
+    for (int i = 0; i < batch.count; i++) weights = weights || batch.v[i].weight != nullptr;
+    if (weights) {
+        const int grid = resident_blocks(render_fwd_kernel<true>, batch.count * batch.max_tiles);
+        render_fwd_kernel<true><<<grid, kLanes, 0, s>>>(batch);
+    } else {
+        const int grid = resident_blocks(render_fwd_kernel<false>, batch.count * batch.max_tiles);
+        render_fwd_kernel<false><<<grid, kLanes, 0, s>>>(batch);
+    }
     return hipGetLastError();
 }
 

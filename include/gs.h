@@ -237,7 +237,14 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
                         float *image, float *final_T, uint32_t *n_contrib,
                         void *stream);
 
-/* One view's arguments of gs_render_fwd, for gs_render_fwd_views. */
+/* One view's arguments of gs_render_fwd, for gs_render_fwd_views.
+ * weight (optional, NULL to skip): float[n] indexed by Gaussian, to which
+ * the call adds, for every Gaussian the view composites, the sum over the
+ * view's pixels of its blending weight alpha_i T_i (the share of the pixel's
+ * colour it supplies; summed over views, the per-Gaussian visibility weight
+ * of the BlitzGS page's section 2.2).  Several views may share one array.
+ * The additions are fp32 atomics in an unspecified order, so results agree
+ * with a sequential sum to fp32 rounding. */
 typedef struct gs_fwd_view {
     gs_camera camera;
     const gs_splat *splats;
@@ -247,14 +254,16 @@ typedef struct gs_fwd_view {
     float *image;
     float *final_T;
     uint32_t *n_contrib;
+    float *weight;
 } gs_fwd_view;
 
 /* gs_render_fwd of n_views views (host array) with one background colour,
  * up to 8 views per launch: the views' tiles form one work queue (each
  * view's longest tiles first, the views interleaved), so one view's last
  * long tiles overlap the others' work instead of idling the device.  The
- * outputs are those of n_views gs_render_fwd calls.  A launch uses the
- * forward queue counters of its first view's schedule.
+ * outputs are those of n_views gs_render_fwd calls, plus the optional
+ * blending weights.  A launch uses the forward queue counters of its first
+ * view's schedule.
  * Errors: GS_ERR_INVALID_ARG. */
 gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views,
                               const float *bg /* host [3] */, void *stream);

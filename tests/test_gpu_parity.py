@@ -282,3 +282,65 @@ def test_batched_sort_equals_per_view_calls():
             for key in r:
                 assert np.array_equal(np.asarray(got[key]), np.asarray(r[key])), f"view {i}: {key} differs"
 
+
+
+def _ambiguous_gaussians(ob, oo, cam):
+    """Gaussians listed in a tile that holds a pixel with a near-threshold
+    decision (or an alpha near the cap): their weights may legitimately
+    differ between two correct forwards."""
+    amb = (oo["events"] > 0) | (oo["capflag"] > 0)
+    ty, tx = np.nonzero(amb)
+    tiles = np.unique((ty // 16) * cam.tiles_x + tx // 16)
+    out = np.zeros(0, np.int64)
+    for t in tiles:
+        s, e = ob["ranges"][t]
+        out = np.concatenate([out, ob["vals"][s:e].astype(np.int64)])
+    return np.unique(out)
+
+
+def _compare_weights(gpu, ref, skip, name):
+    keep = np.ones(ref.shape[0], bool)
+    keep[skip] = False
+    err = np.abs(gpu - ref)
+    tol = 1e-4 * np.abs(ref) + 1e-6 * np.abs(ref).max()
+    bad = int(np.count_nonzero((err > tol) & keep))
+    say(f"[gpu] {name}: compared {int(keep.sum())} of {ref.shape[0]} Gaussians, "
+        f"max rel err {float((err[keep] / np.maximum(np.abs(ref[keep]), 1e-30)).max()):.2e}, bad {bad}")
+    assert bad == 0
+    assert np.all(gpu[ref == 0.0] == 0.0)             # culled or never composited: nothing added
+
+
+def test_blend_weights_match_oracle():
+    """The per-Gaussian blending weights of gs_render_fwd_views (sum over the
+    view's pixels of alpha_i T_i) against the oracle's: one 720p view, then
+    three views of another scene adding into one shared array."""
+    sc = scenes.config(2)
+    say("[gpu] blend weights: box_100k view 0")
+    buf, K = run_view(sc, 0)
+    op, ob, oo = _oracle_fwd(sc, 0)
+    ref = oracle.render(op, ob, sc.cameras[0], weight=True)["weight"]
+    w = torch.zeros(sc.n, dtype=torch.float32, device="cuda")
+    B.render_fwd_views([buf], (0.0, 0.0, 0.0), weights=w)
+    torch.cuda.synchronize()
+    _compare_weights(w.cpu().numpy().astype(np.float64), ref, _ambiguous_gaussians(ob, oo, sc.cameras[0]),
+                     "weights box_100k")
+
+    sc = scenes.scene_like(seed=61, n=30_000, width=480, height=272, f=350.0, n_views=3)
+    say("[gpu] blend weights: 3 views into one array")
+    bufs, ref, skip = [], np.zeros(sc.n), []
+    for v in range(3):
+        b, K = run_view(sc, v)
+        bufs.append(b)
+        op, ob, oo = _oracle_fwd(sc, v)
+        ref += oracle.render(op, ob, sc.cameras[v], weight=True)["weight"]
+        skip.append(_ambiguous_gaussians(ob, oo, sc.cameras[v]))
+    w = torch.zeros(sc.n, dtype=torch.float32, device="cuda")
+    B.render_fwd_views(bufs, (0.0, 0.0, 0.0), weights=w)
+    torch.cuda.synchronize()
+    _compare_weights(w.cpu().numpy().astype(np.float64), ref, np.concatenate(skip), "weights 3 views")
+    # the images are those of the forward without weights
+    img = [b.image.clone() for b in bufs]
+    B.render_fwd_views(bufs, (0.0, 0.0, 0.0))
+    torch.cuda.synchronize()
+    for b, i0 in zip(bufs, img):
+        assert torch.equal(b.image, i0)
