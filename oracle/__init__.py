@@ -217,6 +217,28 @@ def topk_mask(scores, k):
     return m
 
 
+def sh_quantize8(sh):
+    """8-bit block quantization of SH [K][3][n] (orc_sh_quantize8): codes
+    u8 [K][3][n] and bounds f32 [K*3][ceil(n/256)][2]."""
+    x = np.ascontiguousarray(sh, dtype=np.float32)
+    K, C3, n = x.shape
+    nb = (n + 255) // 256
+    q = np.zeros(x.shape, np.uint8)
+    bounds = np.zeros((K * C3, nb, 2), np.float32)
+    lib().orc_sh_quantize8(C.c_int64(n), C.c_int(K * C3), _p(x), _p(q), _p(bounds))
+    return q, bounds
+
+
+def sh_dequantize8(q, bounds):
+    """Decode of sh_quantize8's codes to f32 [K][3][n]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    b = np.ascontiguousarray(bounds, dtype=np.float32)
+    K, C3, n = q.shape
+    x = np.zeros(q.shape, np.float32)
+    lib().orc_sh_dequantize8(C.c_int64(n), C.c_int(K * C3), _p(q), _p(b), _p(x))
+    return x
+
+
 def sh_basis(d):
     d = np.ascontiguousarray(d, dtype=np.float64)
     Y = np.zeros(16)

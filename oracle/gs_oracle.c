@@ -586,3 +586,43 @@ void orc_topk_mask(int64_t n, const float *scores, int64_t k, uint8_t *mask)
     for (int64_t i = 0; i < k && i < n; i++) mask[e[i].g] = 1;
     free(e);
 }
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit block quantization of SH rows (see gs_oracle.h for the readings).   */
+void orc_sh_quantize8(int64_t n, int rows, const float *x, uint8_t *q, float *bounds)
+{
+    const int64_t nb = (n + 255) / 256;
+    for (int r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const int64_t g0 = b * 256, g1 = g0 + 256 < n ? g0 + 256 : n;
+            const float *row = x + (int64_t)r * n;
+            float lo = row[g0], hi = row[g0];
+            for (int64_t g = g0 + 1; g < g1; g++) {
+                if (row[g] < lo) lo = row[g];
+                if (row[g] > hi) hi = row[g];
+            }
+            bounds[((int64_t)r * nb + b) * 2] = lo;
+            bounds[((int64_t)r * nb + b) * 2 + 1] = hi;
+            const float d = hi - lo;
+            for (int64_t g = g0; g < g1; g++) {
+                uint8_t c = 0;
+                if (d > 0.0f) {
+                    const float t = ((row[g] - lo) * 255.0f) / d;
+                    const float f = floorf(t + 0.5f);
+                    c = f >= 255.0f ? (uint8_t)255 : (uint8_t)f;
+                }
+                q[(int64_t)r * n + g] = c;
+            }
+        }
+}
+
+void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *bounds, float *x)
+{
+    const int64_t nb = (n + 255) / 256;
+    for (int r = 0; r < rows; r++)
+        for (int64_t g = 0; g < n; g++) {
+            const float lo = bounds[((int64_t)r * nb + g / 256) * 2];
+            const float hi = bounds[((int64_t)r * nb + g / 256) * 2 + 1];
+            x[(int64_t)r * n + g] = lo + ((hi - lo) * (float)q[(int64_t)r * n + g]) / 255.0f;
+        }
+}

@@ -131,6 +131,19 @@ void orc_project_bwd(int64_t n, const double *means, const double *scales,
 /* Importance mask: keep the k highest scores, ties to the lower index. */
 void orc_topk_mask(int64_t n, const float *scores, int64_t k, uint8_t *mask);
 
+/* 8-bit linear block quantization of SH storage (the Spirula Studio page,
+ * its section on what each bit width holds and its description of the
+ * block-wise min/max bounds): the coefficients are rows [rows][n] (row =
+ * coefficient x channel, n Gaussians); every block of 256 consecutive
+ * Gaussians of a row shares one (lo, hi) pair, the block's minimum and
+ * maximum, bounds[rows][ceil(n / 256)][2].  Readings (the page gives the
+ * decode formula and the block size, not the rounding): a value x becomes
+ *   q = min(255, floor(((x - lo) * 255) / (hi - lo) + 1/2)),  q = 0 if hi == lo,
+ * and decodes to  lo + ((hi - lo) * q) / 255,  every step one fp32 IEEE
+ * operation in that order. */
+void orc_sh_quantize8(int64_t n, int rows, const float *x, uint8_t *q, float *bounds);
+void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *bounds, float *x);
+
 /* Real spherical-harmonic basis (degree <= 3) at unit direction d, and its
  * gradient with respect to the three components of d. */
 void orc_sh_basis(const double *d, double *Y /*[16]*/, double *dY /*[16][3]*/);

@@ -671,3 +671,42 @@ def test_lod_gate_brute_force():
     vis_off = p_off["radius"] > 0
     assert np.array_equal((p_on["radius"] > 0)[clear], (vis_off & keep)[clear])
     assert 0.2 < keep[vis_off].mean() < 0.95
+
+
+def test_sh_quantize8_bounds_round_trip_and_extremes():
+    """8-bit block quantization of SH rows: each block of 256 Gaussians of a
+    row keeps its exact min and max as bounds, the min codes to 0 and the max
+    to 255, codes are monotone in the value, a constant block decodes
+    exactly, and every decoded value lies within half a step, (hi - lo) / 510,
+    of its source (plus fp32 rounding of the decode)."""
+    rng = np.random.default_rng(21)
+    for n in (1, 255, 256, 257, 1000):
+        sh = rng.normal(0.0, 0.2, (16, 3, n)).astype(np.float32)
+        sh[0] = rng.uniform(-1.0, 1.0, (3, n)).astype(np.float32)
+        if n >= 256:
+            sh[5, 1, :256] = np.float32(0.375)                       # a constant block
+        q, b = oracle.sh_quantize8(sh)
+        x = oracle.sh_dequantize8(q, b)
+        rows = sh.reshape(48, n)
+        qr = q.reshape(48, n)
+        nb = (n + 255) // 256
+        assert b.shape == (48, nb, 2)
+        for r in range(48):
+            for blk in range(nb):
+                seg = rows[r, blk * 256:(blk + 1) * 256]
+                cs = qr[r, blk * 256:(blk + 1) * 256]
+                lo, hi = b[r, blk]
+                assert lo == seg.min() and hi == seg.max()
+                if hi > lo:
+                    assert cs[np.argmin(seg)] == 0 and cs[np.argmax(seg)] == 255
+                    o = np.argsort(seg, kind="stable")
+                    assert np.all(np.diff(cs[o].astype(int)) >= 0)
+                else:
+                    assert np.all(cs == 0)
+        lo_g = np.repeat(b[:, :, 0], 256, axis=1)[:, :n].reshape(16, 3, n)
+        hi_g = np.repeat(b[:, :, 1], 256, axis=1)[:, :n].reshape(16, 3, n)
+        step = (hi_g.astype(np.float64) - lo_g) / 255.0
+        err = np.abs(x.astype(np.float64) - sh)
+        assert np.all(err <= 0.5 * step * (1 + 1e-5) + 4e-7 * np.maximum(np.abs(lo_g), np.abs(hi_g)))
+        if n >= 256:
+            assert np.all(x[5, 1, :256] == np.float32(0.375))
