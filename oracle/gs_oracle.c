@@ -623,6 +623,7 @@ void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *boun
         for (int64_t g = 0; g < n; g++) {
             const float lo = bounds[((int64_t)r * nb + g / 256) * 2];
             const float hi = bounds[((int64_t)r * nb + g / 256) * 2 + 1];
-            x[(int64_t)r * n + g] = lo + ((hi - lo) * (float)q[(int64_t)r * n + g]) / 255.0f;
+            const float step = (hi - lo) * (1.0f / 255.0f);
+            x[(int64_t)r * n + g] = lo + (float)q[(int64_t)r * n + g] * step;
         }
 }

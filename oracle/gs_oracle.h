@@ -139,8 +139,9 @@ void orc_topk_mask(int64_t n, const float *scores, int64_t k, uint8_t *mask);
  * maximum, bounds[rows][ceil(n / 256)][2].  Readings (the page gives the
  * decode formula and the block size, not the rounding): a value x becomes
  *   q = min(255, floor(((x - lo) * 255) / (hi - lo) + 1/2)),  q = 0 if hi == lo,
- * and decodes to  lo + ((hi - lo) * q) / 255,  every step one fp32 IEEE
- * operation in that order. */
+ * and decodes to  lo + q * step,  step = (hi - lo) * fp32(1/255) (the page's
+ * decode is one multiplication per value once the block's step is known),
+ * every step one fp32 IEEE operation in that order. */
 void orc_sh_quantize8(int64_t n, int rows, const float *x, uint8_t *q, float *bounds);
 void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *bounds, float *x);
 
