@@ -50,6 +50,8 @@ def parse():
                     help="HIP streams the views' sorts spread over (batched: one group of views per stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--sh-q8", action="store_true",
+                    help="store SH as 8-bit codes with per-256-Gaussian bounds (quantized from the fp32 source)")
     ap.add_argument("--weights", action="store_true",
                     help="the forward blend also accumulates per-Gaussian blending weights (one array for all views)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -118,6 +120,15 @@ def main():
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities),
              sh=f(sc.sh_fp16 if sc.sh_fp16 is not None else sc.sh))
+    if args.sh_q8:
+        # 8-bit block-quantized SH storage, encoded on the GPU from the fp32 source
+        src = f(sc.sh)
+        K_, c3_, n_ = src.shape
+        g["sh"] = torch.empty((K_, c3_, n_), dtype=torch.uint8, device=dev)
+        g["sh_bounds"] = torch.empty(B.sh_q8_bounds_floats(n_, K_ * c3_), dtype=torch.float32, device=dev)
+        B.sh_quantize8(src, g["sh"], g["sh_bounds"])
+        torch.cuda.synchronize()
+        del src
     stream = torch.cuda.current_stream()
     # importance mask (a global pre-pass of every step when the workload has scores)
     use_mask = sc.importance is not None
@@ -267,7 +278,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if sc.sh_fp16 is None else "f32 (SH stored f16)",
+        "dtype": ("f32 (SH stored u8 + block bounds)" if args.sh_q8 else
+                  "f32" if sc.sh_fp16 is None else "f32 (SH stored f16)"),
         "data": "synthetic (seeded scene generator; no dataset)",
         "config": {"workload": sc.name, "gaussians": sc.n, "sh_degree": sc.sh_degree,
                    "width": sc.cameras[0].width, "height": sc.cameras[0].height, "views_per_step": views,

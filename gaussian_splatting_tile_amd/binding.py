@@ -16,7 +16,7 @@ import torch
 from . import build as _build
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE, GS_ERR_HIP = range(5)
-GS_SH_F32, GS_SH_F16 = 0, 1
+GS_SH_F32, GS_SH_F16, GS_SH_Q8 = 0, 1, 2
 SPLAT_FLOATS = 12          # gs_splat is 48 bytes
 
 
@@ -50,7 +50,8 @@ class GsBwdView(C.Structure):
 class GsGaussians(C.Structure):
     _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("sh_dtype", C.c_int32),
                 ("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p),
-                ("opacities", C.c_void_p), ("sh", C.c_void_p), ("active", C.c_void_p)]
+                ("opacities", C.c_void_p), ("sh", C.c_void_p), ("active", C.c_void_p),
+                ("sh_bounds", C.c_void_p)]
 
 
 class GsGrads(C.Structure):
@@ -69,7 +70,7 @@ SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
-           "gs_active_mask", "gs_status_string", "gs_version")
+           "gs_active_mask", "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_status_string", "gs_version")
 
 
 def lib_path() -> str:
@@ -114,6 +115,9 @@ def lib():
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
     L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
+    L.gs_sh_q8_bounds_floats.argtypes = [i64, C.c_int32]
+    L.gs_sh_q8_bounds_floats.restype = sz
+    L.gs_sh_quantize8.argtypes = [vp, i64, C.c_int32, vp, vp, vp]
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
@@ -121,7 +125,7 @@ def lib():
                  "gs_render_fwd_views",
                  "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
-                 "gs_project_bwd", "gs_active_mask"):
+                 "gs_project_bwd", "gs_active_mask", "gs_sh_quantize8"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -162,7 +166,7 @@ def gaussians_struct(g: Dict[str, torch.Tensor], sh_degree: int, active: Optiona
     s = GsGaussians()
     s.n = int(g["means"].shape[1])
     s.sh_degree = int(sh_degree)
-    s.sh_dtype = GS_SH_F16 if g["sh"].dtype == torch.float16 else GS_SH_F32
+    s.sh_dtype = {torch.float16: GS_SH_F16, torch.uint8: GS_SH_Q8}.get(g["sh"].dtype, GS_SH_F32)
     for k in ("means", "scales", "quats", "opacities"):
         t = g[k]
         assert t.is_cuda and t.dtype == torch.float32 and t.is_contiguous(), k
@@ -172,7 +176,25 @@ def gaussians_struct(g: Dict[str, torch.Tensor], sh_degree: int, active: Optiona
     if active is not None:
         assert active.is_cuda and active.dtype == torch.uint8 and active.is_contiguous()
         s.active = active.data_ptr()
+    if s.sh_dtype == GS_SH_Q8:
+        b = g["sh_bounds"]
+        assert b.is_cuda and b.dtype == torch.float32 and b.is_contiguous()
+        s.sh_bounds = b.data_ptr()
     return s
+
+
+def sh_q8_bounds_floats(n: int, rows: int) -> int:
+    return int(lib().gs_sh_q8_bounds_floats(n, rows))
+
+
+def sh_quantize8(sh: torch.Tensor, codes: torch.Tensor, bounds: torch.Tensor, stream=None):
+    """gs_sh_quantize8: sh float32 [K][3][n] -> codes uint8 [K][3][n], bounds
+    float32 [K*3][ceil(n/256)][2]."""
+    K, c3, n = sh.shape
+    assert sh.dtype == torch.float32 and sh.is_contiguous() and codes.dtype == torch.uint8
+    assert bounds.numel() >= sh_q8_bounds_floats(n, K * c3)
+    _check(lib().gs_sh_quantize8(_ptr(sh), int(n), int(K * c3), _ptr(codes), _ptr(bounds), _stream(stream)),
+           "gs_sh_quantize8")
 
 
 # ---- the four calls ---------------------------------------------------------

@@ -29,9 +29,11 @@ gs_status gaussians_ok(const gs_gaussians *g)
 {
     if (!g || g->n < 0 || g->n > INT32_MAX) return GS_ERR_INVALID_ARG;
     if (g->sh_degree < 0 || g->sh_degree > 3) return GS_ERR_UNSUPPORTED;
-    if (g->sh_dtype != GS_SH_F32 && g->sh_dtype != GS_SH_F16) return GS_ERR_UNSUPPORTED;
+    if (g->sh_dtype != GS_SH_F32 && g->sh_dtype != GS_SH_F16 && g->sh_dtype != GS_SH_Q8)
+        return GS_ERR_UNSUPPORTED;
     if (g->n > 0 && (!g->means || !g->scales || !g->quats || !g->opacities || !g->sh))
         return GS_ERR_INVALID_ARG;
+    if (g->n > 0 && g->sh_dtype == GS_SH_Q8 && !g->sh_bounds) return GS_ERR_INVALID_ARG;
     return GS_OK;
 }
 
@@ -476,6 +478,20 @@ gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *
                                       (hipStream_t)stream);
     if (e == hipErrorNotSupported) return GS_ERR_UNSUPPORTED;
     return from_hip(e);
+}
+
+size_t gs_sh_q8_bounds_floats(int64_t n, int32_t rows)
+{
+    if (n < 0 || rows < 1) return 0;
+    return (size_t)rows * (size_t)((n + 255) / 256) * 2;
+}
+
+gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *codes, float *bounds, void *stream)
+{
+    if (n < 0 || n > INT32_MAX || rows < 1 || rows > 65535) return GS_ERR_INVALID_ARG;
+    if (n > 0 && (!sh || !codes || !bounds)) return GS_ERR_INVALID_ARG;
+    if (n == 0) return GS_OK;
+    return from_hip(launch_sh_quantize8(sh, n, rows, codes, bounds, (hipStream_t)stream));
 }
 
 }  // extern "C"

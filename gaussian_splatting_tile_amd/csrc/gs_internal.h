@@ -113,6 +113,7 @@ struct ProjBatch {
     Splat *out[kMaxProjViews];
 };
 hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStream_t s);
+hipError_t launch_sh_quantize8(const float *sh, int64_t n, int rows, uint8_t *codes, float *bounds, hipStream_t s);
 // Per-Gaussian screen-space gradients, g2[n][9], of up to kMaxSumViews views
 // in one launch, from the blend backward's per-slot partial sums.
 constexpr int kMaxSumViews = 8;

@@ -230,12 +230,34 @@ __device__ __forceinline__ void sh_dir_grad(const float *w, float x, float y, fl
     dd[0] = gx; dd[1] = gy; dd[2] = gz;
 }
 
+// SH coefficient `row` of Gaussian g; blk = g / 256 (the projection passes
+// its workgroup index, which is that block for every lane, so the 8-bit
+// bounds are read with scalar loads)
 template <typename T>
-__device__ __forceinline__ float ld_sh(const T *p);
+__device__ __forceinline__ float ld_sh(const T *sh, const float *bounds, size_t row, int n, int g, int blk);
 template <>
-__device__ __forceinline__ float ld_sh<float>(const float *p) { return *p; }
+__device__ __forceinline__ float ld_sh<float>(const float *sh, const float *, size_t row, int n, int g, int)
+{
+    return sh[row * n + g];
+}
 template <>
-__device__ __forceinline__ float ld_sh<__half>(const __half *p) { return __half2float(*p); }
+__device__ __forceinline__ float ld_sh<__half>(const __half *sh, const float *, size_t row, int n, int g, int)
+{
+    return __half2float(sh[row * n + g]);
+}
+// 8-bit codes: lo + q step, step = (hi - lo) * fp32(1/255), with the
+// (lo, hi) of the row's 256-Gaussian block, each step one fp32 operation
+template <>
+__device__ __forceinline__ float ld_sh<uint8_t>(const uint8_t *sh, const float *bounds, size_t row, int n, int g,
+                                                int blk)
+{
+#pragma clang fp contract(off)
+    const size_t nb = ((size_t)n + 255) / 256;
+    const float *b = bounds + (row * nb + (size_t)blk) * 2;
+    const float lo = b[0], hi = b[1];
+    const float step = (hi - lo) * (1.0f / 255.0f);
+    return lo + (float)sh[row * n + g] * step;
+}
 
 // Camera centre c = -R^T t, sums left to right.
 __device__ __forceinline__ void cam_centre(const Cam &cam, float &ccx, float &ccy, float &ccz)
@@ -261,7 +283,7 @@ template <int DEG, typename TSH>
 __global__ __launch_bounds__(kBlock) void project_kernel(
     int n, const float *__restrict__ means, const float *__restrict__ scales,
     const float *__restrict__ quats, const float *__restrict__ opac, const TSH *__restrict__ sh,
-    const uint8_t *__restrict__ active, const ProjBatch views)
+    const float *__restrict__ sh_bounds, const uint8_t *__restrict__ active, const ProjBatch views)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int g = blockIdx.x * kBlock + threadIdx.x;
@@ -276,8 +298,9 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     // lanes load, g < n; a masked-out Gaussian's coefficients go unused, and
     // predicated loads would each wait for the previous one)
     float shc[3 * K];
+    static_assert(kBlock == 256, "a projection workgroup is one 256-Gaussian SH block");
 #pragma unroll
-    for (int i = 0; i < 3 * K; i++) shc[i] = ld_sh(sh + (size_t)i * n + g);
+    for (int i = 0; i < 3 * K; i++) shc[i] = ld_sh(sh, sh_bounds, (size_t)i, n, g, (int)blockIdx.x);
     for (int v = 0; v < views.count; v++) {
     const Cam &cam = views.cam[v];
     Splat *__restrict__ out = views.out[v];
@@ -512,8 +535,9 @@ __device__ __forceinline__ int compact_range(long long g_begin, long long g_end,
 // only; every lane of the wave calls this, for the cross-lane sums).
 template <int DEG, typename TSH>
 __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int ch, const float *__restrict__ means,
-                                                const TSH *__restrict__ sh, const ViewBatch &views,
-                                                float *__restrict__ d_means, float *__restrict__ d_sh)
+                                                const TSH *__restrict__ sh, const float *__restrict__ sh_bounds,
+                                                const ViewBatch &views, float *__restrict__ d_means,
+                                                float *__restrict__ d_sh)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int lane = threadIdx.x & 63;
@@ -528,7 +552,7 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
     float mx = 0.0f, my = 0.0f, mz = 0.0f;
 #pragma unroll
     for (int j = 0; j < K; j++) {
-        kv[j] = valid ? ld_sh(shr + (size_t)(j * 3 + ch) * n + g) : 0.0f;
+        kv[j] = valid ? ld_sh(shr, sh_bounds, (size_t)(j * 3 + ch), n, g, g >> 8) : 0.0f;
         acc[j] = 0.0f;
     }
     if (valid) {
@@ -604,6 +628,7 @@ template <int DEG, typename TSH, bool COMPACT>
 __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int per_wave,
                                                                    const float *__restrict__ means,
                                                                    const TSH *__restrict__ sh,
+                                                                   const float *__restrict__ sh_bounds,
                                                                    const uint8_t *__restrict__ active,
                                                                    const ViewBatch views,
                                                                    float *__restrict__ d_means,
@@ -620,7 +645,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int pe
             const int idx = r0 + gl;
             const bool valid = gl < kColourPerWave && idx < cnt;
             const int g = valid ? (int)s_list[wv][idx] : 0;
-            colour_backward<DEG, TSH>(n, g, valid, ch, means, sh, views, d_means, d_sh);
+            colour_backward<DEG, TSH>(n, g, valid, ch, means, sh, sh_bounds, views, d_means, d_sh);
         }
     } else {
         const long long wave = (long long)blockIdx.x * (kBlock / 64) + wv;
@@ -632,7 +657,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int pe
             for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][gg].a.w) != 0);
             valid = any;
         }
-        colour_backward<DEG, TSH>(n, valid ? (int)gg : 0, valid, ch, means, sh, views, d_means, d_sh);
+        colour_backward<DEG, TSH>(n, valid ? (int)gg : 0, valid, ch, means, sh, sh_bounds, views, d_means, d_sh);
     }
 }
 
@@ -850,7 +875,7 @@ void launch_project_t(const gs_gaussians &g, const ProjBatch &views, hipStream_t
 {
     const int n = (int)g.n;
     project_kernel<DEG, TSH><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.active, views);
+        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.sh_bounds, g.active, views);
 }
 
 template <int DEG, typename TSH>
@@ -861,7 +886,7 @@ void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const g
         const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
         project_bwd_color_kernel<DEG, TSH, false>
             <<<(unsigned)((colour_waves + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, s>>>(
-                n, 0, g.means, (const TSH *)g.sh, nullptr, views, out.means, out.sh);
+                n, 0, g.means, (const TSH *)g.sh, g.sh_bounds, nullptr, views, out.means, out.sh);
         project_bwd_geom_kernel<false><<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(
             n, 0, g.means, g.scales, g.quats, g.opacities, nullptr, views, out.means, out.log_scales, out.quats,
             out.opacity_logits);
@@ -876,7 +901,8 @@ void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const g
     const long long waves = (n + per_wave - 1) / per_wave;
     const unsigned blocks = (unsigned)((waves + kBlock / 64 - 1) / (kBlock / 64));
     project_bwd_color_kernel<DEG, TSH, true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, (const TSH *)g.sh,
-                                                                       g.active, views, out.means, out.sh);
+                                                                       g.sh_bounds, g.active, views, out.means,
+                                                                       out.sh);
     project_bwd_geom_kernel<true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, g.scales, g.quats, g.opacities,
                                                             g.active, views, out.means, out.log_scales, out.quats,
                                                             out.opacity_logits);
@@ -912,8 +938,66 @@ hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStre
     if (g.n == 0 || views.count == 0) return hipSuccess;
     if (g.sh_dtype == GS_SH_F16)
         dispatch_project<__half>(g.sh_degree, g, views, s);
+    else if (g.sh_dtype == GS_SH_Q8)
+        dispatch_project<uint8_t>(g.sh_degree, g, views, s);
     else
         dispatch_project<float>(g.sh_degree, g, views, s);
+    return hipGetLastError();
+}
+
+namespace {
+// 8-bit block quantization of SH rows: one block per (256-Gaussian block,
+// row); the block's min and max by wave and block reductions, then every
+// code in fp32 with the documented order of operations.
+__global__ __launch_bounds__(kBlock) void sh_quantize8_kernel(const float *__restrict__ x, int n, int nb,
+                                                             uint8_t *__restrict__ q, float *__restrict__ bounds)
+{
+#pragma clang fp contract(off)
+    __shared__ float s_lo[kBlock / 64], s_hi[kBlock / 64];
+    const int row = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
+    const int g0 = b * 256;
+    const int g = g0 + tid;
+    const bool valid = g < n;
+    const float *xr = x + (size_t)row * n;
+    const float v = xr[valid ? g : g0];        // padding lanes repeat the block's first value
+    float lo = v, hi = v;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    }
+    if ((tid & 63) == 0) {
+        s_lo[tid >> 6] = lo;
+        s_hi[tid >> 6] = hi;
+    }
+    __syncthreads();
+    lo = s_lo[0];
+    hi = s_hi[0];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; w++) {
+        lo = fminf(lo, s_lo[w]);
+        hi = fmaxf(hi, s_hi[w]);
+    }
+    if (tid == 0) {
+        bounds[((size_t)row * nb + b) * 2] = lo;
+        bounds[((size_t)row * nb + b) * 2 + 1] = hi;
+    }
+    if (!valid) return;
+    const float d = hi - lo;
+    uint8_t c = 0;
+    if (d > 0.0f) {
+        const float t = ((v - lo) * 255.0f) / d;
+        const float f = floorf(t + 0.5f);
+        c = f >= 255.0f ? (uint8_t)255 : (uint8_t)f;
+    }
+    q[(size_t)row * n + g] = c;
+}
+}  // namespace
+
+hipError_t launch_sh_quantize8(const float *sh, int64_t n, int rows, uint8_t *codes, float *bounds, hipStream_t s)
+{
+    const int nb = (int)((n + 255) / 256);
+    sh_quantize8_kernel<<<dim3(nb, rows), kBlock, 0, s>>>(sh, (int)n, nb, codes, bounds);
     return hipGetLastError();
 }
 
@@ -933,6 +1017,8 @@ hipError_t launch_project_bwd(const gs_gaussians &g, const ViewBatch &views, con
     if (g.n == 0 || views.count == 0) return hipSuccess;
     if (g.sh_dtype == GS_SH_F16)
         dispatch_project_bwd<__half>(g.sh_degree, g, views, out, s);
+    else if (g.sh_dtype == GS_SH_Q8)
+        dispatch_project_bwd<uint8_t>(g.sh_degree, g, views, out, s);
     else
         dispatch_project_bwd<float>(g.sh_degree, g, views, out, s);
     return hipGetLastError();

@@ -70,7 +70,9 @@ typedef enum gs_status {
     GS_ERR_HIP = 4              /* a kernel launch failed                      */
 } gs_status;
 
-typedef enum gs_sh_dtype { GS_SH_F32 = 0, GS_SH_F16 = 1 } gs_sh_dtype;
+/* SH storage: fp32, fp16, or 8-bit codes with per-block bounds (see
+ * gs_sh_quantize8); the kernels compute in fp32 whatever the storage. */
+typedef enum gs_sh_dtype { GS_SH_F32 = 0, GS_SH_F16 = 1, GS_SH_Q8 = 2 } gs_sh_dtype;
 
 /* Pinhole camera (host memory). */
 typedef struct gs_camera {
@@ -97,9 +99,27 @@ typedef struct gs_gaussians {
     const float *quats;         /* [4][n] rotations (w, x, y, z), any norm > 0 */
     const float *opacities;     /* [n] activated opacities (sigmoid of logit)  */
     const void *sh;             /* [K][3][n] SH coefficients, band order
-                                   l = 0..3, m = -l..l, float or half          */
+                                   l = 0..3, m = -l..l: float, half or uint8
+                                   codes                                        */
     const uint8_t *active;      /* [n] per-Gaussian keep mask, or NULL = all   */
+    const float *sh_bounds;     /* GS_SH_Q8 only: [K*3][ceil(n/256)][2] (lo, hi)
+                                   of every 256-Gaussian block of an SH row     */
 } gs_gaussians;
+
+/* 8-bit linear block quantization of SH storage (the Spirula Studio page's
+ * description of its block-quantized tensors: 256 consecutive units share a
+ * min/max pair and decode as min + (max - min) q / 255).
+ * Input sh: float [rows][n] (rows = K * 3, the gs_gaussians layout); output
+ * codes: uint8 [rows][n] and bounds: float [rows][ceil(n/256)][2], the
+ * minimum and maximum of each block of 256 Gaussians of a row.  A value x
+ * becomes q = min(255, floor(((x - lo) * 255) / (hi - lo) + 1/2)) (0 when
+ * hi == lo) and is read back as lo + q * step with step = (hi - lo) *
+ * fp32(1/255), each step one fp32 operation in that order.  Inputs must be
+ * finite.
+ * Errors: GS_ERR_INVALID_ARG (NULL pointers with n > 0, n < 0, rows < 1). */
+size_t gs_sh_q8_bounds_floats(int64_t n, int32_t rows);
+gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *codes, float *bounds,
+                          void *stream);
 
 /* One projected Gaussian (device memory, 48 bytes, 16-byte aligned).
  * A culled Gaussian has every field 0. */

@@ -18,12 +18,17 @@ def say(*a):
 
 
 def device_gaussians(sc, sh=None, device="cuda"):
-    """Scene parameters as contiguous device tensors (SH stays in its storage dtype)."""
+    """Scene parameters as contiguous device tensors (SH stays in its storage
+    dtype; sh may be an 8-bit (codes, bounds) pair)."""
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
     if sh is None:
         sh = sc.sh_fp16 if sc.sh_fp16 is not None else sc.sh
-    return dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities),
-                sh=f(sh))
+    g = dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities))
+    if isinstance(sh, tuple):
+        g["sh"], g["sh_bounds"] = f(sh[0]), f(sh[1])
+    else:
+        g["sh"] = f(sh)
+    return g
 
 
 def splats_np(buf: B.ViewBuffers):

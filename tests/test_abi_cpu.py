@@ -33,10 +33,32 @@ def test_library_exports_every_declared_function():
 
 
 def test_struct_layouts_match_header():
-    assert C.sizeof(B.GsCamera) == 4 * 2 + 4 * 4 + 4 * 12 + 4 * 3
-    assert C.sizeof(B.GsGaussians) == 8 + 4 + 4 + 8 * 6
-    assert C.sizeof(B.GsGrads) == 8 * 5
-    assert B.SPLAT_FLOATS * 4 == 48
+    """Every field offset and struct size of the ctypes mirrors equals what a
+    C compiler makes of include/gs.h."""
+    import shutil
+    import subprocess
+    import tempfile
+    pairs = [("gs_camera", B.GsCamera), ("gs_gaussians", B.GsGaussians), ("gs_grads", B.GsGrads),
+             ("gs_fwd_view", B.GsFwdView), ("gs_sort_view", B.GsSortView), ("gs_bwd_view", B.GsBwdView)]
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gs.h"', "int main(void) {"]
+    expect = []
+    for cname, cls in pairs:
+        lines.append(f'printf("%zu\\n", sizeof({cname}));')
+        expect.append(C.sizeof(cls))
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("%zu\\n", offsetof({cname}, {fname}));')
+            expect.append(getattr(cls, fname).offset)
+    lines += ['printf("%zu\\n", sizeof(gs_splat));', "return 0; }"]
+    expect.append(B.SPLAT_FLOATS * 4)
+    cc = shutil.which("gcc") or shutil.which("cc")
+    assert cc, "no C compiler"
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "layout.c")
+        open(src, "w").write("\n".join(lines) + "\n")
+        exe = os.path.join(d, "layout")
+        subprocess.run([cc, "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == expect
 
 
 def test_status_strings_and_version():
@@ -59,6 +81,21 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
     assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    # 8-bit SH storage
+    assert L.gs_sh_quantize8(None, -1, 48, None, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_sh_quantize8(None, 10, 0, None, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_sh_quantize8(None, 10, 48, None, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_sh_quantize8(None, 0, 48, None, None, None) == B.GS_OK
+    assert L.gs_sh_q8_bounds_floats(257, 48) == 48 * 2 * 2
+    assert L.gs_sh_q8_bounds_floats(-1, 48) == 0
+    gq = B.GsGaussians()
+    gq.n, gq.sh_degree, gq.sh_dtype = 5, 3, B.GS_SH_Q8
+    gq.means = gq.scales = gq.quats = gq.opacities = gq.sh = 0x1000
+    camq = B.GsCamera()
+    camq.width, camq.height, camq.fx, camq.fy, camq.guard = 16, 16, 10.0, 10.0, 1.3
+    assert L.gs_project(C.byref(gq), C.byref(camq), 0x1000, None) == B.GS_ERR_INVALID_ARG   # no bounds
+    gq.sh_dtype = 3
+    assert L.gs_project(C.byref(gq), C.byref(camq), 0x1000, None) == B.GS_ERR_UNSUPPORTED
     # batched sort: every view is checked before anything runs
     views = (B.GsSortView * 2)()
     assert L.gs_bin_sort_views(-1, views, None) == B.GS_ERR_INVALID_ARG
