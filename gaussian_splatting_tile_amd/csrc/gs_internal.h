@@ -207,6 +207,5 @@ struct BwdBatch {
 };
 hipError_t launch_render_bwd(const BwdBatch &batch, hipStream_t s);
 static_assert(kMaxSumViews >= kMaxBlendViews, "a blend-backward batch is summed in one launch");
-hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s);
 
 }  // namespace gsi

@@ -599,12 +599,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const Batch<Sche
     }
 }
 
-__global__ void fill_u32_kernel(uint32_t *p, uint32_t value, size_t count)
-{
-    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i < count) p[i] = value;
-}
-
 // ---------------------------------------------------------------------------
 // Workspace carving.
 struct Carve {
@@ -693,13 +687,6 @@ size_t bin_sort_workspace(int64_t n, int64_t k_capacity, int n_tiles)
 {
     (void)n_tiles;
     return carve_bin(nullptr, n, k_capacity, nullptr);
-}
-
-hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t count, hipStream_t s)
-{
-    if (count == 0) return hipSuccess;
-    fill_u32_kernel<<<(unsigned)((count + kBlock - 1) / kBlock), kBlock, 0, s>>>(p, value, count);
-    return hipGetLastError();
 }
 
 // The views of a batch go through every step together, one launch per step
