@@ -263,3 +263,63 @@ def config(idx: int, n_override: Optional[int] = None) -> Scene:
 def keep_count(n: int, keep_fraction: float) -> int:
     """Number of Gaussians the importance mask keeps: floor(fraction * N)."""
     return int(math.floor(keep_fraction * n + 1e-9))
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the fused SH Adam step: SH gradients, SH values and an optimizer
+# state, all drawn at random (no optimizer arithmetic here).
+def adam_inputs(seed: int, n: int, rows: int, state: str = "q8", value_dtype=np.float16,
+                fresh: bool = False, visible: float = 0.6) -> dict:
+    """Seeded inputs for one SH Adam step over ``rows`` x ``n`` units.
+
+    * grad f32 [rows][n]: zero for Gaussians outside the step's views (a
+      fraction ``1 - visible`` of them), else N(0, sigma) with a per-Gaussian
+      sigma = 1e-6 * LogNormal(0, 1.5), ten times larger on the three DC rows.
+    * value [rows][n] in ``value_dtype``: DC rows U(0, 1), the others N(0, 0.2).
+    * state "f32": m ~ N(0, sigma_m), v = sigma_v^2 * LogNormal(0, 1)^2 per
+      unit (both f32), or zeros when ``fresh``.
+    * state "q8": m and s codes uniform on 0..255; per 256-unit block, m bounds
+      (-a, b) with a, b = 1e-6 * LogNormal(0, 1.5), and s bounds
+      (c - 3 + U(0, 1), c + U(0, 1)) around c = ln(max(a, b) / 1e-15), i.e.
+      second-moment roots from e^-3 to e^1 times the block's first-moment
+      scale; one block in 16 of each row has equal bounds.  ``fresh``: all
+      codes and bounds 0.
+    """
+    rng = np.random.default_rng([seed, n, rows])
+    nb = (n + 255) // 256
+    sig = (1e-6 * np.exp(rng.standard_normal(n) * 1.5)).astype(np.float32)
+    vis = rng.random(n) < visible
+    grad = rng.standard_normal((rows, n), dtype=np.float32) * (sig * vis)[None, :]
+    grad[:min(3, rows)] *= np.float32(10.0)
+    value = np.empty((rows, n), dtype=np.float32)
+    value[:min(3, rows)] = rng.random((min(3, rows), n), dtype=np.float32)
+    if rows > 3:
+        value[3:] = rng.standard_normal((rows - 3, n), dtype=np.float32) * np.float32(0.2)
+    out = dict(grad=grad.astype(np.float32), value=value.astype(value_dtype))
+    if state == "f32":
+        if fresh:
+            out["m"] = np.zeros((rows, n), dtype=np.float32)
+            out["v"] = np.zeros((rows, n), dtype=np.float32)
+        else:
+            out["m"] = (rng.standard_normal((rows, n), dtype=np.float32) * sig[None, :]).astype(np.float32)
+            sv = sig[None, :] * np.exp(rng.standard_normal((rows, n))).astype(np.float32)
+            out["v"] = (sv * sv).astype(np.float32)
+        return out
+    if fresh:
+        for k in ("m", "s"):
+            out[k + "_codes"] = np.zeros((rows, n), dtype=np.uint8)
+            out[k + "_bounds"] = np.zeros((rows, nb, 2), dtype=np.float32)
+        return out
+    out["m_codes"] = rng.integers(0, 256, (rows, n), dtype=np.uint8)
+    out["s_codes"] = rng.integers(0, 256, (rows, n), dtype=np.uint8)
+    a = 1e-6 * np.exp(rng.standard_normal((rows, nb)) * 1.5)
+    b = 1e-6 * np.exp(rng.standard_normal((rows, nb)) * 1.5)
+    mb = np.stack([-a, b], axis=2).astype(np.float32)
+    c = np.log(np.maximum(a, b) / 1e-15)
+    sb = np.stack([c - 3.0 + rng.random((rows, nb)), c + rng.random((rows, nb))], axis=2).astype(np.float32)
+    const = rng.random((rows, nb)) < 1.0 / 16.0
+    mb[const, 1] = mb[const, 0]
+    sb[const, 1] = sb[const, 0]
+    out["m_bounds"] = mb
+    out["s_bounds"] = sb
+    return out
