@@ -54,6 +54,9 @@ def parse():
                     help="store SH as 8-bit codes with per-256-Gaussian bounds (quantized from the fp32 source)")
     ap.add_argument("--weights", action="store_true",
                     help="the forward blend also accumulates per-Gaussian blending weights (one array for all views)")
+    ap.add_argument("--sh-adam", choices=["q8", "f32"], default=None,
+                    help="each step ends with the fused SH Adam update of the SH coefficients past DC: "
+                         "q8 = fp16 values with 8-bit log-domain moments, f32 = fp32 values and moments")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for "
                          "calibrating the HBM byte counters of a profiler run)")
@@ -72,6 +75,7 @@ BLEND_FWD_SLOTS_PER_PAIR = 20
 # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: one non-packed fp32 VALU op per lane
 # per clock (packed-fp32 instructions are not used by this library).
 VALU_PEAK_T = 256 * 64 * 2.4e9 / 1e12
+HBM_PEAK_GBPS = 8000.0
 
 
 def main():
@@ -165,8 +169,29 @@ def main():
     do_bwd = not args.no_backward
     wts = torch.zeros(sc.n, dtype=torch.float32, device=dev) if args.weights else None
 
+    # fused SH Adam over the SH rows past DC (15 coefficients x 3 channels
+    # at degree 3), from a fresh state, consuming the step's SH gradients
+    adam = None
+    if args.sh_adam and do_bwd and K_sh > 1:
+        rest = torch.from_numpy(np.ascontiguousarray(sc.sh[1:])).to(dev)
+        if args.sh_adam == "q8":
+            val = rest.half()
+            m_st = torch.zeros(rest.shape, dtype=torch.uint8, device=dev)
+            v_st = torch.zeros(rest.shape, dtype=torch.uint8, device=dev)
+            nbf = B.sh_q8_bounds_floats(sc.n, (K_sh - 1) * 3)
+            mb_st = torch.zeros(nbf, dtype=torch.float32, device=dev)
+            vb_st = torch.zeros(nbf, dtype=torch.float32, device=dev)
+        else:
+            val = rest
+            m_st = torch.zeros(rest.shape, dtype=torch.float32, device=dev)
+            v_st = torch.zeros(rest.shape, dtype=torch.float32, device=dev)
+            mb_st = vb_st = None
+        adam = dict(val=val, m=m_st, v=v_st, mb=mb_st, vb=vb_st, t=0, units=(K_sh - 1) * 3 * sc.n,
+                    bytes_per_unit=(12.0 + 32.0 / 256.0) if args.sh_adam == "q8" else 28.0)
+        del rest
+
     names = ("active_mask", "project_batch", "bin_sort", "bin_sort_batch", "render_fwd_batch",
-             "render_bwd_batch", "project_bwd_batch")
+             "render_bwd_batch", "project_bwd_batch", "sh_adam")
     # the views' sorts are independent: they may run on a few streams
     # (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
@@ -232,6 +257,11 @@ def main():
                 bufs, [b.dL for b in bufs], [b.g2 for b in bufs], [b.bwd_ws for b in bufs], bg, stream))
             timed("project_bwd_batch", lambda: B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs],
                                                              [b.g2 for b in bufs], grads, stream))
+            if adam is not None:
+                adam["t"] += 1
+                timed("sh_adam", lambda: B.sh_adam_step(grads["sh"][1:], adam["val"], adam["m"], adam["v"],
+                                                        adam["mb"], adam["vb"], step=adam["t"], lr=1e-3,
+                                                        stream=stream))
         e_end.record(stream)
         if record:
             step_ev.append((e_fwd0, e_fwd1, e_end))
@@ -290,7 +320,8 @@ def main():
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
                            ", batched blend fwd of all views" +
                            (" with per-Gaussian blending weights" if args.weights else "") +
-                           (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "")},
+                           (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "") +
+                           (f", then the fused SH Adam update ({args.sh_adam})" if adam is not None else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,
         "per_call_ms": {k: (round(v, 4) if v is not None else None) for k, v in per_call.items()},
@@ -307,6 +338,16 @@ def main():
                                   f"(P_needed), summed over the {views} views of one launch; "
                                   f"peak = 256 CU x 64 lanes x 2.4 GHz"},
     }
+    if adam is not None:
+        t_adam = per_call["sh_adam"] / 1e3
+        gbps = adam["units"] * adam["bytes_per_unit"] / t_adam / 1e9
+        res["sh_adam"] = {"kernel": "adam_q8_kernel" if args.sh_adam == "q8" else "adam_f32_kernel",
+                          "state": "8-bit log-domain moments, fp16 values" if args.sh_adam == "q8"
+                          else "fp32 moments and values",
+                          "units": adam["units"], "ms": round(per_call["sh_adam"], 4),
+                          "bytes_per_unit": adam["bytes_per_unit"], "bound": "hbm",
+                          "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     # the oracle is timed beside the default workload only (a 10M / 4K view
     # takes it minutes)
     if not args.no_cpu_baseline and args.workload == "scene_1m":

@@ -17,6 +17,7 @@ from . import build as _build
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE, GS_ERR_HIP = range(5)
 GS_SH_F32, GS_SH_F16, GS_SH_Q8 = 0, 1, 2
+GS_ADAM_F32, GS_ADAM_Q8LOG = 0, 1
 SPLAT_FLOATS = 12          # gs_splat is 48 bytes
 
 
@@ -59,6 +60,14 @@ class GsGrads(C.Structure):
                 ("opacity_logits", C.c_void_p), ("sh", C.c_void_p)]
 
 
+class GsShAdam(C.Structure):
+    _fields_ = [("n", C.c_int64), ("rows", C.c_int32), ("value_dtype", C.c_int32),
+                ("state_dtype", C.c_int32), ("step", C.c_int32), ("lr", C.c_float),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("grad", C.c_void_p), ("value", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p),
+                ("m_bounds", C.c_void_p), ("v_bounds", C.c_void_p)]
+
+
 class GsError(RuntimeError):
     pass
 
@@ -70,7 +79,8 @@ SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
-           "gs_active_mask", "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_status_string", "gs_version")
+           "gs_active_mask", "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_sh_adam_step", "gs_status_string",
+           "gs_version")
 
 
 def lib_path() -> str:
@@ -118,6 +128,7 @@ def lib():
     L.gs_sh_q8_bounds_floats.argtypes = [i64, C.c_int32]
     L.gs_sh_q8_bounds_floats.restype = sz
     L.gs_sh_quantize8.argtypes = [vp, i64, C.c_int32, vp, vp, vp]
+    L.gs_sh_adam_step.argtypes = [C.POINTER(GsShAdam), vp]
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
@@ -195,6 +206,44 @@ def sh_quantize8(sh: torch.Tensor, codes: torch.Tensor, bounds: torch.Tensor, st
     assert bounds.numel() >= sh_q8_bounds_floats(n, K * c3)
     _check(lib().gs_sh_quantize8(_ptr(sh), int(n), int(K * c3), _ptr(codes), _ptr(bounds), _stream(stream)),
            "gs_sh_quantize8")
+
+
+def sh_adam_struct(grad: torch.Tensor, value: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                   m_bounds: Optional[torch.Tensor] = None, v_bounds: Optional[torch.Tensor] = None,
+                   step: int = 1, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                   eps: float = 1e-15) -> GsShAdam:
+    """Descriptor of gs_sh_adam_step over [rows][n] (or [K][3][n]) arrays:
+    grad float32; value float32 or float16; m, v float32 (full-precision
+    state) or uint8 codes with float32 bounds [rows][ceil(n/256)][2]."""
+    n = grad.shape[-1]
+    rows = grad.numel() // n if n else grad.shape[0]
+    for t in (grad, value, m, v):
+        assert t.is_contiguous() and t.shape == grad.shape, "arrays must be contiguous and of one shape"
+    assert grad.dtype == torch.float32 and value.dtype in (torch.float32, torch.float16)
+    a = GsShAdam()
+    a.n, a.rows, a.step = int(n), int(rows), int(step)
+    a.value_dtype = GS_SH_F16 if value.dtype == torch.float16 else GS_SH_F32
+    a.lr, a.beta1, a.beta2, a.eps = float(lr), float(beta1), float(beta2), float(eps)
+    a.grad, a.value, a.m, a.v = _ptr(grad), _ptr(value), _ptr(m), _ptr(v)
+    if m.dtype == torch.uint8:
+        assert v.dtype == torch.uint8 and m_bounds is not None and v_bounds is not None
+        nbf = sh_q8_bounds_floats(n, rows)
+        assert m_bounds.dtype == torch.float32 and m_bounds.numel() >= nbf and m_bounds.is_contiguous()
+        assert v_bounds.dtype == torch.float32 and v_bounds.numel() >= nbf and v_bounds.is_contiguous()
+        a.state_dtype = GS_ADAM_Q8LOG
+        a.m_bounds, a.v_bounds = _ptr(m_bounds), _ptr(v_bounds)
+    else:
+        assert m.dtype == torch.float32 and v.dtype == torch.float32
+        a.state_dtype = GS_ADAM_F32
+    return a
+
+
+def sh_adam_step(grad, value, m, v, m_bounds=None, v_bounds=None, step=1, lr=1e-3, beta1=0.9,
+                 beta2=0.999, eps=1e-15, stream=None):
+    """gs_sh_adam_step: one fused Adam update of value, m, v (and the bounds)
+    in place."""
+    a = sh_adam_struct(grad, value, m, v, m_bounds, v_bounds, step, lr, beta1, beta2, eps)
+    _check(lib().gs_sh_adam_step(C.byref(a), _stream(stream)), "gs_sh_adam_step")
 
 
 # ---- the four calls ---------------------------------------------------------

@@ -20,8 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgs_hip.so")
-SOURCES = ["gs_api.hip", "gs_project.hip", "gs_sort.hip", "gs_render.hip", "gs_mask.hip"]
-HEADERS = [os.path.join(CSRC, "gs_internal.h"), os.path.join(INCLUDE, "gs.h")]
+SOURCES = ["gs_api.hip", "gs_project.hip", "gs_sort.hip", "gs_render.hip", "gs_mask.hip", "gs_adam.hip"]
+HEADERS = [os.path.join(CSRC, "gs_internal.h"), os.path.join(CSRC, "gs_adam.h"), os.path.join(INCLUDE, "gs.h")]
 ARCH = os.environ.get("GS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -3,6 +3,7 @@
 // synchronisation, no host round trip.
 #include <math.h>
 
+#include "gs_adam.h"
 #include "gs_internal.h"
 
 using namespace gsi;
@@ -492,6 +493,24 @@ gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *cod
     if (n > 0 && (!sh || !codes || !bounds)) return GS_ERR_INVALID_ARG;
     if (n == 0) return GS_OK;
     return from_hip(launch_sh_quantize8(sh, n, rows, codes, bounds, (hipStream_t)stream));
+}
+
+gs_status gs_sh_adam_step(const gs_sh_adam *a, void *stream)
+{
+    if (!a) return GS_ERR_INVALID_ARG;
+    if (a->n < 0 || a->n > INT32_MAX || a->rows < 1 || a->rows > 65535) return GS_ERR_INVALID_ARG;
+    if (a->value_dtype != GS_SH_F32 && a->value_dtype != GS_SH_F16) return GS_ERR_INVALID_ARG;
+    if (a->state_dtype != GS_ADAM_F32 && a->state_dtype != GS_ADAM_Q8LOG) return GS_ERR_INVALID_ARG;
+    if (a->step < 1) return GS_ERR_INVALID_ARG;
+    if (!std::isfinite(a->lr) || !(a->lr >= 0.0f)) return GS_ERR_INVALID_ARG;
+    if (!(a->beta1 >= 0.0f && a->beta1 < 1.0f) || !(a->beta2 >= 0.0f && a->beta2 < 1.0f)) return GS_ERR_INVALID_ARG;
+    if (!std::isfinite(a->eps) || !(a->eps > 0.0f)) return GS_ERR_INVALID_ARG;
+    if (a->n > 0) {
+        if (!a->grad || !a->value || !a->m || !a->v) return GS_ERR_INVALID_ARG;
+        if (a->state_dtype == GS_ADAM_Q8LOG && (!a->m_bounds || !a->v_bounds)) return GS_ERR_INVALID_ARG;
+    }
+    if (a->n == 0) return GS_OK;
+    return from_hip(launch_sh_adam(*a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -121,6 +121,53 @@ size_t gs_sh_q8_bounds_floats(int64_t n, int32_t rows);
 gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *codes, float *bounds,
                           void *stream);
 
+/* Fused SH Adam step (the Spirula Studio page's fused SH optimizer, with its
+ * 16-bit SH values and 8-bit log-domain Adam state).  One launch updates the
+ * SH values and both Adam moments of every unit (one SH coefficient of one
+ * channel of one Gaussian) in place, from the fp32 SH gradients:
+ *     m' = b1 m + (1 - b1) g,   v' = b2 v + (1 - b2) g^2,
+ *     value' = value - lr (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps),
+ * computed in fp32 from the fp32 hyper-parameters given (1 - b and the bias
+ * corrections are formed from them in double precision), the new value
+ * rounded to nearest into its storage type.  The update is lazy: a unit
+ * whose gradient is exactly zero keeps its value and both moments (t still
+ * counts every step), as an 8-bit first moment seldom decodes to exactly 0.
+ * State GS_ADAM_F32: m and v are float [rows][n].
+ * State GS_ADAM_Q8LOG: m holds uint8 codes of the first moment and v uint8
+ * codes of s = log1p(sqrt(v) / eps), each with bounds [rows][ceil(n/256)][2]
+ * (lo, hi) per block of 256 Gaussians of a row, decoded lo + q * step with
+ * step = (hi - lo) * fp32(1/255) as for GS_SH_Q8.  After the update each
+ * block's bounds become the min and max of its new values and each code
+ * min(255, floor((x - lo) * 255 / (hi - lo) + 1/2)) (0 when hi == lo).  A
+ * fresh state is all codes 0 with bounds (0, 0).  The last block of a row
+ * covers only the row's remaining n mod 256 Gaussians.
+ * All arrays are device memory owned by the caller; value, m, v and the
+ * bounds are read and overwritten, grad is only read and must not overlap
+ * them.  Concurrent calls on overlapping arrays race. */
+typedef enum gs_adam_state_dtype { GS_ADAM_F32 = 0, GS_ADAM_Q8LOG = 1 } gs_adam_state_dtype;
+
+typedef struct gs_sh_adam {
+    int64_t n;                  /* Gaussians, 0 .. 2^31-1                      */
+    int32_t rows;               /* SH rows, K * 3 for K coefficients, 1..65535 */
+    int32_t value_dtype;        /* GS_SH_F32 or GS_SH_F16 of `value`           */
+    int32_t state_dtype;        /* gs_adam_state_dtype of m and v              */
+    int32_t step;               /* t >= 1: the number of this update           */
+    float lr;                   /* learning rate >= 0                          */
+    float beta1, beta2;         /* moment decays in [0, 1)                     */
+    float eps;                  /* > 0: Adam's epsilon and the log scale       */
+    const float *grad;          /* [rows][n] fp32 SH gradients                 */
+    void *value;                /* [rows][n] SH values, float or half          */
+    void *m;                    /* [rows][n] float, or uint8 codes             */
+    void *v;                    /* [rows][n] float, or uint8 codes of s        */
+    float *m_bounds;            /* GS_ADAM_Q8LOG: [rows][ceil(n/256)][2]       */
+    float *v_bounds;            /* GS_ADAM_Q8LOG: [rows][ceil(n/256)][2]       */
+} gs_sh_adam;
+
+/* Errors: GS_ERR_INVALID_ARG (NULL descriptor, NULL arrays with n > 0, n or
+ * rows out of range, an unknown dtype, step < 1, lr < 0, a decay outside
+ * [0, 1), eps <= 0, a non-finite hyper-parameter). */
+gs_status gs_sh_adam_step(const gs_sh_adam *adam, void *stream);
+
 /* One projected Gaussian (device memory, 48 bytes, 16-byte aligned).
  * A culled Gaussian has every field 0. */
 typedef struct gs_splat {

@@ -39,7 +39,8 @@ def test_struct_layouts_match_header():
     import subprocess
     import tempfile
     pairs = [("gs_camera", B.GsCamera), ("gs_gaussians", B.GsGaussians), ("gs_grads", B.GsGrads),
-             ("gs_fwd_view", B.GsFwdView), ("gs_sort_view", B.GsSortView), ("gs_bwd_view", B.GsBwdView)]
+             ("gs_fwd_view", B.GsFwdView), ("gs_sort_view", B.GsSortView), ("gs_bwd_view", B.GsBwdView),
+             ("gs_sh_adam", B.GsShAdam)]
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gs.h"', "int main(void) {"]
     expect = []
     for cname, cls in pairs:
@@ -125,3 +126,29 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_bwd_index_words(10, 100) == 100 + 2 * 10 + 2
     assert L.gs_schedule_words(128, 128) == 64 + 4
     assert L.gs_schedule_words(0, 128) == 0
+
+
+def test_sh_adam_argument_errors_without_device():
+    """gs_sh_adam_step checks its descriptor on the host; n == 0 launches
+    nothing."""
+    L = B.lib()
+    assert L.gs_sh_adam_step(None, None) == B.GS_ERR_INVALID_ARG
+
+    def desc(**kw):
+        a = B.GsShAdam()
+        a.n, a.rows, a.value_dtype, a.state_dtype, a.step = 1000, 45, B.GS_SH_F16, B.GS_ADAM_Q8LOG, 1
+        a.lr, a.beta1, a.beta2, a.eps = 1e-3, 0.9, 0.999, 1e-15
+        a.grad = a.value = a.m = a.v = a.m_bounds = a.v_bounds = 0x1000
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    bad = [dict(n=-1), dict(rows=0), dict(rows=65536), dict(value_dtype=B.GS_SH_Q8), dict(state_dtype=2),
+           dict(step=0), dict(lr=-1.0), dict(lr=float("inf")), dict(beta1=1.0), dict(beta2=-0.5),
+           dict(eps=0.0), dict(eps=float("nan")), dict(grad=None), dict(value=None), dict(m=None),
+           dict(v=None), dict(m_bounds=None), dict(v_bounds=None)]
+    for kw in bad:
+        assert L.gs_sh_adam_step(C.byref(desc(**kw)), None) == B.GS_ERR_INVALID_ARG, kw
+    # the full-precision state needs no bounds; an empty update does nothing
+    a = desc(n=0, state_dtype=B.GS_ADAM_F32, m_bounds=None, v_bounds=None, grad=None, value=None, m=None, v=None)
+    assert L.gs_sh_adam_step(C.byref(a), None) == B.GS_OK

@@ -1,0 +1,292 @@
+"""GPU parity of the fused SH Adam step (gs_sh_adam_step) against the fp64
+oracle (oracle/adam.py), through the C ABI.
+
+The kernel computes in fp32 with hardware exp2/log2/sqrt/rcp; the oracle in
+fp64.  Continuous outputs are compared within error bounds derived from that:
+new moments and bounds within a few fp32 ulps (the log-domain value within
+1e-5 + 4e-7 |s|), new values within 2 ulps plus 2e-5 of the update.  An
+8-bit code is an integer decided by floating point, so it must equal the
+oracle's except where the oracle's unrounded code position sits within the
+propagated error of a rounding boundary; there a neighbour is accepted, and
+such codes must stay rare.  fp16 values are held to the same rule around
+fp16 rounding midpoints.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gaussian_splatting_tile_amd import binding as B
+from gaussian_splatting_tile_amd import scenes
+from oracle import adam as A
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+# the ABI takes fp32 hyper-parameters: the oracle gets the same values (0.999
+# is not an fp32 number, and 1 - fp32(0.999) differs from 1e-3 by 1.3e-5)
+LR, B1, B2, EPS = (float(np.float32(x)) for x in (1e-3, 0.9, 0.999, 1e-15))
+
+
+def _dev(x, offset=0):
+    """Host array -> device tensor; offset > 0 places it that many elements
+    into a larger allocation (a misaligned pointer)."""
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if offset == 0:
+        return t.cuda()
+    flat = torch.empty(t.numel() + offset, dtype=t.dtype, device="cuda")
+    view = flat[offset:].view(t.shape)
+    view.copy_(t.cuda())
+    return view
+
+
+def _run_gpu(d, state, step, lr=LR, offset=0):
+    g = _dev(d["grad"], offset)
+    val = _dev(d["value"], offset)
+    if state == "q8":
+        m, v = _dev(d["m_codes"], offset), _dev(d["s_codes"], offset)
+        mb, vb = _dev(d["m_bounds"]), _dev(d["s_bounds"])
+    else:
+        m, v = _dev(d["m"], offset), _dev(d["v"], offset)
+        mb = vb = None
+    B.sh_adam_step(g, val, m, v, mb, vb, step=step, lr=lr, beta1=B1, beta2=B2, eps=EPS)
+    torch.cuda.synchronize()
+    out = dict(value=val.cpu().numpy(), grad_after=g.cpu().numpy())
+    if state == "q8":
+        out.update(m_codes=m.cpu().numpy(), s_codes=v.cpu().numpy(), m_bounds=mb.cpu().numpy(),
+                   s_bounds=vb.cpu().numpy())
+    else:
+        out.update(m=m.cpu().numpy(), v=v.cpu().numpy())
+    return out
+
+
+def _oracle(d, state, step, lr=LR):
+    if state == "q8":
+        return A.adam_step_q8(d["grad"], d["value"], d["m_codes"], d["m_bounds"], d["s_codes"], d["s_bounds"],
+                              step=step, lr=lr, beta1=B1, beta2=B2, eps=EPS)
+    return A.adam_step_f32(d["grad"], d["value"], d["m"], d["v"], step=step, lr=lr, beta1=B1, beta2=B2, eps=EPS)
+
+
+def _ulp32(x):
+    return np.spacing(np.abs(np.asarray(x, np.float64)).astype(np.float32)).astype(np.float64)
+
+
+def _check_values(gpu_val, ref, d, name):
+    """New SH values: fp32 within 2 ulps + 2e-5 |update|; fp16 equal to the
+    oracle's rounding except within that distance of a rounding midpoint."""
+    th0 = d["value"].astype(np.float64)
+    x = ref["value64"]
+    tau = 2.0 * _ulp32(x) + 2e-5 * np.abs(x - th0) + 1e-30
+    g = gpu_val.astype(np.float64)
+    assert np.all(np.isfinite(g)), name
+    if gpu_val.dtype == np.float32:
+        err = np.abs(g - x)
+        assert np.all(err <= tau), (name, float((err / tau).max()))
+        return
+    r16 = ref["value"]
+    same = gpu_val == r16
+    sp = np.maximum(np.spacing(np.abs(gpu_val)), np.spacing(np.abs(r16))).astype(np.float64)
+    near_mid = np.abs(np.abs(g - x) - 0.5 * sp) <= tau
+    bad = ~same & ~near_mid
+    assert not bad.any(), (name, int(bad.sum()), g[bad][:4], x[bad][:4])
+    assert np.mean(~same) < 1e-3, (name, float(np.mean(~same)))
+
+
+def _check_codes(gpu, ref, key, tau, name):
+    """One 8-bit moment: bounds within the error bound of the block's values,
+    codes equal except next to a rounding boundary, decoded values within half
+    a step of the oracle's."""
+    rows, n = gpu[key + "_codes"].shape
+    blk = np.arange(n) // 256
+    b64 = ref[key + "_bounds64"]
+    bg = gpu[key + "_bounds"].reshape(b64.shape).astype(np.float64)
+    assert np.all(np.isfinite(bg)), name
+    x = ref[key + "64"]
+    # the block's largest error bound
+    nb = b64.shape[1]
+    tau_b = np.zeros((rows, nb))
+    np.maximum.at(tau_b, (np.repeat(np.arange(rows), n), np.tile(blk, rows)), tau.reshape(-1))
+    assert np.all(np.abs(bg - b64) <= tau_b[..., None] * 1.0001), (name, key)
+    d = (b64[..., 1] - b64[..., 0])
+    dpx = d[:, blk]
+    t = ref[key + "_t"]
+    tight = (dpx <= 8.0 * tau_b[:, blk])                      # block width within its own error
+    w = 255.0 * 4.0 * tau_b[:, blk] / np.where(dpx > 0, dpx, 1.0) + 1e-4
+    amb = (np.abs(t - np.floor(t) - 0.5) < w) | tight
+    cg = gpu[key + "_codes"].astype(np.int64)
+    cr = ref[key + "_codes"].astype(np.int64)
+    diff = cg - cr
+    assert np.all(diff[~amb] == 0), (name, key, int((diff[~amb] != 0).sum()))
+    assert np.all(np.abs(diff[amb & ~tight]) <= 1), (name, key)
+    assert np.all(cg[dpx == 0] == 0), (name, key)              # constant (e.g. one-unit) blocks
+    n_amb = int(np.sum(amb & ~tight))
+    assert n_amb <= max(2, 0.05 * amb.size), (name, key, n_amb, amb.size)   # rare (a few in tiny cases)
+    dec = A.decode8(gpu[key + "_codes"], gpu[key + "_bounds"].reshape(b64.shape)).astype(np.float64)
+    half = 0.5 * dpx / 255.0
+    assert np.all(np.abs(dec - x) <= half * 1.0001 + 4.0 * tau_b[:, blk] + 1e-30), (name, key)
+    return float(np.mean(amb & ~tight))
+
+
+def _tau_q8(ref, d):
+    g = np.abs(d["grad"].astype(np.float64))
+    m0 = np.abs(A.decode8(d["m_codes"], d["m_bounds"]).astype(np.float64))
+    tau_m = 2.5e-7 * (B1 * m0 + (1 - B1) * g) + 2.5e-7 * np.abs(ref["m64"]) + 1e-45
+    tau_s = 1e-5 + 4e-7 * np.abs(ref["s64"])
+    return tau_m, tau_s
+
+
+def _compare_q8(gpu, ref, d, name):
+    tau_m, tau_s = _tau_q8(ref, d)
+    am = _check_codes(gpu, ref, "m", tau_m, name)
+    as_ = _check_codes(gpu, ref, "s", tau_s, name)
+    _check_values(gpu["value"], ref, d, name)
+    assert np.array_equal(gpu["grad_after"], d["grad"]), name            # gradients are only read
+    say(f"[gpu] {name}: ambiguous codes m {am:.4f} s {as_:.4f}")
+
+
+def _compare_f32(gpu, ref, d, name):
+    g = np.abs(d["grad"].astype(np.float64))
+    tau_m = 2.5e-7 * (B1 * np.abs(d["m"]) + (1 - B1) * g) * 2 + 1e-45
+    assert np.all(np.abs(gpu["m"] - ref["m64"]) <= tau_m), name
+    tau_v = 5e-7 * np.abs(ref["v64"]) + 1e-45
+    assert np.all(np.abs(gpu["v"] - ref["v64"]) <= tau_v), name
+    _check_values(gpu["value"], ref, d, name)
+    assert np.array_equal(gpu["grad_after"], d["grad"]), name
+
+
+@pytest.mark.parametrize("vdt", [np.float16, np.float32])
+@pytest.mark.parametrize("n", [1000, 1001])
+@pytest.mark.parametrize("fresh", [True, False])
+def test_q8_state_step_matches_oracle(vdt, n, fresh):
+    """45 SH rows (the SH3 coefficients past DC) of n Gaussians: 4 blocks with
+    a ragged last one; n = 1000 takes the 4-unit vector path, n = 1001 the
+    per-unit one."""
+    d = scenes.adam_inputs(40 + n, n, 45, state="q8", value_dtype=vdt, fresh=fresh)
+    step = 1 if fresh else 9
+    name = f"q8 {np.dtype(vdt).name} n={n} fresh={fresh}"
+    say(f"[gpu] adam {name}")
+    _compare_q8(_run_gpu(d, "q8", step), _oracle(d, "q8", step), d, name)
+
+
+@pytest.mark.parametrize("vdt", [np.float16, np.float32])
+@pytest.mark.parametrize("n", [1000, 1001])
+def test_f32_state_step_matches_oracle(vdt, n):
+    d = scenes.adam_inputs(50 + n, n, 48, state="f32", value_dtype=vdt)
+    name = f"f32 {np.dtype(vdt).name} n={n}"
+    say(f"[gpu] adam {name}")
+    _compare_f32(_run_gpu(d, "f32", 4), _oracle(d, "f32", 4), d, name)
+
+
+@pytest.mark.parametrize("state", ["q8", "f32"])
+def test_misaligned_arrays_take_the_per_unit_path(state):
+    d = scenes.adam_inputs(60, 2048, 6, state=state, value_dtype=np.float16)
+    say(f"[gpu] adam {state} misaligned")
+    gpu = _run_gpu(d, state, 3, offset=1)
+    ref = _oracle(d, state, 3)
+    (_compare_q8 if state == "q8" else _compare_f32)(gpu, ref, d, f"{state} misaligned")
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 255, 256, 260])
+def test_small_and_boundary_sizes(n):
+    """One unit, fewer than a vector, one lane, one block exactly, a 4-unit
+    tail block."""
+    d = scenes.adam_inputs(70 + n, n, 3, state="q8", value_dtype=np.float16)
+    name = f"q8 n={n}"
+    say(f"[gpu] adam {name}")
+    _compare_q8(_run_gpu(d, "q8", 2), _oracle(d, "q8", 2), d, name)
+
+
+def test_empty_update_touches_nothing():
+    z = torch.zeros((3, 0), device="cuda")
+    B.sh_adam_step(z, z.clone(), z.clone(), z.clone(), step=1)
+    torch.cuda.synchronize()
+
+
+def test_several_steps_track_the_oracle():
+    """Five steps from a fresh state, each side carrying its own state: the
+    full-precision state stays within fp32 error of the oracle's; with the
+    8-bit state an ambiguous code may differ by one and steer later updates a
+    little, so values stay within a fraction of lr and mostly equal.  Either
+    way a Gaussian that no step saw keeps its value bit for bit."""
+    rng = np.random.default_rng(80)
+    for state in ("f32", "q8"):
+        d = scenes.adam_inputs(81, 3000, 12, state=state, value_dtype=np.float32, fresh=True)
+        dev = {k: _dev(v) for k, v in d.items()}
+        ref = dict(d)
+        for t in range(1, 6):
+            g = (d["grad"] * np.float32(rng.random() * 2)).astype(np.float32)
+            dev["grad"].copy_(torch.from_numpy(g).cuda())
+            ref["grad"] = g
+            if state == "q8":
+                B.sh_adam_step(dev["grad"], dev["value"], dev["m_codes"], dev["s_codes"], dev["m_bounds"],
+                               dev["s_bounds"], step=t, lr=LR, beta1=B1, beta2=B2, eps=EPS)
+                r = _oracle(ref, "q8", t)
+                ref.update(value=r["value"], m_codes=r["m_codes"], m_bounds=r["m_bounds"], s_codes=r["s_codes"],
+                           s_bounds=r["s_bounds"])
+            else:
+                B.sh_adam_step(dev["grad"], dev["value"], dev["m"], dev["v"], step=t, lr=LR, beta1=B1,
+                               beta2=B2, eps=EPS)
+                r = _oracle(ref, "f32", t)
+                ref.update(value=r["value"], m=r["m"], v=r["v"])
+        torch.cuda.synchronize()
+        gv = dev["value"].cpu().numpy().astype(np.float64)
+        rv = ref["value"].astype(np.float64)
+        moved = np.abs(rv - d["value"])
+        err = np.abs(gv - rv)
+        say(f"[gpu] adam 5 steps {state}: max err / lr {err.max() / LR:.3g}, mean {err.mean() / LR:.3g}")
+        unseen = d["grad"] == 0
+        assert unseen.any() and np.array_equal(gv[unseen], d["value"][unseen].astype(np.float64))
+        assert np.all(np.isfinite(gv))
+        if state == "f32":
+            assert np.all(err <= 4 * _ulp32(rv) + 1e-4 * moved), state
+            assert np.allclose(dev["m"].cpu().numpy(), ref["m"], rtol=1e-5, atol=1e-20)
+            assert np.allclose(dev["v"].cpu().numpy(), ref["v"], rtol=1e-5, atol=1e-30)
+        else:
+            assert err.max() <= 0.5 * LR and err.mean() <= 2e-3 * LR, state
+
+
+def test_each_of_several_eight_bit_steps_matches_the_oracle():
+    """Five 8-bit steps from a fresh state, the GPU given the oracle's state
+    before each one: every step meets the single-step rules."""
+    rng = np.random.default_rng(82)
+    d = scenes.adam_inputs(83, 2000, 9, state="q8", value_dtype=np.float16, fresh=True)
+    cur = dict(d)
+    for t in range(1, 6):
+        cur["grad"] = (d["grad"] * np.float32(0.5 + rng.random())).astype(np.float32)
+        say(f"[gpu] adam q8 step {t} from the oracle's state")
+        r = _oracle(cur, "q8", t)
+        _compare_q8(_run_gpu(cur, "q8", t), r, cur, f"q8 step {t}")
+        cur = dict(grad=cur["grad"], value=r["value"], m_codes=r["m_codes"], m_bounds=r["m_bounds"],
+                   s_codes=r["s_codes"], s_bounds=r["s_bounds"])
+
+
+def test_full_size_5m_sh3_sampled_blocks():
+    """5M Gaussians x 45 SH rows (225M units, the size the Spirula Studio page
+    times its fused optimizer at), fp16 values and the 8-bit state, one launch
+    at full size; 48 sampled blocks and every row's ragged last block (5M =
+    19531 x 256 + 64) compared with the oracle run on those blocks alone."""
+    n, rows = 5_000_000, 45
+    say("[gpu] adam full size 5M x 45: drawing inputs")
+    d = scenes.adam_inputs(90, n, rows, state="q8", value_dtype=np.float16)
+    dev = {k: _dev(v) for k, v in d.items()}
+    say("[gpu] adam full size: one step")
+    B.sh_adam_step(dev["grad"], dev["value"], dev["m_codes"], dev["s_codes"], dev["m_bounds"], dev["s_bounds"],
+                   step=20, lr=LR, beta1=B1, beta2=B2, eps=EPS)
+    torch.cuda.synchronize()
+    nb = A.n_blocks(n)
+    rng = np.random.default_rng(91)
+    picks = [(int(r), int(b)) for r, b in zip(rng.integers(0, rows, 48), rng.integers(0, nb - 1, 48))]
+    picks += [(r, nb - 1) for r in range(0, rows, 4)]
+    mb = dev["m_bounds"].view(rows, nb, 2)
+    sb = dev["s_bounds"].view(rows, nb, 2)
+    for r, b in picks:
+        lo, hi = b * 256, min(n, b * 256 + 256)
+        sub = {k: d[k][r:r + 1, lo:hi] for k in ("grad", "value", "m_codes", "s_codes")}
+        sub["m_bounds"] = d["m_bounds"][r:r + 1, b:b + 1]
+        sub["s_bounds"] = d["s_bounds"][r:r + 1, b:b + 1]
+        gpu = dict(value=dev["value"][r:r + 1, lo:hi].cpu().numpy(),
+                   m_codes=dev["m_codes"][r:r + 1, lo:hi].cpu().numpy(),
+                   s_codes=dev["s_codes"][r:r + 1, lo:hi].cpu().numpy(),
+                   m_bounds=mb[r:r + 1, b:b + 1].cpu().numpy(), s_bounds=sb[r:r + 1, b:b + 1].cpu().numpy(),
+                   grad_after=dev["grad"][r:r + 1, lo:hi].cpu().numpy())
+        _compare_q8(gpu, _oracle(sub, "q8", 20), sub, f"5M row {r} block {b}")
