@@ -18,6 +18,11 @@ the measured speed-up of its fused optimizer kernel):
   names Adam's two moments but prints no update formula:
       m' = b1 m + (1 - b1) g          v' = b2 v + (1 - b2) g^2
       theta' = theta - lr * (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps)
+  applied lazily: a unit whose gradient is exactly zero in this step (a
+  Gaussian none of the step's views saw) keeps its value and both moments,
+  as in torch.optim.SparseAdam; t counts all steps.  With an 8-bit first
+  moment zero is in general not a code, so a dense step would move every
+  unseen Gaussian by about lr * (quantization residue) / eps.
 * Full-precision state: m and v as fp32.
 * 8-bit state: both moments 8-bit with one (min, max) float pair per block of
   256 consecutive units, decoded lo + q * step, step = (hi - lo) * fp32(1/255)
@@ -82,12 +87,14 @@ def encode8(x: np.ndarray):
 
 
 def _adam(theta, m, v, g, step, lr, beta1, beta2, eps):
-    """One bias-corrected Adam update in fp64; returns theta', m', v'."""
-    m1 = beta1 * m + (1.0 - beta1) * g
-    v1 = beta2 * v + (1.0 - beta2) * g * g
+    """One bias-corrected Adam update in fp64 of the units with g != 0;
+    returns theta', m', v' (the other units unchanged)."""
+    live = g != 0
+    m1 = np.where(live, beta1 * m + (1.0 - beta1) * g, m)
+    v1 = np.where(live, beta2 * v + (1.0 - beta2) * g * g, v)
     bc1 = 1.0 - beta1 ** step
     bc2 = 1.0 - beta2 ** step
-    theta1 = theta - lr * (m1 / bc1) / (np.sqrt(v1 / bc2) + eps)
+    theta1 = np.where(live, theta - lr * (m1 / bc1) / (np.sqrt(v1 / bc2) + eps), theta)
     return theta1, m1, v1
 
 
@@ -110,7 +117,7 @@ def adam_step_q8(grad, value, m_codes, m_bounds, s_codes, s_bounds, step, lr,
     s = decode8(s_codes, s_bounds).astype(np.float64)
     v = (eps * np.expm1(s)) ** 2
     th, m1, v1 = _adam(np.asarray(value, dtype=np.float64), m, v, g, step, lr, beta1, beta2, eps)
-    s1 = np.log1p(np.sqrt(v1) / eps)
+    s1 = np.where(g != 0, np.log1p(np.sqrt(v1) / eps), s)       # an untouched unit keeps its s
     mc, mb, mt = encode8(m1)
     sc, sb, st = encode8(s1)
     return dict(value=th.astype(value.dtype), value64=th, m64=m1, s64=s1,

@@ -1,8 +1,9 @@
 """Pins of the fused SH Adam oracle (oracle/adam.py) to things other than
-itself: torch's own Adam (an independent library implementation of the same
-update, fed the oracle's decoded state), closed forms of a first step, the
-scale invariance of Adam, exact codes of a log-encoded ramp, block locality
-and the round-trip bound of the 8-bit encoding."""
+itself: torch's own Adam and SparseAdam (independent library implementations
+of the same update, Adam also fed the oracle's decoded 8-bit state), closed
+forms of a first step, the scale invariance of Adam, exact codes of a
+log-encoded ramp, block locality and the round-trip bound of the 8-bit
+encoding."""
 
 import numpy as np
 import pytest
@@ -32,10 +33,10 @@ def _torch_adam(theta, grads, m0=None, v0=None, step0=0, lr=LR, eps=EPS):
 
 
 def test_full_precision_matches_torch_adam_over_steps():
+    """Every gradient non-zero: the lazy update is plain Adam."""
     d = scenes.adam_inputs(11, 700, 6, state="f32", value_dtype=np.float64, fresh=True)
     rng = np.random.default_rng(5)
-    grads = [d["grad"] * rng.random() * 3 for _ in range(5)]
-    grads[2] = np.zeros_like(grads[2])                       # a step with no gradient
+    grads = [rng.standard_normal((6, 700)) * 1e-5 * (1 + rng.random()) for _ in range(5)]
     th, m, v = d["value"].astype(np.float64), d["m"].astype(np.float64), d["v"].astype(np.float64)
     for t, g in enumerate(grads, start=1):
         r = A.adam_step_f32(g, th, m, v, step=t, lr=LR)
@@ -46,9 +47,37 @@ def test_full_precision_matches_torch_adam_over_steps():
     np.testing.assert_allclose(v, tv, rtol=1e-12, atol=1e-30)
 
 
+def test_zero_gradient_units_follow_torch_sparse_adam():
+    """Units with a zero gradient are skipped and t counts every step, as in
+    torch.optim.SparseAdam (fed the non-zero entries).  SparseAdam adds eps
+    before the bias correction, so eps is made negligible here."""
+    d = scenes.adam_inputs(19, 700, 6, state="f32", value_dtype=np.float64, fresh=True)
+    rng = np.random.default_rng(6)
+    grads = [d["grad"] * rng.random() * 3 for _ in range(5)]
+    grads[2] = np.zeros_like(grads[2])                       # a step with no gradient at all
+    assert np.mean(grads[0] == 0) > 0.2
+    eps = 1e-300
+    th, m, v = d["value"].astype(np.float64), d["m"].astype(np.float64), d["v"].astype(np.float64)
+    for t, g in enumerate(grads, start=1):
+        r = A.adam_step_f32(g, th, m, v, step=t, lr=LR, eps=eps)
+        th, m, v = r["value64"], r["m64"], r["v64"]
+    p = torch.nn.Parameter(torch.from_numpy(d["value"].astype(np.float64)))
+    opt = torch.optim.SparseAdam([p], lr=LR, betas=(B1, B2), eps=eps)
+    for g in grads:
+        p.grad = torch.from_numpy(np.array(g, dtype=np.float64)).to_sparse()
+        opt.step()
+    st = opt.state[p]
+    np.testing.assert_allclose(th, p.detach().numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-25)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-30)
+    never = np.all([g == 0 for g in grads], axis=0)
+    assert never.any() and np.array_equal(th[never], d["value"][never])
+
+
 def test_eight_bit_step_matches_torch_adam_on_the_decoded_state():
     """The Adam arithmetic of the 8-bit path: torch's Adam started from the
-    decoded moments (v = (eps expm1(s))^2) at the same step count."""
+    decoded moments (v = (eps expm1(s))^2) at the same step count, on the
+    units with a gradient; the others keep their value and decoded moments."""
     d = scenes.adam_inputs(12, 900, 6)
     t = 7
     r = A.adam_step_q8(d["grad"], d["value"], d["m_codes"], d["m_bounds"], d["s_codes"], d["s_bounds"],
@@ -57,9 +86,13 @@ def test_eight_bit_step_matches_torch_adam_on_the_decoded_state():
     s0 = A.decode8(d["s_codes"], d["s_bounds"]).astype(np.float64)
     v0 = (EPS * np.expm1(s0)) ** 2
     tp, tm, tv = _torch_adam(d["value"].astype(np.float64), [d["grad"]], m0, v0, step0=t - 1)
-    np.testing.assert_allclose(r["value64"], tp, rtol=1e-12, atol=1e-15)
-    np.testing.assert_allclose(r["m64"], tm, rtol=1e-12, atol=1e-25)
-    np.testing.assert_allclose(r["s64"], np.log1p(np.sqrt(tv) / EPS), rtol=1e-12, atol=1e-12)
+    live = d["grad"] != 0
+    assert 0.2 < np.mean(~live) < 0.6
+    np.testing.assert_allclose(r["value64"][live], tp[live], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["m64"][live], tm[live], rtol=1e-12, atol=1e-25)
+    np.testing.assert_allclose(r["s64"][live], np.log1p(np.sqrt(tv[live]) / EPS), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r["value64"][~live], d["value"][~live].astype(np.float64))
+    assert np.array_equal(r["m64"][~live], m0[~live]) and np.array_equal(r["s64"][~live], s0[~live])
     assert np.all(np.abs(r["value"].astype(np.float64) - r["value64"])
                   <= 0.5 * np.spacing(np.abs(r["value"])).astype(np.float64) * (1 + 1e-9))
 
