@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--sh-adam", choices=["q8", "f32"], default=None,
                     help="each step ends with the fused SH Adam update of the SH coefficients past DC: "
                          "q8 = fp16 values with 8-bit log-domain moments, f32 = fp32 values and moments")
+    ap.add_argument("--motion", action="store_true",
+                    help="moving Gaussians: a motion vector and a time offset each, the views spread over the "
+                         "time window (the projection and its backward displace the means)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for "
                          "calibrating the HBM byte counters of a profiler run)")
@@ -118,12 +121,16 @@ def main():
     else:
         sc = scenes.tiny()
         sc.upstream_seed = 11
+    if args.motion:
+        sc = scenes.with_motion(sc, seed=sc.n % 1000 + 7)
     views = min(args.views, len(sc.cameras))
     print(f"# scene {sc.name}: N={sc.n} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = dict(means=f(sc.means), scales=f(sc.scales), quats=f(sc.quats), opacities=f(sc.opacities),
              sh=f(sc.sh_fp16 if sc.sh_fp16 is not None else sc.sh))
+    if sc.velocity is not None:
+        g["velocity"], g["t_offset"] = f(sc.velocity), f(sc.t_offset)
     if args.sh_q8:
         # 8-bit block-quantized SH storage, encoded on the GPU from the fp32 source
         src = f(sc.sh)
@@ -165,6 +172,9 @@ def main():
     grads = dict(means=torch.zeros((3, sc.n), device=dev), log_scales=torch.zeros((3, sc.n), device=dev),
                  quats=torch.zeros((4, sc.n), device=dev), opacity_logits=torch.zeros(sc.n, device=dev),
                  sh=torch.zeros((K_sh, 3, sc.n), device=dev))
+    if sc.velocity is not None:
+        grads["velocity"] = torch.zeros((3, sc.n), device=dev)
+        grads["t_offset"] = torch.zeros(sc.n, device=dev)
     bg = (0.0, 0.0, 0.0)
     do_bwd = not args.no_backward
     wts = torch.zeros(sc.n, dtype=torch.float32, device=dev) if args.weights else None
@@ -320,6 +330,7 @@ def main():
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
                            ", batched blend fwd of all views" +
                            (" with per-Gaussian blending weights" if args.weights else "") +
+                           (" (moving Gaussians, views spread over the time window)" if args.motion else "") +
                            (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "") +
                            (f", then the fused SH Adam update ({args.sh_adam})" if adam is not None else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),

@@ -24,7 +24,8 @@ SPLAT_FLOATS = 12          # gs_splat is 48 bytes
 class GsCamera(C.Structure):
     _fields_ = [("width", C.c_int32), ("height", C.c_int32), ("fx", C.c_float), ("fy", C.c_float),
                 ("cx", C.c_float), ("cy", C.c_float), ("viewmat", C.c_float * 12),
-                ("znear", C.c_float), ("guard", C.c_float), ("lod_min_radius_px", C.c_float)]
+                ("znear", C.c_float), ("guard", C.c_float), ("lod_min_radius_px", C.c_float),
+                ("time", C.c_float)]
 
 
 class GsFwdView(C.Structure):
@@ -52,12 +53,13 @@ class GsGaussians(C.Structure):
     _fields_ = [("n", C.c_int64), ("sh_degree", C.c_int32), ("sh_dtype", C.c_int32),
                 ("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p),
                 ("opacities", C.c_void_p), ("sh", C.c_void_p), ("active", C.c_void_p),
-                ("sh_bounds", C.c_void_p)]
+                ("sh_bounds", C.c_void_p), ("velocity", C.c_void_p), ("t_offset", C.c_void_p)]
 
 
 class GsGrads(C.Structure):
     _fields_ = [("means", C.c_void_p), ("log_scales", C.c_void_p), ("quats", C.c_void_p),
-                ("opacity_logits", C.c_void_p), ("sh", C.c_void_p)]
+                ("opacity_logits", C.c_void_p), ("sh", C.c_void_p), ("velocity", C.c_void_p),
+                ("t_offset", C.c_void_p)]
 
 
 class GsShAdam(C.Structure):
@@ -169,7 +171,16 @@ def camera_struct(cam) -> GsCamera:
         c.viewmat[i] = vm[i]
     c.znear, c.guard = float(cam.znear), float(cam.guard)
     c.lod_min_radius_px = float(getattr(cam, "lod_min_radius_px", 0.0))
+    c.time = float(getattr(cam, "time", 0.0))
     return c
+
+
+def grads_struct(grads: Dict[str, torch.Tensor]) -> GsGrads:
+    """fp32 gradient arrays by name; "velocity" and "t_offset" only with
+    moving Gaussians."""
+    return GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
+                   _ptr(grads["opacity_logits"]), _ptr(grads["sh"]), _ptr(grads.get("velocity")),
+                   _ptr(grads.get("t_offset")))
 
 
 def gaussians_struct(g: Dict[str, torch.Tensor], sh_degree: int, active: Optional[torch.Tensor] = None
@@ -191,6 +202,11 @@ def gaussians_struct(g: Dict[str, torch.Tensor], sh_degree: int, active: Optiona
         b = g["sh_bounds"]
         assert b.is_cuda and b.dtype == torch.float32 and b.is_contiguous()
         s.sh_bounds = b.data_ptr()
+    if g.get("velocity") is not None:
+        v, t = g["velocity"], g["t_offset"]
+        assert v.is_cuda and v.dtype == torch.float32 and v.is_contiguous() and tuple(v.shape) == (3, s.n)
+        assert t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and t.numel() == s.n
+        s.velocity, s.t_offset = v.data_ptr(), t.data_ptr()
     return s
 
 
@@ -326,8 +342,7 @@ def render_bwd_workspace_bytes(n: int, k_capacity: int) -> int:
 def render_bwd(gs: GsGaussians, cam: GsCamera, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg,
                final_T, n_contrib, dL_dimage, grads: Dict[str, torch.Tensor], workspace, stream=None):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
-    gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
-                 _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
+    gr = grads_struct(grads)
     _check(lib().gs_render_bwd(C.byref(gs), C.byref(cam), _ptr(splats), _ptr(vals), _ptr(tile_ranges),
                                _ptr(schedule), _ptr(bwd_index), int(k_capacity), C.cast(bgv, C.c_void_p), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
                                C.byref(gr), _ptr(workspace),
@@ -369,8 +384,7 @@ def project_bwd(gs: GsGaussians, cams, splats_list, g2_list, grads: Dict[str, to
     cam_arr = (GsCamera * max(nv, 1))(*cams)
     sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
     g2_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in g2_list])
-    gr = GsGrads(_ptr(grads["means"]), _ptr(grads["log_scales"]), _ptr(grads["quats"]),
-                 _ptr(grads["opacity_logits"]), _ptr(grads["sh"]))
+    gr = grads_struct(grads)
     _check(lib().gs_project_bwd(C.byref(gs), nv, cam_arr, sp_arr, g2_arr, C.byref(gr), _stream(stream)),
            "gs_project_bwd")
 

@@ -23,6 +23,7 @@ bool camera_ok(const gs_camera *c)
         if (!isfinite(c->viewmat[i])) return false;
     if (!isfinite(c->znear) || !finite_pos(c->guard)) return false;
     if (!isfinite(c->lod_min_radius_px) || c->lod_min_radius_px < 0.0f) return false;
+    if (!isfinite(c->time)) return false;
     return true;
 }
 
@@ -35,6 +36,7 @@ gs_status gaussians_ok(const gs_gaussians *g)
     if (g->n > 0 && (!g->means || !g->scales || !g->quats || !g->opacities || !g->sh))
         return GS_ERR_INVALID_ARG;
     if (g->n > 0 && g->sh_dtype == GS_SH_Q8 && !g->sh_bounds) return GS_ERR_INVALID_ARG;
+    if (g->n > 0 && (g->velocity != nullptr) != (g->t_offset != nullptr)) return GS_ERR_INVALID_ARG;
     return GS_OK;
 }
 
@@ -284,10 +286,10 @@ static gs_status screen_args_ok(const gs_camera *camera, int64_t n, const gs_spl
     return GS_OK;
 }
 
-static bool grads_ok(const gs_grads *grads, int64_t n)
+static bool grads_ok(const gs_grads *grads, int64_t n, bool motion)
 {
     return grads && (n == 0 || (grads->means && grads->log_scales && grads->quats && grads->opacity_logits &&
-                                grads->sh));
+                                grads->sh && (!motion || (grads->velocity && grads->t_offset))));
 }
 
 // The blend backward and the per-Gaussian sums of up to kMaxBlendViews views
@@ -347,7 +349,7 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     st = screen_args_ok(camera, n, splats, vals, tile_ranges, schedule, bwd_index, k_capacity, bg, final_T,
                         n_contrib, dL_dimage);
     if (st != GS_OK) return st;
-    if (!grads_ok(grads, n)) return GS_ERR_INVALID_ARG;
+    if (!grads_ok(grads, n, gaussians->velocity != nullptr)) return GS_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, k_capacity)) return GS_ERR_WORKSPACE;
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -439,7 +441,7 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const g
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
     const int64_t n = gaussians->n;
-    if (n_views < 0 || (n_views > 0 && (!cameras || !splats || !g2)) || !grads_ok(grads, n))
+    if (n_views < 0 || (n_views > 0 && (!cameras || !splats || !g2)) || !grads_ok(grads, n, gaussians->velocity != nullptr))
         return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;

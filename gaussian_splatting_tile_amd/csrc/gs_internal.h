@@ -74,6 +74,7 @@ struct Cam {
     float R[9];
     float t[3];
     float znear, guard, lod;
+    float time;                           // the view's time (moving Gaussians)
 };
 
 inline Cam make_cam(const gs_camera &c)
@@ -91,6 +92,7 @@ inline Cam make_cam(const gs_camera &c)
     k.znear = c.znear;
     k.guard = c.guard;
     k.lod = c.lod_min_radius_px;
+    k.time = c.time;
     return k;
 }
 

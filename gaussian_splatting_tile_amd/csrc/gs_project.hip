@@ -279,11 +279,25 @@ __device__ __forceinline__ void view_dir(const Cam &cam, float mx, float my, flo
     dx = dx / dn; dy = dy / dn; dz = dz / dn;
 }
 
-template <int DEG, typename TSH>
+// Moving Gaussians (a motion vector v and a time offset t_g each): in a view
+// at time tau the mean is mu + (tau - t_g) v, one fp32 rounding per
+// operation in that order (contraction is off in this file).  The backward
+// adds dL/dv = sum_views dt dL/dmu' and dL/dt_g = -v . sum_views dL/dmu'.
+struct Motion {
+    const float *v;               // [3][n]
+    const float *t;               // [n]
+    float *dv;                    // [3][n] (backward)
+    float *dt;                    // [n]    (backward)
+};
+
+__device__ __forceinline__ float displace(float mu, float dt, float v) { return mu + dt * v; }
+
+template <int DEG, typename TSH, bool kMotion>
 __global__ __launch_bounds__(kBlock) void project_kernel(
     int n, const float *__restrict__ means, const float *__restrict__ scales,
     const float *__restrict__ quats, const float *__restrict__ opac, const TSH *__restrict__ sh,
-    const float *__restrict__ sh_bounds, const uint8_t *__restrict__ active, const ProjBatch views)
+    const float *__restrict__ sh_bounds, const uint8_t *__restrict__ active, const Motion mo,
+    const ProjBatch views)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int g = blockIdx.x * kBlock + threadIdx.x;
@@ -292,7 +306,17 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     const float sx = scales[g], sy = scales[n + g], sz = scales[2 * n + g];
     const float qw = quats[g], qx = quats[n + g], qy = quats[2 * n + g], qz = quats[3 * n + g];
     const float o = opac[g];
-    const bool on = (active == nullptr || active[g] != 0) && all_finite(mx, my, mz, sx, sy, sz, qw, qx, qy, qz, o);
+    float vx = 0.0f, vy = 0.0f, vz = 0.0f, tg = 0.0f;
+    if constexpr (kMotion) {
+        vx = mo.v[g];
+        vy = mo.v[n + g];
+        vz = mo.v[2 * n + g];
+        tg = mo.t[g];
+    }
+    // with motion the mean's finiteness is that of each view's displaced mean
+    const bool on = (active == nullptr || active[g] != 0) &&
+                    all_finite(kMotion ? 0.0f : mx, kMotion ? 0.0f : my, kMotion ? 0.0f : mz, sx, sy, sz, qw, qx,
+                               qy, qz, o);
 
     // the views of the batch, parameters and SH coefficients read once (all
     // lanes load, g < n; a masked-out Gaussian's coefficients go unused, and
@@ -307,13 +331,21 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     Splat rec;
     rec.a = rec.b = rec.c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     bool vis = on;
+    float px = mx, py = my, pz = mz;
+    if constexpr (kMotion) {
+        const float dt = cam.time - tg;
+        px = displace(mx, dt, vx);
+        py = displace(my, dt, vy);
+        pz = displace(mz, dt, vz);
+        vis = vis && isfinite(px) && isfinite(py) && isfinite(pz);
+    }
     Geo G;
-    if (vis) vis = geometry(cam, mx, my, mz, sx, sy, sz, qw, qx, qy, qz, G);
+    if (vis) vis = geometry(cam, px, py, pz, sx, sy, sz, qw, qx, qy, qz, G);
     if (vis && cam.lod > 0.0f) {
         // distance-LOD gate: undilated 3-sigma pinhole radius below lod px
         float ccx, ccy, ccz;
         cam_centre(cam, ccx, ccy, ccz);
-        const float dx = mx - ccx, dy = my - ccy, dz = mz - ccz;
+        const float dx = px - ccx, dy = py - ccy, dz = pz - ccz;
         float d2 = dx * dx;  d2 = d2 + dy * dy;  d2 = d2 + dz * dz;
         const float dist = sqrtf(d2);
         const float smax = fmaxf(fmaxf(sx, sy), sz);
@@ -335,7 +367,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
         if (r.x0 < r.x1 && r.y0 < r.y1) {
             // colour: SH at the unit view direction (read only for survivors)
             float dx, dy, dz, dn;
-            view_dir(cam, mx, my, mz, dx, dy, dz, dn);
+            view_dir(cam, px, py, pz, dx, dy, dz, dn);
             float Y[K];
             sh_basis<DEG>(dx, dy, dz, Y);
             float col[3];
@@ -533,11 +565,11 @@ __device__ __forceinline__ int compact_range(long long g_begin, long long g_end,
 
 // One round of the colour part: lane (gl, ch) takes Gaussian g (valid lanes
 // only; every lane of the wave calls this, for the cross-lane sums).
-template <int DEG, typename TSH>
+template <int DEG, typename TSH, bool kMotion>
 __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int ch, const float *__restrict__ means,
                                                 const TSH *__restrict__ sh, const float *__restrict__ sh_bounds,
-                                                const ViewBatch &views, float *__restrict__ d_means,
-                                                float *__restrict__ d_sh)
+                                                const Motion &mo, const ViewBatch &views,
+                                                float *__restrict__ d_means, float *__restrict__ d_sh)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int lane = threadIdx.x & 63;
@@ -555,12 +587,21 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
         kv[j] = valid ? ld_sh(shr, sh_bounds, (size_t)(j * 3 + ch), n, g, g >> 8) : 0.0f;
         acc[j] = 0.0f;
     }
+    float vx = 0.0f, vy = 0.0f, vz = 0.0f, tg = 0.0f;
     if (valid) {
         mx = means[g];
         my = means[n + g];
         mz = means[2 * n + g];
+        if constexpr (kMotion) {
+            vx = mo.v[g];
+            vy = mo.v[n + g];
+            vz = mo.v[2 * n + g];
+            tg = mo.t[g];
+        }
     }
     float dm[3] = {0.0f, 0.0f, 0.0f};
+    float dmv[3] = {0.0f, 0.0f, 0.0f};          // sum over views of dt dL/dmu'
+
     bool visible = false;
     // the next view's radius and gradient are loaded one view ahead (a
     // culled Gaussian's gradient row holds no value and is not used)
@@ -581,8 +622,15 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
         if (!valid || rad == 0) continue;
         visible = true;
         const Cam &cam = views.cam[v];
+        float px = mx, py = my, pz = mz, dtv = 0.0f;
+        if constexpr (kMotion) {
+            dtv = cam.time - tg;
+            px = displace(mx, dtv, vx);
+            py = displace(my, dtv, vy);
+            pz = displace(mz, dtv, vz);
+        }
         float dx, dy, dz, dn;
-        view_dir(cam, mx, my, mz, dx, dy, dz, dn);
+        view_dir(cam, px, py, pz, dx, dy, dz, dn);
         float Y[K];
         sh_basis<DEG>(dx, dy, dz, Y);
         float sum = 0.0f;
@@ -598,16 +646,28 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
         dd[1] *= gr;
         dd[2] *= gr;
         const float ddot = dx * dd[0] + dy * dd[1] + dz * dd[2];
-        dm[0] += (dd[0] - dx * ddot) / dn;
-        dm[1] += (dd[1] - dy * ddot) / dn;
-        dm[2] += (dd[2] - dz * ddot) / dn;
+        const float c0 = (dd[0] - dx * ddot) / dn;
+        const float c1 = (dd[1] - dy * ddot) / dn;
+        const float c2 = (dd[2] - dz * ddot) / dn;
+        dm[0] += c0;
+        dm[1] += c1;
+        dm[2] += c2;
+        if constexpr (kMotion) {
+            dmv[0] += dtv * c0;
+            dmv[1] += dtv * c1;
+            dmv[2] += dtv * c2;
+        }
     }
     // channel lanes 3 gl + 1 and 3 gl + 2 hand their mean shares to 3 gl
-    float tot[3];
+    float tot[3], totv[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 3; j++) {
         const float a1 = __shfl(dm[j], lane + 1, 64), a2 = __shfl(dm[j], lane + 2, 64);
         tot[j] = (dm[j] + a1) + a2;
+        if constexpr (kMotion) {
+            const float b1 = __shfl(dmv[j], lane + 1, 64), b2 = __shfl(dmv[j], lane + 2, 64);
+            totv[j] = (dmv[j] + b1) + b2;
+        }
     }
     if (!visible) return;
 #pragma unroll
@@ -618,19 +678,24 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
     if (ch == 0) {
 #pragma unroll
         for (int j = 0; j < 3; j++) d_means[j * n + g] += tot[j];
+        if constexpr (kMotion) {
+#pragma unroll
+            for (int j = 0; j < 3; j++) mo.dv[j * n + g] += totv[j];
+            mo.dt[g] -= (vx * tot[0] + vy * tot[1]) + vz * tot[2];
+        }
     }
 }
 
 // Without a mask (COMPACT false) wave w takes Gaussians 21 w .. 21 w + 20 and
 // Gaussians culled in every view drop out lane by lane; with one, each wave
 // compacts its range of per_wave Gaussians first and takes rounds of 21.
-template <int DEG, typename TSH, bool COMPACT>
+template <int DEG, typename TSH, bool COMPACT, bool kMotion>
 __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int per_wave,
                                                                    const float *__restrict__ means,
                                                                    const TSH *__restrict__ sh,
                                                                    const float *__restrict__ sh_bounds,
                                                                    const uint8_t *__restrict__ active,
-                                                                   const ViewBatch views,
+                                                                   const Motion mo, const ViewBatch views,
                                                                    float *__restrict__ d_means,
                                                                    float *__restrict__ d_sh)
 {
@@ -645,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int pe
             const int idx = r0 + gl;
             const bool valid = gl < kColourPerWave && idx < cnt;
             const int g = valid ? (int)s_list[wv][idx] : 0;
-            colour_backward<DEG, TSH>(n, g, valid, ch, means, sh, sh_bounds, views, d_means, d_sh);
+            colour_backward<DEG, TSH, kMotion>(n, g, valid, ch, means, sh, sh_bounds, mo, views, d_means, d_sh);
         }
     } else {
         const long long wave = (long long)blockIdx.x * (kBlock / 64) + wv;
@@ -657,17 +722,27 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int pe
             for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][gg].a.w) != 0);
             valid = any;
         }
-        colour_backward<DEG, TSH>(n, valid ? (int)gg : 0, valid, ch, means, sh, sh_bounds, views, d_means, d_sh);
+        colour_backward<DEG, TSH, kMotion>(n, valid ? (int)gg : 0, valid, ch, means, sh, sh_bounds, mo, views,
+                                           d_means, d_sh);
     }
 }
 
 // The geometry part for one Gaussian (visible in at least one view).
+template <bool kMotion>
 __device__ __forceinline__ void geom_backward(
     int n, int g, const float *__restrict__ means, const float *__restrict__ scales, const float *__restrict__ quats,
-    const float *__restrict__ opac, const ViewBatch &views, float *__restrict__ d_means,
+    const float *__restrict__ opac, const Motion &mo, const ViewBatch &views, float *__restrict__ d_means,
     float *__restrict__ d_log_scales, float *__restrict__ d_quats, float *__restrict__ d_logits)
 {
     const float mx0 = means[g], my0 = means[n + g], mz0 = means[2 * n + g];
+    float vx = 0.0f, vy = 0.0f, vz = 0.0f, tg = 0.0f;
+    if constexpr (kMotion) {
+        vx = mo.v[g];
+        vy = mo.v[n + g];
+        vz = mo.v[2 * n + g];
+        tg = mo.t[g];
+    }
+    float acc_vel[3] = {0.0f, 0.0f, 0.0f};
     const float s0 = scales[g], s1 = scales[n + g], s2 = scales[2 * n + g];
     const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];
     const float o = opac[g];
@@ -707,6 +782,13 @@ __device__ __forceinline__ void geom_backward(
     asm volatile("" : "+v"(mx), "+v"(my), "+v"(mz), "+v"(qw), "+v"(qx), "+v"(qy), "+v"(qz));
     asm volatile("" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]));
     const Cam &cam = views.cam[v];
+    float dtv = 0.0f;
+    if constexpr (kMotion) {
+        dtv = cam.time - tg;
+        mx = displace(mx, dtv, vx);
+        my = displace(my, dtv, vy);
+        mz = displace(mz, dtv, vz);
+    }
 
     // The compositing pass worked in the principal frame V of the record's
     // conic Qr: mean gradient V (g0, g1), covariance gradient V W V^T.
@@ -823,7 +905,11 @@ __device__ __forceinline__ void geom_backward(
     const double qh[4] = {w, a, b, c};
 
 #pragma unroll
-    for (int j = 0; j < 3; j++) acc_mean[j] += (float)(R[j] * dpx + R[3 + j] * dpy + R[6 + j] * dpz);
+    for (int j = 0; j < 3; j++) {
+        const float c = (float)(R[j] * dpx + R[3 + j] * dpy + R[6 + j] * dpz);
+        acc_mean[j] += c;
+        if constexpr (kMotion) acc_vel[j] += dtv * c;
+    }
 #pragma unroll
     for (int r = 0; r < 3; r++) acc_ls[r] += (float)((double)s[r] * ds[r]);
 #pragma unroll
@@ -833,6 +919,11 @@ __device__ __forceinline__ void geom_backward(
     if (!touched) return;
 #pragma unroll
     for (int j = 0; j < 3; j++) d_means[j * n + g] += acc_mean[j];
+    if constexpr (kMotion) {
+#pragma unroll
+        for (int j = 0; j < 3; j++) mo.dv[j * n + g] += acc_vel[j];
+        mo.dt[g] -= (vx * acc_mean[0] + vy * acc_mean[1]) + vz * acc_mean[2];
+    }
 #pragma unroll
     for (int j = 0; j < 3; j++) d_log_scales[j * n + g] += acc_ls[j];
 #pragma unroll
@@ -840,11 +931,11 @@ __device__ __forceinline__ void geom_backward(
     d_logits[g] += acc_logit;
 }
 
-template <bool COMPACT>
+template <bool COMPACT, bool kMotion>
 __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
     int n, int per_wave, const float *__restrict__ means, const float *__restrict__ scales,
     const float *__restrict__ quats, const float *__restrict__ opac, const uint8_t *__restrict__ active,
-    const ViewBatch views, float *__restrict__ d_means, float *__restrict__ d_log_scales,
+    const Motion mo, const ViewBatch views, float *__restrict__ d_means, float *__restrict__ d_log_scales,
     float *__restrict__ d_quats, float *__restrict__ d_logits)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -856,8 +947,8 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
         for (int r0 = 0; r0 < cnt; r0 += 64) {
             const int idx = r0 + lane;
             if (idx < cnt)
-                geom_backward(n, (int)s_list[wv][idx], means, scales, quats, opac, views, d_means, d_log_scales,
-                              d_quats, d_logits);
+                geom_backward<kMotion>(n, (int)s_list[wv][idx], means, scales, quats, opac, mo, views, d_means,
+                                       d_log_scales, d_quats, d_logits);
         }
     } else {
         const long long g = (long long)blockIdx.x * kBlock + threadIdx.x;
@@ -865,30 +956,52 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
         bool any = false;   // culled in every view: nothing to read or write
         for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
         if (!any) return;
-        geom_backward(n, (int)g, means, scales, quats, opac, views, d_means, d_log_scales, d_quats, d_logits);
+        geom_backward<kMotion>(n, (int)g, means, scales, quats, opac, mo, views, d_means, d_log_scales, d_quats,
+                               d_logits);
     }
 }
 
 
-template <int DEG, typename TSH>
-void launch_project_t(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
+Motion motion_of(const gs_gaussians &g, const gs_grads *out)
+{
+    Motion m;
+    m.v = g.velocity;
+    m.t = g.t_offset;
+    m.dv = out ? out->velocity : nullptr;
+    m.dt = out ? out->t_offset : nullptr;
+    return m;
+}
+
+template <int DEG, typename TSH, bool kMotion>
+void launch_project_m(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
 {
     const int n = (int)g.n;
-    project_kernel<DEG, TSH><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
-        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.sh_bounds, g.active, views);
+    project_kernel<DEG, TSH, kMotion><<<(n + kBlock - 1) / kBlock, kBlock, 0, s>>>(
+        n, g.means, g.scales, g.quats, g.opacities, (const TSH *)g.sh, g.sh_bounds, g.active, motion_of(g, nullptr),
+        views);
 }
 
 template <int DEG, typename TSH>
-void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
+void launch_project_t(const gs_gaussians &g, const ProjBatch &views, hipStream_t s)
+{
+    if (g.velocity)
+        launch_project_m<DEG, TSH, true>(g, views, s);
+    else
+        launch_project_m<DEG, TSH, false>(g, views, s);
+}
+
+template <int DEG, typename TSH, bool kMotion>
+void launch_project_bwd_m(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
 {
     const int n = (int)g.n;
+    const Motion mo = motion_of(g, &out);
     if (g.active == nullptr) {
         const long long colour_waves = (n + kColourPerWave - 1) / kColourPerWave;
-        project_bwd_color_kernel<DEG, TSH, false>
+        project_bwd_color_kernel<DEG, TSH, false, kMotion>
             <<<(unsigned)((colour_waves + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, s>>>(
-                n, 0, g.means, (const TSH *)g.sh, g.sh_bounds, nullptr, views, out.means, out.sh);
-        project_bwd_geom_kernel<false><<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(
-            n, 0, g.means, g.scales, g.quats, g.opacities, nullptr, views, out.means, out.log_scales, out.quats,
+                n, 0, g.means, (const TSH *)g.sh, g.sh_bounds, nullptr, mo, views, out.means, out.sh);
+        project_bwd_geom_kernel<false, kMotion><<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, s>>>(
+            n, 0, g.means, g.scales, g.quats, g.opacities, nullptr, mo, views, out.means, out.log_scales, out.quats,
             out.opacity_logits);
         return;
     }
@@ -900,12 +1013,20 @@ void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const g
     const int per_wave = (int)(64 * m);
     const long long waves = (n + per_wave - 1) / per_wave;
     const unsigned blocks = (unsigned)((waves + kBlock / 64 - 1) / (kBlock / 64));
-    project_bwd_color_kernel<DEG, TSH, true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, (const TSH *)g.sh,
-                                                                       g.sh_bounds, g.active, views, out.means,
-                                                                       out.sh);
-    project_bwd_geom_kernel<true><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, g.scales, g.quats, g.opacities,
-                                                            g.active, views, out.means, out.log_scales, out.quats,
-                                                            out.opacity_logits);
+    project_bwd_color_kernel<DEG, TSH, true, kMotion><<<blocks, kBlock, 0, s>>>(
+        n, per_wave, g.means, (const TSH *)g.sh, g.sh_bounds, g.active, mo, views, out.means, out.sh);
+    project_bwd_geom_kernel<true, kMotion><<<blocks, kBlock, 0, s>>>(n, per_wave, g.means, g.scales, g.quats,
+                                                                     g.opacities, g.active, mo, views, out.means,
+                                                                     out.log_scales, out.quats, out.opacity_logits);
+}
+
+template <int DEG, typename TSH>
+void launch_project_bwd_t(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out, hipStream_t s)
+{
+    if (g.velocity)
+        launch_project_bwd_m<DEG, TSH, true>(g, views, out, s);
+    else
+        launch_project_bwd_m<DEG, TSH, false>(g, views, out, s);
 }
 
 template <typename TSH>

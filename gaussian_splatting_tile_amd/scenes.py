@@ -50,6 +50,7 @@ class Camera:
     znear: float = 0.2
     guard: float = 1.3
     lod_min_radius_px: float = 0.0   # 0 disables the distance-LOD gate
+    time: float = 0.0                # the view's time (for moving Gaussians)
 
     @property
     def tiles_x(self) -> int:
@@ -80,6 +81,8 @@ class Scene:
     importance: Optional[np.ndarray] = None  # f32 [N]
     keep_fraction: float = 1.0
     upstream_seed: Optional[int] = None      # seed of dL/dimage draws
+    velocity: Optional[np.ndarray] = None    # f32 [3][N] motion vectors (moving scenes)
+    t_offset: Optional[np.ndarray] = None    # f32 [N]    time offsets t_g
 
     @property
     def n(self) -> int:
@@ -323,3 +326,19 @@ def adam_inputs(seed: int, n: int, rows: int, state: str = "q8", value_dtype=np.
     out["m_bounds"] = mb
     out["s_bounds"] = sb
     return out
+
+
+# ---------------------------------------------------------------------------
+def with_motion(sc: Scene, seed: int, speed: float = 0.5, span: float = 1.0) -> Scene:
+    """The scene with a motion vector and a time offset per Gaussian (the
+    VisionTech page's 4D record): v ~ N(0, speed^2) per axis in scene units
+    per unit time, t_g ~ U(0, span), and view i of V at time span * i / (V - 1)
+    (the views sweep the time window)."""
+    import dataclasses
+    rng = np.random.default_rng([seed, sc.n, 4])
+    vel = (rng.standard_normal((3, sc.n), dtype=np.float32) * np.float32(speed)).astype(np.float32)
+    t0 = _uniform(rng, 0.0, span, sc.n)
+    V = len(sc.cameras)
+    cams = [dataclasses.replace(c, time=float(np.float32(span * i / max(1, V - 1))))
+            for i, c in enumerate(sc.cameras)]
+    return dataclasses.replace(sc, velocity=vel, t_offset=t0, cameras=cams, name=sc.name + "_motion")

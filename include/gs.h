@@ -87,6 +87,9 @@ typedef struct gs_camera {
     float lod_min_radius_px;    /* distance-LOD gate: cull when the undilated
                                    3-sigma radius 3 max(fx,fy) max(s) / |mu-c|
                                    is below this many pixels; 0 = off          */
+    float time;                 /* the view's time tau: Gaussians with motion
+                                   are drawn at mu + (tau - t_g) v (ignored
+                                   when gs_gaussians.velocity is NULL)         */
 } gs_camera;
 
 /* The Gaussians (device memory, structure of arrays). */
@@ -104,7 +107,19 @@ typedef struct gs_gaussians {
     const uint8_t *active;      /* [n] per-Gaussian keep mask, or NULL = all   */
     const float *sh_bounds;     /* GS_SH_Q8 only: [K*3][ceil(n/256)][2] (lo, hi)
                                    of every 256-Gaussian block of an SH row     */
+    const float *velocity;      /* [3][n] motion vectors v, or NULL: static     */
+    const float *t_offset;      /* [n] time offsets t_g (required with velocity)*/
 } gs_gaussians;
+
+/* Motion (the VisionTech page's 4D Gaussian record: a time offset and a
+ * motion vector per Gaussian).  With velocity set, every step of the path
+ * sees Gaussian g in view c at the displaced mean
+ *     dt = c.time - t_g,   mu'_i = mu_i + dt * v_i,
+ * each an fp32 operation in that order (part of the op-order contract), and
+ * a Gaussian whose displaced mean is not finite is culled in that view.  The
+ * backward adds dL/dv = sum over views of dt dL/dmu' and dL/dt_g = -v . sum
+ * over views of dL/dmu' to gs_grads.velocity and gs_grads.t_offset; dL/dmu
+ * is dL/dmu'. */
 
 /* 8-bit linear block quantization of SH storage (the Spirula Studio page's
  * description of its block-quantized tensors: 256 consecutive units share a
@@ -190,6 +205,9 @@ typedef struct gs_grads {
     float *quats;               /* [4][n]  through the normalisation            */
     float *opacity_logits;      /* [n]     d/d logit = o (1 - o) d/do           */
     float *sh;                  /* [K][3][n] always fp32, also for half SH      */
+    float *velocity;            /* [3][n] with motion (required then), else
+                                   unused                                       */
+    float *t_offset;            /* [n]    with motion (required then)           */
 } gs_grads;
 
 /* ---------------------------------------------------------------------- */

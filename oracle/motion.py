@@ -30,9 +30,10 @@ def displaced_means(means, velocity, t_offset, time, precision: str = "f32") -> 
         dt = float(time) - np.asarray(t_offset, dtype=np.float64)
         return np.asarray(means, dtype=np.float64) + dt[None, :] * np.asarray(velocity, dtype=np.float64)
     f = np.float32
-    dt = (f(time) - np.asarray(t_offset, dtype=f)).astype(f)
-    step = (dt[None, :] * np.asarray(velocity, dtype=f)).astype(f)
-    return (np.asarray(means, dtype=f) + step).astype(f)
+    with np.errstate(invalid="ignore", over="ignore"):      # non-finite motion: culled downstream
+        dt = (f(time) - np.asarray(t_offset, dtype=f)).astype(f)
+        step = (dt[None, :] * np.asarray(velocity, dtype=f)).astype(f)
+        return (np.asarray(means, dtype=f) + step).astype(f)
 
 
 def motion_grads(d_means_displaced, velocity, t_offset, time):

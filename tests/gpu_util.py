@@ -28,6 +28,8 @@ def device_gaussians(sc, sh=None, device="cuda"):
         g["sh"], g["sh_bounds"] = f(sh[0]), f(sh[1])
     else:
         g["sh"] = f(sh)
+    if getattr(sc, "velocity", None) is not None:
+        g["velocity"], g["t_offset"] = f(sc.velocity), f(sc.t_offset)
     return g
 
 

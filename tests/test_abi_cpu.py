@@ -97,6 +97,20 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_project(C.byref(gq), C.byref(camq), 0x1000, None) == B.GS_ERR_INVALID_ARG   # no bounds
     gq.sh_dtype = 3
     assert L.gs_project(C.byref(gq), C.byref(camq), 0x1000, None) == B.GS_ERR_UNSUPPORTED
+    # moving Gaussians: velocity and time offsets come together, the view's
+    # time must be finite, and the backward needs both gradient arrays
+    gm = B.GsGaussians()
+    gm.n, gm.sh_degree, gm.sh_dtype = 5, 0, B.GS_SH_F32
+    gm.means = gm.scales = gm.quats = gm.opacities = gm.sh = 0x1000
+    gm.velocity = 0x1000
+    assert L.gs_project(C.byref(gm), C.byref(camq), 0x1000, None) == B.GS_ERR_INVALID_ARG
+    gm.t_offset = 0x1000
+    camq.time = float("nan")
+    assert L.gs_project(C.byref(gm), C.byref(camq), 0x1000, None) == B.GS_ERR_INVALID_ARG
+    camq.time = 0.5
+    grm = B.GsGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, None)
+    sp = (C.c_void_p * 1)(0x1000)
+    assert L.gs_project_bwd(C.byref(gm), 1, C.byref(camq), sp, sp, C.byref(grm), None) == B.GS_ERR_INVALID_ARG
     # batched sort: every view is checked before anything runs
     views = (B.GsSortView * 2)()
     assert L.gs_bin_sort_views(-1, views, None) == B.GS_ERR_INVALID_ARG
