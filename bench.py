@@ -358,7 +358,9 @@ def main():
                           "units": adam["units"], "ms": round(per_call["sh_adam"], 4),
                           "bytes_per_unit": adam["bytes_per_unit"], "bound": "hbm",
                           "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                          "traffic": (measured_adam_traffic(args.sh_adam) if args.workload == "scene_5m"
+                                      else None)}
     # the oracle is timed beside the default workload only (a 10M / 4K view
     # takes it minutes)
     if not args.no_cpu_baseline and args.workload == "scene_1m":
@@ -368,6 +370,25 @@ def main():
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "traffic_scene_1m_sh3_1080p.md")
+ADAM_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "sh_adam_scene_5m.md")
+
+
+def measured_adam_traffic(state):
+    """HBM bytes per launch of the fused SH Adam kernel at 5M x 45 units
+    from the rocprofv3 counter summary, or None once gs_adam.hip differs from
+    the source the counters were taken on."""
+    import hashlib
+    try:
+        lines = open(ADAM_PROFILE).read().splitlines()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in lines if l.startswith(("traffic_bytes_per_launch", "source_sha256")))
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gaussian_splatting_tile_amd", "csrc",
+                       "gs_adam.hip")
+    if fields.get("source_sha256 (gs_adam.hip)", "").strip() != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    v = fields.get(f"traffic_bytes_per_launch {state}")
+    return int(v) if v else None
 TRAFFIC_SOURCES = ("gaussian_splatting_tile_amd/csrc/gs_render.hip", "gaussian_splatting_tile_amd/csrc/gs_internal.h")
 
 

@@ -441,8 +441,8 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const g
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
     const int64_t n = gaussians->n;
-    if (n_views < 0 || (n_views > 0 && (!cameras || !splats || !g2)) || !grads_ok(grads, n, gaussians->velocity != nullptr))
-        return GS_ERR_INVALID_ARG;
+    if (n_views < 0 || (n_views > 0 && (!cameras || !splats || !g2))) return GS_ERR_INVALID_ARG;
+    if (!grads_ok(grads, n, gaussians->velocity != nullptr)) return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
         if (n > 0 && (!splats[v] || !g2[v])) return GS_ERR_INVALID_ARG;
