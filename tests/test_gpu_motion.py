@@ -170,3 +170,45 @@ def test_moving_scene_1m_1080p_records_and_bins():
     mp, op, ob, oo = _oracle_view(sc, v)
     compare_records(splats_np(buf), op, "motion 1M")
     compare_bins(buf, K, ob, "motion 1M")
+
+
+@pytest.mark.parametrize("sh_mode", ["f16", "q8"])
+def test_moving_masked_scene_with_stored_sh_forward_and_backward(sh_mode):
+    """Motion together with an importance mask (the compacting projection
+    backward) and 16-bit or 8-bit SH storage, over two views at different
+    times: records and bins bit-exact, summed gradients within 1e-3."""
+    sc = scenes.with_motion(scenes.scene_like(seed=25, n=40_000, width=480, height=272, f=350.0, n_views=2,
+                                              sh_fp16=True), seed=125)
+    rng = np.random.default_rng(26)
+    mask = (rng.random(sc.n) < 0.4).astype(np.uint8)
+    if sh_mode == "q8":
+        codes, bounds = oracle.sh_quantize8(sc.sh)
+        sh_dev, sh_ref = (codes, bounds), oracle.sh_dequantize8(codes, bounds)
+    else:
+        sh_dev, sh_ref = None, sc.sh_decoded()
+    grads = _zero_grads(sc)
+    ref, near = None, np.zeros(sc.n, bool)
+    for v in range(2):
+        cam = sc.cameras[v]
+        say(f"[gpu] motion + mask + {sh_mode} SH, view {v} at time {cam.time}")
+        mp = M.displaced_means(sc.means, sc.velocity, sc.t_offset, cam.time)
+        op = oracle.project(mp, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sh_ref, cam, active=mask)
+        ob = oracle.bin_sort(op, cam)
+        oo = oracle.render(op, ob, cam)
+        buf, K = run_view(sc, v, active=mask, sh=sh_dev)
+        compare_records(splats_np(buf), op, f"motion {sh_mode} view {v}")
+        compare_bins(buf, K, ob, f"motion {sh_mode} view {v}")
+        G = _upstream(cam, 400 + v).astype(np.float64)
+        G[:, (oo["events"] > 0) | (oo["capflag"] > 0)] = 0.0
+        g2 = oracle.render_bwd(op, ob, cam, G)
+        r = oracle.project_bwd(mp, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sh_ref, cam, op, g2)
+        r["velocity"], r["t_offset"] = M.motion_grads(r["means"], sc.velocity, sc.t_offset, cam.time)
+        ref = r if ref is None else {k: ref[k] + r[k] for k in NAMES}
+        near |= np.abs(op["rgb_raw"]).min(axis=0) < 1e-5
+        g, act, gs = buf._keep
+        buf.backward(gs, torch.from_numpy(np.ascontiguousarray(G.astype(np.float32))).cuda(), grads,
+                     buf.backward_workspace())
+        torch.cuda.synchronize()
+    gpu = {k: t.cpu().numpy().astype(np.float64) for k, t in grads.items()}
+    assert np.all(gpu["velocity"][:, mask == 0] == 0) and np.all(gpu["t_offset"][mask == 0] == 0)
+    _compare(gpu, ref, near, f"motion + mask + {sh_mode}")
