@@ -192,10 +192,19 @@ __device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, u
 // Stage the fetched records of one batch into LDS with their strip masks
 // (and, with kWeight, their Gaussians), dropping those that cannot reach any
 // pixel of the tile; returns the number kept, in order.
+// One record staged for the forward blend.  The whole wave reads the same
+// record at once (LDS broadcast); keeping its fields together lets one
+// address serve all five reads, at immediate offsets.
+struct FwdRec {
+    double2 uv;                   // mean
+    double2 q01, q23;             // the exponent's terms, log2 o
+    float4 rgb;                   // colour, opacity
+    uint4 meta;                   // list position, strip mask, Gaussian, -
+};
+static_assert(sizeof(FwdRec) == 80, "five 16-byte LDS reads per record");
+
 template <bool kWeight>
-__device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, double2 *s_uv,
-                                             double4 *s_q, float4 *s_rgb, uint32_t *s_pos, uint32_t *s_strips,
-                                             uint32_t *s_g)
+__device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, FwdRec *s_rec)
 {
     const int lane = threadIdx.x;
     const uint32_t strips = f.valid ? strip_mask(f.a.x, f.a.y, f.b, x0, y0) : 0u;
@@ -208,10 +217,16 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
         s.a = f.a;
         s.b = f.b;
         s.c = f.c;
-        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
-        s_pos[slot] = f.m - start;
-        s_strips[slot] = strips;
-        if (kWeight) s_g[slot] = f.g;
+        double2 uv;
+        double4 q;
+        float4 rgb;
+        stage_record(s, uv, q, rgb);
+        FwdRec &r = s_rec[slot];
+        r.uv = uv;
+        r.q01 = make_double2(q.x, q.y);
+        r.q23 = make_double2(q.z, q.w);
+        r.rgb = rgb;
+        r.meta = make_uint4(f.m - start, strips, kWeight ? f.g : 0u, 0u);
     }
     return __popcll(mask);
 }
@@ -310,12 +325,7 @@ __device__ __forceinline__ uint32_t live_strips(const float T[4])
 template <bool kWeight>
 __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch)
 {
-    __shared__ double2 s_uv[kBatch];
-    __shared__ double4 s_q[kBatch];
-    __shared__ float4 s_rgb[kBatch];
-    __shared__ uint32_t s_pos[kBatch];
-    __shared__ uint32_t s_strips[kBatch];
-    __shared__ uint32_t s_g[kWeight ? kBatch : 1];
+    __shared__ FwdRec s_rec[kBatch];
 
     const int lane = threadIdx.x;
     const int n_items = batch.count * batch.max_tiles;
@@ -368,8 +378,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             uint32_t live = live_strips(T);
             if (live == 0u) break;
-            const int nb = stage_fetched<kWeight>(cur, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos,
-                                                  s_strips, s_g);
+            const int nb = stage_fetched<kWeight>(cur, start, tx * kTile, ty * kTile, s_rec);
             cur.m = next_m;
             cur.valid = next_valid;
             fetch_record(splats, next_g, next_valid, cur);
@@ -378,13 +387,16 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
             next_g = next_valid ? vals[next_m] : 0u;
             __syncthreads();
             for (int k = 0; k < nb; k++) {
-                const double2 uv = s_uv[k];
-                const double4 q = s_q[k];
-                const float4 rgb = s_rgb[k];
-                const uint32_t pos = s_pos[k] + 1u;
+                const FwdRec &R = s_rec[k];
+                const double2 uv = R.uv;
+                const double2 q01 = R.q01, q23 = R.q23;
+                const double4 q = make_double4(q01.x, q01.y, q23.x, q23.y);
+                const float4 rgb = R.rgb;
+                const uint4 meta = R.meta;
+                const uint32_t pos = meta.x + 1u;
                 // wave-uniform: the branches below are scalar; a strip whose
                 // pixels have all stopped is skipped too
-                const uint32_t strips = __builtin_amdgcn_readfirstlane(s_strips[k]) & live;
+                const uint32_t strips = __builtin_amdgcn_readfirstlane(meta.y) & live;
                 const ColTerms ct = col_terms(uv, q, px);
                 const double dy0 = uv.y - py0;
                 float wsum = 0.0f;
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                 }
                 if (kWeight && V.weight != nullptr && __ballot(wsum > 0.0f) != 0ull) {
                     wsum = wave_sum(wsum);
-                    if (lane == 0) atomicAdd(V.weight + s_g[k], wsum);
+                    if (lane == 0) atomicAdd(V.weight + meta.z, wsum);
                 }
                 if ((k & 7) == 7) {
                     live = live_strips(T);
