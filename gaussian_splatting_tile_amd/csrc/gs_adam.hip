@@ -285,9 +285,11 @@ __global__ __launch_bounds__(kAdamThreads) void adam_q8_kernel(AdamArgs a)
     const float mscale = md > 0.0f ? 255.0f * __builtin_amdgcn_rcpf(md) : 0.0f;
     const float sscale = sd > 0.0f ? 255.0f * __builtin_amdgcn_rcpf(sd) : 0.0f;
 
-    if (lane == 0) {
-        *reinterpret_cast<float2 *>(a.mb + bi) = make_float2(mlo1, mhi1);
-        *reinterpret_cast<float2 *>(a.vb + bi) = make_float2(slo1, shi1);
+    if (lane == 0) {                              // bounds need only 4-byte alignment
+        a.mb[bi] = mlo1;
+        a.mb[bi + 1] = mhi1;
+        a.vb[bi] = slo1;
+        a.vb[bi + 1] = shi1;
     }
     if (kVec) {
         const int u = u0 + 4 * lane;

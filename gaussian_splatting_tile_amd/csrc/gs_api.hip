@@ -14,6 +14,9 @@ constexpr int32_t kVersion = 1;
 
 bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
 
+// Splat records and workspaces are read with 16-byte vector accesses.
+bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 bool camera_ok(const gs_camera *c)
 {
     if (!c) return false;
@@ -66,7 +69,7 @@ gs_status gs_project(const gs_gaussians *gaussians, const gs_camera *camera, gs_
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
     if (!camera_ok(camera)) return GS_ERR_INVALID_ARG;
-    if (gaussians->n > 0 && !splats) return GS_ERR_INVALID_ARG;
+    if ((gaussians->n > 0 && !splats) || !al16(splats)) return GS_ERR_INVALID_ARG;
     ProjBatch b;
     b.count = 1;
     b.cam[0] = make_cam(*camera);
@@ -82,7 +85,7 @@ gs_status gs_project_views(const gs_gaussians *gaussians, int32_t n_views, const
     if (n_views < 0 || (n_views > 0 && (!cameras || !splats))) return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
-        if (gaussians->n > 0 && !splats[v]) return GS_ERR_INVALID_ARG;
+        if ((gaussians->n > 0 && !splats[v]) || !al16(splats[v])) return GS_ERR_INVALID_ARG;
     }
     for (int v0 = 0; v0 < n_views; v0 += kMaxProjViews) {
         ProjBatch b;
@@ -125,7 +128,7 @@ static gs_status check_sort_view(const gs_sort_view &v)
     if (v.n < 0 || v.n > INT32_MAX || v.k_capacity < 0 || v.k_capacity >= (int64_t)UINT32_MAX)
         return GS_ERR_INVALID_ARG;
     if (!camera_ok(&v.camera) || !v.tile_ranges || !v.schedule || !v.k_total) return GS_ERR_INVALID_ARG;
-    if (v.n > 0 && !v.splats) return GS_ERR_INVALID_ARG;
+    if ((v.n > 0 && !v.splats) || !al16(v.splats) || !al16(v.workspace)) return GS_ERR_INVALID_ARG;
     if (v.k_capacity > 0 && !v.vals) return GS_ERR_INVALID_ARG;
     const Cam cam = make_cam(v.camera);
     const size_t need = bin_sort_workspace(v.n, v.k_capacity, cam.tiles_x * cam.tiles_y);
@@ -193,7 +196,8 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
                         uint32_t *schedule, const gs_camera *camera, const float *bg, float *image,
                         float *final_T, uint32_t *n_contrib, void *stream)
 {
-    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !image || !final_T || !n_contrib)
+    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !image || !final_T || !n_contrib ||
+        !al16(splats))
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
@@ -223,7 +227,8 @@ gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views, const f
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         const gs_fwd_view &w = views[v];
-        if (!camera_ok(&w.camera) || !w.tile_ranges || !w.schedule || !w.image || !w.final_T || !w.n_contrib)
+        if (!camera_ok(&w.camera) || !w.tile_ranges || !w.schedule || !w.image || !w.final_T || !w.n_contrib ||
+            !al16(w.splats))
             return GS_ERR_INVALID_ARG;
     }
     for (int v0 = 0; v0 < n_views; v0 += kMaxBlendViews) {
@@ -281,7 +286,7 @@ static gs_status screen_args_ok(const gs_camera *camera, int64_t n, const gs_spl
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
-    if (n > 0 && (!splats || !bwd_index)) return GS_ERR_INVALID_ARG;
+    if ((n > 0 && (!splats || !bwd_index)) || !al16(splats)) return GS_ERR_INVALID_ARG;
     if (k_capacity > 0 && !vals) return GS_ERR_INVALID_ARG;
     return GS_OK;
 }
@@ -351,6 +356,7 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     if (st != GS_OK) return st;
     if (!grads_ok(grads, n, gaussians->velocity != nullptr)) return GS_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < gs_render_bwd_workspace_bytes(n, k_capacity)) return GS_ERR_WORKSPACE;
+    if (!al16(workspace)) return GS_ERR_INVALID_ARG;
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
     float *g2 = (float *)((char *)workspace + partial_bytes(k_capacity));
@@ -390,6 +396,7 @@ gs_status gs_render_bwd_screen(const gs_camera *camera, int64_t n, const gs_spla
     if (st != GS_OK) return st;
     if (n > 0 && !g2) return GS_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < gs_render_bwd_screen_workspace_bytes(k_capacity)) return GS_ERR_WORKSPACE;
+    if (!al16(workspace)) return GS_ERR_INVALID_ARG;
     if (n == 0) return GS_OK;
     gs_bwd_view w;
     w.camera = *camera;
@@ -420,6 +427,7 @@ gs_status gs_render_bwd_screen_views(int32_t n_views, const gs_bwd_view *views, 
         if (w.n > 0 && !w.g2) return GS_ERR_INVALID_ARG;
         if (!w.workspace || w.workspace_bytes < gs_render_bwd_screen_workspace_bytes(w.k_capacity))
             return GS_ERR_WORKSPACE;
+        if (!al16(w.workspace)) return GS_ERR_INVALID_ARG;
     }
     // views without Gaussians have nothing to do; the rest go in batches
     gs_bwd_view batch[kMaxBlendViews];
@@ -445,7 +453,7 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const g
     if (!grads_ok(grads, n, gaussians->velocity != nullptr)) return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
-        if (n > 0 && (!splats[v] || !g2[v])) return GS_ERR_INVALID_ARG;
+        if ((n > 0 && (!splats[v] || !g2[v])) || !al16(splats[v])) return GS_ERR_INVALID_ARG;
     }
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -477,6 +485,7 @@ gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *
     if (n > 0 && (!scores || !mask)) return GS_ERR_INVALID_ARG;
     if (workspace_bytes < active_mask_workspace(n) || (!workspace && active_mask_workspace(n) > 0))
         return GS_ERR_WORKSPACE;
+    if (!al16(workspace)) return GS_ERR_INVALID_ARG;
     hipError_t e = launch_active_mask(scores, n, keep, mask, workspace, workspace_bytes,
                                       (hipStream_t)stream);
     if (e == hipErrorNotSupported) return GS_ERR_UNSUPPORTED;

@@ -43,6 +43,9 @@
  *     host pointers are named as such.  The library never allocates device
  *     memory: temporaries live in a caller workspace sized by the matching
  *     *_workspace_bytes query.
+ *   - Splat arrays and workspaces must be 16-byte aligned (they are read with
+ *     16-byte vector accesses); a misaligned one is GS_ERR_INVALID_ARG.  Every
+ *     other array needs only the natural alignment of its element type.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work and return; results are ready once the stream
  *     is synchronised.  Nothing is read back to the host, so a view's four

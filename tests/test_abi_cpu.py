@@ -166,3 +166,28 @@ def test_sh_adam_argument_errors_without_device():
     # the full-precision state needs no bounds; an empty update does nothing
     a = desc(n=0, state_dtype=B.GS_ADAM_F32, m_bounds=None, v_bounds=None, grad=None, value=None, m=None, v=None)
     assert L.gs_sh_adam_step(C.byref(a), None) == B.GS_OK
+
+
+def test_misaligned_splats_and_workspaces_are_rejected():
+    """Splat arrays and workspaces are read with 16-byte vector accesses: a
+    pointer off a 16-byte boundary is an argument error, found before
+    anything is launched."""
+    L = B.lib()
+    cam = B.GsCamera()
+    cam.width, cam.height, cam.fx, cam.fy, cam.guard = 16, 16, 10.0, 10.0, 1.3
+    g = B.GsGaussians()
+    g.n, g.sh_degree, g.sh_dtype = 5, 0, B.GS_SH_F32
+    g.means = g.scales = g.quats = g.opacities = g.sh = 0x1000
+    assert L.gs_project(C.byref(g), C.byref(cam), 0x1008, None) == B.GS_ERR_INVALID_ARG
+    sp = (C.c_void_p * 1)(0x1004)
+    assert L.gs_project_views(C.byref(g), 1, C.byref(cam), sp, None) == B.GS_ERR_INVALID_ARG
+    bgv = (C.c_float * 3)(0.0, 0.0, 0.0)
+    assert L.gs_render_fwd(0x1008, 0x1000, 0x1000, 0x1000, C.byref(cam), C.cast(bgv, C.c_void_p), 0x1000,
+                           0x1000, 0x1000, None) == B.GS_ERR_INVALID_ARG
+    v = B.GsSortView()
+    v.camera = cam
+    v.n, v.k_capacity = 5, 100
+    v.splats, v.vals, v.tile_ranges, v.schedule, v.k_total = 0x1000, 0x1000, 0x1000, 0x1000, 0x1000
+    v.workspace, v.workspace_bytes = 0x1004, 1 << 30
+    assert L.gs_bin_sort_views(1, C.byref(v), None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_active_mask(0x1000, 10, 5, 0x1000, 0x1004, 1 << 20, None) == B.GS_ERR_INVALID_ARG
