@@ -174,6 +174,36 @@ def render_pixel(proj, bins, cam, px, py, flips=0, bg=(0.0, 0.0, 0.0), bands=Non
     return out_rgb, out_T.value, out_n.value, ev
 
 
+def render_pixels(proj, bins, cam, xs, ys, bg=(0.0, 0.0, 0.0), bands=None):
+    """render_pixel over many pixels, the arrays marshalled once (for images
+    too large to composite whole).  Returns rgb [3][m], T [m], n_contrib [m],
+    events [m]."""
+    n = proj["u"].shape[0]
+    b = bands_struct(**(bands or {}))
+    c = cam_struct(cam)
+    bgv = np.asarray(bg, dtype=np.float64)
+    arr = {k: np.ascontiguousarray(proj[k], dtype=np.float64) for k in ("u", "v", "conic", "opacity", "rgb")}
+    vals = np.ascontiguousarray(bins["vals"], dtype=np.uint32)
+    ranges = np.ascontiguousarray(bins["ranges"], dtype=np.uint32)
+    m = len(xs)
+    rgb = np.zeros((3, m))
+    T = np.zeros(m)
+    nc = np.zeros(m, np.int64)
+    ev = np.zeros(m, np.int64)
+    one = np.zeros(3)
+    t = C.c_double(0.0)
+    k = C.c_int32(0)
+    for i in range(m):
+        ev[i] = lib().orc_render_pixel(C.byref(c), _p(arr["u"]), _p(arr["v"]), _p(arr["conic"]),
+                                       _p(arr["opacity"]), _p(arr["rgb"]), C.c_int64(n), _p(vals),
+                                       _p(ranges), _p(bgv), C.byref(b), C.c_int(int(xs[i])), C.c_int(int(ys[i])),
+                                       C.c_uint32(0), _p(one), C.byref(t), C.byref(k))
+        rgb[:, i] = one
+        T[i] = t.value
+        nc[i] = k.value
+    return rgb, T, nc, ev
+
+
 def render_bwd(proj, bins, cam, dL_dimage, bg=(0.0, 0.0, 0.0), tile_mask=None):
     n = proj["u"].shape[0]
     grad2d = np.zeros((9, n))

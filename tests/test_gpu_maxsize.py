@@ -1,0 +1,89 @@
+"""The largest image the ABI takes, 32768 x 32768 (2048 x 2048 = 4.2M tiles,
+22 tile bits, so the sort runs three tile passes; pixel offsets of the second
+and third colour planes pass 2^31): records and bins bit-exact against the
+oracle, and sampled pixels (whole tiles where the Gaussians are, random
+pixels there and anywhere, the corners) against the oracle's per-pixel
+compositing."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_splatting_tile_amd import scenes
+from tests.gpu_util import compare_bins, compare_records, run_view, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _scene():
+    n = 20_000
+    rng = np.random.default_rng(77)
+    z = rng.uniform(4.0, 9.0, n)
+    x = rng.uniform(-0.6, 0.6, n) * z
+    y = rng.uniform(-0.6, 0.6, n) * z
+    means = np.stack([x, y, z]).astype(np.float32)
+    log_s = rng.normal(-3.2, 0.6, (3, n)).clip(-6, -1.5).astype(np.float32)
+    quats = rng.standard_normal((4, n)).astype(np.float32)
+    quats /= np.linalg.norm(quats, axis=0, keepdims=True)
+    logits = rng.normal(0.0, 1.5, n).astype(np.float32)
+    sh = np.concatenate([rng.random((1, 3, n), dtype=np.float32),
+                         (rng.standard_normal((15, 3, n)) * 0.2).astype(np.float32)])
+    vm = np.concatenate([np.eye(3), np.zeros((3, 1))], axis=1).astype(np.float32)
+    # the principal point near the far corner: the Gaussians land around pixel (32000, 32000)
+    cam = scenes.Camera(32768, 32768, 1000.0, 1000.0, 32000.0, 32000.0, vm)
+    return scenes.Scene(name="max_image_20k_sh3_32768", means=means, log_scales=log_s, scales=np.exp(log_s),
+                        quats=quats, opacity_logits=logits, opacities=scenes._sigmoid32(logits), sh_degree=3,
+                        sh=sh, cameras=[cam])
+
+
+def test_maximum_image_size():
+    sc = _scene()
+    cam = sc.cameras[0]
+    say("[gpu] 32768 x 32768 view: project, bin, blend")
+    buf, K = run_view(sc, 0, with_keys=True)
+    op = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 3, sc.sh, cam)
+    ob = oracle.bin_sort(op, cam)
+    assert ob["K"] > 50_000
+    from tests.gpu_util import splats_np
+    compare_records(splats_np(buf), op, "max image")
+    compare_bins(buf, K, ob, "max image")
+    # sampled pixels
+    rng = np.random.default_rng(78)
+    ranges = ob["ranges"].reshape(-1, 2).astype(np.int64)
+    lens = ranges[:, 1] - ranges[:, 0]
+    busy = np.argsort(-lens)[:4]
+    xs, ys = [], []
+    for t in busy:
+        tx, ty = t % cam.tiles_x, t // cam.tiles_x
+        gx, gy = np.meshgrid(np.arange(16) + 16 * tx, np.arange(16) + 16 * ty)
+        xs += list(gx.ravel())
+        ys += list(gy.ravel())
+    vis = op["radius"] > 0
+    u0, u1 = int(op["u"][vis].min()), int(op["u"][vis].max())
+    v0, v1 = int(op["v"][vis].min()), int(op["v"][vis].max())
+    xs += list(rng.integers(max(u0, 0), min(u1, 32767) + 1, 2000))
+    ys += list(rng.integers(max(v0, 0), min(v1, 32767) + 1, 2000))
+    xs += list(rng.integers(0, 32768, 300)) + [0, 32767, 0, 32767]
+    ys += list(rng.integers(0, 32768, 300)) + [0, 0, 32767, 32767]
+    xs, ys = np.array(xs), np.array(ys)
+    say(f"[gpu] max image: K={K}, comparing {len(xs)} pixels")
+    idx = torch.from_numpy(ys * 32768 + xs).cuda()
+    img = buf.image.view(3, -1)[:, idx].cpu().numpy().astype(np.float64)
+    T = buf.final_T.view(-1)[idx].cpu().numpy().astype(np.float64)
+    nc = buf.n_contrib.view(-1)[idx].cpu().numpy().astype(np.int64)
+    rgb, rT, rn, ev = oracle.render_pixels(op, ob, cam, xs, ys)
+    bad = (np.abs(img - rgb).max(axis=0) > 1e-4) | (np.abs(T - rT) > 1e-4) | (nc != rn)
+    # a mismatch is accepted only at a pixel with a near-threshold decision
+    # whose alternative branch matches
+    for i in np.nonzero(bad)[0]:
+        ok = False
+        for flips in range(1, 1 << min(int(ev[i]), 6)):
+            a, t, k, _ = oracle.render_pixel(op, ob, cam, int(xs[i]), int(ys[i]), flips=flips)
+            if np.abs(a - img[:, i]).max() <= 1e-4 and abs(t - T[i]) <= 1e-4 and k == nc[i]:
+                ok = True
+                break
+        assert ok, (int(xs[i]), int(ys[i]), img[:, i], rgb[:, i], T[i], rT[i], nc[i], rn[i])
+    assert (rn > 0).sum() > 1000                      # the samples do cover the Gaussians
+    say(f"[gpu] max image: {int(bad.sum())} near-threshold pixels resolved, max err "
+        f"{float(np.abs(img - rgb).max(axis=0)[~bad].max()):.2e}")
