@@ -290,3 +290,47 @@ def test_full_size_5m_sh3_sampled_blocks():
                    m_bounds=mb[r:r + 1, b:b + 1].cpu().numpy(), s_bounds=sb[r:r + 1, b:b + 1].cpu().numpy(),
                    grad_after=dev["grad"][r:r + 1, lo:hi].cpu().numpy())
         _compare_q8(gpu, _oracle(sub, "q8", 20), sub, f"5M row {r} block {b}")
+
+
+def test_hundred_million_gaussians_take_64_bit_offsets():
+    """100M Gaussians x 45 SH rows: 4.5G units, so offsets into the gradient
+    array pass 2^32 elements (the Spirula Studio page's note that at 100M
+    Gaussians units need 64-bit indices).  fp16 values and a fresh 8-bit
+    state; inputs drawn on the device by torch's seeded generator; blocks in
+    the first and last rows (past 2^32 units), among them the last row's
+    ragged tail, compared with the oracle on those blocks."""
+    n, rows = 100_000_100, 45
+    say("[gpu] adam 100M x 45: drawing inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(95)
+    grad = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    value = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+    for r in range(rows):
+        g = torch.randn(n, generator=gen, device="cuda") * 1e-5
+        g *= (torch.rand(n, generator=gen, device="cuda") < 0.6)
+        grad[r] = g
+        value[r] = (torch.randn(n, generator=gen, device="cuda") * 0.2).half()
+    del g
+    m = torch.zeros((rows, n), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((rows, n), dtype=torch.uint8, device="cuda")
+    nb = A.n_blocks(n)
+    mb = torch.zeros((rows, nb, 2), dtype=torch.float32, device="cuda")
+    sb = torch.zeros((rows, nb, 2), dtype=torch.float32, device="cuda")
+    picks = [(0, 0), (0, 1), (1, 7), (rows - 1, nb - 2), (rows - 1, nb - 1), (rows // 2, nb // 2), (44, 390_000)]
+    before = {}
+    for r, b in picks:
+        lo, hi = b * 256, min(n, b * 256 + 256)
+        before[(r, b)] = (grad[r, lo:hi].cpu().numpy()[None], value[r, lo:hi].cpu().numpy()[None])
+    assert (rows - 1) * n > 2 ** 32
+    say("[gpu] adam 100M x 45: one step")
+    B.sh_adam_step(grad, value, m, s, mb, sb, step=1, lr=LR, beta1=B1, beta2=B2, eps=EPS)
+    torch.cuda.synchronize()
+    for (r, b), (g0, v0) in before.items():
+        lo, hi = b * 256, min(n, b * 256 + 256)
+        z8 = np.zeros_like(g0, dtype=np.uint8)
+        zb = np.zeros((1, 1, 2), np.float32)
+        sub = dict(grad=g0, value=v0, m_codes=z8, m_bounds=zb, s_codes=z8.copy(), s_bounds=zb.copy())
+        gpu = dict(value=value[r, lo:hi].cpu().numpy()[None], m_codes=m[r, lo:hi].cpu().numpy()[None],
+                   s_codes=s[r, lo:hi].cpu().numpy()[None], m_bounds=mb[r:r + 1, b:b + 1].cpu().numpy(),
+                   s_bounds=sb[r:r + 1, b:b + 1].cpu().numpy(), grad_after=grad[r, lo:hi].cpu().numpy()[None])
+        _compare_q8(gpu, _oracle(sub, "q8", 1), sub, f"100M row {r} block {b}")
