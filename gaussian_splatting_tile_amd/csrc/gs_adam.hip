@@ -41,6 +41,23 @@ struct AdamArgs {
     long long total;                           // rows * n
 };
 
+// Streaming accesses: the gradients and the moments are touched once per
+// step, so their loads and stores carry the non-temporal hint (native vector
+// types, as the builtins require).  At 5M x 45 units it took the fp32 state
+// from 1.14 to about 1.0 ms and the 8-bit state from 0.50 to 0.49 ms; the
+// hint on the values' accesses measured no better and is left off.
+typedef float nf4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt(const float *p)
+{
+    const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float *p, float a, float b, float c, float d)
+{
+    nf4 v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<nf4 *>(p));
+}
+
 template <typename TV> __device__ __forceinline__ float to_f(TV x);
 template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f<__half>(__half x) { return __half2float(x); }
@@ -101,9 +118,9 @@ __global__ __launch_bounds__(kAdamThreads) void adam_f32_kernel(AdamArgs a)
     for (long long i = ((long long)blockIdx.x * kAdamThreads + threadIdx.x) * 4; i < a.total; i += stride) {
         float g[4], th[4], m[4], v[4];
         if (kVec) {
-            const float4 g4 = *reinterpret_cast<const float4 *>(gp + i);
-            const float4 m4 = *reinterpret_cast<const float4 *>(mp + i);
-            const float4 v4 = *reinterpret_cast<const float4 *>(sp + i);
+            const float4 g4 = ld_nt(gp + i);
+            const float4 m4 = ld_nt(mp + i);
+            const float4 v4 = ld_nt(sp + i);
             load4<TV>(vp + i, th);
             g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
             m[0] = m4.x; m[1] = m4.y; m[2] = m4.z; m[3] = m4.w;
@@ -111,8 +128,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_f32_kernel(AdamArgs a)
 #pragma unroll
             for (int j = 0; j < 4; j++) th[j] = adam_unit(th[j], m[j], v[j], g[j], a.k);
             store4<TV>(vp + i, th);
-            *reinterpret_cast<float4 *>(mp + i) = make_float4(m[0], m[1], m[2], m[3]);
-            *reinterpret_cast<float4 *>(sp + i) = make_float4(v[0], v[1], v[2], v[3]);
+            st_nt(mp + i, m[0], m[1], m[2], m[3]);
+            st_nt(sp + i, v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -212,11 +229,11 @@ __global__ __launch_bounds__(kAdamThreads) void adam_q8_kernel(AdamArgs a)
         const int u = u0 + 4 * lane;
         const bool valid = u < a.n;
         const int ul = valid ? u : a.n - 4;
-        const float4 g4 = *reinterpret_cast<const float4 *>(gp + ul);
+        const float4 g4 = ld_nt(gp + ul);
         g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
         load4<TV>(vp + ul, th);
-        const uint32_t wm = *reinterpret_cast<const uint32_t *>(mp + ul);
-        const uint32_t ws = *reinterpret_cast<const uint32_t *>(sp + ul);
+        const uint32_t wm = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(mp + ul));
+        const uint32_t ws = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sp + ul));
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             cm[j] = (wm >> (8 * j)) & 255u;
@@ -301,8 +318,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_q8_kernel(AdamArgs a)
                 ws |= encode8(s1[j], slo2n, sscale) << (8 * j);
             }
             store4<TV>(vp + u, th);
-            *reinterpret_cast<uint32_t *>(mp + u) = wm;
-            *reinterpret_cast<uint32_t *>(sp + u) = ws;
+            __builtin_nontemporal_store(wm, reinterpret_cast<uint32_t *>(mp + u));
+            __builtin_nontemporal_store(ws, reinterpret_cast<uint32_t *>(sp + u));
         }
     } else {
 #pragma unroll
