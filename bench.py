@@ -469,7 +469,7 @@ def cpu_baseline(sc):
     project + bin + composite of one full view (forward), repeated while under
     ~15 s; reported in ms/frame."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     frames = 0
     while True:

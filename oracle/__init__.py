@@ -174,6 +174,11 @@ def render_pixel(proj, bins, cam, px, py, flips=0, bg=(0.0, 0.0, 0.0), bands=Non
     return out_rgb, out_T.value, out_n.value, ev
 
 
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(lib().orc_num_threads())
+
+
 def render_pixels(proj, bins, cam, xs, ys, bg=(0.0, 0.0, 0.0), bands=None):
     """render_pixel over many pixels, the arrays marshalled once (for images
     too large to composite whole).  Returns rgb [3][m], T [m], n_contrib [m],

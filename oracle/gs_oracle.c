@@ -9,6 +9,7 @@
 #include "gs_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -627,3 +628,5 @@ void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *boun
             x[(int64_t)r * n + g] = lo + (float)q[(int64_t)r * n + g] * step;
         }
 }
+
+int orc_num_threads(void) { return omp_get_max_threads(); }

@@ -145,6 +145,9 @@ void orc_topk_mask(int64_t n, const float *scores, int64_t k, uint8_t *mask);
 void orc_sh_quantize8(int64_t n, int rows, const float *x, uint8_t *q, float *bounds);
 void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *bounds, float *x);
 
+/* The number of OpenMP threads the oracle's parallel loops use. */
+int orc_num_threads(void);
+
 /* Real spherical-harmonic basis (degree <= 3) at unit direction d, and its
  * gradient with respect to the three components of d. */
 void orc_sh_basis(const double *d, double *Y /*[16]*/, double *dY /*[16][3]*/);
