@@ -191,3 +191,13 @@ def test_misaligned_splats_and_workspaces_are_rejected():
     v.workspace, v.workspace_bytes = 0x1004, 1 << 30
     assert L.gs_bin_sort_views(1, C.byref(v), None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(0x1000, 10, 5, 0x1000, 0x1004, 1 << 20, None) == B.GS_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library the binding raises; nothing falls back to
+    another implementation."""
+    import pytest
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "lib_path", lambda: str(tmp_path / "absent.so"))
+    with pytest.raises(B.GsError, match="not built"):
+        B.lib()
