@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--motion", action="store_true",
                     help="moving Gaussians: a motion vector and a time offset each, the views spread over the "
                          "time window (the projection and its backward displace the means)")
+    ap.add_argument("--scores-from-weights", action="store_true",
+                    help="workloads with an importance mask: score each Gaussian by its blending weights "
+                         "summed over the views (an untimed pass before the steps) instead of the synthetic scores")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for "
                          "calibrating the HBM byte counters of a profiler run)")
@@ -146,6 +149,24 @@ def main():
     if use_mask:
         keep = scenes.keep_count(sc.n, sc.keep_fraction)
         scores = f(sc.importance)
+        if args.scores_from_weights:
+            # cross-view visibility scores: every view rendered once without
+            # a mask, each Gaussian's blending weights summed over the views
+            gs_all = B.gaussians_struct(g, sc.sh_degree)
+            scores = torch.zeros(sc.n, dtype=torch.float32, device=dev)
+            for v in range(min(args.views, len(sc.cameras))):
+                probe = B.ViewBuffers(sc.n, sc.cameras[v], 16 * sc.n, with_backward=False)
+                probe.forward(gs_all)
+                torch.cuda.synchronize()
+                k = int(probe.k_total.item())
+                del probe
+                vb = B.ViewBuffers(sc.n, sc.cameras[v], k, with_backward=False)
+                vb.forward(gs_all)
+                B.render_fwd_views([vb], (0.0, 0.0, 0.0), stream, weights=scores)
+                torch.cuda.synchronize()
+                del vb
+            print(f"# scores from blending weights: {int((scores > 0).sum())} of {sc.n} Gaussians seen",
+                  file=sys.stderr, flush=True)
         mask = torch.zeros(sc.n, dtype=torch.uint8, device=dev)
         mask_ws = torch.empty(B.active_mask_workspace_bytes(sc.n), dtype=torch.uint8, device=dev)
         B.active_mask(scores, sc.n, keep, mask, mask_ws, stream)
@@ -324,6 +345,9 @@ def main():
         "config": {"workload": sc.name, "gaussians": sc.n, "sh_degree": sc.sh_degree,
                    "width": sc.cameras[0].width, "height": sc.cameras[0].height, "views_per_step": views,
                    "importance_keep": (keep if use_mask else None),
+                   "importance_scores": (None if not use_mask else
+                                         "blending weights summed over the views" if args.scores_from_weights
+                                         else "synthetic Exp(1)"),
                    "lod_min_radius_px": cam0.lod_min_radius_px,
                    "step": ("importance mask, then " if use_mask else "") +
                            "batched project, " +
