@@ -131,10 +131,19 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const Batch<PassArgs> b,
             const uint32_t i = base + r * kBlock + threadIdx.x;
             k[r] = keys[i < end ? i : end - 1];
         }
+        // Lanes that share the first lane's digit (often most of the wave:
+        // the high digits of depths and tiles take few values) are counted
+        // with one add; the others add one each (LDS atomics at one address
+        // serialise).
 #pragma unroll
         for (int r = 0; r < kIpt; r++) {
             const uint32_t i = base + r * kBlock + threadIdx.x;
-            if (i < end && !(drop_sentinel && k[r] == kSentinel)) atomicAdd(&h[(k[r] >> shift) & mask], 1u);
+            const bool valid = i < end && !(drop_sentinel && k[r] == kSentinel);
+            const uint32_t d = (k[r] >> shift) & mask;
+            const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+            const uint64_t same = __ballot(valid && d == d0);
+            if (lane_id() == 0 && same != 0ull) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+            if (valid && d != d0) atomicAdd(&h[d], 1u);
         }
     }
     __syncthreads();
