@@ -106,7 +106,22 @@ struct PassArgs {
     uint32_t *counts;            // per-digit, per-block counts [256][grid]
     uint32_t *digit_total;       // [256]
     int shift, bits;
+    int key16;                   // keys stored as 16-bit (tile ids of views with <= 65536 tiles)
 };
+
+// Tile ids of views with at most 65536 tiles travel as 16-bit keys (half the
+// key bytes of every tile pass); depths and larger tile ids as 32-bit.
+__device__ __forceinline__ uint32_t ld_key(const uint32_t *p, size_t i, int k16)
+{
+    return k16 ? (uint32_t)reinterpret_cast<const uint16_t *>(p)[i] : p[i];
+}
+__device__ __forceinline__ void st_key(uint32_t *p, size_t i, uint32_t v, int k16)
+{
+    if (k16)
+        reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)v;
+    else
+        p[i] = v;
+}
 
 __global__ __launch_bounds__(kBlock) void radix_upsweep(const Batch<PassArgs> b, int drop_sentinel)
 {
@@ -129,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const Batch<PassArgs> b,
 #pragma unroll
         for (int r = 0; r < kIpt; r++) {
             const uint32_t i = base + r * kBlock + threadIdx.x;
-            k[r] = keys[i < end ? i : end - 1];
+            k[r] = ld_key(keys, i < end ? i : end - 1, a.key16);
         }
         // Lanes that share the first lane's digit (often most of the wave:
         // the high digits of depths and tiles take few values) are counted
@@ -223,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(const Batch<PassArgs> 
         for (int r = 0; r < kIpt; r++) {
             const uint32_t idx = tb + w * kWaveItems + r * kWave + lane;
             const uint32_t ci = idx < end ? idx : end - 1;
-            kk[r] = keys_in[ci];
+            kk[r] = ld_key(keys_in, ci, a.key16);
             vv[r] = vals_in ? vals_in[ci] : idx;
             if (two) vv2[r] = vals2_in[ci];
         }
@@ -290,7 +305,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(const Batch<PassArgs> 
             const uint32_t kk = sk[i];
             const uint32_t d = (kk >> shift) & mask;
             const uint32_t o = digit_base[d] + (i - tile_start[d]);
-            keys_out[o] = kk;
+            st_key(keys_out, o, kk, a.key16);
             vals_out[o] = sv[i];
             if (two) vals2_out[o] = sv2[i];
         }
@@ -372,6 +387,7 @@ struct DupArgs {
     uint32_t *k_eff;             // K clamped to the capacity
     uint32_t *tile_keys, *gslot; // duplicated entries
     uint32_t *bwd_order, *bwd_off, *bwd_count;   // optional backward index parts
+    int key16;                   // tile ids stored as 16-bit keys
 };
 
 __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
@@ -504,7 +520,7 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(const Batch<DupArgs> b)
         const uint32_t xy = s_xy[lo];
         const uint32_t ty = (xy >> 16) + q;
         const uint32_t tx = (xy & 0xFFFFu) + (within - q * w);
-        tile_keys[slot] = ty * (uint32_t)tiles_x + tx;
+        st_key(tile_keys, slot, ty * (uint32_t)tiles_x + tx, a.key16);
         gslot[slot] = s_g[lo];
     }
 }
@@ -520,6 +536,7 @@ struct RangeArgs {
     const uint32_t *gslot;       // without tile passes: the duplication order's Gaussians
     uint32_t *ranges, *vals, *entry_slots;
     uint64_t *keys64;
+    int key16;                   // tile ids stored as 16-bit keys
 };
 
 __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const Batch<RangeArgs> b)
@@ -535,9 +552,10 @@ __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const Batch<RangeAr
     const uint32_t k = *a.k_ptr;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i >= k) return;
-    const uint32_t t = tile_keys[i];
-    if (i == 0 || tile_keys[i - 1] != t) ranges[2 * t] = i;
-    if (i == k - 1 || tile_keys[i + 1] != t) ranges[2 * t + 1] = i + 1;
+    const int k16 = a.key16;
+    const uint32_t t = ld_key(tile_keys, i, k16);
+    if (i == 0 || ld_key(tile_keys, i - 1, k16) != t) ranges[2 * t] = i;
+    if (i == k - 1 || ld_key(tile_keys, i + 1, k16) != t) ranges[2 * t + 1] = i + 1;
     uint32_t g;
     if (gslot) {
         g = gslot[i];
@@ -758,6 +776,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         }
 
         // 2. slots and duplication (K clamped to the capacity in counters[2])
+        const int key16 = tbits_max <= 16 ? 1 : 0;
         Batch<DupArgs> d;
         d.count = n_live;
         for (int i = 0; i < n_live; i++) {
@@ -769,7 +788,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             d.v[i] = DupArgs{W.grect, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
                              W.rect_info, W.counts, W.block_sums, J.k_total, &W.counters[2], W.tk[0], W.gslot,
                              bi ? bi + cap : nullptr, bi ? bi + cap + n : nullptr,
-                             bi ? bi + cap + 2 * n + 1 : nullptr};
+                             bi ? bi + cap + 2 * n + 1 : nullptr, key16};
         }
         const uint32_t nblk = (n_max + kScanItems - 1) / kScanItems;
         scan_reduce<<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
@@ -800,10 +819,10 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
                     const uint32_t *sin = p == 0 ? nullptr : W.ts[(p - 1) & 1];
                     uint32_t *sout = last ? entry_slots : W.ts[p & 1];
                     b.v[i] = PassArgs{W.tk[p & 1], sin, gin, W.tk[(p + 1) & 1], sout, gout, &W.counters[2],
-                                      nullptr, W.digit_counts, W.digit_total, shift, bits};
+                                      nullptr, W.digit_counts, W.digit_total, shift, bits, key16};
                 } else {
                     b.v[i] = PassArgs{W.tk[p & 1], gin, nullptr, W.tk[(p + 1) & 1], gout, nullptr,
-                                      &W.counters[2], nullptr, W.digit_counts, W.digit_total, shift, bits};
+                                      &W.counters[2], nullptr, W.digit_counts, W.digit_total, shift, bits, key16};
                 }
             }
             if ((e = radix_pass(b, radix_grid(cap_max), 0, any_bwd, s)) != hipSuccess) return e;
@@ -816,7 +835,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             const SortJob &J = jobs[live[i]];
             const BinWs &W = w[live[i]];
             r.v[i] = RangeArgs{W.tk[passes & 1], &W.counters[2], J.splats, passes == 0 ? W.gslot : nullptr,
-                               J.ranges, J.vals, J.bwd_index, J.keys};
+                               J.ranges, J.vals, J.bwd_index, J.keys, key16};
         }
         const uint64_t kgrid = (cap_max + kBlock - 1) / kBlock;
         if (kgrid > 0) tile_ranges_kernel<<<dim3((unsigned)kgrid, n_live), kBlock, 0, s>>>(r);
