@@ -255,10 +255,12 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
         stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
         s_pos[slot] = f.m - start;
         s_slot[slot] = entry_slot;
-        // w' = P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex))
+        // -w' = -P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex)), stored
+        // negated: the wave then sums -W1, -W2 directly (the products in
+        // W11, W12, W22 do not change sign)
         double ex, ey, l1, l2;
         conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
-        s_P[slot] = make_double4(l1 * ex, l1 * ey, -(l2 * ey), l2 * ex);
+        s_P[slot] = make_double4(-(l1 * ex), -(l1 * ey), l2 * ey, -(l2 * ex));
     }
     return __popcll(mask);
 }
@@ -522,6 +524,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
 
     const int lane = threadIdx.x;
     const int slot = reduce_slot(lane);
+    // the second-moment sums are halved once, on the lane that stores them
+    const float slot_scale = (slot >= 2 && slot <= 4) ? 0.5f : 1.0f;
     const int n_items = batch.count * batch.max_tiles;
     uint32_t *head = batch.queue, *done = batch.queue + 1;
     for (int item = next_item(head, n_items); item >= 0; item = next_item(head, n_items)) {
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             }
             const float4 col = s_rgb[k];
             const float inv_o = __builtin_amdgcn_rcpf(col.w);
-            // w' = P d per pixel in fp32: in the principal frame the terms
+            // -w' = -P d per pixel in fp32: in the principal frame the terms
             // cancel by at most the square root of the conic's eigenvalue
             // ratio (~1e2), so fp32 keeps ~1e-5 relative accuracy
             const double4 P = s_P[k];
@@ -664,17 +668,17 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
                 }
             }
             float v[9];
-            v[0] = -W1;
-            v[1] = -W2;
-            v[2] = 0.5f * W11;
-            v[3] = 0.5f * W12;
-            v[4] = 0.5f * W22;
+            v[0] = W1;                                         // -W1, -W2 (P is negated)
+            v[1] = W2;
+            v[2] = W11;                                        // halved after the sum
+            v[3] = W12;
+            v[4] = W22;
             v[5] = go;
             v[6] = g6;
             v[7] = g7;
             v[8] = g8;
             const float tot = wave_reduce9(v, lane);
-            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot;
+            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot * slot_scale;
         }
         __syncthreads();
     }
