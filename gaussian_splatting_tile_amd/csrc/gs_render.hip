@@ -238,7 +238,7 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
 // dropped entry gets its nine partial sums zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
                                                  int y0, double2 *s_uv, double4 *s_q, float4 *s_rgb,
-                                                 uint32_t *s_pos, uint32_t *s_slot, double4 *s_P,
+                                                 uint32_t *s_pos, uint32_t *s_slot, float4 *s_P,
                                                  float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
@@ -257,10 +257,10 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
         s_slot[slot] = entry_slot;
         // -w' = -P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex)), stored
         // negated: the wave then sums -W1, -W2 directly (the products in
-        // W11, W12, W22 do not change sign)
+        // W11, W12, W22 do not change sign); formed in fp64, kept in fp32
         double ex, ey, l1, l2;
         conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
-        s_P[slot] = make_double4(-(l1 * ex), -(l1 * ey), l2 * ey, -(l2 * ex));
+        s_P[slot] = make_float4((float)(-(l1 * ex)), (float)(-(l1 * ey)), (float)(l2 * ey), (float)(-(l2 * ex)));
     }
     return __popcll(mask);
 }
@@ -459,8 +459,10 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
 // Gaussian Q's eigenvalues differ by up to ~1e4; summed as conic gradients
 // or in image axes, fp32 rounding of the large-eigenvalue direction would
 // swamp the small one after the change of variables.  In the principal
-// frame each direction keeps its own relative precision.  w' is formed per
-// pixel in fp64 (no cancellation) and rounded once; a lane accumulates, over
+// frame each direction keeps its own relative precision.  P = L V^T is formed
+// per record in fp64 and kept in fp32, w' = P d per pixel in fp32 (its two
+// terms cancel by at most the square root of the eigenvalue ratio); a lane
+// accumulates, over
 // its pixels with dp = dL/dpower,
 //   W1 = sum dp w'_1,  W2 = sum dp w'_2,  W11, W12, W22 = sum dp w' w'^T.
 // The 9 per-lane values of a record, (-W1, -W2, W11/2, W12/2, W22/2, dL/do,
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
     __shared__ float4 s_rgb[kBatch];
     __shared__ uint32_t s_pos[kBatch];
     __shared__ uint32_t s_slot[kBatch];
-    __shared__ double4 s_P[kBatch];
+    __shared__ float4 s_P[kBatch];
 
     const int lane = threadIdx.x;
     const int slot = reduce_slot(lane);
@@ -634,9 +636,10 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             // -w' = -P d per pixel in fp32: in the principal frame the terms
             // cancel by at most the square root of the conic's eigenvalue
             // ratio (~1e2), so fp32 keeps ~1e-5 relative accuracy
-            const double4 P = s_P[k];
-            const float p1dx = (float)(P.x * ct.dx), p2dx = (float)(P.z * ct.dx);
-            const float p1y = (float)P.y, p2y = (float)P.w, fdy0 = (float)dy0;
+            const float4 P = s_P[k];
+            const float fdx = (float)ct.dx;
+            const float p1dx = P.x * fdx, p2dx = P.z * fdx;
+            const float p1y = P.y, p2y = P.w, fdy0 = (float)dy0;
             float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f;
             float W1 = 0.0f, W2 = 0.0f, W11 = 0.0f, W12 = 0.0f, W22 = 0.0f;
 #pragma unroll
