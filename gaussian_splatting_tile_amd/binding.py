@@ -81,7 +81,8 @@ SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
-           "gs_active_mask", "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_sh_adam_step", "gs_status_string",
+           "gs_active_mask", "gs_active_mask_static", "gs_active_mask_static_scratch_bytes",
+           "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_sh_adam_step", "gs_status_string",
            "gs_version")
 
 
@@ -127,6 +128,9 @@ def lib():
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
     L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
+    L.gs_active_mask_static.argtypes = [vp, i64, i64, vp, vp]
+    L.gs_active_mask_static_scratch_bytes.argtypes = []
+    L.gs_active_mask_static_scratch_bytes.restype = sz
     L.gs_sh_q8_bounds_floats.argtypes = [i64, C.c_int32]
     L.gs_sh_q8_bounds_floats.restype = sz
     L.gs_sh_quantize8.argtypes = [vp, i64, C.c_int32, vp, vp, vp]
@@ -138,7 +142,7 @@ def lib():
                  "gs_render_fwd_views",
                  "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
-                 "gs_project_bwd", "gs_active_mask", "gs_sh_quantize8"):
+                 "gs_project_bwd", "gs_active_mask", "gs_active_mask_static", "gs_sh_quantize8"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -397,6 +401,13 @@ def active_mask(scores, n, keep, mask, workspace, stream=None):
     _check(lib().gs_active_mask(_ptr(scores), int(n), int(keep), _ptr(mask), _ptr(workspace),
                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                 _stream(stream)), "gs_active_mask")
+
+
+def active_mask_static(scores, n, keep, mask, stream=None):
+    """gs_active_mask with the library's fixed scratch array: no workspace,
+    nothing allocated (n up to 2^30)."""
+    _check(lib().gs_active_mask_static(_ptr(scores), int(n), int(keep), _ptr(mask), _stream(stream)),
+           "gs_active_mask_static")
 
 
 # ---- buffers for one view ---------------------------------------------------

@@ -492,6 +492,16 @@ gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *
     return from_hip(e);
 }
 
+gs_status gs_active_mask_static(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *stream)
+{
+    if (n < 0 || n > INT32_MAX || keep < 0 || keep > n) return GS_ERR_INVALID_ARG;
+    if (n > 0 && (!scores || !mask)) return GS_ERR_INVALID_ARG;
+    if (n > GS_ACTIVE_MASK_STATIC_MAX_N) return GS_ERR_WORKSPACE;
+    return from_hip(launch_active_mask_static(scores, n, keep, mask, (hipStream_t)stream));
+}
+
+size_t gs_active_mask_static_scratch_bytes(void) { return static_mask_scratch_bytes(); }
+
 size_t gs_sh_q8_bounds_floats(int64_t n, int32_t rows)
 {
     if (n < 0 || rows < 1) return 0;

@@ -164,6 +164,9 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s);
 size_t active_mask_workspace(int64_t n);
 hipError_t launch_active_mask(const float *scores, int64_t n, int64_t keep, uint8_t *mask, void *ws,
                               size_t ws_bytes, hipStream_t s);
+// gs_active_mask with the library's own fixed scratch array (no workspace).
+size_t static_mask_scratch_bytes();
+hipError_t launch_active_mask_static(const float *scores, int64_t n, int64_t keep, uint8_t *mask, hipStream_t s);
 
 // Views blended by one launch: their tiles form one work queue.
 constexpr int kMaxBlendViews = 8;

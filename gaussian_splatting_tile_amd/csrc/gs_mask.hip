@@ -11,6 +11,8 @@
 // keeps, key == T keeps the first `need` in index order (a block-ordered
 // rank), key < T drops.  Everything stays on the device; the selection
 // state lives in the workspace.
+#include <mutex>
+
 #include "gs_internal.h"
 
 namespace gsi {
@@ -258,6 +260,66 @@ size_t carve_mask(char *base, int64_t n, MaskWs *ws)
 }  // namespace
 
 size_t active_mask_workspace(int64_t n) { return carve_mask(nullptr, n > 0 ? n : 0, nullptr) + 256; }
+
+}  // namespace gsi
+
+// ---- allocation-free variant -------------------------------------------------
+// For callers that cannot allocate device memory: the selection state
+// (histograms, threshold, per-block tie counts) lives in this fixed array,
+// one copy per GPU, held until the process ends.  Its size is carve_mask's
+// layout for GS_ACTIVE_MASK_STATIC_MAX_N scores: 4 KiB of histograms, the
+// state, and one word per 4096-score block (+1), each part 256-byte aligned.
+// Every word a call reads is first written by that call's own kernels
+// (mask_init clears the histograms and sets the state; mask_count_eq writes
+// every block count before the scan), so nothing carries over between calls.
+// Host code never uses the array's name as an address: the device address
+// comes from hipGetSymbolAddress, once per device.
+namespace {
+constexpr size_t kStaticMaskBlocks =
+    (size_t)((GS_ACTIVE_MASK_STATIC_MAX_N + gsi::kMaskBlockItems - 1) / gsi::kMaskBlockItems);
+constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+constexpr size_t kStaticMaskBytes =
+    align256(align256(align256(4 * 256 * sizeof(uint32_t)) + sizeof(gsi::MaskState)) +
+             (kStaticMaskBlocks + 1) * sizeof(uint32_t));
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];          // device address of `scratch` per device
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticMaskBytes];
+
+namespace gsi {
+
+size_t static_mask_scratch_bytes() { return kStaticMaskBytes; }
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current.
+static hipError_t static_mask_scratch(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_active_mask_static(const float *scores, int64_t n, int64_t keep, uint8_t *mask, hipStream_t s)
+{
+    if (carve_mask(nullptr, n, nullptr) > kStaticMaskBytes) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = static_mask_scratch(&ws);
+    if (e != hipSuccess) return e;
+    return launch_active_mask(scores, n, keep, mask, ws, kStaticMaskBytes, s);
+}
 
 hipError_t launch_active_mask(const float *scores, int64_t n64, int64_t keep, uint8_t *mask, void *ws_ptr,
                               size_t ws_bytes, hipStream_t s)

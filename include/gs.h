@@ -42,7 +42,8 @@
  *   - Device pointers are caller-owned device memory on the current device;
  *     host pointers are named as such.  The library never allocates device
  *     memory: temporaries live in a caller workspace sized by the matching
- *     *_workspace_bytes query.
+ *     *_workspace_bytes query (gs_active_mask_static uses a fixed array of
+ *     the library instead).
  *   - Splat arrays and workspaces must be 16-byte aligned (they are read with
  *     16-byte vector accesses); a misaligned one is GS_ERR_INVALID_ARG.  Every
  *     other array needs only the natural alignment of its element type.
@@ -53,7 +54,8 @@
  *   - Argument errors are returned synchronously and nothing is enqueued.
  *     A failed kernel launch returns GS_ERR_HIP.
  *   - Calls on different streams may run concurrently if they use disjoint
- *     outputs and workspaces.  The library keeps no global mutable state.
+ *     outputs and workspaces.  The library keeps no global mutable state
+ *     apart from the fixed scratch array of gs_active_mask_static.
  */
 #ifndef GS_H
 #define GS_H
@@ -469,6 +471,29 @@ size_t gs_active_mask_workspace_bytes(int64_t n);
 gs_status gs_active_mask(const float *scores, int64_t n, int64_t keep,
                          uint8_t *mask, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* gs_active_mask for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same mask, bit for bit, computed with the library's own
+ * fixed scratch array instead of a caller workspace.  The call allocates
+ * nothing and needs no workspace; the caller still passes scores and mask.
+ *   n  0 .. GS_ACTIVE_MASK_STATIC_MAX_N; larger n returns GS_ERR_WORKSPACE
+ *      (the fixed array is too small) before anything is enqueued
+ * The array (gs_active_mask_static_scratch_bytes() bytes, about 1 MiB) is a
+ * static device variable: every GPU the library runs on holds its own copy
+ * until the process ends, and its device address is looked up once per
+ * device, on the first call made with that device current.  All calls on
+ * one GPU share that GPU's copy, so calls that may overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined masks; calls ordered on one stream are safe.  Each call
+ * re-initialises whatever it reads, so nothing carries over between calls.
+ * Errors: GS_ERR_INVALID_ARG (as gs_active_mask), GS_ERR_WORKSPACE (n above
+ * the maximum), GS_ERR_HIP (no current device, the array's address could
+ * not be found, or a launch failed). */
+#define GS_ACTIVE_MASK_STATIC_MAX_N ((int64_t)1 << 30)
+gs_status gs_active_mask_static(const float *scores, int64_t n, int64_t keep,
+                                uint8_t *mask, void *stream);
+size_t gs_active_mask_static_scratch_bytes(void);
 
 /* Static description of a status code. */
 const char *gs_status_string(gs_status status);

@@ -82,6 +82,17 @@ def test_host_side_argument_errors_without_device():
     assert L.gs_project(C.byref(gs), C.byref(cam), None, None) == B.GS_ERR_UNSUPPORTED
     assert L.gs_bin_sort(None, -1, C.byref(cam), 0, None, None, None, None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_active_mask(None, 10, 11, None, None, 0, None) == B.GS_ERR_INVALID_ARG
+    # the allocation-free mask: same argument rules, and n above the fixed
+    # scratch array's maximum (2^30) is refused before any device call
+    assert L.gs_active_mask_static(None, 10, 11, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_active_mask_static(None, 10, 5, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_active_mask_static(None, -1, 0, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_active_mask_static(0x1000, (1 << 30) + 1, 7, 0x1000, None) == B.GS_ERR_WORKSPACE
+    assert L.gs_active_mask_static(0x1000, 1 << 31, 7, 0x1000, None) == B.GS_ERR_INVALID_ARG
+    # the array holds the workspace layout of 2^30 scores (one word per
+    # 4096-score block plus histograms and state)
+    sb = L.gs_active_mask_static_scratch_bytes()
+    assert sb >= L.gs_active_mask_workspace_bytes(1 << 30) - 256 and sb < (2 << 20)
     # 8-bit SH storage
     assert L.gs_sh_quantize8(None, -1, 48, None, None, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_sh_quantize8(None, 10, 0, None, None, None) == B.GS_ERR_INVALID_ARG
