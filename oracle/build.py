@@ -12,15 +12,18 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(HERE, "liboracle.so")
+# GS_ORACLE_LIB names another build of these sources (the planted-mistake
+# tests load deliberately broken copies this way); it is never rebuilt here.
+LIB_OVERRIDE = os.environ.get("GS_ORACLE_LIB")
+LIB = LIB_OVERRIDE or os.path.join(HERE, "liboracle.so")
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+          "-Wall", "-Wno-unused-function"]
 SOURCES = ["gs_oracle.c"]
 HEADERS = ["gs_oracle.h", "project_real.h"]
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
-           "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
-           "-o", LIB + ".tmp"] + [os.path.join(HERE, s) for s in SOURCES] + ["-lm"]
+    cmd = ["gcc"] + CFLAGS + ["-o", LIB + ".tmp"] + [os.path.join(HERE, s) for s in SOURCES] + ["-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -29,6 +32,8 @@ def build(verbose: bool = False) -> str:
 
 
 def needs_build() -> bool:
+    if LIB_OVERRIDE:
+        return False
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)

@@ -565,20 +565,124 @@ def _fd_scene(seed=7, n=6, W=32, H=32, degree=3):
     return means, log_s, quats, logits, sh, cam, G
 
 
+def _branch_scene(kind, seed, n=6, W=32, H=32, f=40.0):
+    """Tiny scenes whose gradients pass through one held branch of the
+    forward, placed in camera space (world means = R^T (p - t)):
+      "guard": three Gaussians with x/z or y/z beyond the guard (1.3 x the
+               half field of view; one beyond both) whose footprints still
+               reach the image, so their Jacobian is taken at the clamp;
+      "cap":   a large front Gaussian with opacity 0.9985 and a smaller one
+               with 0.9993: at the pixel centres nearest their means
+               o exp(power) >= 0.99, so alpha sits on the 0.99 cap;
+      "clamp": DC colours of -3.4 on four (Gaussian, channel) pairs, so
+               0.5 + sum k Y < 0 and the colour clamps at 0."""
+    rng = np.random.default_rng(seed)
+    vm = scenes.look_at(np.array([0.4, -0.3, -0.5]), target=(0.0, 0.0, 3.0))
+    cam = _cam(width=W, height=H, f=f, viewmat=vm)
+    lx = 1.3 * (0.5 * W / f)
+    logits = rng.normal(0.0, 1.0, n)
+    dc = rng.uniform(0.2, 0.8, (1, 3, n))
+    log_s = rng.uniform(-2.4, -1.6, (3, n))
+    if kind == "guard":
+        z = rng.uniform(2.6, 3.6, n)
+        tx = np.concatenate([[lx + 0.1, -(lx + 0.18), 0.3 * rng.uniform(-1, 1)], rng.uniform(-0.4, 0.4, 3)])
+        ty = np.concatenate([[0.2 * rng.uniform(-1, 1), -(lx + 0.12), lx + 0.15], rng.uniform(-0.4, 0.4, 3)])
+        pc = np.stack([tx * z, ty * z, z])
+        log_s[:, :3] = rng.uniform(-1.3, -0.9, (3, 3))
+        logits[:3] = rng.uniform(1.5, 2.5, 3)
+    elif kind == "cap":
+        # the second one's mean on the centre of pixel (8, 23): alpha = o there
+        z = np.concatenate([[2.2, 2.8], rng.uniform(2.6, 4.0, n - 2)])
+        pc = np.stack([np.concatenate([[0.03, (8.5 - 16.0) / f], rng.uniform(-0.4, 0.4, n - 2)]) * z,
+                       np.concatenate([[-0.02, (23.5 - 16.0) / f], rng.uniform(-0.4, 0.4, n - 2)]) * z, z])
+        log_s[:, 0] = rng.uniform(-0.5, -0.2, 3)
+        log_s[:, 1] = rng.uniform(-1.2, -0.8, 3)
+        logits[0], logits[1] = math.log(0.9985 / 0.0015), math.log(0.9993 / 0.0007)
+    elif kind == "clamp":
+        z = rng.uniform(2.5, 4.0, n)
+        pc = np.stack([rng.uniform(-0.4, 0.4, n) * z, rng.uniform(-0.4, 0.4, n) * z, z])
+        log_s = rng.uniform(-2.6, -1.6, (3, n))
+        dc[0, 1, 0] = dc[0, 0, 2] = dc[0, 2, 2] = dc[0, 1, 4] = -3.4
+    else:
+        raise ValueError(kind)
+    R = vm[:, :3].astype(np.float64)
+    t = vm[:, 3].astype(np.float64)
+    means = R.T @ (pc - t[:, None])
+    quats = rng.standard_normal((4, n))
+    sh = np.concatenate([dc, 0.2 * rng.standard_normal((15, 3, n))])
+    G = rng.standard_normal((3, H, W))
+    return means, log_s, quats, logits, sh, cam, G
+
+
+def _scene(kind, seed):
+    return _fd_scene(seed=seed) if kind == "plain" else _branch_scene(kind, seed)
+
+
+def _guard_flags(means, cam):
+    """Per Gaussian: bit 0 when x/z lies beyond the guard, bit 1 for y/z
+    (computed here in fp64 from the camera, independently of the oracle)."""
+    vm = np.asarray(cam.viewmat, np.float64)
+    pc = vm[:, :3] @ means + vm[:, 3:4]
+    lx = cam.guard * 0.5 * cam.width / cam.fx
+    ly = cam.guard * 0.5 * cam.height / cam.fy
+    return ((np.abs(pc[0] / pc[2]) > lx).astype(np.uint8) | ((np.abs(pc[1] / pc[2]) > ly).astype(np.uint8) << 1),
+            np.minimum(np.abs(np.abs(pc[0] / pc[2]) - lx), np.abs(np.abs(pc[1] / pc[2]) - ly)))
+
+
+# a composited alpha within this relative distance of the 0.99 cap flags its
+# pixel; the finite-difference scenes must have none, so no step of h ~ 1e-6
+# can move a cap decision
+_CAP_BAND = 1e-4
+
+
 def _loss_and_structure(means, log_s, quats, logits, sh, cam, G, degree=3):
+    """Loss <G, image> and every discrete decision of the forward: tile lists,
+    n_contrib, the colour clamps, the guard clamps and the pixels with an
+    alpha near the cap."""
     s = np.exp(log_s)
     o = 1.0 / (1.0 + np.exp(-logits))
     p = oracle.project(means, s, quats, o, degree, sh, cam, precision="f64")
     b = oracle.bin_sort(p, cam)
-    out = oracle.render(p, b, cam)
+    out = oracle.render(p, b, cam, bands=dict(cap=_CAP_BAND))
     struct = (tuple(b["vals"]), tuple(b["ranges"].reshape(-1)), out["n_contrib"].tobytes(),
-              p["clamped"].tobytes())
+              p["clamped"].tobytes(), _guard_flags(means, cam)[0].tobytes(), out["capflag"].tobytes())
     return float((G * out["image"]).sum()), struct, p, b, out
 
 
-def test_render_bwd_matches_finite_differences_of_records():
-    means, log_s, quats, logits, sh, cam, G = _fd_scene()
+def _capped_pixels(p, cam, g):
+    """Pixel centres where Gaussian g's o exp(power) reaches the 0.99 cap."""
+    ys, xs = np.mgrid[0:cam.height, 0:cam.width] + 0.5
+    dx, dy = p["u"][g] - xs, p["v"][g] - ys
+    a, b, c = p["conic"][:, g]
+    raw = p["opacity"][g] * np.exp(-0.5 * (a * dx * dx + c * dy * dy) - b * dx * dy)
+    return int((raw >= 0.99).sum())
+
+
+def _branch_reached(kind, means, p, out, cam):
+    """The scene really takes the branch it is built for, clear of its
+    threshold."""
+    vis = p["radius"] > 0
+    assert np.all(out["capflag"] == 0), "an alpha within the band of the cap"
+    flags, margin = _guard_flags(means, cam)
+    assert margin[vis].min() > 1e-3
+    assert np.abs(p["rgb_raw"][:, vis]).min() > 1e-3
+    if kind == "guard":
+        assert flags[0] == 1 and flags[1] == 3 and flags[2] == 2 and np.all(flags[3:] == 0)
+        # each clamped Gaussian composites somewhere (its record gradients are not 0)
+        for g in range(3):
+            assert vis[g] and out["n_contrib"].max() > 0
+    if kind == "cap":
+        assert _capped_pixels(p, cam, 0) >= 5 and _capped_pixels(p, cam, 1) >= 1
+    if kind == "clamp":
+        assert int(np.unpackbits(p["clamped"]).sum()) == 4 and p["clamped"][0] == 2 and p["clamped"][2] == 5
+
+
+@pytest.mark.parametrize("kind,seed", [("plain", 7), ("cap", 1), ("cap", 2)])
+def test_render_bwd_matches_finite_differences_of_records(kind, seed):
+    means, log_s, quats, logits, sh, cam, G = _scene(kind, seed)
     _, _, p, b, out = _loss_and_structure(means, log_s, quats, logits, sh, cam, G)
+    if kind != "plain":
+        _branch_reached(kind, means, p, out, cam)
     g2 = oracle.render_bwd(p, b, cam, G)
     h = 1e-6
     keys = [("u", None), ("v", None), ("conic", 0), ("conic", 1), ("conic", 2), ("opacity", None),
@@ -596,8 +700,9 @@ def test_render_bwd_matches_finite_differences_of_records():
                     pp[name][g] += sgn * h
                 else:
                     pp[name][row, g] += sgn * h
-                o2 = oracle.render(pp, b, cam)
+                o2 = oracle.render(pp, b, cam, bands=dict(cap=_CAP_BAND))
                 assert np.array_equal(o2["n_contrib"], out["n_contrib"])
+                assert np.array_equal(o2["capflag"], out["capflag"])
                 vals.append((G * o2["image"]).sum())
             num = (vals[0] - vals[1]) / (2 * h)
             assert abs(num - g2[q, g]) <= 1e-6 * max(1.0, abs(num)), (name, row, g, num, g2[q, g])
@@ -605,11 +710,14 @@ def test_render_bwd_matches_finite_differences_of_records():
     assert checked >= 9 * 4
 
 
-@pytest.mark.parametrize("seed", [7, 8])
-def test_full_backward_matches_finite_differences(seed):
-    means, log_s, quats, logits, sh, cam, G = _fd_scene(seed=seed)
+@pytest.mark.parametrize("kind,seed", [("plain", 7), ("plain", 8), ("guard", 1), ("guard", 2), ("cap", 1), ("cap", 2),
+                                       ("clamp", 1), ("clamp", 2)])
+def test_full_backward_matches_finite_differences(kind, seed):
+    means, log_s, quats, logits, sh, cam, G = _scene(kind, seed)
     L0, s0, p, b, out = _loss_and_structure(means, log_s, quats, logits, sh, cam, G)
     assert (p["radius"] > 0).sum() >= 4
+    if kind != "plain":
+        _branch_reached(kind, means, p, out, cam)
     g2 = oracle.render_bwd(p, b, cam, G)
     grads = oracle.project_bwd(means, np.exp(log_s), quats, 1 / (1 + np.exp(-logits)), 3, sh, cam, p, g2)
     params = dict(means=means, log_scales=log_s, quats=quats, opacity_logits=logits, sh=sh)
@@ -619,6 +727,10 @@ def test_full_backward_matches_finite_differences(seed):
         flat_idx = list(np.ndindex(arr.shape))
         if len(flat_idx) > 60:
             flat_idx = [flat_idx[i] for i in rng.choice(len(flat_idx), 60, replace=False)]
+            if kind == "clamp":
+                # every coefficient of the clamped channels, and of their
+                # unclamped neighbours, besides the random sample
+                flat_idx += [(j, ch, g) for j in range(0, 16, 3) for ch in range(3) for g in (0, 2, 4)]
         for idx in flat_idx:
             vals = []
             for sgn in (1, -1):
