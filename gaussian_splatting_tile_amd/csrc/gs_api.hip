@@ -24,7 +24,9 @@ bool camera_ok(const gs_camera *c)
     if (!finite_pos(c->fx) || !finite_pos(c->fy) || !isfinite(c->cx) || !isfinite(c->cy)) return false;
     for (int i = 0; i < 12; i++)
         if (!isfinite(c->viewmat[i])) return false;
-    if (!isfinite(c->znear) || !finite_pos(c->guard)) return false;
+    // znear >= 0: every kept depth is then positive, the range on which the
+    // depth key (the fp32 bit pattern of z) orders like z itself
+    if (!isfinite(c->znear) || !(c->znear >= 0.0f) || !finite_pos(c->guard)) return false;
     if (!isfinite(c->lod_min_radius_px) || c->lod_min_radius_px < 0.0f) return false;
     if (!isfinite(c->time)) return false;
     return true;
@@ -196,8 +198,8 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
                         uint32_t *schedule, const gs_camera *camera, const float *bg, float *image,
                         float *final_T, uint32_t *n_contrib, void *stream)
 {
-    if (!camera_ok(camera) || !tile_ranges || !schedule || !bg || !image || !final_T || !n_contrib ||
-        !al16(splats))
+    if (!camera_ok(camera) || !splats || !vals || !tile_ranges || !schedule || !bg || !image || !final_T ||
+        !n_contrib || !al16(splats))
         return GS_ERR_INVALID_ARG;
     for (int c = 0; c < 3; c++)
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
@@ -227,8 +229,8 @@ gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views, const f
         if (!isfinite(bg[c])) return GS_ERR_INVALID_ARG;
     for (int v = 0; v < n_views; v++) {
         const gs_fwd_view &w = views[v];
-        if (!camera_ok(&w.camera) || !w.tile_ranges || !w.schedule || !w.image || !w.final_T || !w.n_contrib ||
-            !al16(w.splats))
+        if (!camera_ok(&w.camera) || !w.splats || !w.vals || !w.tile_ranges || !w.schedule || !w.image ||
+            !w.final_T || !w.n_contrib || !al16(w.splats))
             return GS_ERR_INVALID_ARG;
     }
     for (int v0 = 0; v0 < n_views; v0 += kMaxBlendViews) {

@@ -86,7 +86,9 @@ typedef struct gs_camera {
     float viewmat[12];          /* row-major 3x4 world->camera [R | t];
                                    camera axes x right, y down, z forward     */
     float znear;                /* Gaussians with camera z <= znear are culled
-                                   (0.2 in every workload)                     */
+                                   (0.2 in every workload); must be >= 0, so
+                                   that every kept depth is positive (the sort
+                                   key is the bit pattern of the fp32 depth)   */
     float guard;                /* Jacobian taken at x/z, y/z clamped to guard
                                    x the half field of view (1.3)              */
     float lod_min_radius_px;    /* distance-LOD gate: cull when the undilated
@@ -319,7 +321,8 @@ gs_status gs_bin_sort_views(int32_t n_views, const gs_sort_view *views /* host *
  * Tiles are processed by persistent waves in the schedule's order; the
  * result does not depend on it.  The call uses the schedule's forward queue
  * counters and leaves them reset, so calls sharing a schedule must be
- * ordered on one stream.
+ * ordered on one stream.  splats and vals must not be NULL, even for a view
+ * with no visible Gaussian (pass buffers of at least one element).
  * Errors: GS_ERR_INVALID_ARG. */
 gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals,
                         const uint32_t *tile_ranges, uint32_t *schedule,
@@ -353,7 +356,8 @@ typedef struct gs_fwd_view {
  * long tiles overlap the others' work instead of idling the device.  The
  * outputs are those of n_views gs_render_fwd calls, plus the optional
  * blending weights.  A launch uses the forward queue counters of its first
- * view's schedule.
+ * view's schedule.  As for gs_render_fwd, no view's splats or vals may be
+ * NULL.
  * Errors: GS_ERR_INVALID_ARG. */
 gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views,
                               const float *bg /* host [3] */, void *stream);

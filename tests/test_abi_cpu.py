@@ -140,6 +140,29 @@ def test_host_side_argument_errors_without_device():
     views[1].workspace_bytes = 16
     assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_WORKSPACE
     bgv = (C.c_float * 3)(0.0, 0.0, 0.0)
+    # a negative near plane would let depths of either sign through, which the
+    # depth key does not order; it is refused like any other bad camera field
+    camz = B.GsCamera()
+    camz.width, camz.height, camz.fx, camz.fy, camz.guard = 16, 16, 10.0, 10.0, 1.3
+    gz = B.GsGaussians()
+    gz.n = 0
+    assert L.gs_project(C.byref(gz), C.byref(camz), None, None) == B.GS_OK
+    camz.znear = -0.1
+    assert L.gs_project(C.byref(gz), C.byref(camz), None, None) == B.GS_ERR_INVALID_ARG
+    camz.znear = float("nan")
+    assert L.gs_project(C.byref(gz), C.byref(camz), None, None) == B.GS_ERR_INVALID_ARG
+    camz.znear = 0.2
+    # the forward refuses NULL records or list entries (a GPU fault otherwise)
+    d = 0x1000
+    assert L.gs_render_fwd(None, d, d, d, C.byref(camz), C.cast(bgv, C.c_void_p), d, d, d, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_render_fwd(d, None, d, d, C.byref(camz), C.cast(bgv, C.c_void_p), d, d, d, None) == B.GS_ERR_INVALID_ARG
+    fv = (B.GsFwdView * 1)()
+    fv[0].camera = camz
+    fv[0].splats, fv[0].vals = d, None
+    fv[0].tile_ranges = fv[0].schedule = fv[0].image = fv[0].final_T = fv[0].n_contrib = d
+    assert L.gs_render_fwd_views(1, fv, C.cast(bgv, C.c_void_p), None) == B.GS_ERR_INVALID_ARG
+    fv[0].splats, fv[0].vals = None, d
+    assert L.gs_render_fwd_views(1, fv, C.cast(bgv, C.c_void_p), None) == B.GS_ERR_INVALID_ARG
     assert L.gs_render_bwd_screen(None, 10, None, None, None, None, None, 0, C.cast(bgv, C.c_void_p), None,
                                   None, None, None, None, 0, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_project_bwd(C.byref(gs), 1, None, None, None, None, None) == B.GS_ERR_UNSUPPORTED
