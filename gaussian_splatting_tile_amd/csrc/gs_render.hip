@@ -406,13 +406,17 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                 for (int r = 0; r < kPx; r++) {
                     if (!((strips >> r) & 1u)) continue;
                     const float raw = alpha_raw(ct, q.z, dy0 - 4.0 * r);
-                    const float alpha = fminf(kAlphaMax, raw);
                     const bool take = T[r] >= kTMin && raw >= kAlphaMin;
-                    const float w = take ? alpha * T[r] : 0.0f;
+                    const float alpha = take ? fminf(kAlphaMax, raw) : 0.0f;
+                    const float w = alpha * T[r];
                     c0[r] = fmaf(rgb.x, w, c0[r]);
                     c1[r] = fmaf(rgb.y, w, c1[r]);
                     c2[r] = fmaf(rgb.z, w, c2[r]);
-                    T[r] = T[r] - w;
+                    // T (1 - alpha) with one rounding: T - w would round
+                    // alpha T first, an error of up to 50 ulp of the result
+                    // at alpha = 0.99, which the backward's recovery of T
+                    // by division then carries to every entry in front
+                    T[r] = fmaf(-alpha, T[r], T[r]);
                     last[r] = take ? pos : last[r];
                     if (kWeight) wsum += w;
                 }

@@ -5,11 +5,12 @@ far off screen and at the guard band, opacities at and around the 1/255 skip
 threshold and the 0.99 cap, DC colours that clamp, SH degrees 0 to 3.
 Records and bins must be bit-exact and images within 1e-4 under the
 near-threshold protocol, as for the regular workloads; gradients within 1e-3
-relative L2 per tensor and elementwise within 1e-3 of max(|r|, 1e-2 max|r|).
-The floor is 1e-2 here instead of 1e-3: Gaussians larger than the image make
-a gradient element a sum of ~1e5 per-pixel terms that can cancel to 1e-3 of
-the tensor's largest value, while the fp32 per-tile partial sums carry ~1e-5
-absolute error (observed: 8e-6 on an element of 6e-3, tensor maximum 6)."""
+relative L2 per tensor and elementwise within 1e-3 of max(|r|, 1e-3 max|r|),
+the bar of every other workload.  The hardest element is the colour
+gradient of a Gaussian just past the near plane that covers the whole image:
+a sum of ~5e4 per-pixel terms that cancels to ~4e-6 of their absolute sum,
+so it needs every pixel's recovered transmittance to ~1e-6 relative (the
+forward's one-rounding update of T is what gives that)."""
 
 import numpy as np
 import pytest
@@ -77,4 +78,4 @@ def test_awkward_mixtures_forward_and_backward(seed, degree):
     G = _upstream(cam, 3000 + seed)
     ref, Gz, nc, amb = _oracle_grads(sc, 0, G)
     gpu = _gpu_grads(sc, [(0, Gz)])
-    _compare(gpu, ref, nc, name, floor=1e-2)
+    _compare(gpu, ref, nc, name)
