@@ -18,10 +18,19 @@ scene_10m_4k (10M Gaussians, SH stored fp16, 3840x2160, f = 2800; each step
 first builds the importance mask keeping 30 % of the Gaussians by their
 Exp(1) scores, and the projection applies it and the 0.5 px LOD gate).
 
-Prints ONE JSON line: value = forward ms/frame (project + bin/sort + blend),
-plus fwd+bwd ms/frame, per-call averages, the roofline of the dominant
-kernel (the forward blend, one kernel per gs_render_fwd call, timed with
-events on its stream), and the CPU oracle timed on a bounded sample.
+Each step reads the views' key counts back to the host after the sort (one
+synchronisation, inside the timed region) and checks them against the key
+capacities, which are sized once with 25 % headroom over a probe pass, as a
+training loop would.  Steps are timed warm (back to back) and cold (a 2 GiB
+device copy before each step scrubs the 256 MB last-level cache and the L2).
+
+Prints ONE JSON line: value = median warm forward ms/frame (project +
+bin/sort + K readback + blend), plus p90 and the cold figures, fwd+bwd
+ms/frame, per-call medians, the rooflines of the two blend kernels (VALU lane
+slots against the chip's published rate and against the rate measured on the
+same GPU by csrc/peaks.hip), the HBM fractions of the projection, the sort
+and the projection backward, and the CPU oracle timed on a bounded sample
+(all cores and one core).
 """
 
 from __future__ import annotations
@@ -63,25 +72,34 @@ def parse():
     ap.add_argument("--scores-from-weights", action="store_true",
                     help="workloads with an importance mask: score each Gaussian by its blending weights "
                          "summed over the views (an untimed pass before the steps) instead of the synthetic scores")
+    ap.add_argument("--cold-steps", type=int, default=None,
+                    help="steps timed after a cache scrub each (default: --steps; 0 skips them)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for "
                          "calibrating the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
-# Algorithmic work of the forward blend per evaluated (pixel, Gaussian) pair,
-# in fp32 VALU lane-op slots: 2 sub (offset), 5 mul/fma (quadratic form),
-# v_exp_f32 (quarter rate: 4 slots), 1 mul (o * G), 1 min (cap), 1 compare
-# (skip), 1 mul (alpha T), 3 fma (colour), 1 sub (T), 1 select (n_contrib),
-# 1 compare (stop) = 21; taken as 20 (the select of the stop is fused).
-# Pairs are counted only for list entries that can reach alpha >= 1/255 at
-# some pixel centre of their tile: the others are provably skipped by every
-# pixel, and the kernel drops them before the per-pixel loop.
-BLEND_FWD_SLOTS_PER_PAIR = 20
-# 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: one non-packed fp32 VALU op per lane
-# per clock (packed-fp32 instructions are not used by this library).
+# Algorithmic work of the forward blend per (pixel, Gaussian) pair, in VALU
+# lane-op slots (one slot = one non-packed lane operation of a full-rate
+# instruction): 2 sub (offset), 5 mul/fma (quadratic form), 1 mul (o * G),
+# 1 min (cap), 1 compare (skip), 1 mul (alpha T), 3 fma (colour), 1 sub (T),
+# 1 select (n_contrib) = 16, plus v_exp_f32 at its measured cost of 2 slots
+# (half rate on this chip: csrc/peaks.hip) = 18.  Pairs are counted only for
+# list entries that can reach alpha >= 1/255 somewhere in the pixel's 16x4
+# strip of its tile (P_needed): the others are provably skipped by every
+# such pixel, and the kernel drops them before the per-pixel loop.
+BLEND_FWD_SLOTS_PER_PAIR = 18
+# The backward per composited pair: ~45 lane ops of reverse compositing
+# (transmittance recovery, colour and alpha gradients, the power's partials
+# and the covariance sums) plus v_exp_f32 and v_rcp_f32 at 2 slots each = 49.
+BLEND_BWD_SLOTS_PER_PAIR = 49
+# 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: one non-packed fp32 (or fp64) FMA
+# per lane per clock (packed-fp32 instructions are not used by this library).
 VALU_PEAK_T = 256 * 64 * 2.4e9 / 1e12
 HBM_PEAK_GBPS = 8000.0
+CAPACITY_HEADROOM = 1.25
 
 
 def main():
@@ -110,6 +128,13 @@ def main():
         print(f"# calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written",
               file=sys.stderr, flush=True)
         del src, dst
+
+    # the GPU's own peak rates (csrc/peaks.hip): fp32/fp64 FMA, exp, LDS, copy
+    peaks_measured = None
+    if not args.no_peaks:
+        from gaussian_splatting_tile_amd import peaks
+        peaks_measured = peaks.measure(torch, dev)
+        torch.cuda.synchronize()
 
     t0 = time.time()
     if args.workload == "scene_1m":
@@ -174,8 +199,11 @@ def main():
     else:
         gs = B.gaussians_struct(g, sc.sh_degree)
 
-    # per-view buffers with the exact key capacity (K is deterministic)
-    bufs, Ks = [], []
+    # per-view buffers: key capacity = 25 % over a probe pass (rounded up to
+    # 1024); every step reads the true K back and checks it
+    k_all = torch.zeros(views, dtype=torch.int64, device=dev)
+    k_host = torch.zeros(views, dtype=torch.int64).pin_memory()
+    bufs, Ks, caps = [], [], []
     for v in range(views):
         cam = sc.cameras[v]
         probe = B.ViewBuffers(sc.n, cam, 16 * sc.n, with_backward=False)
@@ -183,12 +211,16 @@ def main():
         torch.cuda.synchronize()
         k = int(probe.k_total.item())
         del probe
-        b = B.ViewBuffers(sc.n, cam, k)
+        cap = int(math.ceil(k * CAPACITY_HEADROOM / 1024.0)) * 1024
+        b = B.ViewBuffers(sc.n, cam, cap)
+        b.k_total = k_all[v:v + 1]
         b.dL = f(sc.upstream(v))
-        b.bwd_ws = torch.empty(B.render_bwd_screen_workspace_bytes(k), dtype=torch.uint8, device=dev)
+        b.bwd_ws = torch.empty(B.render_bwd_screen_workspace_bytes(cap), dtype=torch.uint8, device=dev)
         b.g2 = torch.empty((sc.n, 9), dtype=torch.float32, device=dev)
         bufs.append(b)
         Ks.append(k)
+        caps.append(cap)
+    caps_t = torch.tensor(caps, dtype=torch.int64)
     K_sh = (sc.sh_degree + 1) ** 2
     grads = dict(means=torch.zeros((3, sc.n), device=dev), log_scales=torch.zeros((3, sc.n), device=dev),
                  quats=torch.zeros((4, sc.n), device=dev), opacity_logits=torch.zeros(sc.n, device=dev),
@@ -227,37 +259,41 @@ def main():
     # (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
     lanes = [stream] + side
-    ev = {k: [] for k in names}
-    step_ev = []
+    # a 2 GiB device copy (1 GiB read + 1 GiB written) before each cold step
+    # pushes the step's inputs out of the 256 MB last-level cache and the L2
+    n_cold = args.steps if args.cold_steps is None else args.cold_steps
+    scrub = (torch.empty(1 << 28, dtype=torch.float32, device=dev),
+             torch.empty(1 << 28, dtype=torch.float32, device=dev)) if n_cold > 0 else None
+    rec = {"warm": dict(ev={k: [] for k in names}, steps=[]), "cold": dict(ev={k: [] for k in names}, steps=[])}
 
-    def step(record: bool):
+    def step(mode):
         for gr in grads.values():
             gr.zero_()
-        e_fwd0 = torch.cuda.Event(enable_timing=True)
-        e_fwd1 = torch.cuda.Event(enable_timing=True)
-        e_end = torch.cuda.Event(enable_timing=True)
+        if mode == "cold":
+            scrub[1].copy_(scrub[0])
+        R = rec[mode] if mode else None
+        E = lambda: torch.cuda.Event(enable_timing=True)
+        e_fwd0, e_sort0, e_sort1, e_fwd1, e_end = E(), E(), E(), E(), E()
         e_fwd0.record(stream)
 
         def timed(name, fn, st=stream):
-            if not record:
+            if R is None:
                 fn()
                 return
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a, b = E(), E()
             a.record(st)
             fn()
             b.record(st)
-            ev[name].append((a, b))
+            R["ev"][name].append((a, b))
 
         if use_mask:
             timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
         # the views' records in one pass over the Gaussians
         timed("project_batch", lambda: B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
                                                        stream))
-        go = torch.cuda.Event()
-        go.record(stream)
+        e_sort0.record(stream)
         for st in side:
-            st.wait_event(go)
+            st.wait_event(e_sort0)
         if args.sort == "batched":
             # the views split into one group per stream, each group sorted
             # by one gs_bin_sort_views call
@@ -275,6 +311,16 @@ def main():
             joined = torch.cuda.Event()
             joined.record(st)
             stream.wait_event(joined)
+        e_sort1.record(stream)
+        # K of every view back to the host (the one synchronisation of a
+        # step): a view whose K passed its capacity would be sorted again
+        # with a larger buffer
+        k_host.copy_(k_all, non_blocking=True)
+        e_k = torch.cuda.Event()
+        e_k.record(stream)
+        e_k.synchronize()
+        if bool((k_host > caps_t).any()):
+            raise RuntimeError(f"key capacity exceeded: K {k_host.tolist()} capacities {caps}")
         # the 8 views' blends share one work queue
         if wts is not None:
             wts.zero_()
@@ -294,37 +340,134 @@ def main():
                                                         adam["mb"], adam["vb"], step=adam["t"], lr=1e-3,
                                                         stream=stream))
         e_end.record(stream)
-        if record:
-            step_ev.append((e_fwd0, e_fwd1, e_end))
+        if R is not None:
+            R["steps"].append((e_fwd0, e_sort0, e_sort1, e_fwd1, e_end))
 
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
     print(f"# warmup done; K per view {Ks}", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("warm")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in step_ev) / (args.steps * views)
-    tot_ms = sum(a.elapsed_time(c) for a, _, c in step_ev) / (args.steps * views)
-    per_call = {k: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None) for k, v in ev.items()}
+    for _ in range(n_cold):
+        step("cold")
+    torch.cuda.synchronize()
+    del scrub
+    if list(k_host.tolist()) != Ks:
+        raise RuntimeError(f"K changed between passes: {k_host.tolist()} vs {Ks}")
     ms_per_step = wall * 1e3 / args.steps
+    print(f"# timed {args.steps} warm and {n_cold} cold steps", file=sys.stderr, flush=True)
 
-    # algorithmic work of the blend per view, from the outputs: a pixel that
-    # stopped examined n_contrib entries of its tile's list, otherwise all.
-    p_eval, p_need, p_tile = [], [], []
+    def stats(xs):
+        if not xs:
+            return None
+        a = np.sort(np.asarray(xs, dtype=np.float64))
+        return dict(median=round(float(np.median(a)), 4), p90=round(float(np.percentile(a, 90)), 4),
+                    mean=round(float(a.mean()), 4))
+
+    def summary(R):
+        st = R["steps"]
+        if not st:
+            return None
+        fwd = [a.elapsed_time(d) / views for a, _, _, d, _ in st]
+        tot = [a.elapsed_time(e) / views for a, _, _, _, e in st]
+        sort = [b.elapsed_time(c) for _, b, c, _, _ in st]
+        calls = {k: stats([a.elapsed_time(b) for a, b in v]) for k, v in R["ev"].items()}
+        return dict(fwd_ms_per_frame=stats(fwd), fwd_bwd_ms_per_frame=stats(tot) if do_bwd else None,
+                    sort_phase_ms=stats(sort), per_call_ms={k: v for k, v in calls.items() if v is not None})
+
+    warm, cold = summary(rec["warm"]), summary(rec["cold"])
+    fwd_ms = warm["fwd_ms_per_frame"]["median"]
+    tot_ms = warm["fwd_bwd_ms_per_frame"]["median"] if do_bwd else None
+    med = lambda k: warm["per_call_ms"][k]["median"] if k in warm["per_call_ms"] else None
+
+    # algorithmic work of the blends per view, from the outputs (untimed)
+    counts = [blend_pairs(torch, b) for b in bufs]
+    p_eval = [c["eval"] for c in counts]
+    p_need = [c["needed"] for c in counts]
+    p_tile = [c["tile"] for c in counts]
+    p_comp = [c["composited"] for c in counts]
+    p_bwd = [c["bwd_examined"] for c in counts]
+    vis = torch.zeros(sc.n, dtype=torch.bool, device=dev)
+    n_vis = []
     for b in bufs:
-        pe, pn, pt = blend_pairs(torch, b)
-        p_eval.append(pe)
-        p_need.append(pn)
-        p_tile.append(pt)
-    # one forward-blend launch covers all the step's views
-    t_blend_s = per_call["render_fwd_batch"] / 1e3
-    achieved = sum(p_need) * BLEND_FWD_SLOTS_PER_PAIR / t_blend_s / 1e12
+        r = b.splats[: sc.n, 3].view(torch.int32) > 0
+        n_vis.append(int(r.sum().item()))
+        vis |= r
+    n_any = int(vis.sum().item())
+    del vis
+    fma_meas = peaks_measured["fma32"] / 1e12 if peaks_measured else None
+    copy_meas = peaks_measured["copy"] / 1e9 if peaks_measured else None
+
+    def valu_roofline(kernel, pairs, slots, ms, note):
+        ach = sum(pairs) * slots / (ms / 1e3) / 1e12
+        out = {"kernel": kernel, "bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_T, 2),
+               "unit": "Tslot/s", "frac": round(ach / VALU_PEAK_T, 4)}
+        if fma_meas:
+            out["peak_measured"] = round(fma_meas, 2)
+            out["frac_measured"] = round(ach / fma_meas, 4)
+        out["work_unit"] = note
+        return out
+
+    roof_fwd = valu_roofline(
+        "render_fwd_kernel (forward blend)", p_need, BLEND_FWD_SLOTS_PER_PAIR, med("render_fwd_batch"),
+        f"{BLEND_FWD_SLOTS_PER_PAIR} VALU lane-op slots per (pixel, Gaussian) pair whose entry can reach "
+        f"alpha >= 1/255 in the pixel's 16x4 strip of its tile (P_needed), summed over the {views} views of one "
+        f"launch, over the launch's median event-timed duration; a slot is one lane of a full-rate non-packed "
+        f"VALU instruction (v_exp_f32, half rate, counts 2); peak = 256 CU x 64 lanes x 2.4 GHz, "
+        f"peak_measured = non-packed fp32 FMA rate measured on this GPU")
+    roof_fwd["traffic"] = measured_traffic() if args.workload == "scene_1m" else None
+    roof_bwd = None
+    if do_bwd:
+        roof_bwd = valu_roofline(
+            "render_bwd_kernel + sum_partials_kernel (one gs_render_bwd_screen_views call)", p_comp,
+            BLEND_BWD_SLOTS_PER_PAIR, med("render_bwd_batch"),
+            f"{BLEND_BWD_SLOTS_PER_PAIR} VALU lane-op slots per composited (pixel, Gaussian) pair (alpha >= 1/255 "
+            f"before the pixel's last composited entry), summed over the {views} views, over the call's median "
+            f"duration (the blend backward and the per-Gaussian sums of its partial rows)")
+
+    # algorithmic HBM bytes of the memory-bound stages (what the method must
+    # move once for the step's views: parameters and SH read once per batch,
+    # one record per view written, gradients read-modified-written once)
+    sh_b = {"f32": 12, "f16": 6, "q8": 3}["q8" if args.sh_q8 else ("f16" if sc.sh_fp16 is not None else "f32")]
+    sh_bytes = sh_b * K_sh + (8.0 * 3 * K_sh / 256.0 if args.sh_q8 else 0.0)
+    geo = 44 + (16 if sc.velocity is not None else 0)
+    bytes_proj = sc.n * geo + (sc.n if use_mask else 0) + views * sc.n * 48 + n_any * sh_bytes
+    # the sort per the survey's per-unit model of a 64-bit LSB radix sort:
+    # scan 8 B x N, duplication 20 B x N + 12 B x K, 6 passes of 24 B + an
+    # 8 B histogram read per key, ranges 8 B x K
+    bytes_sort = sum(8 * sc.n + 20 * sc.n + 12 * k + (8 + 6 * 24) * k + 8 * k for k in Ks)
+    bytes_pbwd = n_any * (geo + sh_bytes) + sum(nv * (48 + 36) for nv in n_vis) + n_any * 2 * (geo + 12 * K_sh)
+
+    def hbm(name, nbytes, ms, model):
+        if ms is None:
+            return None
+        gbps = nbytes / (ms / 1e3) / 1e9
+        out = {"kernel": name, "bytes": int(nbytes), "ms": ms, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+               "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "model": model}
+        if copy_meas:
+            out["peak_measured_copy"] = round(copy_meas, 1)
+            out["frac_measured"] = round(gbps / copy_meas, 4)
+        return out
+
+    hbm_stages = {
+        "project": hbm("project_kernel (one launch, all views)", bytes_proj, med("project_batch"),
+                       f"N x {geo} B parameters + {views} x N x 48 B records + {sh_bytes:g} B of SH per Gaussian "
+                       f"visible in any view" + (" + N B mask" if use_mask else "")),
+        "sort": hbm("gs_bin_sort_views (all views, 4 streams: the sort phase)",
+                    bytes_sort, warm["sort_phase_ms"]["median"],
+                    "per view 28 B x N + 180 B x K (scan, duplication, 6 radix passes, ranges)"),
+        "project_bwd": (hbm("project_bwd_color_kernel + project_bwd_geom_kernel (one call, all views)",
+                            bytes_pbwd, med("project_bwd_batch"),
+                            f"per Gaussian visible in any view {geo} B + {sh_bytes:g} B parameters read and "
+                            f"2 x ({geo} + {12 * K_sh}) B gradients read and written; per view and visible "
+                            f"Gaussian 48 B record + 36 B screen-space sums") if do_bwd else None),
+    }
 
     cam0 = sc.cameras[0]
     res = {
@@ -352,52 +495,51 @@ def main():
                    "step": ("importance mask, then " if use_mask else "") +
                            "batched project, " +
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
-                           ", batched blend fwd of all views" +
+                           ", K read back and checked, batched blend fwd of all views" +
                            (" with per-Gaussian blending weights" if args.weights else "") +
                            (" (moving Gaussians, views spread over the time window)" if args.motion else "") +
                            (", then batched blend bwd of all views + one batched project bwd" if do_bwd else "") +
                            (f", then the fused SH Adam update ({args.sh_adam})" if adam is not None else "")},
         "fwd_ms_per_frame": round(fwd_ms, 4),
         "fwd_bwd_ms_per_frame": round(tot_ms, 4) if do_bwd else None,
-        "per_call_ms": {k: (round(v, 4) if v is not None else None) for k, v in per_call.items()},
+        "timing": {"statistic": "median over steps (p90 and mean beside it); events on the streams the calls run on",
+                   "warm": warm, "cold": cold,
+                   "cold_scrub": "2 GiB device copy (1 GiB read + 1 GiB written) before each cold step"},
+        "per_call_ms": {k: med(k) for k in names},
         "K_per_view": Ks,
+        "key_capacity_per_view": caps,
+        "visible_per_view": n_vis,
+        "visible_any_view": n_any,
         "P_eval_per_view": p_eval,
-        "P_needed_per_view": p_need,
         "P_tile_per_view": p_tile,
-        "roofline": {"kernel": "render_fwd_kernel (forward blend)", "bound": "alu",
-                     "achieved": round(achieved, 3), "peak": round(VALU_PEAK_T, 2), "unit": "TFLOP/s",
-                     "frac": round(achieved / VALU_PEAK_T, 4),
-                     "traffic": measured_traffic() if args.workload == "scene_1m" else None,
-                     "work_unit": f"{BLEND_FWD_SLOTS_PER_PAIR} fp32 VALU lane-op slots per evaluated "
-                                  f"(pixel, Gaussian) pair whose entry can reach alpha >= 1/255 in the pixel's 16x4 strip of its tile "
-                                  f"(P_needed), summed over the {views} views of one launch; "
-                                  f"peak = 256 CU x 64 lanes x 2.4 GHz"},
+        "P_needed_per_view": p_need,
+        "P_composited_per_view": p_comp,
+        "P_bwd_examined_per_view": p_bwd,
+        "roofline": roof_fwd,
+        "roofline_bwd": roof_bwd,
+        "hbm_stages": hbm_stages,
+        "peaks_measured": ({"fp32_fma_Tlane_per_s": round(peaks_measured["fma32"] / 1e12, 2),
+                            "fp64_fma_Tlane_per_s": round(peaks_measured["fma64"] / 1e12, 2),
+                            "exp_f32_Tlane_per_s": round(peaks_measured["exp32"] / 1e12, 2),
+                            "exp_cost_slots_alone": round(peaks_measured["fma32"] / peaks_measured["exp32"], 2),
+                            "exp_cost_slots_among_4_fma": round(peaks_measured["fma32"] / peaks_measured["mix"] - 4, 2),
+                            "lds_read_TBps": round(peaks_measured["lds"] / 1e12, 1),
+                            "copy_GBps": round(peaks_measured["copy"] / 1e9, 1),
+                            "source": "csrc/peaks.hip, run once before the steps"}
+                           if peaks_measured else None),
     }
     if adam is not None:
-        t_adam = per_call["sh_adam"] / 1e3
+        t_adam = med("sh_adam") / 1e3
         gbps = adam["units"] * adam["bytes_per_unit"] / t_adam / 1e9
-        # the measured counterpart of the spec peak: a plain 1 GiB device copy
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
-        del src, dst
         res["sh_adam"] = {"kernel": "adam_q8_kernel" if args.sh_adam == "q8" else "adam_f32_kernel",
                           "state": "8-bit log-domain moments, fp16 values" if args.sh_adam == "q8"
                           else "fp32 moments and values",
-                          "units": adam["units"], "ms": round(per_call["sh_adam"], 4),
+                          "units": adam["units"], "ms": med("sh_adam"),
                           "bytes_per_unit": adam["bytes_per_unit"], "bound": "hbm",
                           "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                          "measured_copy_GBps": round(copy_gbps, 1),
-                          "frac_of_measured_copy": round(gbps / copy_gbps, 4),
+                          "measured_copy_GBps": round(copy_meas, 1) if copy_meas else None,
+                          "frac_of_measured_copy": round(gbps / copy_meas, 4) if copy_meas else None,
                           "traffic": (measured_adam_traffic(args.sh_adam) if args.workload == "scene_5m"
                                       else None)}
     # the oracle is timed beside the default workload only (a 10M / 4K view
@@ -453,10 +595,14 @@ def measured_traffic():
 
 
 def blend_pairs(torch, b):
-    """(pairs examined under the compositing rule, pairs among them whose list
-    entry can reach alpha >= 1/255 at some pixel centre of the pixel's 16x4
-    strip of its tile (rows 4r .. 4r+3, the strip a wave's pixel r covers),
-    the same count with the whole tile instead of the strip)."""
+    """Per view, from its outputs: pairs examined under the compositing rule
+    ("eval": a pixel that stopped examined n_contrib entries of its tile's
+    list, otherwise all of them); among them those whose list entry can reach
+    alpha >= 1/255 at some pixel centre of the pixel's 16x4 strip of its tile
+    (rows 4r .. 4r+3, the strip a wave's pixel r covers: "needed"), the same
+    with the whole tile ("tile"); the pairs the pixel composited ("composited":
+    alpha >= 1/255 before its last composited entry) and the pairs the
+    backward must examine ("bwd_examined": the entries before n_contrib)."""
     cam = b.cam
     TX, TY = cam.tiles_x, cam.tiles_y
     rng = b.ranges.long()
@@ -464,14 +610,18 @@ def blend_pairs(torch, b):
     K = int(L.sum().item())
     start = rng[:, 0]
     Lpix = L.reshape(TY, TX).repeat_interleave(16, 0).repeat_interleave(16, 1)[: cam.height, : cam.width]
-    examined = torch.where(b.final_T < 1e-4, b.n_contrib.long(), Lpix)
+    nc = b.n_contrib.long()
+    examined = torch.where(b.final_T < 1e-4, nc, Lpix)
     p_eval = int(examined.sum().item())
+    p_bwd = int(nc.sum().item())
     tile = torch.repeat_interleave(torch.arange(TX * TY, device=rng.device), L)
     sp = b.splats[b.vals[:K].long()].double()
     u, v, a, bb, c, o = sp[:, 0], sp[:, 1], sp[:, 4], sp[:, 5], sp[:, 6], sp[:, 7]
-    dxl = (tile % TX).double() * 16 + 0.5 - u
-    dyl = (tile // TX).double() * 16 + 0.5 - v
-    del sp, tile
+    del sp
+    tx0 = (tile % TX).double() * 16
+    ty0 = (tile // TX).double() * 16
+    dxl = tx0 + 0.5 - u
+    dyl = ty0 + 0.5 - v
     q = lambda dx, dy: a * dx * dx + 2 * bb * dx * dy + c * dy * dy
 
     def box_keep(dyb, h):
@@ -500,13 +650,40 @@ def blend_pairs(torch, b):
     p_need = 0
     for r in range(4):
         p_need += count(keep_tile & box_keep(dyl + 4 * r, 3), (strip == r).long())
-    return p_eval, p_need, p_tile
+    del keep_tile
+    # composited pairs: for each of the 256 pixel offsets of a tile, every
+    # list entry whose position is before that pixel's n_contrib and whose
+    # o exp(power) reaches 1/255 there
+    pos = torch.arange(K, device=u.device) - start[tile]
+    ncp = torch.zeros((TY * 16, TX * 16), dtype=torch.long, device=u.device)
+    ncp[: cam.height, : cam.width] = nc
+    txi, tyi = (tile % TX) * 16, (tile // TX) * 16
+    p_comp = 0
+    for oy in range(16):
+        for ox in range(16):
+            n_here = ncp[tyi + oy, txi + ox]
+            dx = u - (tx0 + (ox + 0.5))
+            dy = v - (ty0 + (oy + 0.5))
+            power = -0.5 * (a * dx * dx + c * dy * dy) - bb * dx * dy
+            p_comp += int(((pos < n_here) & (o * torch.exp(power) >= 1.0 / 255.0)).sum().item())
+    return dict(eval=p_eval, needed=p_need, tile=p_tile, composited=p_comp, bwd_examined=p_bwd)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(sc):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    project + bin + composite of one full view (forward), repeated while under
-    ~15 s; reported in ms/frame."""
+    project + bin + composite of whole views (forward) on all the threads
+    OpenMP gives it (up to 4 views, ~10 s), then one whole view on one thread;
+    reported in ms/frame."""
     import oracle
     threads = oracle.num_threads()
     t0 = time.perf_counter()
@@ -517,9 +694,16 @@ def cpu_baseline(sc):
         if time.perf_counter() - t0 > 10.0 or frames >= 4:
             break
     dt = time.perf_counter() - t0
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    oracle.forward(sc, view=0)
+    dt1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
     return {"value": round(dt * 1e3 / frames, 1), "unit": "ms/frame", "cores": threads, "kind": "oracle",
             "sample": f"{frames} full forward view(s) of {sc.name} (project fp32-contract, brute-force "
-                      f"binning + qsort, fp64 compositing), OpenMP"}
+                      f"binning + qsort, fp64 compositing), OpenMP; then view 0 on one thread",
+            "one_core_ms_per_frame": round(dt1 * 1e3, 1),
+            "cpu_model": cpu_model(), "cpus_visible": os.cpu_count()}
 
 
 if __name__ == "__main__":

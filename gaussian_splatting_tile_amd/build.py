@@ -21,6 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgs_hip.so")
 SOURCES = ["gs_api.hip", "gs_project.hip", "gs_sort.hip", "gs_render.hip", "gs_mask.hip", "gs_adam.hip"]
+# the peak-rate microbenchmarks the roofline fractions are also taken against
+# (not part of the rasterizer's ABI)
+PEAKS_LIB = os.path.join(PKG, "libgs_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 HEADERS = [os.path.join(CSRC, "gs_internal.h"), os.path.join(CSRC, "gs_adam.h"), os.path.join(INCLUDE, "gs.h")]
 ARCH = os.environ.get("GS_OFFLOAD_ARCH", "gfx950")
 
@@ -45,26 +49,32 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PEAKS_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PEAKS_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS_LIB)
     return LIB
 
 
 def needs_build() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(PEAKS_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in [os.path.join(CSRC, s) for s in SOURCES] + HEADERS)
+    t = min(os.path.getmtime(LIB), os.path.getmtime(PEAKS_LIB))
+    return any(os.path.getmtime(p) > t
+               for p in [os.path.join(CSRC, s) for s in SOURCES + PEAKS_SOURCES] + HEADERS)
 
 
 if __name__ == "__main__":

@@ -179,6 +179,11 @@ def num_threads() -> int:
     return int(lib().orc_num_threads())
 
 
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls."""
+    lib().orc_set_num_threads(C.c_int(int(n)))
+
+
 def render_pixels(proj, bins, cam, xs, ys, bg=(0.0, 0.0, 0.0), bands=None):
     """render_pixel over many pixels, the arrays marshalled once (for images
     too large to composite whole).  Returns rgb [3][m], T [m], n_contrib [m],

@@ -630,3 +630,7 @@ void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *boun
 }
 
 int orc_num_threads(void) { return omp_get_max_threads(); }
+
+/* Threads for the OpenMP loops of the following calls (the CPU baseline
+ * times the oracle on one core and on all of them). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

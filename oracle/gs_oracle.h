@@ -147,6 +147,7 @@ void orc_sh_dequantize8(int64_t n, int rows, const uint8_t *q, const float *boun
 
 /* The number of OpenMP threads the oracle's parallel loops use. */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 /* Real spherical-harmonic basis (degree <= 3) at unit direction d, and its
  * gradient with respect to the three components of d. */

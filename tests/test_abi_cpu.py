@@ -235,3 +235,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "lib_path", lambda: str(tmp_path / "absent.so"))
     with pytest.raises(B.GsError, match="not built"):
         B.lib()
+
+
+def test_peaks_library_loads_and_refuses_bad_arguments_without_device():
+    """The measured-peak microbenchmarks (libgs_peaks.so) load and check their
+    arguments before touching a device."""
+    from gaussian_splatting_tile_amd import peaks
+    L = peaks.lib()
+    assert L.gsp_measure(99, 1, C.c_void_p(0x1000), 1 << 20, None) == -3.0
+    assert L.gsp_measure(peaks.FMA32, 0, C.c_void_p(0x1000), 1 << 20, None) == -3.0
+    assert L.gsp_measure(peaks.FMA32, 1, None, 1 << 20, None) == -3.0

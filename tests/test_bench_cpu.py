@@ -1,5 +1,5 @@
 """Host logic of bench.py, on the CPU: the one-GPU guard, the pair counters
-behind the forward blend's roofline (checked on the oracle's outputs against
+behind the blend kernels' rooflines (checked on the oracle's outputs against
 brute-force counts), and the tie between the reported traffic and the
 kernel sources the counters were taken on."""
 
@@ -47,12 +47,13 @@ def _view_from_oracle(sc, view=0):
 def test_blend_pair_counts_against_brute_force():
     sc = scenes.tiny(seed=6, n=600)
     b, op, ob, oo = _view_from_oracle(sc)
-    p_eval, p_need, p_tile = bench.blend_pairs(torch, b)
+    cnt = bench.blend_pairs(torch, b)
+    p_eval, p_need, p_tile = cnt["eval"], cnt["needed"], cnt["tile"]
     cam = sc.cameras[0]
     TX = cam.tiles_x
     ranges = ob["ranges"].reshape(-1, 2).astype(np.int64)
     vals = ob["vals"].astype(np.int64)
-    brute_eval = brute_need = 0
+    brute_eval = brute_need = brute_comp = brute_bwd = 0
     a, bb, c = (op["conic"][i].astype(np.float64) for i in range(3))
     for y in range(cam.height):
         for x in range(cam.width):
@@ -60,6 +61,13 @@ def test_blend_pair_counts_against_brute_force():
             s, e = ranges[t]
             m = int(oo["n_contrib"][y, x]) if oo["final_T"][y, x] < 1e-4 else e - s
             brute_eval += m
+            # composited: alpha >= 1/255 among the entries before n_contrib
+            nci = int(oo["n_contrib"][y, x])
+            brute_bwd += nci
+            for g in vals[s:s + nci]:
+                dxp, dyp = op["u"][g] - (x + 0.5), op["v"][g] - (y + 0.5)
+                pw = -0.5 * (a[g] * dxp * dxp + c[g] * dyp * dyp) - bb[g] * dxp * dyp
+                brute_comp += op["opacity"][g] * np.exp(pw) >= 1.0 / 255.0
             # the pixel's strip: rows 4r .. 4r + 3 of its tile, all 16 columns,
             # the quadratic form at every pixel centre of it
             y0 = (y // 16) * 16 + ((y % 16) // 4) * 4
@@ -77,6 +85,9 @@ def test_blend_pair_counts_against_brute_force():
     assert brute_need <= p_need <= p_tile <= p_eval
     assert p_need <= 1.05 * brute_need + 50
     assert p_need > 0
+    assert cnt["bwd_examined"] == brute_bwd
+    assert abs(cnt["composited"] - brute_comp) <= 2 and brute_comp > 1000
+    assert cnt["composited"] <= cnt["bwd_examined"] <= p_eval
 
 
 def test_traffic_figure_follows_the_kernel_sources(tmp_path, monkeypatch):
