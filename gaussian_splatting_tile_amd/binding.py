@@ -18,6 +18,7 @@ from . import build as _build
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_UNSUPPORTED, GS_ERR_WORKSPACE, GS_ERR_HIP = range(5)
 GS_SH_F32, GS_SH_F16, GS_SH_Q8 = 0, 1, 2
 GS_ADAM_F32, GS_ADAM_Q8LOG = 0, 1
+GS_ADAM_DENSE, GS_ADAM_LAZY = 0, 1
 SPLAT_FLOATS = 12          # gs_splat is 48 bytes
 
 
@@ -65,7 +66,7 @@ class GsGrads(C.Structure):
 class GsShAdam(C.Structure):
     _fields_ = [("n", C.c_int64), ("rows", C.c_int32), ("value_dtype", C.c_int32),
                 ("state_dtype", C.c_int32), ("step", C.c_int32), ("lr", C.c_float),
-                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("update", C.c_int32),
                 ("grad", C.c_void_p), ("value", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p),
                 ("m_bounds", C.c_void_p), ("v_bounds", C.c_void_p)]
 
@@ -231,10 +232,12 @@ def sh_quantize8(sh: torch.Tensor, codes: torch.Tensor, bounds: torch.Tensor, st
 def sh_adam_struct(grad: torch.Tensor, value: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
                    m_bounds: Optional[torch.Tensor] = None, v_bounds: Optional[torch.Tensor] = None,
                    step: int = 1, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
-                   eps: float = 1e-15) -> GsShAdam:
+                   eps: float = 1e-15, lazy: bool = True) -> GsShAdam:
     """Descriptor of gs_sh_adam_step over [rows][n] (or [K][3][n]) arrays:
     grad float32; value float32 or float16; m, v float32 (full-precision
-    state) or uint8 codes with float32 bounds [rows][ceil(n/256)][2]."""
+    state) or uint8 codes with float32 bounds [rows][ceil(n/256)][2];
+    lazy: units with a zero gradient keep their state (else every unit
+    moves)."""
     n = grad.shape[-1]
     rows = grad.numel() // n if n else grad.shape[0]
     for t in (grad, value, m, v):
@@ -244,6 +247,7 @@ def sh_adam_struct(grad: torch.Tensor, value: torch.Tensor, m: torch.Tensor, v: 
     a.n, a.rows, a.step = int(n), int(rows), int(step)
     a.value_dtype = GS_SH_F16 if value.dtype == torch.float16 else GS_SH_F32
     a.lr, a.beta1, a.beta2, a.eps = float(lr), float(beta1), float(beta2), float(eps)
+    a.update = GS_ADAM_LAZY if lazy else GS_ADAM_DENSE
     a.grad, a.value, a.m, a.v = _ptr(grad), _ptr(value), _ptr(m), _ptr(v)
     if m.dtype == torch.uint8:
         assert v.dtype == torch.uint8 and m_bounds is not None and v_bounds is not None
@@ -259,10 +263,10 @@ def sh_adam_struct(grad: torch.Tensor, value: torch.Tensor, m: torch.Tensor, v: 
 
 
 def sh_adam_step(grad, value, m, v, m_bounds=None, v_bounds=None, step=1, lr=1e-3, beta1=0.9,
-                 beta2=0.999, eps=1e-15, stream=None):
+                 beta2=0.999, eps=1e-15, stream=None, lazy=True):
     """gs_sh_adam_step: one fused Adam update of value, m, v (and the bounds)
-    in place."""
-    a = sh_adam_struct(grad, value, m, v, m_bounds, v_bounds, step, lr, beta1, beta2, eps)
+    in place; lazy (SparseAdam's rule) or dense (every unit)."""
+    a = sh_adam_struct(grad, value, m, v, m_bounds, v_bounds, step, lr, beta1, beta2, eps, lazy)
     _check(lib().gs_sh_adam_step(C.byref(a), _stream(stream)), "gs_sh_adam_step")
 
 

@@ -29,6 +29,7 @@ struct AdamCoef {
     float lr, b1, b2, omb1, omb2;              // omb = 1 - b
     float rbc1, rbc2;                          // 1 / (1 - b^t)
     float eps, reps;                           // eps and 1 / eps
+    int lazy;                                  // 1: zero-gradient units keep their state
 };
 
 struct AdamArgs {
@@ -89,13 +90,16 @@ __device__ __forceinline__ void store4(TV *p, const float in[4])
     *reinterpret_cast<typename Vec4<TV>::T *>(p) = w;
 }
 
+// Whether a unit moves this step: every unit (dense), or only those with a
+// non-zero gradient (lazy: a Gaussian none of the step's views saw keeps
+// its value and moments).
+__device__ __forceinline__ bool unit_live(float g, const AdamCoef &k) { return !k.lazy || g != 0.0f; }
+
 // The bias-corrected Adam update of one unit; m and v are replaced by the
 // new moments, the new value is returned (fp32, before storage rounding).
-// The update is lazy: a unit whose gradient is zero (a Gaussian none of the
-// step's views saw) keeps its value and moments.
 __device__ __forceinline__ float adam_unit(float th, float &m, float &v, float g, const AdamCoef &k)
 {
-    const bool live = g != 0.0f;
+    const bool live = unit_live(g, k);
     const float m1 = k.b1 * m + k.omb1 * g;
     const float v1 = k.b2 * v + k.omb2 * (g * g);
     const float den = __builtin_amdgcn_sqrtf(v1 * k.rbc2) + k.eps;
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(kAdamThreads) void adam_q8_kernel(AdamArgs a)
         th[j] = adam_unit(th[j], m, v, g[j], a.k);
         m1[j] = m;
         const float s2n = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_sqrtf(v) * a.k.reps);
-        s1[j] = g[j] != 0.0f ? s2n : s2;                  // an untouched unit keeps its s
+        s1[j] = unit_live(g[j], a.k) ? s2n : s2;          // an untouched unit keeps its s
     }
     // the block's new bounds: lane minima and maxima in fp32, then wave
     // minima of (m, -m, s, -s) as integer keys (s >= 0 is its own key)
@@ -372,6 +376,7 @@ hipError_t launch_sh_adam(const gs_sh_adam &p, hipStream_t s)
     a.k.rbc2 = (float)(1.0 / bc2);
     a.k.eps = p.eps;
     a.k.reps = (float)(1.0 / (double)p.eps);
+    a.k.lazy = p.update == GS_ADAM_LAZY ? 1 : 0;
     a.grad = p.grad;
     a.value = p.value;
     a.m = p.m;

@@ -2,6 +2,7 @@
 // workspace sizing and the launch sequence of each call.  No allocation, no
 // synchronisation, no host round trip.
 #include <math.h>
+#include <string.h>
 
 #include "gs_adam.h"
 #include "gs_internal.h"
@@ -55,7 +56,11 @@ int32_t gs_version(void) { return kVersion; }
 
 const char *gs_status_string(gs_status s)
 {
-    switch (s) {
+    // a C caller may pass any int: take the value's bytes as an int first (a
+    // load of an out-of-range value as the enum type is undefined in C++)
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
     case GS_OK: return "ok";
     case GS_ERR_INVALID_ARG: return "invalid argument";
     case GS_ERR_UNSUPPORTED: return "unsupported argument value";
@@ -524,6 +529,7 @@ gs_status gs_sh_adam_step(const gs_sh_adam *a, void *stream)
     if (a->n < 0 || a->n > INT32_MAX || a->rows < 1 || a->rows > 65535) return GS_ERR_INVALID_ARG;
     if (a->value_dtype != GS_SH_F32 && a->value_dtype != GS_SH_F16) return GS_ERR_INVALID_ARG;
     if (a->state_dtype != GS_ADAM_F32 && a->state_dtype != GS_ADAM_Q8LOG) return GS_ERR_INVALID_ARG;
+    if (a->update != GS_ADAM_DENSE && a->update != GS_ADAM_LAZY) return GS_ERR_INVALID_ARG;
     if (a->step < 1) return GS_ERR_INVALID_ARG;
     if (!std::isfinite(a->lr) || !(a->lr >= 0.0f)) return GS_ERR_INVALID_ARG;
     if (!(a->beta1 >= 0.0f && a->beta1 < 1.0f) || !(a->beta2 >= 0.0f && a->beta2 < 1.0f)) return GS_ERR_INVALID_ARG;

@@ -151,9 +151,16 @@ gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *cod
  *     value' = value - lr (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps),
  * computed in fp32 from the fp32 hyper-parameters given (1 - b and the bias
  * corrections are formed from them in double precision), the new value
- * rounded to nearest into its storage type.  The update is lazy: a unit
- * whose gradient is exactly zero keeps its value and both moments (t still
- * counts every step), as an 8-bit first moment seldom decodes to exactly 0.
+ * rounded to nearest into its storage type.  `update` picks which units
+ * move: GS_ADAM_DENSE updates every unit (torch.optim.Adam's rule: a unit
+ * with a zero gradient still decays its moments and moves by its first
+ * moment); GS_ADAM_LAZY updates only units whose gradient is not exactly
+ * zero, the others keeping their value and both moments (torch.optim.
+ * SparseAdam's rule; t still counts every step).  The page names neither;
+ * lazy is the usual choice with the 8-bit state: a first moment seldom
+ * decodes to exactly 0, so a dense step moves every Gaussian no view saw,
+ * by about lr x (code residue) / eps where its second moment decodes to 0
+ * (far past fp16 range with eps = 1e-15).
  * State GS_ADAM_F32: m and v are float [rows][n].
  * State GS_ADAM_Q8LOG: m holds uint8 codes of the first moment and v uint8
  * codes of s = log1p(sqrt(v) / eps), each with bounds [rows][ceil(n/256)][2]
@@ -167,6 +174,7 @@ gs_status gs_sh_quantize8(const float *sh, int64_t n, int32_t rows, uint8_t *cod
  * bounds are read and overwritten, grad is only read and must not overlap
  * them.  Concurrent calls on overlapping arrays race. */
 typedef enum gs_adam_state_dtype { GS_ADAM_F32 = 0, GS_ADAM_Q8LOG = 1 } gs_adam_state_dtype;
+typedef enum gs_adam_update { GS_ADAM_DENSE = 0, GS_ADAM_LAZY = 1 } gs_adam_update;
 
 typedef struct gs_sh_adam {
     int64_t n;                  /* Gaussians, 0 .. 2^31-1                      */
@@ -177,6 +185,7 @@ typedef struct gs_sh_adam {
     float lr;                   /* learning rate >= 0                          */
     float beta1, beta2;         /* moment decays in [0, 1)                     */
     float eps;                  /* > 0: Adam's epsilon and the log scale       */
+    int32_t update;             /* gs_adam_update: GS_ADAM_DENSE or _LAZY      */
     const float *grad;          /* [rows][n] fp32 SH gradients                 */
     void *value;                /* [rows][n] SH values, float or half          */
     void *m;                    /* [rows][n] float, or uint8 codes             */
@@ -186,8 +195,8 @@ typedef struct gs_sh_adam {
 } gs_sh_adam;
 
 /* Errors: GS_ERR_INVALID_ARG (NULL descriptor, NULL arrays with n > 0, n or
- * rows out of range, an unknown dtype, step < 1, lr < 0, a decay outside
- * [0, 1), eps <= 0, a non-finite hyper-parameter). */
+ * rows out of range, an unknown dtype or update mode, step < 1, lr < 0, a
+ * decay outside [0, 1), eps <= 0, a non-finite hyper-parameter). */
 gs_status gs_sh_adam_step(const gs_sh_adam *adam, void *stream);
 
 /* One projected Gaussian (device memory, 48 bytes, 16-byte aligned).

@@ -18,11 +18,15 @@ the measured speed-up of its fused optimizer kernel):
   names Adam's two moments but prints no update formula:
       m' = b1 m + (1 - b1) g          v' = b2 v + (1 - b2) g^2
       theta' = theta - lr * (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps)
-  applied lazily: a unit whose gradient is exactly zero in this step (a
-  Gaussian none of the step's views saw) keeps its value and both moments,
-  as in torch.optim.SparseAdam; t counts all steps.  With an 8-bit first
-  moment zero is in general not a code, so a dense step would move every
-  unseen Gaussian by about lr * (quantization residue) / eps.
+  applied to every unit (lazy=False: the dense rule of torch.optim.Adam,
+  where a unit with a zero gradient still decays both moments and moves by
+  its first moment) or lazily (lazy=True: a unit whose gradient is exactly
+  zero in this step, a Gaussian none of the step's views saw, keeps its
+  value and both moments, as in torch.optim.SparseAdam).  t counts all
+  steps.  The page states neither rule; lazy is the reading taken with the
+  8-bit state, where zero is in general not a code of the first moment and a
+  dense step would move every unseen Gaussian by about lr * (quantization
+  residue) / eps.
 * Full-precision state: m and v as fp32.
 * 8-bit state: both moments 8-bit with one (min, max) float pair per block of
   256 consecutive units, decoded lo + q * step, step = (hi - lo) * fp32(1/255)
@@ -86,10 +90,11 @@ def encode8(x: np.ndarray):
     return codes, bounds, t
 
 
-def _adam(theta, m, v, g, step, lr, beta1, beta2, eps):
-    """One bias-corrected Adam update in fp64 of the units with g != 0;
-    returns theta', m', v' (the other units unchanged)."""
-    live = g != 0
+def _adam(theta, m, v, g, step, lr, beta1, beta2, eps, lazy):
+    """One bias-corrected Adam update in fp64 of every unit (lazy=False) or
+    of the units with g != 0 (lazy=True, the others unchanged); returns
+    theta', m', v'."""
+    live = (g != 0) if lazy else np.ones(np.shape(g), dtype=bool)
     m1 = np.where(live, beta1 * m + (1.0 - beta1) * g, m)
     v1 = np.where(live, beta2 * v + (1.0 - beta2) * g * g, v)
     bc1 = 1.0 - beta1 ** step
@@ -98,26 +103,27 @@ def _adam(theta, m, v, g, step, lr, beta1, beta2, eps):
     return theta1, m1, v1
 
 
-def adam_step_f32(grad, value, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-15):
+def adam_step_f32(grad, value, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-15, lazy=True):
     """Full-precision state: m and v fp32 [rows][n].  value is fp32 or fp16;
     the new value is rounded into the same type."""
     g = np.asarray(grad, dtype=np.float64)
     th, m1, v1 = _adam(np.asarray(value, dtype=np.float64), np.asarray(m, dtype=np.float64),
-                       np.asarray(v, dtype=np.float64), g, step, lr, beta1, beta2, eps)
+                       np.asarray(v, dtype=np.float64), g, step, lr, beta1, beta2, eps, lazy)
     return dict(value=th.astype(value.dtype), value64=th, m=m1.astype(np.float32), m64=m1,
                 v=v1.astype(np.float32), v64=v1)
 
 
 def adam_step_q8(grad, value, m_codes, m_bounds, s_codes, s_bounds, step, lr,
-                 beta1=0.9, beta2=0.999, eps=1e-15):
+                 beta1=0.9, beta2=0.999, eps=1e-15, lazy=True):
     """8-bit state: m and s = log1p(sqrt(v)/eps) as codes [rows][n] (uint8)
     with bounds [rows][nb][2] (fp32).  value is fp32 or fp16."""
     g = np.asarray(grad, dtype=np.float64)
     m = decode8(m_codes, m_bounds).astype(np.float64)
     s = decode8(s_codes, s_bounds).astype(np.float64)
     v = (eps * np.expm1(s)) ** 2
-    th, m1, v1 = _adam(np.asarray(value, dtype=np.float64), m, v, g, step, lr, beta1, beta2, eps)
-    s1 = np.where(g != 0, np.log1p(np.sqrt(v1) / eps), s)       # an untouched unit keeps its s
+    th, m1, v1 = _adam(np.asarray(value, dtype=np.float64), m, v, g, step, lr, beta1, beta2, eps, lazy)
+    live = (g != 0) if lazy else np.ones(g.shape, dtype=bool)
+    s1 = np.where(live, np.log1p(np.sqrt(v1) / eps), s)          # an untouched unit keeps its s
     mc, mb, mt = encode8(m1)
     sc, sb, st = encode8(s1)
     return dict(value=th.astype(value.dtype), value64=th, m64=m1, s64=s1,

@@ -194,7 +194,7 @@ def test_sh_adam_argument_errors_without_device():
     bad = [dict(n=-1), dict(rows=0), dict(rows=65536), dict(value_dtype=B.GS_SH_Q8), dict(state_dtype=2),
            dict(step=0), dict(lr=-1.0), dict(lr=float("inf")), dict(beta1=1.0), dict(beta2=-0.5),
            dict(eps=0.0), dict(eps=float("nan")), dict(grad=None), dict(value=None), dict(m=None),
-           dict(v=None), dict(m_bounds=None), dict(v_bounds=None)]
+           dict(v=None), dict(m_bounds=None), dict(v_bounds=None), dict(update=2), dict(update=-1)]
     for kw in bad:
         assert L.gs_sh_adam_step(C.byref(desc(**kw)), None) == B.GS_ERR_INVALID_ARG, kw
     # the full-precision state needs no bounds; an empty update does nothing

@@ -1,6 +1,7 @@
 """Pins of the fused SH Adam oracle (oracle/adam.py) to things other than
-itself: torch's own Adam and SparseAdam (independent library implementations
-of the same update, Adam also fed the oracle's decoded 8-bit state), closed
+itself: torch's own Adam (the dense rule, zero gradients included) and
+SparseAdam (the lazy rule) -- independent library implementations of the
+same update, Adam also fed the oracle's decoded 8-bit state -- closed
 forms of a first step, the scale invariance of Adam, exact codes of a
 log-encoded ramp, block locality and the round-trip bound of the 8-bit
 encoding."""
@@ -72,6 +73,52 @@ def test_zero_gradient_units_follow_torch_sparse_adam():
     np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-30)
     never = np.all([g == 0 for g in grads], axis=0)
     assert never.any() and np.array_equal(th[never], d["value"][never])
+
+
+def test_dense_rule_matches_torch_adam_with_zero_gradient_units():
+    """lazy=False is torch.optim.Adam's rule: units whose gradient is zero
+    (about 40 % here, and a whole step without any gradient) still decay both
+    moments and move by their first moment."""
+    d = scenes.adam_inputs(23, 700, 6, state="f32", value_dtype=np.float64, fresh=True)
+    rng = np.random.default_rng(7)
+    grads = [d["grad"] * rng.random() * 3 for _ in range(5)]
+    grads[3] = np.zeros_like(grads[3])
+    assert np.mean(grads[0] == 0) > 0.2
+    th, m, v = d["value"].astype(np.float64), d["m"].astype(np.float64), d["v"].astype(np.float64)
+    for t, g in enumerate(grads, start=1):
+        r = A.adam_step_f32(g, th, m, v, step=t, lr=LR, lazy=False)
+        th, m, v = r["value64"], r["m64"], r["v64"]
+    tp, tm, tv = _torch_adam(d["value"].astype(np.float64), grads)
+    np.testing.assert_allclose(th, tp, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(m, tm, rtol=1e-12, atol=1e-25)
+    np.testing.assert_allclose(v, tv, rtol=1e-12, atol=1e-30)
+    # the lazy rule leaves exactly the never-seen units where they were; the
+    # dense one moves the units seen once and then left alone
+    lz = dict(th=d["value"].astype(np.float64), m=d["m"].astype(np.float64), v=d["v"].astype(np.float64))
+    for t, g in enumerate(grads, start=1):
+        r = A.adam_step_f32(g, lz["th"], lz["m"], lz["v"], step=t, lr=LR, lazy=True)
+        lz = dict(th=r["value64"], m=r["m64"], v=r["v64"])
+    seen = np.any([g != 0 for g in grads], axis=0)
+    assert seen.any() and np.all(np.abs(th - lz["th"])[seen] > 0)
+
+
+def test_dense_eight_bit_step_matches_torch_adam_on_the_decoded_state():
+    """The dense rule on the 8-bit state: torch's Adam from the decoded
+    moments on every unit, zero gradients included."""
+    d = scenes.adam_inputs(13, 900, 6)
+    t = 5
+    r = A.adam_step_q8(d["grad"], d["value"], d["m_codes"], d["m_bounds"], d["s_codes"], d["s_bounds"],
+                       step=t, lr=LR, lazy=False)
+    m0 = A.decode8(d["m_codes"], d["m_bounds"]).astype(np.float64)
+    s0 = A.decode8(d["s_codes"], d["s_bounds"]).astype(np.float64)
+    v0 = (EPS * np.expm1(s0)) ** 2
+    tp, tm, tv = _torch_adam(d["value"].astype(np.float64), [d["grad"]], m0, v0, step0=t - 1)
+    assert 0.2 < np.mean(d["grad"] == 0) < 0.6
+    np.testing.assert_allclose(r["value64"], tp, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["m64"], tm, rtol=1e-12, atol=1e-25)
+    np.testing.assert_allclose(r["s64"], np.log1p(np.sqrt(tv) / EPS), rtol=1e-12, atol=1e-12)
+    zero = d["grad"] == 0
+    assert np.all(r["value64"][zero] != d["value"][zero].astype(np.float64)) or not np.any(m0[zero])
 
 
 def test_eight_bit_step_matches_torch_adam_on_the_decoded_state():
