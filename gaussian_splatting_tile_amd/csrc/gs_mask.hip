@@ -247,11 +247,11 @@ size_t carve_mask(char *base, int64_t n, MaskWs *ws)
 {
     size_t off = 0;
     MaskWs w;
-    w.hist = (uint32_t *)(base + off);
+    w.hist = (uint32_t *)((uintptr_t)base + off);     // integer: also sized on a null base
     off = align_up(off + 4 * 256 * sizeof(uint32_t), 256);
-    w.state = (MaskState *)(base + off);
+    w.state = (MaskState *)((uintptr_t)base + off);
     off = align_up(off + sizeof(MaskState), 256);
-    w.block_eq = (uint32_t *)(base + off);
+    w.block_eq = (uint32_t *)((uintptr_t)base + off);
     off = align_up(off + (size_t)(mask_blocks(n) + 1) * sizeof(uint32_t), 256);
     if (ws) *ws = w;
     return off;

@@ -627,7 +627,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_tiles(const Batch<Sche
 }
 
 // ---------------------------------------------------------------------------
-// Workspace carving.
+// Workspace carving (also run on a null base to size the workspace, so the
+// addresses are formed as integers: no pointer arithmetic on null).
 struct Carve {
     char *p;
     size_t off = 0;
@@ -635,7 +636,7 @@ struct Carve {
     T *take(size_t count)
     {
         off = align_up(off, 256);
-        T *r = (T *)(p + off);
+        T *r = (T *)((uintptr_t)p + off);
         off += count * sizeof(T);
         return r;
     }
