@@ -41,16 +41,39 @@ constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-// Inclusive scan across one wave64 (Kogge-Stone with cross-lane moves).
+// DPP lane moves for the wave scans: row_shr:n takes the value of lane
+// i - n of the same 16-lane row, row_bcast:15 / row_bcast:31 the last lane
+// of the previous row / of the first two rows, for the rows row_mask
+// enables.  Lanes without a source (or disabled) read 0.
+constexpr int kDppRowShr = 0x110;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v)
+{
+    const uint32_t lo = dpp_move<kCtrl, kRowMask>((uint32_t)v);
+    const uint32_t hi = dpp_move<kCtrl, kRowMask>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan across one wave64: Kogge-Stone inside each 16-lane row on
+// DPP row shifts, then the rows' totals carried forward by the two row
+// broadcasts.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T x)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        T y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    x += dpp_move<kDppRowShr + 1>(x);
+    x += dpp_move<kDppRowShr + 2>(x);
+    x += dpp_move<kDppRowShr + 4>(x);
+    x += dpp_move<kDppRowShr + 8>(x);
+    x += dpp_move<kDppRowBcast15, 0xA>(x);     // rows 1, 3 += last lane of rows 0, 2
+    x += dpp_move<kDppRowBcast31, 0xC>(x);     // rows 2, 3 += last lane of row 1
     return x;
 }
 
@@ -148,8 +171,9 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const Batch<PassArgs> b,
         }
         // Lanes that share the first lane's digit (often most of the wave:
         // the high digits of depths and tiles take few values) are counted
-        // with one add; the others add one each (LDS atomics at one address
-        // serialise).
+        // with one add; the others add one each.  (Grouping the other lanes
+        // by digit with one ballot per digit bit, one add per group, was
+        // slower: 0.38 -> 0.60 ms of upsweeps per 8-view step at 1080p.)
 #pragma unroll
         for (int r = 0; r < kIpt; r++) {
             const uint32_t i = base + r * kBlock + threadIdx.x;
@@ -259,9 +283,10 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(const Batch<PassArgs> 
             if (drop_sentinel && k[r] == kSentinel) valid = false;
             const uint32_t d = (k[r] >> shift) & mask;
             uint64_t peers = __ballot(valid);
-            // digit bits above the pass width are zero in every lane
+            // one ballot per digit bit of the pass (a uniform bound)
 #pragma unroll
             for (int bit = 0; bit < 8; bit++) {
+                if (bit >= bits) break;
                 const uint64_t bb = __ballot((d >> bit) & 1u);
                 peers &= ((d >> bit) & 1u) ? bb : ~bb;
             }
@@ -331,7 +356,7 @@ struct InitArgs {
     const Splat *splats;
     uint32_t n, n_ranges;
     int tiles_x, tiles_y;
-    uint32_t *dkeys, *dvals, *ranges, *counters;
+    uint32_t *dkeys, *ranges, *counters;
     uint2 *grect;
 };
 
@@ -341,15 +366,13 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
     const Splat *__restrict__ splats = a.splats;
     const uint32_t n = a.n, n_ranges = a.n_ranges;
     uint32_t *__restrict__ dkeys = a.dkeys;
-    uint32_t *__restrict__ dvals = a.dvals;
     uint32_t *__restrict__ ranges = a.ranges;
     uint32_t *__restrict__ counters = a.counters;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
     if (i < n) {
         const float4 sa = splats[i].a;
         const uint32_t tiles = __float_as_uint(splats[i].c.w);
-        dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;
-        dvals[i] = i;
+        dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;   // the first pass takes i as the value
         // written for every Gaussian (culled ones get an unused value): a
         // full, coalesced row costs less than scattered partial lines
         uint2 gr = make_uint2(0u, 0u);
@@ -747,7 +770,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         for (int v = 0; v < count; v++) {
             const SortJob &J = jobs[v];
             b.v[v] = InitArgs{J.splats, (uint32_t)J.n, 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y),
-                              J.cam.tiles_x, J.cam.tiles_y, w[v].dk[0], w[v].dv[0], J.ranges, w[v].counters,
+                              J.cam.tiles_x, J.cam.tiles_y, w[v].dk[0], J.ranges, w[v].counters,
                               w[v].grect};
         }
         bin_init<<<dim3((init_max + kBlock - 1) / kBlock, count), kBlock, 0, s>>>(b);
@@ -768,7 +791,8 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             b.count = n_live;
             for (int i = 0; i < n_live; i++) {
                 const BinWs &W = w[live[i]];
-                b.v[i] = PassArgs{W.dk[cur], W.dv[cur], nullptr, W.dk[cur ^ 1], W.dv[cur ^ 1], nullptr,
+                b.v[i] = PassArgs{W.dk[cur], pass == 0 ? nullptr : W.dv[cur], nullptr, W.dk[cur ^ 1], W.dv[cur ^ 1],
+                                  nullptr,
                                   pass == 0 ? &W.counters[0] : &W.counters[1], &W.counters[1],
                                   W.digit_counts, W.digit_total, 8 * pass, 8};
             }
@@ -810,9 +834,13 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             for (int i = 0; i < n_live; i++) {
                 const SortJob &J = jobs[live[i]];
                 const BinWs &W = w[live[i]];
+                // the view's tile bits split as evenly as the passes allow
+                // (13 bits: 7 + 6, not 8 + 5: longer digit runs, fuller
+                // writes in the first pass)
                 const int tbits = bits_for((uint32_t)(J.cam.tiles_x * J.cam.tiles_y));
-                const int shift = 8 * p < tbits ? 8 * p : tbits;
-                const int bits = tbits - shift < 8 ? tbits - shift : 8;
+                const int base_bits = tbits / passes, extra = tbits % passes;
+                const int bits = base_bits + (p < extra ? 1 : 0);
+                const int shift = p * base_bits + (p < extra ? p : extra);
                 const uint32_t *gin = p == 0 ? W.gslot : W.tv[(p - 1) & 1];
                 uint32_t *gout = last ? J.vals : W.tv[p & 1];
                 uint32_t *entry_slots = J.bwd_index;                  // [cap], optional
