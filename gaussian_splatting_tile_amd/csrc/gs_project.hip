@@ -416,6 +416,9 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 // j, j + 7, ... of component q, then the seven partial sums are added in j
 // order.  Both orders are fixed, so the result is reproducible.  The rows of
 // round r + 1 (their first four slots) are loaded while round r is summed.
+// (Loading a group of 21 Gaussians' contiguous rows into LDS with 16-byte
+// loads first, then summing from LDS in the same order, measured 5 % slower:
+// the scattered 36-byte reads are not what limits this kernel.)
 // Slots at or past the capacity were never written and are left out.
 // Output: g2[g][9], visible Gaussians only.
 constexpr int kSumPerRound = 7;
