@@ -504,6 +504,16 @@ __device__ __forceinline__ float wave_reduce9(const float v[9], int lane)
     return f;
 }
 
+// The lanes where c holds, kept in scalar registers: tests of it are then
+// scalar compares (a branch on the ballot itself is emitted as a vector
+// select and compare per test).
+__device__ __forceinline__ uint64_t lanes_where(bool c)
+{
+    uint64_t m = __builtin_amdgcn_ballot_w64(c);
+    asm volatile("" : "+s"(m));
+    return m;
+}
+
 // Which of the nine totals lane L holds after wave_reduce9, or -1.
 __device__ __forceinline__ int reduce_slot(int lane)
 {
@@ -628,45 +638,51 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             const double dy0 = uv.y - py0;
             float raws[kPx];
             bool take[kPx];
-            bool any = false;
+            uint64_t rows[kPx];
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
                 raws[r] = alpha_raw(ct, q.z, dy0 - 4.0 * r);
                 take[r] = pos < last[r] && raws[r] >= kAlphaMin;
-                any = any || take[r];
+                rows[r] = lanes_where(pos < last[r]) & lanes_where(raws[r] >= kAlphaMin);
             }
-            if (__ballot(any) == 0) {
-                if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = 0.0f;
-                continue;
-            }
-            const float4 col = s_rgb[k];
-            const float inv_o = __builtin_amdgcn_rcpf(col.w);
-            // -w' = -P d per pixel in fp32: in the principal frame the terms
-            // cancel by at most the square root of the conic's eigenvalue
-            // ratio (~1e2), so fp32 keeps ~1e-5 relative accuracy
-            const float4 P = s_P[k];
-            const float fdx = (float)ct.dx;
-            const float p1dx = P.x * fdx, p2dx = P.z * fdx;
-            const float p1y = P.y, p2y = P.w, fdy0 = (float)dy0;
-            float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f;
-            float W1 = 0.0f, W2 = 0.0f, W11 = 0.0f, W12 = 0.0f, W22 = 0.0f;
+            // an entry no pixel of the tile uses gets zeros
+            float tot = 0.0f;
+            if ((rows[0] | rows[1] | rows[2] | rows[3]) != 0ull) {
+                const float4 col = s_rgb[k];
+                // -w' = -P d per pixel in fp32: in the principal frame the terms
+                // cancel by at most the square root of the conic's eigenvalue
+                // ratio (~1e2), so fp32 keeps ~1e-5 relative accuracy
+                const float4 P = s_P[k];
+                const float fdx = (float)ct.dx;
+                const float p1dx = P.x * fdx, p2dx = P.z * fdx;
+                const float p1y = P.y, p2y = P.w, fdy0 = (float)dy0;
+                float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f;
+                float W1 = 0.0f, W2 = 0.0f, W11 = 0.0f, W12 = 0.0f, W22 = 0.0f;
 #pragma unroll
-            for (int r = 0; r < kPx; r++) {
-                if (!take[r]) continue;
-                const float raw = raws[r];
-                const float alpha = fminf(kAlphaMax, raw);
-                const float one_m = 1.0f - alpha;
-                T[r] = T[r] * __builtin_amdgcn_rcpf(one_m);
-                const float w = alpha * T[r];
-                g6 = fmaf(w, G0[r], g6);
-                g7 = fmaf(w, G1[r], g7);
-                g8 = fmaf(w, G2[r], g8);
-                const float cg = fmaf(col.z, G2[r], fmaf(col.y, G1[r], col.x * G0[r]));
-                const float dla = T[r] * (cg - AG[r]);
-                AG[r] = fmaf(alpha, cg, one_m * AG[r]);
-                if (raw < kAlphaMax) {
-                    go = fmaf(dla, raw * inv_o, go);
-                    const float dp = dla * alpha;
+                for (int r = 0; r < kPx; r++) {
+                    // rows the wave skips as a whole; in the others the
+                    // lanes that do not take the entry see alpha = 0, which
+                    // leaves T and <A, G> as they are and adds nothing
+                    if (rows[r] == 0ull) continue;
+                    const float raw = take[r] ? raws[r] : 0.0f;
+                    // min(0.99, raw) in one instruction (raw is finite: an exp2)
+                    const float alpha = __builtin_amdgcn_fmed3f(raw, kAlphaMax, -3.0e38f);
+                    const float one_m = 1.0f - alpha;
+                    T[r] = T[r] * __builtin_amdgcn_rcpf(one_m);
+                    const float w = alpha * T[r];
+                    g6 = fmaf(w, G0[r], g6);
+                    g7 = fmaf(w, G1[r], g7);
+                    g8 = fmaf(w, G2[r], g8);
+                    const float cg = fmaf(col.z, G2[r], fmaf(col.y, G1[r], col.x * G0[r]));
+                    const float diff = cg - AG[r];
+                    const float dla = T[r] * diff;
+                    // alpha cg + (1 - alpha) AG, formed from the difference above
+                    AG[r] = fmaf(alpha, diff, AG[r]);
+                    // at the cap alpha does not depend on o or the power: no
+                    // gradient through them (a select, not a branch)
+                    const float dlc = raw < kAlphaMax ? dla : 0.0f;
+                    go = fmaf(dlc, raw, go);                           // times 1/o once per record
+                    const float dp = dlc * alpha;
                     const float dy = fdy0 - 4.0f * r;
                     const float w1 = fmaf(p1y, dy, p1dx);
                     const float w2 = fmaf(p2y, dy, p2dx);
@@ -677,19 +693,19 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
                     W12 = fmaf(t1, w2, W12);
                     W22 = fmaf(t2, w2, W22);
                 }
+                float v[9];
+                v[0] = W1;                                         // -W1, -W2 (P is negated)
+                v[1] = W2;
+                v[2] = W11;                                        // halved after the sum
+                v[3] = W12;
+                v[4] = W22;
+                v[5] = go * __builtin_amdgcn_rcpf(col.w);
+                v[6] = g6;
+                v[7] = g7;
+                v[8] = g8;
+                tot = wave_reduce9(v, lane) * slot_scale;
             }
-            float v[9];
-            v[0] = W1;                                         // -W1, -W2 (P is negated)
-            v[1] = W2;
-            v[2] = W11;                                        // halved after the sum
-            v[3] = W12;
-            v[4] = W22;
-            v[5] = go;
-            v[6] = g6;
-            v[7] = g7;
-            v[8] = g8;
-            const float tot = wave_reduce9(v, lane);
-            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot * slot_scale;
+            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot;
         }
         __syncthreads();
     }
