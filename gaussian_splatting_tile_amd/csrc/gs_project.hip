@@ -420,7 +420,8 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
 // loads first, then summing from LDS in the same order, measured 5 % slower:
 // the scattered 36-byte reads are not what limits this kernel.)
 // Slots at or past the capacity were never written and are left out.
-// Output: g2[g][9], visible Gaussians only.
+// Output: g2[g][9], visible Gaussians only, components 2..4 halved (the
+// rows hold the second moments sum dp w' w'^T).
 constexpr int kSumPerRound = 7;
 constexpr int kSumRounds = 9;
 constexpr int kSumPerWave = kSumPerRound * kSumRounds;   // 63
@@ -518,7 +519,8 @@ __global__ __launch_bounds__(kBlock) void sum_partials_kernel(const SumBatch bat
             for (int t = 0; t < kSumPerRound; t++) tot += __shfl(part, t * 9 + q, 64);
             if (gl == src / 9) acc = tot;
         }
-        if (cur.valid) g2[(size_t)cur.g * 9 + q] = (float)acc;
+        // the rows carry sum dp w' w'^T; d/dSigma' takes half of it (exact)
+        if (cur.valid) g2[(size_t)cur.g * 9 + q] = (float)(q >= 2 && q <= 4 ? 0.5 * acc : acc);
         cur = nxt;
     }
 }

@@ -240,10 +240,19 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
 // more than the skipped evaluations),
 // plus the entry's duplication slot and the principal frame of its conic; a
 // dropped entry gets its nine partial sums zeroed.
+// One record staged for the blend backward; as in the forward, the whole
+// wave reads one record at once from one address, at immediate offsets.
+struct BwdRec {
+    double4 q;                    // the exponent's terms, log2 o
+    double2 uv;                   // mean
+    float4 rgb;                   // colour, 1 / opacity
+    float4 P;                     // -P = -L V^T (the conic's principal frame)
+    uint4 meta;                   // list position, duplication slot, -, -
+};
+static_assert(sizeof(BwdRec) == 96, "six 16-byte LDS reads per record");
+
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
-                                                 int y0, double2 *s_uv, double4 *s_q, float4 *s_rgb,
-                                                 uint32_t *s_pos, uint32_t *s_slot, float4 *s_P,
-                                                 float *__restrict__ partial)
+                                                 int y0, BwdRec *s_rec, float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
     const bool keep = f.valid && box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1);
@@ -256,15 +265,18 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
         s.a = f.a;
         s.b = f.b;
         s.c = f.c;
-        stage_record(s, s_uv[slot], s_q[slot], s_rgb[slot]);
-        s_pos[slot] = f.m - start;
-        s_slot[slot] = entry_slot;
+        BwdRec &r = s_rec[slot];
+        float4 rgb;
+        stage_record(s, r.uv, r.q, rgb);
+        // dL/do is a sum of dL/dalpha alpha / o: divided once per record
+        r.rgb = make_float4(rgb.x, rgb.y, rgb.z, __builtin_amdgcn_rcpf(rgb.w));
+        r.meta = make_uint4(f.m - start, entry_slot, 0u, 0u);
         // -w' = -P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex)), stored
         // negated: the wave then sums -W1, -W2 directly (the products in
         // W11, W12, W22 do not change sign); formed in fp64, kept in fp32
         double ex, ey, l1, l2;
         conic_frame(s.b.x, s.b.y, s.b.z, ex, ey, l1, l2);
-        s_P[slot] = make_float4((float)(-(l1 * ex)), (float)(-(l1 * ey)), (float)(l2 * ey), (float)(-(l2 * ex)));
+        r.P = make_float4((float)(-(l1 * ex)), (float)(-(l1 * ey)), (float)(l2 * ey), (float)(-(l2 * ex)));
     }
     return __popcll(mask);
 }
@@ -473,13 +485,14 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
 // accumulates, over
 // its pixels with dp = dL/dpower,
 //   W1 = sum dp w'_1,  W2 = sum dp w'_2,  W11, W12, W22 = sum dp w' w'^T.
-// The 9 per-lane values of a record, (-W1, -W2, W11/2, W12/2, W22/2, dL/do,
+// The 9 per-lane values of a record, (-W1, -W2, W11, W12, W22, dL/do,
 // dL/drgb), are then summed over the wave by a split
 // butterfly on VALU lane swaps and DPP moves (each exchange halves the values
 // a lane carries) and nine lanes store the totals at the record's
 // duplication slot, partial[slot][9]: every (Gaussian, tile) pair owns one
 // slot, the slots of a Gaussian are contiguous, and the projection backward
-// sums them.  No atomics, so the gradients are bit-reproducible.
+// sums them (halving the three second moments: d/dSigma' = w w^T / 2).  No
+// atomics, so the gradients are bit-reproducible.
 
 // Wave sums of v[0..8] by a split butterfly: each exchange halves the values
 // a lane carries (9 -> 5 -> 3 -> 2 -> 1), then two plain steps finish.
@@ -535,17 +548,10 @@ __device__ __forceinline__ int reduce_slot(int lane)
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) void render_bwd_kernel(
     const BwdBatch batch)
 {
-    __shared__ double2 s_uv[kBatch];
-    __shared__ double4 s_q[kBatch];
-    __shared__ float4 s_rgb[kBatch];
-    __shared__ uint32_t s_pos[kBatch];
-    __shared__ uint32_t s_slot[kBatch];
-    __shared__ float4 s_P[kBatch];
+    __shared__ BwdRec s_rec[kBatch];
 
     const int lane = threadIdx.x;
     const int slot = reduce_slot(lane);
-    // the second-moment sums are halved once, on the lane that stores them
-    const float slot_scale = (slot >= 2 && slot <= 4) ? 0.5f : 1.0f;
     const int n_items = batch.count * batch.max_tiles;
     uint32_t *head = batch.queue, *done = batch.queue + 1;
     for (int item = next_item(head, n_items); item >= 0; item = next_item(head, n_items)) {
@@ -619,8 +625,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
     uint32_t next_g = next_valid ? vals[(uint32_t)next_m] : 0u;
     uint32_t next_slot = next_valid ? entry_slots[(uint32_t)next_m] : 0u;
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
-        const int nb = stage_fetched_bwd(cur, cur_slot, start, tx * kTile, ty * kTile, s_uv, s_q, s_rgb, s_pos,
-                                         s_slot, s_P, partial);
+        const int nb = stage_fetched_bwd(cur, cur_slot, start, tx * kTile, ty * kTile, s_rec, partial);
         cur.m = next_valid ? (uint32_t)next_m : 0u;
         cur.valid = next_valid;
         cur_slot = next_slot;
@@ -631,9 +636,10 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
         next_slot = next_valid ? entry_slots[(uint32_t)next_m] : 0u;
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
-            const uint32_t pos = s_pos[k];                     // list position
-            const double2 uv = s_uv[k];
-            const double4 q = s_q[k];
+            const BwdRec &rec = s_rec[k];
+            const uint32_t pos = rec.meta.x;                   // list position
+            const double2 uv = rec.uv;
+            const double4 q = rec.q;
             const ColTerms ct = col_terms(uv, q, px);
             const double dy0 = uv.y - py0;
             float raws[kPx];
@@ -648,14 +654,15 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             // an entry no pixel of the tile uses gets zeros
             float tot = 0.0f;
             if ((rows[0] | rows[1] | rows[2] | rows[3]) != 0ull) {
-                const float4 col = s_rgb[k];
+                const float4 col = rec.rgb;
                 // -w' = -P d per pixel in fp32: in the principal frame the terms
                 // cancel by at most the square root of the conic's eigenvalue
                 // ratio (~1e2), so fp32 keeps ~1e-5 relative accuracy
-                const float4 P = s_P[k];
-                const float fdx = (float)ct.dx;
-                const float p1dx = P.x * fdx, p2dx = P.z * fdx;
-                const float p1y = P.y, p2y = P.w, fdy0 = (float)dy0;
+                const float4 P = rec.P;
+                const float fdx = (float)ct.dx, fdy0 = (float)dy0;
+                const float p1y = P.y, p2y = P.w;
+                // w' at the lane's first row; a row 4 r further down adds -4 r (p1y, p2y)
+                const float w10 = fmaf(p1y, fdy0, P.x * fdx), w20 = fmaf(p2y, fdy0, P.z * fdx);
                 float go = 0.0f, g6 = 0.0f, g7 = 0.0f, g8 = 0.0f;
                 float W1 = 0.0f, W2 = 0.0f, W11 = 0.0f, W12 = 0.0f, W22 = 0.0f;
 #pragma unroll
@@ -683,9 +690,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
                     const float dlc = raw < kAlphaMax ? dla : 0.0f;
                     go = fmaf(dlc, raw, go);                           // times 1/o once per record
                     const float dp = dlc * alpha;
-                    const float dy = fdy0 - 4.0f * r;
-                    const float w1 = fmaf(p1y, dy, p1dx);
-                    const float w2 = fmaf(p2y, dy, p2dx);
+                    const float w1 = r == 0 ? w10 : fmaf(p1y, -4.0f * r, w10);
+                    const float w2 = r == 0 ? w20 : fmaf(p2y, -4.0f * r, w20);
                     const float t1 = dp * w1, t2 = dp * w2;
                     W1 += t1;
                     W2 += t2;
@@ -696,16 +702,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
                 float v[9];
                 v[0] = W1;                                         // -W1, -W2 (P is negated)
                 v[1] = W2;
-                v[2] = W11;                                        // halved after the sum
+                v[2] = W11;                                        // halved by the Gaussian's sum
                 v[3] = W12;
                 v[4] = W22;
-                v[5] = go * __builtin_amdgcn_rcpf(col.w);
+                v[5] = go * col.w;
                 v[6] = g6;
                 v[7] = g7;
                 v[8] = g8;
-                tot = wave_reduce9(v, lane) * slot_scale;
+                tot = wave_reduce9(v, lane);
             }
-            if (slot >= 0) partial[(size_t)s_slot[k] * 9 + slot] = tot;
+            if (slot >= 0) partial[(size_t)rec.meta.y * 9 + slot] = tot;
         }
         __syncthreads();
     }
