@@ -124,18 +124,34 @@ __device__ __forceinline__ bool box_may_contribute(float fu, float fv, const flo
     return amax >= kAlphaMin * (1.0f - 1e-3f);
 }
 
-// The strips of a tile a record can reach: bit r is set when some pixel of
-// rows 4 r .. 4 r + 3 of the tile (the rows a lane's pixel r covers across
-// the wave) may reach alpha >= 1/255; 0 when no pixel of the tile can.  A
-// wave skips pixel r of every lane for a record whose bit r is clear: exact,
-// since each of those pixels would have skipped the record.
-__device__ __forceinline__ uint32_t strip_mask(float fu, float fv, const float4 &conic_o, int x0, int y0)
+// The strips of a tile whose pixel rows lie within the vertical reach of a
+// record: for a fixed dy, Q(dx, dy) is smallest at dx = -b dy / a, where it
+// equals dy^2 det / a (det = ac - b^2), so a pixel of that row can reach
+// alpha >= 1/255 only if dy^2 <= 2 ln(255 o) a / det.  The bound is widened
+// by the relative margin of 1e-3 on alpha that box_may_contribute uses, far
+// above the error of the per-pixel evaluation, so a strip outside it holds no
+// pixel that could take the record, and the blend skips pixel r of every
+// lane for a record whose bit r is clear.  Strip r covers rows 4 r .. 4 r + 3
+// of the tile (the rows a lane's pixel r covers across the wave).  The test
+// ignores the tile's columns: weaker than a box test per strip, at a
+// fraction of the cost (four box tests per staged record took the forward
+// blend from 1.77 to 1.90 ms per 8 views at 1080p).
+__device__ __forceinline__ uint32_t strips_in_reach(float fv, const float4 &conic_o, int y0)
 {
-    if (!box_may_contribute(fu, fv, conic_o, x0, y0, kTile - 1, kTile - 1)) return 0u;
+    const double a = conic_o.x, b = conic_o.y, c = conic_o.z;
+    const double det = a * c - b * b;
+    if (!(det > 0.0) || !(a > 0.0)) return 0xFu;
+    // 2 ln(255 o / (1 - 1e-3)), through log2 in fp32 (error ~1e-7, inside the margin)
+    const float lim = 2.0f * 0.6931471805599453f * __builtin_amdgcn_logf(conic_o.w * (255.0f / (1.0f - 1e-3f)));
+    if (!(lim > 0.0f)) return 0u;
+    const double ext = sqrt((double)lim * a / det);
+    const double lo = (double)fv - ext, hi = (double)fv + ext;
     uint32_t m = 0;
-#pragma unroll 1
-    for (int r = 0; r < 4; r++)
-        if (box_may_contribute(fu, fv, conic_o, x0, y0 + 4 * r, kTile - 1, 3)) m |= 1u << r;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const double ylo = (double)(y0 + 4 * r) + 0.5;
+        if (hi >= ylo && lo <= ylo + 3.0) m |= 1u << r;
+    }
     return m;
 }
 
@@ -207,7 +223,9 @@ template <bool kWeight>
 __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, FwdRec *s_rec)
 {
     const int lane = threadIdx.x;
-    const uint32_t strips = f.valid ? strip_mask(f.a.x, f.a.y, f.b, x0, y0) : 0u;
+    // the cheap test first: most records that fail, fail it
+    uint32_t strips = f.valid ? strips_in_reach(f.a.y, f.b, y0) : 0u;
+    if (strips != 0u && !box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1)) strips = 0u;
     const bool keep = strips != 0u;
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -231,15 +249,6 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
     return __popcll(mask);
 }
 
-// The backward's staging of fetched records: the tile test only (per-strip
-// skipping, by the staged strip mask or by the strips' largest n_contrib,
-// measured slower: its registers push the backward into spills; both
-// together, the skips as scalar branches, took the blend backward + sums
-// from 4.33 to 4.73 ms per 8 views at 1080p: the four extra box tests per
-// staged record and the lost overlap of the four pixels' exp chains cost
-// more than the skipped evaluations),
-// plus the entry's duplication slot and the principal frame of its conic; a
-// dropped entry gets its nine partial sums zeroed.
 // One record staged for the blend backward; as in the forward, the whole
 // wave reads one record at once from one address, at immediate offsets.
 struct BwdRec {
@@ -247,15 +256,19 @@ struct BwdRec {
     double2 uv;                   // mean
     float4 rgb;                   // colour, 1 / opacity
     float4 P;                     // -P = -L V^T (the conic's principal frame)
-    uint4 meta;                   // list position, duplication slot, -, -
+    uint4 meta;                   // list position, duplication slot, strips in reach, -
 };
 static_assert(sizeof(BwdRec) == 96, "six 16-byte LDS reads per record");
 
+// The backward's staging of fetched records: the strips in reach and the
+// tile test, plus the entry's duplication slot and the principal frame of its
+// conic; a dropped entry gets its nine partial sums zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
                                                  int y0, BwdRec *s_rec, float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
-    const bool keep = f.valid && box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1);
+    const uint32_t strips = f.valid ? strips_in_reach(f.a.y, f.b, y0) : 0u;
+    const bool keep = strips != 0u && box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1);
     if (f.valid && !keep) zero_partial(partial, entry_slot);
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -270,7 +283,7 @@ __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entr
         stage_record(s, r.uv, r.q, rgb);
         // dL/do is a sum of dL/dalpha alpha / o: divided once per record
         r.rgb = make_float4(rgb.x, rgb.y, rgb.z, __builtin_amdgcn_rcpf(rgb.w));
-        r.meta = make_uint4(f.m - start, entry_slot, 0u, 0u);
+        r.meta = make_uint4(f.m - start, entry_slot, strips, 0u);
         // -w' = -P d with P = L V^T (rows: l1 (ex, ey), l2 (-ey, ex)), stored
         // negated: the wave then sums -W1, -W2 directly (the products in
         // W11, W12, W22 do not change sign); formed in fp64, kept in fp32
@@ -596,10 +609,18 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             G2[r] = dL_dimage[2 * hw + p];
         }
         AG[r] = bg0 * G0[r] + bg1 * G1[r] + bg2 * G2[r];
-        lmax = max(lmax, last[r]);
     }
+    // per strip, the largest number of entries a pixel composited: entries
+    // at or past it cannot be taken by any pixel of the strip
+    uint32_t lrow[kPx];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, (uint32_t)__shfl_xor((int)lmax, off, 64));
+    for (int r = 0; r < kPx; r++) {
+        uint32_t l = last[r];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) l = max(l, (uint32_t)__shfl_xor((int)l, off, 64));
+        lrow[r] = __builtin_amdgcn_readfirstlane(l);
+        lmax = max(lmax, lrow[r]);
+    }
 
     const uint32_t start = ranges[2 * tile];
     const uint32_t stop = start + lmax;           // entries at or past this are unused
@@ -637,7 +658,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
         __syncthreads();
         for (int k = nb - 1; k >= 0; k--) {
             const BwdRec &rec = s_rec[k];
-            const uint32_t pos = rec.meta.x;                   // list position
+            const uint32_t pos = __builtin_amdgcn_readfirstlane(rec.meta.x);   // list position
+            const uint32_t strips = __builtin_amdgcn_readfirstlane(rec.meta.z);
             const double2 uv = rec.uv;
             const double4 q = rec.q;
             const ColTerms ct = col_terms(uv, q, px);
@@ -647,9 +669,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
             uint64_t rows[kPx];
 #pragma unroll
             for (int r = 0; r < kPx; r++) {
-                raws[r] = alpha_raw(ct, q.z, dy0 - 4.0 * r);
-                take[r] = pos < last[r] && raws[r] >= kAlphaMin;
-                rows[r] = lanes_where(pos < last[r]) & lanes_where(raws[r] >= kAlphaMin);
+                // a strip out of the record's reach, or past every pixel's
+                // last entry, is not evaluated (scalar branch)
+                raws[r] = 0.0f;
+                take[r] = false;
+                rows[r] = 0ull;
+                if (((strips >> r) & 1u) && pos < lrow[r]) {
+                    raws[r] = alpha_raw(ct, q.z, dy0 - 4.0 * r);
+                    take[r] = pos < last[r] && raws[r] >= kAlphaMin;
+                    rows[r] = lanes_where(pos < last[r]) & lanes_where(raws[r] >= kAlphaMin);
+                }
             }
             // an entry no pixel of the tile uses gets zeros
             float tot = 0.0f;
