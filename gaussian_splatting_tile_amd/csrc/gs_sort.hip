@@ -562,6 +562,12 @@ struct RangeArgs {
     int key16;                   // tile ids stored as 16-bit keys
 };
 
+// Each thread takes kRangeItems consecutive entries (one 16-byte load of
+// 16-bit tile ids when the run is whole) and writes the boundaries between
+// them and the entry before: the start of the tile at position p and the end
+// of the tile at p - 1 wherever the ids at p - 1 and p differ.
+constexpr int kRangeItems = 8;
+
 __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const Batch<RangeArgs> b)
 {
     const RangeArgs &a = b.v[blockIdx.y];
@@ -573,21 +579,51 @@ __global__ __launch_bounds__(kBlock) void tile_ranges_kernel(const Batch<RangeAr
     uint32_t *__restrict__ entry_slots = a.entry_slots;
     uint64_t *__restrict__ keys64 = a.keys64;
     const uint32_t k = *a.k_ptr;
-    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (i >= k) return;
+    const uint64_t i64 = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * kRangeItems;
+    if (i64 >= k) return;
+    const uint32_t i0 = (uint32_t)i64;
+    const uint32_t n = k - i0 < (uint32_t)kRangeItems ? k - i0 : (uint32_t)kRangeItems;
     const int k16 = a.key16;
-    const uint32_t t = ld_key(tile_keys, i, k16);
-    if (i == 0 || ld_key(tile_keys, i - 1, k16) != t) ranges[2 * t] = i;
-    if (i == k - 1 || ld_key(tile_keys, i + 1, k16) != t) ranges[2 * t + 1] = i + 1;
-    uint32_t g;
-    if (gslot) {
-        g = gslot[i];
-        vals[i] = g;
-        if (entry_slots) entry_slots[i] = i;
-    } else if (keys64) {
-        g = vals[i];
+    uint32_t t[kRangeItems];
+    if (k16 && n == (uint32_t)kRangeItems) {
+        // i0 is a multiple of 8, so the 16 bytes are aligned
+        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(tile_keys) + i0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            t[2 * j] = ws[j] & 0xFFFFu;
+            t[2 * j + 1] = ws[j] >> 16;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRangeItems; j++) t[j] = (uint32_t)j < n ? ld_key(tile_keys, i0 + j, k16) : 0u;
     }
-    if (keys64) keys64[i] = ((uint64_t)t << 32) | __float_as_uint(splats[g].a.z);
+    uint32_t prev = i0 == 0 ? 0u : ld_key(tile_keys, i0 - 1, k16);
+#pragma unroll
+    for (int j = 0; j < kRangeItems; j++) {
+        if ((uint32_t)j >= n) break;
+        const uint32_t p = i0 + j;
+        if (p == 0) {
+            ranges[2 * t[j]] = 0;
+        } else if (t[j] != prev) {
+            ranges[2 * t[j]] = p;
+            ranges[2 * prev + 1] = p;
+        }
+        prev = t[j];
+    }
+    if (i0 + n == k) ranges[2 * prev + 1] = k;
+    for (uint32_t j = 0; j < n; j++) {
+        const uint32_t p = i0 + j;
+        uint32_t g = 0;
+        if (gslot) {
+            g = gslot[p];
+            vals[p] = g;
+            if (entry_slots) entry_slots[p] = p;
+        } else if (keys64) {
+            g = vals[p];
+        }
+        if (keys64) keys64[p] = ((uint64_t)t[j] << 32) | __float_as_uint(splats[g].a.z);
+    }
 }
 
 // Tile schedule for the blend kernels.  Per-tile work varies by two orders
@@ -866,7 +902,8 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             r.v[i] = RangeArgs{W.tk[passes & 1], &W.counters[2], J.splats, passes == 0 ? W.gslot : nullptr,
                                J.ranges, J.vals, J.bwd_index, J.keys, key16};
         }
-        const uint64_t kgrid = (cap_max + kBlock - 1) / kBlock;
+        const uint64_t per_block = (uint64_t)kBlock * kRangeItems;
+        const uint64_t kgrid = (cap_max + per_block - 1) / per_block;
         if (kgrid > 0) tile_ranges_kernel<<<dim3((unsigned)kgrid, n_live), kBlock, 0, s>>>(r);
     }
 
