@@ -443,10 +443,28 @@ def main():
     sh_bytes = sh_b * K_sh + (8.0 * 3 * K_sh / 256.0 if args.sh_q8 else 0.0)
     geo = 44 + (16 if sc.velocity is not None else 0)
     bytes_proj = sc.n * geo + (sc.n if use_mask else 0) + views * sc.n * 48 + n_any * sh_bytes
-    # the sort per the survey's per-unit model of a 64-bit LSB radix sort:
-    # scan 8 B x N, duplication 20 B x N + 12 B x K, 6 passes of 24 B + an
-    # 8 B histogram read per key, ranges 8 B x K
-    bytes_sort = sum(8 * sc.n + 20 * sc.n + 12 * k + (8 + 6 * 24) * k + 8 * k for k in Ks)
+    # the sort: what this design must move once (depth digits on the visible
+    # Gaussians, then the tile digits on the K keys): per Gaussian 20 B of its
+    # record read and 12 B of depth key and tile rect written; per visible
+    # Gaussian 4 depth passes of 20 B (4 B histogram read, 8 B read, 8 B
+    # written), the slot scan's 24 B and the duplication's 16 B of reads; per
+    # key 6 B written by the duplication, tile passes of 18 B (the first: the
+    # slot is the index) and 22 B (2 B histogram read, 10 B read, 10 B
+    # written) with 16-bit tile ids, and the 2 B read of the ranges
+    def tile_passes(c):
+        t, b = c.tiles_x * c.tiles_y, 0
+        while (1 << b) < t:
+            b += 1
+        return (b + 7) // 8
+    kb = 2 if all(c.tiles_x * c.tiles_y <= 65536 for c in sc.cameras[:views]) else 4
+    bytes_sort = sum(32 * sc.n + 128 * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
+                                              + max(0, tile_passes(c) - 1) * (kb + kb + 8 + kb + 8) + kb) * k
+                     for nv, k, c in zip(n_vis, Ks, sc.cameras[:views]))
+    # the survey's per-unit model of a plain 64-bit LSB radix sort of the K
+    # keys (scan 8 B x N, duplication 20 B x N + 12 B x K, 6 passes of 24 B +
+    # an 8 B histogram read per key, ranges 8 B x K), which this design
+    # does not move: reported beside it
+    bytes_sort_lsb64 = sum(8 * sc.n + 20 * sc.n + 12 * k + (8 + 6 * 24) * k + 8 * k for k in Ks)
     bytes_pbwd = n_any * (geo + sh_bytes) + sum(nv * (48 + 36) for nv in n_vis) + n_any * 2 * (geo + 12 * K_sh)
 
     def hbm(name, nbytes, ms, model):
@@ -466,7 +484,9 @@ def main():
                        f"visible in any view" + (" + N B mask" if use_mask else "")),
         "sort": hbm("gs_bin_sort_views (all views, 4 streams: the sort phase)",
                     bytes_sort, warm["sort_phase_ms"]["median"],
-                    "per view 28 B x N + 180 B x K (scan, duplication, 6 radix passes, ranges)"),
+                    "per view 32 B x N + 128 B x visible + 48 B x K (depth passes on the visible Gaussians, "
+                    "scan, duplication, 2 tile passes with 16-bit tile ids, ranges); the survey's 64-bit "
+                    f"6-pass model would be {bytes_sort_lsb64} B"),
         "project_bwd": (hbm("project_bwd_color_kernel + project_bwd_geom_kernel (one call, all views)",
                             bytes_pbwd, med("project_bwd_batch"),
                             f"per Gaussian visible in any view {geo} B + {sh_bytes:g} B parameters read and "

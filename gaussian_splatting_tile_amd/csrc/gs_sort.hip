@@ -437,43 +437,43 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
     if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
 }
 
-// Exclusive scan of the block sums (one block); K and the clamped count.
+// Exclusive scan of the block sums (one block per view); K and the clamped
+// count.  The sums go through in chunks of 1024, one per thread (coalesced
+// loads and stores), each chunk scanned across the block and carried into
+// the next.
 __global__ __launch_bounds__(1024) void scan_blocks(const Batch<DupArgs> b)
 {
-    __shared__ uint64_t wsum[16];
+    constexpr int kThreads = 1024, kW = kThreads / kWave;
+    __shared__ uint64_t wsum[kW];
     const DupArgs &a = b.v[blockIdx.y];
     uint64_t *__restrict__ block_sums = a.block_sums;
     const uint64_t cap = a.cap;
     uint32_t *__restrict__ bwd_off = a.bwd_off;
     const uint32_t m = *a.m_ptr;
     const int nb = (int)((m + kScanItems - 1) / kScanItems);
-    const int per = (nb + 1023) / 1024;
-    const int b0 = threadIdx.x * per;
-    uint64_t local = 0;
-    for (int i = 0; i < per; i++)
-        if (b0 + i < nb) local += block_sums[b0 + i];
-    // block-wide exclusive scan of `local` over 1024 threads (16 waves)
-    const uint64_t inc = wave_inclusive_scan(local);
     const int w = threadIdx.x / kWave;
-    if (lane_id() == kWave - 1) wsum[w] = inc;
-    __syncthreads();
-    uint64_t before = 0, total = 0;
-    for (int i = 0; i < 16; i++) {
-        if (i < w) before += wsum[i];
-        total += wsum[i];
-    }
-    uint64_t run = before + inc - local;
-    for (int i = 0; i < per; i++)
-        if (b0 + i < nb) {
-            const uint64_t c = block_sums[b0 + i];
-            block_sums[b0 + i] = run;
-            run += c;
+    uint64_t carry = 0;
+    for (int base = 0; base < nb; base += kThreads) {
+        const int i = base + threadIdx.x;
+        const uint64_t x = i < nb ? block_sums[i] : 0ull;
+        const uint64_t inc = wave_inclusive_scan(x);
+        if (lane_id() == kWave - 1) wsum[w] = inc;
+        __syncthreads();
+        uint64_t before = 0, total = 0;
+#pragma unroll
+        for (int j = 0; j < kW; j++) {
+            if (j < w) before += wsum[j];
+            total += wsum[j];
         }
+        __syncthreads();
+        if (i < nb) block_sums[i] = carry + before + inc - x;
+        carry += total;
+    }
     if (threadIdx.x == 0) {
-        *a.k_total = total;
-        *a.k_eff = (uint32_t)(total < cap ? total : cap);
+        *a.k_total = carry;
+        *a.k_eff = (uint32_t)(carry < cap ? carry : cap);
         if (bwd_off) {
-            bwd_off[m] = (uint32_t)(total < 0xFFFFFFFFull ? total : 0xFFFFFFFFull);
+            bwd_off[m] = (uint32_t)(carry < 0xFFFFFFFFull ? carry : 0xFFFFFFFFull);
             *a.bwd_count = m;
         }
     }
