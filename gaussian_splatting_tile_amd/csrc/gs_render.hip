@@ -205,9 +205,6 @@ __device__ __forceinline__ void fetch_record(const Splat *__restrict__ splats, u
     }
 }
 
-// Stage the fetched records of one batch into LDS with their strip masks
-// (and, with kWeight, their Gaussians), dropping those that cannot reach any
-// pixel of the tile; returns the number kept, in order.
 // One record staged for the forward blend.  The whole wave reads the same
 // record at once (LDS broadcast); keeping its fields together lets one
 // address serve all five reads, at immediate offsets.
@@ -219,6 +216,10 @@ struct FwdRec {
 };
 static_assert(sizeof(FwdRec) == 80, "five 16-byte LDS reads per record");
 
+// Stage the fetched records of one batch into LDS with their strip masks
+// (and, with kWeight, their Gaussians), dropping those that cannot reach a
+// pixel of the tile that is still compositing; returns the number kept, in
+// order.
 template <bool kWeight>
 __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, uint32_t live,
                                              FwdRec *s_rec)
@@ -262,9 +263,11 @@ struct BwdRec {
 };
 static_assert(sizeof(BwdRec) == 96, "six 16-byte LDS reads per record");
 
-// The backward's staging of fetched records: the strips in reach and the
-// tile test, plus the entry's duplication slot and the principal frame of its
-// conic; a dropped entry gets its nine partial sums zeroed.
+// The backward's staging of fetched records: the strips in reach (left out:
+// strips whose pixels all composited fewer entries than the record's list
+// position) and the tile test, plus the entry's duplication slot and the
+// principal frame of its conic; a dropped entry gets its nine partial sums
+// zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
                                                  int y0, const uint32_t lrow[4], BwdRec *s_rec,
                                                  float *__restrict__ partial)
