@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--views", type=int, default=8)
     ap.add_argument("--sort", choices=["batched", "per-view"], default="batched",
                     help="bin/sort all views in one gs_bin_sort_views call, or one gs_bin_sort per view")
+    ap.add_argument("--bin-keys", choices=["projection", "sort"], default="projection",
+                    help="batched sort only: each view's depth keys and tile rects written by the projection "
+                         "(gs_project_views_binned), or read back from the records by the sort")
     ap.add_argument("--streams", type=int, default=4,
                     help="HIP streams the views' sorts spread over (batched: one group of views per stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -259,6 +262,7 @@ def main():
     # the views' sorts are independent: they may run on a few streams
     # (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
+    prebinned = args.sort == "batched" and args.bin_keys == "projection"
     lanes = [stream] + side
     # a 2 GiB device copy (1 GiB read + 1 GiB written) before each cold step
     # pushes the step's inputs out of the 256 MB last-level cache and the L2
@@ -294,7 +298,8 @@ def main():
             timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
         # the views' records in one pass over the Gaussians
         timed("project_batch", lambda: B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
-                                                       stream))
+                                                       stream, bin_keys=[b.bin_keys for b in bufs]
+                                                       if prebinned else None))
         e_sort0.record(stream)
         for st in side:
             st.wait_event(e_sort0)
@@ -304,7 +309,7 @@ def main():
             for i, st in enumerate(lanes):
                 grp = bufs[i::len(lanes)]
                 if grp:
-                    timed("bin_sort_batch", lambda: B.bin_sort_views(grp, do_bwd, st), st)
+                    timed("bin_sort_batch", lambda: B.bin_sort_views(grp, do_bwd, st, prebinned=prebinned), st)
         else:
             for i, b in enumerate(bufs):
                 st = lanes[i % len(lanes)]
@@ -442,10 +447,12 @@ def main():
     sh_b = {"f32": 12, "f16": 6, "q8": 3}["q8" if args.sh_q8 else ("f16" if sc.sh_fp16 is not None else "f32")]
     sh_bytes = sh_b * K_sh + (8.0 * 3 * K_sh / 256.0 if args.sh_q8 else 0.0)
     geo = 44 + (16 if sc.velocity is not None else 0)
-    bytes_proj = sc.n * geo + (sc.n if use_mask else 0) + views * sc.n * 48 + n_any * sh_bytes
+    rec_b = 48 + (12 if prebinned else 0)      # + depth key and tile rect when the projection writes them
+    bytes_proj = sc.n * geo + (sc.n if use_mask else 0) + views * sc.n * rec_b + n_any * sh_bytes
     # the sort: what this design must move once (depth digits on the visible
     # Gaussians, then the tile digits on the K keys): per Gaussian 20 B of its
-    # record read and 12 B of depth key and tile rect written; per visible
+    # record read and 12 B of depth key and tile rect written (none of it
+    # when the projection writes those 12 B, counted there); per visible
     # Gaussian 4 depth passes of 20 B (4 B histogram read, 8 B read, 8 B
     # written), the slot scan's 24 B and the duplication's 16 B of reads; per
     # key 6 B written by the duplication, tile passes of 18 B (the first: the
@@ -457,7 +464,8 @@ def main():
             b += 1
         return (b + 7) // 8
     kb = 2 if all(c.tiles_x * c.tiles_y <= 65536 for c in sc.cameras[:views]) else 4
-    bytes_sort = sum(32 * sc.n + 128 * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
+    per_g = 0 if prebinned else 32
+    bytes_sort = sum(per_g * sc.n + 128 * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
                                               + max(0, tile_passes(c) - 1) * (kb + kb + 8 + kb + 8) + kb) * k
                      for nv, k, c in zip(n_vis, Ks, sc.cameras[:views]))
     # the survey's per-unit model of a plain 64-bit LSB radix sort of the K
@@ -480,11 +488,12 @@ def main():
 
     hbm_stages = {
         "project": hbm("project_kernel (one launch, all views)", bytes_proj, med("project_batch"),
-                       f"N x {geo} B parameters + {views} x N x 48 B records + {sh_bytes:g} B of SH per Gaussian "
-                       f"visible in any view" + (" + N B mask" if use_mask else "")),
+                       f"N x {geo} B parameters + {views} x N x {rec_b} B records"
+                       + (" (48 B + the sort's 12 B depth key and tile rect)" if prebinned else "") +
+                       f" + {sh_bytes:g} B of SH per Gaussian visible in any view" + (" + N B mask" if use_mask else "")),
         "sort": hbm("gs_bin_sort_views (all views, 4 streams: the sort phase)",
                     bytes_sort, warm["sort_phase_ms"]["median"],
-                    "per view 32 B x N + 128 B x visible + 48 B x K (depth passes on the visible Gaussians, "
+                    f"per view {per_g} B x N + 128 B x visible + 48 B x K (depth passes on the visible Gaussians, "
                     "scan, duplication, 2 tile passes with 16-bit tile ids, ranges); the survey's 64-bit "
                     f"6-pass model would be {bytes_sort_lsb64} B"),
         "project_bwd": (hbm("project_bwd_color_kernel + project_bwd_geom_kernel (one call, all views)",
@@ -518,7 +527,8 @@ def main():
                                          else "synthetic Exp(1)"),
                    "lod_min_radius_px": cam0.lod_min_radius_px,
                    "step": ("importance mask, then " if use_mask else "") +
-                           "batched project, " +
+                           ("batched project writing the sort's depth keys and tile rects, " if prebinned
+                            else "batched project, ") +
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
                            ", K copied to the host (checked after the steps), batched blend fwd of all views" +
                            (" with per-Gaussian blending weights" if args.weights else "") +

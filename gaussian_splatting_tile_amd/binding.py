@@ -39,7 +39,12 @@ class GsSortView(C.Structure):
     _fields_ = [("camera", GsCamera), ("splats", C.c_void_p), ("n", C.c_int64), ("k_capacity", C.c_int64),
                 ("vals", C.c_void_p), ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p),
                 ("bwd_index", C.c_void_p), ("keys", C.c_void_p), ("k_total", C.c_void_p),
-                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("depth_keys", C.c_void_p), ("tile_rects", C.c_void_p)]
+
+
+class GsBinKeys(C.Structure):
+    _fields_ = [("depth_keys", C.c_void_p), ("tile_rects", C.c_void_p)]
 
 
 class GsBwdView(C.Structure):
@@ -78,7 +83,7 @@ class GsError(RuntimeError):
 _lib = None
 SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs_bwd_index_words", "gs_bin_sort",
            "gs_bin_sort_views",
-           "gs_render_fwd_views", "gs_render_bwd_screen_views", "gs_project_views",
+           "gs_render_fwd_views", "gs_render_bwd_screen_views", "gs_project_views", "gs_project_views_binned",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
            "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
@@ -115,6 +120,8 @@ def lib():
     L.gs_render_fwd.argtypes = [vp, vp, vp, vp, C.POINTER(GsCamera), vp, vp, vp, vp, vp]
     L.gs_render_fwd_views.argtypes = [C.c_int32, C.POINTER(GsFwdView), vp, vp]
     L.gs_project_views.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp), vp]
+    L.gs_project_views_binned.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp),
+                                          C.POINTER(GsBinKeys), vp]
     L.gs_render_bwd_screen_views.argtypes = [C.c_int32, C.POINTER(GsBwdView), vp, vp]
     L.gs_render_bwd_workspace_bytes.argtypes = [i64, i64]
     L.gs_render_bwd_workspace_bytes.restype = sz
@@ -139,7 +146,7 @@ def lib():
     L.gs_status_string.restype = C.c_char_p
     L.gs_status_string.argtypes = [C.c_int]
     L.gs_version.restype = C.c_int32
-    for name in ("gs_project", "gs_project_views", "gs_bin_sort", "gs_bin_sort_views", "gs_render_fwd",
+    for name in ("gs_project", "gs_project_views", "gs_project_views_binned", "gs_bin_sort", "gs_bin_sort_views", "gs_render_fwd",
                  "gs_render_fwd_views",
                  "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
@@ -298,16 +305,22 @@ def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, 
                              _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_bin_sort")
 
 
-def bin_sort_views(bufs, with_bwd: bool = True, stream=None):
+def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned: bool = False):
     """gs_bin_sort_views over ViewBuffers objects (their splats must be
-    current): one launch per sort step for up to 8 views."""
+    current): one launch per sort step for up to 8 views.  prebinned: take
+    the depth keys and tile rects that project_views(..., binned=True) wrote
+    into the buffers with those splats (one flag for all views, or one per
+    view)."""
     nv = len(bufs)
+    pre = list(prebinned) if isinstance(prebinned, (list, tuple)) else [prebinned] * nv
     arr = (GsSortView * max(nv, 1))()
     for i, b in enumerate(bufs):
         arr[i] = GsSortView(b.camc, _ptr(b.splats), int(b.n), int(b.k_capacity), _ptr(b.vals), _ptr(b.ranges),
                             _ptr(b.schedule), _ptr(b.bwd_index) if with_bwd else None, _ptr(b.keys),
                             _ptr(b.k_total),
-                            _ptr(b.ws), _nbytes(b.ws))
+                            _ptr(b.ws), _nbytes(b.ws),
+                            _ptr(b.depth_keys) if pre[i] else None,
+                            _ptr(b.tile_rects) if pre[i] else None)
     _check(lib().gs_bin_sort_views(nv, arr, _stream(stream)), "gs_bin_sort_views")
 
 
@@ -319,12 +332,23 @@ def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[
                                _stream(stream)), "gs_render_fwd")
 
 
-def project_views(gs: GsGaussians, cams, splats_list, stream=None):
-    """gs_project_views: records for every camera of the list in one pass."""
+def project_views(gs: GsGaussians, cams, splats_list, stream=None, bin_keys=None):
+    """gs_project_views: records for every camera of the list in one pass.
+    bin_keys: None, or one (depth_keys uint32/int32 [n], tile_rects
+    uint32/int32 [2n]) pair (or None) per camera, for
+    gs_project_views_binned."""
     nv = len(cams)
     cam_arr = (GsCamera * max(nv, 1))(*cams)
     sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
-    _check(lib().gs_project_views(C.byref(gs), nv, cam_arr, sp_arr, _stream(stream)), "gs_project_views")
+    if bin_keys is None:
+        _check(lib().gs_project_views(C.byref(gs), nv, cam_arr, sp_arr, _stream(stream)), "gs_project_views")
+        return
+    bk = (GsBinKeys * max(nv, 1))()
+    for i, pair in enumerate(bin_keys):
+        if pair is not None:
+            bk[i] = GsBinKeys(_ptr(pair[0]), _ptr(pair[1]))
+    _check(lib().gs_project_views_binned(C.byref(gs), nv, cam_arr, sp_arr, bk, _stream(stream)),
+           "gs_project_views_binned")
 
 
 def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None, weights=None):
@@ -440,6 +464,13 @@ class ViewBuffers:
         self.schedule = torch.empty(schedule_words(W, H), dtype=torch.int32, device=device)
         self.bwd_index = (torch.empty(bwd_index_words(n, self.k_capacity), dtype=torch.int32, device=device)
                           if with_backward else None)
+        # the sort's per-Gaussian inputs when the projection writes them
+        self.depth_keys = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+        self.tile_rects = torch.empty(2 * max(n, 1), dtype=torch.int32, device=device)
+
+    @property
+    def bin_keys(self):
+        return (self.depth_keys, self.tile_rects)
 
     def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
         project(gs, self.camc, self.splats, stream)

@@ -81,11 +81,24 @@ gs_status gs_project(const gs_gaussians *gaussians, const gs_camera *camera, gs_
     b.count = 1;
     b.cam[0] = make_cam(*camera);
     b.out[0] = (Splat *)splats;
+    b.dkeys[0] = nullptr;
+    b.grect[0] = nullptr;
     return from_hip(launch_project(*gaussians, b, (hipStream_t)stream));
 }
 
-gs_status gs_project_views(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
-                           gs_splat *const *splats, void *stream)
+// The sort inputs of one view: both pointers or neither, depth keys 4-byte
+// and rects 8-byte aligned, and tile coordinates that fit the 16-bit fields.
+static bool bin_keys_ok(const uint32_t *dk, const uint32_t *gr, const gs_camera &cam)
+{
+    if ((dk == nullptr) != (gr == nullptr)) return false;
+    if (dk == nullptr) return true;
+    if (((uintptr_t)dk & 3u) != 0 || ((uintptr_t)gr & 7u) != 0) return false;
+    const Cam c = make_cam(cam);
+    return c.tiles_x <= 65535 && c.tiles_y <= 65535;
+}
+
+static gs_status project_views(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                               gs_splat *const *splats, const gs_bin_keys *bin_keys, void *stream)
 {
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
@@ -93,18 +106,41 @@ gs_status gs_project_views(const gs_gaussians *gaussians, int32_t n_views, const
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
         if ((gaussians->n > 0 && !splats[v]) || !al16(splats[v])) return GS_ERR_INVALID_ARG;
+        if (bin_keys && !bin_keys_ok(bin_keys[v].depth_keys, bin_keys[v].tile_rects, cameras[v]))
+            return GS_ERR_INVALID_ARG;
     }
     for (int v0 = 0; v0 < n_views; v0 += kMaxProjViews) {
         ProjBatch b;
         b.count = n_views - v0 < kMaxProjViews ? n_views - v0 : kMaxProjViews;
+        for (int i = 0; i < kMaxProjViews; i++) {
+            b.dkeys[i] = nullptr;
+            b.grect[i] = nullptr;
+        }
         for (int i = 0; i < b.count; i++) {
             b.cam[i] = make_cam(cameras[v0 + i]);
             b.out[i] = (Splat *)splats[v0 + i];
+            if (bin_keys) {
+                b.dkeys[i] = bin_keys[v0 + i].depth_keys;
+                b.grect[i] = (uint2 *)bin_keys[v0 + i].tile_rects;
+            }
         }
         hipError_t e = launch_project(*gaussians, b, (hipStream_t)stream);
         if (e != hipSuccess) return GS_ERR_HIP;
     }
     return GS_OK;
+}
+
+gs_status gs_project_views(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                           gs_splat *const *splats, void *stream)
+{
+    return project_views(gaussians, n_views, cameras, splats, nullptr, stream);
+}
+
+gs_status gs_project_views_binned(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                                  gs_splat *const *splats, const gs_bin_keys *bin_keys, void *stream)
+{
+    if (n_views > 0 && !bin_keys) return GS_ERR_INVALID_ARG;
+    return project_views(gaussians, n_views, cameras, splats, bin_keys, stream);
 }
 
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles)
@@ -137,6 +173,7 @@ static gs_status check_sort_view(const gs_sort_view &v)
     if (!camera_ok(&v.camera) || !v.tile_ranges || !v.schedule || !v.k_total) return GS_ERR_INVALID_ARG;
     if ((v.n > 0 && !v.splats) || !al16(v.splats) || !al16(v.workspace)) return GS_ERR_INVALID_ARG;
     if (v.k_capacity > 0 && !v.vals) return GS_ERR_INVALID_ARG;
+    if (!bin_keys_ok(v.depth_keys, v.tile_rects, v.camera)) return GS_ERR_INVALID_ARG;
     const Cam cam = make_cam(v.camera);
     const size_t need = bin_sort_workspace(v.n, v.k_capacity, cam.tiles_x * cam.tiles_y);
     if (v.workspace_bytes < need || !v.workspace) return GS_ERR_WORKSPACE;
@@ -157,6 +194,8 @@ static SortJob sort_job(const gs_sort_view &v)
     j.keys = v.keys;
     j.k_total = v.k_total;
     j.ws = v.workspace;
+    j.dkeys = v.depth_keys;
+    j.grect = (const uint2 *)v.tile_rects;
     return j;
 }
 
@@ -179,6 +218,8 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera
     v.k_total = k_total;
     v.workspace = workspace;
     v.workspace_bytes = workspace_bytes;
+    v.depth_keys = nullptr;
+    v.tile_rects = nullptr;
     return gs_bin_sort_views(1, &v, stream);
 }
 

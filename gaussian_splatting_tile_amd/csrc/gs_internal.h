@@ -35,6 +35,17 @@ __device__ __forceinline__ Rect tile_rect(float u, float v, float rf, float tile
     return Rect{(int)fx0, (int)fx1, (int)fy0, (int)fy1};
 }
 
+// The sort's per-Gaussian inputs: the depth key (fp32 depth bits; the
+// sentinel, which no finite depth has, for a Gaussian that touches no tile)
+// and the tile rect packed as (x0 | y0 << 16, width | height << 16).
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint2 pack_rect(const Rect &r)
+{
+    return make_uint2((uint32_t)r.x0 | ((uint32_t)r.y0 << 16),
+                      (uint32_t)(r.x1 - r.x0) | ((uint32_t)(r.y1 - r.y0) << 16));
+}
+
 // Principal frame of a 2D conic [[a, b], [b, c]] in fp64: the unit
 // eigenvector (ex, ey) of the larger eigenvalue l1 and the smaller one l2;
 // the second axis is (-ey, ex).  Each component of the eigenvector is formed
@@ -113,6 +124,10 @@ struct ProjBatch {
     int count;
     Cam cam[kMaxProjViews];
     Splat *out[kMaxProjViews];
+    // optional per view (both or neither): the sort's depth keys and packed
+    // tile rects, written beside the records
+    uint32_t *dkeys[kMaxProjViews];
+    uint2 *grect[kMaxProjViews];
 };
 hipError_t launch_project(const gs_gaussians &g, const ProjBatch &views, hipStream_t s);
 hipError_t launch_sh_quantize8(const float *sh, int64_t n, int rows, uint8_t *codes, float *bounds, hipStream_t s);
@@ -159,6 +174,8 @@ struct SortJob {
     uint64_t *keys;               // optional
     uint64_t *k_total;
     void *ws;                     // bin_sort_workspace(n, cap) bytes
+    const uint32_t *dkeys;        // optional (both or neither): depth keys and
+    const uint2 *grect;           // tile rects from the projection
 };
 hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s);
 size_t active_mask_workspace(int64_t n);

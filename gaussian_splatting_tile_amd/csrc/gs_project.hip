@@ -339,6 +339,8 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
         pz = displace(mz, dt, vz);
         vis = vis && isfinite(px) && isfinite(py) && isfinite(pz);
     }
+    uint32_t dkey = kSentinel;
+    uint2 grect = make_uint2(0u, 0u);
     Geo G;
     if (vis) vis = geometry(cam, px, py, pz, sx, sy, sz, qw, qx, qy, qz, G);
     if (vis && cam.lod > 0.0f) {
@@ -383,9 +385,17 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
             rec.b = make_float4(ca, cb, cc, o);
             rec.c = make_float4(col[0], col[1], col[2],
                                 __uint_as_float((uint32_t)((r.x1 - r.x0) * (r.y1 - r.y0))));
+            dkey = __float_as_uint(G.z);
+            grect = pack_rect(r);
         }
     }
     out[g] = rec;
+    // the sort's inputs from the same values (the binning would otherwise
+    // read them back from the record)
+    if (views.dkeys[v] != nullptr) {
+        views.dkeys[v][g] = dkey;
+        views.grect[v][g] = grect;
+    }
     }   // views
 }
 

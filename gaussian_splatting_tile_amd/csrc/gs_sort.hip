@@ -36,7 +36,6 @@ constexpr int kIpt = 16;                        // items per thread per tile
 constexpr int kTileItems = kBlock * kIpt;       // 4096
 constexpr int kWaveItems = kWave * kIpt;        // 1024
 constexpr int kMaxGrid = 512;                   // radix blocks per pass
-constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
@@ -358,6 +357,7 @@ struct InitArgs {
     int tiles_x, tiles_y;
     uint32_t *dkeys, *ranges, *counters;
     uint2 *grect;
+    int prebinned;               // depth keys and rects came from the projection
 };
 
 __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
@@ -369,18 +369,15 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
     uint32_t *__restrict__ ranges = a.ranges;
     uint32_t *__restrict__ counters = a.counters;
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (i < n) {
+    if (i < n && !a.prebinned) {
         const float4 sa = splats[i].a;
         const uint32_t tiles = __float_as_uint(splats[i].c.w);
         dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;   // the first pass takes i as the value
         // written for every Gaussian (culled ones get an unused value): a
         // full, coalesced row costs less than scattered partial lines
         uint2 gr = make_uint2(0u, 0u);
-        if (tiles) {
-            const Rect rc = tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x, (float)a.tiles_y);
-            gr = make_uint2((uint32_t)rc.x0 | ((uint32_t)rc.y0 << 16),
-                            (uint32_t)(rc.x1 - rc.x0) | ((uint32_t)(rc.y1 - rc.y0) << 16));
-        }
+        if (tiles) gr = pack_rect(tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x,
+                                            (float)a.tiles_y));
         a.grect[i] = gr;
     }
     if (i < n_ranges) ranges[i] = 0;
@@ -792,7 +789,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         const uint32_t n = (uint32_t)J.n;
         const uint32_t n_ranges = 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y);
         n_max = n > n_max ? n : n_max;
-        init_max = n > init_max ? n : init_max;
+        if (J.dkeys == nullptr) init_max = n > init_max ? n : init_max;
         init_max = n_ranges > init_max ? n_ranges : init_max;
         const uint32_t tb = (uint32_t)bits_for((uint32_t)(J.cam.tiles_x * J.cam.tiles_y));
         tbits_max = tb > tbits_max ? tb : tbits_max;
@@ -800,14 +797,14 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         any_bwd = any_bwd || J.bwd_index != nullptr;
     }
 
-    {   // counters, empty ranges, depth keys
+    {   // counters, empty ranges, depth keys and rects (unless the projection wrote them)
         Batch<InitArgs> b;
         b.count = count;
         for (int v = 0; v < count; v++) {
             const SortJob &J = jobs[v];
             b.v[v] = InitArgs{J.splats, (uint32_t)J.n, 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y),
                               J.cam.tiles_x, J.cam.tiles_y, w[v].dk[0], J.ranges, w[v].counters,
-                              w[v].grect};
+                              w[v].grect, J.dkeys != nullptr ? 1 : 0};
         }
         bin_init<<<dim3((init_max + kBlock - 1) / kBlock, count), kBlock, 0, s>>>(b);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -827,7 +824,8 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             b.count = n_live;
             for (int i = 0; i < n_live; i++) {
                 const BinWs &W = w[live[i]];
-                b.v[i] = PassArgs{W.dk[cur], pass == 0 ? nullptr : W.dv[cur], nullptr, W.dk[cur ^ 1], W.dv[cur ^ 1],
+                const uint32_t *kin = pass == 0 && jobs[live[i]].dkeys ? jobs[live[i]].dkeys : W.dk[cur];
+                b.v[i] = PassArgs{kin, pass == 0 ? nullptr : W.dv[cur], nullptr, W.dk[cur ^ 1], W.dv[cur ^ 1],
                                   nullptr,
                                   pass == 0 ? &W.counters[0] : &W.counters[1], &W.counters[1],
                                   W.digit_counts, W.digit_total, 8 * pass, 8};
@@ -846,7 +844,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             const size_t n = (size_t)J.n, cap = (size_t)J.cap;
             // backward index: [entry slot: cap][depth-ordered Gaussian: n][first slot: n + 1][visible count]
             uint32_t *bi = J.bwd_index;
-            d.v[i] = DupArgs{W.grect, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
+            d.v[i] = DupArgs{J.grect ? J.grect : W.grect, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
                              W.rect_info, W.counts, W.block_sums, J.k_total, &W.counters[2], W.tk[0], W.gslot,
                              bi ? bi + cap : nullptr, bi ? bi + cap + n : nullptr,
                              bi ? bi + cap + 2 * n + 1 : nullptr, key16};

@@ -249,6 +249,38 @@ gs_status gs_project(const gs_gaussians *gaussians /* host struct */,
 gs_status gs_project_views(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
                            const gs_camera *cameras, gs_splat *const *splats, void *stream);
 
+/* The sort's per-Gaussian inputs of one view, written by the projection
+ * (gs_project_views_binned) so that gs_bin_sort_views need not read the
+ * records back for them.  Device arrays of n entries each (depth_keys
+ * 4-byte, tile_rects 8-byte aligned):
+ *   depth_keys[n]   bits of the record's fp32 depth, 0xFFFFFFFF for a
+ *                   Gaussian that touches no tile
+ *   tile_rects[2n]  per Gaussian (x0 | y0 << 16, width | height << 16): its
+ *                   tile rect, first tile and extent in tiles; (0, 0) for a
+ *                   Gaussian that touches no tile
+ * Owned by the caller.  Both describe the records of the same call and stay
+ * valid only as long as those records are unchanged. */
+typedef struct gs_bin_keys {
+    uint32_t *depth_keys;
+    uint32_t *tile_rects;
+} gs_bin_keys;
+
+/* gs_project_views that also writes, for every view i whose bin_keys[i]
+ * has both pointers set, the sort inputs above (bin_keys: host array of
+ * n_views entries; an entry with NULL pointers writes records only).  The
+ * records are those of gs_project_views.  Passing the arrays to
+ * gs_bin_sort_views (gs_sort_view.depth_keys / tile_rects) spares the sort
+ * its read of every record: one pass over the Gaussians produces both (the
+ * projection of the VisionTech 4DGS page, section on technical architecture
+ * and key mechanisms, ahead of the tile binning of the BlitzGS page,
+ * section 2.1).
+ * Errors: as gs_project_views; GS_ERR_INVALID_ARG for one pointer of a
+ * pair set without the other, a misaligned pointer, or a view whose tile
+ * grid has more than 65535 tiles across or down. */
+gs_status gs_project_views_binned(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
+                                  const gs_camera *cameras, gs_splat *const *splats,
+                                  const gs_bin_keys *bin_keys /* host */, void *stream);
+
 /* Workspace for gs_bin_sort, in bytes, for n Gaussians, a key capacity
  * k_capacity and the camera's tile count. */
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t k_capacity, int32_t n_tiles);
@@ -309,14 +341,23 @@ typedef struct gs_sort_view {
     uint64_t *k_total;
     void *workspace;            /* its own, gs_bin_sort_workspace_bytes */
     size_t workspace_bytes;
+    /* optional, both or neither: the view's gs_bin_keys from
+     * gs_project_views_binned for these splats; the sort then takes each
+     * Gaussian's depth key and tile rect from them instead of its record
+     * (same results) */
+    const uint32_t *depth_keys;
+    const uint32_t *tile_rects;
 } gs_sort_view;
 
 /* gs_bin_sort for n_views views (host array) at once: the views go through
  * each step of the sort together, one launch per step for up to 8 views, so
  * views of a few million keys still fill the device.  Every view has its
  * own buffers and workspace; the results are those of n_views gs_bin_sort
- * calls.  Views may differ in size and resolution.
- * Errors: as gs_bin_sort, checked for every view before anything runs. */
+ * calls.  Views may differ in size and resolution, and in whether they
+ * bring gs_bin_keys.
+ * Errors: as gs_bin_sort, checked for every view before anything runs;
+ * GS_ERR_INVALID_ARG also for one of depth_keys / tile_rects set without
+ * the other or misaligned. */
 gs_status gs_bin_sort_views(int32_t n_views, const gs_sort_view *views /* host */,
                             void *stream);
 

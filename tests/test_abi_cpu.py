@@ -40,7 +40,7 @@ def test_struct_layouts_match_header():
     import tempfile
     pairs = [("gs_camera", B.GsCamera), ("gs_gaussians", B.GsGaussians), ("gs_grads", B.GsGrads),
              ("gs_fwd_view", B.GsFwdView), ("gs_sort_view", B.GsSortView), ("gs_bwd_view", B.GsBwdView),
-             ("gs_sh_adam", B.GsShAdam)]
+             ("gs_sh_adam", B.GsShAdam), ("gs_bin_keys", B.GsBinKeys)]
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "gs.h"', "int main(void) {"]
     expect = []
     for cname, cls in pairs:
@@ -139,6 +139,29 @@ def test_host_side_argument_errors_without_device():
     views[1].splats = 0x1000
     views[1].workspace_bytes = 16
     assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_WORKSPACE
+    # the projection's sort inputs: both or neither, aligned
+    views[1].workspace_bytes = 1 << 30
+    views[1].depth_keys = 0x1000
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    views[1].tile_rects = 0x1004
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    views[1].depth_keys, views[1].tile_rects = 0x1002, 0x1008
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    views[1].depth_keys = views[1].tile_rects = None
+    gb = B.GsGaussians()
+    gb.n, gb.sh_degree = 0, 0
+    camb = B.GsCamera()
+    camb.width, camb.height, camb.fx, camb.fy, camb.guard = 16, 16, 10.0, 10.0, 1.3
+    spb = (C.c_void_p * 1)(0x1000)
+    bk = (B.GsBinKeys * 1)()
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, None, None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_OK   # n = 0: nothing runs
+    bk[0].depth_keys = 0x1000
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_ERR_INVALID_ARG
+    bk[0].tile_rects = 0x100C
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_ERR_INVALID_ARG
+    bk[0].tile_rects = 0x1008
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_OK
     bgv = (C.c_float * 3)(0.0, 0.0, 0.0)
     # a negative near plane would let depths of either sign through, which the
     # depth key does not order; it is refused like any other bad camera field

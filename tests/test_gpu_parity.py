@@ -284,6 +284,51 @@ def test_batched_sort_equals_per_view_calls():
 
 
 
+def test_binned_projection_feeds_the_sort():
+    """gs_project_views_binned writes the records of gs_project_views plus
+    each view's depth keys and tile rects, and gs_bin_sort_views fed with
+    them (all views, or some) writes the bins of the plain calls, bit for
+    bit: four views of one scene, one of them a single tile."""
+    import dataclasses
+    sc = scenes.scene_like(seed=45, n=40_000, width=640, height=360, f=450.0, n_views=4)
+    sc.cameras[3] = dataclasses.replace(sc.cameras[3], width=15, height=9, cx=7.5, cy=4.5)
+    say("[gpu] binned projection: per-view references, 4 views")
+    refs, bufs = [], []
+    for v in range(4):
+        buf, K = run_view(sc, v)
+        refs.append((buf.splats.clone(), _bins_of(buf, K), K))
+        bufs.append(buf)
+    g = device_gaussians(sc)
+    gs = B.gaussians_struct(g, sc.sh_degree)
+    for rep, pre in enumerate((True, [True, False, True, False])):
+        say(f"[gpu] binned projection + sort, call {rep} (prebinned {pre})")
+        for b in bufs:
+            for t in (b.splats, b.vals, b.ranges, b.bwd_index, b.schedule, b.k_total, b.keys, b.depth_keys,
+                      b.tile_rects):
+                t.fill_(-1)
+        B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs], bin_keys=[b.bin_keys for b in bufs])
+        torch.cuda.synchronize()
+        for i, (b, (rec, _, _)) in enumerate(zip(bufs, refs)):
+            assert torch.equal(b.splats.view(torch.int32), rec.view(torch.int32)), f"view {i}: records"
+            tiles = rec[:, 11].view(torch.int32).cpu().numpy().view(np.uint32)
+            depth = rec[:, 2].contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+            dk = b.depth_keys.cpu().numpy().view(np.uint32)
+            gr = b.tile_rects.view(-1, 2).cpu().numpy().view(np.uint32)
+            vis = tiles > 0
+            assert np.array_equal(dk[vis], depth[vis]) and np.all(dk[~vis] == 0xFFFFFFFF), f"view {i}: keys"
+            assert np.all(gr[~vis] == 0), f"view {i}: culled rects"
+            w, h = gr[:, 1] & 0xFFFF, gr[:, 1] >> 16
+            assert np.array_equal((w * h)[vis], tiles[vis]), f"view {i}: rect sizes"
+            x0, y0 = gr[:, 0] & 0xFFFF, gr[:, 0] >> 16
+            assert np.all(x0[vis] + w[vis] <= b.cam.tiles_x) and np.all(y0[vis] + h[vis] <= b.cam.tiles_y)
+        B.bin_sort_views(bufs, True, prebinned=pre)
+        torch.cuda.synchronize()
+        for i, (b, (_, r, K)) in enumerate(zip(bufs, refs)):
+            got = _bins_of(b, K)
+            for key in r:
+                assert np.array_equal(np.asarray(got[key]), np.asarray(r[key])), f"view {i}: {key} differs"
+
+
 def _ambiguous_gaussians(ob, oo, cam):
     """Gaussians listed in a tile that holds a pixel with a near-threshold
     decision (or an alpha near the cap): their weights may legitimately
