@@ -156,6 +156,9 @@ __device__ __forceinline__ uint32_t strips_in_reach(float fv, const float4 &coni
 }
 
 // Per record and column: the dx terms shared by the lane's four pixels.
+// Contraction is off and the one fused step is an explicit fma, so the
+// forward and the backward evaluate the same operations wherever the
+// compiler inlines this.
 struct ColTerms { double dx, a0, bdx; };
 
 __device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double4 &q, double px)
@@ -163,7 +166,7 @@ __device__ __forceinline__ ColTerms col_terms(const double2 &uv, const double4 &
 #pragma clang fp contract(off)
     ColTerms c;
     c.dx = uv.x - px;                 // exact: difference of two floats
-    c.a0 = (q.x * c.dx) * c.dx + q.w;
+    c.a0 = fma(q.x * c.dx, c.dx, q.w);
     c.bdx = q.y * c.dx;
     return c;
 }
@@ -212,7 +215,7 @@ struct FwdRec {
     double2 uv;                   // mean
     double2 q01, q23;             // the exponent's terms, log2 o
     float4 rgb;                   // colour, opacity
-    uint4 meta;                   // list position, strip mask, Gaussian, -
+    uint4 meta;                   // 1 + list position, strip mask, Gaussian, -
 };
 static_assert(sizeof(FwdRec) == 80, "five 16-byte LDS reads per record");
 
@@ -247,7 +250,7 @@ __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, i
         r.q01 = make_double2(q.x, q.y);
         r.q23 = make_double2(q.z, q.w);
         r.rgb = rgb;
-        r.meta = make_uint4(f.m - start, strips, kWeight ? f.g : 0u, 0u);
+        r.meta = make_uint4(f.m - start + 1u, strips, kWeight ? f.g : 0u, 0u);
     }
     return __popcll(mask);
 }
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
                 const double4 q = make_double4(q01.x, q01.y, q23.x, q23.y);
                 const float4 rgb = R.rgb;
                 const uint4 meta = R.meta;
-                const uint32_t pos = meta.x + 1u;
+                const uint32_t pos = meta.x;         // what n_contrib records
                 // wave-uniform: the branches below are scalar; a strip whose
                 // pixels have all stopped is skipped too
                 const uint32_t strips = __builtin_amdgcn_readfirstlane(meta.y) & live;
