@@ -52,6 +52,9 @@ def lib():
             _build.build()
         _lib = C.CDLL(_build.LIB)
         _lib.orc_bin.restype = C.c_int64
+        _lib.orc_bin_reach.restype = C.c_int64
+        _lib.orc_tile_reach.restype = C.c_double
+        _lib.orc_tile_reach.argtypes = [C.c_double] * 6 + [C.c_int, C.c_int]
         _lib.orc_render.restype = C.c_int64
         _lib.orc_render_pixel.restype = C.c_int
     return _lib
@@ -106,9 +109,10 @@ def project(means, scales, quats, opacities, sh_degree, sh, cam, active=None,
     return out
 
 
-def bin_sort(proj: Dict[str, np.ndarray], cam) -> Dict[str, np.ndarray]:
+def bin_sort(proj: Dict[str, np.ndarray], cam, reach: bool = False) -> Dict[str, np.ndarray]:
     """Per-tile lists sorted by (tile, depth, index); keys built as
-    tile << 32 | fp32 bits of the depth (valid for fp32-contract records)."""
+    tile << 32 | fp32 bits of the depth (valid for fp32-contract records).
+    reach=True keeps only the tiles each Gaussian reaches (orc_bin_reach)."""
     rect = np.ascontiguousarray(proj["rect"], dtype=np.int32)
     z = np.ascontiguousarray(proj["z"], dtype=np.float64)
     n = rect.shape[1]
@@ -117,13 +121,27 @@ def bin_sort(proj: Dict[str, np.ndarray], cam) -> Dict[str, np.ndarray]:
     vals = np.zeros(max(k, 1), np.uint32)
     tile_of = np.zeros(max(k, 1), np.uint32)
     ranges = np.zeros(2 * tx * ty, np.uint32)
-    kk = lib().orc_bin(C.c_int64(n), _p(rect), _p(z), C.c_int(tx), C.c_int(ty), _p(vals),
-                       _p(tile_of), _p(ranges))
-    assert kk == k
+    if reach:
+        f64 = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+        u, v, conic, opac = f64(proj["u"]), f64(proj["v"]), f64(proj["conic"]), f64(proj["opacity"])
+        k = lib().orc_bin_reach(C.c_int64(n), _p(rect), _p(z), _p(u), _p(v), _p(conic), _p(opac), C.c_int(tx),
+                                C.c_int(ty), _p(vals), _p(tile_of), _p(ranges))
+    else:
+        kk = lib().orc_bin(C.c_int64(n), _p(rect), _p(z), C.c_int(tx), C.c_int(ty), _p(vals),
+                           _p(tile_of), _p(ranges))
+        assert kk == k
     vals, tile_of = vals[:k], tile_of[:k]
     depth_bits = proj["z"].astype(np.float32).view(np.uint32).astype(np.uint64)
     keys = (tile_of.astype(np.uint64) << np.uint64(32)) | depth_bits[vals]
     return dict(K=k, vals=vals, tile_of=tile_of, ranges=ranges.reshape(-1, 2), keys=keys)
+
+
+def tile_reach(proj, g: int, tile: int, cam) -> float:
+    """orc_tile_reach for Gaussian g and tile id `tile` of the camera's grid."""
+    tx_n = (cam.width + 15) // 16
+    c = proj["conic"]
+    return float(lib().orc_tile_reach(float(proj["u"][g]), float(proj["v"][g]), float(c[0][g]), float(c[1][g]),
+                                      float(c[2][g]), float(proj["opacity"][g]), tile % tx_n, tile // tx_n))
 
 
 def render(proj, bins, cam, bg=(0.0, 0.0, 0.0), tile_mask=None, bands=None, weight=False):

@@ -119,7 +119,13 @@ void orc_sh_basis(const double *d, double *Y, double *dY)
 /* Binning.  Every Gaussian emits one entry per tile of its rectangle; the
  * per-tile lists are ordered by view depth with the lower index first among
  * equal depths (readings: camera-space z, not Euclidean distance; index
- * tiebreak).  Done by brute force: collect everything, qsort. */
+ * tiebreak).  Done by brute force: collect everything, qsort.
+ * The reached-tile variant keeps an entry only when the Gaussian can reach
+ * alpha >= (1/255)(1 - 1e-3) somewhere on the box of the tile's pixel
+ * centres.  An entry it drops has alpha below 1/255 at every pixel of the
+ * tile, where compositing skips it anyway, so images are those of the full
+ * lists (a choice of this implementation: the pages do not say which tiles
+ * a Gaussian is listed in). */
 typedef struct { uint32_t tile; double z; uint32_t g; } bin_entry;
 
 static int bin_cmp(const void *pa, const void *pb)
@@ -131,22 +137,62 @@ static int bin_cmp(const void *pa, const void *pb)
     return 0;
 }
 
-int64_t orc_bin(int64_t n, const int32_t *rect, const double *z, int tiles_x,
-                int tiles_y, uint32_t *vals, uint32_t *tile_of, uint32_t *ranges)
+/* Minimum of the convex quadratic Q(d) = a dx^2 + 2 b dx dy + c dy^2 over
+ * the box [x0, x1] x [y0, y1]: 0 if the box holds d = 0, its unconstrained
+ * minimiser; otherwise the minimum lies on the boundary, and along each edge
+ * Q is a 1D convex quadratic whose minimum is at its vertex clamped to the
+ * edge (vertex dy = -b dx / c on an edge of fixed dx, dx = -b dy / a on an
+ * edge of fixed dy). */
+static double box_min_q(double a, double b, double c, double x0, double x1, double y0, double y1)
+{
+    if (x0 <= 0.0 && 0.0 <= x1 && y0 <= 0.0 && 0.0 <= y1) return 0.0;
+    double best = INFINITY;
+    const double xe[2] = {x0, x1}, ye[2] = {y0, y1};
+    for (int i = 0; i < 2; i++) {
+        const double dx = xe[i];
+        const double dy = fmin(fmax(-b * dx / c, y0), y1);
+        best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);
+    }
+    for (int i = 0; i < 2; i++) {
+        const double dy = ye[i];
+        const double dx = fmin(fmax(-b * dy / a, x0), x1);
+        best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);
+    }
+    return best;
+}
+
+/* Pixel centres of tile (tx, ty) are (16 tx + i + 1/2, 16 ty + j + 1/2),
+ * i, j = 0..15; the box they span, relative to the mean. */
+double orc_tile_reach(double u, double v, double a, double b, double c, double o, int tx, int ty)
+{
+    const double x0 = 16.0 * tx + 0.5 - u, y0 = 16.0 * ty + 0.5 - v;
+    return o * exp(-0.5 * box_min_q(a, b, c, x0, x0 + 15.0, y0, y0 + 15.0));
+}
+
+/* Collects the pairs (every pair of each rectangle, or only those whose tile
+ * the Gaussian reaches), sorts them and fills the outputs. */
+static int64_t bin_pairs(int64_t n, const int32_t *rect, const double *z, const double *u, const double *v,
+                         const double *conic, const double *opac, int tiles_x, int tiles_y, uint32_t *vals,
+                         uint32_t *tile_of, uint32_t *ranges)
 {
     int64_t K = 0;
     for (int64_t g = 0; g < n; g++)
         K += (int64_t)(rect[n + g] - rect[g]) * (rect[3 * n + g] - rect[2 * n + g]);
     bin_entry *e = (bin_entry *)malloc(sizeof(bin_entry) * (size_t)(K > 0 ? K : 1));
+    const double reach_min = (1.0 / 255.0) * (1.0 - 1e-3);
     int64_t m = 0;
     for (int64_t g = 0; g < n; g++)
         for (int ty = rect[2 * n + g]; ty < rect[3 * n + g]; ty++)
             for (int tx = rect[g]; tx < rect[n + g]; tx++) {
+                if (conic && !(orc_tile_reach(u[g], v[g], conic[g], conic[n + g], conic[2 * n + g], opac[g], tx,
+                                              ty) >= reach_min))
+                    continue;
                 e[m].tile = (uint32_t)(ty * tiles_x + tx);
                 e[m].z = z[g];
                 e[m].g = (uint32_t)g;
                 m++;
             }
+    K = m;
     qsort(e, (size_t)K, sizeof(bin_entry), bin_cmp);
     const int64_t T = (int64_t)tiles_x * tiles_y;
     for (int64_t t = 0; t < 2 * T; t++) ranges[t] = 0;
@@ -158,6 +204,19 @@ int64_t orc_bin(int64_t n, const int32_t *rect, const double *z, int tiles_x,
     }
     free(e);
     return K;
+}
+
+int64_t orc_bin(int64_t n, const int32_t *rect, const double *z, int tiles_x,
+                int tiles_y, uint32_t *vals, uint32_t *tile_of, uint32_t *ranges)
+{
+    return bin_pairs(n, rect, z, NULL, NULL, NULL, NULL, tiles_x, tiles_y, vals, tile_of, ranges);
+}
+
+int64_t orc_bin_reach(int64_t n, const int32_t *rect, const double *z, const double *u, const double *v,
+                      const double *conic, const double *opac, int tiles_x, int tiles_y, uint32_t *vals,
+                      uint32_t *tile_of, uint32_t *ranges)
+{
+    return bin_pairs(n, rect, z, u, v, conic, opac, tiles_x, tiles_y, vals, tile_of, ranges);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -73,6 +73,19 @@ void orc_project_f64(int64_t n, const double *means, const double *scales,
 int64_t orc_bin(int64_t n, const int32_t *rect, const double *z, int tiles_x,
                 int tiles_y, uint32_t *vals, uint32_t *tile_of, uint32_t *ranges);
 
+/* The largest opacity-scaled Gaussian value o exp(-Q_min / 2) over the box
+ * spanned by the pixel centres of tile (tx, ty), Q_min the minimum there of
+ * Q(d) = a dx^2 + 2 b dx dy + c dy^2, d = pixel centre - (u, v). */
+double orc_tile_reach(double u, double v, double a, double b, double c, double o, int tx, int ty);
+
+/* Binning restricted to reached tiles: as orc_bin, keeping the pair
+ * (Gaussian, tile) of a rectangle only when orc_tile_reach of that tile is at
+ * least (1/255)(1 - 1e-3).  u, v, opac[n], conic[3][n] as orc_proj_out.
+ * vals / tile_of need room for every pair of the rectangles. */
+int64_t orc_bin_reach(int64_t n, const int32_t *rect, const double *z, const double *u, const double *v,
+                      const double *conic, const double *opac, int tiles_x, int tiles_y, uint32_t *vals,
+                      uint32_t *tile_of, uint32_t *ranges);
+
 /* Near-threshold bands (relative) used to flag decisions that fp32 arithmetic
  * may legitimately take the other way. */
 typedef struct orc_bands { double alpha, trans, cap, clamp; } orc_bands;

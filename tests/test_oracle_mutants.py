@@ -64,6 +64,18 @@ MUTANTS = [
      "if (a->g != b->g) return a->g > b->g ? -1 : 1;", "binning"),
     ("radius_sqrt_dropped", "project_real.h", "REAL rf = CEIL((REAL)3.0 * SQRT(lam));",
      "REAL rf = CEIL((REAL)3.0 * lam);", "closed_form or rect"),
+    # the reached-tile binning
+    ("reach_edge_vertex_sign", "gs_oracle.c", "const double dy = fmin(fmax(-b * dx / c, y0), y1);",
+     "const double dy = fmin(fmax(b * dx / c, y0), y1);", "reach"),
+    ("reach_cross_term_factor", "gs_oracle.c",
+     "        best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);\n    }\n    for",
+     "        best = fmin(best, a * dx * dx + b * dx * dy + c * dy * dy);\n    }\n    for", "reach"),
+    ("reach_inside_test_dropped", "gs_oracle.c",
+     "if (x0 <= 0.0 && 0.0 <= x1 && y0 <= 0.0 && 0.0 <= y1) return 0.0;", "", "reach"),
+    ("reach_box_one_pixel_short", "gs_oracle.c", "return o * exp(-0.5 * box_min_q(a, b, c, x0, x0 + 15.0, y0, y0 + 15.0));",
+     "return o * exp(-0.5 * box_min_q(a, b, c, x0, x0 + 14.0, y0, y0 + 15.0));", "reach"),
+    ("reach_threshold_without_margin", "gs_oracle.c", "const double reach_min = (1.0 / 255.0) * (1.0 - 1e-3);",
+     "const double reach_min = (1.0 / 255.0) * (1.0 + 1e-3);", "reach"),
 ]
 
 

@@ -6,6 +6,7 @@ wrong sign or index, or a transposed operand in that part fails here.
 None of these needs a GPU.
 """
 
+import ctypes as C
 import math
 
 import numpy as np
@@ -327,6 +328,111 @@ def test_binning_equal_depths_keep_index_order():
         assert lst == sorted(lst, key=lambda g: (z32[g], g))
         front = [g for g in lst if z32[g] == z32.min()]
         assert front == sorted(front) and lst[:len(front)] == front
+
+
+def test_tile_reach_against_dense_sampling_and_closed_forms():
+    """orc_tile_reach (the maximum of o exp(-Q/2) over the box of a tile's
+    pixel centres) against a dense grid over that box, which it must bound
+    from above and approach; against the 256 pixel centres; o exactly when the
+    mean lies in the box; and the separable closed form of an axis-aligned
+    conic (b = 0: each axis at its nearest point of the box)."""
+    rng = np.random.default_rng(17)
+    grid = np.linspace(0.5, 15.5, 301)
+    centres = np.arange(16) + 0.5
+    for it in range(300):
+        tx, ty = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+        u, v = rng.uniform(-20, 84), rng.uniform(-20, 84)
+        l1, l2 = np.exp(rng.uniform(-6, 1.2, 2))
+        th = rng.uniform(0, np.pi)
+        R = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+        Q = R @ np.diag([l1, l2]) @ R.T
+        a, b, c = Q[0, 0], Q[0, 1], Q[1, 1]
+        o = rng.uniform(0.01, 1.0)
+        got = oracle.lib().orc_tile_reach(u, v, a, b, c, o, tx, ty)
+        dx = 16 * tx + grid[None, :] - u
+        dy = 16 * ty + grid[:, None] - v
+        dense = (o * np.exp(-0.5 * (a * dx * dx + 2 * b * dx * dy + c * dy * dy))).max()
+        assert got >= dense * (1 - 1e-12)
+        # the grid step is 0.05 px: the box maximum lies within half a step of a grid point
+        grad = np.sqrt(max(l1, l2)) * 0.05
+        assert got <= dense * math.exp(grad * (abs(math.log(max(got, 1e-300) / o)) * 2) ** 0.5 + grad * grad)
+        pdx = 16 * tx + centres[None, :] - u
+        pdy = 16 * ty + centres[:, None] - v
+        pix = (o * np.exp(-0.5 * (a * pdx * pdx + 2 * b * pdx * pdy + c * pdy * pdy))).max()
+        assert got >= pix * (1 - 1e-12)
+        if 16 * tx + 0.5 <= u <= 16 * tx + 15.5 and 16 * ty + 0.5 <= v <= 16 * ty + 15.5:
+            assert got == o
+    for it in range(100):
+        tx, ty = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+        u, v = rng.uniform(-20, 84), rng.uniform(-20, 84)
+        a, c = np.exp(rng.uniform(-6, 1.2, 2))
+        o = rng.uniform(0.01, 1.0)
+        ex = max(16 * tx + 0.5 - u, 0.0, u - (16 * tx + 15.5))
+        ey = max(16 * ty + 0.5 - v, 0.0, v - (16 * ty + 15.5))
+        want = o * math.exp(-0.5 * (a * ex * ex + c * ey * ey))
+        assert abs(oracle.lib().orc_tile_reach(u, v, a, 0.0, c, o, tx, ty) - want) <= 1e-14 * max(want, 1e-300)
+
+
+def test_reach_binning_is_the_full_lists_filtered():
+    """orc_bin_reach lists exactly the pairs of orc_bin whose tile the
+    Gaussian reaches (orc_tile_reach >= (1/255)(1 - 1e-3)), in the same
+    (tile, depth, index) order; a sizeable share is dropped."""
+    sc = scenes.scene_like(seed=6, n=3000, width=160, height=96, f=120.0, n_views=1)
+    cam = sc.cameras[0]
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sc.sh, cam)
+    full = oracle.bin_sort(p, cam)
+    red = oracle.bin_sort(p, cam, reach=True)
+    thr = (1.0 / 255.0) * (1.0 - 1e-3)
+    keep = np.array([oracle.tile_reach(p, int(g), int(t), cam) >= thr
+                     for g, t in zip(full["vals"], full["tile_of"])], bool)
+    assert 0.05 * full["K"] < full["K"] - keep.sum()
+    assert red["K"] == int(keep.sum())
+    assert np.array_equal(red["vals"], full["vals"][keep]) and np.array_equal(red["tile_of"], full["tile_of"][keep])
+    assert np.array_equal(red["keys"], full["keys"][keep])
+    T = cam.tiles_x * cam.tiles_y
+    for t in range(T):
+        s, e = red["ranges"][t]
+        assert np.all(red["tile_of"][s:e] == t) and (e - s) == int(np.sum(red["tile_of"] == t))
+
+
+def test_reach_threshold_keeps_the_margin_band():
+    """The reach test keeps a tile at (1/255)(1 - 1e-3) and above: an
+    axis-aligned Gaussian 4 px left of tile (1, 0), reach set by its opacity to
+    just inside, then just outside that bound, is listed there, then not
+    (tile (0, 0), which holds its mean, stays listed)."""
+    rect = np.array([[0], [2], [0], [1]], np.int32)
+    z = np.array([1.0])
+    u, v = np.array([12.5]), np.array([8.0])
+    conic = np.array([[0.5], [0.0], [0.5]])          # Q = (dx^2 + dy^2) / 2; tile 1's box is 4 px away
+    tiles = []
+    for rel in (1.0 - 0.4e-3, 1.0 - 1.6e-3, 1.0 + 0.5e-3):
+        o = np.array([(1.0 / 255.0) * rel * math.exp(0.5 * 0.5 * 16.0)])   # reach = rel / 255
+        vals, tile_of, ranges = np.zeros(2, np.uint32), np.zeros(2, np.uint32), np.zeros(4, np.uint32)
+        k = oracle.lib().orc_bin_reach(C.c_int64(1), oracle._p(rect), oracle._p(z), oracle._p(u), oracle._p(v),
+                                       oracle._p(conic), oracle._p(o), C.c_int(2), C.c_int(1), oracle._p(vals),
+                                       oracle._p(tile_of), oracle._p(ranges))
+        tiles.append(sorted(tile_of[:k].tolist()))
+    assert tiles == [[0, 1], [0], [0, 1]]
+
+
+def test_reach_binning_renders_the_same_images():
+    """The pairs the reach test drops are never composited: images and final
+    transmittance equal those of the full lists bit for bit, and each pixel's
+    last composited entry is the same Gaussian in both lists."""
+    sc = scenes.scene_like(seed=8, n=4000, width=96, height=80, f=90.0, n_views=1)
+    cam = sc.cameras[0]
+    p = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sc.sh, cam)
+    full, red = oracle.bin_sort(p, cam), oracle.bin_sort(p, cam, reach=True)
+    assert red["K"] < full["K"]
+    of, orr = oracle.render(p, full, cam, bg=(0.2, 0.3, 0.4)), oracle.render(p, red, cam, bg=(0.2, 0.3, 0.4))
+    assert np.array_equal(of["image"], orr["image"]) and np.array_equal(of["final_T"], orr["final_T"])
+    for j in range(cam.height):
+        for i in range(cam.width):
+            t = (j // 16) * cam.tiles_x + i // 16
+            nf, nr = int(of["n_contrib"][j, i]), int(orr["n_contrib"][j, i])
+            assert (nf == 0) == (nr == 0) and nr <= nf
+            if nf:
+                assert full["vals"][full["ranges"][t, 0] + nf - 1] == red["vals"][red["ranges"][t, 0] + nr - 1]
 
 
 # ---------------------------------------------------------- compositing ---
