@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--views", type=int, default=8)
     ap.add_argument("--sort", choices=["batched", "per-view"], default="batched",
                     help="bin/sort all views in one gs_bin_sort_views call, or one gs_bin_sort per view")
+    ap.add_argument("--tile-lists", choices=["reach", "rect"], default="reach",
+                    help="batched sort only: list each Gaussian in the tiles it reaches (alpha >= 1/255 possible "
+                         "at a pixel centre; same images and gradients), or in every tile of its 3-sigma rect")
     ap.add_argument("--bin-keys", choices=["projection", "sort"], default="projection",
                     help="batched sort only: each view's depth keys and tile rects written by the projection "
                          "(gs_project_views_binned), or read back from the records by the sort")
@@ -205,6 +208,10 @@ def main():
     else:
         gs = B.gaussians_struct(g, sc.sh_degree)
 
+    # the projection writes the sort's keys; lists hold the tiles each
+    # Gaussian reaches (both with the batched sort)
+    prebinned = args.sort == "batched" and args.bin_keys == "projection"
+    reach = args.sort == "batched" and args.tile_lists == "reach"
     # per-view buffers: key capacity = 25 % over a probe pass (rounded up to
     # 1024); every step reads the true K back and checks it
     k_all = torch.zeros(views, dtype=torch.int64, device=dev)
@@ -212,7 +219,8 @@ def main():
     for v in range(views):
         cam = sc.cameras[v]
         probe = B.ViewBuffers(sc.n, cam, 16 * sc.n, with_backward=False)
-        probe.forward(gs)
+        B.project(gs, probe.camc, probe.splats)
+        B.bin_sort_views([probe], False, reach=reach)
         torch.cuda.synchronize()
         k = int(probe.k_total.item())
         del probe
@@ -262,7 +270,6 @@ def main():
     # the views' sorts are independent: they may run on a few streams
     # (default priority) and join before the batched blend
     side = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.streams) - 1)]
-    prebinned = args.sort == "batched" and args.bin_keys == "projection"
     lanes = [stream] + side
     # a 2 GiB device copy (1 GiB read + 1 GiB written) before each cold step
     # pushes the step's inputs out of the 256 MB last-level cache and the L2
@@ -309,7 +316,8 @@ def main():
             for i, st in enumerate(lanes):
                 grp = bufs[i::len(lanes)]
                 if grp:
-                    timed("bin_sort_batch", lambda: B.bin_sort_views(grp, do_bwd, st, prebinned=prebinned), st)
+                    timed("bin_sort_batch", lambda: B.bin_sort_views(grp, do_bwd, st, prebinned=prebinned,
+                                                                     reach=reach), st)
         else:
             for i, b in enumerate(bufs):
                 st = lanes[i % len(lanes)]
@@ -465,7 +473,11 @@ def main():
         return (b + 7) // 8
     kb = 2 if all(c.tiles_x * c.tiles_y <= 65536 for c in sc.cameras[:views]) else 4
     per_g = 0 if prebinned else 32
-    bytes_sort = sum(per_g * sc.n + 128 * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
+    # the reach test: per visible Gaussian its rect, count and Gaussian index
+    # (16 B) and its mean and conic (32 B of the record) read by the count
+    # kernel, the same 32 B again by the duplication
+    per_vis = 128 + (80 if reach else 0)
+    bytes_sort = sum(per_g * sc.n + per_vis * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
                                               + max(0, tile_passes(c) - 1) * (kb + kb + 8 + kb + 8) + kb) * k
                      for nv, k, c in zip(n_vis, Ks, sc.cameras[:views]))
     # the survey's per-unit model of a plain 64-bit LSB radix sort of the K
@@ -493,8 +505,9 @@ def main():
                        f" + {sh_bytes:g} B of SH per Gaussian visible in any view" + (" + N B mask" if use_mask else "")),
         "sort": hbm("gs_bin_sort_views (all views, 4 streams: the sort phase)",
                     bytes_sort, warm["sort_phase_ms"]["median"],
-                    f"per view {per_g} B x N + 128 B x visible + 48 B x K (depth passes on the visible Gaussians, "
-                    "scan, duplication, 2 tile passes with 16-bit tile ids, ranges); the survey's 64-bit "
+                    f"per view {per_g} B x N + {per_vis} B x visible + 48 B x K (depth passes on the visible Gaussians, "
+                    f"scan, {'reach test, ' if reach else ''}duplication, 2 tile passes with 16-bit tile ids, "
+                    "ranges); the survey's 64-bit "
                     f"6-pass model would be {bytes_sort_lsb64} B"),
         "project_bwd": (hbm("project_bwd_color_kernel + project_bwd_geom_kernel (one call, all views)",
                             bytes_pbwd, med("project_bwd_batch"),
@@ -530,6 +543,7 @@ def main():
                            ("batched project writing the sort's depth keys and tile rects, " if prebinned
                             else "batched project, ") +
                            ("batched bin/sort" if args.sort == "batched" else "per view bin/sort") +
+                           (" (each Gaussian listed in the tiles it reaches)" if reach else "") +
                            ", K copied to the host (checked after the steps), batched blend fwd of all views" +
                            (" with per-Gaussian blending weights" if args.weights else "") +
                            (" (moving Gaussians, views spread over the time window)" if args.motion else "") +

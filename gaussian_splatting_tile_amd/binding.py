@@ -40,7 +40,7 @@ class GsSortView(C.Structure):
                 ("vals", C.c_void_p), ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p),
                 ("bwd_index", C.c_void_p), ("keys", C.c_void_p), ("k_total", C.c_void_p),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("depth_keys", C.c_void_p), ("tile_rects", C.c_void_p)]
+                ("depth_keys", C.c_void_p), ("tile_rects", C.c_void_p), ("reach_tiles", C.c_int32)]
 
 
 class GsBinKeys(C.Structure):
@@ -305,14 +305,16 @@ def bin_sort(splats, n, cam: GsCamera, k_capacity, vals, tile_ranges, schedule, 
                              _ptr(workspace), _nbytes(workspace), _stream(stream)), "gs_bin_sort")
 
 
-def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned: bool = False):
+def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned=False, reach=False):
     """gs_bin_sort_views over ViewBuffers objects (their splats must be
     current): one launch per sort step for up to 8 views.  prebinned: take
     the depth keys and tile rects that project_views(..., binned=True) wrote
     into the buffers with those splats (one flag for all views, or one per
-    view)."""
+    view).  reach: list each Gaussian only in the tiles it reaches (one flag
+    for all views, or one per view)."""
     nv = len(bufs)
     pre = list(prebinned) if isinstance(prebinned, (list, tuple)) else [prebinned] * nv
+    rch = list(reach) if isinstance(reach, (list, tuple)) else [reach] * nv
     arr = (GsSortView * max(nv, 1))()
     for i, b in enumerate(bufs):
         arr[i] = GsSortView(b.camc, _ptr(b.splats), int(b.n), int(b.k_capacity), _ptr(b.vals), _ptr(b.ranges),
@@ -320,7 +322,7 @@ def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned: bool = F
                             _ptr(b.k_total),
                             _ptr(b.ws), _nbytes(b.ws),
                             _ptr(b.depth_keys) if pre[i] else None,
-                            _ptr(b.tile_rects) if pre[i] else None)
+                            _ptr(b.tile_rects) if pre[i] else None, 1 if rch[i] else 0)
     _check(lib().gs_bin_sort_views(nv, arr, _stream(stream)), "gs_bin_sort_views")
 
 

@@ -196,6 +196,7 @@ static SortJob sort_job(const gs_sort_view &v)
     j.ws = v.workspace;
     j.dkeys = v.depth_keys;
     j.grect = (const uint2 *)v.tile_rects;
+    j.reach = v.reach_tiles != 0;
     return j;
 }
 
@@ -220,6 +221,7 @@ gs_status gs_bin_sort(const gs_splat *splats, int64_t n, const gs_camera *camera
     v.workspace_bytes = workspace_bytes;
     v.depth_keys = nullptr;
     v.tile_rects = nullptr;
+    v.reach_tiles = 0;
     return gs_bin_sort_views(1, &v, stream);
 }
 

@@ -85,45 +85,6 @@ __device__ __forceinline__ void stage_record(const Splat &s, double2 &uv, double
     rgb = make_float4(s.c.x, s.c.y, s.c.z, s.b.w);
 }
 
-// Can any pixel centre of the box of pixels [x0, x0 + w] x [y0, y0 + h]
-// (inclusive, pixel indices) reach alpha >= 1/255?  The minimum of
-// Q(d) = a dx^2 + 2 b dx dy + c dy^2 over the box of pixel centres is at the
-// mean if it lies inside, else on an edge, where Q is a 1D quadratic
-// minimised in closed form.  A record is dropped only when o exp(-Q_min / 2)
-// is below 1/255 by a relative margin of 1e-3, far above the error of the
-// per-pixel evaluation.
-// The edge minimiser is located in fp32 and clamped into the box; Q is then
-// evaluated there in fp64.  Q at any point of the box is >= its minimum, and
-// the location error only adds c * O(ulp)^2 (Q is stationary there), far
-// inside the margin.
-__device__ __forceinline__ bool box_may_contribute(float fu, float fv, const float4 &conic_o, int x0, int y0, int w,
-                                                   int h)
-{
-    const double a = conic_o.x, b = conic_o.y, c = conic_o.z;
-    const double W = (double)w, H = (double)h;
-    const double dxl = (double)x0 + 0.5 - (double)fu, dyl = (double)y0 + 0.5 - (double)fv;
-    if (dxl <= 0.0 && dxl + W >= 0.0 && dyl <= 0.0 && dyl + H >= 0.0) return true;
-    const float rb_c = -conic_o.y / conic_o.z, rb_a = -conic_o.y / conic_o.x;
-    const float fxl = (float)dxl, fyl = (float)dyl;
-    double best = 1e300;
-#pragma unroll 1
-    for (int e = 0; e < 4; e++) {
-        double dx, dy;
-        if (e < 2) {                   // edges x = const: minimise over dy
-            dx = dxl + W * e;
-            dy = (double)fminf(fmaxf(rb_c * (float)dx, fyl), fyl + (float)h);
-            dy = fmin(fmax(dy, dyl), dyl + H);
-        } else {                       // edges y = const: minimise over dx
-            dy = dyl + H * (e - 2);
-            dx = (double)fminf(fmaxf(rb_a * (float)dy, fxl), fxl + (float)w);
-            dx = fmin(fmax(dx, dxl), dxl + W);
-        }
-        best = fmin(best, a * dx * dx + 2.0 * b * dx * dy + c * dy * dy);
-    }
-    const float amax = conic_o.w * __expf((float)(-0.5 * best));
-    return amax >= kAlphaMin * (1.0f - 1e-3f);
-}
-
 // The strips of a tile whose pixel rows lie within the vertical reach of a
 // record: for a fixed dy, Q(dx, dy) is smallest at dx = -b dy / a, where it
 // equals dy^2 det / a (det = ac - b^2), so a pixel of that row can reach

@@ -395,43 +395,159 @@ constexpr int kScanItems = kBlock;               // Gaussians per scan / duplica
 
 // Per-view arguments of the slot scan and the duplication.
 struct DupArgs {
-    const uint2 *grect;          // tile rects by Gaussian index (bin_init)
+    const uint2 *grect;          // tile rects by Gaussian index (bin_init or the projection)
     const uint32_t *order;       // visible Gaussians in depth order
     const uint32_t *m_ptr;       // their number
     int tiles_x, tiles_y;
     uint64_t cap;                // key capacity
-    uint2 *rect_info;
-    uint32_t *counts;
-    uint64_t *block_sums;        // per 256 Gaussians: tiles, then their exclusive scan
+    uint2 *rect_info;            // [n] the rects in depth order
+    uint32_t *counts;            // [n] pairs per depth-ordered Gaussian
+    uint64_t *block_sums;        // per 256 Gaussians: pairs, then their exclusive scan
     uint64_t *k_total;
     uint32_t *k_eff;             // K clamped to the capacity
     uint32_t *tile_keys, *gslot; // duplicated entries
     uint32_t *bwd_order, *bwd_off, *bwd_count;   // optional backward index parts
     int key16;                   // tile ids stored as 16-bit keys
+    const Splat *splats;         // records (means and conics for the reach test)
+    uint32_t *reach_mask;        // [n] reached tiles of rects up to 32 tiles, row-major bits
+    int reach;                   // list only the tiles each Gaussian reaches
 };
 
+// For the reach test of a Gaussian's tiles: its conic and mean (fp64), the
+// slopes of the edge vertices (dy = -b dx / c on an edge of fixed dx,
+// dx = -b dy / a on an edge of fixed dy) and the largest Q at which
+// o exp(-Q / 2) still reaches (1/255)(1 - 1e-3), 2 ln(255 o / (1 - 1e-3)).
+// The slopes only place the point where Q is evaluated, and Q is stationary
+// along the edge there, so their fp32 rounding moves Q by a second-order
+// amount; the bound is formed in fp32 (error ~1e-7): a decision can differ
+// from an exact one only within ~1e-7 of the bound, relative.
+struct ReachG {
+    double a, b, c, sx, sy, u, v, qlim;
+};
+
+__device__ __forceinline__ ReachG reach_of(const Splat *__restrict__ splats, uint32_t g)
+{
+    const float4 sa = splats[g].a, sb = splats[g].b;
+    ReachG r;
+    r.a = sb.x;
+    r.b = sb.y;
+    r.c = sb.z;
+    r.sx = (double)(-sb.y * __builtin_amdgcn_rcpf(sb.z));
+    r.sy = (double)(-sb.y * __builtin_amdgcn_rcpf(sb.x));
+    r.u = sa.x;
+    r.v = sa.y;
+    r.qlim = (double)(2.0f * 0.6931471805599453f *
+                      __builtin_amdgcn_logf(sb.w * (255.0f / (1.0f - 1e-3f))));
+    return r;
+}
+
+// Does the Gaussian reach alpha >= (1/255)(1 - 1e-3) on the box of tile
+// (tx, ty)'s pixel centres, i.e. is the minimum there of
+// Q(d) = a dx^2 + 2 b dx dy + c dy^2 (d = pixel centre - mean) at most qlim?
+// The minimum is 0 if the box holds the mean.  Otherwise it lies on an edge
+// that faces the mean (the mean outside that edge's half-plane): at a
+// minimiser inside another edge, or at a corner of two others, the
+// optimality condition -Q d in the box's normal cone would give d^T Q d <= 0
+// with d != 0, impossible for a positive definite Q.  So at most one
+// vertical and one horizontal edge are evaluated, each at its vertex clamped
+// to the edge, all in fp64.  (The blend kernels apply an fp32 variant of
+// the same test, with the same margin, to every entry they stage.)
+__device__ __forceinline__ bool reaches(const ReachG &r, uint32_t tx, uint32_t ty)
+{
+    const double xl = (double)(tx * kTile) + 0.5 - r.u, xh = xl + (double)(kTile - 1);
+    const double yl = (double)(ty * kTile) + 0.5 - r.v, yh = yl + (double)(kTile - 1);
+    const bool out_x = xl > 0.0 || xh < 0.0, out_y = yl > 0.0 || yh < 0.0;
+    double q = 0.0;
+    if (out_x || out_y) {
+        q = INFINITY;
+        if (out_x) {
+            const double dx = xl > 0.0 ? xl : xh;
+            const double dy = fmin(fmax(r.sx * dx, yl), yh);
+            q = fmin(q, dx * (r.a * dx + 2.0 * r.b * dy) + r.c * dy * dy);
+        }
+        if (out_y) {
+            const double dy = yl > 0.0 ? yl : yh;
+            const double dx = fmin(fmax(r.sy * dy, xl), xh);
+            q = fmin(q, dx * (r.a * dx + 2.0 * r.b * dy) + r.c * dy * dy);
+        }
+    }
+    return q <= r.qlim;
+}
+
+constexpr uint32_t kMaskTiles = 32;   // rects up to this size keep their reached tiles as bits
+constexpr uint32_t kLaneTiles = 8;    // rects up to this size are tested by their own lane
+
+// Per depth-ordered Gaussian j (256 per block): its tile rect and its number
+// of pairs, and the block's sum.  A view that lists only reached tiles counts
+// the tiles of the rect the Gaussian reaches: a lane tests a rect of up to 8
+// tiles itself, the wave takes larger rects together (64 tiles per round),
+// and rects of up to 32 tiles keep their reached tiles as a row-major bit
+// mask for the duplication.
+template <bool kReach>
 __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
 {
     const DupArgs &a = b.v[blockIdx.y];
-    const uint2 *__restrict__ grect = a.grect;
-    const uint32_t *__restrict__ order = a.order;
-    uint2 *__restrict__ rect_info = a.rect_info;
-    uint32_t *__restrict__ counts = a.counts;
-    uint64_t *__restrict__ block_sums = a.block_sums;
     const uint32_t m = *a.m_ptr;
     const uint32_t j = blockIdx.x * kScanItems + threadIdx.x;
     if (blockIdx.x * kScanItems >= m) return;
-    uint64_t c = 0;
+    uint32_t c = 0, g = 0;
+    uint2 r = make_uint2(0u, 0u);
     if (j < m) {
-        const uint2 r = grect[order[j]];
-        const uint32_t w = r.y & 0xFFFFu, h = r.y >> 16;
-        c = (uint64_t)(w * h);
-        rect_info[j] = make_uint2(r.x, w);
-        counts[j] = w * h;
+        g = a.order[j];
+        r = a.grect[g];
+        c = (r.y & 0xFFFFu) * (r.y >> 16);
+        a.rect_info[j] = r;
     }
+    if (kReach && a.reach) {
+        const uint32_t x0 = r.x & 0xFFFFu, y0 = r.x >> 16, w = r.y & 0xFFFFu, h = r.y >> 16;
+        uint32_t mask = 0;
+        const bool own = j < m && c <= kLaneTiles;
+        if (own) {
+            const ReachG rg = reach_of(a.splats, g);
+            uint32_t bit = 1u;
+            for (uint32_t ty = y0; ty < y0 + h; ty++)
+                for (uint32_t tx = x0; tx < x0 + w; tx++, bit <<= 1)
+                    if (reaches(rg, tx, ty)) mask |= bit;
+        }
+        // the wave's larger rects, one after another, 64 tiles per round in
+        // row-major order
+        const int lane = threadIdx.x & (kWave - 1);
+        uint64_t shared_rects = __ballot(j < m && c > kLaneTiles);
+        uint32_t kept_shared = 0;
+        while (shared_rects) {
+            const int src = __builtin_ctzll(shared_rects);
+            shared_rects &= shared_rects - 1;
+            const uint32_t sg = (uint32_t)__shfl((int)g, src, kWave);
+            const uint32_t sxy = (uint32_t)__shfl((int)r.x, src, kWave);
+            const uint32_t swh = (uint32_t)__shfl((int)r.y, src, kWave);
+            const uint32_t sw = swh & 0xFFFFu, sn = sw * (swh >> 16);
+            const ReachG rg = reach_of(a.splats, sg);
+            uint32_t kept = 0, first_bits = 0;
+            for (uint32_t t0 = 0; t0 < sn; t0 += kWave) {
+                const uint32_t t = t0 + (uint32_t)lane;
+                bool k = false;
+                if (t < sn) {
+                    const uint32_t q = t / sw;
+                    k = reaches(rg, (sxy & 0xFFFFu) + (t - q * sw), (sxy >> 16) + q);
+                }
+                const uint64_t bits = __ballot(k);
+                if (t0 == 0) first_bits = (uint32_t)bits;
+                kept += (uint32_t)__popcll(bits);
+            }
+            if (lane == src) {
+                kept_shared = kept;
+                if (sn <= kMaskTiles) mask = first_bits;
+            }
+        }
+        if (j < m) {
+            c = own ? (uint32_t)__popc(mask) : kept_shared;
+            a.reach_mask[j] = mask;
+        }
+    }
+    if (j < m) a.counts[j] = c;
     uint64_t total;
-    block_exclusive_scan(c, &total);
-    if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+    block_exclusive_scan((uint64_t)c, &total);
+    if (threadIdx.x == 0) a.block_sums[blockIdx.x] = total;
 }
 
 // Exclusive scan of the block sums (one block per view); K and the clamped
@@ -476,29 +592,54 @@ __global__ __launch_bounds__(1024) void scan_blocks(const Batch<DupArgs> b)
     }
 }
 
-// Each depth-ordered Gaussian writes (tile id, g) for every tile of its rect,
-// row-major, at its slots.  A block takes 256 Gaussians, scans their counts
-// in LDS, then hands the block's entries out 256 at a time: each lane finds
-// its Gaussian by binary search over the block's offsets, so the work is
-// balanced however unequal the rects are.
+// The 256 depth-ordered Gaussians of a duplication block in LDS: the first
+// pair of each within the block (exclusive scan of their pair counts), its
+// Gaussian, rect and (reach views) reached-tile mask.
+struct DupBlock {
+    uint32_t off[kScanItems];
+    uint32_t g[kScanItems];
+    uint32_t xy[kScanItems];
+    uint32_t wh[kScanItems];
+    uint32_t mask[kScanItems];
+    float inv[kScanItems];
+};
+
+// Position of the k-th set bit (k from 0) of m, which has more than k.
+__device__ __forceinline__ uint32_t select_bit(uint32_t m, uint32_t k)
+{
+    uint32_t pos = 0;
+#pragma unroll
+    for (uint32_t s = 16; s > 0; s >>= 1) {
+        const uint32_t low = (uint32_t)__popc(m & ((1u << s) - 1u));
+        if (k >= low) {
+            k -= low;
+            m >>= s;
+            pos += s;
+        }
+    }
+    return pos;
+}
+
+// Each depth-ordered Gaussian writes (tile id, g) for every tile of its rect
+// (or, in a reach view, every tile it reaches), row-major, at its slots.  A
+// block takes 256 Gaussians, scans their counts in LDS, then hands the
+// block's entries out 256 at a time: each lane finds its Gaussian by binary
+// search over the block's offsets, so the work is balanced however unequal
+// the rects are.  In a reach view an entry's tile is the matching set bit of
+// its Gaussian's mask; rects of more than 32 tiles are left to a second
+// pass in which a wave tests each of its own such rects 64 tiles at a time
+// and compacts the reached ones in order with ballots.
+template <bool kReach>
 __global__ __launch_bounds__(kBlock) void duplicate_keys(const Batch<DupArgs> b)
 {
-    __shared__ uint32_t s_off[kScanItems];
-    __shared__ uint32_t s_g[kScanItems];
-    __shared__ uint32_t s_xy[kScanItems];
-    __shared__ uint32_t s_w[kScanItems];
-    __shared__ float s_inv[kScanItems];
+    __shared__ DupBlock s;
     const DupArgs &a = b.v[blockIdx.y];
-    const uint32_t *__restrict__ order = a.order;
-    const uint2 *__restrict__ rect_info = a.rect_info;
-    const uint32_t *__restrict__ counts = a.counts;
     const uint64_t *__restrict__ block_offsets = a.block_sums;
     const int tiles_x = a.tiles_x;
     const uint64_t cap = a.cap;
     uint32_t *__restrict__ tile_keys = a.tile_keys;
     uint32_t *__restrict__ gslot = a.gslot;
-    uint32_t *__restrict__ bwd_order = a.bwd_order;
-    uint32_t *__restrict__ bwd_off = a.bwd_off;
+    const bool reach = kReach && a.reach != 0;
     const uint32_t m = *a.m_ptr;
     const uint32_t base = blockIdx.x * kScanItems;
     if (base >= m) return;
@@ -506,42 +647,80 @@ __global__ __launch_bounds__(kBlock) void duplicate_keys(const Batch<DupArgs> b)
     const uint32_t j = base + threadIdx.x;
     uint32_t c = 0;
     if (threadIdx.x < n_items) {
-        const uint2 ri = rect_info[j];
-        c = counts[j];
-        s_g[threadIdx.x] = order[j];
-        s_xy[threadIdx.x] = ri.x;
-        s_w[threadIdx.x] = ri.y;
-        s_inv[threadIdx.x] = 1.0f / (float)ri.y;
+        const uint2 ri = a.rect_info[j];
+        c = a.counts[j];
+        s.g[threadIdx.x] = a.order[j];
+        s.xy[threadIdx.x] = ri.x;
+        s.wh[threadIdx.x] = ri.y;
+        s.mask[threadIdx.x] = reach ? a.reach_mask[j] : 0u;
+        s.inv[threadIdx.x] = 1.0f / (float)(ri.y & 0xFFFFu);
     }
     uint32_t total;
-    s_off[threadIdx.x] = block_exclusive_scan(c, &total);
+    s.off[threadIdx.x] = block_exclusive_scan(c, &total);
     __syncthreads();
     const uint64_t blk = block_offsets[blockIdx.x];
-    if (bwd_order && threadIdx.x < n_items) {
+    if (a.bwd_order && threadIdx.x < n_items) {
         // backward index: the depth-ordered Gaussians and their first slots
-        const uint64_t f = blk + s_off[threadIdx.x];
-        bwd_order[j] = s_g[threadIdx.x];
-        bwd_off[j] = (uint32_t)(f < 0xFFFFFFFFull ? f : 0xFFFFFFFFull);
+        const uint64_t f = blk + s.off[threadIdx.x];
+        a.bwd_order[j] = s.g[threadIdx.x];
+        a.bwd_off[j] = (uint32_t)(f < 0xFFFFFFFFull ? f : 0xFFFFFFFFull);
     }
     for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
         const uint64_t slot = blk + e;
         if (slot >= cap) break;
-        // the last li with s_off[li] <= e (every listed Gaussian has >= 1 tile)
+        // the last li with off[li] <= e (every Gaussian with an entry here has >= 1)
         int lo = 0;
 #pragma unroll
         for (int step = kScanItems / 2; step > 0; step >>= 1)
-            if (lo + step < (int)n_items && s_off[lo + step] <= e) lo += step;
-        const uint32_t within = e - s_off[lo];
-        const uint32_t w = s_w[lo];
-        // within / w via the reciprocal, corrected to the exact quotient
-        uint32_t q = (uint32_t)((float)within * s_inv[lo]);
-        if (q * w > within) q--;
-        else if ((q + 1) * w <= within) q++;
-        const uint32_t xy = s_xy[lo];
+            if (lo + step < (int)n_items && s.off[lo + step] <= e) lo += step;
+        const uint32_t wh = s.wh[lo], w = wh & 0xFFFFu;
+        uint32_t t = e - s.off[lo];
+        if (reach) {
+            if (w * (wh >> 16) > kMaskTiles) continue;           // the second pass
+            t = select_bit(s.mask[lo], t);
+        }
+        // t / w via the reciprocal, corrected to the exact quotient
+        uint32_t q = (uint32_t)((float)t * s.inv[lo]);
+        if (q * w > t) q--;
+        else if ((q + 1) * w <= t) q++;
+        const uint32_t xy = s.xy[lo];
         const uint32_t ty = (xy >> 16) + q;
-        const uint32_t tx = (xy & 0xFFFFu) + (within - q * w);
+        const uint32_t tx = (xy & 0xFFFFu) + (t - q * w);
         st_key(tile_keys, slot, ty * (uint32_t)tiles_x + tx, a.key16);
-        gslot[slot] = s_g[lo];
+        gslot[slot] = s.g[lo];
+    }
+    if (!kReach || !reach) return;
+    // rects of more than 32 tiles: the wave of their Gaussian, in order
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wh = threadIdx.x < n_items ? s.wh[threadIdx.x] : 0u;
+    uint64_t large = __ballot(threadIdx.x < n_items && (wh & 0xFFFFu) * (wh >> 16) > kMaskTiles);
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    while (large) {
+        const int src = __builtin_ctzll(large);
+        large &= large - 1;
+        const int li = (int)(threadIdx.x & ~(kWave - 1)) + src;
+        const uint32_t sxy = s.xy[li], swh = s.wh[li], sg = s.g[li];
+        const uint32_t sw = swh & 0xFFFFu, sn = sw * (swh >> 16);
+        const ReachG rg = reach_of(a.splats, sg);
+        uint64_t slot0 = blk + s.off[li];
+        for (uint32_t t0 = 0; t0 < sn; t0 += kWave) {
+            const uint32_t t = t0 + (uint32_t)lane;
+            bool k = false;
+            uint32_t tx = 0, ty = 0;
+            if (t < sn) {
+                const uint32_t q = t / sw;
+                tx = (sxy & 0xFFFFu) + (t - q * sw);
+                ty = (sxy >> 16) + q;
+                k = reaches(rg, tx, ty);
+            }
+            const uint64_t bits = __ballot(k);
+            const uint64_t slot = slot0 + (uint64_t)__popcll(bits & lt);
+            if (k && slot < cap) {
+                st_key(tile_keys, slot, ty * (uint32_t)tiles_x + tx, a.key16);
+                gslot[slot] = sg;
+            }
+            slot0 += (uint64_t)__popcll(bits);
+        }
     }
 }
 
@@ -717,7 +896,8 @@ struct BinWs {
     uint32_t *dk[2], *dv[2];           // depth sort ping-pong [n]
     uint2 *grect;                      // [n] tile rect by Gaussian index
     uint2 *rect_info;                  // [n] per depth-ordered Gaussian
-    uint32_t *counts;                  // [n] tiles touched, depth order
+    uint32_t *counts;                  // [n] tiles touched (or reached), depth order
+    uint32_t *reach_mask;              // [n] reached tiles of small rects, depth order
     uint64_t *block_sums;              // [ceil(n / 256)]
     uint32_t *tk[2], *tv[2], *ts[2];   // tile keys, Gaussians, slots ping-pong [cap]
     uint32_t *gslot;                   // [cap] Gaussian of each duplication slot
@@ -738,6 +918,7 @@ size_t carve_bin(char *base, int64_t n, int64_t cap, BinWs *ws)
     w.grect = c.take<uint2>(nn);
     w.rect_info = c.take<uint2>(nn);
     w.counts = c.take<uint32_t>(nn);
+    w.reach_mask = c.take<uint32_t>(nn);
     w.block_sums = c.take<uint64_t>((nn + kScanItems - 1) / kScanItems);
     w.tk[0] = c.take<uint32_t>(kk);
     w.tk[1] = c.take<uint32_t>(kk);
@@ -838,6 +1019,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
         const int key16 = tbits_max <= 16 ? 1 : 0;
         Batch<DupArgs> d;
         d.count = n_live;
+        bool any_reach = false;
         for (int i = 0; i < n_live; i++) {
             const SortJob &J = jobs[live[i]];
             const BinWs &W = w[live[i]];
@@ -847,12 +1029,15 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             d.v[i] = DupArgs{J.grect ? J.grect : W.grect, W.dv[cur], &W.counters[1], J.cam.tiles_x, J.cam.tiles_y, (uint64_t)J.cap,
                              W.rect_info, W.counts, W.block_sums, J.k_total, &W.counters[2], W.tk[0], W.gslot,
                              bi ? bi + cap : nullptr, bi ? bi + cap + n : nullptr,
-                             bi ? bi + cap + 2 * n + 1 : nullptr, key16};
+                             bi ? bi + cap + 2 * n + 1 : nullptr, key16, J.splats, W.reach_mask, J.reach ? 1 : 0};
+            any_reach = any_reach || J.reach;
         }
         const uint32_t nblk = (n_max + kScanItems - 1) / kScanItems;
-        scan_reduce<<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        if (any_reach) scan_reduce<true><<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        else scan_reduce<false><<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
         scan_blocks<<<dim3(1, n_live), 1024, 0, s>>>(d);
-        duplicate_keys<<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        if (any_reach) duplicate_keys<true><<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
+        else duplicate_keys<false><<<dim3(nblk, n_live), kBlock, 0, s>>>(d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
 
         // 3. tile passes over the tile ids, carrying each entry's Gaussian

@@ -347,6 +347,15 @@ typedef struct gs_sort_view {
      * (same results) */
     const uint32_t *depth_keys;
     const uint32_t *tile_rects;
+    /* nonzero: list a Gaussian only in the tiles of its rect that it reaches,
+     * i.e. where o exp(-Q/2) >= (1/255)(1 - 1e-3) somewhere on the box of
+     * the tile's pixel centres (Q the minimum over that box of the conic's
+     * quadratic form: closed form, evaluated in fp64).  The pairs it leaves
+     * out have alpha below 1/255 at every pixel of their tile, so the blend
+     * skips them anyway: images, final_T and gradients equal those of the
+     * full lists; K, vals, the ranges and n_contrib refer to the shorter
+     * lists.  0: every tile of the rect. */
+    int32_t reach_tiles;
 } gs_sort_view;
 
 /* gs_bin_sort for n_views views (host array) at once: the views go through

@@ -329,6 +329,100 @@ def test_binned_projection_feeds_the_sort():
                 assert np.array_equal(np.asarray(got[key]), np.asarray(r[key])), f"view {i}: {key} differs"
 
 
+def _pairs(vals, ranges):
+    """(tile, Gaussian) pairs of a binning, as a set."""
+    out = set()
+    for t, (a, b) in enumerate(np.asarray(ranges).reshape(-1, 2)):
+        out.update((t, int(g)) for g in vals[a:b])
+    return out
+
+
+def test_reach_binning_matches_oracle_and_leaves_results_unchanged():
+    """Lists restricted to the tiles each Gaussian reaches (gs_sort_view
+    .reach_tiles): bins equal the oracle's reach binning (a pair may differ
+    only within 1e-5 of the reach bound, where fp32 and fp64 can decide
+    apart); the blend over them writes the images and final_T of the full
+    lists bit for bit, each pixel's last composited entry is the same
+    Gaussian, and the backward's per-Gaussian sums are the same.  Three
+    views, the projection writing the sort keys for two of them."""
+    sc = scenes.scene_like(seed=47, n=40_000, width=640, height=360, f=450.0, n_views=3, upstream=True)
+    # some large Gaussians (rects past 32 tiles take the duplication's second pass)
+    big = np.random.default_rng(48).choice(sc.n, 300, replace=False)
+    sc.scales = sc.scales.copy()
+    sc.scales[:, big] *= np.float32(12.0)
+    sc.log_scales = np.log(sc.scales).astype(np.float32)
+    thr = (1.0 / 255.0) * (1.0 - 1e-3)
+    say("[gpu] reach binning: full-list references, 3 views")
+    full, reach = [], []
+    for v in range(3):
+        buf, K = run_view(sc, v)
+        full.append((buf, K))
+    g = device_gaussians(sc)
+    gs = B.gaussians_struct(g, sc.sh_degree)
+    bufs = [B.ViewBuffers(sc.n, sc.cameras[v], full[v][1], with_keys=True) for v in range(3)]
+    say("[gpu] reach binning: batched projection + sort with reach_tiles")
+    B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs], bin_keys=[b.bin_keys for b in bufs])
+    B.bin_sort_views(bufs, True, prebinned=[True, False, True], reach=True)
+    torch.cuda.synchronize()
+    for v, b in enumerate(bufs):
+        cam = sc.cameras[v]
+        op = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, sc.sh_degree, sc.sh, cam)
+        ob = oracle.bin_sort(op, cam, reach=True)
+        K = int(b.k_total.item())
+        assert K < full[v][1]
+        assert int((op["tiles"] > 32).sum()) > 20 and int(((op["tiles"] > 8) & (op["tiles"] <= 32)).sum()) > 20
+        vals = b.vals[:K].cpu().numpy().view(np.uint32)
+        ranges = b.ranges.cpu().numpy().view(np.uint32)
+        diff = _pairs(vals, ranges) ^ _pairs(ob["vals"], ob["ranges"])
+        for t, gi in diff:
+            assert abs(oracle.tile_reach(op, gi, t, cam) / thr - 1.0) < 1e-5, f"view {v}: pair ({t}, {gi})"
+        if not diff:
+            assert K == ob["K"] and np.array_equal(vals, ob["vals"])
+            assert np.array_equal(ranges.reshape(-1), ob["ranges"].reshape(-1))
+            assert np.array_equal(b.keys[:K].cpu().numpy().view(np.uint64), ob["keys"])
+        # backward index: the depth-ordered Gaussians' first slots partition [0, K)
+        bi = b.bwd_index.cpu().numpy().view(np.uint32)
+        n, cap = b.n, b.k_capacity
+        n_vis = int(bi[cap + 2 * n + 1])
+        off = bi[cap + n:cap + n + n_vis + 1].astype(np.int64)
+        assert off[0] == 0 and off[-1] == K and np.all(np.diff(off) >= 0)
+        order = bi[cap:cap + n_vis]
+        slot_g = np.repeat(order, np.diff(off))
+        assert np.array_equal(np.sort(vals), np.sort(slot_g))
+        assert np.array_equal(slot_g[bi[:K]], vals)              # each entry's slot belongs to its Gaussian
+    say("[gpu] reach binning: blend forward over reach and full lists")
+    B.render_fwd_views(bufs, (0.1, 0.2, 0.3))
+    for fb, _ in full:
+        fb.n_contrib.zero_()
+    B.render_fwd_views([fb for fb, _ in full], (0.1, 0.2, 0.3))
+    torch.cuda.synchronize()
+    for v, (b, (fb, _)) in enumerate(zip(bufs, full)):
+        assert torch.equal(b.image, fb.image) and torch.equal(b.final_T, fb.final_T), f"view {v}"
+        nr, nf = b.n_contrib.long(), fb.n_contrib.long()
+        assert torch.equal(nr == 0, nf == 0) and bool((nr <= nf).all())
+        H, W = nr.shape
+        tile = ((torch.arange(H, device="cuda") // 16)[:, None] * b.cam.tiles_x +
+                (torch.arange(W, device="cuda") // 16)[None, :]).long()
+        has = nf > 0
+        gr = b.vals.long()[b.ranges.long()[:, 0][tile] + nr - 1][has]
+        gf = fb.vals.long()[fb.ranges.long()[:, 0][tile] + nf - 1][has]
+        assert torch.equal(gr, gf), f"view {v}: last composited entry"
+    say("[gpu] reach binning: blend backward sums over reach and full lists")
+    dLs = [torch.from_numpy(np.ascontiguousarray(sc.upstream(v))).cuda() for v in range(3)]
+    g2r = [torch.full((sc.n, 9), float("nan"), device="cuda") for _ in range(3)]
+    g2f = [torch.full((sc.n, 9), float("nan"), device="cuda") for _ in range(3)]
+    wsr = [torch.empty(B.render_bwd_screen_workspace_bytes(b.k_capacity), dtype=torch.uint8, device="cuda")
+           for b in bufs]
+    wsf = [torch.empty(B.render_bwd_screen_workspace_bytes(fb.k_capacity), dtype=torch.uint8, device="cuda")
+           for fb, _ in full]
+    B.render_bwd_screen_views(bufs, dLs, g2r, wsr, (0.1, 0.2, 0.3))
+    B.render_bwd_screen_views([fb for fb, _ in full], dLs, g2f, wsf, (0.1, 0.2, 0.3))
+    torch.cuda.synchronize()
+    for v in range(3):
+        vis = bufs[v].splats[:, 11].view(torch.int32) != 0
+        assert torch.equal(g2r[v][vis], g2f[v][vis]), f"view {v}: screen-space sums"
+
+
 def _ambiguous_gaussians(ob, oo, cam):
     """Gaussians listed in a tile that holds a pixel with a near-threshold
     decision (or an alpha near the cap): their weights may legitimately
