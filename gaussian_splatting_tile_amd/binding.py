@@ -32,7 +32,8 @@ class GsCamera(C.Structure):
 class GsFwdView(C.Structure):
     _fields_ = [("camera", GsCamera), ("splats", C.c_void_p), ("vals", C.c_void_p),
                 ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("image", C.c_void_p),
-                ("final_T", C.c_void_p), ("n_contrib", C.c_void_p), ("weight", C.c_void_p)]
+                ("final_T", C.c_void_p), ("n_contrib", C.c_void_p), ("weight", C.c_void_p),
+                ("reached_lists", C.c_int32)]
 
 
 class GsSortView(C.Structure):
@@ -52,7 +53,7 @@ class GsBwdView(C.Structure):
                 ("tile_ranges", C.c_void_p), ("schedule", C.c_void_p), ("bwd_index", C.c_void_p),
                 ("k_capacity", C.c_int64), ("final_T", C.c_void_p), ("n_contrib", C.c_void_p),
                 ("dL_dimage", C.c_void_p), ("g2", C.c_void_p), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t)]
+                ("workspace_bytes", C.c_size_t), ("reached_lists", C.c_int32)]
 
 
 class GsGaussians(C.Structure):
@@ -317,6 +318,7 @@ def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned=False, re
     rch = list(reach) if isinstance(reach, (list, tuple)) else [reach] * nv
     arr = (GsSortView * max(nv, 1))()
     for i, b in enumerate(bufs):
+        b.reached = bool(rch[i])
         arr[i] = GsSortView(b.camc, _ptr(b.splats), int(b.n), int(b.k_capacity), _ptr(b.vals), _ptr(b.ranges),
                             _ptr(b.schedule), _ptr(b.bwd_index) if with_bwd else None, _ptr(b.keys),
                             _ptr(b.k_total),
@@ -364,7 +366,8 @@ def render_fwd_views(bufs, bg: Sequence[float] = (0.0, 0.0, 0.0), stream=None, w
     arr = (GsFwdView * max(nv, 1))()
     for i, b in enumerate(bufs):
         arr[i] = GsFwdView(b.camc, _ptr(b.splats), _ptr(b.vals), _ptr(b.ranges), _ptr(b.schedule),
-                           _ptr(b.image), _ptr(b.final_T), _ptr(b.n_contrib), _ptr(weights[i]))
+                           _ptr(b.image), _ptr(b.final_T), _ptr(b.n_contrib), _ptr(weights[i]),
+                           1 if getattr(b, "reached", False) else 0)
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     _check(lib().gs_render_fwd_views(nv, arr, C.cast(bgv, C.c_void_p), _stream(stream)), "gs_render_fwd_views")
 
@@ -405,7 +408,7 @@ def render_bwd_screen_views(bufs, dLs, g2s, workspaces, bg: Sequence[float] = (0
     for i, (b, dL, g2, ws) in enumerate(zip(bufs, dLs, g2s, workspaces)):
         arr[i] = GsBwdView(b.camc, b.n, _ptr(b.splats), _ptr(b.vals), _ptr(b.ranges), _ptr(b.schedule),
                            _ptr(b.bwd_index), b.k_capacity, _ptr(b.final_T), _ptr(b.n_contrib), _ptr(dL),
-                           _ptr(g2), _ptr(ws), _nbytes(ws))
+                           _ptr(g2), _ptr(ws), _nbytes(ws), 1 if getattr(b, "reached", False) else 0)
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     _check(lib().gs_render_bwd_screen_views(nv, arr, C.cast(bgv, C.c_void_p), _stream(stream)),
            "gs_render_bwd_screen_views")
@@ -467,6 +470,9 @@ class ViewBuffers:
         self.bwd_index = (torch.empty(bwd_index_words(n, self.k_capacity), dtype=torch.int32, device=device)
                           if with_backward else None)
         # the sort's per-Gaussian inputs when the projection writes them
+        # set by bin_sort_views: the lists hold only reached tiles (a hint
+        # passed on to the blend kernels)
+        self.reached = False
         self.depth_keys = torch.empty(max(n, 1), dtype=torch.int32, device=device)
         self.tile_rects = torch.empty(2 * max(n, 1), dtype=torch.int32, device=device)
 
@@ -475,6 +481,7 @@ class ViewBuffers:
         return (self.depth_keys, self.tile_rects)
 
     def forward(self, gs: GsGaussians, bg=(0.0, 0.0, 0.0), stream=None):
+        self.reached = False
         project(gs, self.camc, self.splats, stream)
         bin_sort(self.splats, self.n, self.camc, self.k_capacity, self.vals, self.ranges, self.schedule,
                  self.bwd_index, self.keys, self.k_total, self.ws, stream)

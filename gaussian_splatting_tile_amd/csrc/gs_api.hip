@@ -267,6 +267,7 @@ gs_status gs_render_fwd(const gs_splat *splats, const uint32_t *vals, const uint
     b.v[0].final_T = final_T;
     b.v[0].n_contrib = n_contrib;
     b.v[0].weight = nullptr;
+    b.v[0].tile_test = 1;
     return from_hip(launch_render_fwd(b, (hipStream_t)stream));
 }
 
@@ -300,6 +301,7 @@ gs_status gs_render_fwd_views(int32_t n_views, const gs_fwd_view *views, const f
             d.final_T = w.final_T;
             d.n_contrib = w.n_contrib;
             d.weight = w.weight;
+            d.tile_test = w.reached_lists ? 0 : 1;
             const int nt = d.cam.tiles_x * d.cam.tiles_y;
             if (nt > b.max_tiles) b.max_tiles = nt;
         }
@@ -371,6 +373,7 @@ static hipError_t screen_backward(int count, const gs_bwd_view *views, const flo
         d.n_contrib = w.n_contrib;
         d.dL_dimage = w.dL_dimage;
         d.partial = (float *)w.workspace;
+        d.tile_test = w.reached_lists ? 0 : 1;
         const int nt = d.cam.tiles_x * d.cam.tiles_y;
         if (nt > b.max_tiles) b.max_tiles = nt;
     }
@@ -425,6 +428,7 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     w.g2 = g2;
     w.workspace = workspace;
     w.workspace_bytes = workspace_bytes;
+    w.reached_lists = 0;
     hipError_t e = screen_backward(1, &w, bg, s);
     if (e != hipSuccess) return GS_ERR_HIP;
     ViewBatch vb;
@@ -463,6 +467,7 @@ gs_status gs_render_bwd_screen(const gs_camera *camera, int64_t n, const gs_spla
     w.g2 = g2;
     w.workspace = workspace;
     w.workspace_bytes = workspace_bytes;
+    w.reached_lists = 0;
     return from_hip(screen_backward(1, &w, bg, (hipStream_t)stream));
 }
 

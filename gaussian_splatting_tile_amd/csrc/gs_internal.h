@@ -237,6 +237,7 @@ struct FwdView {
     float *final_T;
     uint32_t *n_contrib;
     float *weight;                // optional: += per-Gaussian blending weights
+    int tile_test;                // apply the per-entry tile test while staging
 };
 struct FwdBatch {
     int count;
@@ -258,6 +259,7 @@ struct BwdView {
     const uint32_t *n_contrib;
     const float *dL_dimage;
     float *partial;               // [k_capacity][9]
+    int tile_test;                // apply the per-entry tile test while staging
 };
 struct BwdBatch {
     int count;

@@ -186,13 +186,15 @@ static_assert(sizeof(FwdRec) == 80, "five 16-byte LDS reads per record");
 // order.
 template <bool kWeight>
 __device__ __forceinline__ int stage_fetched(const Fetched &f, uint32_t start, int x0, int y0, uint32_t live,
-                                             FwdRec *s_rec)
+                                             bool tile_test, FwdRec *s_rec)
 {
     const int lane = threadIdx.x;
     // the cheap test first: most records that fail, fail it; strips whose
-    // pixels have all stopped stay stopped, so they are left out here too
+    // pixels have all stopped stay stopped, so they are left out here too.
+    // Lists of reached tiles have passed the tile test in the sort.
     uint32_t strips = f.valid ? strips_in_reach(f.a.y, f.b, y0) & live : 0u;
-    if (strips != 0u && !box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1)) strips = 0u;
+    if (tile_test && strips != 0u && !box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1))
+        strips = 0u;
     const bool keep = strips != 0u;
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -233,16 +235,18 @@ static_assert(sizeof(BwdRec) == 96, "six 16-byte LDS reads per record");
 // principal frame of its conic; a dropped entry gets its nine partial sums
 // zeroed.
 __device__ __forceinline__ int stage_fetched_bwd(const Fetched &f, uint32_t entry_slot, uint32_t start, int x0,
-                                                 int y0, const uint32_t lrow[4], BwdRec *s_rec,
+                                                 int y0, const uint32_t lrow[4], bool tile_test, BwdRec *s_rec,
                                                  float *__restrict__ partial)
 {
     const int lane = threadIdx.x;
     // strips in reach whose pixels composited entries at or past this one
+    // (lists of reached tiles have passed the tile test in the sort)
     uint32_t alive = 0;
 #pragma unroll
     for (int r = 0; r < 4; r++) alive |= (f.m - start < lrow[r] ? 1u : 0u) << r;
     const uint32_t strips = f.valid ? strips_in_reach(f.a.y, f.b, y0) & alive : 0u;
-    const bool keep = strips != 0u && box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1);
+    const bool keep = strips != 0u &&
+                      (!tile_test || box_may_contribute(f.a.x, f.a.y, f.b, x0, y0, kTile - 1, kTile - 1));
     if (f.valid && !keep) zero_partial(partial, entry_slot);
     const uint64_t mask = __ballot(keep);
     if (keep) {
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(kLanes) void render_fwd_kernel(const FwdBatch batch
         for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
             uint32_t live = live_strips(T);
             if (live == 0u) break;
-            const int nb = stage_fetched<kWeight>(cur, start, tx * kTile, ty * kTile, live, s_rec);
+            const int nb = stage_fetched<kWeight>(cur, start, tx * kTile, ty * kTile, live, V.tile_test != 0, s_rec);
             cur.m = next_m;
             cur.valid = next_valid;
             fetch_record(splats, next_g, next_valid, cur);
@@ -620,7 +624,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(5))) voi
     uint32_t next_g = next_valid ? vals[(uint32_t)next_m] : 0u;
     uint32_t next_slot = next_valid ? entry_slots[(uint32_t)next_m] : 0u;
     for (int64_t bend = (int64_t)stop; bend > (int64_t)start; bend -= kBatch) {
-        const int nb = stage_fetched_bwd(cur, cur_slot, start, tx * kTile, ty * kTile, lrow, s_rec, partial);
+        const int nb = stage_fetched_bwd(cur, cur_slot, start, tx * kTile, ty * kTile, lrow, V.tile_test != 0,
+                                         s_rec, partial);
         cur.m = next_valid ? (uint32_t)next_m : 0u;
         cur.valid = next_valid;
         cur_slot = next_slot;

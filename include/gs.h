@@ -407,6 +407,10 @@ typedef struct gs_fwd_view {
     float *final_T;
     uint32_t *n_contrib;
     float *weight;
+    /* nonzero when the lists come from gs_bin_sort_views with reach_tiles:
+     * every entry passed the reach test there, so the blend skips its own
+     * per-entry tile test (a hint: the results are the same either way) */
+    int32_t reached_lists;
 } gs_fwd_view;
 
 /* gs_render_fwd of n_views views (host array) with one background colour,
@@ -493,6 +497,7 @@ typedef struct gs_bwd_view {
     float *g2;
     void *workspace;
     size_t workspace_bytes;
+    int32_t reached_lists;      /* as in gs_fwd_view */
 } gs_bwd_view;
 
 /* gs_render_bwd_screen of n_views views (host array) with one background
