@@ -473,10 +473,10 @@ def main():
         return (b + 7) // 8
     kb = 2 if all(c.tiles_x * c.tiles_y <= 65536 for c in sc.cameras[:views]) else 4
     per_g = 0 if prebinned else 32
-    # the reach test: per visible Gaussian its rect, count and Gaussian index
-    # (16 B) and its mean and conic (32 B of the record) read by the count
-    # kernel, the same 32 B again by the duplication
-    per_vis = 128 + (80 if reach else 0)
+    # the reach test: per visible Gaussian the mean and conic of its record
+    # (32 B) read by the slot scan, and its tile mask written there and read
+    # by the duplication (4 + 4 B)
+    per_vis = 128 + (40 if reach else 0)
     bytes_sort = sum(per_g * sc.n + per_vis * nv + (6 + (tile_passes(c) > 0) * (kb + kb + 4 + kb + 8)
                                               + max(0, tile_passes(c) - 1) * (kb + kb + 8 + kb + 8) + kb) * k
                      for nv, k, c in zip(n_vis, Ks, sc.cameras[:views]))

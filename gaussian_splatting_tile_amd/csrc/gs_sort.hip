@@ -475,11 +475,11 @@ __device__ __forceinline__ bool reaches(const ReachG &r, uint32_t tx, uint32_t t
 }
 
 constexpr uint32_t kMaskTiles = 32;   // rects up to this size keep their reached tiles as bits
-constexpr uint32_t kLaneTiles = 8;    // rects up to this size are tested by their own lane
+constexpr uint32_t kLaneTiles = 16;   // rects up to this size are tested by their own lane
 
 // Per depth-ordered Gaussian j (256 per block): its tile rect and its number
 // of pairs, and the block's sum.  A view that lists only reached tiles counts
-// the tiles of the rect the Gaussian reaches: a lane tests a rect of up to 8
+// the tiles of the rect the Gaussian reaches: a lane tests a rect of up to 16
 // tiles itself, the wave takes larger rects together (64 tiles per round),
 // and rects of up to 32 tiles keep their reached tiles as a row-major bit
 // mask for the duplication.
