@@ -425,9 +425,8 @@ struct ReachG {
     double a, b, c, sx, sy, u, v, qlim;
 };
 
-__device__ __forceinline__ ReachG reach_of(const Splat *__restrict__ splats, uint32_t g)
+__device__ __forceinline__ ReachG reach_of(const float4 &sa, const float4 &sb)
 {
-    const float4 sa = splats[g].a, sb = splats[g].b;
     ReachG r;
     r.a = sb.x;
     r.b = sb.y;
@@ -439,6 +438,11 @@ __device__ __forceinline__ ReachG reach_of(const Splat *__restrict__ splats, uin
     r.qlim = (double)(2.0f * 0.6931471805599453f *
                       __builtin_amdgcn_logf(sb.w * (255.0f / (1.0f - 1e-3f))));
     return r;
+}
+
+__device__ __forceinline__ ReachG reach_of(const Splat *__restrict__ splats, uint32_t g)
+{
+    return reach_of(splats[g].a, splats[g].b);
 }
 
 // Does the Gaussian reach alpha >= (1/255)(1 - 1e-3) on the box of tile
@@ -492,9 +496,19 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
     if (blockIdx.x * kScanItems >= m) return;
     uint32_t c = 0, g = 0;
     uint2 r = make_uint2(0u, 0u);
+    float4 sa = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sb = sa;
     if (j < m) {
         g = a.order[j];
-        r = a.grect[g];
+        if (kReach && a.reach) {
+            // the reach test reads the record's mean and conic anyway; the
+            // rect follows from them by the projection's own function (the
+            // same bits), which saves gathering it
+            sa = a.splats[g].a;
+            sb = a.splats[g].b;
+            r = pack_rect(tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x, (float)a.tiles_y));
+        } else {
+            r = a.grect[g];
+        }
         c = (r.y & 0xFFFFu) * (r.y >> 16);
         a.rect_info[j] = r;
     }
@@ -503,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void scan_reduce(const Batch<DupArgs> b)
         uint32_t mask = 0;
         const bool own = j < m && c <= kLaneTiles;
         if (own) {
-            const ReachG rg = reach_of(a.splats, g);
+            const ReachG rg = reach_of(sa, sb);
             uint32_t bit = 1u;
             for (uint32_t ty = y0; ty < y0 + h; ty++)
                 for (uint32_t tx = x0; tx < x0 + w; tx++, bit <<= 1)
