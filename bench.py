@@ -305,8 +305,8 @@ def main():
             timed("active_mask", lambda: B.active_mask(scores, sc.n, keep, mask, mask_ws, stream))
         # the views' records in one pass over the Gaussians
         timed("project_batch", lambda: B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
-                                                       stream, bin_keys=[b.bin_keys for b in bufs]
-                                                       if prebinned else None))
+                                                       stream, bin_keys=[(b.depth_keys, None if reach else b.tile_rects)
+                                                                         for b in bufs] if prebinned else None))
         e_sort0.record(stream)
         for st in side:
             st.wait_event(e_sort0)
@@ -455,7 +455,9 @@ def main():
     sh_b = {"f32": 12, "f16": 6, "q8": 3}["q8" if args.sh_q8 else ("f16" if sc.sh_fp16 is not None else "f32")]
     sh_bytes = sh_b * K_sh + (8.0 * 3 * K_sh / 256.0 if args.sh_q8 else 0.0)
     geo = 44 + (16 if sc.velocity is not None else 0)
-    rec_b = 48 + (12 if prebinned else 0)      # + depth key and tile rect when the projection writes them
+    # + depth key (and tile rect, unless only reached tiles are listed) when
+    # the projection writes them
+    rec_b = 48 + ((4 if reach else 12) if prebinned else 0)
     bytes_proj = sc.n * geo + (sc.n if use_mask else 0) + views * sc.n * rec_b + n_any * sh_bytes
     # the sort: what this design must move once (depth digits on the visible
     # Gaussians, then the tile digits on the K keys): per Gaussian 20 B of its
@@ -501,7 +503,8 @@ def main():
     hbm_stages = {
         "project": hbm("project_kernel (one launch, all views)", bytes_proj, med("project_batch"),
                        f"N x {geo} B parameters + {views} x N x {rec_b} B records"
-                       + (" (48 B + the sort's 12 B depth key and tile rect)" if prebinned else "") +
+                       + ((" (48 B + the sort's 4 B depth key)" if reach else
+                           " (48 B + the sort's 12 B depth key and tile rect)") if prebinned else "") +
                        f" + {sh_bytes:g} B of SH per Gaussian visible in any view" + (" + N B mask" if use_mask else "")),
         "sort": hbm("gs_bin_sort_views (all views, 4 streams: the sort phase)",
                     bytes_sort, warm["sort_phase_ms"]["median"],

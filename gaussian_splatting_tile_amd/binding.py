@@ -324,7 +324,7 @@ def bin_sort_views(bufs, with_bwd: bool = True, stream=None, prebinned=False, re
                             _ptr(b.k_total),
                             _ptr(b.ws), _nbytes(b.ws),
                             _ptr(b.depth_keys) if pre[i] else None,
-                            _ptr(b.tile_rects) if pre[i] else None, 1 if rch[i] else 0)
+                            _ptr(b.tile_rects) if pre[i] and not rch[i] else None, 1 if rch[i] else 0)
     _check(lib().gs_bin_sort_views(nv, arr, _stream(stream)), "gs_bin_sort_views")
 
 
@@ -339,8 +339,9 @@ def render_fwd(splats, vals, tile_ranges, schedule, cam: GsCamera, bg: Sequence[
 def project_views(gs: GsGaussians, cams, splats_list, stream=None, bin_keys=None):
     """gs_project_views: records for every camera of the list in one pass.
     bin_keys: None, or one (depth_keys uint32/int32 [n], tile_rects
-    uint32/int32 [2n]) pair (or None) per camera, for
-    gs_project_views_binned."""
+    uint32/int32 [2n] or None) pair (or None) per camera, for
+    gs_project_views_binned (rects may be left out for views sorted with
+    reach=True)."""
     nv = len(cams)
     cam_arr = (GsCamera * max(nv, 1))(*cams)
     sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
@@ -350,7 +351,7 @@ def project_views(gs: GsGaussians, cams, splats_list, stream=None, bin_keys=None
     bk = (GsBinKeys * max(nv, 1))()
     for i, pair in enumerate(bin_keys):
         if pair is not None:
-            bk[i] = GsBinKeys(_ptr(pair[0]), _ptr(pair[1]))
+            bk[i] = GsBinKeys(_ptr(pair[0]), None if pair[1] is None else _ptr(pair[1]))
     _check(lib().gs_project_views_binned(C.byref(gs), nv, cam_arr, sp_arr, bk, _stream(stream)),
            "gs_project_views_binned")
 

@@ -88,10 +88,12 @@ gs_status gs_project(const gs_gaussians *gaussians, const gs_camera *camera, gs_
 
 // The sort inputs of one view: both pointers or neither, depth keys 4-byte
 // and rects 8-byte aligned, and tile coordinates that fit the 16-bit fields.
-static bool bin_keys_ok(const uint32_t *dk, const uint32_t *gr, const gs_camera &cam)
+// (The rects may be left out where only reached tiles are listed: that
+// sort takes each rect from the record.)
+static bool bin_keys_ok(const uint32_t *dk, const uint32_t *gr, const gs_camera &cam, bool rects_optional)
 {
-    if ((dk == nullptr) != (gr == nullptr)) return false;
-    if (dk == nullptr) return true;
+    if (dk == nullptr) return gr == nullptr;
+    if (gr == nullptr && !rects_optional) return false;
     if (((uintptr_t)dk & 3u) != 0 || ((uintptr_t)gr & 7u) != 0) return false;
     const Cam c = make_cam(cam);
     return c.tiles_x <= 65535 && c.tiles_y <= 65535;
@@ -106,7 +108,7 @@ static gs_status project_views(const gs_gaussians *gaussians, int32_t n_views, c
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
         if ((gaussians->n > 0 && !splats[v]) || !al16(splats[v])) return GS_ERR_INVALID_ARG;
-        if (bin_keys && !bin_keys_ok(bin_keys[v].depth_keys, bin_keys[v].tile_rects, cameras[v]))
+        if (bin_keys && !bin_keys_ok(bin_keys[v].depth_keys, bin_keys[v].tile_rects, cameras[v], true))
             return GS_ERR_INVALID_ARG;
     }
     for (int v0 = 0; v0 < n_views; v0 += kMaxProjViews) {
@@ -173,7 +175,7 @@ static gs_status check_sort_view(const gs_sort_view &v)
     if (!camera_ok(&v.camera) || !v.tile_ranges || !v.schedule || !v.k_total) return GS_ERR_INVALID_ARG;
     if ((v.n > 0 && !v.splats) || !al16(v.splats) || !al16(v.workspace)) return GS_ERR_INVALID_ARG;
     if (v.k_capacity > 0 && !v.vals) return GS_ERR_INVALID_ARG;
-    if (!bin_keys_ok(v.depth_keys, v.tile_rects, v.camera)) return GS_ERR_INVALID_ARG;
+    if (!bin_keys_ok(v.depth_keys, v.tile_rects, v.camera, v.reach_tiles != 0)) return GS_ERR_INVALID_ARG;
     const Cam cam = make_cam(v.camera);
     const size_t need = bin_sort_workspace(v.n, v.k_capacity, cam.tiles_x * cam.tiles_y);
     if (v.workspace_bytes < need || !v.workspace) return GS_ERR_WORKSPACE;

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
     // read them back from the record)
     if (views.dkeys[v] != nullptr) {
         views.dkeys[v][g] = dkey;
-        views.grect[v][g] = grect;
+        if (views.grect[v] != nullptr) views.grect[v][g] = grect;
     }
     }   // views
 }

@@ -356,7 +356,7 @@ struct InitArgs {
     uint32_t n, n_ranges;
     int tiles_x, tiles_y;
     uint32_t *dkeys, *ranges, *counters;
-    uint2 *grect;
+    uint2 *grect;                // null: no rects needed (only reached tiles listed)
     int prebinned;               // depth keys and rects came from the projection
 };
 
@@ -375,10 +375,12 @@ __global__ __launch_bounds__(kBlock) void bin_init(const Batch<InitArgs> b)
         dkeys[i] = tiles ? __float_as_uint(sa.z) : kSentinel;   // the first pass takes i as the value
         // written for every Gaussian (culled ones get an unused value): a
         // full, coalesced row costs less than scattered partial lines
-        uint2 gr = make_uint2(0u, 0u);
-        if (tiles) gr = pack_rect(tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x,
-                                            (float)a.tiles_y));
-        a.grect[i] = gr;
+        if (a.grect) {
+            uint2 gr = make_uint2(0u, 0u);
+            if (tiles) gr = pack_rect(tile_rect(sa.x, sa.y, (float)__float_as_int(sa.w), (float)a.tiles_x,
+                                                (float)a.tiles_y));
+            a.grect[i] = gr;
+        }
     }
     if (i < n_ranges) ranges[i] = 0;
     if (i == 0) {
@@ -999,7 +1001,7 @@ hipError_t launch_bin_sort_views(int count, const SortJob *jobs, hipStream_t s)
             const SortJob &J = jobs[v];
             b.v[v] = InitArgs{J.splats, (uint32_t)J.n, 2u * (uint32_t)(J.cam.tiles_x * J.cam.tiles_y),
                               J.cam.tiles_x, J.cam.tiles_y, w[v].dk[0], J.ranges, w[v].counters,
-                              w[v].grect, J.dkeys != nullptr ? 1 : 0};
+                              J.reach ? nullptr : w[v].grect, J.dkeys != nullptr ? 1 : 0};
         }
         bin_init<<<dim3((init_max + kBlock - 1) / kBlock, count), kBlock, 0, s>>>(b);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -259,14 +259,16 @@ gs_status gs_project_views(const gs_gaussians *gaussians /* host struct */, int3
  *                   tile rect, first tile and extent in tiles; (0, 0) for a
  *                   Gaussian that touches no tile
  * Owned by the caller.  Both describe the records of the same call and stay
- * valid only as long as those records are unchanged. */
+ * valid only as long as those records are unchanged.  tile_rects may be NULL
+ * for a view that is sorted with reach_tiles (that sort takes each rect from
+ * the record it reads for the reach test). */
 typedef struct gs_bin_keys {
     uint32_t *depth_keys;
     uint32_t *tile_rects;
 } gs_bin_keys;
 
 /* gs_project_views that also writes, for every view i whose bin_keys[i]
- * has both pointers set, the sort inputs above (bin_keys: host array of
+ * has depth_keys set, the sort inputs above (bin_keys: host array of
  * n_views entries; an entry with NULL pointers writes records only).  The
  * records are those of gs_project_views.  Passing the arrays to
  * gs_bin_sort_views (gs_sort_view.depth_keys / tile_rects) spares the sort
@@ -274,9 +276,9 @@ typedef struct gs_bin_keys {
  * projection of the VisionTech 4DGS page, section on technical architecture
  * and key mechanisms, ahead of the tile binning of the BlitzGS page,
  * section 2.1).
- * Errors: as gs_project_views; GS_ERR_INVALID_ARG for one pointer of a
- * pair set without the other, a misaligned pointer, or a view whose tile
- * grid has more than 65535 tiles across or down. */
+ * Errors: as gs_project_views; GS_ERR_INVALID_ARG for tile_rects without
+ * depth_keys, a misaligned pointer, or a view whose tile grid has more than
+ * 65535 tiles across or down. */
 gs_status gs_project_views_binned(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
                                   const gs_camera *cameras, gs_splat *const *splats,
                                   const gs_bin_keys *bin_keys /* host */, void *stream);
@@ -341,10 +343,10 @@ typedef struct gs_sort_view {
     uint64_t *k_total;
     void *workspace;            /* its own, gs_bin_sort_workspace_bytes */
     size_t workspace_bytes;
-    /* optional, both or neither: the view's gs_bin_keys from
-     * gs_project_views_binned for these splats; the sort then takes each
-     * Gaussian's depth key and tile rect from them instead of its record
-     * (same results) */
+    /* optional: the view's gs_bin_keys from gs_project_views_binned for
+     * these splats; the sort then takes each Gaussian's depth key and tile
+     * rect from them instead of its record (same results).  tile_rects may
+     * be NULL with depth_keys set when reach_tiles is nonzero. */
     const uint32_t *depth_keys;
     const uint32_t *tile_rects;
     /* nonzero: list a Gaussian only in the tiles of its rect that it reaches,
@@ -365,8 +367,8 @@ typedef struct gs_sort_view {
  * calls.  Views may differ in size and resolution, and in whether they
  * bring gs_bin_keys.
  * Errors: as gs_bin_sort, checked for every view before anything runs;
- * GS_ERR_INVALID_ARG also for one of depth_keys / tile_rects set without
- * the other or misaligned. */
+ * GS_ERR_INVALID_ARG also for tile_rects without depth_keys, depth_keys
+ * without tile_rects in a view without reach_tiles, or either misaligned. */
 gs_status gs_bin_sort_views(int32_t n_views, const gs_sort_view *views /* host */,
                             void *stream);
 

@@ -143,6 +143,19 @@ def test_host_side_argument_errors_without_device():
     views[1].workspace_bytes = 1 << 30
     views[1].depth_keys = 0x1000
     assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    # a reach sort takes its rects from the records: view 1 passes its
+    # checks, so the call fails only at view 2's small workspace (and
+    # launches nothing)
+    views3 = (B.GsSortView * 3)(views[0], views[1], views[1])
+    views3[1].reach_tiles = 1
+    views3[2].depth_keys = None
+    views3[2].workspace_bytes = 16
+    assert L.gs_bin_sort_views(3, views3, None) == B.GS_ERR_WORKSPACE
+    views3[1].reach_tiles = 0
+    assert L.gs_bin_sort_views(3, views3, None) == B.GS_ERR_INVALID_ARG
+    views[1].depth_keys, views[1].tile_rects = None, 0x1008
+    assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
+    views[1].depth_keys = 0x1000
     views[1].tile_rects = 0x1004
     assert L.gs_bin_sort_views(2, views, None) == B.GS_ERR_INVALID_ARG
     views[1].depth_keys, views[1].tile_rects = 0x1002, 0x1008
@@ -156,8 +169,11 @@ def test_host_side_argument_errors_without_device():
     bk = (B.GsBinKeys * 1)()
     assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, None, None) == B.GS_ERR_INVALID_ARG
     assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_OK   # n = 0: nothing runs
-    bk[0].depth_keys = 0x1000
+    bk[0].depth_keys = 0x1000                  # depth keys alone are allowed
+    assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_OK
+    bk[0].depth_keys, bk[0].tile_rects = None, 0x1008
     assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_ERR_INVALID_ARG
+    bk[0].depth_keys = 0x1000
     bk[0].tile_rects = 0x100C
     assert L.gs_project_views_binned(C.byref(gb), 1, C.byref(camb), spb, bk, None) == B.GS_ERR_INVALID_ARG
     bk[0].tile_rects = 0x1008

@@ -362,7 +362,9 @@ def test_reach_binning_matches_oracle_and_leaves_results_unchanged():
     gs = B.gaussians_struct(g, sc.sh_degree)
     bufs = [B.ViewBuffers(sc.n, sc.cameras[v], full[v][1], with_keys=True) for v in range(3)]
     say("[gpu] reach binning: batched projection + sort with reach_tiles")
-    B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs], bin_keys=[b.bin_keys for b in bufs])
+    # view 0's projection writes depth keys only (a reach sort needs no rects)
+    B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
+                    bin_keys=[(b.depth_keys, None) if v == 0 else b.bin_keys for v, b in enumerate(bufs)])
     B.bin_sort_views(bufs, True, prebinned=[True, False, True], reach=True)
     torch.cuda.synchronize()
     for v, b in enumerate(bufs):
