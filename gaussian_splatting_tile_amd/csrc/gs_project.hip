@@ -314,13 +314,13 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
         tg = mo.t[g];
     }
     // with motion the mean's finiteness is that of each view's displaced mean
-    const bool on = (active == nullptr || active[g] != 0) &&
-                    all_finite(kMotion ? 0.0f : mx, kMotion ? 0.0f : my, kMotion ? 0.0f : mz, sx, sy, sz, qw, qx,
-                               qy, qz, o);
+    const bool act = active == nullptr || active[g] != 0;
+    const bool on = act && all_finite(kMotion ? 0.0f : mx, kMotion ? 0.0f : my, kMotion ? 0.0f : mz, sx, sy, sz,
+                                      qw, qx, qy, qz, o);
 
     // the views of the batch, parameters and SH coefficients read once (all
     // lanes load, g < n; a masked-out Gaussian's coefficients go unused, and
-    // predicated loads would each wait for the previous one)
+    // with a random mask nearly every line of a row holds a kept Gaussian)
     float shc[3 * K];
     static_assert(kBlock == 256, "a projection workgroup is one 256-Gaussian SH block");
 #pragma unroll
@@ -389,7 +389,11 @@ __global__ __launch_bounds__(kBlock) void project_kernel(
             grect = pack_rect(r);
         }
     }
-    out[g] = rec;
+    // With the sort's keys requested, the record of a Gaussian outside the
+    // importance mask is not written: the sort takes visibility from the
+    // depth key, the blend reads listed Gaussians only and the projection
+    // backward skips Gaussians outside the mask.
+    if (act || views.dkeys[v] == nullptr) out[g] = rec;
     // the sort's inputs from the same values (the binning would otherwise
     // read them back from the record)
     if (views.dkeys[v] != nullptr) {

@@ -270,7 +270,12 @@ typedef struct gs_bin_keys {
 /* gs_project_views that also writes, for every view i whose bin_keys[i]
  * has depth_keys set, the sort inputs above (bin_keys: host array of
  * n_views entries; an entry with NULL pointers writes records only).  The
- * records are those of gs_project_views.  Passing the arrays to
+ * records are those of gs_project_views, except that in a view with
+ * depth_keys the records of Gaussians outside the importance mask
+ * (gs_gaussians.active) are left unwritten: gs_bin_sort_views given the
+ * depth keys reads no record of an unlisted Gaussian, the blend reads listed
+ * Gaussians only and gs_project_bwd skips Gaussians outside the mask (such
+ * records must not be handed to gs_bin_sort without the depth keys).  Passing the arrays to
  * gs_bin_sort_views (gs_sort_view.depth_keys / tile_rects) spares the sort
  * its read of every record: one pass over the Gaussians produces both (the
  * projection of the VisionTech 4DGS page, section on technical architecture

@@ -426,6 +426,66 @@ def test_reach_binning_matches_oracle_and_leaves_results_unchanged():
         assert torch.equal(g2r[v][vis], g2f[v][vis]), f"view {v}: screen-space sums"
 
 
+def test_binned_projection_under_a_mask_leaves_inactive_records_unwritten():
+    """With an importance mask, gs_project_views_binned writes no record of a
+    Gaussian outside the mask (the sort takes visibility from the depth keys)
+    and every other record as the plain projection does; the prebinned reach
+    sort, the blend and the backward over those records equal the plain
+    path's bit for bit."""
+    sc = scenes.scene_like(seed=53, n=30_000, width=480, height=272, f=350.0, n_views=2, upstream=True)
+    active = (np.random.default_rng(54).random(sc.n) < 0.4).astype(np.uint8)
+    g = device_gaussians(sc)
+    act = torch.from_numpy(active).cuda()
+    gs = B.gaussians_struct(g, sc.sh_degree, act)
+    say("[gpu] masked binned projection: plain references, 2 views")
+    ref = []
+    for v in range(2):
+        buf, K = run_view(sc, v, active=active)
+        ref.append(buf)
+    bufs = [B.ViewBuffers(sc.n, sc.cameras[v], ref[v].k_capacity, with_keys=True) for v in range(2)]
+    for b in bufs:
+        b.splats.fill_(-1.0)
+    say("[gpu] masked binned projection: binned path")
+    B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
+                    bin_keys=[(b.depth_keys, None) for b in bufs])
+    plain = [torch.empty_like(b.splats) for b in bufs]
+    B.project_views(gs, [b.camc for b in bufs], plain)
+    torch.cuda.synchronize()
+    inactive = torch.from_numpy(active == 0).cuda()
+    for b, p in zip(bufs, plain):
+        assert bool((b.splats[inactive] == -1.0).all())
+        assert torch.equal(b.splats[~inactive].view(torch.int32), p[~inactive].view(torch.int32))
+    # reach sorts of the plain records as the reference lists
+    for r, p in zip(ref, plain):
+        r.splats.copy_(p)
+    B.bin_sort_views(ref, True, reach=True)
+    B.bin_sort_views(bufs, True, prebinned=True, reach=True)
+    B.render_fwd_views(ref, (0.0, 0.0, 0.0))
+    B.render_fwd_views(bufs, (0.0, 0.0, 0.0))
+    torch.cuda.synchronize()
+    for r, b in zip(ref, bufs):
+        K = int(r.k_total.item())
+        assert int(b.k_total.item()) == K and torch.equal(r.vals[:K], b.vals[:K]) and torch.equal(r.ranges, b.ranges)
+        assert torch.equal(r.image, b.image) and torch.equal(r.final_T, b.final_T)
+        assert torch.equal(r.n_contrib, b.n_contrib)
+    say("[gpu] masked binned projection: backward")
+    dLs = [torch.from_numpy(np.ascontiguousarray(sc.upstream(v))).cuda() for v in range(2)]
+    out = []
+    for set_ in (ref, bufs):
+        g2s = [torch.empty((sc.n, 9), device="cuda") for _ in range(2)]
+        wss = [torch.empty(B.render_bwd_screen_workspace_bytes(b.k_capacity), dtype=torch.uint8, device="cuda")
+               for b in set_]
+        B.render_bwd_screen_views(set_, dLs, g2s, wss)
+        grads = dict(means=torch.zeros((3, sc.n), device="cuda"), log_scales=torch.zeros((3, sc.n), device="cuda"),
+                     quats=torch.zeros((4, sc.n), device="cuda"), opacity_logits=torch.zeros(sc.n, device="cuda"),
+                     sh=torch.zeros((sc.sh.shape[0], 3, sc.n), device="cuda"))
+        B.project_bwd(gs, [b.camc for b in set_], [b.splats for b in set_], g2s, grads)
+        torch.cuda.synchronize()
+        out.append(grads)
+    for k in out[0]:
+        assert torch.equal(out[0][k], out[1][k]), k
+
+
 def _ambiguous_gaussians(ob, oo, cam):
     """Gaussians listed in a tile that holds a pixel with a near-threshold
     decision (or an alpha near the cap): their weights may legitimately
