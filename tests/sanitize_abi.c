@@ -75,6 +75,18 @@ int main(void)
     gs_splat *const splat_list[2] = {(gs_splat *)dev, NULL};
     EXPECT(gs_project_views(&g, 2, (const gs_camera[]){cam, cam}, splat_list, NULL), GS_ERR_INVALID_ARG);
     EXPECT(gs_project_views(&g, -1, NULL, NULL, NULL), GS_ERR_INVALID_ARG);
+    gs_bin_keys bk[2];
+    memset(bk, 0, sizeof bk);
+    gs_splat *const splat_ok[2] = {(gs_splat *)dev, (gs_splat *)dev};
+    EXPECT(gs_project_views_binned(&g, 2, (const gs_camera[]){cam, cam}, splat_ok, NULL, NULL), GS_ERR_INVALID_ARG);
+    bk[1].tile_rects = (uint32_t *)dev;                                              /* rects without keys */
+    EXPECT(gs_project_views_binned(&g, 2, (const gs_camera[]){cam, cam}, splat_ok, bk, NULL), GS_ERR_INVALID_ARG);
+    bk[1].depth_keys = (uint32_t *)0x1002;                                           /* misaligned keys */
+    EXPECT(gs_project_views_binned(&g, 2, (const gs_camera[]){cam, cam}, splat_ok, bk, NULL), GS_ERR_INVALID_ARG);
+    bk[1].depth_keys = (uint32_t *)dev;
+    bk[1].tile_rects = (uint32_t *)0x1004;                                           /* misaligned rects */
+    EXPECT(gs_project_views_binned(&g, 2, (const gs_camera[]){cam, cam}, splat_ok, bk, NULL), GS_ERR_INVALID_ARG);
+    EXPECT(gs_project_views_binned(&g, 2, (const gs_camera[]){cam, bad}, splat_ok, bk, NULL), GS_ERR_INVALID_ARG);
     gs_gaussians g0 = g;
     g0.n = 0;
     EXPECT(gs_project(&g0, &cam, NULL, NULL), GS_OK);                                /* nothing to do */
@@ -93,6 +105,14 @@ int main(void)
     EXPECT(gs_bin_sort_views(2, NULL, NULL), GS_ERR_INVALID_ARG);
     EXPECT(gs_bin_sort_views(2, sv, NULL), GS_ERR_INVALID_ARG);
     EXPECT(gs_bin_sort_views(0, NULL, NULL), GS_OK);
+    sv[0].camera = cam;                                                              /* keys without rects, no reach */
+    sv[0].tile_ranges = sv[0].schedule = u32;
+    sv[0].k_total = u64;
+    sv[0].workspace = dev;
+    sv[0].workspace_bytes = (size_t)1 << 30;
+    sv[0].depth_keys = u32;
+    EXPECT(gs_bin_sort_views(1, sv, NULL), GS_ERR_INVALID_ARG);
+    sv[0].depth_keys = NULL;
 
     const float bg[3] = {0.0f, 0.0f, 0.0f};
     const float bgnan[3] = {0.0f, NAN, 0.0f};
