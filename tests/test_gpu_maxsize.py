@@ -87,3 +87,41 @@ def test_maximum_image_size():
     assert (rn > 0).sum() > 1000                      # the samples do cover the Gaussians
     say(f"[gpu] max image: {int(bad.sum())} near-threshold pixels resolved, max err "
         f"{float(np.abs(img - rgb).max(axis=0)[~bad].max()):.2e}")
+
+
+def test_reached_tile_lists_with_32_bit_tile_keys():
+    """Reached-tile lists where tile ids need 32-bit keys: an 8192 x 8192 view
+    (262144 tiles, 18 tile bits, three tile passes) of the same Gaussians.
+    Bins against the oracle's reach binning (a pair may differ only within
+    1e-5 of the reach bound, and then the bins must be bit-exact), the image
+    and final T equal to the full lists' bit for bit."""
+    import dataclasses
+    from gaussian_splatting_tile_amd import binding as B
+    sc = _scene()
+    sc.cameras[0] = dataclasses.replace(sc.cameras[0], width=8192, height=8192, cx=7600.0, cy=7600.0)
+    cam = sc.cameras[0]
+    assert cam.tiles_x * cam.tiles_y > 65536
+    say("[gpu] 8192 x 8192 view: full lists, then reached-tile lists")
+    full, K = run_view(sc, 0)
+    rb = B.ViewBuffers(sc.n, cam, K, with_keys=True)
+    rb.splats.copy_(full.splats)
+    B.bin_sort_views([rb], True, reach=True)
+    B.render_fwd_views([rb], (0.0, 0.0, 0.0))
+    torch.cuda.synchronize()
+    op = oracle.project(sc.means, sc.scales, sc.quats, sc.opacities, 3, sc.sh, cam)
+    ob = oracle.bin_sort(op, cam, reach=True)
+    Kr = int(rb.k_total.item())
+    assert 0 < Kr < K
+    thr = (1.0 / 255.0) * (1.0 - 1e-3)
+    vals = rb.vals[:Kr].cpu().numpy().view(np.uint32)
+    ranges = rb.ranges.cpu().numpy().view(np.uint32).reshape(-1, 2)
+    got = {(t, int(g)) for t in np.nonzero(ranges[:, 1] > ranges[:, 0])[0] for g in vals[ranges[t, 0]:ranges[t, 1]]}
+    ranges_o = ob["ranges"].reshape(-1, 2)
+    want = {(t, int(g)) for t in np.nonzero(ranges_o[:, 1] > ranges_o[:, 0])[0]
+            for g in ob["vals"][ranges_o[t, 0]:ranges_o[t, 1]]}
+    for t, g in got ^ want:
+        assert abs(oracle.tile_reach(op, g, t, cam) / thr - 1.0) < 1e-5, (t, g)
+    if got == want:
+        assert Kr == ob["K"] and np.array_equal(vals, ob["vals"]) and np.array_equal(ranges, ranges_o)
+        assert np.array_equal(rb.keys[:Kr].cpu().numpy().view(np.uint64), ob["keys"])
+    assert torch.equal(rb.image, full.image) and torch.equal(rb.final_T, full.final_T)
