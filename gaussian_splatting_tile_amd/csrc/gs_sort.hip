@@ -11,13 +11,16 @@
 //   1. depth passes: stable 4 x 8-bit LSB sort of (depth bits, g) over the
 //      visible Gaussians (culled ones drop out in the first pass);
 //   2. duplication in that order: an exclusive scan of tiles_touched gives
-//      each Gaussian its slots, where it writes (tile, g) for its rect;
+//      each Gaussian its slots, where it writes (tile, g) for its rect (or,
+//      with reach lists, for the tiles of its rect it can reach with
+//      alpha >= 1/255: counted in the scan, the rest never emitted);
 //   3. tile passes: stable LSB passes of <= 8 bits over the tile id (the high
 //      digits of the key) on the K entries;
 //   4. tile ranges from the boundaries of the sorted tile ids.
 // Duplication keeps the relative order of the Gaussians, so this is the same
 // permutation as sorting all K 64-bit keys, with the depth digits moved
-// before the duplication.
+// before the duplication.  The depth keys and tile rects come from the
+// projection when it wrote them, else from the records (bin_init).
 //
 // No host round trip: item counts (visible Gaussians, K) stay in device
 // memory; every grid is sized from host-known upper bounds and blocks past
