@@ -356,7 +356,9 @@ def main():
             timed("render_bwd_batch", lambda: B.render_bwd_screen_views(
                 bufs, [b.dL for b in bufs], [b.g2 for b in bufs], [b.bwd_ws for b in bufs], bg, stream))
             timed("project_bwd_batch", lambda: B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs],
-                                                             [b.g2 for b in bufs], grads, stream))
+                                                             [b.g2 for b in bufs], grads, stream,
+                                                             depth_keys=[b.depth_keys for b in bufs]
+                                                             if prebinned else None))
             if adam is not None:
                 adam["t"] += 1
                 timed("sh_adam", lambda: B.sh_adam_step(grads["sh"][1:], adam["val"], adam["m"], adam["v"],
@@ -505,6 +507,8 @@ def main():
     # does not move: reported beside it
     bytes_sort_lsb64 = sum(8 * sc.n + 20 * sc.n + 12 * k + (8 + 6 * 24) * k + 8 * k for k in Ks)
     bytes_pbwd = n_any * (geo + sh_bytes) + sum(nv * (48 + 36) for nv in n_vis) + n_any * 2 * (geo + 12 * K_sh)
+    if prebinned:
+        bytes_pbwd += views * sc.n * 4     # the depth keys (visibility of every Gaussian in every view)
 
     def hbm(name, nbytes, ms, model):
         if ms is None:
@@ -533,7 +537,8 @@ def main():
                             bytes_pbwd, med("project_bwd_batch"),
                             f"per Gaussian visible in any view {geo} B + {sh_bytes:g} B parameters read and "
                             f"2 x ({geo} + {12 * K_sh}) B gradients read and written; per view and visible "
-                            f"Gaussian 48 B record + 36 B screen-space sums") if do_bwd else None),
+                            f"Gaussian 48 B record + 36 B screen-space sums"
+                            + (f"; per view N x 4 B depth keys (visibility)" if prebinned else "")) if do_bwd else None),
     }
 
     cam0 = sc.cameras[0]

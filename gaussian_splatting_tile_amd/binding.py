@@ -87,7 +87,7 @@ SYMBOLS = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_schedule_words", "gs
            "gs_render_fwd_views", "gs_render_bwd_screen_views", "gs_project_views", "gs_project_views_binned",
            "gs_render_fwd",
            "gs_render_bwd_workspace_bytes", "gs_render_bwd", "gs_render_bwd_screen_workspace_bytes",
-           "gs_render_bwd_screen", "gs_project_bwd", "gs_active_mask_workspace_bytes",
+           "gs_render_bwd_screen", "gs_project_bwd", "gs_project_bwd_binned", "gs_active_mask_workspace_bytes",
            "gs_active_mask", "gs_active_mask_static", "gs_active_mask_static_scratch_bytes",
            "gs_sh_q8_bounds_floats", "gs_sh_quantize8", "gs_sh_adam_step", "gs_status_string",
            "gs_version")
@@ -134,6 +134,8 @@ def lib():
                                        vp, sz, vp]
     L.gs_project_bwd.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp),
                                  C.POINTER(vp), C.POINTER(GsGrads), vp]
+    L.gs_project_bwd_binned.argtypes = [C.POINTER(GsGaussians), C.c_int32, C.POINTER(GsCamera), C.POINTER(vp),
+                                        C.POINTER(vp), C.POINTER(vp), C.POINTER(GsGrads), vp]
     L.gs_active_mask_workspace_bytes.argtypes = [i64]
     L.gs_active_mask_workspace_bytes.restype = sz
     L.gs_active_mask.argtypes = [vp, i64, i64, vp, vp, sz, vp]
@@ -151,7 +153,8 @@ def lib():
                  "gs_render_fwd_views",
                  "gs_render_bwd",
                  "gs_render_bwd_screen", "gs_render_bwd_screen_views",
-                 "gs_project_bwd", "gs_active_mask", "gs_active_mask_static", "gs_sh_quantize8"):
+                 "gs_project_bwd", "gs_project_bwd_binned", "gs_active_mask", "gs_active_mask_static",
+                 "gs_sh_quantize8"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -415,16 +418,26 @@ def render_bwd_screen_views(bufs, dLs, g2s, workspaces, bg: Sequence[float] = (0
            "gs_render_bwd_screen_views")
 
 
-def project_bwd(gs: GsGaussians, cams, splats_list, g2_list, grads: Dict[str, torch.Tensor], stream=None):
+def project_bwd(gs: GsGaussians, cams, splats_list, g2_list, grads: Dict[str, torch.Tensor], stream=None,
+                depth_keys=None):
     """Chain rule of a batch of views: cams is a list of GsCamera, splats_list
-    and g2_list the matching device tensors."""
+    and g2_list the matching device tensors.  depth_keys (a list of the views'
+    depth-key tensors from project_views(bin_keys=...), None entries allowed)
+    selects gs_project_bwd_binned, which takes visibility from the keys."""
     nv = len(cams)
     cam_arr = (GsCamera * max(nv, 1))(*cams)
     sp_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in splats_list])
     g2_arr = (C.c_void_p * max(nv, 1))(*[_ptr(t) for t in g2_list])
     gr = grads_struct(grads)
-    _check(lib().gs_project_bwd(C.byref(gs), nv, cam_arr, sp_arr, g2_arr, C.byref(gr), _stream(stream)),
-           "gs_project_bwd")
+    if depth_keys is None:
+        _check(lib().gs_project_bwd(C.byref(gs), nv, cam_arr, sp_arr, g2_arr, C.byref(gr), _stream(stream)),
+               "gs_project_bwd")
+        return
+    if len(depth_keys) != nv:
+        raise ValueError("project_bwd: one depth-key tensor (or None) per view")
+    dk_arr = (C.c_void_p * max(nv, 1))(*[None if t is None else _ptr(t) for t in depth_keys])
+    _check(lib().gs_project_bwd_binned(C.byref(gs), nv, cam_arr, sp_arr, g2_arr, dk_arr, C.byref(gr),
+                                       _stream(stream)), "gs_project_bwd_binned")
 
 
 def active_mask_workspace_bytes(n: int) -> int:

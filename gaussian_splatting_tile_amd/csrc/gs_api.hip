@@ -438,6 +438,7 @@ gs_status gs_render_bwd(const gs_gaussians *gaussians, const gs_camera *camera, 
     vb.cam[0] = make_cam(*camera);
     vb.splats[0] = (const Splat *)splats;
     vb.g2[0] = g2;
+    vb.dkeys[0] = nullptr;
     return from_hip(launch_project_bwd(*gaussians, vb, *grads, s));
 }
 
@@ -500,8 +501,10 @@ gs_status gs_render_bwd_screen_views(int32_t n_views, const gs_bwd_view *views, 
     return GS_OK;
 }
 
-gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
-                         const gs_splat *const *splats, const float *const *g2, const gs_grads *grads, void *stream)
+namespace {
+gs_status project_bwd(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                      const gs_splat *const *splats, const float *const *g2, const uint32_t *const *depth_keys,
+                      const gs_grads *grads, void *stream)
 {
     gs_status st = gaussians_ok(gaussians);
     if (st != GS_OK) return st;
@@ -511,6 +514,7 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const g
     for (int v = 0; v < n_views; v++) {
         if (!camera_ok(&cameras[v])) return GS_ERR_INVALID_ARG;
         if ((n > 0 && (!splats[v] || !g2[v])) || !al16(splats[v])) return GS_ERR_INVALID_ARG;
+        if (depth_keys && ((uintptr_t)depth_keys[v] & 3u) != 0) return GS_ERR_INVALID_ARG;
     }
     if (n == 0) return GS_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -522,11 +526,27 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const g
             vb.cam[i] = make_cam(cameras[v0 + i]);
             vb.splats[i] = (const Splat *)splats[v0 + i];
             vb.g2[i] = g2[v0 + i];
+            vb.dkeys[i] = depth_keys ? depth_keys[v0 + i] : nullptr;
         }
         hipError_t e = launch_project_bwd(*gaussians, vb, *grads, s);
         if (e != hipSuccess) return GS_ERR_HIP;
     }
     return GS_OK;
+}
+}  // namespace
+
+gs_status gs_project_bwd(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                         const gs_splat *const *splats, const float *const *g2, const gs_grads *grads, void *stream)
+{
+    return project_bwd(gaussians, n_views, cameras, splats, g2, nullptr, grads, stream);
+}
+
+gs_status gs_project_bwd_binned(const gs_gaussians *gaussians, int32_t n_views, const gs_camera *cameras,
+                                const gs_splat *const *splats, const float *const *g2,
+                                const uint32_t *const *depth_keys, const gs_grads *grads, void *stream)
+{
+    if (n_views > 0 && !depth_keys) return GS_ERR_INVALID_ARG;
+    return project_bwd(gaussians, n_views, cameras, splats, g2, depth_keys, grads, stream);
 }
 
 size_t gs_active_mask_workspace_bytes(int64_t n)

@@ -195,6 +195,7 @@ struct ViewBatch {
     Cam cam[kMaxViews];
     const Splat *splats[kMaxViews];
     const float *g2[kMaxViews];
+    const uint32_t *dkeys[kMaxViews];   // optional: the projection's depth keys (visibility)
 };
 hipError_t launch_project_bwd(const gs_gaussians &g, const ViewBatch &views, const gs_grads &out,
                               hipStream_t s);

@@ -559,6 +559,16 @@ constexpr int kColourPerWave = 21;
 // a full one, so each wave first compacts its range (64 per ballot) into a
 // per-wave list in LDS and then works through the list densely.
 constexpr int kMaxCompact = 1024;             // Gaussians per wave range, at most
+
+// Was Gaussian g visible in view v?  From the view's depth keys when the
+// projection wrote them (4 bytes per Gaussian, not a sentinel), else from
+// the record's radius (non-zero): the projection sets both together, so the
+// two agree.  The keys spare the colour part a read of every record line.
+__device__ __forceinline__ bool seen(const ViewBatch &views, int v, long long g)
+{
+    const uint32_t *k = views.dkeys[v];
+    return k != nullptr ? k[g] != kSentinel : __float_as_int(views.splats[v][g].a.w) != 0;
+}
 __device__ __forceinline__ int compact_range(long long g_begin, long long g_end, const uint8_t *__restrict__ active,
                                              const ViewBatch &views, uint32_t *list)
 {
@@ -570,7 +580,7 @@ __device__ __forceinline__ int compact_range(long long g_begin, long long g_end,
         bool keep = g < g_end && (active == nullptr || active[g] != 0);
         if (keep) {
             bool any = false;
-            for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+            for (int v = 0; v < views.count; v++) any = any | seen(views, v, g);
             keep = any;
         }
         const uint64_t m = __ballot(keep);
@@ -623,23 +633,23 @@ __device__ __forceinline__ void colour_backward(int n_, int g, bool valid, int c
     float dmv[3] = {0.0f, 0.0f, 0.0f};          // sum over views of dt dL/dmu'
 
     bool visible = false;
-    // the next view's radius and gradient are loaded one view ahead (a
+    // the next view's visibility and gradient are loaded one view ahead (a
     // culled Gaussian's gradient row holds no value and is not used)
-    int rad_next = 0;
+    bool seen_next = false;
     float gr_next = 0.0f;
     if (valid && views.count > 0) {
-        rad_next = __float_as_int(views.splats[0][g].a.w);
+        seen_next = seen(views, 0, g);
         gr_next = views.g2[0][(size_t)g * 9 + 6 + ch];
     }
     for (int v = 0; v < views.count; v++) {
-        const int rad = rad_next;
+        const bool in_view = seen_next;
         const float gr = gr_next;
         if (valid && v + 1 < views.count) {
-            rad_next = __float_as_int(views.splats[v + 1][g].a.w);
+            seen_next = seen(views, v + 1, g);
             gr_next = views.g2[v + 1][(size_t)g * 9 + 6 + ch];
         }
-        // culled Gaussians have radius 0 and receive nothing
-        if (!valid || rad == 0) continue;
+        // culled Gaussians receive nothing
+        if (!valid || !in_view) continue;
         visible = true;
         const Cam &cam = views.cam[v];
         float px = mx, py = my, pz = mz, dtv = 0.0f;
@@ -739,7 +749,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_color_kernel(int n, int pe
         // culled in every view of the batch: leave the SH rows untouched
         if (valid) {
             bool any = false;
-            for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][gg].a.w) != 0);
+            for (int v = 0; v < views.count; v++) any = any | seen(views, v, gg);
             valid = any;
         }
         colour_backward<DEG, TSH, kMotion>(n, valid ? (int)gg : 0, valid, ch, means, sh, sh_bounds, mo, views,
@@ -974,7 +984,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_geom_kernel(
         const long long g = (long long)blockIdx.x * kBlock + threadIdx.x;
         if (g >= n || (active != nullptr && active[g] == 0)) return;
         bool any = false;   // culled in every view: nothing to read or write
-        for (int v = 0; v < views.count; v++) any = any | (__float_as_int(views.splats[v][g].a.w) != 0);
+        for (int v = 0; v < views.count; v++) any = any | seen(views, v, g);
         if (!any) return;
         geom_backward<kMotion>(n, (int)g, means, scales, quats, opac, mo, views, d_means, d_log_scales, d_quats,
                                d_logits);

@@ -530,6 +530,23 @@ gs_status gs_project_bwd(const gs_gaussians *gaussians /* host struct */, int32_
                          const float *const *g2, const gs_grads *grads /* host struct */,
                          void *stream);
 
+/* gs_project_bwd for views projected by gs_project_views_binned: the same
+ * gradients, with each view's visibility taken from the depth keys that call
+ * wrote (a key other than 0xFFFFFFFF: visible) instead of from the record's
+ * radius, so the colour part reads 4 bytes per Gaussian and view in place of
+ * a line of records (the projection backward of the VisionTech 4DGS page,
+ * section on technical architecture and key mechanisms).
+ *   depth_keys  host array of n_views device pointers (4-byte aligned), each
+ *               the gs_bin_keys.depth_keys of the same view and records, or
+ *               NULL for a view whose visibility is read from its records
+ * Errors: as gs_project_bwd; GS_ERR_INVALID_ARG for a NULL depth_keys array
+ * (with n_views > 0) or a misaligned key pointer.  Keys that do not belong to
+ * the records give unspecified gradients. */
+gs_status gs_project_bwd_binned(const gs_gaussians *gaussians /* host struct */, int32_t n_views,
+                                const gs_camera *cameras, const gs_splat *const *splats,
+                                const float *const *g2, const uint32_t *const *depth_keys,
+                                const gs_grads *grads /* host struct */, void *stream);
+
 /* Workspace for gs_active_mask, in bytes. */
 size_t gs_active_mask_workspace_bytes(int64_t n);
 

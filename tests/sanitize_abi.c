@@ -141,6 +141,9 @@ int main(void)
     const float *const g2[1] = {f32};
     EXPECT(gs_project_bwd(&g, 1, &cam, sp, g2, &gr, NULL), GS_ERR_INVALID_ARG);
     EXPECT(gs_project_bwd(&g, -3, &cam, sp, g2, &gr, NULL), GS_ERR_INVALID_ARG);
+    const uint32_t *const dk_odd[1] = {(const uint32_t *)((char *)dev + 2)};
+    EXPECT(gs_project_bwd_binned(&g, 1, &cam, sp, g2, NULL, &gr, NULL), GS_ERR_INVALID_ARG);
+    EXPECT(gs_project_bwd_binned(&g, 1, &cam, sp, g2, dk_odd, &gr, NULL), GS_ERR_INVALID_ARG);
 
     EXPECT(gs_active_mask((const float *)dev, 10, 11, (uint8_t *)dev, dev, 1 << 20, NULL), GS_ERR_INVALID_ARG);
     EXPECT(gs_active_mask((const float *)dev, 1000, 10, (uint8_t *)dev, dev, 4, NULL), GS_ERR_WORKSPACE);

@@ -122,6 +122,18 @@ def test_host_side_argument_errors_without_device():
     grm = B.GsGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, None)
     sp = (C.c_void_p * 1)(0x1000)
     assert L.gs_project_bwd(C.byref(gm), 1, C.byref(camq), sp, sp, C.byref(grm), None) == B.GS_ERR_INVALID_ARG
+    # the keyed projection backward: the key array is required, each key
+    # pointer 4-byte aligned (checked before anything is launched)
+    gk = B.GsGaussians()
+    gk.n, gk.sh_degree, gk.sh_dtype = 5, 0, B.GS_SH_F32
+    gk.means = gk.scales = gk.quats = gk.opacities = gk.sh = 0x1000
+    grk = B.GsGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, None)
+    keys = (C.c_void_p * 1)(0x1002)
+    assert L.gs_project_bwd_binned(C.byref(gk), 1, C.byref(camq), sp, sp, None, C.byref(grk),
+                                   None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_project_bwd_binned(C.byref(gk), 1, C.byref(camq), sp, sp, keys, C.byref(grk),
+                                   None) == B.GS_ERR_INVALID_ARG
+    assert L.gs_project_bwd_binned(C.byref(gk), 0, None, None, None, None, C.byref(grk), None) == B.GS_OK
     # batched sort: every view is checked before anything runs
     views = (B.GsSortView * 2)()
     assert L.gs_bin_sort_views(-1, views, None) == B.GS_ERR_INVALID_ARG

@@ -468,22 +468,55 @@ def test_binned_projection_under_a_mask_leaves_inactive_records_unwritten():
         assert int(b.k_total.item()) == K and torch.equal(r.vals[:K], b.vals[:K]) and torch.equal(r.ranges, b.ranges)
         assert torch.equal(r.image, b.image) and torch.equal(r.final_T, b.final_T)
         assert torch.equal(r.n_contrib, b.n_contrib)
-    say("[gpu] masked binned projection: backward")
+    say("[gpu] masked binned projection: backward (records, then the depth keys for visibility)")
     dLs = [torch.from_numpy(np.ascontiguousarray(sc.upstream(v))).cuda() for v in range(2)]
     out = []
-    for set_ in (ref, bufs):
-        g2s = [torch.empty((sc.n, 9), device="cuda") for _ in range(2)]
-        wss = [torch.empty(B.render_bwd_screen_workspace_bytes(b.k_capacity), dtype=torch.uint8, device="cuda")
-               for b in set_]
-        B.render_bwd_screen_views(set_, dLs, g2s, wss)
-        grads = dict(means=torch.zeros((3, sc.n), device="cuda"), log_scales=torch.zeros((3, sc.n), device="cuda"),
-                     quats=torch.zeros((4, sc.n), device="cuda"), opacity_logits=torch.zeros(sc.n, device="cuda"),
-                     sh=torch.zeros((sc.sh.shape[0], 3, sc.n), device="cuda"))
-        B.project_bwd(gs, [b.camc for b in set_], [b.splats for b in set_], g2s, grads)
-        torch.cuda.synchronize()
-        out.append(grads)
-    for k in out[0]:
-        assert torch.equal(out[0][k], out[1][k]), k
+    for set_, keys in ((ref, None), (bufs, None), (bufs, [b.depth_keys for b in bufs]),
+                       (bufs, [bufs[0].depth_keys, None])):
+        out.append(_screen_and_projection_backward(sc, gs, set_, dLs, keys))
+    for o in out[1:]:
+        for k in out[0]:
+            assert torch.equal(out[0][k], o[k]), k
+
+
+def _screen_and_projection_backward(sc, gs, bufs, dLs, depth_keys):
+    g2s = [torch.empty((sc.n, 9), device="cuda") for _ in bufs]
+    wss = [torch.empty(B.render_bwd_screen_workspace_bytes(b.k_capacity), dtype=torch.uint8, device="cuda")
+           for b in bufs]
+    B.render_bwd_screen_views(bufs, dLs, g2s, wss)
+    grads = dict(means=torch.zeros((3, sc.n), device="cuda"), log_scales=torch.zeros((3, sc.n), device="cuda"),
+                 quats=torch.zeros((4, sc.n), device="cuda"), opacity_logits=torch.zeros(sc.n, device="cuda"),
+                 sh=torch.zeros((sc.sh.shape[0], 3, sc.n), device="cuda"))
+    B.project_bwd(gs, [b.camc for b in bufs], [b.splats for b in bufs], g2s, grads, depth_keys=depth_keys)
+    torch.cuda.synchronize()
+    return grads
+
+
+def test_projection_backward_with_depth_key_visibility_equals_record_visibility():
+    """gs_project_bwd_binned, which reads each view's visibility from the
+    projection's depth keys, gives the gradients of gs_project_bwd (radius
+    from the records) bit for bit: all views keyed, and one view keyed with
+    the other read from its records."""
+    sc = scenes.scene_like(seed=57, n=30_000, width=480, height=272, f=350.0, n_views=3, upstream=True)
+    g = device_gaussians(sc)
+    gs = B.gaussians_struct(g, sc.sh_degree)
+    say("[gpu] projection backward with depth-key visibility, 3 views")
+    probe = [run_view(sc, v)[0] for v in range(3)]
+    bufs = [B.ViewBuffers(sc.n, sc.cameras[v], probe[v].k_capacity, with_keys=True) for v in range(3)]
+    B.project_views(gs, [b.camc for b in bufs], [b.splats for b in bufs],
+                    bin_keys=[(b.depth_keys, None) for b in bufs])
+    B.bin_sort_views(bufs, True, prebinned=True, reach=True)
+    B.render_fwd_views(bufs, (0.0, 0.0, 0.0))
+    torch.cuda.synchronize()
+    for b in bufs:
+        seen = b.depth_keys[: sc.n] != -1
+        assert torch.equal(seen, b.splats[:, 3].view(torch.int32) != 0)
+    dLs = [torch.from_numpy(np.ascontiguousarray(sc.upstream(v))).cuda() for v in range(3)]
+    out = [_screen_and_projection_backward(sc, gs, bufs, dLs, keys)
+           for keys in (None, [b.depth_keys for b in bufs], [None, bufs[1].depth_keys, None])]
+    for o in out[1:]:
+        for k in out[0]:
+            assert torch.equal(out[0][k], o[k]), k
 
 
 def _ambiguous_gaussians(ob, oo, cam):
