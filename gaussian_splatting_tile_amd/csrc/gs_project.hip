@@ -49,6 +49,34 @@ __device__ __forceinline__ float rmax(float a, float b) { return fmaxf(a, b); }
 __device__ __forceinline__ double rmin(double a, double b) { return fmin(a, b); }
 __device__ __forceinline__ double rmax(double a, double b) { return fmax(a, b); }
 
+// The view-independent part: normalised quaternion, its rotation Rq and
+// M = Rq diag(s); false for a zero quaternion.
+template <typename R>
+__device__ __forceinline__ bool rot_scale(R sx, R sy, R sz, R qw, R qx, R qy, R qz, GeoT<R> &o)
+{
+    R nq2 = qw * qw;  nq2 = nq2 + qx * qx;  nq2 = nq2 + qy * qy;  nq2 = nq2 + qz * qz;
+    if (!(nq2 > (R)0)) return false;
+    const R nq = sqrt(nq2);
+    const R w = qw / nq, a = qx / nq, b = qy / nq, c = qz / nq;
+    o.w = w; o.qa = a; o.qb = b; o.qc = c; o.nq = nq;
+    const R one = (R)1, two = (R)2;
+    R *Q = o.Rq;
+    Q[0] = one - two * (b * b + c * c);
+    Q[1] = two * (a * b - w * c);
+    Q[2] = two * (a * c + w * b);
+    Q[3] = two * (a * b + w * c);
+    Q[4] = one - two * (a * a + c * c);
+    Q[5] = two * (b * c - w * a);
+    Q[6] = two * (a * c - w * b);
+    Q[7] = two * (b * c + w * a);
+    Q[8] = one - two * (a * a + b * b);
+    R *M = o.M;
+    M[0] = Q[0] * sx; M[1] = Q[1] * sy; M[2] = Q[2] * sz;
+    M[3] = Q[3] * sx; M[4] = Q[4] * sy; M[5] = Q[5] * sz;
+    M[6] = Q[6] * sx; M[7] = Q[7] * sy; M[8] = Q[8] * sz;
+    return true;
+}
+
 // Geometry of one Gaussian in scalar type R (float: the op-order contract of
 // the forward; double: the backward's recomputation); returns false when it
 // is culled before the rect.
@@ -71,26 +99,8 @@ __device__ __forceinline__ bool geometry(const Cam &cam, R mx, R my, R mz, R sx,
     o.u = fx * o.tx + (R)cam.cx;
     o.v = fy * o.ty + (R)cam.cy;
 
-    R nq2 = qw * qw;  nq2 = nq2 + qx * qx;  nq2 = nq2 + qy * qy;  nq2 = nq2 + qz * qz;
-    if (!(nq2 > (R)0)) return false;
-    const R nq = sqrt(nq2);
-    const R w = qw / nq, a = qx / nq, b = qy / nq, c = qz / nq;
-    o.w = w; o.qa = a; o.qb = b; o.qc = c; o.nq = nq;
-    const R one = (R)1, two = (R)2;
-    R *Q = o.Rq;
-    Q[0] = one - two * (b * b + c * c);
-    Q[1] = two * (a * b - w * c);
-    Q[2] = two * (a * c + w * b);
-    Q[3] = two * (a * b + w * c);
-    Q[4] = one - two * (a * a + c * c);
-    Q[5] = two * (b * c - w * a);
-    Q[6] = two * (a * c - w * b);
-    Q[7] = two * (b * c + w * a);
-    Q[8] = one - two * (a * a + b * b);
-    R *M = o.M;
-    M[0] = Q[0] * sx; M[1] = Q[1] * sy; M[2] = Q[2] * sz;
-    M[3] = Q[3] * sx; M[4] = Q[4] * sy; M[5] = Q[5] * sz;
-    M[6] = Q[6] * sx; M[7] = Q[7] * sy; M[8] = Q[8] * sz;
+    if (!rot_scale(sx, sy, sz, qw, qx, qy, qz, o)) return false;
+    const R *M = o.M;
     R *S = o.S;
     S[0] = (M[0] * M[0] + M[1] * M[1]) + M[2] * M[2];
     S[1] = (M[0] * M[3] + M[1] * M[4]) + M[2] * M[5];
@@ -776,8 +786,8 @@ __device__ __forceinline__ void geom_backward(
     const float s0 = scales[g], s1 = scales[n + g], s2 = scales[2 * n + g];
     const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];
     const float o = opac[g];
-    float acc_mean[3] = {0.0f, 0.0f, 0.0f}, acc_ls[3] = {0.0f, 0.0f, 0.0f};
-    float acc_q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc_logit = 0.0f;
+    float acc_mean[3] = {0.0f, 0.0f, 0.0f}, acc_ls[3], acc_q[4], acc_logit = 0.0f;
+    double dS_sum[3][3] = {{0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}};
     bool touched = false;
     // the next view's radius, conic and gradients are loaded one view ahead
     // (a culled Gaussian's gradient row holds no value and is not used)
@@ -806,7 +816,8 @@ __device__ __forceinline__ void geom_backward(
     touched = true;
     // The view-independent part (rotation, 3D covariance) is recomputed per
     // view from opaque copies of the parameters: held across views in fp64
-    // it would cost ~50 registers.
+    // it would cost ~50 registers.  Its gradient chain runs once, after the
+    // views, on the summed Sigma gradient.
     float mx = mx0, my = my0, mz = mz0, qw = qw0, qx = qx0, qy = qy0, qz = qz0;
     float s[3] = {s0, s1, s2};
     asm volatile("" : "+v"(mx), "+v"(my), "+v"(mz), "+v"(qw), "+v"(qx), "+v"(qy), "+v"(qz));
@@ -907,32 +918,13 @@ __device__ __forceinline__ void geom_backward(
         dpz = dpz + dJ12 * fy * (G.J12 * (-z / fy)) * iz2;
     }
 
-    const double *M = G.M, *Q = G.Rq;
-    double dM[9];
+    // Sigma's gradient is summed over the views (fp64); the rest of the
+    // chain (Sigma = M M^T, M = Rq diag(s), the quaternion) is linear in it
+    // and view-independent, so it runs once after the loop
 #pragma unroll
     for (int i = 0; i < 3; i++)
 #pragma unroll
-        for (int j = 0; j < 3; j++)
-            dM[i * 3 + j] = 2.0 * (dS[i][0] * M[j] + dS[i][1] * M[3 + j] + dS[i][2] * M[6 + j]);
-    double ds[3];
-#pragma unroll
-    for (int j = 0; j < 3; j++) ds[j] = Q[j] * dM[j] + Q[3 + j] * dM[3 + j] + Q[6 + j] * dM[6 + j];
-    double dR[9];
-#pragma unroll
-    for (int i = 0; i < 3; i++)
-#pragma unroll
-        for (int j = 0; j < 3; j++) dR[i * 3 + j] = dM[i * 3 + j] * (double)s[j];
-    const double w = G.w, a = G.qa, b = G.qb, c = G.qc;
-    double dq[4];
-    dq[0] = 2.0 * (-c * dR[1] + b * dR[2] + c * dR[3] - a * dR[5] - b * dR[6] + a * dR[7]);
-    dq[1] = 2.0 * (b * dR[1] + c * dR[2] + b * dR[3] - w * dR[5] + c * dR[6] + w * dR[7]) -
-            4.0 * a * (dR[4] + dR[8]);
-    dq[2] = 2.0 * (a * dR[1] + w * dR[2] + a * dR[3] + c * dR[5] - w * dR[6] + c * dR[7]) -
-            4.0 * b * (dR[0] + dR[8]);
-    dq[3] = 2.0 * (-w * dR[1] + a * dR[2] + w * dR[3] + b * dR[5] + a * dR[6] + b * dR[7]) -
-            4.0 * c * (dR[0] + dR[4]);
-    const double qdot = w * dq[0] + a * dq[1] + b * dq[2] + c * dq[3];
-    const double qh[4] = {w, a, b, c};
+        for (int j = 0; j < 3; j++) dS_sum[i][j] += dS[i][j];
 
 #pragma unroll
     for (int j = 0; j < 3; j++) {
@@ -940,13 +932,44 @@ __device__ __forceinline__ void geom_backward(
         acc_mean[j] += c;
         if constexpr (kMotion) acc_vel[j] += dtv * c;
     }
-#pragma unroll
-    for (int r = 0; r < 3; r++) acc_ls[r] += (float)((double)s[r] * ds[r]);
-#pragma unroll
-    for (int r = 0; r < 4; r++) acc_q[r] += (float)((dq[r] - qh[r] * qdot) / G.nq);
     acc_logit += o * (1.0f - o) * go;
     }   // views
     if (!touched) return;
+    {
+        GeoT<double> H;
+        rot_scale<double>(s0, s1, s2, qw0, qx0, qy0, qz0, H);   // a touched Gaussian has a non-zero quaternion
+        const double *M = H.M, *Q = H.Rq;
+        const double sd[3] = {s0, s1, s2};
+        double dM[9];
+#pragma unroll
+        for (int i = 0; i < 3; i++)
+#pragma unroll
+            for (int j = 0; j < 3; j++)
+                dM[i * 3 + j] = 2.0 * (dS_sum[i][0] * M[j] + dS_sum[i][1] * M[3 + j] + dS_sum[i][2] * M[6 + j]);
+        double ds[3];
+#pragma unroll
+        for (int j = 0; j < 3; j++) ds[j] = Q[j] * dM[j] + Q[3 + j] * dM[3 + j] + Q[6 + j] * dM[6 + j];
+        double dR[9];
+#pragma unroll
+        for (int i = 0; i < 3; i++)
+#pragma unroll
+            for (int j = 0; j < 3; j++) dR[i * 3 + j] = dM[i * 3 + j] * sd[j];
+        const double w = H.w, a = H.qa, b = H.qb, c = H.qc;
+        double dq[4];
+        dq[0] = 2.0 * (-c * dR[1] + b * dR[2] + c * dR[3] - a * dR[5] - b * dR[6] + a * dR[7]);
+        dq[1] = 2.0 * (b * dR[1] + c * dR[2] + b * dR[3] - w * dR[5] + c * dR[6] + w * dR[7]) -
+                4.0 * a * (dR[4] + dR[8]);
+        dq[2] = 2.0 * (a * dR[1] + w * dR[2] + a * dR[3] + c * dR[5] - w * dR[6] + c * dR[7]) -
+                4.0 * b * (dR[0] + dR[8]);
+        dq[3] = 2.0 * (-w * dR[1] + a * dR[2] + w * dR[3] + b * dR[5] + a * dR[6] + b * dR[7]) -
+                4.0 * c * (dR[0] + dR[4]);
+        const double qdot = w * dq[0] + a * dq[1] + b * dq[2] + c * dq[3];
+        const double qh[4] = {w, a, b, c};
+#pragma unroll
+        for (int r = 0; r < 3; r++) acc_ls[r] = (float)(sd[r] * ds[r]);
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc_q[r] = (float)((dq[r] - qh[r] * qdot) / H.nq);
+    }
 #pragma unroll
     for (int j = 0; j < 3; j++) d_means[j * n + g] += acc_mean[j];
     if constexpr (kMotion) {
