@@ -787,7 +787,7 @@ __device__ __forceinline__ void geom_backward(
     const float qw0 = quats[g], qx0 = quats[n + g], qy0 = quats[2 * n + g], qz0 = quats[3 * n + g];
     const float o = opac[g];
     float acc_mean[3] = {0.0f, 0.0f, 0.0f}, acc_ls[3], acc_q[4], acc_logit = 0.0f;
-    double dS_sum[3][3] = {{0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}};
+    double dS_sum[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     bool touched = false;
     // the next view's radius, conic and gradients are loaded one view ahead
     // (a culled Gaussian's gradient row holds no value and is not used)
@@ -875,12 +875,6 @@ __device__ __forceinline__ void geom_backward(
         D11 = P10 * F10 + P11 * F11;
     }
     const double *T = G.T;
-    double dS[3][3];
-#pragma unroll
-    for (int k = 0; k < 3; k++)
-#pragma unroll
-        for (int l = 0; l < 3; l++)
-            dS[k][l] = T[k] * (D00 * T[l] + D01 * T[3 + l]) + T[3 + k] * (D01 * T[l] + D11 * T[3 + l]);
     const double Sg[3][3] = {{G.S[0], G.S[1], G.S[2]}, {G.S[1], G.S[3], G.S[4]}, {G.S[2], G.S[4], G.S[5]}};
     double DT[2][3];
 #pragma unroll
@@ -918,13 +912,14 @@ __device__ __forceinline__ void geom_backward(
         dpz = dpz + dJ12 * fy * (G.J12 * (-z / fy)) * iz2;
     }
 
-    // Sigma's gradient is summed over the views (fp64); the rest of the
-    // chain (Sigma = M M^T, M = Rq diag(s), the quaternion) is linear in it
-    // and view-independent, so it runs once after the loop
+    // Sigma's gradient T^T D T (symmetric: its upper triangle, 00 01 02 11
+    // 12 22) is summed over the views in fp64; the rest of the chain (Sigma =
+    // M M^T, M = Rq diag(s), the quaternion) is linear in it and
+    // view-independent, so it runs once after the loop
 #pragma unroll
-    for (int i = 0; i < 3; i++)
+    for (int k = 0, e = 0; k < 3; k++)
 #pragma unroll
-        for (int j = 0; j < 3; j++) dS_sum[i][j] += dS[i][j];
+        for (int l = k; l < 3; l++, e++) dS_sum[e] += T[k] * DT[0][l] + T[3 + k] * DT[1][l];
 
 #pragma unroll
     for (int j = 0; j < 3; j++) {
@@ -940,12 +935,15 @@ __device__ __forceinline__ void geom_backward(
         rot_scale<double>(s0, s1, s2, qw0, qx0, qy0, qz0, H);   // a touched Gaussian has a non-zero quaternion
         const double *M = H.M, *Q = H.Rq;
         const double sd[3] = {s0, s1, s2};
+        const double dSg[3][3] = {{dS_sum[0], dS_sum[1], dS_sum[2]},
+                                  {dS_sum[1], dS_sum[3], dS_sum[4]},
+                                  {dS_sum[2], dS_sum[4], dS_sum[5]}};
         double dM[9];
 #pragma unroll
         for (int i = 0; i < 3; i++)
 #pragma unroll
             for (int j = 0; j < 3; j++)
-                dM[i * 3 + j] = 2.0 * (dS_sum[i][0] * M[j] + dS_sum[i][1] * M[3 + j] + dS_sum[i][2] * M[6 + j]);
+                dM[i * 3 + j] = 2.0 * (dSg[i][0] * M[j] + dSg[i][1] * M[3 + j] + dSg[i][2] * M[6 + j]);
         double ds[3];
 #pragma unroll
         for (int j = 0; j < 3; j++) ds[j] = Q[j] * dM[j] + Q[3 + j] * dM[3 + j] + Q[6 + j] * dM[6 + j];
